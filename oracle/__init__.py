@@ -1,0 +1,232 @@
+"""CPU oracle of wave-index sparse decode attention (ctypes front of liboracle.so).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU-baseline
+leg use it.  The GPU library never imports it, and the two share no code.
+
+The arithmetic lives in oracle.c (plain C, binary64 except the steps defined in
+fp32/bf16).  This module only marshals numpy arrays.  Method: RetroInfer page,
+section 2.A (steady, retrieval and estimation zones over a segmented-clustered
+KV cache).
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+D = 128
+
+
+def build():
+    """Compile liboracle.so (gcc, OpenMP over independent units, no fused or fast math)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra", "-ffp-contract=off",
+           "-fno-fast-math", "-o", _LIB_PATH, os.path.join(_HERE, "oracle.c"), "-lm"]
+    subprocess.check_call(cmd)
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, i32, i64, u64, f64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_double
+        lib.ref_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        lib.ref_bf16_to_f32.restype = ctypes.c_float
+        lib.ref_f32_to_bf16.argtypes = [ctypes.c_float]
+        lib.ref_f32_to_bf16.restype = ctypes.c_uint16
+        lib.ref_f32_to_bf16_array.argtypes = [P, i64, P]
+        lib.ref_splitmix64_stream.argtypes = [u64, i64, P]
+        lib.ref_init_indices.argtypes = [i32, i32, u64, i64, P]
+        lib.ref_segment_clusters.argtypes = [i64, i32, i32]
+        lib.ref_segment_clusters.restype = i64
+        lib.ref_num_clusters.argtypes = [i64, i32, i32]
+        lib.ref_num_clusters.restype = i64
+        lib.ref_k_from_frac.argtypes = [f64, i64]
+        lib.ref_k_from_frac.restype = i64
+        lib.ref_sq_dist.argtypes = [P, P]
+        lib.ref_sq_dist.restype = f64
+        lib.ref_assign_point.argtypes = [P, P, i32]
+        lib.ref_assign_point.restype = i32
+        lib.ref_kmeans_segment.argtypes = [P, i32, i32, i32, u64, i64, i32, P, P, P, P]
+        lib.ref_build.argtypes = [i32, i32, P, P, P, i32, i32, i32, u64] + [P] * 11
+        lib.ref_build.restype = ctypes.c_int
+        lib.ref_index_from_assign.argtypes = [i32, i32, P, P, P, i32, i32, u64, P] + [P] * 10
+        lib.ref_index_from_assign.restype = ctypes.c_int
+        lib.ref_rank_key.argtypes = [P, P]
+        lib.ref_rank_key.restype = ctypes.c_float
+        lib.ref_select.argtypes = [P, P, i32, i32, P]
+        lib.ref_decode.argtypes = [i32, i32, i32, P, i32, i32, P, P, P, P, P, P, i32, i32, f64, i32, P, P, P, P]
+        lib.ref_decode.restype = ctypes.c_int
+        lib.ref_full_attention.argtypes = [i32, i32, i32, P, P, P, P, P, P]
+        _lib = lib
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+# ---------------------------------------------------------------- format / rng
+def f32_to_bf16(x):
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().ref_f32_to_bf16_array(_p(x), x.size, _p(out))
+    return out
+
+
+def bf16_to_f32(h):
+    return (_c(h, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def splitmix64_stream(state, n):
+    out = np.empty(n, dtype=np.uint64)
+    _load().ref_splitmix64_stream(state, n, _p(out))
+    return out
+
+
+def init_indices(L, K, seed, unit):
+    out = np.empty(K, dtype=np.int32)
+    _load().ref_init_indices(L, K, seed, unit, _p(out))
+    return out
+
+
+# ---------------------------------------------------------------- segments / k
+def segment_clusters(L, seg_len, K_s):
+    return _load().ref_segment_clusters(L, seg_len, K_s)
+
+
+def num_clusters(N, seg_len, K_s):
+    return _load().ref_num_clusters(N, seg_len, K_s)
+
+
+def k_from_frac(frac, C):
+    return _load().ref_k_from_frac(frac, C)
+
+
+# ---------------------------------------------------------------- k-means
+def sq_dist(x, c):
+    return _load().ref_sq_dist(_p(_c(x, np.uint16)), _p(_c(c, np.uint16)))
+
+
+def assign_point(x, chat):
+    chat = _c(chat, np.uint16)
+    return _load().ref_assign_point(_p(_c(x, np.uint16)), _p(chat), chat.shape[0])
+
+
+def kmeans_segment(X, K, iters, seed, unit=0, exact=False):
+    """Lloyd's k-means of one segment. Returns (assign, centroids fp32, trace [iters][L], objective [iters])."""
+    X = _c(X, np.uint16)
+    L = X.shape[0]
+    a = np.empty(L, dtype=np.int32)
+    c = np.empty((K, D), dtype=np.float32)
+    tr = np.empty((iters, L), dtype=np.int32)
+    obj = np.empty(iters, dtype=np.float64)
+    _load().ref_kmeans_segment(_p(X), L, K, iters, seed, unit, 1 if exact else 0, _p(a), _p(c), _p(tr), _p(obj))
+    return a, c, tr, obj
+
+
+class Index:
+    """Host copy of every index array (same layout as the GPU library's)."""
+
+    FIELDS = ("k_sorted", "v_sorted", "perm", "inv_perm", "assign", "offsets", "sizes", "centroids",
+              "centroids_bf16", "vsum")
+
+    def __init__(self, n_kv_heads, ctx, seg_len, clusters_per_seg):
+        self.G = int(n_kv_heads)
+        self.ctx = _c(ctx, np.int64)
+        self.seg_len = int(seg_len)
+        self.K_s = int(clusters_per_seg)
+        C = [num_clusters(int(n), seg_len, clusters_per_seg) for n in self.ctx]
+        self.C = np.array(C, dtype=np.int64)
+        rows = int(self.G * self.ctx.sum())
+        ncl = int(self.G * self.C.sum())
+        noff = int(self.G * (self.C + 1).sum())
+        self.k_sorted = np.empty((rows, D), np.uint16)
+        self.v_sorted = np.empty((rows, D), np.uint16)
+        self.perm = np.empty(rows, np.int32)
+        self.inv_perm = np.empty(rows, np.int32)
+        self.assign = np.empty(rows, np.int32)
+        self.offsets = np.empty(noff, np.int32)
+        self.sizes = np.empty(ncl, np.int32)
+        self.centroids = np.empty((ncl, D), np.float32)
+        self.centroids_bf16 = np.empty((ncl, D), np.uint16)
+        self.vsum = np.empty((ncl, D), np.float32)
+
+    def _outs(self):
+        return [_p(getattr(self, f)) for f in self.FIELDS]
+
+
+def build(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, iters, seed, trace=False):
+    """Whole index build (segmented k-means + layout). Returns Index (and the trace if asked)."""
+    idx = Index(n_kv_heads, ctx, seg_len, clusters_per_seg)
+    K, V = _c(K, np.uint16), _c(V, np.uint16)
+    tr = np.empty((iters, K.shape[0]), np.int32) if trace else None
+    rc = _load().ref_build(len(idx.ctx), idx.G, _p(idx.ctx), _p(K), _p(V), seg_len, clusters_per_seg, iters, seed,
+                           *idx._outs(), _p(tr))
+    if rc != 0:
+        raise ValueError("ref_build rejected its arguments")
+    return (idx, tr) if trace else idx
+
+
+def index_from_assign(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, seed, assign):
+    """Index over a prescribed clustering: one update from the seeded init with the given labels, then layout."""
+    idx = Index(n_kv_heads, ctx, seg_len, clusters_per_seg)
+    K, V = _c(K, np.uint16), _c(V, np.uint16)
+    rc = _load().ref_index_from_assign(len(idx.ctx), idx.G, _p(idx.ctx), _p(K), _p(V), seg_len, clusters_per_seg,
+                                       seed, _p(_c(assign, np.int32)), *idx._outs())
+    if rc != 0:
+        raise ValueError("ref_index_from_assign rejected its arguments")
+    return idx
+
+
+# ---------------------------------------------------------------- decode
+def rank_key(q, c):
+    return _load().ref_rank_key(_p(_c(q, np.uint16)), _p(_c(c, np.uint16)))
+
+
+def select(keys, ids, k):
+    keys, ids = _c(keys, np.float32), _c(ids, np.int32)
+    out = np.empty(k, np.int32)
+    _load().ref_select(_p(keys), _p(ids), len(keys), k, _p(out))
+    return out
+
+
+def decode_k_max(C_list, topk_frac):
+    return max([k_from_frac(topk_frac, int(C)) for C in C_list] + [0])
+
+
+def decode(index, K, V, q, n_sink, n_local, topk_frac, k_max=None):
+    """Wave-index decode for q [B][H][128] against `index`. Returns (out [B,H,128] f64, lse [B,H], ids, k [B,H])."""
+    q = _c(q, np.uint16)
+    B, H = q.shape[0], q.shape[1]
+    if k_max is None:
+        k_max = decode_k_max(index.C, topk_frac)
+    out = np.empty((B, H, D), np.float64)
+    lse = np.empty((B, H), np.float64)
+    ids = np.empty((B, H, max(k_max, 1)), np.int32)
+    kc = np.empty((B, H), np.int32)
+    rc = _load().ref_decode(B, H, index.G, _p(index.ctx), index.seg_len, index.K_s, _p(_c(K, np.uint16)),
+                            _p(_c(V, np.uint16)), _p(index.assign), _p(index.centroids_bf16), _p(index.vsum), _p(q),
+                            n_sink, n_local, topk_frac, k_max, _p(out), _p(lse), _p(ids), _p(kc))
+    if rc != 0:
+        raise ValueError("ref_decode rejected its arguments (rc=%d)" % rc)
+    return out, lse, ids[:, :, :k_max], kc
+
+
+def full_attention(K, V, q, n_kv_heads, ctx):
+    q = _c(q, np.uint16)
+    B, H = q.shape[0], q.shape[1]
+    ctx = _c(ctx, np.int64)
+    out = np.empty((B, H, D), np.float64)
+    lse = np.empty((B, H), np.float64)
+    _load().ref_full_attention(B, H, n_kv_heads, _p(ctx), _p(_c(K, np.uint16)), _p(_c(V, np.uint16)), _p(q),
+                               _p(out), _p(lse))
+    return out, lse

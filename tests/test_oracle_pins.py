@@ -1,0 +1,487 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix (no GPU).
+
+Each test fixes one part of the oracle with something other than the oracle itself:
+format definitions and hand-worked rounding cases, published generator outputs,
+brute force on tiny inputs, library routines (scipy, scikit-learn, torch's bf16
+conversion), closed forms and invariants.  The method is RetroInfer's wave index
+(gist.science summary page, section 2.A: steady, retrieval and estimation zones over
+a segmented-clustered KV cache).
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import scipy.cluster.vq
+import scipy.special
+import torch
+
+import oracle
+import synth
+
+D = 128
+
+
+def _bits(x):
+    return np.array([x], dtype=np.float32).view(np.uint32)[0]
+
+
+def _f(bits):
+    return np.array([bits], dtype=np.uint32).view(np.float32)[0]
+
+
+# ------------------------------------------------------------------------- bf16
+@pytest.mark.parametrize("src,dst", [
+    (0x3F808000, 0x3F80),  # 1 + 2^-8: halfway between 0x3F80 and 0x3F81, tie to even -> 0x3F80
+    (0x3F818000, 0x3F82),  # halfway between 0x3F81 and 0x3F82, tie to even -> 0x3F82
+    (0x3F80C000, 0x3F81),  # above halfway -> up
+    (0x3F804000, 0x3F80),  # below halfway -> down
+    (0xBF808000, 0xBF80),  # negative tie, magnitude rounds to even
+    (0x7F7FFFFF, 0x7F80),  # largest float rounds past the largest bf16 to infinity
+    (0x00000000, 0x0000),
+    (0x80000000, 0x8000),  # -0 stays -0
+])
+def test_bf16_rne_hand_cases(src, dst):
+    assert oracle.f32_to_bf16(np.array([_f(src)]))[0] == dst
+
+
+def test_bf16_roundtrip_and_library_conversion():
+    # every non-NaN bf16 value is exactly representable: widening then rounding returns it
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f = oracle.bf16_to_f32(h)
+    ok = ~np.isnan(f)
+    assert np.array_equal(oracle.f32_to_bf16(f[ok]), h[ok])
+    # NaN stays NaN
+    assert np.isnan(oracle.bf16_to_f32(oracle.f32_to_bf16(np.array([np.nan], np.float32))))[0]
+    # random floats: same as torch's round-to-nearest-even float32 -> bfloat16 conversion
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.f32_to_bf16(x), ref)
+
+
+# ------------------------------------------------------------------- SplitMix64
+def test_splitmix64_published_outputs():
+    # Reference outputs of SplitMix64 (Steele, Lea and Flood 2014; public-domain
+    # reference implementation): state 0 and state 1234567.
+    assert [int(v) for v in oracle.splitmix64_stream(0, 3)] == [
+        0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+    assert [int(v) for v in oracle.splitmix64_stream(1234567, 5)] == [
+        6457827717110365317, 3203168211198807973, 9817491932198370423, 4593380528125082431,
+        16408922859458223821]
+
+
+def test_init_indices_distinct_in_range():
+    for L, K in [(8192, 512), (100, 100), (37, 3), (1, 1)]:
+        for u in range(5):
+            idx = oracle.init_indices(L, K, 1234, u)
+            assert len(set(idx.tolist())) == K
+            assert idx.min() >= 0 and idx.max() < L
+    # K = L: the shuffle is a full permutation
+    assert sorted(oracle.init_indices(64, 64, 7, 3).tolist()) == list(range(64))
+    # deterministic, and different units differ
+    assert np.array_equal(oracle.init_indices(8192, 512, 1, 0), oracle.init_indices(8192, 512, 1, 0))
+    assert not np.array_equal(oracle.init_indices(8192, 512, 1, 0), oracle.init_indices(8192, 512, 1, 1))
+
+
+def test_init_shuffle_is_uniform():
+    # Fisher-Yates draws every permutation with equal probability; the classic
+    # "j = next() mod L" mistake does not (chi-square over the 24 orders of 4 items).
+    counts = {}
+    n = 48000
+    for u in range(n):
+        p = tuple(oracle.init_indices(4, 4, 99, u).tolist())
+        counts[p] = counts.get(p, 0) + 1
+    assert len(counts) == 24
+    exp = n / 24
+    chi2 = sum((c - exp) ** 2 / exp for c in counts.values())
+    assert chi2 < 60.0  # 23 dof: p ~ 5e-5 at 60
+
+
+# ------------------------------------------------------------- segments and k
+def test_segment_cluster_counts():
+    assert oracle.num_clusters(16384, 8192, 512) == 1024
+    assert oracle.num_clusters(131072, 8192, 512) == 8192
+    assert oracle.num_clusters(1048576, 16384, 1024) == 65536
+    assert oracle.num_clusters(1048576, 8192, 512) == 65536
+    # partial last segment of 1000 tokens: ceil(1000 * 512 / 8192) = ceil(62.5) = 63
+    assert oracle.segment_clusters(1000, 8192, 512) == 63
+    assert oracle.num_clusters(8 * 8192 + 1000, 8192, 512) == 8 * 512 + 63
+    assert oracle.segment_clusters(1, 8192, 512) == 1
+    assert oracle.num_clusters(5, 8192, 512) == 1
+
+
+@pytest.mark.parametrize("frac,C,k", [(0.05, 1024, 52), (0.02, 8192, 164), (0.018, 65536, 1180),
+                                      (0.0, 8192, 0), (1.0, 8192, 8192), (1e-9, 10, 1)])
+def test_k_from_frac(frac, C, k):
+    assert oracle.k_from_frac(frac, C) == k
+
+
+# ---------------------------------------------------------------------- k-means
+def _tiny_data(seed, L, spread=3.0):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((L, D)) * 0.3
+    X[:, :4] += rng.integers(0, 4, (L, 1)) * spread  # a few separated groups along the first dims
+    return oracle.f32_to_bf16(X.astype(np.float32))
+
+
+def test_assign_point_matches_scipy_vq():
+    rng = np.random.default_rng(1)
+    X = oracle.f32_to_bf16(rng.standard_normal((300, D)).astype(np.float32))
+    Cb = oracle.f32_to_bf16(rng.standard_normal((17, D)).astype(np.float32))
+    codes, _ = scipy.cluster.vq.vq(oracle.bf16_to_f32(X).astype(np.float64), oracle.bf16_to_f32(Cb).astype(np.float64))
+    ours = np.array([oracle.assign_point(x, Cb) for x in X])
+    assert np.array_equal(ours, codes)
+
+
+def test_assign_ties_go_to_lowest_id():
+    rng = np.random.default_rng(2)
+    c = oracle.f32_to_bf16(rng.standard_normal((1, D)).astype(np.float32))
+    other = oracle.f32_to_bf16(rng.standard_normal((1, D)).astype(np.float32) + 5)
+    chat = np.concatenate([other, c, c, c])  # ids 1, 2, 3 identical
+    assert oracle.assign_point(c[0], chat) == 1
+
+
+def test_kmeans_hand_example_two_groups():
+    # Six points on the first axis, two groups {-2,-1.5,-1} and {1,1.5,2}; whatever two
+    # tokens the seeded init picks, Lloyd's rounds reach the two groups with means -1.5
+    # and 1.5 (exact in fp32: -4.5/3 and 4.5/3).
+    vals = [-2.0, -1.5, -1.0, 1.0, 1.5, 2.0]
+    X = np.zeros((6, D), np.float32)
+    X[:, 0] = vals
+    Xb = oracle.f32_to_bf16(X)
+    for seed in range(20):
+        a, c, _, _ = oracle.kmeans_segment(Xb, 2, 6, seed)
+        assert a[0] == a[1] == a[2] and a[3] == a[4] == a[5] and a[0] != a[3]
+        assert c[a[0], 0] == -1.5 and c[a[3], 0] == 1.5
+        assert np.all(c[:, 1:] == 0.0)
+
+
+def test_kmeans_exact_mode_matches_sklearn_lloyd():
+    from sklearn.cluster import KMeans
+    for seed in range(3):
+        Xb = _tiny_data(seed, 64)
+        K, iters = 6, 30
+        a, c, tr, obj = oracle.kmeans_segment(Xb, K, iters, 1000 + seed, exact=True)
+        init = oracle.bf16_to_f32(Xb[oracle.init_indices(64, K, 1000 + seed, 0)]).astype(np.float64)
+        km = KMeans(n_clusters=K, init=init, n_init=1, max_iter=iters, tol=0.0, algorithm="lloyd")
+        km.fit(oracle.bf16_to_f32(Xb).astype(np.float64))
+        assert np.array_equal(a, km.labels_)
+        np.testing.assert_allclose(c, km.cluster_centers_.astype(np.float32), rtol=1e-6, atol=1e-6)
+
+
+def test_kmeans_exact_mode_objective_monotone():
+    K, _, _ = synth.kv(11, 1, 1, np.array([2048]), 2048)
+    for unit in range(3):
+        _, _, _, obj = oracle.kmeans_segment(K, 128, 10, 5, unit=unit, exact=True)
+        assert np.all(obj[1:] <= obj[:-1] * (1 + 1e-12)), obj
+    # spec mode (bf16 centroids in the assignment) stays monotone to 1e-3
+    _, _, _, obj = oracle.kmeans_segment(K, 128, 10, 5, unit=0, exact=False)
+    assert np.all(obj[1:] <= obj[:-1] * (1 + 1e-3)), obj
+
+
+def test_kmeans_update_is_ordered_fp32_mean():
+    # one round: centroids are the ordered fp32 sums of the first assignment's members
+    # divided by n (numpy's sequential float32 cumsum and IEEE float32 division);
+    # empty clusters keep the initial token.
+    Xb = _tiny_data(5, 300)
+    K = 40
+    a, c, tr, _ = oracle.kmeans_segment(Xb, K, 1, 77, unit=2)
+    X = oracle.bf16_to_f32(Xb)
+    init = oracle.init_indices(300, K, 77, 2)
+    for j in range(K):
+        mem = np.nonzero(tr[0] == j)[0]
+        if len(mem) == 0:
+            assert np.array_equal(c[j], X[init[j]])
+            continue
+        S = np.cumsum(X[mem], axis=0, dtype=np.float32)[-1]
+        assert np.array_equal(c[j], S / np.float32(len(mem)))
+
+
+def test_kmeans_brute_force_tiny():
+    # tiny segments: every assignment is the brute-force argmin over all centroids
+    # computed independently (float64 distances through numpy), with the centroids
+    # the oracle used in that round (bf16 of the previous round's fp32 centroids).
+    Xb = _tiny_data(9, 48)
+    K, iters = 5, 4
+    X = oracle.bf16_to_f32(Xb).astype(np.float64)
+    init = oracle.init_indices(48, K, 3, 0)
+    cent = X[init].astype(np.float32)
+    _, _, tr, _ = oracle.kmeans_segment(Xb, K, iters, 3)
+    for it in range(iters):
+        chat = oracle.bf16_to_f32(oracle.f32_to_bf16(cent)).astype(np.float64)
+        d = ((X[:, None, :] - chat[None, :, :]) ** 2).sum(-1)
+        assert np.array_equal(tr[it], d.argmin(1))
+        for j in range(K):
+            mem = np.nonzero(tr[it] == j)[0]
+            if len(mem):
+                cent[j] = np.cumsum(X[mem].astype(np.float32), axis=0, dtype=np.float32)[-1] / np.float32(len(mem))
+
+
+# ------------------------------------------------------------------ index layout
+def _small_build(seed=3, ctx=(3000, 1700), G=2, seg=1024, K_s=64, iters=3):
+    ctx = np.array(ctx, np.int64)
+    K, V, _ = synth.kv(seed, len(ctx), G, ctx, seg)
+    idx = oracle.build(K, V, G, ctx, seg, K_s, iters, 1234)
+    return K, V, ctx, idx
+
+
+def test_layout_invariants():
+    K, V, ctx, idx = _small_build()
+    G = idx.G
+    row = clu = off = 0
+    for b, N in enumerate(ctx):
+        C = oracle.num_clusters(int(N), idx.seg_len, idx.K_s)
+        for g in range(G):
+            sl = slice(row, row + N)
+            perm, inv, a = idx.perm[sl], idx.inv_perm[sl], idx.assign[sl]
+            assert np.array_equal(np.sort(perm), np.arange(N))
+            assert np.array_equal(inv[perm], np.arange(N))
+            assert np.array_equal(idx.k_sorted[sl], K[sl][perm])
+            assert np.array_equal(idx.v_sorted[sl], V[sl][perm])
+            # sorted by (cluster, position)
+            key = a[perm].astype(np.int64) * (N + 1) + perm
+            assert np.all(np.diff(key) > 0)
+            sizes = idx.sizes[clu:clu + C]
+            offs = idx.offsets[off:off + C + 1]
+            assert np.array_equal(sizes, np.bincount(a, minlength=C))
+            assert offs[0] == 0 and np.array_equal(np.diff(offs), sizes)
+            # segments: ids of segment s own exactly its tokens; offsets at segment bases
+            nseg = -(-N // idx.seg_len)
+            for s in range(nseg):
+                t0, t1 = s * idx.seg_len, min((s + 1) * idx.seg_len, N)
+                kc = oracle.segment_clusters(t1 - t0, idx.seg_len, idx.K_s)
+                assert a[t0:t1].min() >= s * idx.K_s and a[t0:t1].max() < s * idx.K_s + kc
+                assert offs[s * idx.K_s] == t0
+            Vf = oracle.bf16_to_f32(V[sl]).astype(np.float64)
+            for j in range(C):
+                mem = np.nonzero(a == j)[0]
+                vs = idx.vsum[clu + j]
+                if len(mem) == 0:
+                    assert np.all(vs == 0)
+                    continue
+                # ordered fp32 sum, and within 1e-6 of the exact sum
+                assert np.array_equal(vs, np.cumsum(oracle.bf16_to_f32(V[sl][mem]), axis=0, dtype=np.float32)[-1])
+                ex = Vf[mem].sum(0)
+                assert np.all(np.abs(vs - ex) <= 1e-6 * np.abs(Vf[mem]).sum(0) + 1e-30)
+            # chat = RNE bf16 of the fp32 centroids (torch's conversion)
+            cc = idx.centroids[clu:clu + C]
+            ref = torch.from_numpy(cc).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            assert np.array_equal(idx.centroids_bf16[clu:clu + C], ref)
+            row += N
+            clu += C
+            off += C + 1
+
+
+def test_build_equals_per_segment_kmeans():
+    K, V, ctx, idx = _small_build(ctx=(2500,), G=1, iters=4)
+    # units are enumerated (b, g, segment); unit u seeds segment u here (B=1, G=1)
+    for s in range(3):
+        t0, t1 = s * 1024, min((s + 1) * 1024, 2500)
+        kc = oracle.segment_clusters(t1 - t0, 1024, 64)
+        a, c, _, _ = oracle.kmeans_segment(K[t0:t1], kc, 4, 1234, unit=s)
+        assert np.array_equal(idx.assign[t0:t1], a + s * 64)
+        assert np.array_equal(idx.centroids[s * 64:s * 64 + kc], c)
+
+
+# ---------------------------------------------------------------------- rank key
+def _bf(vals):
+    return oracle.f32_to_bf16(np.asarray(vals, np.float32))
+
+
+def test_rank_key_error_bound():
+    rng = np.random.default_rng(4)
+    for _ in range(200):
+        q = _bf(rng.standard_normal(D) * rng.uniform(0.1, 10))
+        c = _bf(rng.standard_normal(D) * rng.uniform(0.1, 10))
+        p = oracle.bf16_to_f32(q).astype(np.float64) * oracle.bf16_to_f32(c).astype(np.float64)
+        r = oracle.rank_key(q, c)
+        assert abs(r - p.sum()) <= 128 * 2.0 ** -24 * np.abs(p).sum()
+
+
+def test_rank_key_tree_order_worked_cases():
+    ones = np.ones(D, np.float32)
+    # (1) inside a lane the 8 products are added left to right from +0:
+    #     dims 0,1,2 = 2^24, 1, 1 -> ((2^24 + 1) + 1): 2^24 + 1 is a tie between 2^24 and
+    #     2^24 + 2 and rounds to the even 2^24, twice -> 2^24 (any order adding the two
+    #     ones first would give 2^24 + 2 exactly).
+    c = np.zeros(D, np.float32)
+    c[0], c[1], c[2] = 2.0 ** 24, 1.0, 1.0
+    assert oracle.rank_key(_bf(ones), _bf(c)) == 2.0 ** 24
+    # (2) lanes hold consecutive 8-dim blocks: dims 0 and 8 (lanes 0 and 1) with the
+    #     same values do not share a lane sum; butterfly s=8: lanes 0+8, 1+9 -> u0 = 2^24,
+    #     u1 = 1; ... s=1: 2^24 + 1 -> 2^24. Check with dims 0 = 2^24 and 8 = 1, 16 = 1:
+    #     lanes 0, 1, 2 -> s=8,4 leave them; s=2: u0+u2 = 2^24+1 -> 2^24, u1+u3 = 1;
+    #     s=1: 2^24 + 1 -> 2^24.
+    c = np.zeros(D, np.float32)
+    c[0], c[8], c[16] = 2.0 ** 24, 1.0, 1.0
+    assert oracle.rank_key(_bf(ones), _bf(c)) == 2.0 ** 24
+    # (3) butterfly order s = 8, 4, 2, 1: lane 0 = 2^24, lane 8 = 1, lane 12 = 1.
+    #     s=8: u0 = 2^24 + 1 -> 2^24, u4 = u4 + u12 = 1; s=4: u0 = 2^24 + 1 -> 2^24 -> 2^24.
+    #     (Order s = 4 first would give u8 + u12 = 2 and then 2^24 + 2 exactly.)
+    c = np.zeros(D, np.float32)
+    c[0], c[64], c[96] = 2.0 ** 24, 1.0, 1.0
+    assert oracle.rank_key(_bf(ones), _bf(c)) == 2.0 ** 24
+    # (4) q = 0 gives +0 (sign bit clear)
+    r = oracle.rank_key(_bf(np.zeros(D)), _bf(-np.ones(D)))
+    assert r == 0.0 and not math.copysign(1.0, r) < 0
+    # (5) a unit query picks one coordinate exactly
+    e = np.zeros(D, np.float32)
+    e[37] = 1.0
+    c = np.random.default_rng(5).standard_normal(D).astype(np.float32)
+    assert oracle.rank_key(_bf(e), _bf(c)) == oracle.bf16_to_f32(_bf(c))[37]
+
+
+def test_select_brute_force_with_ties():
+    rng = np.random.default_rng(6)
+    for trial in range(50):
+        n = int(rng.integers(1, 300))
+        keys = rng.choice(np.array([-1.5, -0.0, 0.0, 0.25, 3.0, 7.5], np.float32), n)
+        ids = rng.permutation(1000)[:n].astype(np.int32)
+        k = int(rng.integers(0, n + 1))
+        got = oracle.select(keys, ids, k)
+        want = [i for _, i in sorted(zip(keys.tolist(), ids.tolist()), key=lambda t: (-t[0], t[1]))][:k]
+        assert got.tolist() == want
+
+
+# ------------------------------------------------------------------------ decode
+def _softmax_attention(K, V, q, G, ctx):
+    """Dense attention through scipy.special.softmax, float64."""
+    B, H = q.shape[:2]
+    out = np.zeros((B, H, D))
+    row = 0
+    for b, N in enumerate(ctx):
+        for h in range(H):
+            g = h * G // H
+            Kf = oracle.bf16_to_f32(K[row + g * N: row + (g + 1) * N]).astype(np.float64)
+            Vf = oracle.bf16_to_f32(V[row + g * N: row + (g + 1) * N]).astype(np.float64)
+            qf = oracle.bf16_to_f32(q[b, h]).astype(np.float64)
+            w = scipy.special.softmax(Kf @ qf / math.sqrt(D))
+            out[b, h] = w @ Vf
+        row += G * N
+    return out
+
+
+def _setup_decode(seed=21, ctx=(3000, 1700), G=2, H=4, seg=1024, K_s=64, iters=3):
+    K, V, ctx, idx = _small_build(seed, ctx, G, seg, K_s, iters)
+    q, _ = synth.queries(seed + 1, 1, len(ctx), H, G, ctx, K)
+    return K, V, ctx, idx, q[0]
+
+
+def test_full_attention_matches_scipy_softmax():
+    K, V, ctx, idx, q = _setup_decode()
+    of, _ = oracle.full_attention(K, V, q, idx.G, ctx)
+    np.testing.assert_allclose(of, _softmax_attention(K, V, q, idx.G, ctx), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("n_sink,n_local", [(0, 0), (4, 64), (100, 0), (0, 333)])
+def test_decode_topk_all_equals_full_attention(n_sink, n_local):
+    # topk_frac = 1 retrieves every eligible cluster: the three zones together are
+    # exactly dense attention, whatever the clustering.
+    K, V, ctx, idx, q = _setup_decode()
+    o, lse, ids, kc = oracle.decode(idx, K, V, q, n_sink, n_local, 1.0)
+    of, lf = oracle.full_attention(K, V, q, idx.G, ctx)
+    np.testing.assert_allclose(o, of, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, lf, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("frac,n_sink,n_local", [(0.0, 0, 0), (0.05, 4, 64), (0.3, 0, 17), (0.0, 50, 50)])
+def test_decode_singleton_clusters_equal_full_attention(frac, n_sink, n_local):
+    # clusters_per_seg = seg_len: every token is its own cluster, its centroid is the
+    # key itself, so the estimation zone is exact and any split of the zones gives
+    # dense attention.
+    ctx = np.array([700, 300], np.int64)
+    G, H, seg = 2, 4, 256
+    K, V, _ = synth.kv(31, 2, G, ctx, seg)
+    idx = oracle.build(K, V, G, ctx, seg, seg, 2, 9)
+    q, _ = synth.queries(32, 1, 2, H, G, ctx, K)
+    o, lse, _, _ = oracle.decode(idx, K, V, q[0], n_sink, n_local, frac)
+    of, lf = oracle.full_attention(K, V, q[0], G, ctx)
+    np.testing.assert_allclose(o, of, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(lse, lf, rtol=1e-10, atol=1e-10)
+
+
+def test_decode_zero_query_closed_forms():
+    # q = 0: every score is 0, every rank key +0, so the ids are the k lowest eligible
+    # ids in ascending order, and every token weighs the same: o = mean of all V
+    # (up to the fp32 rounding of the stored value sums, <= 1e-8 here).
+    K, V, ctx, idx, q = _setup_decode()
+    q0 = np.zeros_like(q)
+    for frac, ns, nl in [(0.05, 4, 64), (0.2, 0, 0), (0.0, 10, 10)]:
+        o, lse, ids, kc = oracle.decode(idx, K, V, q0, ns, nl, frac)
+        row = 0
+        for b, N in enumerate(ctx):
+            C = int(idx.C[b])
+            for h in range(q.shape[1]):
+                g = h * idx.G // q.shape[1]
+                sl = slice(row + g * N, row + (g + 1) * N)
+                Vf = oracle.bf16_to_f32(V[sl]).astype(np.float64)
+                np.testing.assert_allclose(o[b, h], Vf.mean(0), rtol=0, atol=1e-8)
+                assert abs(lse[b, h] - math.log(N)) < 1e-12
+                t = np.arange(N)
+                nonsteady = ~((t < ns) | (t >= N - nl))
+                elig = np.unique(idx.assign[sl][nonsteady])
+                k = min(oracle.k_from_frac(frac, C), len(elig))
+                assert kc[b, h] == k
+                assert ids[b, h, :k].tolist() == elig[:k].tolist()
+                assert np.all(ids[b, h, k:] == -1)
+            row += idx.G * N
+
+
+def test_decode_constant_values():
+    K, V, ctx, idx, q = _setup_decode()
+    v = np.random.default_rng(3).standard_normal(D).astype(np.float32)
+    Vc = np.tile(oracle.f32_to_bf16(v), (V.shape[0], 1))
+    idx2 = oracle.build(K, Vc, idx.G, ctx, idx.seg_len, idx.K_s, 3, 1234)
+    o, _, _, _ = oracle.decode(idx2, K, Vc, q, 4, 64, 0.05)
+    want = oracle.bf16_to_f32(oracle.f32_to_bf16(v)).astype(np.float64)
+    np.testing.assert_allclose(o, np.broadcast_to(want, o.shape), rtol=1e-6, atol=1e-6)
+
+
+def test_decode_all_steady():
+    K, V, ctx, idx, q = _setup_decode()
+    o, lse, ids, kc = oracle.decode(idx, K, V, q, 1500, 1500, 0.05)  # covers N_b = 3000 and 1700
+    of, lf = oracle.full_attention(K, V, q, idx.G, ctx)
+    np.testing.assert_allclose(o, of, rtol=1e-12, atol=1e-12)
+    assert np.all(ids == -1) and np.all(kc == 0)
+
+
+def test_decode_estimation_only_closed_form():
+    # topk_frac = 0 and no steady tokens: o = sum_j e^{s_j} Vsum_j / sum_j e^{s_j} n_j
+    K, V, ctx, idx, q = _setup_decode()
+    o, lse, _, _ = oracle.decode(idx, K, V, q, 0, 0, 0.0)
+    clu = 0
+    for b, N in enumerate(ctx):
+        C = int(idx.C[b])
+        for h in range(q.shape[1]):
+            g = h * idx.G // q.shape[1]
+            cs = slice(clu + g * C, clu + (g + 1) * C)
+            n = idx.sizes[cs].astype(np.float64)
+            chat = oracle.bf16_to_f32(idx.centroids_bf16[cs]).astype(np.float64)
+            s = chat @ oracle.bf16_to_f32(q[b, h]).astype(np.float64) / math.sqrt(D)
+            s = np.where(n > 0, s, -np.inf)
+            w = np.exp(s - s.max())
+            want = (w[:, None] * idx.vsum[cs].astype(np.float64)).sum(0) / (w * n).sum()
+            np.testing.assert_allclose(o[b, h], want, rtol=1e-10, atol=1e-10)
+        clu += idx.G * C
+
+
+def test_decode_selection_brute_force():
+    # ids are the brute-force top-k of the rank keys over eligible clusters
+    K, V, ctx, idx, q = _setup_decode()
+    ns, nl, frac = 4, 64, 0.1
+    _, _, ids, kc = oracle.decode(idx, K, V, q, ns, nl, frac)
+    row = clu = 0
+    for b, N in enumerate(ctx):
+        C = int(idx.C[b])
+        for h in range(q.shape[1]):
+            g = h * idx.G // q.shape[1]
+            a = idx.assign[row + g * N: row + (g + 1) * N]
+            t = np.arange(N)
+            elig = np.unique(a[~((t < ns) | (t >= N - nl))])
+            keys = [oracle.rank_key(q[b, h], idx.centroids_bf16[clu + g * C + j]) for j in elig]
+            k = min(oracle.k_from_frac(frac, C), len(elig))
+            want = [j for _, j in sorted(zip(keys, elig.tolist()), key=lambda u: (-u[0], u[1]))][:k]
+            assert ids[b, h, :k].tolist() == want
+        row += idx.G * N
+        clu += idx.G * C
