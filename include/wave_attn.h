@@ -1,0 +1,191 @@
+/*
+ * wave_attn.h -- C ABI of the wave-index sparse decode attention library for
+ * AMD MI355X (gfx950): retrieval-based sparse attention over a clustered,
+ * HBM-resident KV cache.
+ *
+ * Method: RetroInfer, "A Vector Storage Engine for Scalable Long-Context LLM
+ * Inference" (gist.science summary page), section 2.A: the KV cache is
+ * clustered at prefill by segmented clustering; each decode query gets exact
+ * attention over a steady zone (sink and recent tokens) and over the clusters
+ * its index retrieves (retrieval zone), while the remaining clusters contribute
+ * through their centroids (estimation zone). The split into a query-independent
+ * build and a query-dependent decode follows Vortex (gist.science summary page,
+ * section 2.A, two-phase decomposition into a cache pre-processing step and a
+ * query-dependent indexer step).
+ *
+ * Conventions for every entry point:
+ *  - head_dim must be 128; K, V, q and the sorted K/V are bf16 (raw 16-bit
+ *    patterns), row major, 128 elements per row, rows 16-byte aligned;
+ *  - ragged batch layout: sequence b owns rows [G * sum_{b'<b} N_b', ...) as G
+ *    consecutive blocks of N_b rows (kv head major): row of (b, g, t) is
+ *    G * sum_{b'<b} N_b' + g * N_b + t;
+ *  - the caller owns and allocates every buffer (device memory unless noted
+ *    "host"); the library never allocates device memory and keeps no global
+ *    state apart from a thread-local error message;
+ *  - all argument checks run on the host before anything is enqueued; on an
+ *    error status nothing is enqueued and no output is touched; device faults
+ *    surface at the caller's next synchronisation of the stream;
+ *  - work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    default stream) and never synchronises with the host.
+ */
+#ifndef WAVE_ATTN_H
+#define WAVE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* wave_stream_t; /* same type as hipStream_t */
+
+#define WAVE_HEAD_DIM 128
+#define WAVE_MAX_BATCH 256     /* sequences per call */
+#define WAVE_MAX_SEG_LEN 65536 /* tokens per segment */
+#define WAVE_MAX_CLUSTERS_PER_SEG 2048
+#define WAVE_MAX_STEADY 4096   /* steady tokens per sequence unless they cover it all */
+#define WAVE_MAX_GROUP 8       /* q heads per kv head */
+
+typedef enum wave_status {
+  WAVE_OK = 0,
+  WAVE_ERR_ARG = -1,         /* null pointer, NaN or out-of-range scalar */
+  WAVE_ERR_SHAPE = -2,       /* inconsistent sizes (K_s > L_s, H % G != 0, N_b < 1, iters < 1, ...) */
+  WAVE_ERR_UNSUPPORTED = -3, /* head_dim != 128 or a limit above exceeded */
+  WAVE_ERR_WORKSPACE = -4,   /* workspace smaller than the plan asked for */
+  WAVE_ERR_ALIGN = -5,       /* a device pointer is not 16-byte aligned */
+  WAVE_ERR_HIP = -6          /* no device, or a HIP launch failed */
+} wave_status;
+
+/* Shape of a (ragged) batch of KV caches of one layer. */
+typedef struct wave_shape {
+  int32_t batch;        /* B, 1..WAVE_MAX_BATCH */
+  int32_t n_kv_heads;   /* G >= 1 */
+  int32_t head_dim;     /* must be 128 */
+  int32_t reserved;     /* 0 */
+  const int64_t* ctx;   /* host [B]: N_b, 1 <= N_b < 2^31 */
+} wave_shape;
+
+/* Sizes of the index arrays (element counts) and of the build workspace (bytes). */
+typedef struct wave_index_sizes {
+  int64_t rows;          /* sum_b G * N_b: rows of k_sorted, v_sorted; length of perm, inv_perm, assign */
+  int64_t clusters;      /* sum_b G * C_b: rows of centroids, centroids_bf16, vsum; length of sizes */
+  int64_t offsets_len;   /* sum_b G * (C_b + 1): length of offsets */
+  int64_t units;         /* sum_b G * ceil(N_b / seg_len): independent k-means problems */
+  int32_t max_clusters;  /* max_b C_b */
+  int32_t reserved;
+  size_t build_ws_bytes; /* workspace wave_index_build needs */
+} wave_index_sizes;
+
+/*
+ * The index: host metadata plus caller-owned device arrays, all filled by
+ * wave_index_build (or uploaded by the caller in exactly this layout).
+ * Cluster ids are local to one (sequence b, kv head g) block, in [0, C_b),
+ * segment major: segment s owns ids [s*K_s, s*K_s + K(s)).
+ */
+typedef struct wave_index {
+  wave_shape shape;         /* ctx points at caller host memory that must outlive the index */
+  int32_t seg_len;          /* L_s */
+  int32_t clusters_per_seg; /* K_s */
+  void* k_sorted;           /* bf16 [rows][128]: K rows grouped by cluster, ascending position inside a cluster */
+  void* v_sorted;           /* bf16 [rows][128]: V rows in the same order */
+  int32_t* perm;            /* [rows]: original position (within its block) of sorted slot p */
+  int32_t* inv_perm;        /* [rows]: sorted slot of original position t */
+  int32_t* assign;          /* [rows]: cluster id of original position t */
+  int32_t* offsets;         /* [offsets_len]: per block, C_b + 1 exclusive prefix sums of sizes */
+  int32_t* sizes;           /* [clusters]: members per cluster */
+  float* centroids;         /* [clusters][128]: fp32 centroids (member means) */
+  void* centroids_bf16;     /* bf16 [clusters][128]: round-to-nearest-even of centroids */
+  float* vsum;              /* [clusters][128]: ordered fp32 sum of the members' V rows */
+} wave_index;
+
+/*
+ * wave_index_plan -- host only. Sizes of the index arrays and of the build
+ * workspace for `shape`, segment length seg_len (L_s, 1..WAVE_MAX_SEG_LEN) and
+ * clusters_per_seg (K_s, 1..min(L_s, WAVE_MAX_CLUSTERS_PER_SEG)).
+ * Segmentation (RetroInfer page, section 2.A, segmented clustering): segments
+ * [s*L_s, min((s+1)*L_s, N_b)); a full segment has K_s clusters, a shorter
+ * last one of length L has ceil(L*K_s/L_s); C_b is their sum.
+ */
+wave_status wave_index_plan(const wave_shape* shape, int32_t seg_len, int32_t clusters_per_seg,
+                            wave_index_sizes* out);
+
+/*
+ * wave_index_build -- the query-independent phase (RetroInfer page, section
+ * 2.A: segmented clustering at prefill). Per (sequence, kv head, segment):
+ * seeded init (SplitMix64 seeded at seed + 0x9E3779B97F4A7C15*(u+1) for unit u
+ * in (b, g, s) order, partial Fisher-Yates choice of K(s) tokens), then exactly
+ * `iters` Lloyd rounds: assignment to the nearest bf16-rounded centroid by
+ * squared Euclidean distance (exact ties: lowest id), update to the ordered
+ * fp32 mean of the members (empty clusters keep their centroid). Then the
+ * layout of wave_index.
+ *  K, V:   device bf16, rows [sizes.rows][128] in the ragged layout; read only.
+ *  out:    caller-filled device pointers of every wave_index array (sizes
+ *          from wave_index_plan); the call writes shape, seg_len and
+ *          clusters_per_seg and fills the arrays.
+ *  ws:     device workspace of at least build_ws_bytes (16-byte aligned).
+ *  assign_trace: nullable device int32 [iters][rows]: the assignment after
+ *          every round.
+ * Errors: ARG (null pointer), SHAPE / UNSUPPORTED (as in wave_index_plan,
+ * iters < 1), WORKSPACE, ALIGN, HIP.
+ */
+wave_status wave_index_build(const wave_shape* shape, const void* K, const void* V, int32_t seg_len,
+                             int32_t clusters_per_seg, int32_t iters, uint64_t seed, wave_index* out, void* ws,
+                             size_t ws_bytes, int32_t* assign_trace, wave_stream_t stream);
+
+/*
+ * wave_attn_decode_plan -- host only. For q heads n_q_heads (a multiple of G,
+ * at most WAVE_MAX_GROUP per kv head), steady zone (n_sink, n_local) and
+ * topk_frac in [0, 1]: k_max = max_b min(ceil(topk_frac*C_b), C_b) (the id
+ * columns of wave_attn_decode) and the decode workspace size in bytes.
+ * UNSUPPORTED if a sequence's steady zone has more than WAVE_MAX_STEADY
+ * tokens without covering the whole sequence.
+ */
+wave_status wave_attn_decode_plan(const wave_index* index, int32_t n_q_heads, int32_t n_sink, int32_t n_local,
+                                  double topk_frac, int32_t* k_max, size_t* ws_bytes);
+
+/*
+ * wave_attn_decode -- the query-dependent phase (RetroInfer page, section 2.A,
+ * the three zones), for every (sequence b, q head h), kv head g = h*G/H:
+ *   S = {t < n_sink} U {t >= N_b - n_local} (steady zone, exact);
+ *   n'_j, Vsum'_j = cluster j's size and value sum without its steady tokens;
+ *   E = {j : n'_j > 0};  k_b = min(ceil(topk_frac*C_b), |E|);
+ *   R = the k_b clusters of E with the largest rank key (a fixed-order fp32
+ *       inner product of q and the bf16 centroid; ties: lower id);
+ *   retrieval zone: exact attention over the non-steady members of R;
+ *   estimation zone: every j in E \ R adds exp(s_j)*n'_j to the denominator
+ *       and exp(s_j)*Vsum'_j to the numerator, s_j = q . chat_j / sqrt(128);
+ *   out = numerator / denominator, lse = log(denominator) (shifted-max form).
+ *  q:       device bf16 [B][n_q_heads][128].
+ *  out:     device fp32 [B][n_q_heads][128].
+ *  sel_ids: device int32 [B][n_q_heads][k_max] (nullable if k_max == 0): the
+ *           selected cluster ids of R in rank order, then -1.
+ *  lse:     nullable device fp32 [B][n_q_heads].
+ *  ws:      device workspace of at least the planned size; one workspace per
+ *           concurrent call (the index itself is read only and may be shared).
+ * Errors: ARG, SHAPE, UNSUPPORTED, WORKSPACE, ALIGN, HIP.
+ */
+wave_status wave_attn_decode(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
+                             int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse, void* ws,
+                             size_t ws_bytes, wave_stream_t stream);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* wave_last_error(void);
+
+/*
+ * Kernel timing hook (not part of the method): while enabled, every kernel
+ * launch of the calls above is bracketed by a pair of HIP events recorded on
+ * the launch stream. wave_profiler_read synchronises on those events and
+ * returns, per kernel name, the number of launches and their summed duration.
+ *  wave_profiler_enable(1) clears previous records and starts recording;
+ *  wave_profiler_enable(0) stops. names: host buffer of n_max * 64 chars.
+ * Returns the number of distinct kernels written (or a negative status).
+ */
+wave_status wave_profiler_enable(int32_t on);
+int32_t wave_profiler_read(char* names, int64_t* launches, double* total_ms, int32_t n_max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WAVE_ATTN_H */

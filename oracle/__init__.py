@@ -20,7 +20,7 @@ _lib = None
 D = 128
 
 
-def build():
+def compile_lib():
     """Compile liboracle.so (gcc, OpenMP over independent units, no fused or fast math)."""
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra", "-ffp-contract=off",
            "-fno-fast-math", "-o", _LIB_PATH, os.path.join(_HERE, "oracle.c"), "-lm"]
@@ -31,7 +31,7 @@ def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
-            build()
+            compile_lib()
         lib = ctypes.CDLL(_LIB_PATH)
         P, i32, i64, u64, f64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_double
         lib.ref_bf16_to_f32.argtypes = [ctypes.c_uint16]

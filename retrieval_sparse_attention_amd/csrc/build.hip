@@ -1,0 +1,655 @@
+// build.hip -- query-independent phase of wave-index attention on gfx950:
+// segmented k-means over the keys of every (sequence, kv head), then the
+// cluster-sorted layout.
+//
+// RetroInfer summary page, section 2.A (segmented clustering): the sequence is
+// cut into segments that are clustered independently at prefill. One k-means
+// problem ("unit") per (sequence b, kv head g, segment s), enumerated in that
+// order. Launch sequence, all on the caller's stream:
+//   k_init                  seeded choice of K(s) tokens per unit, key norms
+//   iters x { k_round_norm  bf16 rounding of the centroids, their squared norms
+//             k_assign      nearest centroid on bf16 MFMA (32x32x16), fp32
+//             k_assign_fix  binary64 decision where fp32 cannot separate the two best
+//             k_sort        stable counting sort of each unit by cluster
+//             k_update      ordered fp32 member sums, correctly rounded means }
+//   k_layout                sorted K/V, inv_perm, ordered fp32 value sums, bf16 centroids
+#include <math.h>
+
+#include "common.h"
+#include "internal.h"
+
+namespace wave {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr uint64_t GAMMA = 0x9E3779B97F4A7C15ULL;
+
+// ------------------------------------------------------------------ unit lookup
+struct Unit {
+  int b, g, s;
+  int64_t row0;   // first row of the segment
+  int64_t brow;   // first row of the (b, g) block
+  int64_t gclu;   // global index of the segment's first cluster
+  int32_t L, Kc;  // segment length and clusters
+  int32_t cbase;  // block-level id of the first cluster (s * K_s)
+  int32_t tok0;   // segment start within the block (s * L_s)
+  int64_t boff;   // first offsets entry of the block
+  int32_t N, C;
+  int64_t u;      // unit index
+};
+
+__device__ inline Unit unit_of(const SeqArgs& sa, int64_t u) {
+  Unit r;
+  r.u = u;
+  int b = 0;
+  int64_t row = 0, clu = 0, off = 0;
+  for (;; ++b) {
+    const int64_t nseg = (sa.N[b] + sa.seg_len - 1) / sa.seg_len;
+    if (u < sa.G * nseg) break;
+    u -= sa.G * nseg;
+    row += (int64_t)sa.G * sa.N[b];
+    clu += (int64_t)sa.G * sa.C[b];
+    off += (int64_t)sa.G * (sa.C[b] + 1);
+  }
+  const int64_t nseg = (sa.N[b] + sa.seg_len - 1) / sa.seg_len;
+  r.b = b;
+  r.g = (int)(u / nseg);
+  r.s = (int)(u % nseg);
+  r.N = sa.N[b];
+  r.C = sa.C[b];
+  r.brow = row + (int64_t)r.g * r.N;
+  r.tok0 = r.s * sa.seg_len;
+  r.row0 = r.brow + r.tok0;
+  r.L = (int32_t)min((int64_t)sa.seg_len, (int64_t)r.N - r.tok0);
+  r.Kc = seg_clusters(r.L, sa.seg_len, sa.K_s);
+  r.cbase = r.s * sa.K_s;
+  r.gclu = clu + (int64_t)r.g * r.C + r.cbase;
+  r.boff = off + (int64_t)r.g * (r.C + 1);
+  return r;
+}
+
+// global cluster index -> (block row base, block cluster base, offsets base, local id)
+struct CluRef {
+  int64_t brow, bclu, boff;
+  int32_t j, N, C;
+};
+
+__device__ inline CluRef clu_of(const SeqArgs& sa, int64_t F) {
+  int b = 0;
+  int64_t row = 0, clu = 0, off = 0;
+  for (;; ++b) {
+    if (F < clu + (int64_t)sa.G * sa.C[b]) break;
+    row += (int64_t)sa.G * sa.N[b];
+    clu += (int64_t)sa.G * sa.C[b];
+    off += (int64_t)sa.G * (sa.C[b] + 1);
+  }
+  CluRef r;
+  const int64_t rel = F - clu;
+  const int g = (int)(rel / sa.C[b]);
+  r.j = (int32_t)(rel % sa.C[b]);
+  r.N = sa.N[b];
+  r.C = sa.C[b];
+  r.brow = row + (int64_t)g * r.N;
+  r.bclu = clu + (int64_t)g * r.C;
+  r.boff = off + (int64_t)g * (r.C + 1);
+  return r;
+}
+
+__device__ __forceinline__ uint64_t sm64_mix(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+
+// ------------------------------------------------------------------ k_init
+// One workgroup per unit. The i-th SplitMix64 draw of unit u is
+// mix(seed + GAMMA*(u+1) + GAMMA*(i+1)); the draws do not depend on the
+// shuffle, so they are taken in parallel and one lane then performs the K(s)
+// swaps of the partial Fisher-Yates shuffle of [0, L) held in LDS (16-bit
+// entries). Centroid i becomes the fp32 copy of key row idx[i]. The same
+// workgroup writes |x| of every key of the segment (used for the fp32 error
+// margin of the assignment).
+__global__ __launch_bounds__(256) void k_init(SeqArgs sa, uint64_t seed, const uint16_t* __restrict__ K,
+                                              float* __restrict__ cent, float* __restrict__ xnorm) {
+  extern __shared__ uint8_t smem[];
+  const Unit U = unit_of(sa, blockIdx.x);
+  uint16_t* idx = reinterpret_cast<uint16_t*>(smem);
+  int32_t* jsel = reinterpret_cast<int32_t*>(smem + ((2 * (size_t)U.L + 15) & ~(size_t)15));
+  const uint64_t st0 = seed + GAMMA * (uint64_t)(U.u + 1);
+  for (int i = threadIdx.x; i < U.L; i += blockDim.x) idx[i] = (uint16_t)i;
+  for (int i = threadIdx.x; i < U.Kc; i += blockDim.x) {
+    const uint64_t r = sm64_mix(st0 + GAMMA * (uint64_t)(i + 1));
+    jsel[i] = i + (int32_t)(r % (uint64_t)(U.L - i));
+  }
+  // key norms of the segment (one row per 16 lanes)
+  {
+    const int lane = threadIdx.x & 63, l16 = lane & 15, grp = threadIdx.x >> 4;
+    for (int t = grp; t < U.L; t += blockDim.x / 16) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(K + (U.row0 + t) * D + l16 * 8);
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = bf16_lo(v[e]), c = bf16_hi(v[e]);
+        s = fmaf(a, a, s);
+        s = fmaf(c, c, s);
+      }
+      s += xor_shfl(s, 8);
+      s += xor_shfl(s, 4);
+      s += xor_shfl(s, 2);
+      s += xor_shfl(s, 1);
+      if (l16 == 0) xnorm[U.row0 + t] = sqrtf(s);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = 0; i < U.Kc; ++i) {
+      const int j = jsel[i];
+      const uint16_t a = idx[i];
+      idx[i] = idx[j];
+      idx[j] = a;
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < U.Kc * D; e += blockDim.x) {
+    const int i = e / D, d = e % D;
+    cent[(U.gclu + i) * D + d] = bf16_to_f(K[(U.row0 + idx[i]) * D + d]);
+  }
+}
+
+// ------------------------------------------------------------------ k_round_norm
+// chat = bf16(c) for every cluster; norm = |chat|^2 in fp32; resets the
+// near-tie list. One wave per cluster, 2 dims per lane.
+__global__ __launch_bounds__(256) void k_round_norm(int64_t nclu, const float* __restrict__ cent,
+                                                    uint16_t* __restrict__ chat, float* __restrict__ norm,
+                                                    int32_t* __restrict__ amb) {
+  const int64_t F = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (blockIdx.x == 0 && threadIdx.x == 0) amb[0] = 0;
+  if (F >= nclu) return;
+  const float2 c = *reinterpret_cast<const float2*>(cent + F * D + 2 * lane);
+  const uint16_t h0 = f_to_bf16(c.x), h1 = f_to_bf16(c.y);
+  *reinterpret_cast<uint32_t*>(chat + F * D + 2 * lane) = (uint32_t)h0 | ((uint32_t)h1 << 16);
+  const float a = bf16_to_f(h0), b = bf16_to_f(h1);
+  float s = fmaf(a, a, b * b);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += xor_shfl(s, o);
+  if (lane == 0) norm[F] = s;
+}
+
+// ------------------------------------------------------------------ k_assign (bf16 MFMA)
+// For a key x and bf16 centroids c_j the nearest centroid maximises
+// f_j = x.c_j - |c_j|^2 / 2. D[centroid][token] = C . X^T is computed with
+// v_mfma_f32_32x32x16_bf16: every wave keeps 64 centroid rows (two 32-row A
+// tiles, all 128 dims) in registers; token tiles (B operand) stream through
+// LDS; the accumulator starts at -|c_j|^2/2. A lane of the 32x32 result holds
+// one token (column) and 16 centroid rows, so the running best, its id and the
+// second best are kept per lane and merged across the two half-waves and the
+// 8 waves. When the fp32 gap between best and second best is within twice
+// the bound on the fp32 error of f, the token is sent to the exact binary64
+// decision (k_assign_fix).
+constexpr int AS_WAVES = 8;
+constexpr int AS_THREADS = AS_WAVES * 64;
+constexpr int AS_TT = 128;     // tokens per LDS tile
+constexpr int AS_TPW = 1024;   // tokens per workgroup
+constexpr int AS_GROUP = AS_WAVES * 64;  // centroids per pass
+
+struct AssignLds {
+  u32x4 tile[AS_TT * 16];           // token rows, 16-byte chunk c of row t stored at chunk c ^ (t & 15)
+  float red[AS_WAVES][AS_TT][3];    // per wave: best, id (bits), second best
+  unsigned int rmax;                // max |c_j|^2 of the unit (float bits)
+};
+
+struct Best {
+  float b1, b2;
+  int i1;
+};
+
+__device__ __forceinline__ void best_merge(Best& a, const Best& o) {
+  // a keeps the larger best (lower id on equal values); second = largest of the rest
+  const bool take = (o.b1 > a.b1) || (o.b1 == a.b1 && o.i1 < a.i1);
+  const float lo = fminf(a.b1, o.b1);
+  const float s = fmaxf(lo, fmaxf(a.b2, o.b2));
+  if (take) { a.b1 = o.b1; a.i1 = o.i1; }
+  a.b2 = s;
+}
+
+__device__ inline void assign_wg_map(const SeqArgs& sa, int w, Unit& U, int& tok_begin) {
+  // workgroups per unit: ceil(L / AS_TPW), units in (b, g, s) order
+  int64_t u = 0;
+  int b = 0;
+  for (;; ++b) {
+    const int64_t N = sa.N[b];
+    const int64_t nseg = (N + sa.seg_len - 1) / sa.seg_len;
+    const int64_t last = N - (nseg - 1) * sa.seg_len;
+    const int wf = (sa.seg_len + AS_TPW - 1) / AS_TPW, wl = (int)((last + AS_TPW - 1) / AS_TPW);
+    const int64_t per_g = (nseg - 1) * wf + wl;
+    if (w < sa.G * per_g) {
+      const int g = (int)(w / per_g);
+      const int64_t r = w % per_g;
+      int64_t s = r / wf;
+      int64_t k = r % wf;
+      if (s >= nseg - 1) { s = nseg - 1; k = r - (nseg - 1) * wf; }
+      U = unit_of(sa, u + (int64_t)g * nseg + s);
+      tok_begin = (int)(k * AS_TPW);
+      return;
+    }
+    w -= (int)(sa.G * per_g);
+    u += sa.G * nseg;
+  }
+}
+
+__global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint16_t* __restrict__ K,
+                                                          const uint16_t* __restrict__ chat,
+                                                          const float* __restrict__ norm,
+                                                          const float* __restrict__ xnorm,
+                                                          int32_t* __restrict__ assign, int32_t* __restrict__ amb) {
+  extern __shared__ uint8_t smem[];
+  AssignLds& S = *reinterpret_cast<AssignLds*>(smem);
+  Unit U;
+  int tb0;
+  assign_wg_map(sa, blockIdx.x, U, tb0);
+  const int tend = min(tb0 + AS_TPW, U.L);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, h = lane >> 5, col = lane & 31;
+  // largest squared centroid norm of the unit (all norms are >= 0)
+  if (tid == 0) S.rmax = 0u;
+  __syncthreads();
+  {
+    unsigned int m = 0u;
+    for (int j = tid; j < U.Kc; j += AS_THREADS) m = max(m, __float_as_uint(norm[U.gclu + j]));
+    atomicMax(&S.rmax, m);
+  }
+  const int ngroups = (U.Kc + AS_GROUP - 1) / AS_GROUP;
+  bf16x8_t A[2][8];
+  floatx16 nh[2];
+  auto load_group = [&](int grp) {
+    const int cb = grp * AS_GROUP + wv * 64;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int row = cb + r * 32 + col;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (row < U.Kc) v = *reinterpret_cast<const u32x4*>(chat + (U.gclu + row) * D + (2 * st + h) * 8);
+        A[r][st] = __builtin_bit_cast(bf16x8_t, v);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rr = cb + r * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+        nh[r][i] = rr < U.Kc ? -0.5f * norm[U.gclu + rr] : -INFINITY;
+      }
+    }
+  };
+  if (ngroups == 1) load_group(0);
+  for (int t0 = tb0; t0 < tend; t0 += AS_TT) {
+    // token tile -> LDS (zero rows past the end)
+    for (int e = tid; e < AS_TT * 16; e += AS_THREADS) {
+      const int t = e >> 4, c = e & 15;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (t0 + t < tend) v = *reinterpret_cast<const u32x4*>(K + (U.row0 + t0 + t) * D + c * 8);
+      S.tile[t * 16 + (c ^ (t & 15))] = v;
+    }
+    __syncthreads();
+    Best run[AS_TT / 32];
+#pragma unroll
+    for (int tb = 0; tb < AS_TT / 32; ++tb) { run[tb].b1 = -INFINITY; run[tb].b2 = -INFINITY; run[tb].i1 = 0x7FFFFFFF; }
+    for (int grp = 0; grp < ngroups; ++grp) {
+      if (ngroups > 1) load_group(grp);
+      const int cb = grp * AS_GROUP + wv * 64;
+#pragma unroll 1
+      for (int tb = 0; tb < AS_TT / 32; ++tb) {
+        floatx16 acc[2];
+        const int t = tb * 32 + col;
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+          const int c = 2 * st + h;
+          const bf16x8_t Bv = __builtin_bit_cast(bf16x8_t, S.tile[t * 16 + (c ^ (t & 15))]);
+#pragma unroll
+          for (int r = 0; r < 2; ++r)
+            acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[r][st], Bv, st == 0 ? nh[r] : acc[r], 0, 0, 0);
+        }
+        Best bs;
+        bs.b1 = -INFINITY;
+        bs.b2 = -INFINITY;
+        bs.i1 = 0x7FFFFFFF;
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float v = acc[r][i];
+            const int j = cb + r * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+            const bool gt = v > bs.b1;
+            bs.b2 = __builtin_amdgcn_fmed3f(v, bs.b1, bs.b2);
+            bs.i1 = gt ? j : bs.i1;
+            bs.b1 = fmaxf(bs.b1, v);
+          }
+        Best o;
+        o.b1 = xor_shfl(bs.b1, 32);
+        o.b2 = xor_shfl(bs.b2, 32);
+        o.i1 = xor_shfl(bs.i1, 32);
+        best_merge(bs, o);
+        best_merge(run[tb], bs);
+      }
+    }
+    if (h == 0) {
+#pragma unroll
+      for (int tb = 0; tb < AS_TT / 32; ++tb) {
+        S.red[wv][tb * 32 + col][0] = run[tb].b1;
+        S.red[wv][tb * 32 + col][1] = __int_as_float(run[tb].i1);
+        S.red[wv][tb * 32 + col][2] = run[tb].b2;
+      }
+    }
+    __syncthreads();
+    if (tid < AS_TT && t0 + tid < tend) {
+      Best bst;
+      bst.b1 = S.red[0][tid][0];
+      bst.i1 = __float_as_int(S.red[0][tid][1]);
+      bst.b2 = S.red[0][tid][2];
+      for (int w2 = 1; w2 < AS_WAVES; ++w2) {
+        Best o;
+        o.b1 = S.red[w2][tid][0];
+        o.i1 = __float_as_int(S.red[w2][tid][1]);
+        o.b2 = S.red[w2][tid][2];
+        best_merge(bst, o);
+      }
+      const int64_t row = U.row0 + t0 + tid;
+      // |f~ - f| <= 2^-15 (|x| R + R^2) with R = max |c_j| (many times the
+      // worst-case fp32 accumulation bound); a gap within twice that may hide
+      // an exact order different from the fp32 one.
+      const float R2 = __uint_as_float(S.rmax);
+      const float margin = 0x1p-14f * (xnorm[row] * sqrtf(R2) + R2);
+      assign[row] = U.cbase + bst.i1;
+      if (bst.b1 - bst.b2 <= margin) {
+        const int pos = atomicAdd(amb, 1);
+        amb[1 + 2 * pos] = (int32_t)U.u;
+        amb[2 + 2 * pos] = t0 + tid;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ k_assign_fix
+// Exact decision for the listed tokens: D_j = sum_i (x_i - c_j,i)^2 in binary64,
+// dims in order, each operation rounded (no fused multiply-add), argmin with
+// the lowest id on ties. One wave per token; lanes take centroids j = lane,
+// lane + 64, ...
+__global__ __launch_bounds__(256) void k_assign_fix(SeqArgs sa, const uint16_t* __restrict__ K,
+                                                    const uint16_t* __restrict__ chat,
+                                                    int32_t* __restrict__ assign, const int32_t* __restrict__ amb) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int count = amb[0];
+  for (int item = blockIdx.x * 4 + wv; item < count; item += gridDim.x * 4) {
+    const Unit U = unit_of(sa, amb[1 + 2 * item]);
+    const int t = amb[2 + 2 * item];
+    const int64_t row = U.row0 + t;
+    u32x4 xr[16];  // the whole key row in every lane
+#pragma unroll
+    for (int e = 0; e < 16; ++e) xr[e] = *reinterpret_cast<const u32x4*>(K + row * D + e * 8);
+    double best = INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int j = lane; j < U.Kc; j += 64) {
+      const u32x4* c = reinterpret_cast<const u32x4*>(chat + (U.gclu + j) * D);
+      double acc = 0.0;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const u32x4 cv = c[e];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const double d0 = __dsub_rn((double)bf16_lo(xr[e][w]), (double)bf16_lo(cv[w]));
+          acc = __dadd_rn(acc, __dmul_rn(d0, d0));
+          const double d1 = __dsub_rn((double)bf16_hi(xr[e][w]), (double)bf16_hi(cv[w]));
+          acc = __dadd_rn(acc, __dmul_rn(d1, d1));
+        }
+      }
+      if (acc < best) { best = acc; bi = j; }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const double ob = __shfl_xor(best, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ob < best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+    }
+    if (lane == 0) assign[row] = U.cbase + bi;
+  }
+}
+
+// ------------------------------------------------------------------ k_sort
+// Stable counting sort of one unit by cluster: sorted slot of token t is
+// offset(c) + #{t' < t in the unit : a(t') = c}. The 16 waves take consecutive
+// token ranges; inside a wave, 64 tokens at a time, equal ids are ranked by a
+// ballot loop (one iteration per distinct id); per-wave counts then become
+// per-wave bases. Writes sizes, offsets (block level) and perm.
+constexpr int SORT_THREADS = 1024;
+
+__global__ __launch_bounds__(SORT_THREADS) void k_sort(SeqArgs sa, const int32_t* __restrict__ assign,
+                                                       int32_t* __restrict__ rank, int32_t* __restrict__ sizes,
+                                                       int32_t* __restrict__ offsets, int32_t* __restrict__ perm) {
+  extern __shared__ uint8_t smem[];
+  const Unit U = unit_of(sa, blockIdx.x);
+  const int Kc = U.Kc;
+  int32_t* hist = reinterpret_cast<int32_t*>(smem);  // [16][Kc]
+  __shared__ uint64_t scan[17];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int e = tid; e < 16 * Kc; e += SORT_THREADS) hist[e] = 0;
+  __syncthreads();
+  const int span = (U.L + 15) / 16;
+  const int w0 = min(wv * span, U.L), w1 = min(w0 + span, U.L);
+  const uint64_t ltmask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int t0 = w0; t0 < w1; t0 += 64) {
+    const int t = t0 + lane;
+    const bool valid = t < w1;
+    // ids are in [0, Kc) by construction; the clamp keeps every sorted slot inside
+    // the segment even if they were not
+    const int c = valid ? min(max(assign[U.row0 + t] - U.cbase, 0), Kc - 1) : -1;
+    uint64_t active = __ballot(valid);
+    int myrank = 0;
+    while (active) {
+      const int leader = __ffsll((unsigned long long)active) - 1;
+      const int v = __shfl(c, leader, 64);
+      const uint64_t same = __ballot(valid && c == v);
+      const int basecnt = hist[wv * Kc + v];
+      if (valid && c == v) myrank = basecnt + __popcll(same & ltmask);
+      if (lane == leader) hist[wv * Kc + v] = basecnt + __popcll(same);
+      active &= ~same;
+    }
+    if (valid) rank[U.row0 + t] = myrank;
+  }
+  __syncthreads();
+  // per-cluster totals, per-wave bases, exclusive offsets over clusters
+  const int per = (Kc + SORT_THREADS - 1) / SORT_THREADS;
+  const int c0 = min(tid * per, Kc), c1 = min(c0 + per, Kc);
+  int64_t mysum = 0;
+  for (int c = c0; c < c1; ++c) {
+    int run = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int x = hist[w * Kc + c];
+      hist[w * Kc + c] = run;
+      run += x;
+    }
+    sizes[U.gclu + c] = run;
+    mysum += run;
+  }
+  // exclusive scan of mysum over threads
+  {
+    uint64_t x = (uint64_t)mysum;
+#pragma unroll
+    for (int s = 1; s < 64; s <<= 1) {
+      const uint64_t y = __shfl_up(x, s, 64);
+      if (lane >= s) x += y;
+    }
+    if (lane == 63) scan[wv] = x;
+    __syncthreads();
+    if (wv == 0) {
+      const uint64_t v0 = lane < 16 ? scan[lane] : 0;
+      uint64_t tt = v0;
+#pragma unroll
+      for (int s = 1; s < 16; s <<= 1) {
+        const uint64_t y = __shfl_up(tt, s, 64);
+        if (lane >= s) tt += y;
+      }
+      if (lane < 16) scan[lane] = tt - v0;
+    }
+    __syncthreads();
+    int64_t run = (int64_t)(scan[wv] + x - (uint64_t)mysum);
+    for (int c = c0; c < c1; ++c) {
+      const int sz = sizes[U.gclu + c];
+      offsets[U.boff + U.cbase + c] = U.tok0 + (int32_t)run;
+      for (int w = 0; w < 16; ++w) hist[w * Kc + c] += (int32_t)run;
+      run += sz;
+    }
+  }
+  if (tid == 0 && U.tok0 + U.L == U.N) offsets[U.boff + U.C] = U.N;
+  __syncthreads();
+  for (int t = tid; t < U.L; t += SORT_THREADS) {
+    const int c = min(max(assign[U.row0 + t] - U.cbase, 0), Kc - 1);
+    const int w = t / span;
+    const int p = U.tok0 + hist[w * Kc + c] + rank[U.row0 + t];
+    perm[U.brow + p] = U.tok0 + t;
+  }
+}
+
+// ------------------------------------------------------------------ k_update
+// Ordered fp32 sums of the members' keys (ascending position), correctly
+// rounded division by the count; empty clusters keep their centroid. One
+// wave per cluster, 2 dims per lane.
+__global__ __launch_bounds__(256) void k_update(SeqArgs sa, int64_t nclu, const uint16_t* __restrict__ K,
+                                                const int32_t* __restrict__ sizes,
+                                                const int32_t* __restrict__ offsets,
+                                                const int32_t* __restrict__ perm, float* __restrict__ cent) {
+  const int64_t F = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (F >= nclu) return;
+  const int n = sizes[F];
+  if (n == 0) return;
+  const CluRef cr = clu_of(sa, F);
+  const int off = offsets[cr.boff + cr.j];
+  const uint16_t* Kb = K + cr.brow * D + 2 * lane;
+  const int32_t* pb = perm + cr.brow + off;
+  float s0 = 0.f, s1 = 0.f;
+  int k = 0;
+  for (; k + 4 <= n; k += 4) {
+    uint32_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const uint32_t*>(Kb + (int64_t)pb[k + u] * D);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      s0 = __fadd_rn(s0, bf16_lo(v[u]));
+      s1 = __fadd_rn(s1, bf16_hi(v[u]));
+    }
+  }
+  for (; k < n; ++k) {
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(Kb + (int64_t)pb[k] * D);
+    s0 = __fadd_rn(s0, bf16_lo(v));
+    s1 = __fadd_rn(s1, bf16_hi(v));
+  }
+  const float fn = (float)n;
+  float2 c;
+  c.x = __fdiv_rn(s0, fn);
+  c.y = __fdiv_rn(s1, fn);
+  *reinterpret_cast<float2*>(cent + F * D + 2 * lane) = c;
+}
+
+// ------------------------------------------------------------------ k_layout
+// Final layout of every cluster: K/V rows copied to their sorted slots,
+// inv_perm, ordered fp32 value sums, bf16 centroids. One wave per cluster.
+__global__ __launch_bounds__(256) void k_layout(SeqArgs sa, int64_t nclu, const uint16_t* __restrict__ K,
+                                                const uint16_t* __restrict__ V, wave_index ix) {
+  const int64_t F = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (F >= nclu) return;
+  const CluRef cr = clu_of(sa, F);
+  const int n = ix.sizes[F];
+  const int off = ix.offsets[cr.boff + cr.j];
+  {
+    const float2 c = *reinterpret_cast<const float2*>(ix.centroids + F * D + 2 * lane);
+    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(ix.centroids_bf16) + F * D + 2 * lane) =
+        (uint32_t)f_to_bf16(c.x) | ((uint32_t)f_to_bf16(c.y) << 16);
+  }
+  uint16_t* Ks = reinterpret_cast<uint16_t*>(ix.k_sorted) + cr.brow * D + 2 * lane;
+  uint16_t* Vs = reinterpret_cast<uint16_t*>(ix.v_sorted) + cr.brow * D + 2 * lane;
+  const uint16_t* Kb = K + cr.brow * D + 2 * lane;
+  const uint16_t* Vb = V + cr.brow * D + 2 * lane;
+  float s0 = 0.f, s1 = 0.f;
+  for (int k = 0; k < n; ++k) {
+    const int p = off + k;
+    const int t = ix.perm[cr.brow + p];
+    const uint32_t kv = *reinterpret_cast<const uint32_t*>(Kb + (int64_t)t * D);
+    const uint32_t vv = *reinterpret_cast<const uint32_t*>(Vb + (int64_t)t * D);
+    *reinterpret_cast<uint32_t*>(Ks + (int64_t)p * D) = kv;
+    *reinterpret_cast<uint32_t*>(Vs + (int64_t)p * D) = vv;
+    s0 = __fadd_rn(s0, bf16_lo(vv));
+    s1 = __fadd_rn(s1, bf16_hi(vv));
+    if (lane == 0) ix.inv_perm[cr.brow + t] = p;
+  }
+  *reinterpret_cast<float2*>(ix.vsum + F * D + 2 * lane) = make_float2(s0, s1);
+}
+
+// ------------------------------------------------------------------ host side
+static int64_t assign_grid(const SeqArgs& sa) {
+  int64_t n = 0;
+  for (int b = 0; b < sa.B; ++b) {
+    const int64_t N = sa.N[b];
+    const int64_t nseg = (N + sa.seg_len - 1) / sa.seg_len;
+    const int64_t last = N - (nseg - 1) * sa.seg_len;
+    const int64_t wf = (sa.seg_len + AS_TPW - 1) / AS_TPW, wl = (last + AS_TPW - 1) / AS_TPW;
+    n += (int64_t)sa.G * ((nseg - 1) * wf + wl);
+  }
+  return n;
+}
+
+hipError_t launch_build(const SeqArgs& sa, const void* Kv, const void* Vv, int32_t iters, uint64_t seed,
+                        const wave_index& ix, const BuildWs& ws, int64_t units, int32_t* trace, int64_t rows,
+                        hipStream_t st) {
+  static bool attrs = false;
+  if (!attrs) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_init), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_assign), hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(AssignLds));
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sort), hipFuncAttributeMaxDynamicSharedMemorySize, 16 * WAVE_MAX_CLUSTERS_PER_SEG * 4);
+    attrs = true;
+  }
+  const uint16_t* K = reinterpret_cast<const uint16_t*>(Kv);
+  const uint16_t* V = reinterpret_cast<const uint16_t*>(Vv);
+  int64_t nclu = 0;
+  for (int b = 0; b < sa.B; ++b) nclu += (int64_t)sa.G * sa.C[b];
+  const size_t init_lds = ((2 * (size_t)sa.seg_len + 15) & ~(size_t)15) + 4 * (size_t)sa.K_s;
+  const size_t sort_lds = 16 * (size_t)sa.K_s * 4;
+  const unsigned cgrid = (unsigned)((nclu + 3) / 4);
+  uint16_t* chat = reinterpret_cast<uint16_t*>(ix.centroids_bf16);
+  prof_begin("k_init", st);
+  hipLaunchKernelGGL(k_init, dim3((unsigned)units), dim3(256), init_lds, st, sa, seed, K, ix.centroids, ws.xnorm);
+  prof_end(st);
+  const int64_t agrid = assign_grid(sa);
+  for (int it = 0; it < iters; ++it) {
+    prof_begin("k_round_norm", st);
+    hipLaunchKernelGGL(k_round_norm, dim3(cgrid), dim3(256), 0, st, nclu, ix.centroids, chat, ws.norm, ws.amb);
+    prof_end(st);
+    prof_begin("k_assign", st);
+    hipLaunchKernelGGL(k_assign, dim3((unsigned)agrid), dim3(AS_THREADS), sizeof(AssignLds), st, sa, K, chat,
+                       ws.norm, ws.xnorm, ix.assign, ws.amb);
+    prof_end(st);
+    prof_begin("k_assign_fix", st);
+    hipLaunchKernelGGL(k_assign_fix, dim3(1024), dim3(256), 0, st, sa, K, chat, ix.assign, ws.amb);
+    prof_end(st);
+    if (trace != nullptr) {
+      hipError_t e = hipMemcpyAsync(trace + (int64_t)it * rows, ix.assign, sizeof(int32_t) * (size_t)rows,
+                                    hipMemcpyDeviceToDevice, st);
+      if (e != hipSuccess) return e;
+    }
+    prof_begin("k_sort", st);
+    hipLaunchKernelGGL(k_sort, dim3((unsigned)units), dim3(SORT_THREADS), sort_lds, st, sa, ix.assign, ws.rank,
+                       ix.sizes, ix.offsets, ix.perm);
+    prof_end(st);
+    prof_begin("k_update", st);
+    hipLaunchKernelGGL(k_update, dim3(cgrid), dim3(256), 0, st, sa, nclu, K, ix.sizes, ix.offsets, ix.perm,
+                       ix.centroids);
+    prof_end(st);
+  }
+  prof_begin("k_layout", st);
+  hipLaunchKernelGGL(k_layout, dim3(cgrid), dim3(256), 0, st, sa, nclu, K, V, ix);
+  prof_end(st);
+  return hipGetLastError();
+}
+
+}  // namespace wave

@@ -1,0 +1,62 @@
+// internal.h -- declarations shared by the library's translation units (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace wave {
+
+// ------------------------------------------------------------------ decode
+struct DecodeArgs {
+  int32_t H, GS;          // q heads, q heads per kv head
+  int32_t n_sink, n_local;
+  int32_t k_max;          // id columns of the output
+  int32_t P;              // retrieval workgroups per (b, h)
+  int32_t NP;             // partial slots per (b, h): P + max_b ceil(C_b / EST_CH)
+  int32_t scap;           // steady entries per (b, h)
+  float tau;              // 1/sqrt(128)
+  int32_t sort_stride;    // per-(b, h) entries of the global sort buffer
+  int32_t kreq[MAXB];     // min(ceil(topk_frac * C_b), C_b), binary64 on the host
+};
+
+struct DecodeWs {
+  float* keys;       // [sum_b H*C_b] rank keys
+  uint32_t* key32;   // [sum_b H*C_b] sortable keys, 0 = not eligible
+  int32_t* selid;    // [sum_b H*C_b] selected ids in id order
+  int32_t* selpre;   // [sum_b H*(C_b+1)] member-count prefix of the selection
+  uint32_t* excl;    // [sum_b H*ceil(C_b/32)] clusters excluded from estimation
+  int32_t* rows;     // [sum_b H*N_b] sorted slots to gather (selected, then steady)
+  float* corr;       // [B*H*scap] rank key of a steady row's cluster if it is estimated, else NaN
+  int32_t* counts;   // [B*H*2] rows from clusters, rows in total
+  float* part;       // [B*H*NP*132] partial softmax states
+  uint64_t* sortg;   // [B*H*pow2(C_max)] global sort buffer (only when k_max > 8192)
+};
+
+constexpr int DEC_EST_CH = 256;
+constexpr int DEC_PART = 132;
+constexpr int DEC_SORT_LDS = 8192;
+
+size_t topk_lds_bytes();
+hipError_t launch_decode(const SeqArgs& sa, const DecodeArgs& da, const wave_index& ix, const DecodeWs& ws,
+                         const uint16_t* q, float* out, int32_t* sel_ids, float* lse, hipStream_t st);
+
+// ------------------------------------------------------------------ build
+struct BuildWs {
+  float* norm;        // [clusters] |chat_j|^2 (fp32) of the current round
+  float* xnorm;       // [rows] |x| of every key (fp32)
+  int32_t* amb;       // [1 + rows] count, then rows whose nearest centroid needs the exact decision
+  int32_t* rank;      // [rows] scratch of the counting sort
+};
+
+hipError_t launch_build(const SeqArgs& sa, const void* K, const void* V, int32_t iters, uint64_t seed,
+                        const wave_index& ix, const BuildWs& ws, int64_t units, int32_t* trace, int64_t rows,
+                        hipStream_t st);
+
+// ------------------------------------------------------------------ kernel timing hook
+void prof_begin(const char* name, hipStream_t st);
+void prof_end(hipStream_t st);
+
+}  // namespace wave

@@ -1,0 +1,377 @@
+// wave_attn.hip -- the C ABI of include/wave_attn.h: argument checks, sizes,
+// workspace carving and kernel sequencing on the caller's stream.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+wave_status fail(wave_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+wave_status ok() {
+  g_err[0] = '\0';
+  return WAVE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ------------------------------------------------------------------ shape checks
+wave_status check_shape(const wave_shape* s) {
+  if (s == nullptr) return fail(WAVE_ERR_ARG, "shape is NULL");
+  if (s->head_dim != WAVE_HEAD_DIM) return fail(WAVE_ERR_UNSUPPORTED, "head_dim %d != 128", s->head_dim);
+  if (s->batch < 1) return fail(WAVE_ERR_SHAPE, "batch %d < 1", s->batch);
+  if (s->batch > WAVE_MAX_BATCH) return fail(WAVE_ERR_UNSUPPORTED, "batch %d > %d", s->batch, WAVE_MAX_BATCH);
+  if (s->n_kv_heads < 1) return fail(WAVE_ERR_SHAPE, "n_kv_heads %d < 1", s->n_kv_heads);
+  if (s->ctx == nullptr) return fail(WAVE_ERR_ARG, "shape.ctx is NULL");
+  for (int b = 0; b < s->batch; ++b) {
+    if (s->ctx[b] < 1) return fail(WAVE_ERR_SHAPE, "ctx[%d] = %lld < 1", b, (long long)s->ctx[b]);
+    if (s->ctx[b] >= ((int64_t)1 << 31)) return fail(WAVE_ERR_UNSUPPORTED, "ctx[%d] >= 2^31", b);
+  }
+  return WAVE_OK;
+}
+
+wave_status check_seg(int32_t seg_len, int32_t K_s) {
+  if (seg_len < 1) return fail(WAVE_ERR_SHAPE, "seg_len %d < 1", seg_len);
+  if (K_s < 1) return fail(WAVE_ERR_SHAPE, "clusters_per_seg %d < 1", K_s);
+  if (K_s > seg_len) return fail(WAVE_ERR_SHAPE, "clusters_per_seg %d > seg_len %d", K_s, seg_len);
+  if (seg_len > WAVE_MAX_SEG_LEN) return fail(WAVE_ERR_UNSUPPORTED, "seg_len %d > %d", seg_len, WAVE_MAX_SEG_LEN);
+  if (K_s > WAVE_MAX_CLUSTERS_PER_SEG)
+    return fail(WAVE_ERR_UNSUPPORTED, "clusters_per_seg %d > %d", K_s, WAVE_MAX_CLUSTERS_PER_SEG);
+  return WAVE_OK;
+}
+
+wave::SeqArgs make_seq(const wave_shape* s, int32_t seg_len, int32_t K_s) {
+  wave::SeqArgs sa;
+  memset(&sa, 0, sizeof(sa));
+  sa.B = s->batch;
+  sa.G = s->n_kv_heads;
+  sa.seg_len = seg_len;
+  sa.K_s = K_s;
+  for (int b = 0; b < s->batch; ++b) {
+    sa.N[b] = (int32_t)s->ctx[b];
+    sa.C[b] = (int32_t)wave::num_clusters(s->ctx[b], seg_len, K_s);
+  }
+  return sa;
+}
+
+void index_sizes(const wave::SeqArgs& sa, wave_index_sizes* o) {
+  memset(o, 0, sizeof(*o));
+  for (int b = 0; b < sa.B; ++b) {
+    o->rows += (int64_t)sa.G * sa.N[b];
+    o->clusters += (int64_t)sa.G * sa.C[b];
+    o->offsets_len += (int64_t)sa.G * (sa.C[b] + 1);
+    o->units += (int64_t)sa.G * ((sa.N[b] + sa.seg_len - 1) / sa.seg_len);
+    if (sa.C[b] > o->max_clusters) o->max_clusters = sa.C[b];
+  }
+}
+
+struct BuildLayout {
+  size_t norm, xnorm, amb, rank, total;
+};
+
+BuildLayout build_layout(const wave_index_sizes& z) {
+  BuildLayout L;
+  size_t o = 0;
+  L.norm = o;  o += align256(sizeof(float) * (size_t)z.clusters);
+  L.xnorm = o; o += align256(sizeof(float) * (size_t)z.rows);
+  L.amb = o;   o += align256(sizeof(int32_t) * (size_t)(1 + 2 * z.rows));
+  L.rank = o;  o += align256(sizeof(int32_t) * (size_t)z.rows);
+  L.total = o;
+  return L;
+}
+
+wave_status hip_device_ok() {
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess || n < 1) return fail(WAVE_ERR_HIP, "no HIP device (%s)", hipGetErrorString(e));
+  return WAVE_OK;
+}
+
+// ------------------------------------------------------------------ decode sizes
+struct DecodePlan {
+  wave::DecodeArgs da;
+  size_t keys, key32, selid, selpre, excl, rows, corr, counts, part, sortg, total;
+};
+
+wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t n_local, double frac,
+                        DecodePlan* P) {
+  if (ix == nullptr) return fail(WAVE_ERR_ARG, "index is NULL");
+  wave_status st = check_shape(&ix->shape);
+  if (st != WAVE_OK) return st;
+  st = check_seg(ix->seg_len, ix->clusters_per_seg);
+  if (st != WAVE_OK) return st;
+  const int G = ix->shape.n_kv_heads;
+  if (H < 1 || H % G != 0) return fail(WAVE_ERR_SHAPE, "n_q_heads %d is not a positive multiple of n_kv_heads %d", H, G);
+  if (H / G > WAVE_MAX_GROUP) return fail(WAVE_ERR_UNSUPPORTED, "%d q heads per kv head > %d", H / G, WAVE_MAX_GROUP);
+  if (n_sink < 0 || n_local < 0) return fail(WAVE_ERR_ARG, "n_sink %d / n_local %d negative", n_sink, n_local);
+  if (!(frac >= 0.0 && frac <= 1.0)) return fail(WAVE_ERR_ARG, "topk_frac %g outside [0, 1]", frac);
+  const wave::SeqArgs sa = make_seq(&ix->shape, ix->seg_len, ix->clusters_per_seg);
+  wave::DecodeArgs& da = P->da;
+  memset(&da, 0, sizeof(da));
+  da.H = H;
+  da.GS = H / G;
+  da.n_sink = n_sink;
+  da.n_local = n_local;
+  da.tau = (float)(1.0 / sqrt((double)WAVE_HEAD_DIM));
+  int kmax = 0, Cmax = 0, nEmax = 0;
+  int64_t Nmax = 0, sumC = 0, sumC1 = 0, sumW = 0, sumN = 0;
+  for (int b = 0; b < sa.B; ++b) {
+    const int64_t N = sa.N[b], C = sa.C[b];
+    double x = ceil(frac * (double)C);
+    if (x < 0) x = 0;
+    if (x > (double)C) x = (double)C;
+    da.kreq[b] = (int32_t)x;
+    kmax = da.kreq[b] > kmax ? da.kreq[b] : kmax;
+    Cmax = C > Cmax ? (int)C : Cmax;
+    Nmax = N > Nmax ? N : Nmax;
+    const int nE = (int)((C + wave::DEC_EST_CH - 1) / wave::DEC_EST_CH);
+    nEmax = nE > nEmax ? nE : nEmax;
+    sumC += C;
+    sumC1 += C + 1;
+    sumW += (C + 31) / 32;
+    sumN += N;
+    const int64_t a = n_sink < N ? n_sink : N;
+    const int64_t c = (N - n_local) > a ? (N - n_local) : a;
+    const int64_t nS = a + (N - c);
+    if (nS < N && nS > WAVE_MAX_STEADY)
+      return fail(WAVE_ERR_UNSUPPORTED, "steady zone of sequence %d has %lld tokens (> %d) without covering it", b,
+                  (long long)nS, WAVE_MAX_STEADY);
+  }
+  da.k_max = kmax;
+  const int64_t steady_req = (int64_t)n_sink + (int64_t)n_local;
+  da.scap = (int32_t)(steady_req < Nmax ? steady_req : Nmax);
+  if (da.scap < 1) da.scap = 1;
+  // retrieval workgroups per (b, h): about 256 gathered rows each
+  const int64_t avg = (ix->seg_len + ix->clusters_per_seg - 1) / ix->clusters_per_seg;
+  int64_t est = (int64_t)kmax * avg + da.scap;
+  if (est > Nmax) est = Nmax;
+  int64_t Pw = (est + 255) / 256;
+  if (Pw < 1) Pw = 1;
+  if (Pw > 2048) Pw = 2048;
+  da.P = (int32_t)Pw;
+  da.NP = da.P + nEmax;
+  int sort_stride = 0;
+  if (kmax > wave::DEC_SORT_LDS) {
+    sort_stride = 1;
+    while (sort_stride < Cmax) sort_stride <<= 1;
+  }
+  da.sort_stride = sort_stride;
+  const int64_t BH = (int64_t)sa.B * H;
+  size_t o = 0;
+  P->keys = o;   o += align256(4 * (size_t)(H * sumC));
+  P->key32 = o;  o += align256(4 * (size_t)(H * sumC));
+  P->selid = o;  o += align256(4 * (size_t)(H * sumC));
+  P->selpre = o; o += align256(4 * (size_t)(H * sumC1));
+  P->excl = o;   o += align256(4 * (size_t)(H * sumW));
+  P->rows = o;   o += align256(4 * (size_t)(H * sumN));
+  P->corr = o;   o += align256(4 * (size_t)(BH * da.scap));
+  P->counts = o; o += align256(4 * (size_t)(BH * 2));
+  P->part = o;   o += align256(4 * (size_t)(BH * da.NP * wave::DEC_PART));
+  P->sortg = o;  o += align256(8 * (size_t)(BH * sort_stride));
+  P->total = o;
+  return WAVE_OK;
+}
+
+// ------------------------------------------------------------------ profiler
+struct ProfRec {
+  std::string name;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+
+}  // namespace
+
+namespace wave {
+
+void prof_begin(const char* name, hipStream_t st) {
+  if (!g_prof_on) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfRec r;
+  r.name = name;
+  (void)hipEventCreate(&r.a);
+  (void)hipEventCreate(&r.b);
+  (void)hipEventRecord(r.a, st);
+  g_prof.push_back(r);
+}
+
+void prof_end(hipStream_t st) {
+  if (!g_prof_on) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof.empty()) (void)hipEventRecord(g_prof.back().b, st);
+}
+
+}  // namespace wave
+
+extern "C" {
+
+const char* wave_last_error(void) { return g_err; }
+
+wave_status wave_index_plan(const wave_shape* shape, int32_t seg_len, int32_t clusters_per_seg,
+                            wave_index_sizes* out) {
+  wave_status st = check_shape(shape);
+  if (st != WAVE_OK) return st;
+  st = check_seg(seg_len, clusters_per_seg);
+  if (st != WAVE_OK) return st;
+  if (out == nullptr) return fail(WAVE_ERR_ARG, "out is NULL");
+  const wave::SeqArgs sa = make_seq(shape, seg_len, clusters_per_seg);
+  index_sizes(sa, out);
+  out->build_ws_bytes = build_layout(*out).total;
+  return ok();
+}
+
+wave_status wave_index_build(const wave_shape* shape, const void* K, const void* V, int32_t seg_len,
+                             int32_t clusters_per_seg, int32_t iters, uint64_t seed, wave_index* out, void* ws,
+                             size_t ws_bytes, int32_t* assign_trace, wave_stream_t stream) {
+  wave_status st = check_shape(shape);
+  if (st != WAVE_OK) return st;
+  st = check_seg(seg_len, clusters_per_seg);
+  if (st != WAVE_OK) return st;
+  if (iters < 1) return fail(WAVE_ERR_SHAPE, "iters %d < 1", iters);
+  if (K == nullptr || V == nullptr || out == nullptr || ws == nullptr)
+    return fail(WAVE_ERR_ARG, "K, V, out and ws must be non-NULL");
+  const void* ptrs[] = {out->k_sorted, out->v_sorted, out->perm, out->inv_perm, out->assign, out->offsets,
+                        out->sizes, out->centroids, out->centroids_bf16, out->vsum};
+  for (const void* p : ptrs)
+    if (p == nullptr) return fail(WAVE_ERR_ARG, "an index array pointer is NULL");
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(WAVE_ERR_ALIGN, "index arrays must be 16-byte aligned");
+  if (!aligned16(K) || !aligned16(V) || !aligned16(ws) || (assign_trace && !aligned16(assign_trace)))
+    return fail(WAVE_ERR_ALIGN, "K, V, ws and assign_trace must be 16-byte aligned");
+  wave_index_sizes z;
+  const wave::SeqArgs sa = make_seq(shape, seg_len, clusters_per_seg);
+  index_sizes(sa, &z);
+  const BuildLayout L = build_layout(z);
+  if (ws_bytes < L.total)
+    return fail(WAVE_ERR_WORKSPACE, "build workspace %zu bytes < %zu", ws_bytes, L.total);
+  st = hip_device_ok();
+  if (st != WAVE_OK) return st;
+  out->shape = *shape;
+  out->seg_len = seg_len;
+  out->clusters_per_seg = clusters_per_seg;
+  uint8_t* w = reinterpret_cast<uint8_t*>(ws);
+  wave::BuildWs bw;
+  bw.norm = reinterpret_cast<float*>(w + L.norm);
+  bw.xnorm = reinterpret_cast<float*>(w + L.xnorm);
+  bw.amb = reinterpret_cast<int32_t*>(w + L.amb);
+  bw.rank = reinterpret_cast<int32_t*>(w + L.rank);
+  hipError_t e = wave::launch_build(sa, K, V, iters, seed, *out, bw, z.units, assign_trace, z.rows,
+                                    reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(WAVE_ERR_HIP, "build launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+wave_status wave_attn_decode_plan(const wave_index* index, int32_t n_q_heads, int32_t n_sink, int32_t n_local,
+                                  double topk_frac, int32_t* k_max, size_t* ws_bytes) {
+  DecodePlan P;
+  wave_status st = decode_plan(index, n_q_heads, n_sink, n_local, topk_frac, &P);
+  if (st != WAVE_OK) return st;
+  if (k_max) *k_max = P.da.k_max;
+  if (ws_bytes) *ws_bytes = P.total;
+  return ok();
+}
+
+wave_status wave_attn_decode(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
+                             int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse, void* ws,
+                             size_t ws_bytes, wave_stream_t stream) {
+  DecodePlan P;
+  wave_status st = decode_plan(index, n_q_heads, n_sink, n_local, topk_frac, &P);
+  if (st != WAVE_OK) return st;
+  if (q == nullptr || out == nullptr || ws == nullptr) return fail(WAVE_ERR_ARG, "q, out and ws must be non-NULL");
+  if (P.da.k_max > 0 && sel_ids == nullptr) return fail(WAVE_ERR_ARG, "sel_ids is NULL but k_max = %d", P.da.k_max);
+  const void* ptrs[] = {index->k_sorted, index->v_sorted, index->perm, index->inv_perm, index->assign,
+                        index->offsets, index->sizes, index->centroids_bf16, index->vsum};
+  for (const void* p : ptrs)
+    if (p == nullptr) return fail(WAVE_ERR_ARG, "an index array pointer is NULL");
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(WAVE_ERR_ALIGN, "index arrays must be 16-byte aligned");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(ws) || (sel_ids && !aligned16(sel_ids)) ||
+      (lse && !aligned16(lse)))
+    return fail(WAVE_ERR_ALIGN, "q, out, sel_ids, lse and ws must be 16-byte aligned");
+  if (ws_bytes < P.total) return fail(WAVE_ERR_WORKSPACE, "decode workspace %zu bytes < %zu", ws_bytes, P.total);
+  st = hip_device_ok();
+  if (st != WAVE_OK) return st;
+  const wave::SeqArgs sa = make_seq(&index->shape, index->seg_len, index->clusters_per_seg);
+  uint8_t* w = reinterpret_cast<uint8_t*>(ws);
+  wave::DecodeWs dw;
+  dw.keys = reinterpret_cast<float*>(w + P.keys);
+  dw.key32 = reinterpret_cast<uint32_t*>(w + P.key32);
+  dw.selid = reinterpret_cast<int32_t*>(w + P.selid);
+  dw.selpre = reinterpret_cast<int32_t*>(w + P.selpre);
+  dw.excl = reinterpret_cast<uint32_t*>(w + P.excl);
+  dw.rows = reinterpret_cast<int32_t*>(w + P.rows);
+  dw.corr = reinterpret_cast<float*>(w + P.corr);
+  dw.counts = reinterpret_cast<int32_t*>(w + P.counts);
+  dw.part = reinterpret_cast<float*>(w + P.part);
+  dw.sortg = reinterpret_cast<uint64_t*>(w + P.sortg);
+  hipError_t e = wave::launch_decode(sa, P.da, *index, dw, reinterpret_cast<const uint16_t*>(q), out, sel_ids, lse,
+                                     reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(WAVE_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+wave_status wave_profiler_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (on) {
+    for (auto& r : g_prof) {
+      (void)hipEventDestroy(r.a);
+      (void)hipEventDestroy(r.b);
+    }
+    g_prof.clear();
+  }
+  g_prof_on = on != 0;
+  return ok();
+}
+
+int32_t wave_profiler_read(char* names, int64_t* launches, double* total_ms, int32_t n_max) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  std::vector<std::string> keys;
+  std::vector<int64_t> cnt;
+  std::vector<double> ms;
+  for (auto& r : g_prof) {
+    if (hipEventSynchronize(r.b) != hipSuccess) return (int32_t)fail(WAVE_ERR_HIP, "event synchronize failed");
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) return (int32_t)fail(WAVE_ERR_HIP, "elapsed time failed");
+    size_t i = 0;
+    while (i < keys.size() && keys[i] != r.name) ++i;
+    if (i == keys.size()) {
+      keys.push_back(r.name);
+      cnt.push_back(0);
+      ms.push_back(0.0);
+    }
+    cnt[i] += 1;
+    ms[i] += t;
+  }
+  int32_t n = 0;
+  for (size_t i = 0; i < keys.size() && n < n_max; ++i, ++n) {
+    if (names) {
+      strncpy(names + 64 * n, keys[i].c_str(), 63);
+      names[64 * n + 63] = '\0';
+    }
+    if (launches) launches[n] = cnt[i];
+    if (total_ms) total_ms[n] = ms[i];
+  }
+  g_err[0] = '\0';
+  return n;
+}
+
+}  // extern "C"

@@ -17,7 +17,7 @@ _LIB_PATH = os.path.join(_HERE, "libsynth.so")
 _lib = None
 
 
-def build():
+def compile_lib():
     """Compile libsynth.so (plain C, OpenMP) in place."""
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
            "-o", _LIB_PATH, os.path.join(_HERE, "synth.c"), "-lm"]
@@ -28,7 +28,7 @@ def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
-            build()
+            compile_lib()
         lib = ctypes.CDLL(_LIB_PATH)
         P = ctypes.c_void_p
         lib.syn_ctx_lengths.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, P]

@@ -1,0 +1,167 @@
+"""The C ABI on the CPU: the library loads, exports every declared entry point, sizes its
+arrays, and rejects bad arguments before touching a device (no GPU needed)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import oracle
+import retrieval_sparse_attention_amd as rsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, ARG, SHAPE, UNSUP, WS, ALIGN, HIP = 0, -1, -2, -3, -4, -5, -6
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "wave_attn.h")).read()
+    return sorted(set(re.findall(r"^(?:wave_status|const char\*|int32_t)\s+(wave_\w+)\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert {"wave_index_plan", "wave_index_build", "wave_attn_decode_plan", "wave_attn_decode",
+            "wave_last_error"} <= set(names)
+    L = rsa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _shape(G, ctx, head_dim=128):
+    arr = (ctypes.c_int64 * len(ctx))(*ctx)
+    return rsa._Shape(len(ctx), G, head_dim, 0, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64))), arr
+
+
+def _plan(G, ctx, L, K, head_dim=128):
+    sh, keep = _shape(G, ctx, head_dim)
+    z = rsa._Sizes()
+    return rsa.lib().wave_index_plan(ctypes.byref(sh), L, K, ctypes.byref(z)), z
+
+
+def test_index_plan_sizes():
+    for G, ctx, L, K in [(8, [131072], 8192, 512), (8, [1048576], 16384, 1024), (2, [16384], 8192, 512),
+                         (3, [70000, 8192 * 2 + 5, 1], 8192, 512)]:
+        st, z = _plan(G, ctx, L, K)
+        assert st == OK
+        C = [oracle.num_clusters(n, L, K) for n in ctx]
+        assert z.rows == G * sum(ctx)
+        assert z.clusters == G * sum(C)
+        assert z.offsets_len == G * sum(c + 1 for c in C)
+        assert z.units == G * sum(-(-n // L) for n in ctx)
+        assert z.max_clusters == max(C)
+        assert z.build_ws_bytes >= 4 * (z.clusters + 4 * z.rows)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((8, [1000], 256, 16, 64), UNSUP),     # head_dim 64
+    ((8, [1000], 256, 300), SHAPE),        # K_s > L_s
+    ((8, [1000], 0, 1), SHAPE),
+    ((8, [1000], 256, 0), SHAPE),
+    ((0, [1000], 256, 16), SHAPE),
+    ((8, [0], 256, 16), SHAPE),
+    ((8, [1000], 65537, 16), UNSUP),
+    ((8, [1000], 4096, 4096), UNSUP),     # K_s above the per-segment limit
+    ((8, [1 << 31], 4096, 16), UNSUP),
+])
+def test_index_plan_rejects(args, status):
+    st, _ = _plan(*args)
+    assert st == status
+    assert rsa.lib().wave_last_error().decode() != ""
+
+
+def test_index_plan_batch_limits():
+    st, _ = _plan(1, [10] * 257, 8, 2)
+    assert st == UNSUP
+    sh = rsa._Shape(1, 1, 128, 0, None)
+    z = rsa._Sizes()
+    assert rsa.lib().wave_index_plan(ctypes.byref(sh), 8, 2, ctypes.byref(z)) == ARG
+
+
+def _fake_index(G, ctx, L, K):
+    sh, keep = _shape(G, ctx)
+    ix = rsa._Index()
+    ix.shape = sh
+    ix.seg_len, ix.clusters_per_seg = L, K
+    for i, f in enumerate(("k_sorted", "v_sorted", "perm", "inv_perm", "assign", "offsets", "sizes",
+                           "centroids", "centroids_bf16", "vsum")):
+        setattr(ix, f, 0x10000 * (i + 1))  # aligned, never dereferenced on the CPU
+    return ix, keep
+
+
+def _dplan(ix, H, ns, nl, frac):
+    k = ctypes.c_int32()
+    w = ctypes.c_size_t()
+    st = rsa.lib().wave_attn_decode_plan(ctypes.byref(ix), H, ns, nl, frac, ctypes.byref(k), ctypes.byref(w))
+    return st, k.value, w.value
+
+
+@pytest.mark.parametrize("G,H,N,L,K,frac,kmax", [(2, 8, 16384, 8192, 512, 0.05, 52), (8, 32, 131072, 8192, 512, 0.02, 164),
+                                              (8, 32, 1048576, 16384, 1024, 0.018, 1180),
+                                              (8, 32, 131072, 8192, 512, 0.0, 0), (8, 32, 131072, 8192, 512, 1.0, 8192)])
+def test_decode_plan_k_max(G, H, N, L, K, frac, kmax):
+    ix, keep = _fake_index(G, [N], L, K)
+    st, k, w = _dplan(ix, H, 4, 64, frac)
+    assert st == OK and k == kmax and k == oracle.k_from_frac(frac, oracle.num_clusters(N, L, K))
+    assert w > 4 * H * oracle.num_clusters(N, L, K)
+
+
+@pytest.mark.parametrize("H,ns,nl,frac,status", [
+    (30, 4, 64, 0.02, SHAPE),        # 30 % 8
+    (0, 4, 64, 0.02, SHAPE),
+    (80, 4, 64, 0.02, UNSUP),        # 10 q heads per kv head
+    (32, -1, 64, 0.02, ARG),
+    (32, 4, -5, 0.02, ARG),
+    (32, 4, 64, float("nan"), ARG),
+    (32, 4, 64, 1.5, ARG),
+    (32, 4, 64, -0.1, ARG),
+    (32, 3000, 3000, 0.02, UNSUP),   # 6000 steady tokens, not the whole sequence
+])
+def test_decode_plan_rejects(H, ns, nl, frac, status):
+    ix, keep = _fake_index(8, [131072], 8192, 512)
+    st, _, _ = _dplan(ix, H, ns, nl, frac)
+    assert st == status
+
+
+def test_decode_plan_all_steady_is_supported():
+    ix, keep = _fake_index(8, [5000], 1024, 64)
+    st, k, w = _dplan(ix, 32, 2500, 2500, 0.1)
+    assert st == OK
+
+
+def test_calls_fail_cleanly_without_device():
+    if os.path.exists("/dev/kfd"):
+        pytest.skip("a GPU is present")
+    L = rsa.lib()
+    sh, keep = _shape(2, [4096])
+    ix, keep2 = _fake_index(2, [4096], 1024, 64)
+    st, z = _plan(2, [4096], 1024, 64)
+    args = [ctypes.byref(sh), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), 1024, 64, 2, ctypes.c_uint64(1),
+            ctypes.byref(ix), ctypes.c_void_p(0x3000), z.build_ws_bytes, None, None]
+    assert L.wave_index_build(*args) == HIP
+    # argument errors win over the missing device and nothing is touched
+    bad = list(args)
+    bad[1] = None
+    assert L.wave_index_build(*bad) == ARG
+    bad = list(args)
+    bad[1] = ctypes.c_void_p(0x1001)
+    assert L.wave_index_build(*bad) == ALIGN
+    bad = list(args)
+    bad[9] = z.build_ws_bytes - 1
+    assert L.wave_index_build(*bad) == WS
+    bad = list(args)
+    bad[5] = 0
+    assert L.wave_index_build(*bad) == SHAPE
+    st, k, w = _dplan(ix, 8, 4, 64, 0.05)
+    dargs = [ctypes.byref(ix), ctypes.c_void_p(0x4000), 8, 4, 64, 0.05, ctypes.c_void_p(0x5000),
+             ctypes.c_void_p(0x6000), None, ctypes.c_void_p(0x7000), w, None]
+    assert L.wave_attn_decode(*dargs) == HIP
+    bad = list(dargs)
+    bad[10] = w - 1
+    assert L.wave_attn_decode(*bad) == WS
+    bad = list(dargs)
+    bad[7] = None
+    assert L.wave_attn_decode(*bad) == ARG
+    bad = list(dargs)
+    bad[1] = ctypes.c_void_p(0x4008)
+    assert L.wave_attn_decode(*bad) == ALIGN
