@@ -334,6 +334,7 @@ static int build_impl(int32_t B, int32_t G, const int64_t* ctx, const uint16_t* 
   seq_base* sb = make_bases(B, G, ctx, seg_len, K_s);
   int64_t rows = sb[B].row;
   int64_t n_units = sb[B].unit;
+  int rc = 0;
   /* enumerate units (b, g, s) in order */
   int64_t* ub = (int64_t*)malloc(sizeof(int64_t) * (size_t)n_units * 3);
   int64_t u = 0;
@@ -361,7 +362,16 @@ static int build_impl(int32_t B, int32_t G, const int64_t* ctx, const uint16_t* 
       for (int32_t j = 0; j < Kc; ++j)
         for (int i = 0; i < D; ++i) cent[(int64_t)j * D + i] = ref_bf16_to_f32(X[(int64_t)idx[j] * D + i]);
       free(idx);
-      for (int32_t t = 0; t < L; ++t) la[t] = given_assign[row0 + t] - (int32_t)(s * K_s);
+      int bad = 0;
+      for (int32_t t = 0; t < L; ++t) {
+        la[t] = given_assign[row0 + t] - (int32_t)(s * K_s);
+        if (la[t] < 0 || la[t] >= Kc) bad = 1;
+      }
+      if (bad) {
+#pragma omp atomic write
+        rc = -1;
+        for (int32_t t = 0; t < L; ++t) la[t] = 0;
+      }
       update_centroids_f32(X, L, Kc, la, cent);
     } else {
       int32_t* tr = trace ? (int32_t*)malloc(sizeof(int32_t) * (size_t)L * iters) : NULL;
@@ -387,7 +397,7 @@ static int build_impl(int32_t B, int32_t G, const int64_t* ctx, const uint16_t* 
   }
   (void)rows;
   free(sb);
-  return 0;
+  return rc;
 }
 
 int ref_build(int32_t B, int32_t G, const int64_t* ctx, const uint16_t* K, const uint16_t* V, int32_t seg_len,

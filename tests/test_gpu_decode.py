@@ -102,7 +102,7 @@ def test_global_sort_path():
     ctx = np.array([40000], np.int64)
     G, H = 1, 2
     K, V, comp = synth.kv(51, 1, G, ctx, 1024, comp=True)
-    idx = oracle.index_from_assign(K, V, G, ctx, 1024, 256, 3, comp % 256 + (np.arange(40000) // 1024) * 256)
+    idx = oracle.index_from_assign(K, V, G, ctx, 1024, 256, 3, _label_assign(comp, ctx, G, 1024, 256))
     q, _ = synth.queries(52, 1, 1, H, G, ctx, K)
     _compare(idx, K, V, q[0], upload_index(idx), 4, 64, 1.0, "global sort")
     _compare(idx, K, V, q[0], upload_index(idx), 4, 64, 0.9, "global sort 0.9")
