@@ -1,0 +1,327 @@
+"""Benchmark: wave-index sparse decode attention on one MI355X.
+
+Workload (Llama-3-8B-shaped attention layer at 128K context; RetroInfer summary page,
+section 4 evaluates 120K and 1M contexts on Llama3-class models): batch 1, 32 q heads /
+8 kv heads, head_dim 128, ctx 131072 bf16 keys/values drawn by the seeded generator;
+segments of 8192 tokens with 512 clusters (16 tokens per cluster), 10 k-means rounds;
+steady zone 4 sink + 64 local tokens; top 2% of the clusters retrieved.
+
+One step = the whole hot path over one batch of input: the index build of one layer
+(segmented k-means + layout) and 64 decode queries.  `value` is decode steps (queries)
+per second of that whole job.  Inputs are resident in HBM before timing.  L = 32 layers
+live in HBM at distinct addresses; step i rebuilds layer i mod L and its 64 queries visit
+the layers round robin, so no decode reuses the 256 MB Infinity Cache.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+WORKLOAD = dict(workload="llama3-8b-attention-layer-128k", batch=1, q_heads=32, kv_heads=8, head_dim=128,
+                ctx=131072, seg_len=8192, clusters_per_seg=512, kmeans_iters=10, n_sink=4, n_local=64,
+                topk_frac=0.02, decode_queries_per_step=64, layers=32, seed_data=2, seed_build=1234,
+                seed_query=102)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--layers", type=int, default=WORKLOAD["layers"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the oracle timing sample")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a device copy of 1 GiB (scale of the HBM byte counters)")
+    return p.parse_args()
+
+
+def source_sha(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel, sha):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it matches the source."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_128k.txt" % kernel)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha") != sha:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU: this build has no multi-GPU path (the kv-head sharding it "
+              "would use is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import retrieval_sparse_attention_amd as rsa
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        n = 1 << 30
+        x = torch.empty(n, dtype=torch.uint8, device=dev)
+        y = torch.empty_like(x)
+        x.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "launches": 3}))
+        return
+
+    W = dict(WORKLOAD)
+    W["layers"] = args.layers
+    B, H, G, N = W["batch"], W["q_heads"], W["kv_heads"], W["ctx"]
+    seg, K_s, iters = W["seg_len"], W["clusters_per_seg"], W["kmeans_iters"]
+    ns, nl, frac, QPS = W["n_sink"], W["n_local"], W["topk_frac"], W["decode_queries_per_step"]
+    L = args.layers
+    ctx = np.array([N] * B, np.int64)
+
+    print("generating inputs", file=sys.stderr, flush=True)
+    K, V, _ = synth.kv(W["seed_data"], B, G, ctx, seg)
+    nq = QPS * 4
+    q, _ = synth.queries(W["seed_query"], nq, B, H, G, ctx, K)
+    Kd0 = torch.from_numpy(K.view(np.int16)).to(dev).view(torch.bfloat16)
+    Vd0 = torch.from_numpy(V.view(np.int16)).to(dev).view(torch.bfloat16)
+    qd = torch.from_numpy(q.view(np.int16)).to(dev).view(torch.bfloat16)  # [nq, B, H, 128]
+    # L layers at distinct addresses (copies of the seeded layer)
+    Ks = [Kd0] + [Kd0.clone() for _ in range(L - 1)]
+    Vs = [Vd0] + [Vd0.clone() for _ in range(L - 1)]
+    z = rsa.wave_index_plan(G, ctx.tolist(), seg, K_s)
+    idxs = [rsa.WaveIndex.allocate(G, ctx.tolist(), seg, K_s, device=dev)[0] for _ in range(L)]
+    bws = torch.empty(int(z["build_ws_bytes"]), dtype=torch.uint8, device=dev)
+    print("building %d layer indexes" % L, file=sys.stderr, flush=True)
+    for l in range(L):
+        rsa.wave_index_build(Ks[l], Vs[l], G, ctx.tolist(), seg, K_s, iters, W["seed_build"], index=idxs[l], ws=bws)
+    torch.cuda.synchronize()
+    k_max, dwsb = rsa.wave_attn_decode_plan(idxs[0], H, ns, nl, frac)
+    dws = torch.empty(dwsb, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, H, 128), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+
+    ids_buf = torch.empty((B, H, max(k_max, 1)), dtype=torch.int32, device=dev)
+
+    def job(step, ids_log=None, build=True):
+        """One step: rebuild layer (step mod L), then 64 queries over the layers round robin."""
+        l = step % L
+        if build:
+            rsa.wave_index_build(Ks[l], Vs[l], G, ctx.tolist(), seg, K_s, iters, W["seed_build"], index=idxs[l],
+                                 ws=bws)
+        for s in range(QPS):
+            lay = (step * QPS + s) % L
+            qi = (step * QPS + s) % nq
+            ids = ids_log[s] if ids_log is not None else ids_buf
+            rsa.wave_attn_decode(idxs[lay], qd[qi], ns, nl, frac, ws=dws, out=out, sel_ids=ids, lse=lse)
+
+    # the step pattern repeats with period P: one captured HIP graph per phase
+    P = math.lcm(L, max(1, nq // math.gcd(nq, QPS)))
+    print("warmup (eager) and capture of %d step graphs" % P, file=sys.stderr, flush=True)
+    for i in range(max(1, args.warmup)):
+        job(i)
+    torch.cuda.synchronize()
+    graphs, dgraphs = [], []
+    for ph in range(P):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            job(ph)
+        graphs.append(g)
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g2):
+            job(ph, build=False)
+        dgraphs.append(g2)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        graphs[i % P].replay()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K whole-job steps (graph replays on the current stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.warmup, args.warmup + args.steps):
+        graphs[i % P].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t_plain = e0.elapsed_time(e1)
+    print("timed %d steps: %.3f ms" % (args.steps, t_plain), file=sys.stderr, flush=True)
+    # decode queries alone (same 64 per step, no build)
+    e0.record()
+    for i in range(args.warmup, args.warmup + args.steps):
+        dgraphs[i % P].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t_dec = e0.elapsed_time(e1)
+
+    # ---- the same steps once more, eagerly, with HIP events around every kernel on its
+    # launch stream: per-kernel durations for the roofline, and the selected ids
+    ids_log = torch.empty((args.steps * QPS, B, H, max(k_max, 1)), dtype=torch.int32, device=dev)
+    rsa.wave_profiler_enable(True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.warmup, args.warmup + args.steps):
+        job(i, ids_log[(i - args.warmup) * QPS:(i - args.warmup + 1) * QPS])
+    e1.record()
+    torch.cuda.synchronize()
+    rsa.wave_profiler_enable(False)
+    prof = rsa.wave_profiler_read()
+    t_ms = e0.elapsed_time(e1)
+
+    # ---- algorithmic work per launch (actual sizes of the selected clusters)
+    sizes = [ix.sizes.cpu().numpy() for ix in idxs[:1]][0]  # every layer holds the same clustering
+    C = sizes.shape[0] // G
+    ids_h = ids_log[:, :, :, :k_max].cpu().numpy().reshape(args.steps * QPS, B * H, k_max)
+    retrieved_rows = 0
+    for qq in range(ids_h.shape[0]):
+        for h in range(H):
+            g = h * G // H
+            sel = ids_h[qq, h]
+            sel = sel[sel >= 0]
+            retrieved_rows += int(sizes[g * C + sel].sum())
+    rows_per_dec = retrieved_rows / ids_h.shape[0]
+    steady = ns + nl
+    row_bytes = 2 * 128 * 2 + 4  # K + V row (bf16) + its sorted-slot index
+    attend_bytes = (G * C * (128 * 4 + 4)          # value sums + sizes of every cluster (estimation)
+                    + H * C * 4                   # rank keys of every (q head, cluster)
+                    + rows_per_dec * row_bytes + H * steady * row_bytes  # retrieved + steady rows
+                    + B * H * 128 * 2)            # q
+    score_bytes = G * C * 128 * 2 + B * H * 128 * 2 + H * C * 4
+    step_bytes = (G * C * (128 * 2 + 128 * 4 + 4) + rows_per_dec * row_bytes + H * steady * row_bytes
+                  + B * H * 128 * 2 + B * H * 128 * 4 + B * H * k_max * 4)
+    assign_flops = 2.0 * B * N * K_s * 128 * G  # per launch (one k-means round)
+
+    kern = {}
+    for name, (cnt, ms) in prof.items():
+        kern[name] = {"launches": cnt, "avg_us": 1000.0 * ms / cnt, "total_ms": ms}
+    sha = source_sha(["retrieval_sparse_attention_amd/csrc/decode.hip", "retrieval_sparse_attention_amd/csrc/build.hip",
+                      "retrieval_sparse_attention_amd/csrc/common.h"])
+    dom = max(kern, key=lambda k: kern[k]["total_ms"])
+    if dom == "k_assign":
+        ach = assign_flops / (kern[dom]["avg_us"] * 1e-6) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": counter_traffic(dom, sha),
+                "algorithmic_per_launch": assign_flops}
+    else:
+        per = {"k_attend": attend_bytes, "k_score": score_bytes}.get(dom, None)
+        ach = per / (kern[dom]["avg_us"] * 1e-6) / 1e9 if per else None
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1) if ach else None, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4) if ach else None,
+                "traffic": counter_traffic(dom, sha), "algorithmic_per_launch": per}
+    # every kernel's own roofline figure, for the record
+    extra = {}
+    if "k_attend" in kern:
+        a = attend_bytes / (kern["k_attend"]["avg_us"] * 1e-6) / 1e9
+        extra["k_attend"] = {"bound": "hbm", "achieved_GBs": round(a, 1), "frac": round(a / HBM_PEAK_GBS, 4),
+                             "bytes_per_launch": int(attend_bytes), "traffic": counter_traffic("k_attend", sha)}
+    if "k_score" in kern:
+        a = score_bytes / (kern["k_score"]["avg_us"] * 1e-6) / 1e9
+        extra["k_score"] = {"bound": "hbm", "achieved_GBs": round(a, 1), "frac": round(a / HBM_PEAK_GBS, 4),
+                            "bytes_per_launch": int(score_bytes)}
+    if "k_assign" in kern:
+        a = assign_flops / (kern["k_assign"]["avg_us"] * 1e-6) / 1e12
+        extra["k_assign"] = {"bound": "mfma", "achieved_TFLOPs": round(a, 1), "frac": round(a / BF16_PEAK_TFLOPS, 4),
+                             "flops_per_launch": assign_flops}
+
+    decodes = args.steps * QPS
+    value = decodes / (t_plain / 1000.0)
+    build_ms = sum(kern[k]["total_ms"] for k in kern if k not in ("k_score", "k_topk", "k_attend", "k_merge"))
+    result = {
+        "metric": "sparse decode-attn steps/s (whole job: index build + 64 decode queries per step), 8B-shape layer at 128K ctx",
+        "value": round(value, 1),
+        "unit": "decode steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_plain / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": W,
+        "roofline": roof,
+        "decode_only_steps_per_s": round(decodes / (t_dec / 1000.0), 1),
+        "decode_only_us_per_query": round(1000.0 * t_dec / decodes, 2),
+        "decode_only_effective_GBs": round(step_bytes * decodes / (t_dec / 1000.0) / 1e9, 1),
+        "decode_bytes_per_query": int(step_bytes),
+        "build_tokens_per_s": round(args.steps * B * N / (build_ms / 1000.0), 1),
+        "eager_with_kernel_events_ms_per_step": round(t_ms / args.steps, 4),
+        "kernels": {k: {"launches": v["launches"], "avg_us": round(v["avg_us"], 2)} for k, v in kern.items()},
+        "kernel_roofline": extra,
+        "source_sha": sha,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(W, K, V, ctx, q, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+def cpu_baseline(W, K, V, ctx, q, budget_s):
+    """The oracle, as it stands, timed on this host's cores on a bounded sample of one step.
+
+    One step = index build (every unit: B*G*ceil(N/seg) independent k-means problems, then
+    the layout) + 64 decode queries. Sample: a few k-means units and a few decode queries
+    against an oracle index over a prescribed clustering; the step time is extrapolated
+    by the unit and query counts.
+    """
+    import numpy as np
+
+    import oracle
+
+    G, H, seg, K_s, iters = W["kv_heads"], W["q_heads"], W["seg_len"], W["clusters_per_seg"], W["kmeans_iters"]
+    N = int(ctx[0])
+    units_total = len(ctx) * G * (-(-N // seg))
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.time()
+    n_units = 0
+    while n_units < units_total and (n_units == 0 or time.time() - t0 < 0.5 * budget_s):
+        oracle.kmeans_segment(K[n_units * seg:(n_units + 1) * seg], K_s, iters, W["seed_build"], unit=n_units)
+        n_units += 1
+    t_unit = (time.time() - t0) / n_units
+    # decode sample on an oracle index over the generator's labels (k-means cost already sampled)
+    lab = (np.arange(K.shape[0]) % seg) % K_s + (np.arange(K.shape[0]) % N) // seg * K_s
+    t1 = time.time()
+    idx = oracle.index_from_assign(K, V, G, ctx, seg, K_s, W["seed_build"], lab.astype(np.int32))
+    t_layout = time.time() - t1
+    t2 = time.time()
+    n_dec = 0
+    while n_dec < min(q.shape[0], W["decode_queries_per_step"]) and (n_dec == 0 or time.time() - t2 < 0.5 * budget_s):
+        oracle.decode(idx, K, V, q[n_dec], W["n_sink"], W["n_local"], W["topk_frac"])
+        n_dec += 1
+    t_dec = (time.time() - t2) / n_dec
+    step_s = units_total * t_unit + t_layout + W["decode_queries_per_step"] * t_dec
+    return {"value": round(W["decode_queries_per_step"] / step_s, 4), "unit": "decode steps/s",
+            "cores": threads, "kind": "oracle",
+            "sample": "%d of %d k-means units (%.2f s each), one index layout (%.2f s), %d of 64 decode queries "
+                      "(%.3f s each); step time %.1f s extrapolated" % (n_units, units_total, t_unit, t_layout, n_dec,
+                                                                      t_dec, step_s)}
+
+
+if __name__ == "__main__":
+    main()
