@@ -44,7 +44,7 @@ typedef struct ihipStream_t* wave_stream_t; /* same type as hipStream_t */
 #define WAVE_MAX_BATCH 256     /* sequences per call */
 #define WAVE_MAX_SEG_LEN 65536 /* tokens per segment */
 #define WAVE_MAX_CLUSTERS_PER_SEG 2048
-#define WAVE_MAX_STEADY 4096   /* steady tokens per sequence unless they cover it all */
+#define WAVE_MAX_STEADY 2048   /* steady tokens per sequence unless they cover it all */
 #define WAVE_MAX_GROUP 8       /* q heads per kv head */
 
 typedef enum wave_status {

@@ -6,13 +6,13 @@
 // cut into segments that are clustered independently at prefill. One k-means
 // problem ("unit") per (sequence b, kv head g, segment s), enumerated in that
 // order. Launch sequence, all on the caller's stream:
-//   k_init                  seeded choice of K(s) tokens per unit, key norms
-//   iters x { k_round_norm  bf16 rounding of the centroids, their squared norms
-//             k_assign      nearest centroid on bf16 MFMA (32x32x16), fp32
-//             k_assign_fix  binary64 decision where fp32 cannot separate the two best
-//             k_sort        stable counting sort of each unit by cluster
-//             k_update      ordered fp32 member sums, correctly rounded means }
-//   k_layout                sorted K/V, inv_perm, ordered fp32 value sums, bf16 centroids
+//   k_init                   seeded choice of K(s) tokens per unit (bf16 centroids, norms)
+//   iters x { k_assign       nearest centroid on bf16 MFMA (32x32x16), fp32
+//             k_assign_fix   binary64 decision where fp32 cannot separate the two best
+//             k_sort         stable counting sort of each unit by cluster
+//             k_update       ordered fp32 member sums, correctly rounded means, bf16
+//                            centroids and norms; the last round also writes the
+//                            sorted K/V, inv_perm and the ordered fp32 value sums }
 #include <math.h>
 
 #include "common.h"
@@ -108,39 +108,23 @@ __device__ __forceinline__ uint64_t sm64_mix(uint64_t z) {
 // mix(seed + GAMMA*(u+1) + GAMMA*(i+1)); the draws do not depend on the
 // shuffle, so they are taken in parallel and one lane then performs the K(s)
 // swaps of the partial Fisher-Yates shuffle of [0, L) held in LDS (16-bit
-// entries). Centroid i becomes the fp32 copy of key row idx[i]. The same
-// workgroup writes |x| of every key of the segment (used for the fp32 error
-// margin of the assignment).
-__global__ __launch_bounds__(256) void k_init(SeqArgs sa, uint64_t seed, const uint16_t* __restrict__ K,
-                                              float* __restrict__ cent, float* __restrict__ xnorm) {
+// entries). Centroid i becomes the fp32 copy of key row idx[i]; its bf16
+// rounding is the key itself and its squared norm is summed here too.
+constexpr int INIT_THREADS = 1024;
+
+__global__ __launch_bounds__(INIT_THREADS) void k_init(SeqArgs sa, uint64_t seed, const uint16_t* __restrict__ K,
+                                                       float* __restrict__ cent, uint16_t* __restrict__ chat,
+                                                       float* __restrict__ norm, int32_t* __restrict__ amb) {
   extern __shared__ uint8_t smem[];
   const Unit U = unit_of(sa, blockIdx.x);
   uint16_t* idx = reinterpret_cast<uint16_t*>(smem);
   int32_t* jsel = reinterpret_cast<int32_t*>(smem + ((2 * (size_t)U.L + 15) & ~(size_t)15));
   const uint64_t st0 = seed + GAMMA * (uint64_t)(U.u + 1);
+  if (blockIdx.x == 0 && threadIdx.x == 0) amb[0] = 0;
   for (int i = threadIdx.x; i < U.L; i += blockDim.x) idx[i] = (uint16_t)i;
   for (int i = threadIdx.x; i < U.Kc; i += blockDim.x) {
     const uint64_t r = sm64_mix(st0 + GAMMA * (uint64_t)(i + 1));
     jsel[i] = i + (int32_t)(r % (uint64_t)(U.L - i));
-  }
-  // key norms of the segment (one row per 16 lanes)
-  {
-    const int lane = threadIdx.x & 63, l16 = lane & 15, grp = threadIdx.x >> 4;
-    for (int t = grp; t < U.L; t += blockDim.x / 16) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(K + (U.row0 + t) * D + l16 * 8);
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float a = bf16_lo(v[e]), c = bf16_hi(v[e]);
-        s = fmaf(a, a, s);
-        s = fmaf(c, c, s);
-      }
-      s += xor_shfl(s, 8);
-      s += xor_shfl(s, 4);
-      s += xor_shfl(s, 2);
-      s += xor_shfl(s, 1);
-      if (l16 == 0) xnorm[U.row0 + t] = sqrtf(s);
-    }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -152,30 +136,41 @@ __global__ __launch_bounds__(256) void k_init(SeqArgs sa, uint64_t seed, const u
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < U.Kc * D; e += blockDim.x) {
-    const int i = e / D, d = e % D;
-    cent[(U.gclu + i) * D + d] = bf16_to_f(K[(U.row0 + idx[i]) * D + d]);
-  }
-}
-
-// ------------------------------------------------------------------ k_round_norm
-// chat = bf16(c) for every cluster; norm = |chat|^2 in fp32; resets the
-// near-tie list. One wave per cluster, 2 dims per lane.
-__global__ __launch_bounds__(256) void k_round_norm(int64_t nclu, const float* __restrict__ cent,
-                                                    uint16_t* __restrict__ chat, float* __restrict__ norm,
-                                                    int32_t* __restrict__ amb) {
-  const int64_t F = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (blockIdx.x == 0 && threadIdx.x == 0) amb[0] = 0;
-  if (F >= nclu) return;
-  const float2 c = *reinterpret_cast<const float2*>(cent + F * D + 2 * lane);
-  const uint16_t h0 = f_to_bf16(c.x), h1 = f_to_bf16(c.y);
-  *reinterpret_cast<uint32_t*>(chat + F * D + 2 * lane) = (uint32_t)h0 | ((uint32_t)h1 << 16);
-  const float a = bf16_to_f(h0), b = bf16_to_f(h1);
-  float s = fmaf(a, a, b * b);
+  // (centroid i, 16-byte chunk c): 16 lanes per centroid, 8 rows in flight per thread
+  const int l16 = threadIdx.x & 15;
+  constexpr int UI = 8;
+  for (int i0 = threadIdx.x >> 4; i0 < U.Kc; i0 += (INIT_THREADS / 16) * UI) {
+    u32x4 v[UI];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) s += xor_shfl(s, o);
-  if (lane == 0) norm[F] = s;
+    for (int u = 0; u < UI; ++u) {
+      const int i = min(i0 + u * (INIT_THREADS / 16), U.Kc - 1);
+      v[u] = *reinterpret_cast<const u32x4*>(K + (U.row0 + idx[i]) * D + l16 * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < UI; ++u) {
+      const int i = i0 + u * (INIT_THREADS / 16);
+      float f[8];
+      float s2 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[2 * e] = bf16_lo(v[u][e]);
+        f[2 * e + 1] = bf16_hi(v[u][e]);
+        s2 = fmaf(f[2 * e], f[2 * e], s2);
+        s2 = fmaf(f[2 * e + 1], f[2 * e + 1], s2);
+      }
+      s2 += xor_shfl(s2, 8);
+      s2 += xor_shfl(s2, 4);
+      s2 += xor_shfl(s2, 2);
+      s2 += xor_shfl(s2, 1);
+      if (i < U.Kc) {
+        float* cr = cent + (U.gclu + i) * D + l16 * 8;
+        *reinterpret_cast<float4*>(cr) = make_float4(f[0], f[1], f[2], f[3]);
+        *reinterpret_cast<float4*>(cr + 4) = make_float4(f[4], f[5], f[6], f[7]);
+        *reinterpret_cast<u32x4*>(chat + (U.gclu + i) * D + l16 * 8) = v[u];
+        if (l16 == 0) norm[U.gclu + i] = s2;
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------------ k_assign (bf16 MFMA)
@@ -198,6 +193,7 @@ constexpr int AS_GROUP = AS_WAVES * 64;  // centroids per pass
 struct AssignLds {
   u32x4 tile[AS_TT * 16];           // token rows, 16-byte chunk c of row t stored at chunk c ^ (t & 15)
   float red[AS_WAVES][AS_TT][3];    // per wave: best, id (bits), second best
+  float xn[AS_TT];                  // |x| of the tile's tokens
   unsigned int rmax;                // max |c_j|^2 of the unit (float bits)
 };
 
@@ -243,7 +239,6 @@ __device__ inline void assign_wg_map(const SeqArgs& sa, int w, Unit& U, int& tok
 __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint16_t* __restrict__ K,
                                                           const uint16_t* __restrict__ chat,
                                                           const float* __restrict__ norm,
-                                                          const float* __restrict__ xnorm,
                                                           int32_t* __restrict__ assign, int32_t* __restrict__ amb) {
   extern __shared__ uint8_t smem[];
   AssignLds& S = *reinterpret_cast<AssignLds*>(smem);
@@ -252,6 +247,27 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint
   assign_wg_map(sa, blockIdx.x, U, tb0);
   const int tend = min(tb0 + AS_TPW, U.L);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, h = lane >> 5, col = lane & 31;
+  // the first token tile in flight: AS_TT rows x 16 chunks, 4 chunks per thread
+  constexpr int PF = AS_TT * 16 / AS_THREADS;
+  u32x4 pre[PF];
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int m = 0; m < PF; ++m) {
+      const int e = tid + m * AS_THREADS;
+      const int t = e >> 4, c = e & 15;
+      pre[m] = (t0 + t < tend) ? *reinterpret_cast<const u32x4*>(K + (U.row0 + t0 + t) * D + c * 8)
+                               : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int m = 0; m < PF; ++m) {
+      const int e = tid + m * AS_THREADS;
+      const int t = e >> 4, c = e & 15;
+      S.tile[t * 16 + (c ^ (t & 15))] = pre[m];
+    }
+  };
+  fetch(tb0);
   // largest squared centroid norm of the unit (all norms are >= 0)
   if (tid == 0) S.rmax = 0u;
   __syncthreads();
@@ -282,15 +298,26 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint
     }
   };
   if (ngroups == 1) load_group(0);
+  stash();
+  __syncthreads();
   for (int t0 = tb0; t0 < tend; t0 += AS_TT) {
-    // token tile -> LDS (zero rows past the end)
-    for (int e = tid; e < AS_TT * 16; e += AS_THREADS) {
-      const int t = e >> 4, c = e & 15;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (t0 + t < tend) v = *reinterpret_cast<const u32x4*>(K + (U.row0 + t0 + t) * D + c * 8);
-      S.tile[t * 16 + (c ^ (t & 15))] = v;
+    const bool more = t0 + AS_TT < tend;
+    if (more) fetch(t0 + AS_TT);  // the next tile's loads overlap this tile's MFMA work
+    if (tid < AS_TT) {
+      // |x| of token tid from the tile (chunk order does not matter for the norm)
+      float s2 = 0.f;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const u32x4 v = S.tile[tid * 16 + c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = bf16_lo(v[e]), b = bf16_hi(v[e]);
+          s2 = fmaf(a, a, s2);
+          s2 = fmaf(b, b, s2);
+        }
+      }
+      S.xn[tid] = sqrtf(s2);
     }
-    __syncthreads();
     Best run[AS_TT / 32];
 #pragma unroll
     for (int tb = 0; tb < AS_TT / 32; ++tb) { run[tb].b1 = -INFINITY; run[tb].b2 = -INFINITY; run[tb].i1 = 0x7FFFFFFF; }
@@ -358,7 +385,7 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint
       // worst-case fp32 accumulation bound); a gap within twice that may hide
       // an exact order different from the fp32 one.
       const float R2 = __uint_as_float(S.rmax);
-      const float margin = 0x1p-14f * (xnorm[row] * sqrtf(R2) + R2);
+      const float margin = 0x1p-14f * (S.xn[tid] * sqrtf(R2) + R2);
       assign[row] = U.cbase + bst.i1;
       if (bst.b1 - bst.b2 <= margin) {
         const int pos = atomicAdd(amb, 1);
@@ -367,29 +394,37 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint
       }
     }
     __syncthreads();
+    if (more) {
+      stash();
+      __syncthreads();
+    }
   }
 }
 
 // ------------------------------------------------------------------ k_assign_fix
 // Exact decision for the listed tokens: D_j = sum_i (x_i - c_j,i)^2 in binary64,
 // dims in order, each operation rounded (no fused multiply-add), argmin with
-// the lowest id on ties. One wave per token; lanes take centroids j = lane,
-// lane + 64, ...
-__global__ __launch_bounds__(256) void k_assign_fix(SeqArgs sa, const uint16_t* __restrict__ K,
-                                                    const uint16_t* __restrict__ chat,
-                                                    int32_t* __restrict__ assign, const int32_t* __restrict__ amb) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+// the lowest id on ties. One workgroup per token; thread t takes centroids
+// j = t, t + 256, ...
+constexpr int FIX_THREADS = 256;
+
+__global__ __launch_bounds__(FIX_THREADS) void k_assign_fix(SeqArgs sa, const uint16_t* __restrict__ K,
+                                                            const uint16_t* __restrict__ chat,
+                                                            int32_t* __restrict__ assign,
+                                                            const int32_t* __restrict__ amb) {
+  __shared__ double xs[D];
+  __shared__ double rb[FIX_THREADS / 64];
+  __shared__ int ri[FIX_THREADS / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int count = amb[0];
-  for (int item = blockIdx.x * 4 + wv; item < count; item += gridDim.x * 4) {
+  for (int item = blockIdx.x; item < count; item += gridDim.x) {
     const Unit U = unit_of(sa, amb[1 + 2 * item]);
-    const int t = amb[2 + 2 * item];
-    const int64_t row = U.row0 + t;
-    u32x4 xr[16];  // the whole key row in every lane
-#pragma unroll
-    for (int e = 0; e < 16; ++e) xr[e] = *reinterpret_cast<const u32x4*>(K + row * D + e * 8);
+    const int64_t row = U.row0 + amb[2 + 2 * item];
+    if (tid < D) xs[tid] = (double)bf16_to_f(K[row * D + tid]);
+    __syncthreads();
     double best = INFINITY;
     int bi = 0x7FFFFFFF;
-    for (int j = lane; j < U.Kc; j += 64) {
+    for (int j = tid; j < U.Kc; j += FIX_THREADS) {
       const u32x4* c = reinterpret_cast<const u32x4*>(chat + (U.gclu + j) * D);
       double acc = 0.0;
 #pragma unroll
@@ -397,9 +432,9 @@ __global__ __launch_bounds__(256) void k_assign_fix(SeqArgs sa, const uint16_t* 
         const u32x4 cv = c[e];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const double d0 = __dsub_rn((double)bf16_lo(xr[e][w]), (double)bf16_lo(cv[w]));
+          const double d0 = __dsub_rn(xs[8 * e + 2 * w], (double)bf16_lo(cv[w]));
           acc = __dadd_rn(acc, __dmul_rn(d0, d0));
-          const double d1 = __dsub_rn((double)bf16_hi(xr[e][w]), (double)bf16_hi(cv[w]));
+          const double d1 = __dsub_rn(xs[8 * e + 2 * w + 1], (double)bf16_hi(cv[w]));
           acc = __dadd_rn(acc, __dmul_rn(d1, d1));
         }
       }
@@ -411,7 +446,14 @@ __global__ __launch_bounds__(256) void k_assign_fix(SeqArgs sa, const uint16_t* 
       const int oi = __shfl_xor(bi, o, 64);
       if (ob < best || (ob == best && oi < bi)) { best = ob; bi = oi; }
     }
-    if (lane == 0) assign[row] = U.cbase + bi;
+    if (lane == 0) { rb[wv] = best; ri[wv] = bi; }
+    __syncthreads();
+    if (tid == 0) {
+      for (int w = 1; w < FIX_THREADS / 64; ++w)
+        if (rb[w] < best || (rb[w] == best && ri[w] < bi)) { best = rb[w]; bi = ri[w]; }
+      assign[row] = U.cbase + bi;
+    }
+    __syncthreads();
   }
 }
 
@@ -444,17 +486,20 @@ __global__ __launch_bounds__(SORT_THREADS) void k_sort(SeqArgs sa, const int32_t
     // the segment even if they were not
     const int c = valid ? min(max(assign[U.row0 + t] - U.cbase, 0), Kc - 1) : -1;
     uint64_t active = __ballot(valid);
-    int myrank = 0;
+    int myrank = 0, myleader = 0, old = 0;
     while (active) {
       const int leader = __ffsll((unsigned long long)active) - 1;
       const int v = __shfl(c, leader, 64);
-      const uint64_t same = __ballot(valid && c == v);
-      const int basecnt = hist[wv * Kc + v];
-      if (valid && c == v) myrank = basecnt + __popcll(same & ltmask);
-      if (lane == leader) hist[wv * Kc + v] = basecnt + __popcll(same);
+      const uint64_t same = __ballot(c == v);
+      if (c == v) {
+        myrank = __popcll(same & ltmask);
+        myleader = leader;
+      }
+      if (lane == leader) old = atomicAdd(&hist[wv * Kc + v], __popcll(same));
       active &= ~same;
     }
-    if (valid) rank[U.row0 + t] = myrank;
+    const int base = __shfl(old, myleader, 64);
+    if (valid) rank[U.row0 + t] = base + myrank;
   }
   __syncthreads();
   // per-cluster totals, per-wave bases, exclusive offsets over clusters
@@ -512,78 +557,78 @@ __global__ __launch_bounds__(SORT_THREADS) void k_sort(SeqArgs sa, const int32_t
 
 // ------------------------------------------------------------------ k_update
 // Ordered fp32 sums of the members' keys (ascending position), correctly
-// rounded division by the count; empty clusters keep their centroid. One
-// wave per cluster, 2 dims per lane.
+// rounded division by the count; empty clusters keep their centroid. One wave
+// per cluster, 2 dims per lane, members fetched 16 at a time (their positions
+// with one load, then 16 row loads in flight). Writes the bf16 centroid and its
+// squared norm. The last round (FINAL) also copies every member's K and V row
+// to its sorted slot, writes inv_perm and the ordered fp32 value sums.
+template <bool FINAL>
 __global__ __launch_bounds__(256) void k_update(SeqArgs sa, int64_t nclu, const uint16_t* __restrict__ K,
-                                                const int32_t* __restrict__ sizes,
-                                                const int32_t* __restrict__ offsets,
-                                                const int32_t* __restrict__ perm, float* __restrict__ cent) {
+                                                const uint16_t* __restrict__ V, wave_index ix,
+                                                float* __restrict__ norm, int32_t* __restrict__ amb) {
   const int64_t F = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
+  if (blockIdx.x == 0 && threadIdx.x == 0) amb[0] = 0;  // the next round's near-tie list
   if (F >= nclu) return;
-  const int n = sizes[F];
-  if (n == 0) return;
-  const CluRef cr = clu_of(sa, F);
-  const int off = offsets[cr.boff + cr.j];
-  const uint16_t* Kb = K + cr.brow * D + 2 * lane;
-  const int32_t* pb = perm + cr.brow + off;
-  float s0 = 0.f, s1 = 0.f;
-  int k = 0;
-  for (; k + 4 <= n; k += 4) {
-    uint32_t v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const uint32_t*>(Kb + (int64_t)pb[k + u] * D);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      s0 = __fadd_rn(s0, bf16_lo(v[u]));
-      s1 = __fadd_rn(s1, bf16_hi(v[u]));
-    }
-  }
-  for (; k < n; ++k) {
-    const uint32_t v = *reinterpret_cast<const uint32_t*>(Kb + (int64_t)pb[k] * D);
-    s0 = __fadd_rn(s0, bf16_lo(v));
-    s1 = __fadd_rn(s1, bf16_hi(v));
-  }
-  const float fn = (float)n;
-  float2 c;
-  c.x = __fdiv_rn(s0, fn);
-  c.y = __fdiv_rn(s1, fn);
-  *reinterpret_cast<float2*>(cent + F * D + 2 * lane) = c;
-}
-
-// ------------------------------------------------------------------ k_layout
-// Final layout of every cluster: K/V rows copied to their sorted slots,
-// inv_perm, ordered fp32 value sums, bf16 centroids. One wave per cluster.
-__global__ __launch_bounds__(256) void k_layout(SeqArgs sa, int64_t nclu, const uint16_t* __restrict__ K,
-                                                const uint16_t* __restrict__ V, wave_index ix) {
-  const int64_t F = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (F >= nclu) return;
-  const CluRef cr = clu_of(sa, F);
   const int n = ix.sizes[F];
-  const int off = ix.offsets[cr.boff + cr.j];
-  {
-    const float2 c = *reinterpret_cast<const float2*>(ix.centroids + F * D + 2 * lane);
-    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(ix.centroids_bf16) + F * D + 2 * lane) =
-        (uint32_t)f_to_bf16(c.x) | ((uint32_t)f_to_bf16(c.y) << 16);
+  if (n == 0) {
+    if (FINAL) *reinterpret_cast<float2*>(ix.vsum + F * D + 2 * lane) = make_float2(0.f, 0.f);
+    return;
   }
-  uint16_t* Ks = reinterpret_cast<uint16_t*>(ix.k_sorted) + cr.brow * D + 2 * lane;
-  uint16_t* Vs = reinterpret_cast<uint16_t*>(ix.v_sorted) + cr.brow * D + 2 * lane;
+  const CluRef cr = clu_of(sa, F);
+  const int off = ix.offsets[cr.boff + cr.j];
   const uint16_t* Kb = K + cr.brow * D + 2 * lane;
   const uint16_t* Vb = V + cr.brow * D + 2 * lane;
-  float s0 = 0.f, s1 = 0.f;
-  for (int k = 0; k < n; ++k) {
-    const int p = off + k;
-    const int t = ix.perm[cr.brow + p];
-    const uint32_t kv = *reinterpret_cast<const uint32_t*>(Kb + (int64_t)t * D);
-    const uint32_t vv = *reinterpret_cast<const uint32_t*>(Vb + (int64_t)t * D);
-    *reinterpret_cast<uint32_t*>(Ks + (int64_t)p * D) = kv;
-    *reinterpret_cast<uint32_t*>(Vs + (int64_t)p * D) = vv;
-    s0 = __fadd_rn(s0, bf16_lo(vv));
-    s1 = __fadd_rn(s1, bf16_hi(vv));
-    if (lane == 0) ix.inv_perm[cr.brow + t] = p;
+  uint16_t* Ks = reinterpret_cast<uint16_t*>(ix.k_sorted) + cr.brow * D + 2 * lane;
+  uint16_t* Vs = reinterpret_cast<uint16_t*>(ix.v_sorted) + cr.brow * D + 2 * lane;
+  const int32_t* pb = ix.perm + cr.brow + off;
+  float s0 = 0.f, s1 = 0.f, w0 = 0.f, w1 = 0.f;
+  for (int k0 = 0; k0 < n; k0 += 16) {
+    const int m = min(16, n - k0);
+    const int ptv = lane < m ? pb[k0 + lane] : 0;
+    // unconditional loads (clamped to the last member) keep all 16 in flight
+    uint32_t kr[16], vr[16];
+    int tt[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      tt[u] = __shfl(ptv, min(u, m - 1), 64);
+      kr[u] = *reinterpret_cast<const uint32_t*>(Kb + (int64_t)tt[u] * D);
+      if (FINAL) vr[u] = *reinterpret_cast<const uint32_t*>(Vb + (int64_t)tt[u] * D);
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const bool in = u < m;
+      s0 = in ? __fadd_rn(s0, bf16_lo(kr[u])) : s0;
+      s1 = in ? __fadd_rn(s1, bf16_hi(kr[u])) : s1;
+      if (FINAL) {
+        w0 = in ? __fadd_rn(w0, bf16_lo(vr[u])) : w0;
+        w1 = in ? __fadd_rn(w1, bf16_hi(vr[u])) : w1;
+      }
+    }
+    if (FINAL) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (u < m) {
+          const int p = off + k0 + u;
+          *reinterpret_cast<uint32_t*>(Ks + (int64_t)p * D) = kr[u];
+          *reinterpret_cast<uint32_t*>(Vs + (int64_t)p * D) = vr[u];
+          if (lane == 0) ix.inv_perm[cr.brow + tt[u]] = p;
+        }
+      }
+    }
   }
-  *reinterpret_cast<float2*>(ix.vsum + F * D + 2 * lane) = make_float2(s0, s1);
+  const float fn = (float)n;
+  const float c0 = __fdiv_rn(s0, fn), c1 = __fdiv_rn(s1, fn);
+  *reinterpret_cast<float2*>(ix.centroids + F * D + 2 * lane) = make_float2(c0, c1);
+  const uint16_t h0 = f_to_bf16(c0), h1 = f_to_bf16(c1);
+  *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(ix.centroids_bf16) + F * D + 2 * lane) =
+      (uint32_t)h0 | ((uint32_t)h1 << 16);
+  const float a = bf16_to_f(h0), b = bf16_to_f(h1);
+  float q2 = fmaf(a, a, b * b);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) q2 += xor_shfl(q2, o);
+  if (lane == 0) norm[F] = q2;
+  if (FINAL) *reinterpret_cast<float2*>(ix.vsum + F * D + 2 * lane) = make_float2(w0, w1);
 }
 
 // ------------------------------------------------------------------ host side
@@ -604,9 +649,12 @@ hipError_t launch_build(const SeqArgs& sa, const void* Kv, const void* Vv, int32
                         hipStream_t st) {
   static bool attrs = false;
   if (!attrs) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_init), hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_assign), hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(AssignLds));
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sort), hipFuncAttributeMaxDynamicSharedMemorySize, 16 * WAVE_MAX_CLUSTERS_PER_SEG * 4);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_init), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_assign), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              sizeof(AssignLds));
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sort), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              16 * WAVE_MAX_CLUSTERS_PER_SEG * 4);
     attrs = true;
   }
   const uint16_t* K = reinterpret_cast<const uint16_t*>(Kv);
@@ -618,19 +666,17 @@ hipError_t launch_build(const SeqArgs& sa, const void* Kv, const void* Vv, int32
   const unsigned cgrid = (unsigned)((nclu + 3) / 4);
   uint16_t* chat = reinterpret_cast<uint16_t*>(ix.centroids_bf16);
   prof_begin("k_init", st);
-  hipLaunchKernelGGL(k_init, dim3((unsigned)units), dim3(256), init_lds, st, sa, seed, K, ix.centroids, ws.xnorm);
+  hipLaunchKernelGGL(k_init, dim3((unsigned)units), dim3(INIT_THREADS), init_lds, st, sa, seed, K, ix.centroids, chat,
+                     ws.norm, ws.amb);
   prof_end(st);
   const int64_t agrid = assign_grid(sa);
   for (int it = 0; it < iters; ++it) {
-    prof_begin("k_round_norm", st);
-    hipLaunchKernelGGL(k_round_norm, dim3(cgrid), dim3(256), 0, st, nclu, ix.centroids, chat, ws.norm, ws.amb);
-    prof_end(st);
     prof_begin("k_assign", st);
-    hipLaunchKernelGGL(k_assign, dim3((unsigned)agrid), dim3(AS_THREADS), sizeof(AssignLds), st, sa, K, chat,
-                       ws.norm, ws.xnorm, ix.assign, ws.amb);
+    hipLaunchKernelGGL(k_assign, dim3((unsigned)agrid), dim3(AS_THREADS), sizeof(AssignLds), st, sa, K, chat, ws.norm,
+                       ix.assign, ws.amb);
     prof_end(st);
     prof_begin("k_assign_fix", st);
-    hipLaunchKernelGGL(k_assign_fix, dim3(1024), dim3(256), 0, st, sa, K, chat, ix.assign, ws.amb);
+    hipLaunchKernelGGL(k_assign_fix, dim3(512), dim3(FIX_THREADS), 0, st, sa, K, chat, ix.assign, ws.amb);
     prof_end(st);
     if (trace != nullptr) {
       hipError_t e = hipMemcpyAsync(trace + (int64_t)it * rows, ix.assign, sizeof(int32_t) * (size_t)rows,
@@ -642,13 +688,12 @@ hipError_t launch_build(const SeqArgs& sa, const void* Kv, const void* Vv, int32
                        ix.sizes, ix.offsets, ix.perm);
     prof_end(st);
     prof_begin("k_update", st);
-    hipLaunchKernelGGL(k_update, dim3(cgrid), dim3(256), 0, st, sa, nclu, K, ix.sizes, ix.offsets, ix.perm,
-                       ix.centroids);
+    if (it + 1 < iters)
+      hipLaunchKernelGGL(k_update<false>, dim3(cgrid), dim3(256), 0, st, sa, nclu, K, V, ix, ws.norm, ws.amb);
+    else
+      hipLaunchKernelGGL(k_update<true>, dim3(cgrid), dim3(256), 0, st, sa, nclu, K, V, ix, ws.norm, ws.amb);
     prof_end(st);
   }
-  prof_begin("k_layout", st);
-  hipLaunchKernelGGL(k_layout, dim3(cgrid), dim3(256), 0, st, sa, nclu, K, V, ix);
-  prof_end(st);
   return hipGetLastError();
 }
 

@@ -84,14 +84,13 @@ void index_sizes(const wave::SeqArgs& sa, wave_index_sizes* o) {
 }
 
 struct BuildLayout {
-  size_t norm, xnorm, amb, rank, total;
+  size_t norm, amb, rank, total;
 };
 
 BuildLayout build_layout(const wave_index_sizes& z) {
   BuildLayout L;
   size_t o = 0;
   L.norm = o;  o += align256(sizeof(float) * (size_t)z.clusters);
-  L.xnorm = o; o += align256(sizeof(float) * (size_t)z.rows);
   L.amb = o;   o += align256(sizeof(int32_t) * (size_t)(1 + 2 * z.rows));
   L.rank = o;  o += align256(sizeof(int32_t) * (size_t)z.rows);
   L.total = o;
@@ -108,7 +107,7 @@ wave_status hip_device_ok() {
 // ------------------------------------------------------------------ decode sizes
 struct DecodePlan {
   wave::DecodeArgs da;
-  size_t keys, key32, selid, selpre, excl, rows, corr, counts, part, sortg, total;
+  size_t keys, key32, span, selpre, excl, corr, counts, part, sortg, total;
 };
 
 wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t n_local, double frac,
@@ -132,7 +131,7 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
   da.n_local = n_local;
   da.tau = (float)(1.0 / sqrt((double)WAVE_HEAD_DIM));
   int kmax = 0, Cmax = 0, nEmax = 0;
-  int64_t Nmax = 0, sumC = 0, sumC1 = 0, sumW = 0, sumN = 0;
+  int64_t sumC = 0, sumW = 0;
   for (int b = 0; b < sa.B; ++b) {
     const int64_t N = sa.N[b], C = sa.C[b];
     double x = ceil(frac * (double)C);
@@ -141,13 +140,10 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
     da.kreq[b] = (int32_t)x;
     kmax = da.kreq[b] > kmax ? da.kreq[b] : kmax;
     Cmax = C > Cmax ? (int)C : Cmax;
-    Nmax = N > Nmax ? N : Nmax;
     const int nE = (int)((C + wave::DEC_EST_CH - 1) / wave::DEC_EST_CH);
     nEmax = nE > nEmax ? nE : nEmax;
     sumC += C;
-    sumC1 += C + 1;
     sumW += (C + 31) / 32;
-    sumN += N;
     const int64_t a = n_sink < N ? n_sink : N;
     const int64_t c = (N - n_local) > a ? (N - n_local) : a;
     const int64_t nS = a + (N - c);
@@ -156,18 +152,27 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
                   (long long)nS, WAVE_MAX_STEADY);
   }
   da.k_max = kmax;
-  const int64_t steady_req = (int64_t)n_sink + (int64_t)n_local;
-  da.scap = (int32_t)(steady_req < Nmax ? steady_req : Nmax);
-  if (da.scap < 1) da.scap = 1;
-  // retrieval workgroups per (b, h): about 256 gathered rows each
+  int64_t nSmax = 0;
+  for (int b = 0; b < sa.B; ++b) {
+    const int64_t N = sa.N[b];
+    const int64_t a = n_sink < N ? n_sink : N;
+    const int64_t c = (N - n_local) > a ? (N - n_local) : a;
+    const int64_t nS = a + (N - c);
+    nSmax = nS > nSmax ? nS : nSmax;
+  }
+  da.scap = (int32_t)(nSmax > 0 ? nSmax : 1);
+  // gathered-row workgroups per (b, h): about DEC_ROWS_PER_WG rows each at the
+  // average cluster size
   const int64_t avg = (ix->seg_len + ix->clusters_per_seg - 1) / ix->clusters_per_seg;
-  int64_t est = (int64_t)kmax * avg + da.scap;
-  if (est > Nmax) est = Nmax;
-  int64_t Pw = (est + 255) / 256;
+  int64_t est = (int64_t)kmax * avg + nSmax;
+  int64_t Pw = (est + wave::DEC_ROWS_PER_WG - 1) / wave::DEC_ROWS_PER_WG;
   if (Pw < 1) Pw = 1;
-  if (Pw > 2048) Pw = 2048;
+  if (Pw > 4096) Pw = 4096;
   da.P = (int32_t)Pw;
   da.NP = da.P + nEmax;
+  da.NV = 0;
+  for (int nv = 4; nv <= 64; nv *= 2)
+    if (16 * 64 * nv >= Cmax) { da.NV = nv; break; }
   int sort_stride = 0;
   if (kmax > wave::DEC_SORT_LDS) {
     sort_stride = 1;
@@ -178,12 +183,11 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
   size_t o = 0;
   P->keys = o;   o += align256(4 * (size_t)(H * sumC));
   P->key32 = o;  o += align256(4 * (size_t)(H * sumC));
-  P->selid = o;  o += align256(4 * (size_t)(H * sumC));
-  P->selpre = o; o += align256(4 * (size_t)(H * sumC1));
+  P->span = o;   o += align256(8 * (size_t)(H * sumC));
+  P->selpre = o; o += align256(4 * (size_t)(H * sumC + BH));
   P->excl = o;   o += align256(4 * (size_t)(H * sumW));
-  P->rows = o;   o += align256(4 * (size_t)(H * sumN));
   P->corr = o;   o += align256(4 * (size_t)(BH * da.scap));
-  P->counts = o; o += align256(4 * (size_t)(BH * 2));
+  P->counts = o; o += align256(4 * (size_t)(BH * 4));
   P->part = o;   o += align256(4 * (size_t)(BH * da.NP * wave::DEC_PART));
   P->sortg = o;  o += align256(8 * (size_t)(BH * sort_stride));
   P->total = o;
@@ -271,7 +275,6 @@ wave_status wave_index_build(const wave_shape* shape, const void* K, const void*
   uint8_t* w = reinterpret_cast<uint8_t*>(ws);
   wave::BuildWs bw;
   bw.norm = reinterpret_cast<float*>(w + L.norm);
-  bw.xnorm = reinterpret_cast<float*>(w + L.xnorm);
   bw.amb = reinterpret_cast<int32_t*>(w + L.amb);
   bw.rank = reinterpret_cast<int32_t*>(w + L.rank);
   hipError_t e = wave::launch_build(sa, K, V, iters, seed, *out, bw, z.units, assign_trace, z.rows,
@@ -315,10 +318,9 @@ wave_status wave_attn_decode(const wave_index* index, const void* q, int32_t n_q
   wave::DecodeWs dw;
   dw.keys = reinterpret_cast<float*>(w + P.keys);
   dw.key32 = reinterpret_cast<uint32_t*>(w + P.key32);
-  dw.selid = reinterpret_cast<int32_t*>(w + P.selid);
+  dw.span = reinterpret_cast<int2*>(w + P.span);
   dw.selpre = reinterpret_cast<int32_t*>(w + P.selpre);
   dw.excl = reinterpret_cast<uint32_t*>(w + P.excl);
-  dw.rows = reinterpret_cast<int32_t*>(w + P.rows);
   dw.corr = reinterpret_cast<float*>(w + P.corr);
   dw.counts = reinterpret_cast<int32_t*>(w + P.counts);
   dw.part = reinterpret_cast<float*>(w + P.part);
