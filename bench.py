@@ -42,6 +42,15 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the oracle timing sample")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a device copy of 1 GiB (scale of the HBM byte counters)")
+    p.add_argument("--eager", action="store_true",
+                   help="time eager launches instead of graph replays (for counter collection)")
+    p.add_argument("--summarize-trace", metavar="DIR",
+                   help="print the per-kernel table of a rocprofv3 --kernel-trace --stats csv run and exit")
+    p.add_argument("--summarize-traffic", nargs=5, metavar=("KERNEL", "FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR",
+                                                            "CAL_WRITE_DIR"),
+                   help="print HBM bytes per launch of KERNEL from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv "
+                        "runs of the benchmark and of --calibrate-copy, and exit")
+    p.add_argument("--command", default="", help="command line recorded in a summary")
     return p.parse_args()
 
 
@@ -71,8 +80,85 @@ def counter_traffic(kernel, sha):
         return None
 
 
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit("no *%s under %s" % (suffix, d))
+    return rows
+
+
+def _short(name):
+    """wave::k_attend<4>(...) -> k_attend<4>; other kernels keep 60 characters."""
+    base = name.split("(")[0].replace("void ", "").strip()
+    return base.split("::")[-1] if "wave::" in base else base[:60]
+
+
+def summarize_trace(d, command):
+    rows = _csv_rows(d, "kernel_stats.csv")
+    out = ["# rocprofv3 kernel statistics", "command: %s" % command, "",
+           "%-28s %8s %12s %12s %12s %12s %7s" % ("kernel", "calls", "total_us", "avg_us", "min_us", "max_us", "pct")]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        out.append("%-28s %8d %12.1f %12.2f %12.2f %12.2f %7.2f" % (
+            _short(r["Name"]), int(r["Calls"]), float(r["TotalDurationNs"]) / 1e3, float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    print("\n".join(out))
+
+
+def _counter_per_dispatch(d, counter, kernel=None):
+    """Per-dispatch values of one counter; the kernel's dispatches, or the largest one."""
+    vals = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        key = (r["Dispatch_Id"], r["Kernel_Name"])
+        vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+    if kernel is None:
+        return [max(vals.values())]
+    return [v for (_, n), v in vals.items() if _short(n).split("<")[0] == kernel]
+
+
+def summarize_traffic(kernel, fdir, wdir, cfdir, cwdir, command):
+    n_cal = 1 << 30
+    cf = _counter_per_dispatch(cfdir, "FETCH_SIZE")[0] * 1024.0
+    cw = _counter_per_dispatch(cwdir, "WRITE_SIZE")[0] * 1024.0
+    f = _counter_per_dispatch(fdir, "FETCH_SIZE", kernel)
+    w = _counter_per_dispatch(wdir, "WRITE_SIZE", kernel)
+    if not f or not w:
+        raise SystemExit("no dispatch of %s in the counter runs" % kernel)
+    fs, ws_ = n_cal / cf, n_cal / cw
+    fb = sum(f) / len(f) * 1024.0 * fs
+    wb = sum(w) / len(w) * 1024.0 * ws_
+    sha = source_sha(SOURCES)
+    print("\n".join([
+        "# HBM traffic of %s per launch (rocprofv3 --pmc, TCC counters in KiB per dispatch)" % kernel,
+        "command: %s" % command,
+        "calibration: a device copy of %d bytes read FETCH_SIZE %.0f B (scale %.4f), WRITE_SIZE %.0f B (scale %.4f)"
+        % (n_cal, cf, fs, cw, ws_),
+        "dispatches: %d fetch, %d write" % (len(f), len(w)),
+        "fetch_bytes_per_launch: %.0f" % fb,
+        "write_bytes_per_launch: %.0f" % wb,
+        "hbm_bytes_per_launch: %.0f" % (fb + wb),
+        "source_sha: %s" % sha]))
+
+
+SOURCES = ["retrieval_sparse_attention_amd/csrc/decode.hip", "retrieval_sparse_attention_amd/csrc/build.hip",
+           "retrieval_sparse_attention_amd/csrc/common.h", "retrieval_sparse_attention_amd/csrc/internal.h",
+           "retrieval_sparse_attention_amd/csrc/wave_attn.hip"]
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.command)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, command=args.command)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU: this build has no multi-GPU path (the kv-head sharding it "
               "would use is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
@@ -87,12 +173,12 @@ def main():
     torch.cuda.set_device(dev)
     if args.calibrate_copy:
         n = 1 << 30
-        x = torch.empty(n, dtype=torch.uint8, device=dev)
+        # an elementwise kernel that reads and writes n bytes once (fp32 negation)
+        x = torch.ones(n // 4, dtype=torch.float32, device=dev)
         y = torch.empty_like(x)
-        x.fill_(1)
         torch.cuda.synchronize()
         for _ in range(3):
-            y.copy_(x)
+            torch.neg(x, out=y)
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "launches": 3}))
         return
@@ -143,31 +229,39 @@ def main():
 
     # the step pattern repeats with period P: one captured HIP graph per phase
     P = math.lcm(L, max(1, nq // math.gcd(nq, QPS)))
-    print("warmup (eager) and capture of %d step graphs" % P, file=sys.stderr, flush=True)
+    print("warmup (eager)%s" % ("" if args.eager else " and capture of %d step graphs" % P), file=sys.stderr,
+          flush=True)
     for i in range(max(1, args.warmup)):
         job(i)
     torch.cuda.synchronize()
     graphs, dgraphs = [], []
-    for ph in range(P):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            job(ph)
-        graphs.append(g)
-        g2 = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g2):
-            job(ph, build=False)
-        dgraphs.append(g2)
+    if not args.eager:
+        for ph in range(P):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                job(ph)
+            graphs.append(g)
+            g2 = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g2):
+                job(ph, build=False)
+            dgraphs.append(g2)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % P].replay()
     torch.cuda.synchronize()
-    for i in range(args.warmup):
-        graphs[i % P].replay()
-    torch.cuda.synchronize()
+
+    def run(i, build=True):
+        if args.eager:
+            job(i, build=build)
+        else:
+            (graphs if build else dgraphs)[i % P].replay()
 
     # ---- timed region: K whole-job steps (graph replays on the current stream)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
     for i in range(args.warmup, args.warmup + args.steps):
-        graphs[i % P].replay()
+        run(i)
     e1.record()
     torch.cuda.synchronize()
     t_plain = e0.elapsed_time(e1)
@@ -175,7 +269,7 @@ def main():
     # decode queries alone (same 64 per step, no build)
     e0.record()
     for i in range(args.warmup, args.warmup + args.steps):
-        dgraphs[i % P].replay()
+        run(i, build=False)
     e1.record()
     torch.cuda.synchronize()
     t_dec = e0.elapsed_time(e1)
@@ -220,8 +314,7 @@ def main():
     kern = {}
     for name, (cnt, ms) in prof.items():
         kern[name] = {"launches": cnt, "avg_us": 1000.0 * ms / cnt, "total_ms": ms}
-    sha = source_sha(["retrieval_sparse_attention_amd/csrc/decode.hip", "retrieval_sparse_attention_amd/csrc/build.hip",
-                      "retrieval_sparse_attention_amd/csrc/common.h"])
+    sha = source_sha(SOURCES)
     dom = max(kern, key=lambda k: kern[k]["total_ms"])
     if dom == "k_assign":
         ach = assign_flops / (kern[dom]["avg_us"] * 1e-6) / 1e12
@@ -272,6 +365,7 @@ def main():
         "decode_only_effective_GBs": round(step_bytes * decodes / (t_dec / 1000.0) / 1e9, 1),
         "decode_bytes_per_query": int(step_bytes),
         "build_tokens_per_s": round(args.steps * B * N / (build_ms / 1000.0), 1),
+        "timing": "eager launches" if args.eager else "HIP graph replays",
         "eager_with_kernel_events_ms_per_step": round(t_ms / args.steps, 4),
         "kernels": {k: {"launches": v["launches"], "avg_us": round(v["avg_us"], 2)} for k, v in kern.items()},
         "kernel_roofline": extra,

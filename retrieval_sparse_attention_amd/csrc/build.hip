@@ -179,11 +179,19 @@ __global__ __launch_bounds__(INIT_THREADS) void k_init(SeqArgs sa, uint64_t seed
 // v_mfma_f32_32x32x16_bf16: every wave keeps 64 centroid rows (two 32-row A
 // tiles, all 128 dims) in registers; token tiles (B operand) stream through
 // LDS; the accumulator starts at -|c_j|^2/2. A lane of the 32x32 result holds
-// one token (column) and 16 centroid rows, so the running best, its id and the
-// second best are kept per lane and merged across the two half-waves and the
-// 8 waves. When the fp32 gap between best and second best is within twice
-// the bound on the fp32 error of f, the token is sent to the exact binary64
-// decision (k_assign_fix).
+// one token (column) and 16 centroid rows of each A tile.
+//
+// Selection per lane: the 5-bit position of each of its 32 values is written
+// into the value's low mantissa bits, so the best and second best of the 32
+// come from max3/med3 over triples (about 2.7 VALU operations per value) and the
+// best's position is read back from its bits. The packing moves a value by less
+// than 2^-18 |f|. The running best, its id and the second best are then merged
+// across the two half-waves and the 8 waves. When the gap between best and
+// second best is within 2^-14 (|x| R + R^2), R = max_j |c_j|, plus 2^-100 for
+// denormal flushing, the token goes to the exact binary64 decision
+// (k_assign_fix): that margin is more than twice the fp32 accumulation error of
+// a 128-term dot product and a norm (each below 2^-17 of those magnitudes) plus
+// the packing error, so every token not sent there has the exact argmin.
 constexpr int AS_WAVES = 8;
 constexpr int AS_THREADS = AS_WAVES * 64;
 constexpr int AS_TT = 128;     // tokens per LDS tile
@@ -236,6 +244,11 @@ __device__ inline void assign_wg_map(const SeqArgs& sa, int w, Unit& U, int& tok
   }
 }
 
+// value with its position p (0..31) in the low 5 mantissa bits
+__device__ __forceinline__ float pack5(float v, int p) {
+  return __uint_as_float((__float_as_uint(v) & ~31u) | (unsigned)p);
+}
+
 __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint16_t* __restrict__ K,
                                                           const uint16_t* __restrict__ chat,
                                                           const float* __restrict__ norm,
@@ -247,7 +260,8 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint
   assign_wg_map(sa, blockIdx.x, U, tb0);
   const int tend = min(tb0 + AS_TPW, U.L);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, h = lane >> 5, col = lane & 31;
-  // the first token tile in flight: AS_TT rows x 16 chunks, 4 chunks per thread
+  // the next token tile in flight: AS_TT rows x 16 chunks, 4 chunks per thread;
+  // chunk m of this thread is chunk (tid & 15) of tile row (tid >> 4) + 32 m
   constexpr int PF = AS_TT * 16 / AS_THREADS;
   u32x4 pre[PF];
   auto fetch = [&](int t0) {
@@ -255,16 +269,30 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint
     for (int m = 0; m < PF; ++m) {
       const int e = tid + m * AS_THREADS;
       const int t = e >> 4, c = e & 15;
-      pre[m] = (t0 + t < tend) ? *reinterpret_cast<const u32x4*>(K + (U.row0 + t0 + t) * D + c * 8)
-                               : u32x4{0u, 0u, 0u, 0u};
+      const int tt = min(t0 + t, tend - 1);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(K + (U.row0 + tt) * D + c * 8);
+      pre[m] = (t0 + t < tend) ? v : u32x4{0u, 0u, 0u, 0u};
     }
   };
+  // store the tile and the norms of its tokens (16 lanes hold one row)
   auto stash = [&]() {
 #pragma unroll
     for (int m = 0; m < PF; ++m) {
       const int e = tid + m * AS_THREADS;
       const int t = e >> 4, c = e & 15;
       S.tile[t * 16 + (c ^ (t & 15))] = pre[m];
+      float s2 = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float a = bf16_lo(pre[m][q]), b = bf16_hi(pre[m][q]);
+        s2 = fmaf(a, a, s2);
+        s2 = fmaf(b, b, s2);
+      }
+      s2 += xor_shfl(s2, 8);
+      s2 += xor_shfl(s2, 4);
+      s2 += xor_shfl(s2, 2);
+      s2 += xor_shfl(s2, 1);
+      if (c == 0) S.xn[t] = sqrtf(s2);
     }
   };
   fetch(tb0);
@@ -284,16 +312,18 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int row = cb + r * 32 + col;
+      const int rc = min(row, U.Kc - 1);
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (row < U.Kc) v = *reinterpret_cast<const u32x4*>(chat + (U.gclu + row) * D + (2 * st + h) * 8);
-        A[r][st] = __builtin_bit_cast(bf16x8_t, v);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(chat + (U.gclu + rc) * D + (2 * st + h) * 8);
+        A[r][st] = __builtin_bit_cast(bf16x8_t, row < U.Kc ? v : u32x4{0u, 0u, 0u, 0u});
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int rr = cb + r * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        nh[r][i] = rr < U.Kc ? -0.5f * norm[U.gclu + rr] : -INFINITY;
+        const float nv = norm[U.gclu + min(rr, U.Kc - 1)];
+        // rows past the unit's clusters: a finite floor that every real value beats
+        nh[r][i] = rr < U.Kc ? -0.5f * nv : -__FLT_MAX__;
       }
     }
   };
@@ -303,24 +333,6 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint
   for (int t0 = tb0; t0 < tend; t0 += AS_TT) {
     const bool more = t0 + AS_TT < tend;
     if (more) fetch(t0 + AS_TT);  // the next tile's loads overlap this tile's MFMA work
-    if (tid < AS_TT) {
-      // |x| of token tid from the tile (chunk order does not matter for the norm)
-      float s2 = 0.f;
-#pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        const u32x4 v = S.tile[tid * 16 + c];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float a = bf16_lo(v[e]), b = bf16_hi(v[e]);
-          s2 = fmaf(a, a, s2);
-          s2 = fmaf(b, b, s2);
-        }
-      }
-      S.xn[tid] = sqrtf(s2);
-    }
-    Best run[AS_TT / 32];
-#pragma unroll
-    for (int tb = 0; tb < AS_TT / 32; ++tb) { run[tb].b1 = -INFINITY; run[tb].b2 = -INFINITY; run[tb].i1 = 0x7FFFFFFF; }
     for (int grp = 0; grp < ngroups; ++grp) {
       if (ngroups > 1) load_group(grp);
       const int cb = grp * AS_GROUP + wv * 64;
@@ -336,35 +348,47 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint
           for (int r = 0; r < 2; ++r)
             acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[r][st], Bv, st == 0 ? nh[r] : acc[r], 0, 0, 0);
         }
-        Best bs;
-        bs.b1 = -INFINITY;
-        bs.b2 = -INFINITY;
-        bs.i1 = 0x7FFFFFFF;
+        float v[32];
 #pragma unroll
         for (int r = 0; r < 2; ++r)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float v = acc[r][i];
-            const int j = cb + r * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-            const bool gt = v > bs.b1;
-            bs.b2 = __builtin_amdgcn_fmed3f(v, bs.b1, bs.b2);
-            bs.i1 = gt ? j : bs.i1;
-            bs.b1 = fmaxf(bs.b1, v);
-          }
+          for (int i = 0; i < 16; ++i) v[16 * r + i] = pack5(acc[r][i], 16 * r + i);
+        float b1 = -INFINITY, b2 = -INFINITY;
+#pragma unroll
+        for (int k3 = 0; k3 < 10; ++k3) {
+          const float x = v[3 * k3], y = v[3 * k3 + 1], z = v[3 * k3 + 2];
+          const float m = fmaxf(fmaxf(x, y), z), md = __builtin_amdgcn_fmed3f(x, y, z);
+          b2 = fmaxf(md, __builtin_amdgcn_fmed3f(m, b1, b2));
+          b1 = fmaxf(b1, m);
+        }
+        {
+          const float hi = fmaxf(v[30], v[31]), lo = fminf(v[30], v[31]);
+          b2 = fmaxf(lo, __builtin_amdgcn_fmed3f(hi, b1, b2));
+          b1 = fmaxf(b1, hi);
+        }
+        const int p = (int)(__float_as_uint(b1) & 31u);
+        Best bs;
+        bs.b1 = b1;
+        bs.b2 = b2;
+        bs.i1 = cb + (p >> 4) * 32 + 8 * ((p & 15) >> 2) + 4 * h + (p & 3);
         Best o;
         o.b1 = xor_shfl(bs.b1, 32);
         o.b2 = xor_shfl(bs.b2, 32);
         o.i1 = xor_shfl(bs.i1, 32);
         best_merge(bs, o);
-        best_merge(run[tb], bs);
-      }
-    }
-    if (h == 0) {
-#pragma unroll
-      for (int tb = 0; tb < AS_TT / 32; ++tb) {
-        S.red[wv][tb * 32 + col][0] = run[tb].b1;
-        S.red[wv][tb * 32 + col][1] = __int_as_float(run[tb].i1);
-        S.red[wv][tb * 32 + col][2] = run[tb].b2;
+        if (h == 0) {
+          float* rd = S.red[wv][t];
+          if (grp > 0) {
+            Best prev;
+            prev.b1 = rd[0];
+            prev.i1 = __float_as_int(rd[1]);
+            prev.b2 = rd[2];
+            best_merge(bs, prev);
+          }
+          rd[0] = bs.b1;
+          rd[1] = __int_as_float(bs.i1);
+          rd[2] = bs.b2;
+        }
       }
     }
     __syncthreads();
@@ -381,13 +405,11 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint
         best_merge(bst, o);
       }
       const int64_t row = U.row0 + t0 + tid;
-      // |f~ - f| <= 2^-15 (|x| R + R^2) with R = max |c_j| (many times the
-      // worst-case fp32 accumulation bound); a gap within twice that may hide
-      // an exact order different from the fp32 one.
       const float R2 = __uint_as_float(S.rmax);
-      const float margin = 0x1p-14f * (S.xn[tid] * sqrtf(R2) + R2);
+      const float margin = 0x1p-14f * (S.xn[tid] * sqrtf(R2) + R2) + 0x1p-100f;
       assign[row] = U.cbase + bst.i1;
-      if (bst.b1 - bst.b2 <= margin) {
+      // also undecided: a best at the floor of the padding rows (values beyond fp32 range)
+      if (!(bst.b1 - bst.b2 > margin) || !(bst.b1 > -0x1p127f)) {
         const int pos = atomicAdd(amb, 1);
         amb[1 + 2 * pos] = (int32_t)U.u;
         amb[2 + 2 * pos] = t0 + tid;
