@@ -198,10 +198,13 @@ constexpr int AS_TT = 128;     // tokens per LDS tile
 constexpr int AS_TPW = 1024;   // tokens per workgroup
 constexpr int AS_GROUP = AS_WAVES * 64;  // centroids per pass
 
+// Token tiles are double buffered and loaded straight into LDS (global_load_lds,
+// 16 bytes per lane); one barrier per tile. The reduction over the 8 waves of
+// tile T runs in waves 0-1 while every wave already works on tile T + 1.
 struct AssignLds {
-  u32x4 tile[AS_TT * 16];           // token rows, 16-byte chunk c of row t stored at chunk c ^ (t & 15)
-  float red[AS_WAVES][AS_TT][3];    // per wave: best, id (bits), second best
-  float xn[AS_TT];                  // |x| of the tile's tokens
+  u32x4 tile[2][AS_TT * 16];        // token rows, 16-byte chunk c of row t stored at slot t*16 + (c ^ (t & 15))
+  float red[2][AS_WAVES][AS_TT][3]; // per tile buffer and wave: best, id (bits), second best
+  float xnp[2][2][AS_TT];           // per tile buffer: two halves of |x|^2
   unsigned int rmax;                // max |c_j|^2 of the unit (float bits)
 };
 
@@ -259,43 +262,25 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint
   int tb0;
   assign_wg_map(sa, blockIdx.x, U, tb0);
   const int tend = min(tb0 + AS_TPW, U.L);
+  const int ntiles = (tend - tb0 + AS_TT - 1) / AS_TT;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, h = lane >> 5, col = lane & 31;
-  // the next token tile in flight: AS_TT rows x 16 chunks, 4 chunks per thread;
-  // chunk m of this thread is chunk (tid & 15) of tile row (tid >> 4) + 32 m
-  constexpr int PF = AS_TT * 16 / AS_THREADS;
-  u32x4 pre[PF];
-  auto fetch = [&](int t0) {
+  // tile T -> buffer T & 1: wave wv fills slots [(4 wv + m) * 64, +64), m < 4; lane i of a
+  // load writes slot base + i, i.e. token t = slot / 16, chunk (slot % 16) ^ (t % 16).
+  // Rows past the segment end repeat its last row; their results are never stored.
+  auto issue = [&](int T) {
+    const int t0 = tb0 + T * AS_TT;
 #pragma unroll
-    for (int m = 0; m < PF; ++m) {
-      const int e = tid + m * AS_THREADS;
-      const int t = e >> 4, c = e & 15;
+    for (int m = 0; m < 4; ++m) {
+      const int s0 = (wv * 4 + m) * 64;
+      const int slot = s0 + lane;
+      const int t = slot >> 4, c = (slot & 15) ^ (t & 15);
       const int tt = min(t0 + t, tend - 1);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(K + (U.row0 + tt) * D + c * 8);
-      pre[m] = (t0 + t < tend) ? v : u32x4{0u, 0u, 0u, 0u};
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(K + (U.row0 + tt) * D + c * 8),
+          (__attribute__((address_space(3))) void*)(&S.tile[T & 1][s0]), 16, 0, 0);
     }
   };
-  // store the tile and the norms of its tokens (16 lanes hold one row)
-  auto stash = [&]() {
-#pragma unroll
-    for (int m = 0; m < PF; ++m) {
-      const int e = tid + m * AS_THREADS;
-      const int t = e >> 4, c = e & 15;
-      S.tile[t * 16 + (c ^ (t & 15))] = pre[m];
-      float s2 = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float a = bf16_lo(pre[m][q]), b = bf16_hi(pre[m][q]);
-        s2 = fmaf(a, a, s2);
-        s2 = fmaf(b, b, s2);
-      }
-      s2 += xor_shfl(s2, 8);
-      s2 += xor_shfl(s2, 4);
-      s2 += xor_shfl(s2, 2);
-      s2 += xor_shfl(s2, 1);
-      if (c == 0) S.xn[t] = sqrtf(s2);
-    }
-  };
-  fetch(tb0);
+  issue(0);
   // largest squared centroid norm of the unit (all norms are >= 0)
   if (tid == 0) S.rmax = 0u;
   __syncthreads();
@@ -328,26 +313,78 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint
     }
   };
   if (ngroups == 1) load_group(0);
-  stash();
-  __syncthreads();
-  for (int t0 = tb0; t0 < tend; t0 += AS_TT) {
-    const bool more = t0 + AS_TT < tend;
-    if (more) fetch(t0 + AS_TT);  // the next tile's loads overlap this tile's MFMA work
+  // the 128 tokens of tile T: merge the 8 waves, decide or defer, store
+  auto reduce = [&](int T) {
+    const int t0 = tb0 + T * AS_TT;
+    if (tid < AS_TT && t0 + tid < tend) {
+      const int bi = T & 1;
+      Best bst;
+      bst.b1 = S.red[bi][0][tid][0];
+      bst.i1 = __float_as_int(S.red[bi][0][tid][1]);
+      bst.b2 = S.red[bi][0][tid][2];
+      for (int w2 = 1; w2 < AS_WAVES; ++w2) {
+        Best o;
+        o.b1 = S.red[bi][w2][tid][0];
+        o.i1 = __float_as_int(S.red[bi][w2][tid][1]);
+        o.b2 = S.red[bi][w2][tid][2];
+        best_merge(bst, o);
+      }
+      const int64_t row = U.row0 + t0 + tid;
+      const float R2 = __uint_as_float(S.rmax);
+      const float xn = sqrtf(S.xnp[bi][0][tid] + S.xnp[bi][1][tid]);
+      const float margin = 0x1p-14f * (xn * sqrtf(R2) + R2) + 0x1p-100f;
+      assign[row] = U.cbase + bst.i1;
+      // also undecided: a best at the floor of the padding rows (values beyond fp32 range)
+      if (!(bst.b1 - bst.b2 > margin) || !(bst.b1 > -0x1p127f)) {
+        const int pos = atomicAdd(amb, 1);
+        amb[1 + 2 * pos] = (int32_t)U.u;
+        amb[2 + 2 * pos] = t0 + tid;
+      }
+    }
+  };
+  // |x|^2 of 32-token block (wv & 3) of a tile, half (wv >> 2) of the dims, from the B fragments
+  const int xtb = wv & 3, xhalf = wv >> 2;
+  for (int T = 0; T < ntiles; ++T) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of tile T have landed
+    __syncthreads();  // tile T is in LDS; red[(T - 1) & 1] is complete
+    if (T + 1 < ntiles) issue(T + 1);  // into the buffer of tile T - 1, which every wave has finished
+    if (T > 0) reduce(T - 1);
+    const int bi = T & 1;
+    const u32x4* tl = S.tile[bi];
     for (int grp = 0; grp < ngroups; ++grp) {
       if (ngroups > 1) load_group(grp);
       const int cb = grp * AS_GROUP + wv * 64;
-#pragma unroll 1
+#pragma unroll 2
       for (int tb = 0; tb < AS_TT / 32; ++tb) {
-        floatx16 acc[2];
         const int t = tb * 32 + col;
+        bf16x8_t Bv[8];
 #pragma unroll
-        for (int st = 0; st < 8; ++st) {
-          const int c = 2 * st + h;
-          const bf16x8_t Bv = __builtin_bit_cast(bf16x8_t, S.tile[t * 16 + (c ^ (t & 15))]);
+        for (int st = 0; st < 8; ++st) Bv[st] = __builtin_bit_cast(bf16x8_t, tl[t * 16 + ((2 * st + h) ^ (t & 15))]);
+        if (grp == 0 && tb == xtb) {
+          float s2 = 0.f;
+          auto sq = [&](const bf16x8_t& f) {
+            const u32x4 w = __builtin_bit_cast(u32x4, f);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float a = bf16_lo(w[e]), b = bf16_hi(w[e]);
+              s2 = fmaf(a, a, s2);
+              s2 = fmaf(b, b, s2);
+            }
+          };
+          if (xhalf == 0) {
+            sq(Bv[0]); sq(Bv[1]); sq(Bv[2]); sq(Bv[3]);
+          } else {
+            sq(Bv[4]); sq(Bv[5]); sq(Bv[6]); sq(Bv[7]);
+          }
+          s2 += xor_shfl(s2, 32);
+          if (h == 0) S.xnp[bi][xhalf][t] = s2;
+        }
+        floatx16 acc[2];
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
 #pragma unroll
           for (int r = 0; r < 2; ++r)
-            acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[r][st], Bv, st == 0 ? nh[r] : acc[r], 0, 0, 0);
-        }
+            acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[r][st], Bv[st], st == 0 ? nh[r] : acc[r], 0, 0, 0);
         float v[32];
 #pragma unroll
         for (int r = 0; r < 2; ++r)
@@ -377,7 +414,7 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint
         o.i1 = xor_shfl(bs.i1, 32);
         best_merge(bs, o);
         if (h == 0) {
-          float* rd = S.red[wv][t];
+          float* rd = S.red[bi][wv][t];
           if (grp > 0) {
             Best prev;
             prev.b1 = rd[0];
@@ -391,36 +428,9 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint
         }
       }
     }
-    __syncthreads();
-    if (tid < AS_TT && t0 + tid < tend) {
-      Best bst;
-      bst.b1 = S.red[0][tid][0];
-      bst.i1 = __float_as_int(S.red[0][tid][1]);
-      bst.b2 = S.red[0][tid][2];
-      for (int w2 = 1; w2 < AS_WAVES; ++w2) {
-        Best o;
-        o.b1 = S.red[w2][tid][0];
-        o.i1 = __float_as_int(S.red[w2][tid][1]);
-        o.b2 = S.red[w2][tid][2];
-        best_merge(bst, o);
-      }
-      const int64_t row = U.row0 + t0 + tid;
-      const float R2 = __uint_as_float(S.rmax);
-      const float margin = 0x1p-14f * (S.xn[tid] * sqrtf(R2) + R2) + 0x1p-100f;
-      assign[row] = U.cbase + bst.i1;
-      // also undecided: a best at the floor of the padding rows (values beyond fp32 range)
-      if (!(bst.b1 - bst.b2 > margin) || !(bst.b1 > -0x1p127f)) {
-        const int pos = atomicAdd(amb, 1);
-        amb[1 + 2 * pos] = (int32_t)U.u;
-        amb[2 + 2 * pos] = t0 + tid;
-      }
-    }
-    __syncthreads();
-    if (more) {
-      stash();
-      __syncthreads();
-    }
   }
+  __syncthreads();
+  reduce(ntiles - 1);
 }
 
 // ------------------------------------------------------------------ k_assign_fix
