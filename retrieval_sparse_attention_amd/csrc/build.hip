@@ -158,10 +158,7 @@ __global__ __launch_bounds__(INIT_THREADS) void k_init(SeqArgs sa, uint64_t seed
         s2 = fmaf(f[2 * e], f[2 * e], s2);
         s2 = fmaf(f[2 * e + 1], f[2 * e + 1], s2);
       }
-      s2 += xor_shfl(s2, 8);
-      s2 += xor_shfl(s2, 4);
-      s2 += xor_shfl(s2, 2);
-      s2 += xor_shfl(s2, 1);
+      s2 = row_sum16(s2);
       if (i < U.Kc) {
         float* cr = cent + (U.gclu + i) * D + l16 * 8;
         *reinterpret_cast<float4*>(cr) = make_float4(f[0], f[1], f[2], f[3]);
@@ -376,7 +373,7 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint
           } else {
             sq(Bv[4]); sq(Bv[5]); sq(Bv[6]); sq(Bv[7]);
           }
-          s2 += xor_shfl(s2, 32);
+          s2 += swap32(s2);
           if (h == 0) S.xnp[bi][xhalf][t] = s2;
         }
         floatx16 acc[2];
@@ -409,9 +406,9 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint
         bs.b2 = b2;
         bs.i1 = cb + (p >> 4) * 32 + 8 * ((p & 15) >> 2) + 4 * h + (p & 3);
         Best o;
-        o.b1 = xor_shfl(bs.b1, 32);
-        o.b2 = xor_shfl(bs.b2, 32);
-        o.i1 = xor_shfl(bs.i1, 32);
+        o.b1 = swap32(bs.b1);
+        o.b2 = swap32(bs.b2);
+        o.i1 = swap32(bs.i1);
         best_merge(bs, o);
         if (h == 0) {
           float* rd = S.red[bi][wv][t];
@@ -656,9 +653,7 @@ __global__ __launch_bounds__(256) void k_update(SeqArgs sa, int64_t nclu, const 
   *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(ix.centroids_bf16) + F * D + 2 * lane) =
       (uint32_t)h0 | ((uint32_t)h1 << 16);
   const float a = bf16_to_f(h0), b = bf16_to_f(h1);
-  float q2 = fmaf(a, a, b * b);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) q2 += xor_shfl(q2, o);
+  const float q2 = wave_sum(fmaf(a, a, b * b));
   if (lane == 0) norm[F] = q2;
   if (FINAL) *reinterpret_cast<float2*>(ix.vsum + F * D + 2 * lane) = make_float2(w0, w1);
 }

@@ -86,4 +86,57 @@ __device__ __forceinline__ T xor_shfl(T v, int m) {
   return __shfl_xor(v, m, 64);
 }
 
+// value held by lane (i - N) mod 16 of this lane's row of 16 (DPP row rotate; no LDS)
+template <int N>
+__device__ __forceinline__ float row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + N, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a row with the association of an xor butterfly of
+// strides 8, 4, 2, 1: lane i adds the value of lane (i - N) mod 16, which differs
+// from lane i ^ N only in bits whose partial sums are already equal, so every
+// lane ends with the bits of the xor-exchange butterfly.
+__device__ __forceinline__ float row_sum16(float v) {
+  v += row_ror<8>(v);
+  v += row_ror<4>(v);
+  v += row_ror<2>(v);
+  v += row_ror<1>(v);
+  return v;
+}
+
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, row_ror<8>(v));
+  v = fmaxf(v, row_ror<4>(v));
+  v = fmaxf(v, row_ror<2>(v));
+  v = fmaxf(v, row_ror<1>(v));
+  return v;
+}
+
+// value held by lane i ^ 32 (v_permlane32_swap; no LDS)
+__device__ __forceinline__ uint32_t swap32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (threadIdx.x & 32) ? r[0] : r[1];
+}
+__device__ __forceinline__ float swap32(float v) { return __uint_as_float(swap32(__float_as_uint(v))); }
+__device__ __forceinline__ int swap32(int v) { return (int)swap32((uint32_t)v); }
+
+// workgroup barrier for LDS traffic only: waits for this wave's LDS operations,
+// not for its outstanding global loads (unlike __syncthreads)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+}
+
+// full-wave reductions: rows by DPP, then lanes i ^ 16 (LDS exchange) and i ^ 32
+__device__ __forceinline__ float wave_max(float v) {
+  v = row_max16(v);
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, swap32(v));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum16(v);
+  v += __shfl_xor(v, 16, 64);
+  return v + swap32(v);
+}
+
 }  // namespace wave

@@ -5,15 +5,23 @@
 // attention (retrieval zone), sink and recent tokens are attended exactly
 // (steady zone), and every other cluster contributes through its centroid
 // (estimation zone). Four launches per call, all on the caller's stream:
-//   k_score  -- rank keys of every centroid for the H/G q heads of a kv head
-//               (one pass over the bf16 centroid rows, HBM bound)
-//   k_topk   -- per (sequence, q head): steady set, eligibility, exact top-k by
-//               (key desc, id asc), the selected ids and their spans
-//   k_attend -- three roles in one grid: online-softmax attention over the
-//               selected clusters' sorted rows (one cluster per 16-lane group),
-//               over the steady rows, and the estimation term over the value
-//               sums of the remaining clusters, each writing a partial state
+//   k_score  -- one pass over the centroid rows and value sums of a kv head:
+//               rank keys of the H/G q heads, eligibility, and the estimation
+//               term of every cluster as partial softmax states
+//   k_topk   -- per (sequence, q head): exact top-k by (key desc, id asc), the
+//               selected ids and spans, steady-row corrections
+//   k_attend -- online-softmax attention over the selected clusters' sorted rows
+//               and over the steady rows; every row of a cluster whose centroid
+//               term was counted in k_score takes that term back out
 //   k_merge  -- log-sum-exp merge of the partials of every (sequence, q head)
+//
+// Estimation bookkeeping. The pages' estimation zone is E \ R with the value
+// sums and sizes of the clusters' non-steady members. k_score adds the centroid
+// term e^{s_j} (n_j, Vsum_j) of EVERY cluster; each member row t of a selected
+// cluster and each steady row t of a cluster that is not selected then adds
+// -e^{s_j} (1, v_t) in k_attend. Summed, this leaves exactly the centroid terms
+// of E \ R over their non-steady members (clusters outside E have only steady
+// members and cancel), up to fp32 rounding of the stored sums.
 #include <math.h>
 
 #include "common.h"
@@ -21,63 +29,137 @@
 
 namespace wave {
 
-constexpr int SCORE_CH = 64;    // clusters per k_score workgroup
+constexpr int SC = DEC_SCORE_CH;  // clusters per k_score workgroup
+constexpr int SCORE_THREADS = 256;
 constexpr int TK_THREADS = 1024;
-constexpr int TK_HASH = 4096;   // steady-cluster hash slots (>= 2 * WAVE_MAX_STEADY)
-constexpr int TK_FILT = 1024;   // filter words: bit (j mod 32768)
-constexpr int TK_CAND = 4096;   // threshold-bin candidates refined in LDS
-constexpr int TK_EXCL = 2048;   // exclusion words kept in LDS (C <= 65536)
+constexpr int TK_CAP = 1024;      // candidates of the fast selection
+constexpr int TK_SORT = DEC_SORT_LDS;
+constexpr int TK_SELW = 2048;     // selection bitmap words kept in LDS (C <= 65536)
 constexpr int TK_RANK_SMALL = 512;
 constexpr int ATT_THREADS = 256;
-constexpr int EST_CH = DEC_EST_CH;  // clusters per estimation workgroup (== ATT_THREADS)
-constexpr int PART = DEC_PART;  // floats per partial: m, l, 2 pad, acc[128]
+constexpr int PART = DEC_PART;    // floats per partial: m, l, 2 pad, acc[128]
 constexpr float LOG2E = 1.4426950408889634f;
 
-static_assert(EST_CH == ATT_THREADS, "one estimation cluster per thread");
-static_assert(TK_HASH >= 2 * WAVE_MAX_STEADY, "steady hash load factor");
+static_assert(SC == 128 && SCORE_THREADS == 256, "k_score thread mapping");
+
+// ------------------------------------------------------------------ steady zone
+struct Steady {
+  int64_t a_end, c_beg;  // S = [0, a_end) U [c_beg, N)
+  int nS;
+  bool all;
+};
+
+__device__ __forceinline__ Steady steady_of(const DecodeArgs& da, int N) {
+  Steady s;
+  s.a_end = min((int64_t)da.n_sink, (int64_t)N);
+  s.c_beg = max((int64_t)N - (int64_t)da.n_local, s.a_end);
+  s.nS = (int)(s.a_end + (N - s.c_beg));
+  s.all = s.nS == N;
+  return s;
+}
+
+// position of steady entry i
+__device__ __forceinline__ int64_t steady_pos(const Steady& s, int i) {
+  return i < s.a_end ? (int64_t)i : s.c_beg + (i - s.a_end);
+}
 
 // ------------------------------------------------------------------ k_score
 // Rank key r_{h,j}: 16 lanes each own 8 consecutive dims of the centroid row;
 // each lane sums its 8 exact bf16 products from +0 in dim order (an fma of
 // two bf16 values equals a rounded product then a rounded add), then an xor
 // butterfly over the 16 lanes with strides 8, 4, 2, 1, then +0.0f.
+//
+// One workgroup per (b, g, 128 clusters). All of the workgroup's HBM reads are
+// issued at entry: centroid rows first, the chunk's value sums (64 KB, 16 float4
+// per thread in registers) last, so the rank keys and weights are computed while
+// the value sums stream in. A cluster is eligible (in E) when it has a member
+// outside the steady zone; the steady tokens' clusters are counted only by
+// workgroups whose ids can hold them (the first and the last segments). Per q
+// head the workgroup writes one partial softmax state of its clusters' centroid
+// terms: weights 2^(r*tau*log2(e) - m) times (n_j, Vsum_j).
 template <int GS>
-__global__ __launch_bounds__(256) void k_score(SeqArgs sa, int32_t H, const uint16_t* __restrict__ chat,
-                                               const uint16_t* __restrict__ q, float* __restrict__ keys) {
-  __shared__ float stage[GS][SCORE_CH];
+struct ScoreLds {
+  float red[4][GS][D];  // per wave: the q heads' weighted value sums
+  float kw[GS][SC];     // rank keys, then estimation weights
+  int32_t nsz[SC];      // cluster sizes
+  int32_t scnt[SC];     // steady members
+  float hred[GS][2][2];
+};
+
+template <int GS>
+__global__ __launch_bounds__(SCORE_THREADS, 2) void k_score(SeqArgs sa, DecodeArgs da, wave_index ix,
+                                                            const uint16_t* __restrict__ q, DecodeWs ws) {
+  extern __shared__ uint8_t smem[];
+  ScoreLds<GS>& S = *reinterpret_cast<ScoreLds<GS>*>(smem);
   int w = blockIdx.x, b = 0;
-  int64_t clu = 0;
   for (;; ++b) {
-    const int nch = (sa.C[b] + SCORE_CH - 1) / SCORE_CH;
+    const int nch = (sa.C[b] + SC - 1) / SC;
     if (w < sa.G * nch) break;
     w -= sa.G * nch;
-    clu += (int64_t)sa.G * sa.C[b];
   }
-  const int C = sa.C[b];
-  const int nch = (C + SCORE_CH - 1) / SCORE_CH;
+  const SeqBase sb = seq_base(sa, b);
+  const int C = sb.C, N = sb.N;
+  const int nch = (C + SC - 1) / SC;
   const int g = w / nch, chunk = w % nch;
-  const int j0 = chunk * SCORE_CH;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, l16 = lane & 15, grp = lane >> 4;
-  const uint16_t* base = chat + (clu + (int64_t)g * C) * D + l16 * 8;
-  // issue the row loads first: 4 rows per wave-iteration, 4 iterations
-  uint4 cv[SCORE_CH / 16];
+  const int j0 = chunk * SC, nc = min(SC, C - j0);
+  const int64_t clu0 = sb.clu + (int64_t)g * C, row0 = sb.row + (int64_t)g * N;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, grp = lane >> 4;
+  const int gi = wv * 4 + grp;
+  const float sc = da.tau * LOG2E;
+
+  // steady tokens whose clusters may lie in this chunk (the first and the last segments):
+  // their clusters, up to 4 per thread in registers, loaded first
+  const Steady sz = steady_of(da, N);
+  bool need = false;
+  if (!sz.all && sz.nS > 0) {
+    const int64_t sink_hi =
+        sz.a_end > 0 ? min((int64_t)C, ((sz.a_end - 1) / sa.seg_len + 1) * (int64_t)sa.K_s) : 0;
+    const int64_t loc_lo = sz.c_beg < N ? (sz.c_beg / sa.seg_len) * (int64_t)sa.K_s : (int64_t)C;
+    need = (j0 < sink_hi) || (j0 + nc > loc_lo);
+  }
+  constexpr int SQ = 4;
+  int32_t sjr[SQ];
 #pragma unroll
-  for (int it = 0; it < SCORE_CH / 16; ++it) {
-    const int j = j0 + it * 16 + wv * 4 + grp;
-    cv[it] = (j < C) ? *reinterpret_cast<const uint4*>(base + (int64_t)j * D) : make_uint4(0, 0, 0, 0);
+  for (int r = 0; r < SQ; ++r) {
+    const int i = tid + r * SCORE_THREADS;
+    sjr[r] = (need && i < sz.nS) ? ix.assign[row0 + steady_pos(sz, i)] : -1;
+  }
+  // 1. centroid rows: group gi takes clusters gi + 16 it
+  uint4 cv[SC / 16];
+  {
+    const uint16_t* cb = reinterpret_cast<const uint16_t*>(ix.centroids_bf16) + (clu0 + j0) * D + l16 * 8;
+#pragma unroll
+    for (int it = 0; it < SC / 16; ++it)
+      cv[it] = *reinterpret_cast<const uint4*>(cb + (int64_t)min(gi + 16 * it, nc - 1) * D);
   }
   float qf[GS][8];
 #pragma unroll
   for (int hh = 0; hh < GS; ++hh) {
-    const uint4 v = *reinterpret_cast<const uint4*>(q + ((int64_t)b * H + g * GS + hh) * D + l16 * 8);
+    const uint4 v = *reinterpret_cast<const uint4*>(q + ((int64_t)b * da.H + g * GS + hh) * D + l16 * 8);
     qf[hh][0] = bf16_lo(v.x); qf[hh][1] = bf16_hi(v.x);
     qf[hh][2] = bf16_lo(v.y); qf[hh][3] = bf16_hi(v.y);
     qf[hh][4] = bf16_lo(v.z); qf[hh][5] = bf16_hi(v.z);
     qf[hh][6] = bf16_lo(v.w); qf[hh][7] = bf16_hi(v.w);
   }
+  const int nsz_r = tid < nc ? ix.sizes[clu0 + j0 + tid] : 0;
+  // value sums: thread (sub, dq) takes dims 4dq..4dq+3 of clusters sub + 8u; rows
+  // past the chunk repeat its last row (their weights are zero)
+  const int sub = tid >> 5, dq = tid & 31;
+  float4 vreg[SC / 8];
+  {
+    const float4* vsrc = reinterpret_cast<const float4*>(ix.vsum + (clu0 + j0) * D) + dq;
 #pragma unroll
-  for (int it = 0; it < SCORE_CH / 16; ++it) {
-    const int jj = it * 16 + wv * 4 + grp;
+    for (int u = 0; u < SC / 8; ++u) vreg[u] = vsrc[(int64_t)min(sub + 8 * u, nc - 1) * (D / 4)];
+  }
+  if (tid < SC) {
+    S.nsz[tid] = nsz_r;
+    S.scnt[tid] = 0;
+  }
+  lds_barrier();
+  // 2. rank keys
+#pragma unroll
+  for (int it = 0; it < SC / 16; ++it) {
+    const int jj = gi + 16 * it;
     const uint4 v = cv[it];
     const float c[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                         bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
@@ -86,17 +168,96 @@ __global__ __launch_bounds__(256) void k_score(SeqArgs sa, int32_t H, const uint
       float u = 0.f;
 #pragma unroll
       for (int m = 0; m < 8; ++m) u = fmaf(qf[hh][m], c[m], u);
-      u += xor_shfl(u, 8);
-      u += xor_shfl(u, 4);
-      u += xor_shfl(u, 2);
-      u += xor_shfl(u, 1);
-      if (l16 == hh) stage[hh][jj] = u + 0.0f;
+      u = row_sum16(u);
+      if (l16 == hh) S.kw[hh][jj] = u + 0.0f;
     }
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < GS * SCORE_CH; e += blockDim.x) {
-    const int hh = e / SCORE_CH, jj = e % SCORE_CH;
-    if (j0 + jj < C) keys[(int64_t)GS * clu + (int64_t)(g * GS + hh) * C + j0 + jj] = stage[hh][jj];
+  // steady members per cluster of the chunk
+  if (need) {
+#pragma unroll
+    for (int r = 0; r < SQ; ++r) {
+      const int j = sjr[r] - j0;
+      if (sjr[r] >= 0 && j >= 0 && j < nc) atomicAdd(&S.scnt[j], 1);
+    }
+    for (int i = tid + SQ * SCORE_THREADS; i < sz.nS; i += SCORE_THREADS) {
+      const int j = ix.assign[row0 + steady_pos(sz, i)] - j0;
+      if (j >= 0 && j < nc) atomicAdd(&S.scnt[j], 1);
+    }
+  }
+  lds_barrier();
+  // 3. keys and eligibility out; the first two waves form the per-head weights
+  const int64_t kb = (int64_t)GS * sb.clu + (int64_t)g * GS * C + j0;
+  for (int e = tid; e < GS * SC; e += SCORE_THREADS) {
+    const int hh = e / SC, jj = e % SC;
+    if (jj < nc) {
+      const float key = S.kw[hh][jj];
+      const int n = S.nsz[jj];
+      const bool elig = !sz.all && n > 0 && S.scnt[jj] < n;
+      ws.keys[kb + (int64_t)hh * C + jj] = key;
+      ws.key32[kb + (int64_t)hh * C + jj] = elig ? float_sortable(key) : 0u;
+    }
+  }
+  float sv[GS];
+  if (tid < SC) {
+    const bool live = tid < nc && S.nsz[tid] > 0;
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh) {
+      sv[hh] = live ? S.kw[hh][tid] * sc : -INFINITY;
+      const float mx = wave_max(sv[hh]);
+      if (lane == 0) S.hred[hh][wv][0] = mx;
+    }
+  }
+  lds_barrier();
+  if (tid < SC) {
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh) {
+      const float M = fmaxf(S.hred[hh][0][0], S.hred[hh][1][0]);
+      const float wgt = sv[hh] == -INFINITY ? 0.f : exp2f(sv[hh] - M);
+      S.kw[hh][tid] = wgt;
+      const float ls = wave_sum(wgt * (float)S.nsz[tid]);
+      if (lane == 0) S.hred[hh][wv][1] = ls;
+    }
+  }
+  lds_barrier();
+  // 4. sum_j w_j Vsum_j over the thread's 16 clusters, then over the 8 subs
+  float acc[GS][4];
+#pragma unroll
+  for (int hh = 0; hh < GS; ++hh)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[hh][e] = 0.f;
+#pragma unroll
+  for (int u = 0; u < SC / 8; ++u) {
+    const int jj = sub + 8 * u;
+    const float4 v = vreg[u];
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh) {
+      const float wgt = jj < nc ? S.kw[hh][jj] : 0.f;
+      acc[hh][0] = fmaf(wgt, v.x, acc[hh][0]);
+      acc[hh][1] = fmaf(wgt, v.y, acc[hh][1]);
+      acc[hh][2] = fmaf(wgt, v.z, acc[hh][2]);
+      acc[hh][3] = fmaf(wgt, v.w, acc[hh][3]);
+    }
+  }
+#pragma unroll
+  for (int hh = 0; hh < GS; ++hh)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[hh][e] += swap32(acc[hh][e]);
+  if (lane < 32)
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S.red[wv][hh][dq * 4 + e] = acc[hh][e];
+  lds_barrier();
+  for (int e = tid; e < GS * D; e += SCORE_THREADS) {
+    const int hh = e / D, d = e % D;
+    const float A = S.red[0][hh][d] + S.red[1][hh][d] + S.red[2][hh][d] + S.red[3][hh][d];
+    float* o = ws.part + (((int64_t)b * da.H + g * GS + hh) * da.NP + da.P + chunk) * PART;
+    if (d == 0) {
+      const float L = S.hred[hh][0][1] + S.hred[hh][1][1];
+      o[0] = L > 0.f ? fmaxf(S.hred[hh][0][0], S.hred[hh][1][0]) : -INFINITY;
+      o[1] = L;
+    }
+    o[4 + d] = A;
   }
 }
 
@@ -149,437 +310,97 @@ __device__ inline void bitonic_desc(uint64_t* a, int n, bool global) {
 }
 
 // ------------------------------------------------------------------ k_topk
-constexpr int TK_BINS = 8192;   // first radix digit: the top 13 bits of the sortable key
-
+// Sortable key u_j = float_sortable(r_j) for j in E, 0 otherwise; the selection
+// R is the k = min(kreq, |E|) largest (u desc, id asc).
+//
+// Ids: wave w owns [w 64 NV, (w + 1) 64 NV); lane L holds ids
+// w0 + 256 blk + 4 L + e (blk < NV / 4, e < 4), so a wave's order of
+// (blk, lane, e) is id order. With NV <= 16 the keys stay in registers.
+//
+// Fast path (keys in registers, k <= 1024): every wave finds the m-th largest
+// of its 64 lane maxima, t_w (m = ceil(kreq / 16)), by bisection over the 32
+// key bits with ballots, no barrier; at least m keys of the wave are >= t_w, so
+// at least 16 m >= k keys are >= min_w t_w. A lane whose maximum is >= t holds a
+// key >= t, so counting lane maxima >= each t_w bounds the keys >= t_w from below:
+// X is the largest t_w with at least k lane maxima at or above it, and the keys
+// >= X contain R. When there are at most 1024 of them, each one's rank and
+// the summed sizes of the candidates ranked before it are counted (split over
+// all threads), which yields R in rank order with its member-count prefix.
+// Otherwise the general path finds the exact k-th key by bisection over the
+// workgroup, selects in id order and sorts the selection.
 struct TopkLds {
-  int32_t hkey[TK_HASH];       // steady clusters: open-addressing hash, -1 = empty
-  int32_t hcnt[TK_HASH];       // steady tokens per hashed cluster
-  int32_t sj[WAVE_MAX_STEADY]; // cluster of every steady token
-  uint32_t filt[TK_FILT];      // steady-cluster filter
-  uint32_t hist[TK_BINS];
   union {
     struct {
-      uint32_t key[TK_CAND];
-      int32_t id[TK_CAND];
-    } cand;
-    uint64_t sortbuf[TK_CAND];
+      uint64_t key[TK_CAP];     // (u << 32) | ~id
+      int32_t n[TK_CAP];        // cluster size
+      int32_t off[TK_CAP];      // first sorted slot
+      int32_t rank[TK_CAP];     // candidates that order before it
+      int32_t pre[TK_CAP];      // their summed sizes
+    } c;                        // fast path
+    uint64_t sortbuf[TK_SORT];  // general path: the selection's (u << 32) | ~id
   } u;
-  uint32_t excl[TK_EXCL];
+  uint32_t selw[TK_SELW];       // selection bitmap (C <= 65536)
   uint64_t scan[17];
-  int32_t misc[16];
+  uint32_t bis[34];             // block counts of the bisection, then of keys above T
+  int32_t wE[16];
+  uint32_t wt[16];
+  int32_t tcnt[16];             // keys >= wt[i] over the workgroup
+  int32_t misc[8];
 };
 
-__device__ __forceinline__ uint32_t hslot(int32_t j) { return ((uint32_t)j * 2654435761u) >> 20; }
-
-__device__ inline int steady_count(const TopkLds& L, int32_t j) {
-  if (!((L.filt[(j >> 5) & (TK_FILT - 1)] >> (j & 31)) & 1u)) return 0;
-  uint32_t h = hslot(j);
-  for (;;) {
-    const int32_t k = L.hkey[h];
-    if (k == j) return L.hcnt[h];
-    if (k < 0) return 0;
-    h = (h + 1) & (TK_HASH - 1);
-  }
-}
-
-// largest bin d of hist[0..nbins) whose suffix count reaches kk (nbins a multiple of
-// TK_THREADS or equal to it); writes d and the count strictly above it to misc[1], misc[2]
-__device__ inline void find_bin(TopkLds& L, int nbins, int kk) {
-  const int tid = threadIdx.x;
-  const int per = nbins / TK_THREADS;
-  const int hi = nbins - 1 - per * tid;  // this thread's bins hi, hi-1, ..., hi-per+1
-  uint64_t local = 0;
-  for (int e = 0; e < per; ++e) local += L.hist[hi - e];
-  uint64_t tot;
-  uint64_t above = block_scan_excl(local, L.scan, &tot);
-  for (int e = 0; e < per; ++e) {
-    const uint64_t suf = above + L.hist[hi - e];
-    if (above < (uint64_t)kk && suf >= (uint64_t)kk) {
-      L.misc[1] = hi - e;
-      L.misc[2] = (int)above;
-    }
-    above = suf;
-  }
-  __syncthreads();
-}
-
-
-// member-count prefix of the id-order selection (selpre[0..k]) and the per-(b, h)
-// counts record {rows of the selected clusters, k, steady rows, 0}
-__device__ inline void selection_prefix(TopkLds& L, const DecodeWs& ws, int64_t kbase, int bh, int k, int nS) {
-  __threadfence_block();
-  __syncthreads();
-  const int tid = threadIdx.x, nt = blockDim.x;
-  const int2* span = ws.span + kbase;
-  int32_t* selpre = ws.selpre + kbase + bh;  // k+1 entries per (b, h)
-  const int R = (k + nt - 1) / nt;
-  const int q0 = min(tid * R, k), q1 = min(q0 + R, k);
-  int64_t msum = 0;
-  for (int i = q0; i < q1; ++i) msum += span[i].y;
-  uint64_t tot;
-  int64_t run = (int64_t)block_scan_excl((uint64_t)msum, L.scan, &tot);
-  for (int i = q0; i < q1; ++i) {
-    selpre[i] = (int32_t)run;
-    run += span[i].y;
-  }
-  if (tid == 0) {
-    selpre[k] = (int32_t)tot;
-    ws.counts[4 * bh + 0] = (int32_t)tot;
-    ws.counts[4 * bh + 1] = k;
-    ws.counts[4 * bh + 2] = nS;
-    ws.counts[4 * bh + 3] = 0;
-  }
-}
-
-// Per (sequence b, q head h), any number of clusters. Ids are split into 16
-// contiguous wave ranges, each walked 64 ids at a time (lane = id offset), so
-// every pass is coalesced and the order of ids inside a wave follows the lanes.
-// The sortable keys are kept in global memory between passes.
-__global__ __launch_bounds__(TK_THREADS) void k_topk_any(SeqArgs sa, DecodeArgs da, wave_index ix, DecodeWs ws,
-                                                         int32_t* __restrict__ sel_ids) {
+template <int NVR>
+__global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, wave_index ix, DecodeWs ws,
+                                                     int32_t* __restrict__ sel_ids) {
+  constexpr bool INREG = NVR > 0;
+  constexpr int CHK = INREG ? NVR : 8;  // keys per lane per chunk
   extern __shared__ uint8_t smem[];
   TopkLds& L = *reinterpret_cast<TopkLds*>(smem);
+  const int NV = INREG ? NVR : da.NVg;
   const int bh = blockIdx.x;
-  const int b = bh / da.H, h = bh % da.H;
-  const int g = h / da.GS;
+  const int b = bh / da.H, h = bh % da.H, g = h / da.GS;
   const SeqBase sb = seq_base(sa, b);
   const int N = sb.N, C = sb.C;
   const int64_t row0 = sb.row + (int64_t)g * N;
   const int64_t clu0 = sb.clu + (int64_t)g * C;
   const int64_t off0 = sb.off + (int64_t)g * (C + 1);
-  const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wv = tid >> 6;
   const int64_t kbase = (int64_t)da.GS * sb.clu + (int64_t)h * C;
-  const int nwords = (C + 31) >> 5;
-  int64_t wbase = 0;
-  for (int i = 0; i < b; ++i) wbase += (int64_t)da.H * ((sa.C[i] + 31) >> 5);
-  wbase += (int64_t)h * nwords;
-  const float* keys = ws.keys + kbase;
-  uint32_t* key32 = ws.key32 + kbase;
-  uint32_t* excl_g = ws.excl + wbase;
-  int2* span = ws.span + kbase;  // (first sorted slot, size) of the i-th selection in id order
-  float* corr = ws.corr + (int64_t)bh * da.scap;
-  const int32_t* sizes = ix.sizes + clu0;
-  const int32_t* offs = ix.offsets + off0;
-  const bool lds_excl = nwords <= TK_EXCL;
-  // this wave's id range [w0, w1)
-  const int wspan = ((C + 15) / 16 + 63) & ~63;
-  const int w0 = min(wv * wspan, C), w1 = min(w0 + wspan, C);
-
-  // 0. LDS init
-  for (int i = tid; i < TK_HASH; i += nt) { L.hkey[i] = -1; L.hcnt[i] = 0; }
-  for (int i = tid; i < TK_FILT; i += nt) L.filt[i] = 0u;
-  for (int i = tid; i < TK_BINS; i += nt) L.hist[i] = 0u;
-  if (lds_excl)
-    for (int i = tid; i < nwords; i += nt) L.excl[i] = 0u;
-  else
-    for (int i = tid; i < nwords; i += nt) excl_g[i] = 0u;
-  if (tid < 16) L.misc[tid] = 0;
-  __threadfence_block();
-  __syncthreads();
-
-  // 1. steady zone S = [0, a) U [c, N): count the steady tokens of every cluster
-  const int64_t a_end = min((int64_t)da.n_sink, (int64_t)N);
-  const int64_t c_beg = max((int64_t)N - (int64_t)da.n_local, a_end);
-  const int nS = (int)(a_end + (N - c_beg));
-  const bool allS = (nS == N);
-  if (!allS) {
-    for (int i = tid; i < nS; i += nt) {
-      const int64_t t = i < a_end ? i : c_beg + (i - a_end);
-      const int32_t j = ix.assign[row0 + t];
-      L.sj[i] = j;
-      atomicOr(&L.filt[(j >> 5) & (TK_FILT - 1)], 1u << (j & 31));
-      uint32_t hs = hslot(j);
-      for (;;) {
-        const int32_t prev = atomicCAS(&L.hkey[hs], -1, j);
-        if (prev == -1 || prev == j) {
-          atomicAdd(&L.hcnt[hs], 1);
-          break;
-        }
-        hs = (hs + 1) & (TK_HASH - 1);
-      }
-    }
-  }
-  __syncthreads();
-
-  // 2. eligibility (some member outside S), sortable keys, |E|, top-13-bit histogram;
-  //    non-empty clusters that are not eligible are excluded from the estimation zone
-  {
-    int myE = 0;
-    for (int j0 = w0; j0 < w1; j0 += 64) {
-      const int j = j0 + lane;
-      const bool in = j < w1;
-      const int n = in ? sizes[j] : 0;
-      const float r = in ? keys[j] : 0.f;
-      bool elig = false;
-      if (n > 0 && !allS) elig = (n - steady_count(L, j)) > 0;
-      const uint32_t u = elig ? float_sortable(r) : 0u;
-      if (in) key32[j] = u;
-      if (elig) {
-        ++myE;
-        atomicAdd(&L.hist[u >> 19], 1u);
-      } else if (n > 0) {
-        if (lds_excl) atomicOr(&L.excl[j >> 5], 1u << (j & 31));
-        else atomicOr(&excl_g[j >> 5], 1u << (j & 31));
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) myE += __shfl_xor(myE, o, 64);
-    if (lane == 0) atomicAdd(&L.misc[0], myE);
-  }
-  __threadfence_block();
-  __syncthreads();
-  const int nE = L.misc[0];
-  const int k = min(da.kreq[b], nE);
-
-  // 3. threshold key T (the k-th largest key32) and k_eq, the number of keys equal to T taken
-  uint32_t T = 0xFFFFFFFFu;
-  int k_eq = 0;
-  if (k > 0) {
-    find_bin(L, TK_BINS, k);
-    const int d1 = L.misc[1];
-    int kk = k - L.misc[2];
-    // candidates: keys whose top 13 bits are d1
-    for (int j0 = w0; j0 < w1; j0 += 64) {
-      const int j = j0 + lane;
-      const uint32_t u = j < w1 ? key32[j] : 0u;
-      if (j < w1 && (int)(u >> 19) == d1) {
-        const int p = atomicAdd(&L.misc[3], 1);
-        if (p < TK_CAND) { L.u.cand.key[p] = u; L.u.cand.id[p] = j; }
-      }
-    }
-    __syncthreads();
-    const int nc = L.misc[3];
-    if (nc <= TK_RANK_SMALL) {
-      // few candidates: the kk-th by (key desc, id asc) by counting
-      if (tid < nc) {
-        const uint32_t u = L.u.cand.key[tid];
-        const int id = L.u.cand.id[tid];
-        int rank = 0;
-#pragma unroll 8
-        for (int i = 0; i < nc; ++i) {
-          const uint32_t v = L.u.cand.key[i];
-          rank += (v > u) || (v == u && L.u.cand.id[i] < id);
-        }
-        if (rank == kk - 1) L.misc[4] = (int)u;
-      }
-      __syncthreads();
-      T = (uint32_t)L.misc[4];
-      // keys == T above the kk-th candidate are all taken: count them among candidates
-      if (tid == 0) {
-        int eq_gt = 0;
-#pragma unroll 8
-        for (int i = 0; i < nc; ++i) eq_gt += L.u.cand.key[i] > T;
-        L.misc[5] = kk - eq_gt;
-      }
-      __syncthreads();
-      k_eq = L.misc[5];
-    } else {
-      // radix passes over bits 18..9 and 8..0 (candidates in LDS, or all keys)
-      const bool in_lds = nc <= TK_CAND;
-      uint32_t prefix = (uint32_t)d1 << 19, mask = 0xFFF80000u;
-      for (int pass = 0; pass < 2; ++pass) {
-        const int sh = pass == 0 ? 9 : 0, nb = pass == 0 ? 1024 : 512;
-        for (int i = tid; i < 1024; i += nt) L.hist[i] = 0u;
-        __syncthreads();
-        if (in_lds) {
-          for (int i = tid; i < nc; i += nt) {
-            const uint32_t u = L.u.cand.key[i];
-            if ((u & mask) == prefix) atomicAdd(&L.hist[(u >> sh) & (nb - 1)], 1u);
-          }
-        } else {
-          for (int j = tid; j < C; j += nt) {
-            const uint32_t u = key32[j];
-            if ((u & mask) == prefix) atomicAdd(&L.hist[(u >> sh) & (nb - 1)], 1u);
-          }
-        }
-        __syncthreads();
-        find_bin(L, 1024, kk);  // bins >= nb are empty
-        prefix |= (uint32_t)L.misc[1] << sh;
-        mask |= (uint32_t)(nb - 1) << sh;
-        kk -= L.misc[2];
-        __syncthreads();
-      }
-      T = prefix;
-      k_eq = kk;
-    }
-  }
-
-  // 4. the selection in id order: keys > T and the k_eq lowest ids with key == T
-  if (k > 0) {
-    int ngt = 0, neq = 0;
-    for (int j0 = w0; j0 < w1; j0 += 64) {
-      const int j = j0 + lane;
-      const uint32_t u = j < w1 ? key32[j] : 0u;
-      ngt += __popcll(__ballot(j < w1 && u > T));
-      neq += __popcll(__ballot(j < w1 && u == T));
-    }
-    uint64_t tot;
-    const uint64_t v = (lane == 0) ? (((uint64_t)ngt << 32) | (uint32_t)neq) : 0ull;
-    const uint64_t pre = block_scan_excl(v, L.scan, &tot);
-    const uint64_t wpre = __shfl(pre, 0, 64);
-    int eq_seen = (int)(wpre & 0xFFFFFFFFu);
-    int pos = (int)(wpre >> 32) + min(eq_seen, k_eq);
-    const uint64_t ltmask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int j0 = w0; j0 < w1; j0 += 64) {
-      const int j = j0 + lane;
-      const uint32_t u = j < w1 ? key32[j] : 0u;
-      const bool eq = j < w1 && u == T;
-      const uint64_t eqm = __ballot(eq);
-      const bool s = (j < w1 && u > T) || (eq && eq_seen + __popcll(eqm & ltmask) < k_eq);
-      const uint64_t sm = __ballot(s);
-      if (s) {
-        const int p = pos + __popcll(sm & ltmask);
-        span[p] = make_int2(offs[j], sizes[j]);
-        const uint64_t comp = ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)j);
-        if (k <= TK_CAND) L.u.sortbuf[p] = comp;
-        else ws.sortg[(int64_t)bh * da.sort_stride + p] = comp;
-        if (lds_excl) atomicOr(&L.excl[j >> 5], 1u << (j & 31));
-        else atomicOr(&excl_g[j >> 5], 1u << (j & 31));
-      }
-      pos += __popcll(sm);
-      eq_seen += __popcll(eqm);
-    }
-    __threadfence_block();
-    __syncthreads();
-    // 5. rank order (key desc, id asc) of the output ids
-    int32_t* out = sel_ids + (int64_t)bh * da.k_max;
-    if (k <= TK_RANK_SMALL) {
-      if (tid < k) {
-        const uint64_t c = L.u.sortbuf[tid];
-        int rank = 0;
-#pragma unroll 8
-        for (int i = 0; i < k; ++i) rank += L.u.sortbuf[i] > c;
-        out[rank] = (int32_t)(0xFFFFFFFFu - (uint32_t)(c & 0xFFFFFFFFu));
-      }
-    } else {
-      int P2 = 1;
-      while (P2 < k) P2 <<= 1;
-      uint64_t* a = (k <= TK_CAND) ? L.u.sortbuf : ws.sortg + (int64_t)bh * da.sort_stride;
-      for (int i = k + tid; i < P2; i += nt) a[i] = 0;
-      if (k > TK_CAND) __threadfence_block();
-      __syncthreads();
-      bitonic_desc(a, P2, k > TK_CAND);
-      for (int i = tid; i < k; i += nt) out[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(a[i] & 0xFFFFFFFFu));
-    }
-  }
-  if (sel_ids != nullptr) {
-    int32_t* out = sel_ids + (int64_t)bh * da.k_max;
-    for (int i = k + tid; i < da.k_max; i += nt) out[i] = -1;
-  }
-  __threadfence_block();
-  __syncthreads();
-  if (lds_excl)
-    for (int i = tid; i < nwords; i += nt) excl_g[i] = L.excl[i];
-
-  // 6. steady rows: their cluster's estimation correction (rank key, NaN if none)
-  for (int i = tid; i < nS; i += nt) {
-    float cv = __uint_as_float(0x7FC00000u);
-    if (!allS) {
-      const int32_t j = L.sj[i];
-      const bool elig = (sizes[j] - steady_count(L, j)) > 0;
-      const uint32_t ew = lds_excl ? L.excl[j >> 5] : excl_g[j >> 5];
-      if (elig && !((ew >> (j & 31)) & 1u)) cv = keys[j];
-    }
-    corr[i] = cv;
-  }
-  selection_prefix(L, ws, kbase, bh, k, nS);
-}
-
-
-// Per (sequence b, q head h) with C <= 16 * 64 * NV clusters. Wave w owns ids
-// [w * 64 * NV, (w + 1) * 64 * NV); lane L holds ids w0 + 256 * blk + 4 * L + e
-// (blk < NV / 4, e < 4), so each load instruction covers 256 consecutive ids and
-// the order of ids inside a wave is (blk, lane, e). Up to 16 keys per lane stay
-// in registers through every pass; larger NV keep them in global memory and
-// reload 16 per lane at a time.
-template <int NV>
-__global__ __launch_bounds__(TK_THREADS) void k_topk_reg(SeqArgs sa, DecodeArgs da, wave_index ix, DecodeWs ws,
-                                                         int32_t* __restrict__ sel_ids) {
-  constexpr int CHK = NV < 16 ? NV : 16;  // keys per lane per chunk
-  constexpr bool INREG = NV <= 16;
-  extern __shared__ uint8_t smem[];
-  TopkLds& L = *reinterpret_cast<TopkLds*>(smem);
-  const int bh = blockIdx.x;
-  const int b = bh / da.H, h = bh % da.H;
-  const int g = h / da.GS;
-  const SeqBase sb = seq_base(sa, b);
-  const int N = sb.N, C = sb.C;
-  const int64_t row0 = sb.row + (int64_t)g * N;
-  const int64_t clu0 = sb.clu + (int64_t)g * C;
-  const int64_t off0 = sb.off + (int64_t)g * (C + 1);
   const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wv = tid >> 6;
-  const int64_t kbase = (int64_t)da.GS * sb.clu + (int64_t)h * C;
-  const int nwords = (C + 31) >> 5;
-  int64_t wbase = 0;
-  for (int i = 0; i < b; ++i) wbase += (int64_t)da.H * ((sa.C[i] + 31) >> 5);
-  wbase += (int64_t)h * nwords;
+  const uint64_t ltmask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const uint32_t* key32 = ws.key32 + kbase;
   const float* keys = ws.keys + kbase;
-  uint32_t* key32 = ws.key32 + kbase;
-  uint32_t* excl_g = ws.excl + wbase;
   int2* span = ws.span + kbase;
-  float* corr = ws.corr + (int64_t)bh * da.scap;
+  float* skey = ws.skey + kbase;
+  int32_t* out = sel_ids + (int64_t)bh * da.k_max;
   const int32_t* sizes = ix.sizes + clu0;
   const int32_t* offs = ix.offsets + off0;
   const int w0 = wv * 64 * NV;
   auto id_of = [&](int v) { return w0 + 256 * (v >> 2) + 4 * lane + (v & 3); };
+  const int nwords = (C + 31) >> 5;
+  const bool lds_sel = nwords <= TK_SELW;
+  int64_t wbase = 0;
+  for (int i = 0; i < b; ++i) wbase += (int64_t)da.H * ((sa.C[i] + 31) >> 5);
+  uint32_t* selw = lds_sel ? L.selw : ws.selw + wbase + (int64_t)h * nwords;
 
-  // 0. LDS init, with the lane's first chunk of sizes and keys in flight
-  int nn[CHK];
-  float rr[CHK];
-  auto load_chunk = [&](int c0) {
+  // 0. keys and the steady tokens' clusters in flight; LDS init
+  constexpr bool PRE = INREG && NVR <= 8;  // sizes and offsets of every key prefetched
+  uint32_t ureg[INREG ? NVR : 1];
+  int32_t nreg[PRE ? NVR : 1], oreg[PRE ? NVR : 1];
+  if constexpr (INREG) {
 #pragma unroll
-    for (int v = 0; v < CHK; ++v) {
-      const int j = id_of(c0 + v);
-      nn[v] = j < C ? sizes[j] : 0;
-      rr[v] = j < C ? keys[j] : 0.f;
-    }
-  };
-  load_chunk(0);
-  // the steady tokens' clusters (at most WAVE_MAX_STEADY = 2 per thread) in flight too
-  const int64_t a_end = min((int64_t)da.n_sink, (int64_t)N);
-  const int64_t c_beg = max((int64_t)N - (int64_t)da.n_local, a_end);
-  const int nS = (int)(a_end + (N - c_beg));
-  const bool allS = (nS == N);
-  int32_t sjr[2] = {0, 0};
-  if (!allS) {
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int i = tid + r * TK_THREADS;
-      if (i < nS) sjr[r] = ix.assign[row0 + (i < a_end ? i : c_beg + (i - a_end))];
+    for (int v = 0; v < NVR; ++v) {
+      const int j = id_of(v);
+      const uint32_t x = key32[min(j, C - 1)];
+      ureg[v] = j < C ? x : 0u;
     }
   }
-  for (int i = tid; i < TK_HASH; i += nt) { L.hkey[i] = -1; L.hcnt[i] = 0; }
-  for (int i = tid; i < TK_FILT; i += nt) L.filt[i] = 0u;
-  for (int i = tid; i < TK_BINS; i += nt) L.hist[i] = 0u;
-  for (int i = tid; i < nwords; i += nt) L.excl[i] = 0u;
-  if (tid < 16) L.misc[tid] = 0;
-  __syncthreads();
-
-  // 1. steady zone S = [0, a) U [c, N): count the steady tokens of every cluster
-  if (!allS) {
+  if constexpr (PRE) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int i = tid + r * TK_THREADS;
-      if (i < nS) {
-        const int32_t j = sjr[r];
-        L.sj[i] = j;
-        atomicOr(&L.filt[(j >> 5) & (TK_FILT - 1)], 1u << (j & 31));
-        uint32_t hs = hslot(j);
-        for (;;) {
-          const int32_t prev = atomicCAS(&L.hkey[hs], -1, j);
-          if (prev == -1 || prev == j) {
-            atomicAdd(&L.hcnt[hs], 1);
-            break;
-          }
-          hs = (hs + 1) & (TK_HASH - 1);
-        }
-      }
+    for (int v = 0; v < NVR; ++v) {
+      const int j = min(id_of(v), C - 1);
+      nreg[v] = sizes[j];
+      oreg[v] = offs[j];
     }
   }
-  __syncthreads();
-
-  // 2. eligibility, sortable keys, |E|, top-13-bit histogram, exclusions
-  uint32_t ureg[INREG ? NV : 1];
   auto chunk_keys = [&](int c0, uint32_t* uc) {  // the lane's CHK keys of chunk c0
     if constexpr (INREG) {
 #pragma unroll
@@ -588,115 +409,187 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_reg(SeqArgs sa, DecodeArgs 
 #pragma unroll
       for (int v = 0; v < CHK; ++v) {
         const int j = id_of(c0 + v);
-        uc[v] = j < C ? key32[j] : 0u;
+        const uint32_t x = key32[min(j, C - 1)];
+        uc[v] = j < C ? x : 0u;
       }
     }
   };
-  {
-    int myE = 0;
-#pragma unroll(INREG ? 16 : 1)
-    for (int c0 = 0; c0 < NV; c0 += CHK) {
-      if (c0 > 0) load_chunk(c0);
+  const Steady sz = steady_of(da, N);
+  int32_t sjr[2] = {0, 0};
 #pragma unroll
-      for (int v = 0; v < CHK; ++v) {
-        const int j = id_of(c0 + v);
-        bool elig = false;
-        if (nn[v] > 0 && !allS) elig = (nn[v] - steady_count(L, j)) > 0;
-        const uint32_t x = elig ? float_sortable(rr[v]) : 0u;
-        if constexpr (INREG) ureg[c0 + v] = x;
-        else if (j < C) key32[j] = x;
-        if (elig) {
-          ++myE;
-          atomicAdd(&L.hist[x >> 19], 1u);
-        } else if (nn[v] > 0) {
-          atomicOr(&L.excl[j >> 5], 1u << (j & 31));
-        }
+  for (int r = 0; r < 2; ++r) {
+    const int i = tid + r * TK_THREADS;
+    if (i < sz.nS) sjr[r] = ix.assign[row0 + steady_pos(sz, i)];
+  }
+  for (int i = tid; i < nwords; i += nt) selw[i] = 0u;
+  if constexpr (INREG) {
+    L.u.c.rank[tid] = 0;
+    L.u.c.pre[tid] = 0;
+  }
+  if (tid < 34) L.bis[tid] = 0u;
+  if (tid < 8) L.misc[tid] = 0;
+  if (tid < 16) L.tcnt[tid] = 0;
+
+  // 1. per wave: eligible keys and (keys in registers) the m-th largest key
+  const int kreq = da.kreq[b];
+  const int m = (kreq + 15) / 16;
+  int Ew = 0;
+  uint32_t tw = 0u;
+  uint32_t lmax = 0u;
+  if constexpr (INREG) {
+#pragma unroll
+    for (int v = 0; v < NVR; ++v) {
+      Ew += __popcll(__ballot(ureg[v] != 0u));
+      lmax = max(lmax, ureg[v]);
+    }
+    if (kreq > 0 && __popcll(__ballot(lmax != 0u)) >= m) {
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = tw | (1u << bit);
+        if (__popcll(__ballot(lmax >= c)) >= m) tw = c;
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) myE += __shfl_xor(myE, o, 64);
-    if (lane == 0) atomicAdd(&L.misc[0], myE);
-  }
-  __threadfence_block();
-  __syncthreads();
-  const int nE = L.misc[0];
-  const int k = min(da.kreq[b], nE);
-
-  // 3. threshold key T and k_eq
-  uint32_t T = 0xFFFFFFFFu;
-  int k_eq = 0;
-  if (k > 0) {
-    find_bin(L, TK_BINS, k);
-    const int d1 = L.misc[1];
-    int kk = k - L.misc[2];
-#pragma unroll(INREG ? 16 : 1)
+  } else {
     for (int c0 = 0; c0 < NV; c0 += CHK) {
       uint32_t uc[CHK];
       chunk_keys(c0, uc);
 #pragma unroll
-      for (int v = 0; v < CHK; ++v) {
-        if (uc[v] != 0u && (int)(uc[v] >> 19) == d1) {
-          const int p = atomicAdd(&L.misc[3], 1);
-          if (p < TK_CAND) { L.u.cand.key[p] = uc[v]; L.u.cand.id[p] = id_of(c0 + v); }
+      for (int v = 0; v < CHK; ++v) Ew += __popcll(__ballot(uc[v] != 0u));
+    }
+  }
+  // rank keys of the steady tokens' clusters, for the corrections at the end
+  float kjr[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) kjr[r] = keys[min(max(sjr[r], 0), C - 1)];
+  if (lane == 0) {
+    L.wE[wv] = Ew;
+    L.wt[wv] = tw;
+  }
+  lds_barrier();
+  int nE = 0;
+  uint32_t X = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    nE += L.wE[i];
+    X = min(X, L.wt[i]);
+  }
+  const int k = min(kreq, nE);
+  if constexpr (INREG) {
+    if (k > 0 && k == kreq && X > 0u) {
+      // lane maxima >= each wave threshold; lane i < 16 of every wave adds its count for wt[i]
+      int mine = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int cnt = __popcll(__ballot(lmax >= L.wt[i]));
+        mine = (lane == i) ? cnt : mine;
+      }
+      if (lane < 16) atomicAdd(&L.tcnt[lane], mine);
+      lds_barrier();
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (L.tcnt[i] >= k) X = max(X, L.wt[i]);
+    }
+  }
+  if (k < kreq) X = 1u;
+  X = max(X, 1u);
+
+  // 2. fast path: candidates u >= X; rank and size prefix by counting
+  bool fast = INREG && k > 0 && k <= TK_CAP;
+  if (fast) {
+    if constexpr (INREG) {
+      uint64_t bal[NVR];
+      int tot = 0;
+#pragma unroll
+      for (int v = 0; v < NVR; ++v) {
+        bal[v] = __ballot(ureg[v] >= X);
+        tot += __popcll(bal[v]);
+      }
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&L.misc[0], tot);
+      base = __shfl(base, 0, 64);
+#pragma unroll
+      for (int v = 0; v < NVR; ++v) {
+        if (ureg[v] >= X) {
+          const int p = base + __popcll(bal[v] & ltmask);
+          if (p < TK_CAP) {
+            const int id = id_of(v);
+            L.u.c.key[p] = ((uint64_t)ureg[v] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)id);
+            if constexpr (PRE) {
+              L.u.c.n[p] = nreg[v];
+              L.u.c.off[p] = oreg[v];
+            } else {
+              L.u.c.n[p] = sizes[id];
+              L.u.c.off[p] = offs[id];
+            }
+          }
         }
+        base += __popcll(bal[v]);
       }
     }
-    __syncthreads();
-    const int nc = L.misc[3];
-    if (nc <= TK_RANK_SMALL) {
+    lds_barrier();
+    const int nc = L.misc[0];
+    fast = nc <= TK_CAP;
+    if (fast) {
+      // candidate i = tid mod nc counts over the part (tid / nc) of the candidates
+      const int P = max(1, TK_THREADS / nc);
+      const int i = tid % nc, part = tid / nc;
+      if (part < P) {
+        const uint64_t c = L.u.c.key[i];
+        const int j0 = nc * part / P, j1 = nc * (part + 1) / P;  // nc <= 1024: no overflow
+        int rank = 0, pre = 0;
+#pragma unroll 16
+        for (int j = j0; j < j1; ++j) {
+          const bool gt = L.u.c.key[j] > c;
+          rank += gt;
+          pre += gt ? L.u.c.n[j] : 0;
+        }
+        atomicAdd(&L.u.c.rank[i], rank);
+        atomicAdd(&L.u.c.pre[i], pre);
+      }
+      lds_barrier();
+      int32_t* selpre = ws.selpre + kbase + bh;  // k + 1 entries per (b, h)
       if (tid < nc) {
-        const uint32_t x = L.u.cand.key[tid];
-        const int id = L.u.cand.id[tid];
-        int rank = 0;
-#pragma unroll 8
-        for (int i = 0; i < nc; ++i) {
-          const uint32_t y = L.u.cand.key[i];
-          rank += (y > x) || (y == x && L.u.cand.id[i] < id);
-        }
-        if (rank == kk - 1) L.misc[4] = (int)x;
-      }
-      __syncthreads();
-      T = (uint32_t)L.misc[4];
-      // candidates above T are taken; the rest of the kk come from keys equal to T
-      if (tid < nc && L.u.cand.key[tid] > T) atomicAdd(&L.misc[5], 1);
-      __syncthreads();
-      k_eq = kk - L.misc[5];
-    } else {
-      const bool in_lds = nc <= TK_CAND;
-      uint32_t prefix = (uint32_t)d1 << 19, mask = 0xFFF80000u;
-      for (int pass = 0; pass < 2; ++pass) {
-        const int sh = pass == 0 ? 9 : 0, nb = pass == 0 ? 1024 : 512;
-        for (int i = tid; i < 1024; i += nt) L.hist[i] = 0u;
-        __syncthreads();
-        if (in_lds) {
-          for (int i = tid; i < nc; i += nt) {
-            const uint32_t x = L.u.cand.key[i];
-            if ((x & mask) == prefix) atomicAdd(&L.hist[(x >> sh) & (nb - 1)], 1u);
-          }
-        } else {
-#pragma unroll(INREG ? 16 : 1)
-          for (int c0 = 0; c0 < NV; c0 += CHK) {
-            uint32_t uc[CHK];
-            chunk_keys(c0, uc);
-#pragma unroll
-            for (int v = 0; v < CHK; ++v)
-              if ((uc[v] & mask) == prefix) atomicAdd(&L.hist[(uc[v] >> sh) & (nb - 1)], 1u);
+        const int rank = L.u.c.rank[tid];
+        if (rank < k) {
+          const uint64_t c = L.u.c.key[tid];
+          const int id = (int)(0xFFFFFFFFu - (uint32_t)c);
+          const int n = L.u.c.n[tid], pre = L.u.c.pre[tid];
+          out[rank] = id;
+          span[rank] = make_int2(L.u.c.off[tid], n);
+          skey[rank] = sortable_float((uint32_t)(c >> 32));
+          selpre[rank] = pre;
+          atomicOr(&L.selw[id >> 5], 1u << (id & 31));
+          if (rank == k - 1) {
+            selpre[k] = pre + n;
+            ws.counts[4 * bh + 0] = pre + n;
           }
         }
-        __syncthreads();
-        find_bin(L, 1024, kk);
-        prefix |= (uint32_t)L.misc[1] << sh;
-        mask |= (uint32_t)(nb - 1) << sh;
-        kk -= L.misc[2];
-        __syncthreads();
       }
-      T = prefix;
-      k_eq = kk;
     }
   }
 
-  // 4. the selection in id order (keys > T, then the k_eq lowest ids with key == T)
-  if (k > 0) {
+  // 3. general path: exact k-th key T by bisection, selection in id order, rank-order sort
+  if (!fast && k > 0) {
+    uint32_t T = 0u;
+    auto block_count = [&](uint32_t c, uint32_t* slot) {  // keys >= c over the workgroup
+      int cnt = 0;
+#pragma unroll(INREG ? 16 : 1)
+      for (int c0 = 0; c0 < NV; c0 += CHK) {
+        uint32_t uc[CHK];
+        chunk_keys(c0, uc);
+#pragma unroll
+        for (int v = 0; v < CHK; ++v) cnt += __popcll(__ballot(uc[v] >= c));
+      }
+      if (lane == 0) atomicAdd(slot, (uint32_t)cnt);
+      __syncthreads();
+      return *slot;
+    };
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = T | (1u << bit);
+      if (block_count(c, &L.bis[bit]) >= (uint32_t)k) T = c;
+    }
+    const int cgt = T == 0xFFFFFFFFu ? 0 : (int)block_count(T + 1u, &L.bis[32]);
+    const int k_eq = k - cgt;
+    // selection in id order: keys > T, then the k_eq lowest ids with key == T
     int ngt = 0, neq = 0;
 #pragma unroll(INREG ? 16 : 1)
     for (int c0 = 0; c0 < NV; c0 += CHK) {
@@ -705,7 +598,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_reg(SeqArgs sa, DecodeArgs 
 #pragma unroll
       for (int v = 0; v < CHK; ++v) {
         ngt += uc[v] > T;
-        neq += (uc[v] == T);
+        neq += uc[v] == T;
       }
     }
 #pragma unroll
@@ -718,17 +611,19 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_reg(SeqArgs sa, DecodeArgs 
     const uint64_t wpre = __shfl(pre, 0, 64);
     int eq_seen = (int)(wpre & 0xFFFFFFFFu);
     int pos = (int)(wpre >> 32) + min(eq_seen, k_eq);
+    uint64_t* sb_ = (k <= TK_SORT) ? L.u.sortbuf : ws.sortg + (int64_t)bh * da.sort_stride;
 #pragma unroll(INREG ? 16 : 1)
     for (int c0 = 0; c0 < NV; c0 += CHK) {
       uint32_t uc[CHK];
       chunk_keys(c0, uc);
-      // spans of the chunk's ids, fetched unconditionally (clamped) so the loads overlap
       int ofv[CHK], szv[CHK];
+      float kfv[CHK];
 #pragma unroll
       for (int v = 0; v < CHK; ++v) {
         const int j = min(id_of(c0 + v), C - 1);
         ofv[v] = offs[j];
         szv[v] = sizes[j];
+        kfv[v] = keys[j];
       }
       // per block of 256 ids: lane-order prefix of (eq, selected) counts
 #pragma unroll
@@ -765,10 +660,9 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_reg(SeqArgs sa, DecodeArgs 
           if (sel[e]) {
             const int j = id_of(c0 + 4 * bb + e);
             span[p] = make_int2(ofv[4 * bb + e], szv[4 * bb + e]);
-            const uint64_t comp = ((uint64_t)uc[4 * bb + e] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)j);
-            if (k <= TK_CAND) L.u.sortbuf[p] = comp;
-            else ws.sortg[(int64_t)bh * da.sort_stride + p] = comp;
-            atomicOr(&L.excl[j >> 5], 1u << (j & 31));
+            skey[p] = kfv[4 * bb + e];
+            sb_[p] = ((uint64_t)uc[4 * bb + e] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)j);
+            atomicOr(&selw[j >> 5], 1u << (j & 31));
             ++p;
           }
         }
@@ -778,45 +672,74 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_reg(SeqArgs sa, DecodeArgs 
     }
     __threadfence_block();
     __syncthreads();
-    // 5. rank order (key desc, id asc) of the output ids
-    int32_t* out = sel_ids + (int64_t)bh * da.k_max;
+    // rank order (key desc, id asc) of the output ids
     if (k <= TK_RANK_SMALL) {
       if (tid < k) {
-        const uint64_t c = L.u.sortbuf[tid];
+        const uint64_t c = sb_[tid];
         int rank = 0;
 #pragma unroll 8
-        for (int i = 0; i < k; ++i) rank += L.u.sortbuf[i] > c;
+        for (int i = 0; i < k; ++i) rank += sb_[i] > c;
         out[rank] = (int32_t)(0xFFFFFFFFu - (uint32_t)(c & 0xFFFFFFFFu));
       }
     } else {
       int P2 = 1;
       while (P2 < k) P2 <<= 1;
-      uint64_t* sa_ = (k <= TK_CAND) ? L.u.sortbuf : ws.sortg + (int64_t)bh * da.sort_stride;
-      for (int i = k + tid; i < P2; i += nt) sa_[i] = 0;
-      if (k > TK_CAND) __threadfence_block();
+      for (int i = k + tid; i < P2; i += nt) sb_[i] = 0;
+      if (k > TK_SORT) __threadfence_block();
       __syncthreads();
-      bitonic_desc(sa_, P2, k > TK_CAND);
-      for (int i = tid; i < k; i += nt) out[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(sa_[i] & 0xFFFFFFFFu));
+      bitonic_desc(sb_, P2, k > TK_SORT);
+      for (int i = tid; i < k; i += nt) out[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)(sb_[i] & 0xFFFFFFFFu));
     }
   }
-  if (sel_ids != nullptr) {
-    int32_t* out = sel_ids + (int64_t)bh * da.k_max;
-    for (int i = k + tid; i < da.k_max; i += nt) out[i] = -1;
-  }
-  __syncthreads();
-  for (int i = tid; i < nwords; i += nt) excl_g[i] = L.excl[i];
 
-  // 6. steady rows: their cluster's estimation correction (rank key, NaN if none)
-  for (int i = tid; i < nS; i += nt) {
-    float cv = __uint_as_float(0x7FC00000u);
-    if (!allS) {
-      const int32_t j = L.sj[i];
-      const bool elig = (sizes[j] - steady_count(L, j)) > 0;
-      if (elig && !((L.excl[j >> 5] >> (j & 31)) & 1u)) cv = keys[j];
+  // 4. member-count prefix of the general path's selection, counts
+  if (!fast) {
+    int32_t* selpre = ws.selpre + kbase + bh;
+    __threadfence_block();
+    __syncthreads();
+    const int R = (k + nt - 1) / nt;
+    const int q0 = min(tid * R, k), q1 = min(q0 + R, k);
+    int64_t msum = 0;
+    for (int i = q0; i < q1; ++i) msum += span[i].y;
+    uint64_t tot;
+    int64_t run = (int64_t)block_scan_excl((uint64_t)msum, L.scan, &tot);
+    for (int i = q0; i < q1; ++i) {
+      selpre[i] = (int32_t)run;
+      run += span[i].y;
     }
-    corr[i] = cv;
+    if (tid == 0) {
+      selpre[k] = (int32_t)tot;
+      ws.counts[4 * bh + 0] = (int32_t)tot;
+    }
   }
-  selection_prefix(L, ws, kbase, bh, k, nS);
+  if (tid == 0) {
+    ws.counts[4 * bh + 1] = k;
+    ws.counts[4 * bh + 2] = sz.nS;
+    ws.counts[4 * bh + 3] = 0;
+  }
+  for (int i = k + tid; i < da.k_max; i += nt) out[i] = -1;
+
+  // 5. steady rows: the rank key of their cluster if it is not selected, else NaN
+  if (lds_sel) {
+    lds_barrier();
+  } else {
+    __threadfence_block();
+    __syncthreads();
+  }
+  float* corr = ws.corr + (int64_t)bh * da.scap;
+  for (int i = tid; i < sz.nS; i += nt) {
+    int32_t j;
+    float kj;
+    if (i < 2 * TK_THREADS) {
+      j = i < TK_THREADS ? sjr[0] : sjr[1];
+      kj = i < TK_THREADS ? kjr[0] : kjr[1];
+    } else {
+      j = ix.assign[row0 + steady_pos(sz, i)];
+      kj = keys[j];
+    }
+    const bool sel = (selw[j >> 5] >> (j & 31)) & 1u;
+    corr[i] = sel ? __uint_as_float(0x7FC00000u) : kj;
+  }
 }
 
 // ------------------------------------------------------------------ k_attend
@@ -843,14 +766,11 @@ __device__ __forceinline__ float dot8(const float* qf, uint4 kv) {
   s = fmaf(qf[5], bf16_hi(kv.z), s);
   s = fmaf(qf[6], bf16_lo(kv.w), s);
   s = fmaf(qf[7], bf16_hi(kv.w), s);
-  s += xor_shfl(s, 8);
-  s += xor_shfl(s, 4);
-  s += xor_shfl(s, 2);
-  s += xor_shfl(s, 1);
-  return s;
+  return row_sum16(s);
 }
 
-// U rows at once: scores s[u] (-inf when masked), estimation corrections cs[u] (-inf if none)
+// U rows at once: weight 2^(s - m) - 2^(cs - m) (exact term minus the centroid term it
+// replaces); s = cs = -inf for padding rows
 template <int U>
 __device__ __forceinline__ void softmax_rows(RowState& st, const float* s, const float* cs, const uint4* vv) {
   float mn = st.m;
@@ -873,277 +793,171 @@ __device__ __forceinline__ void softmax_rows(RowState& st, const float* s, const
   st.m = mn;
 }
 
+// Rows of one (b, h): the members of the selected clusters in selection order,
+// then the steady rows. Workgroup `part` takes rows [part*T/P, (part+1)*T/P),
+// each 16-lane group a contiguous 1/16 of that.
 template <int GS>
 __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs da, wave_index ix, DecodeWs ws,
                                                         const uint16_t* __restrict__ q) {
   __shared__ float red[4][PART];
-  __shared__ float wts[GS][EST_CH];
-  __shared__ float hred[GS][4][2];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, l16 = lane & 15, grp = lane >> 4;
   const int gi = wv * 4 + grp;  // 16-lane group in the workgroup
   const float sc = da.tau * LOG2E;
   const int per_bh = da.P;
-  const int nret = sa.B * da.H * per_bh;
-  if ((int)blockIdx.x < nret) {
-    // ---------------- gathered rows of one (b, h): the members of the selected
-    // clusters (id order, steady members skipped), then the steady rows.
-    // Workgroup `part` takes rows [part*T/P, (part+1)*T/P), each 16-lane group a
-    // contiguous 1/16 of that.
-    const int bh = blockIdx.x / per_bh, part = blockIdx.x % per_bh;
-    const int b = bh / da.H, h = bh % da.H, g = h / da.GS;
-    const SeqBase sb = seq_base(sa, b);
-    const int N = sb.N;
-    const int64_t row0 = sb.row + (int64_t)g * N;
-    const int64_t kbase = (int64_t)da.GS * sb.clu + (int64_t)h * sb.C;
-    const int M = ws.counts[4 * bh + 0], k = ws.counts[4 * bh + 1], nS = ws.counts[4 * bh + 2];
-    const int T = M + nS;
-    const int64_t a_end = min((int64_t)da.n_sink, (int64_t)N);
-    const int64_t c_beg = max((int64_t)N - (int64_t)da.n_local, a_end);
-    const int i0 = (int)((int64_t)T * part / per_bh), i1 = (int)((int64_t)T * (part + 1) / per_bh);
-    const int s0 = i0 + (int)((int64_t)(i1 - i0) * gi / 16), s1 = i0 + (int)((int64_t)(i1 - i0) * (gi + 1) / 16);
-    float qf[8];
-    {
-      const uint4 v = *reinterpret_cast<const uint4*>(q + (int64_t)bh * D + l16 * 8);
-      qf[0] = bf16_lo(v.x) * sc; qf[1] = bf16_hi(v.x) * sc; qf[2] = bf16_lo(v.y) * sc; qf[3] = bf16_hi(v.y) * sc;
-      qf[4] = bf16_lo(v.z) * sc; qf[5] = bf16_hi(v.z) * sc; qf[6] = bf16_lo(v.w) * sc; qf[7] = bf16_hi(v.w) * sc;
-    }
-    const uint16_t* Ks = reinterpret_cast<const uint16_t*>(ix.k_sorted) + row0 * D + l16 * 8;
-    const uint16_t* Vs = reinterpret_cast<const uint16_t*>(ix.v_sorted) + row0 * D + l16 * 8;
-    const int32_t* selpre = ws.selpre + kbase + bh;
-    const int2* span = ws.span + kbase;
-    const float* corr = ws.corr + (int64_t)bh * da.scap;
-    RowState st;
-    st.m = -INFINITY;
-    st.l = 0.f;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) st.acc[d] = 0.f;
-    // window of 16 selected clusters [ci0, ci0 + 16) held one per lane of the group:
-    // wpre = first row of the cluster, wsx = its first sorted slot
-    const int gbase = grp * 16;
-    int ci0 = 0, wpre = 0x7FFFFFFF, wsx = 0, wend = 0;
-    auto load_window = [&](int c0) {
-      ci0 = c0;
-      const int c = c0 + l16;
-      wpre = c <= k ? selpre[c] : 0x7FFFFFFF;
-      wsx = c < k ? span[c].x : 0;
-      wend = __shfl(c0 + 16 <= k ? selpre[min(c0 + 16, k)] : 0x7FFFFFFF, gbase, 64);
-    };
-    if (s0 < min(s1, M)) {
-      // 16-ary search for the last cluster whose first row is <= s0
-      int lo = 0, hi = k;
-      while (hi - lo > 1) {
-        const int step = (hi - lo + 15) / 16;
-        const int c = lo + l16 * step;
-        const int v = c < hi ? selpre[c] : 0x7FFFFFFF;
-        const uint32_t m = (uint32_t)(__ballot(v <= s0) >> gbase) & 0xFFFFu;
-        const int cnt = __popc(m);
-        lo = lo + (cnt - 1) * step;
-        hi = min(lo + step, hi);
-      }
-      load_window(lo);
-    }
-    constexpr int U = 4;
-    // members of the selected clusters: rows [s0, min(s1, M))
-    const int r1 = min(s1, M);
-    for (int r = s0; r < r1; r += U) {
-      if (r + U - 1 >= wend) {
-        // re-anchor the window at the cluster of row r; r <= wend here (the previous
-        // batch ended inside the window), and r == wend starts cluster ci0 + 16. A window
-        // anchored at r's cluster reaches at least 16 rows past r (clusters are non-empty).
-        const uint32_t m0 = (uint32_t)(__ballot(wpre <= r) >> gbase) & 0xFFFFu;
-        load_window(r >= wend ? ci0 + 16 : ci0 + __popc(m0) - 1);
-      }
-      uint4 kv[U], vv[U];
-      int32_t t[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int row = min(r + u, r1 - 1);
-        const uint32_t m = (uint32_t)(__ballot(wpre <= row) >> gbase) & 0xFFFFu;
-        const int l = __popc(m) - 1;
-        const int32_t p = __shfl(wsx, gbase + l, 64) + row - __shfl(wpre, gbase + l, 64);
-        t[u] = ix.perm[row0 + p];
-        kv[u] = *reinterpret_cast<const uint4*>(Ks + (int64_t)p * D);
-        vv[u] = *reinterpret_cast<const uint4*>(Vs + (int64_t)p * D);
-      }
-      float sv[U], cs[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float x = dot8(qf, kv[u]);
-        const bool keep = (r + u < r1) && !(t[u] < a_end || t[u] >= c_beg);
-        sv[u] = keep ? x : -INFINITY;
-        cs[u] = -INFINITY;
-      }
-      softmax_rows<U>(st, sv, cs, vv);
-    }
-    // steady rows: entries e = row - M for rows [max(s0, M), s1)
-    for (int r = max(s0, M); r < s1; r += U) {
-      int32_t p[U];
-      float cvv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int e = min(r + u, s1 - 1) - M;
-        const int64_t tt = e < a_end ? e : c_beg + (e - a_end);
-        p[u] = ix.inv_perm[row0 + tt];
-        cvv[u] = corr[e];
-      }
-      uint4 kv[U], vv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        kv[u] = *reinterpret_cast<const uint4*>(Ks + (int64_t)p[u] * D);
-        vv[u] = *reinterpret_cast<const uint4*>(Vs + (int64_t)p[u] * D);
-      }
-      float sv[U], cs[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float x = dot8(qf, kv[u]);
-        const bool valid = r + u < s1;
-        sv[u] = valid ? x : -INFINITY;
-        cs[u] = (valid && cvv[u] == cvv[u]) ? cvv[u] * sc : -INFINITY;
-      }
-      softmax_rows<U>(st, sv, cs, vv);
-    }
-    // merge the 4 groups of the wave, then the 4 waves
-#pragma unroll
-    for (int o = 16; o < 64; o <<= 1) {
-      const float m2 = xor_shfl(st.m, o), l2 = xor_shfl(st.l, o);
-      float a2[8];
-#pragma unroll
-      for (int d = 0; d < 8; ++d) a2[d] = xor_shfl(st.acc[d], o);
-      merge_state(st.m, st.l, st.acc, m2, l2, a2, 8);
-    }
-    if (grp == 0) {
-      if (l16 == 0) { red[wv][0] = st.m; red[wv][1] = st.l; }
-#pragma unroll
-      for (int d = 0; d < 8; ++d) red[wv][4 + l16 * 8 + d] = st.acc[d];
-    }
-    __syncthreads();
-    if (threadIdx.x < D) {
-      const int d = threadIdx.x;
-      float M = -INFINITY;
-      for (int w2 = 0; w2 < 4; ++w2) M = fmaxf(M, red[w2][0]);
-      float Ls = 0.f, A = 0.f;
-      if (M != -INFINITY)
-        for (int w2 = 0; w2 < 4; ++w2) {
-          const float f = exp2f(red[w2][0] - M);
-          Ls += red[w2][1] * f;
-          A += red[w2][4 + d] * f;
-        }
-      float* o = ws.part + ((int64_t)bh * da.NP + part) * PART;
-      if (d == 0) { o[0] = M; o[1] = Ls; }
-      o[4 + d] = A;
-    }
-    return;
-  }
-  // ---------------- estimation role: clusters [j0, j0 + EST_CH) of one (b, g), all GS heads
-  int w = blockIdx.x - nret, b = 0;
-  for (;; ++b) {
-    const int nch = (sa.C[b] + EST_CH - 1) / EST_CH;
-    if (w < sa.G * nch) break;
-    w -= sa.G * nch;
-  }
+  const int bh = blockIdx.x / per_bh, part = blockIdx.x % per_bh;
+  const int b = bh / da.H, h = bh % da.H, g = h / da.GS;
   const SeqBase sb = seq_base(sa, b);
-  const int C = sb.C;
-  const int nch = (C + EST_CH - 1) / EST_CH;
-  const int g = w / nch, chunk = w % nch;
-  const int j0 = chunk * EST_CH;
-  const int64_t clu0 = sb.clu + (int64_t)g * C;
-  const int nwords = (C + 31) >> 5;
-  int64_t wbase = 0;
-  for (int i = 0; i < b; ++i) wbase += (int64_t)da.H * ((sa.C[i] + 31) >> 5);
+  const int N = sb.N;
+  const int64_t row0 = sb.row + (int64_t)g * N;
+  const int64_t kbase = (int64_t)da.GS * sb.clu + (int64_t)h * sb.C;
+  const int M = ws.counts[4 * bh + 0], k = ws.counts[4 * bh + 1], nS = ws.counts[4 * bh + 2];
+  const int T = M + nS;
+  const Steady sz = steady_of(da, N);
+  const int i0 = (int)((int64_t)T * part / per_bh), i1 = (int)((int64_t)T * (part + 1) / per_bh);
+  const int s0 = i0 + (int)((int64_t)(i1 - i0) * gi / 16), s1 = i0 + (int)((int64_t)(i1 - i0) * (gi + 1) / 16);
+  float qf[8];
   {
-    const int jj = threadIdx.x;
-    const int j = j0 + jj;
-    const int n = j < C ? ix.sizes[clu0 + j] : 0;
+    const uint4 v = *reinterpret_cast<const uint4*>(q + (int64_t)bh * D + l16 * 8);
+    qf[0] = bf16_lo(v.x) * sc; qf[1] = bf16_hi(v.x) * sc; qf[2] = bf16_lo(v.y) * sc; qf[3] = bf16_hi(v.y) * sc;
+    qf[4] = bf16_lo(v.z) * sc; qf[5] = bf16_hi(v.z) * sc; qf[6] = bf16_lo(v.w) * sc; qf[7] = bf16_hi(v.w) * sc;
+  }
+  const uint16_t* Ks = reinterpret_cast<const uint16_t*>(ix.k_sorted) + row0 * D + l16 * 8;
+  const uint16_t* Vs = reinterpret_cast<const uint16_t*>(ix.v_sorted) + row0 * D + l16 * 8;
+  const int32_t* selpre = ws.selpre + kbase + bh;
+  const int2* span = ws.span + kbase;
+  const float* skey = ws.skey + kbase;
+  const float* corr = ws.corr + (int64_t)bh * da.scap;
+  RowState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
 #pragma unroll
-    for (int hh = 0; hh < GS; ++hh) {
-      const int h = g * GS + hh;
-      float s = -INFINITY;
-      if (n > 0) {
-        const uint32_t ew = ws.excl[wbase + (int64_t)h * nwords + (j >> 5)];
-        if (!((ew >> (j & 31)) & 1u)) s = ws.keys[(int64_t)GS * sb.clu + (int64_t)h * C + j] * sc;
+  for (int d = 0; d < 8; ++d) st.acc[d] = 0.f;
+  // window of 16 selected clusters [ci0, ci0 + 16) held one per lane of the group:
+  // wpre = first row of the cluster, wsx = its first sorted slot, wkey = its centroid score
+  const int gbase = grp * 16;
+  int ci0 = 0, wpre = 0x7FFFFFFF, wsx = 0, wend = 0;
+  float wkey = -INFINITY;
+  auto load_window = [&](int c0) {
+    ci0 = c0;
+    const int c = c0 + l16;
+    wpre = c <= k ? selpre[c] : 0x7FFFFFFF;
+    wsx = c < k ? span[c].x : 0;
+    wkey = c < k ? skey[c] * sc : -INFINITY;
+    wend = __shfl(c0 + 16 <= k ? selpre[min(c0 + 16, k)] : 0x7FFFFFFF, gbase, 64);
+  };
+  if (s0 < min(s1, M)) {
+    // 16-ary search for the last cluster whose first row is <= s0
+    int lo = 0, hi = k;
+    while (hi - lo > 1) {
+      const int step = (hi - lo + 15) / 16;
+      const int c = lo + l16 * step;
+      const int v = c < hi ? selpre[c] : 0x7FFFFFFF;
+      const uint32_t m = (uint32_t)(__ballot(v <= s0) >> gbase) & 0xFFFFu;
+      const int cnt = __popc(m);
+      lo = lo + (cnt - 1) * step;
+      hi = min(lo + step, hi);
+    }
+    load_window(lo);
+  }
+  constexpr int U = 4;
+  // members of the selected clusters: rows [s0, min(s1, M))
+  const int r1 = min(s1, M);
+  for (int r = s0; r < r1; r += U) {
+    if (r + U - 1 >= wend) {
+      // re-anchor the window at the cluster of row r; r <= wend here (the previous
+      // batch ended inside the window), and r == wend starts cluster ci0 + 16. A window
+      // anchored at r's cluster reaches at least 16 rows past r (clusters are non-empty).
+      const uint32_t m0 = (uint32_t)(__ballot(wpre <= r) >> gbase) & 0xFFFFu;
+      load_window(r >= wend ? ci0 + 16 : ci0 + __popc(m0) - 1);
+    }
+    uint4 kv[U], vv[U];
+    int32_t t[U];
+    float ck[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int row = min(r + u, r1 - 1);
+      const uint32_t m = (uint32_t)(__ballot(wpre <= row) >> gbase) & 0xFFFFu;
+      const int l = gbase + __popc(m) - 1;
+      const int32_t p = __shfl(wsx, l, 64) + row - __shfl(wpre, l, 64);
+      ck[u] = __shfl(wkey, l, 64);
+      t[u] = ix.perm[row0 + p];
+      kv[u] = *reinterpret_cast<const uint4*>(Ks + (int64_t)p * D);
+      vv[u] = *reinterpret_cast<const uint4*>(Vs + (int64_t)p * D);
+    }
+    float sv[U], cs[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float x = dot8(qf, kv[u]);
+      const bool valid = r + u < r1;
+      const bool steady = t[u] < sz.a_end || t[u] >= sz.c_beg;  // counted exactly with the steady rows
+      sv[u] = (valid && !steady) ? x : -INFINITY;
+      cs[u] = valid ? ck[u] : -INFINITY;
+    }
+    softmax_rows<U>(st, sv, cs, vv);
+  }
+  // steady rows: entries e = row - M for rows [max(s0, M), s1)
+  for (int r = max(s0, M); r < s1; r += U) {
+    int32_t p[U];
+    float cvv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = min(r + u, s1 - 1) - M;
+      p[u] = ix.inv_perm[row0 + steady_pos(sz, e)];
+      cvv[u] = corr[e];
+    }
+    uint4 kv[U], vv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      kv[u] = *reinterpret_cast<const uint4*>(Ks + (int64_t)p[u] * D);
+      vv[u] = *reinterpret_cast<const uint4*>(Vs + (int64_t)p[u] * D);
+    }
+    float sv[U], cs[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float x = dot8(qf, kv[u]);
+      const bool valid = r + u < s1;
+      sv[u] = valid ? x : -INFINITY;
+      cs[u] = (valid && cvv[u] == cvv[u]) ? cvv[u] * sc : -INFINITY;
+    }
+    softmax_rows<U>(st, sv, cs, vv);
+  }
+  // merge the 4 groups of the wave, then the 4 waves
+#pragma unroll
+  for (int o = 16; o < 64; o <<= 1) {
+    const float m2 = xor_shfl(st.m, o), l2 = xor_shfl(st.l, o);
+    float a2[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) a2[d] = xor_shfl(st.acc[d], o);
+    merge_state(st.m, st.l, st.acc, m2, l2, a2, 8);
+  }
+  if (grp == 0) {
+    if (l16 == 0) { red[wv][0] = st.m; red[wv][1] = st.l; }
+#pragma unroll
+    for (int d = 0; d < 8; ++d) red[wv][4 + l16 * 8 + d] = st.acc[d];
+  }
+  __syncthreads();
+  if (threadIdx.x < D) {
+    const int d = threadIdx.x;
+    float Mx = -INFINITY;
+    for (int w2 = 0; w2 < 4; ++w2) Mx = fmaxf(Mx, red[w2][0]);
+    float Ls = 0.f, A = 0.f;
+    if (Mx != -INFINITY)
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const float f = exp2f(red[w2][0] - Mx);
+        Ls += red[w2][1] * f;
+        A += red[w2][4 + d] * f;
       }
-      float mx = s;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, xor_shfl(mx, o));
-      if (lane == 0) hred[hh][wv][0] = mx;
-      wts[hh][jj] = s;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int hh = 0; hh < GS; ++hh) {
-      const float M = fmaxf(fmaxf(hred[hh][0][0], hred[hh][1][0]), fmaxf(hred[hh][2][0], hred[hh][3][0]));
-      const float s = wts[hh][jj];
-      const float wgt = (s == -INFINITY) ? 0.f : exp2f(s - M);
-      float ls = wgt * (float)n;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) ls += xor_shfl(ls, o);
-      __syncthreads();
-      wts[hh][jj] = wgt;
-      if (lane == 0) hred[hh][wv][1] = ls;
-      if (threadIdx.x == 0) hred[hh][0][0] = M;
-    }
-    __syncthreads();
-  }
-  float acc[GS][8];
-#pragma unroll
-  for (int hh = 0; hh < GS; ++hh)
-#pragma unroll
-    for (int d = 0; d < 8; ++d) acc[hh][d] = 0.f;
-  const float* vs = ix.vsum + clu0 * D + l16 * 8;
-  constexpr int UE = 4;
-  for (int jb = gi; jb < EST_CH; jb += 16 * UE) {
-    float4 v0[UE], v1[UE];
-#pragma unroll
-    for (int u = 0; u < UE; ++u) {
-      const int j = min(j0 + jb + 16 * u, C - 1);
-      v0[u] = *reinterpret_cast<const float4*>(vs + (int64_t)j * D);
-      v1[u] = *reinterpret_cast<const float4*>(vs + (int64_t)j * D + 4);
-    }
-#pragma unroll
-    for (int u = 0; u < UE; ++u) {
-      const int jj = jb + 16 * u;
-      if (jj >= EST_CH || j0 + jj >= C) continue;
-#pragma unroll
-      for (int hh = 0; hh < GS; ++hh) {
-        const float wgt = wts[hh][jj];
-        acc[hh][0] = fmaf(wgt, v0[u].x, acc[hh][0]); acc[hh][1] = fmaf(wgt, v0[u].y, acc[hh][1]);
-        acc[hh][2] = fmaf(wgt, v0[u].z, acc[hh][2]); acc[hh][3] = fmaf(wgt, v0[u].w, acc[hh][3]);
-        acc[hh][4] = fmaf(wgt, v1[u].x, acc[hh][4]); acc[hh][5] = fmaf(wgt, v1[u].y, acc[hh][5]);
-        acc[hh][6] = fmaf(wgt, v1[u].z, acc[hh][6]); acc[hh][7] = fmaf(wgt, v1[u].w, acc[hh][7]);
-      }
-    }
-  }
-#pragma unroll
-  for (int hh = 0; hh < GS; ++hh) {
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      acc[hh][d] += xor_shfl(acc[hh][d], 16);
-      acc[hh][d] += xor_shfl(acc[hh][d], 32);
-    }
-  }
-  for (int hh = 0; hh < GS; ++hh) {
-    if (grp == 0)
-#pragma unroll
-      for (int d = 0; d < 8; ++d) red[wv][4 + l16 * 8 + d] = acc[hh][d];
-    __syncthreads();
-    const int h = g * GS + hh;
-    const int bh = b * da.H + h;
-    if (threadIdx.x < D) {
-      const int d = threadIdx.x;
-      float* o = ws.part + ((int64_t)bh * da.NP + da.P + chunk) * PART;
-      const float A = red[0][4 + d] + red[1][4 + d] + red[2][4 + d] + red[3][4 + d];
-      const float Ls = hred[hh][0][1] + hred[hh][1][1] + hred[hh][2][1] + hred[hh][3][1];
-      const float M = hred[hh][0][0];
-      if (d == 0) { o[0] = (Ls > 0.f) ? M : -INFINITY; o[1] = Ls; }
-      o[4 + d] = A;
-    }
-    __syncthreads();
+    float* o = ws.part + ((int64_t)bh * da.NP + part) * PART;
+    if (d == 0) { o[0] = Mx; o[1] = Ls; }
+    o[4 + d] = A;
   }
 }
 
 // ------------------------------------------------------------------ k_merge
-// Log-sum-exp merge of the partials of one (b, h): thread (sub, dq) takes dims
-// 4dq..4dq+3 over partials sub, sub + 8, ...; the 8 subsets meet in LDS.
+// Log-sum-exp merge of the partials of one (b, h): the P row partials and one
+// centroid partial per k_score chunk. Thread (sub, dq) takes dims 4dq..4dq+3
+// over partials sub, sub + 8, ...; the 8 subsets meet in LDS. Row partials may
+// carry negative sums (they take centroid terms back out); the total is positive.
 __global__ __launch_bounds__(256) void k_merge(SeqArgs sa, DecodeArgs da, DecodeWs ws, float* __restrict__ out,
                                                float* __restrict__ lse) {
   __shared__ float4 accs[8][32];
@@ -1151,13 +965,12 @@ __global__ __launch_bounds__(256) void k_merge(SeqArgs sa, DecodeArgs da, Decode
   __shared__ float mx[4];
   const int bh = blockIdx.x;
   const int b = bh / da.H;
-  const int npart = da.P + (sa.C[b] + EST_CH - 1) / EST_CH;
+  const int npart = da.P + (sa.C[b] + SC - 1) / SC;
   const float* pp = ws.part + (int64_t)bh * da.NP * PART;
   const int tid = threadIdx.x, dq = tid & 31, sub = tid >> 5;
   float M = -INFINITY;
   for (int i = tid; i < npart; i += 256) M = fmaxf(M, pp[(int64_t)i * PART]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, xor_shfl(M, o));
+  M = wave_max(M);
   if ((tid & 63) == 0) mx[tid >> 6] = M;
   __syncthreads();
   M = fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]));
@@ -1192,63 +1005,59 @@ __global__ __launch_bounds__(256) void k_merge(SeqArgs sa, DecodeArgs da, Decode
 }
 
 // ------------------------------------------------------------------ host side
-size_t topk_lds_bytes() { return sizeof(TopkLds); }
-
 template <int GS>
 static void launch_gs(const SeqArgs& sa, const DecodeArgs& da, const wave_index& ix, const DecodeWs& ws,
-                      const uint16_t* q, float* out, int32_t* sel_ids, float* lse, hipStream_t st, int nscore,
-                      int nest) {
-  const uint16_t* chat = reinterpret_cast<const uint16_t*>(ix.centroids_bf16);
+                      const uint16_t* q, float* out, int32_t* sel_ids, float* lse, hipStream_t st, int nscore) {
   prof_begin("k_score", st);
-  hipLaunchKernelGGL(k_score<GS>, dim3(nscore), dim3(256), 0, st, sa, da.H, chat, q, ws.keys);
+  hipLaunchKernelGGL(k_score<GS>, dim3(nscore), dim3(SCORE_THREADS), sizeof(ScoreLds<GS>), st, sa, da, ix, q, ws);
   prof_end(st);
   prof_begin("k_topk", st);
   const dim3 tg(sa.B * da.H), tb(TK_THREADS);
   const size_t tl = sizeof(TopkLds);
   switch (da.NV) {
-    case 4: hipLaunchKernelGGL(k_topk_reg<4>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
-    case 8: hipLaunchKernelGGL(k_topk_reg<8>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
-    case 16: hipLaunchKernelGGL(k_topk_reg<16>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
-    case 32: hipLaunchKernelGGL(k_topk_reg<32>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
-    case 64: hipLaunchKernelGGL(k_topk_reg<64>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
-    default: hipLaunchKernelGGL(k_topk_any, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
+    case 4: hipLaunchKernelGGL(k_topk<4>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
+    case 8: hipLaunchKernelGGL(k_topk<8>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
+    case 16: hipLaunchKernelGGL(k_topk<16>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
+    default: hipLaunchKernelGGL(k_topk<0>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
   }
   prof_end(st);
   prof_begin("k_attend", st);
-  hipLaunchKernelGGL(k_attend<GS>, dim3(sa.B * da.H * da.P + nest), dim3(ATT_THREADS), 0, st, sa, da, ix,
-                     ws, q);
+  hipLaunchKernelGGL(k_attend<GS>, dim3(sa.B * da.H * da.P), dim3(ATT_THREADS), 0, st, sa, da, ix, ws, q);
   prof_end(st);
   prof_begin("k_merge", st);
   hipLaunchKernelGGL(k_merge, dim3(sa.B * da.H), dim3(256), 0, st, sa, da, ws, out, lse);
   prof_end(st);
 }
 
+template <int GS>
+static void score_attr() {
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<GS>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            sizeof(ScoreLds<GS>));
+}
+
 hipError_t launch_decode(const SeqArgs& sa, const DecodeArgs& da, const wave_index& ix, const DecodeWs& ws,
                          const uint16_t* q, float* out, int32_t* sel_ids, float* lse, hipStream_t st) {
   static bool attrs = false;
   if (!attrs) {
-    const void* fns[] = {reinterpret_cast<const void*>(&k_topk_any), reinterpret_cast<const void*>(&k_topk_reg<4>),
-                         reinterpret_cast<const void*>(&k_topk_reg<8>), reinterpret_cast<const void*>(&k_topk_reg<16>),
-                         reinterpret_cast<const void*>(&k_topk_reg<32>),
-                         reinterpret_cast<const void*>(&k_topk_reg<64>)};
+    const void* fns[] = {reinterpret_cast<const void*>(&k_topk<0>), reinterpret_cast<const void*>(&k_topk<4>),
+                         reinterpret_cast<const void*>(&k_topk<8>), reinterpret_cast<const void*>(&k_topk<16>)};
     for (const void* f : fns)
       (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(TopkLds));
+    score_attr<1>(); score_attr<2>(); score_attr<3>(); score_attr<4>();
+    score_attr<5>(); score_attr<6>(); score_attr<7>(); score_attr<8>();
     attrs = true;
   }
-  int nscore = 0, nest = 0;
-  for (int b = 0; b < sa.B; ++b) {
-    nscore += sa.G * ((sa.C[b] + SCORE_CH - 1) / SCORE_CH);
-    nest += sa.G * ((sa.C[b] + EST_CH - 1) / EST_CH);
-  }
+  int nscore = 0;
+  for (int b = 0; b < sa.B; ++b) nscore += sa.G * ((sa.C[b] + SC - 1) / SC);
   switch (da.GS) {
-    case 1: launch_gs<1>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
-    case 2: launch_gs<2>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
-    case 3: launch_gs<3>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
-    case 4: launch_gs<4>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
-    case 5: launch_gs<5>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
-    case 6: launch_gs<6>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
-    case 7: launch_gs<7>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
-    default: launch_gs<8>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
+    case 1: launch_gs<1>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore); break;
+    case 2: launch_gs<2>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore); break;
+    case 3: launch_gs<3>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore); break;
+    case 4: launch_gs<4>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore); break;
+    case 5: launch_gs<5>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore); break;
+    case 6: launch_gs<6>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore); break;
+    case 7: launch_gs<7>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore); break;
+    default: launch_gs<8>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore); break;
   }
   return hipGetLastError();
 }

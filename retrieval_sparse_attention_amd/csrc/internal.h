@@ -15,33 +15,33 @@ struct DecodeArgs {
   int32_t n_sink, n_local;
   int32_t k_max;          // id columns of the output
   int32_t P;              // gathered-row workgroups per (b, h)
-  int32_t NV;             // keys per lane of the register top-k (0: the general kernel)
-  int32_t NP;             // partial slots per (b, h): P + max_b ceil(C_b / DEC_EST_CH)
+  int32_t NV;             // keys per lane of the register top-k (4, 8, 16), 0: keys read from memory
+  int32_t NP;             // partial slots per (b, h): P + max_b ceil(C_b / DEC_SCORE_CH)
   int32_t scap;           // steady entries per (b, h)
   float tau;              // 1/sqrt(128)
   int32_t sort_stride;    // per-(b, h) entries of the global sort buffer
-  int32_t pad;
+  int32_t NVg;            // keys per lane when NV == 0 (a multiple of 16)
   int32_t kreq[MAXB];     // min(ceil(topk_frac * C_b), C_b), binary64 on the host
 };
 
 struct DecodeWs {
   float* keys;       // [sum_b H*C_b] rank keys
   uint32_t* key32;   // [sum_b H*C_b] sortable keys, 0 = not eligible
-  int2* span;        // [sum_b H*C_b] (first sorted slot, size) of the selection, id order
+  int2* span;        // [sum_b H*C_b] (first sorted slot, size) of the i-th selected cluster
+  float* skey;       // [sum_b H*C_b] rank key of the i-th selected cluster
   int32_t* selpre;   // [sum_b H*(C_b+1)] rows of the selection before its i-th cluster
-  uint32_t* excl;    // [sum_b H*ceil(C_b/32)] clusters excluded from estimation
-  float* corr;       // [B*H*scap] rank key of a steady row's cluster if it is estimated, else NaN
+  uint32_t* selw;    // [sum_b H*ceil(C_b/32)] selection bitmap when C_b > 65536
+  float* corr;       // [B*H*scap] rank key of a steady row's cluster if it is not selected, else NaN
   int32_t* counts;   // [B*H*4] rows of the selected clusters, k, steady rows, 0
   float* part;       // [B*H*NP*132] partial softmax states
   uint64_t* sortg;   // [B*H*pow2(C_max)] global sort buffer (only when k_max > 4096)
 };
 
-constexpr int DEC_EST_CH = 256;
+constexpr int DEC_SCORE_CH = 128;
 constexpr int DEC_PART = 132;
 constexpr int DEC_SORT_LDS = 4096;
 constexpr int DEC_ROWS_PER_WG = 256;
 
-size_t topk_lds_bytes();
 hipError_t launch_decode(const SeqArgs& sa, const DecodeArgs& da, const wave_index& ix, const DecodeWs& ws,
                          const uint16_t* q, float* out, int32_t* sel_ids, float* lse, hipStream_t st);
 

@@ -107,7 +107,7 @@ wave_status hip_device_ok() {
 // ------------------------------------------------------------------ decode sizes
 struct DecodePlan {
   wave::DecodeArgs da;
-  size_t keys, key32, span, selpre, excl, corr, counts, part, sortg, total;
+  size_t keys, key32, span, skey, selpre, selw, corr, counts, part, sortg, total;
 };
 
 wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t n_local, double frac,
@@ -140,7 +140,7 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
     da.kreq[b] = (int32_t)x;
     kmax = da.kreq[b] > kmax ? da.kreq[b] : kmax;
     Cmax = C > Cmax ? (int)C : Cmax;
-    const int nE = (int)((C + wave::DEC_EST_CH - 1) / wave::DEC_EST_CH);
+    const int nE = (int)((C + wave::DEC_SCORE_CH - 1) / wave::DEC_SCORE_CH);
     nEmax = nE > nEmax ? nE : nEmax;
     sumC += C;
     sumW += (C + 31) / 32;
@@ -171,8 +171,9 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
   da.P = (int32_t)Pw;
   da.NP = da.P + nEmax;
   da.NV = 0;
-  for (int nv = 4; nv <= 64; nv *= 2)
+  for (int nv = 4; nv <= 16; nv *= 2)
     if (16 * 64 * nv >= Cmax) { da.NV = nv; break; }
+  da.NVg = (int32_t)(((Cmax + 16 * 64 * 16 - 1) / (16 * 64 * 16)) * 16);
   int sort_stride = 0;
   if (kmax > wave::DEC_SORT_LDS) {
     sort_stride = 1;
@@ -184,8 +185,9 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
   P->keys = o;   o += align256(4 * (size_t)(H * sumC));
   P->key32 = o;  o += align256(4 * (size_t)(H * sumC));
   P->span = o;   o += align256(8 * (size_t)(H * sumC));
+  P->skey = o;   o += align256(4 * (size_t)(H * sumC));
   P->selpre = o; o += align256(4 * (size_t)(H * sumC + BH));
-  P->excl = o;   o += align256(4 * (size_t)(H * sumW));
+  P->selw = o;   o += align256(4 * (size_t)(H * sumW));
   P->corr = o;   o += align256(4 * (size_t)(BH * da.scap));
   P->counts = o; o += align256(4 * (size_t)(BH * 4));
   P->part = o;   o += align256(4 * (size_t)(BH * da.NP * wave::DEC_PART));
@@ -319,8 +321,9 @@ wave_status wave_attn_decode(const wave_index* index, const void* q, int32_t n_q
   dw.keys = reinterpret_cast<float*>(w + P.keys);
   dw.key32 = reinterpret_cast<uint32_t*>(w + P.key32);
   dw.span = reinterpret_cast<int2*>(w + P.span);
+  dw.skey = reinterpret_cast<float*>(w + P.skey);
   dw.selpre = reinterpret_cast<int32_t*>(w + P.selpre);
-  dw.excl = reinterpret_cast<uint32_t*>(w + P.excl);
+  dw.selw = reinterpret_cast<uint32_t*>(w + P.selw);
   dw.corr = reinterpret_cast<float*>(w + P.corr);
   dw.counts = reinterpret_cast<int32_t*>(w + P.counts);
   dw.part = reinterpret_cast<float*>(w + P.part);
