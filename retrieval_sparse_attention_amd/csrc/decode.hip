@@ -5,18 +5,20 @@
 // attention (retrieval zone), sink and recent tokens are attended exactly
 // (steady zone), and every other cluster contributes through its centroid
 // (estimation zone). Four launches per call, all on the caller's stream:
-//   k_score  -- one pass over the centroid rows and value sums of a kv head:
-//               rank keys of the H/G q heads, eligibility, and the estimation
-//               term of every cluster as partial softmax states
-//   k_topk   -- per (sequence, q head): exact top-k by (key desc, id asc), the
-//               selected ids and spans, steady-row corrections
+//   k_score  -- one pass over the centroid rows of a kv head: rank keys of the
+//               H/G q heads and eligibility
+//   k_topk   -- two roles in one grid: per (sequence, q head) the exact top-k by
+//               (key desc, id asc), selected ids and spans and steady-row
+//               corrections; and, on the remaining CUs meanwhile, the estimation
+//               term of every cluster (one pass over the value sums) as partial
+//               softmax states
 //   k_attend -- online-softmax attention over the selected clusters' sorted rows
 //               and over the steady rows; every row of a cluster whose centroid
 //               term was counted in k_score takes that term back out
 //   k_merge  -- log-sum-exp merge of the partials of every (sequence, q head)
 //
 // Estimation bookkeeping. The pages' estimation zone is E \ R with the value
-// sums and sizes of the clusters' non-steady members. k_score adds the centroid
+// sums and sizes of the clusters' non-steady members. k_topk adds the centroid
 // term e^{s_j} (n_j, Vsum_j) of EVERY cluster; each member row t of a selected
 // cluster and each steady row t of a cluster that is not selected then adds
 // -e^{s_j} (1, v_t) in k_attend. Summed, this leaves exactly the centroid terms
@@ -30,6 +32,7 @@
 namespace wave {
 
 constexpr int SC = DEC_SCORE_CH;  // clusters per k_score workgroup
+constexpr int EC = DEC_EST_CH;    // clusters per estimation workgroup
 constexpr int SCORE_THREADS = 256;
 constexpr int TK_THREADS = 1024;
 constexpr int TK_CAP = 1024;      // candidates of the fast selection
@@ -69,28 +72,21 @@ __device__ __forceinline__ int64_t steady_pos(const Steady& s, int i) {
 // two bf16 values equals a rounded product then a rounded add), then an xor
 // butterfly over the 16 lanes with strides 8, 4, 2, 1, then +0.0f.
 //
-// One workgroup per (b, g, 128 clusters). All of the workgroup's HBM reads are
-// issued at entry: centroid rows first, the chunk's value sums (64 KB, 16 float4
-// per thread in registers) last, so the rank keys and weights are computed while
-// the value sums stream in. A cluster is eligible (in E) when it has a member
-// outside the steady zone; the steady tokens' clusters are counted only by
-// workgroups whose ids can hold them (the first and the last segments). Per q
-// head the workgroup writes one partial softmax state of its clusters' centroid
-// terms: weights 2^(r*tau*log2(e) - m) times (n_j, Vsum_j).
+// One workgroup per (b, g, 128 clusters), 16-lane groups over the centroid rows.
+// A cluster is eligible (in E) when it has a member outside the steady zone; the
+// steady tokens' clusters are counted only by workgroups whose ids can hold them
+// (the first and the last segments).
 template <int GS>
 struct ScoreLds {
-  float red[4][GS][D];  // per wave: the q heads' weighted value sums
-  float kw[GS][SC];     // rank keys, then estimation weights
-  int32_t nsz[SC];      // cluster sizes
-  int32_t scnt[SC];     // steady members
-  float hred[GS][2][2];
+  float kw[GS][SC];   // rank keys
+  int32_t nsz[SC];    // cluster sizes
+  int32_t scnt[SC];   // steady members
 };
 
 template <int GS>
-__global__ __launch_bounds__(SCORE_THREADS, 2) void k_score(SeqArgs sa, DecodeArgs da, wave_index ix,
-                                                            const uint16_t* __restrict__ q, DecodeWs ws) {
-  extern __shared__ uint8_t smem[];
-  ScoreLds<GS>& S = *reinterpret_cast<ScoreLds<GS>*>(smem);
+__global__ __launch_bounds__(SCORE_THREADS) void k_score(SeqArgs sa, DecodeArgs da, wave_index ix,
+                                                         const uint16_t* __restrict__ q, DecodeWs ws) {
+  __shared__ ScoreLds<GS> S;
   int w = blockIdx.x, b = 0;
   for (;; ++b) {
     const int nch = (sa.C[b] + SC - 1) / SC;
@@ -105,7 +101,6 @@ __global__ __launch_bounds__(SCORE_THREADS, 2) void k_score(SeqArgs sa, DecodeAr
   const int64_t clu0 = sb.clu + (int64_t)g * C, row0 = sb.row + (int64_t)g * N;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, grp = lane >> 4;
   const int gi = wv * 4 + grp;
-  const float sc = da.tau * LOG2E;
 
   // steady tokens whose clusters may lie in this chunk (the first and the last segments):
   // their clusters, up to 4 per thread in registers, loaded first
@@ -141,18 +136,8 @@ __global__ __launch_bounds__(SCORE_THREADS, 2) void k_score(SeqArgs sa, DecodeAr
     qf[hh][4] = bf16_lo(v.z); qf[hh][5] = bf16_hi(v.z);
     qf[hh][6] = bf16_lo(v.w); qf[hh][7] = bf16_hi(v.w);
   }
-  const int nsz_r = tid < nc ? ix.sizes[clu0 + j0 + tid] : 0;
-  // value sums: thread (sub, dq) takes dims 4dq..4dq+3 of clusters sub + 8u; rows
-  // past the chunk repeat its last row (their weights are zero)
-  const int sub = tid >> 5, dq = tid & 31;
-  float4 vreg[SC / 8];
-  {
-    const float4* vsrc = reinterpret_cast<const float4*>(ix.vsum + (clu0 + j0) * D) + dq;
-#pragma unroll
-    for (int u = 0; u < SC / 8; ++u) vreg[u] = vsrc[(int64_t)min(sub + 8 * u, nc - 1) * (D / 4)];
-  }
   if (tid < SC) {
-    S.nsz[tid] = nsz_r;
+    S.nsz[tid] = tid < nc ? ix.sizes[clu0 + j0 + tid] : 0;
     S.scnt[tid] = 0;
   }
   lds_barrier();
@@ -185,7 +170,7 @@ __global__ __launch_bounds__(SCORE_THREADS, 2) void k_score(SeqArgs sa, DecodeAr
     }
   }
   lds_barrier();
-  // 3. keys and eligibility out; the first two waves form the per-head weights
+  // 3. keys and eligibility out
   const int64_t kb = (int64_t)GS * sb.clu + (int64_t)g * GS * C + j0;
   for (int e = tid; e < GS * SC; e += SCORE_THREADS) {
     const int hh = e / SC, jj = e % SC;
@@ -197,67 +182,133 @@ __global__ __launch_bounds__(SCORE_THREADS, 2) void k_score(SeqArgs sa, DecodeAr
       ws.key32[kb + (int64_t)hh * C + jj] = elig ? float_sortable(key) : 0u;
     }
   }
-  float sv[GS];
-  if (tid < SC) {
-    const bool live = tid < nc && S.nsz[tid] > 0;
+}
+
+// ------------------------------------------------------------------ estimation role
+// Workgroup (b, g, 512 clusters) of the k_topk grid: weights 2^(r tau log2(e) - m)
+// of every cluster for the GS q heads of kv head g, and one partial softmax state
+// per q head: (m, sum_j w_j n_j, sum_j w_j Vsum_j). Thread (sub, dq) takes dims
+// 4dq..4dq+3 of clusters sub + 32u (16 float4 loads in flight per thread, issued
+// after the keys and sizes, which the weights need first).
+struct EstLds {
+  float kw[WAVE_MAX_GROUP][EC];         // weights
+  float red[16][WAVE_MAX_GROUP][D / 2]; // per wave pair: half-width sums, reused for both halves
+  float hred[WAVE_MAX_GROUP][16][2];
+  int32_t nsz[EC];
+};
+
+__device__ void est_role(const SeqArgs& sa, const DecodeArgs& da, const wave_index& ix, const DecodeWs& ws, int w,
+                         EstLds& S) {
+  int b = 0;
+  for (;; ++b) {
+    const int nch = (sa.C[b] + EC - 1) / EC;
+    if (w < sa.G * nch) break;
+    w -= sa.G * nch;
+  }
+  const SeqBase sb = seq_base(sa, b);
+  const int C = sb.C, GS = da.GS;
+  const int nch = (C + EC - 1) / EC;
+  const int g = w / nch, chunk = w % nch;
+  const int j0 = chunk * EC, nc = min(EC, C - j0);
+  const int64_t clu0 = sb.clu + (int64_t)g * C;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int sub = tid >> 5, dq = tid & 31;
+  const float sc = da.tau * LOG2E;
+  // weights: thread jj < EC takes cluster jj for every head (keys and sizes loaded first)
+  const int jj = tid;
+  const int jc = min(jj, nc - 1);
+  const int n0 = ix.sizes[clu0 + j0 + jc];
+  const float* kb = ws.keys + (int64_t)GS * sb.clu + (int64_t)g * GS * C + j0;
+  float kr[WAVE_MAX_GROUP];
 #pragma unroll
-    for (int hh = 0; hh < GS; ++hh) {
-      sv[hh] = live ? S.kw[hh][tid] * sc : -INFINITY;
+  for (int hh = 0; hh < WAVE_MAX_GROUP; ++hh) kr[hh] = kb[(int64_t)min(hh, GS - 1) * C + jc];
+  float4 vreg[EC / 32];
+  {
+    const float4* vsrc = reinterpret_cast<const float4*>(ix.vsum + (clu0 + j0) * D) + dq;
+#pragma unroll
+    for (int u = 0; u < EC / 32; ++u) vreg[u] = vsrc[(int64_t)min(sub + 32 * u, nc - 1) * (D / 4)];
+  }
+  const int n = jj < nc ? n0 : 0;
+  float sv[WAVE_MAX_GROUP];
+#pragma unroll
+  for (int hh = 0; hh < WAVE_MAX_GROUP; ++hh) sv[hh] = (hh < GS && jj < nc && n > 0) ? kr[hh] * sc : -INFINITY;
+  if (jj < EC) S.nsz[jj] = n;
+#pragma unroll
+  for (int hh = 0; hh < WAVE_MAX_GROUP; ++hh) {
+    if (hh < GS) {
       const float mx = wave_max(sv[hh]);
       if (lane == 0) S.hred[hh][wv][0] = mx;
     }
   }
   lds_barrier();
-  if (tid < SC) {
+  constexpr int EW = EC / 64;  // waves holding clusters
 #pragma unroll
-    for (int hh = 0; hh < GS; ++hh) {
-      const float M = fmaxf(S.hred[hh][0][0], S.hred[hh][1][0]);
+  for (int hh = 0; hh < WAVE_MAX_GROUP; ++hh) {
+    if (hh < GS) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int w2 = 0; w2 < EW; ++w2) M = fmaxf(M, S.hred[hh][w2][0]);
       const float wgt = sv[hh] == -INFINITY ? 0.f : exp2f(sv[hh] - M);
-      S.kw[hh][tid] = wgt;
-      const float ls = wave_sum(wgt * (float)S.nsz[tid]);
+      if (jj < EC) S.kw[hh][jj] = wgt;
+      const float ls = wave_sum(wgt * (float)n);
       if (lane == 0) S.hred[hh][wv][1] = ls;
     }
   }
   lds_barrier();
-  // 4. sum_j w_j Vsum_j over the thread's 16 clusters, then over the 8 subs
-  float acc[GS][4];
+  float acc[WAVE_MAX_GROUP][4];
 #pragma unroll
-  for (int hh = 0; hh < GS; ++hh)
+  for (int hh = 0; hh < WAVE_MAX_GROUP; ++hh)
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[hh][e] = 0.f;
 #pragma unroll
-  for (int u = 0; u < SC / 8; ++u) {
-    const int jj = sub + 8 * u;
+  for (int u = 0; u < EC / 32; ++u) {
+    const int c = sub + 32 * u;
     const float4 v = vreg[u];
 #pragma unroll
-    for (int hh = 0; hh < GS; ++hh) {
-      const float wgt = jj < nc ? S.kw[hh][jj] : 0.f;
-      acc[hh][0] = fmaf(wgt, v.x, acc[hh][0]);
-      acc[hh][1] = fmaf(wgt, v.y, acc[hh][1]);
-      acc[hh][2] = fmaf(wgt, v.z, acc[hh][2]);
-      acc[hh][3] = fmaf(wgt, v.w, acc[hh][3]);
+    for (int hh = 0; hh < WAVE_MAX_GROUP; ++hh) {
+      if (hh < GS) {
+        const float wgt = c < nc ? S.kw[hh][c] : 0.f;
+        acc[hh][0] = fmaf(wgt, v.x, acc[hh][0]);
+        acc[hh][1] = fmaf(wgt, v.y, acc[hh][1]);
+        acc[hh][2] = fmaf(wgt, v.z, acc[hh][2]);
+        acc[hh][3] = fmaf(wgt, v.w, acc[hh][3]);
+      }
     }
   }
 #pragma unroll
-  for (int hh = 0; hh < GS; ++hh)
+  for (int hh = 0; hh < WAVE_MAX_GROUP; ++hh)
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[hh][e] += swap32(acc[hh][e]);
-  if (lane < 32)
+  // 16 waves x (32 lanes x 4 dims): two passes of half the dims through red
+  float* o_base = ws.part + (((int64_t)b * da.H + g * GS) * da.NP + da.P + chunk) * PART;
 #pragma unroll
-    for (int hh = 0; hh < GS; ++hh)
+  for (int half = 0; half < 2; ++half) {
+    if (lane < 32 && (dq >> 4) == half)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S.red[wv][hh][dq * 4 + e] = acc[hh][e];
-  lds_barrier();
-  for (int e = tid; e < GS * D; e += SCORE_THREADS) {
-    const int hh = e / D, d = e % D;
-    const float A = S.red[0][hh][d] + S.red[1][hh][d] + S.red[2][hh][d] + S.red[3][hh][d];
-    float* o = ws.part + (((int64_t)b * da.H + g * GS + hh) * da.NP + da.P + chunk) * PART;
-    if (d == 0) {
-      const float L = S.hred[hh][0][1] + S.hred[hh][1][1];
-      o[0] = L > 0.f ? fmaxf(S.hred[hh][0][0], S.hred[hh][1][0]) : -INFINITY;
-      o[1] = L;
+      for (int hh = 0; hh < WAVE_MAX_GROUP; ++hh)
+        if (hh < GS)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) S.red[wv][hh][(dq & 15) * 4 + e] = acc[hh][e];
+    lds_barrier();
+    for (int e = tid; e < GS * (D / 2); e += blockDim.x) {
+      const int hh = e / (D / 2), d = e % (D / 2);
+      float A = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < 16; ++w2) A += S.red[w2][hh][d];
+      float* o = o_base + (int64_t)hh * da.NP * PART;
+      if (half == 0 && d == 0) {
+        float L = 0.f, Mx = -INFINITY;
+#pragma unroll
+        for (int w2 = 0; w2 < EW; ++w2) {
+          L += S.hred[hh][w2][1];
+          Mx = fmaxf(Mx, S.hred[hh][w2][0]);
+        }
+        o[0] = L > 0.f ? Mx : -INFINITY;
+        o[1] = L;
+      }
+      o[4 + half * (D / 2) + d] = A;
     }
-    o[4 + d] = A;
+    lds_barrier();
   }
 }
 
@@ -331,9 +382,7 @@ __device__ inline void bitonic_desc(uint64_t* a, int n, bool global) {
 struct TopkLds {
   union {
     struct {
-      uint64_t key[TK_CAP];     // (u << 32) | ~id
-      int32_t n[TK_CAP];        // cluster size
-      int32_t off[TK_CAP];      // first sorted slot
+      uint4 rec[TK_CAP];        // (~id, u, size, first sorted slot): the order key is (u << 32) | ~id
       int32_t rank[TK_CAP];     // candidates that order before it
       int32_t pre[TK_CAP];      // their summed sizes
     } c;                        // fast path
@@ -354,6 +403,10 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
   constexpr bool INREG = NVR > 0;
   constexpr int CHK = INREG ? NVR : 8;  // keys per lane per chunk
   extern __shared__ uint8_t smem[];
+  if ((int)blockIdx.x >= sa.B * da.H) {
+    est_role(sa, da, ix, ws, blockIdx.x - sa.B * da.H, *reinterpret_cast<EstLds*>(smem));
+    return;
+  }
   TopkLds& L = *reinterpret_cast<TopkLds*>(smem);
   const int NV = INREG ? NVR : da.NVg;
   const int bh = blockIdx.x;
@@ -512,14 +565,17 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
           const int p = base + __popcll(bal[v] & ltmask);
           if (p < TK_CAP) {
             const int id = id_of(v);
-            L.u.c.key[p] = ((uint64_t)ureg[v] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)id);
+            uint4 r;
+            r.x = 0xFFFFFFFFu - (uint32_t)id;
+            r.y = ureg[v];
             if constexpr (PRE) {
-              L.u.c.n[p] = nreg[v];
-              L.u.c.off[p] = oreg[v];
+              r.z = (uint32_t)nreg[v];
+              r.w = (uint32_t)oreg[v];
             } else {
-              L.u.c.n[p] = sizes[id];
-              L.u.c.off[p] = offs[id];
+              r.z = (uint32_t)sizes[id];
+              r.w = (uint32_t)offs[id];
             }
+            L.u.c.rec[p] = r;
           }
         }
         base += __popcll(bal[v]);
@@ -533,14 +589,16 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
       const int P = max(1, TK_THREADS / nc);
       const int i = tid % nc, part = tid / nc;
       if (part < P) {
-        const uint64_t c = L.u.c.key[i];
+        const uint4 ri = L.u.c.rec[i];
+        const uint64_t c = ((uint64_t)ri.y << 32) | ri.x;
         const int j0 = nc * part / P, j1 = nc * (part + 1) / P;  // nc <= 1024: no overflow
         int rank = 0, pre = 0;
-#pragma unroll 16
+#pragma unroll 8
         for (int j = j0; j < j1; ++j) {
-          const bool gt = L.u.c.key[j] > c;
+          const uint4 rj = L.u.c.rec[j];
+          const bool gt = (((uint64_t)rj.y << 32) | rj.x) > c;
           rank += gt;
-          pre += gt ? L.u.c.n[j] : 0;
+          pre += (int)(rj.z & (0u - (uint32_t)gt));
         }
         atomicAdd(&L.u.c.rank[i], rank);
         atomicAdd(&L.u.c.pre[i], pre);
@@ -550,12 +608,12 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
       if (tid < nc) {
         const int rank = L.u.c.rank[tid];
         if (rank < k) {
-          const uint64_t c = L.u.c.key[tid];
-          const int id = (int)(0xFFFFFFFFu - (uint32_t)c);
-          const int n = L.u.c.n[tid], pre = L.u.c.pre[tid];
+          const uint4 r = L.u.c.rec[tid];
+          const int id = (int)(0xFFFFFFFFu - r.x);
+          const int n = (int)r.z, pre = L.u.c.pre[tid];
           out[rank] = id;
-          span[rank] = make_int2(L.u.c.off[tid], n);
-          skey[rank] = sortable_float((uint32_t)(c >> 32));
+          span[rank] = make_int2((int)r.w, n);
+          skey[rank] = sortable_float(r.y);
           selpre[rank] = pre;
           atomicOr(&L.selw[id >> 5], 1u << (id & 31));
           if (rank == k - 1) {
@@ -955,7 +1013,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
 
 // ------------------------------------------------------------------ k_merge
 // Log-sum-exp merge of the partials of one (b, h): the P row partials and one
-// centroid partial per k_score chunk. Thread (sub, dq) takes dims 4dq..4dq+3
+// centroid partial per estimation chunk. Thread (sub, dq) takes dims 4dq..4dq+3
 // over partials sub, sub + 8, ...; the 8 subsets meet in LDS. Row partials may
 // carry negative sums (they take centroid terms back out); the total is positive.
 __global__ __launch_bounds__(256) void k_merge(SeqArgs sa, DecodeArgs da, DecodeWs ws, float* __restrict__ out,
@@ -965,7 +1023,7 @@ __global__ __launch_bounds__(256) void k_merge(SeqArgs sa, DecodeArgs da, Decode
   __shared__ float mx[4];
   const int bh = blockIdx.x;
   const int b = bh / da.H;
-  const int npart = da.P + (sa.C[b] + SC - 1) / SC;
+  const int npart = da.P + (sa.C[b] + EC - 1) / EC;
   const float* pp = ws.part + (int64_t)bh * da.NP * PART;
   const int tid = threadIdx.x, dq = tid & 31, sub = tid >> 5;
   float M = -INFINITY;
@@ -1007,13 +1065,14 @@ __global__ __launch_bounds__(256) void k_merge(SeqArgs sa, DecodeArgs da, Decode
 // ------------------------------------------------------------------ host side
 template <int GS>
 static void launch_gs(const SeqArgs& sa, const DecodeArgs& da, const wave_index& ix, const DecodeWs& ws,
-                      const uint16_t* q, float* out, int32_t* sel_ids, float* lse, hipStream_t st, int nscore) {
+                      const uint16_t* q, float* out, int32_t* sel_ids, float* lse, hipStream_t st, int nscore,
+                      int nest) {
   prof_begin("k_score", st);
-  hipLaunchKernelGGL(k_score<GS>, dim3(nscore), dim3(SCORE_THREADS), sizeof(ScoreLds<GS>), st, sa, da, ix, q, ws);
+  hipLaunchKernelGGL(k_score<GS>, dim3(nscore), dim3(SCORE_THREADS), 0, st, sa, da, ix, q, ws);
   prof_end(st);
   prof_begin("k_topk", st);
-  const dim3 tg(sa.B * da.H), tb(TK_THREADS);
-  const size_t tl = sizeof(TopkLds);
+  const dim3 tg(sa.B * da.H + nest), tb(TK_THREADS);
+  const size_t tl = sizeof(TopkLds) > sizeof(EstLds) ? sizeof(TopkLds) : sizeof(EstLds);
   switch (da.NV) {
     case 4: hipLaunchKernelGGL(k_topk<4>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
     case 8: hipLaunchKernelGGL(k_topk<8>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
@@ -1029,35 +1088,30 @@ static void launch_gs(const SeqArgs& sa, const DecodeArgs& da, const wave_index&
   prof_end(st);
 }
 
-template <int GS>
-static void score_attr() {
-  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<GS>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            sizeof(ScoreLds<GS>));
-}
-
 hipError_t launch_decode(const SeqArgs& sa, const DecodeArgs& da, const wave_index& ix, const DecodeWs& ws,
                          const uint16_t* q, float* out, int32_t* sel_ids, float* lse, hipStream_t st) {
   static bool attrs = false;
   if (!attrs) {
+    const size_t tl = sizeof(TopkLds) > sizeof(EstLds) ? sizeof(TopkLds) : sizeof(EstLds);
     const void* fns[] = {reinterpret_cast<const void*>(&k_topk<0>), reinterpret_cast<const void*>(&k_topk<4>),
                          reinterpret_cast<const void*>(&k_topk<8>), reinterpret_cast<const void*>(&k_topk<16>)};
-    for (const void* f : fns)
-      (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(TopkLds));
-    score_attr<1>(); score_attr<2>(); score_attr<3>(); score_attr<4>();
-    score_attr<5>(); score_attr<6>(); score_attr<7>(); score_attr<8>();
+    for (const void* f : fns) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, tl);
     attrs = true;
   }
-  int nscore = 0;
-  for (int b = 0; b < sa.B; ++b) nscore += sa.G * ((sa.C[b] + SC - 1) / SC);
+  int nscore = 0, nest = 0;
+  for (int b = 0; b < sa.B; ++b) {
+    nscore += sa.G * ((sa.C[b] + SC - 1) / SC);
+    nest += sa.G * ((sa.C[b] + EC - 1) / EC);
+  }
   switch (da.GS) {
-    case 1: launch_gs<1>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore); break;
-    case 2: launch_gs<2>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore); break;
-    case 3: launch_gs<3>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore); break;
-    case 4: launch_gs<4>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore); break;
-    case 5: launch_gs<5>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore); break;
-    case 6: launch_gs<6>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore); break;
-    case 7: launch_gs<7>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore); break;
-    default: launch_gs<8>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore); break;
+    case 1: launch_gs<1>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
+    case 2: launch_gs<2>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
+    case 3: launch_gs<3>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
+    case 4: launch_gs<4>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
+    case 5: launch_gs<5>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
+    case 6: launch_gs<6>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
+    case 7: launch_gs<7>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
+    default: launch_gs<8>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
   }
   return hipGetLastError();
 }

@@ -140,7 +140,7 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
     da.kreq[b] = (int32_t)x;
     kmax = da.kreq[b] > kmax ? da.kreq[b] : kmax;
     Cmax = C > Cmax ? (int)C : Cmax;
-    const int nE = (int)((C + wave::DEC_SCORE_CH - 1) / wave::DEC_SCORE_CH);
+    const int nE = (int)((C + wave::DEC_EST_CH - 1) / wave::DEC_EST_CH);
     nEmax = nE > nEmax ? nE : nEmax;
     sumC += C;
     sumW += (C + 31) / 32;
