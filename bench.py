@@ -300,16 +300,35 @@ def main():
             sel = sel[sel >= 0]
             retrieved_rows += int(sizes[g * C + sel].sum())
     rows_per_dec = retrieved_rows / ids_h.shape[0]
+    # algorithmic HBM bytes per launch: every byte a kernel must read or write once
     steady = ns + nl
-    row_bytes = 2 * 128 * 2 + 4  # K + V row (bf16) + its sorted-slot index
-    attend_bytes = (G * C * (128 * 4 + 4)          # value sums + sizes of every cluster (estimation)
-                    + H * C * 4                   # rank keys of every (q head, cluster)
-                    + rows_per_dec * row_bytes + H * steady * row_bytes  # retrieved + steady rows
-                    + B * H * 128 * 2)            # q
-    score_bytes = G * C * 128 * 2 + B * H * 128 * 2 + H * C * 4
-    step_bytes = (G * C * (128 * 2 + 128 * 4 + 4) + rows_per_dec * row_bytes + H * steady * row_bytes
-                  + B * H * 128 * 2 + B * H * 128 * 4 + B * H * k_max * 4)
-    assign_flops = 2.0 * B * N * K_s * 128 * G  # per launch (one k-means round)
+    k_sel = k_max                                 # clusters selected per q head
+    n_est = -(-C // 512)                          # estimation chunks per kv head
+    P = (int(rows_per_dec / H) + steady + 255) // 256
+    part = 132 * 4                                # one partial softmax state
+    rows = B * N * G                              # index rows
+    score_bytes = (G * C * (128 * 2 + 4)          # bf16 centroid rows + sizes
+                   + B * H * 128 * 2              # q
+                   + H * C * 8)                   # rank keys + sortable keys out
+    topk_bytes = (H * C * 4 + G * C * 8           # sortable keys; sizes + offsets
+                  + H * k_sel * (4 + 8 + 4 + 4)   # ids, spans, keys, member prefix out
+                  + G * C * (128 * 4 + 4)         # estimation: value sums + sizes
+                  + H * C * 4                     # estimation: rank keys
+                  + H * n_est * part)             # estimation partials out
+    attend_bytes = (rows_per_dec * (2 * 128 * 2 + 4)       # K, V and perm of the retrieved rows
+                    + H * steady * (2 * 128 * 2 + 4 + 4)   # steady rows: K, V, inv_perm, correction
+                    + H * k_sel * 16                       # window metadata
+                    + B * H * 128 * 2 + H * P * part)      # q, partials out
+    merge_bytes = H * (P + n_est) * part + B * H * (128 * 4 + 4)
+    step_bytes = score_bytes + topk_bytes + attend_bytes + merge_bytes
+    assign_flops = 2.0 * B * N * K_s * 128 * G    # per launch (one k-means round)
+    assign_bytes = rows * (128 * 2 + 4) + G * C * (128 * 2 + 4)
+    update_bytes = ((iters - 1) * (rows * (128 * 2 + 4) + G * C * (128 * 4 + 128 * 2 + 4))
+                    + rows * (4 * 128 * 2 + 3 * 4) + G * C * (2 * 128 * 4 + 128 * 2 + 4)) / iters
+    sort_bytes = rows * 12 + G * C * 8
+    init_bytes = G * C * (128 * 2 + 128 * 4 + 128 * 2 + 4)
+    hbm_bytes = {"k_score": score_bytes, "k_topk": topk_bytes, "k_attend": attend_bytes, "k_merge": merge_bytes,
+                 "k_update": update_bytes, "k_sort": sort_bytes, "k_init": init_bytes}
 
     kern = {}
     for name, (cnt, ms) in prof.items():
@@ -322,25 +341,23 @@ def main():
                 "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": counter_traffic(dom, sha),
                 "algorithmic_per_launch": assign_flops}
     else:
-        per = {"k_attend": attend_bytes, "k_score": score_bytes}.get(dom, None)
+        per = hbm_bytes.get(dom)
         ach = per / (kern[dom]["avg_us"] * 1e-6) / 1e9 if per else None
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1) if ach else None, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4) if ach else None,
                 "traffic": counter_traffic(dom, sha), "algorithmic_per_launch": per}
     # every kernel's own roofline figure, for the record
     extra = {}
-    if "k_attend" in kern:
-        a = attend_bytes / (kern["k_attend"]["avg_us"] * 1e-6) / 1e9
-        extra["k_attend"] = {"bound": "hbm", "achieved_GBs": round(a, 1), "frac": round(a / HBM_PEAK_GBS, 4),
-                             "bytes_per_launch": int(attend_bytes), "traffic": counter_traffic("k_attend", sha)}
-    if "k_score" in kern:
-        a = score_bytes / (kern["k_score"]["avg_us"] * 1e-6) / 1e9
-        extra["k_score"] = {"bound": "hbm", "achieved_GBs": round(a, 1), "frac": round(a / HBM_PEAK_GBS, 4),
-                            "bytes_per_launch": int(score_bytes)}
+    for name, per in hbm_bytes.items():
+        if name in kern:
+            a = per / (kern[name]["avg_us"] * 1e-6) / 1e9
+            extra[name] = {"bound": "hbm", "achieved_GBs": round(a, 1), "frac": round(a / HBM_PEAK_GBS, 4),
+                           "bytes_per_launch": int(per), "traffic": counter_traffic(name, sha)}
     if "k_assign" in kern:
         a = assign_flops / (kern["k_assign"]["avg_us"] * 1e-6) / 1e12
         extra["k_assign"] = {"bound": "mfma", "achieved_TFLOPs": round(a, 1), "frac": round(a / BF16_PEAK_TFLOPS, 4),
-                             "flops_per_launch": assign_flops}
+                             "flops_per_launch": assign_flops, "hbm_bytes_per_launch": int(assign_bytes),
+                             "traffic": counter_traffic("k_assign", sha)}
 
     decodes = args.steps * QPS
     value = decodes / (t_plain / 1000.0)

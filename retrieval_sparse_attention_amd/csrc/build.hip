@@ -257,7 +257,7 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint
   AssignLds& S = *reinterpret_cast<AssignLds*>(smem);
   Unit U;
   int tb0;
-  assign_wg_map(sa, blockIdx.x, U, tb0);
+  assign_wg_map(sa, xcd_linear(blockIdx.x, gridDim.x), U, tb0);
   const int tend = min(tb0 + AS_TPW, U.L);
   const int ntiles = (tend - tb0 + AS_TT - 1) / AS_TT;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, h = lane >> 5, col = lane & 31;

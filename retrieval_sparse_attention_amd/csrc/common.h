@@ -51,6 +51,18 @@ __host__ __device__ inline int64_t num_clusters(int64_t N, int32_t seg_len, int3
   return (nseg - 1) * (int64_t)K_s + seg_clusters(N - (nseg - 1) * seg_len, seg_len, K_s);
 }
 
+// ---------------------------------------------------------------- XCD-aware workgroup order
+// Workgroups are dispatched round robin over the 8 XCDs (workgroup w runs on XCD
+// w mod 8), each with its own L2. The linear index of w in a grid of n puts
+// XCD x's workgroups at one contiguous run of [0, n), so neighbouring work
+// items (here: the workgroups of one k-means unit, which read the same
+// centroids) share an L2. A bijection of [0, n) for any n.
+__device__ __forceinline__ int xcd_linear(int w, int n) {
+  const int x = w & 7, s = w >> 3;
+  const int q = n >> 3, r = n & 7;  // XCD x holds q + (x < r) workgroups
+  return x * q + min(x, r) + s;
+}
+
 // ---------------------------------------------------------------- bf16
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
