@@ -9,7 +9,8 @@
 //   k_init                   seeded choice of K(s) tokens per unit (bf16 centroids, norms)
 //   iters x { k_assign       nearest centroid on bf16 MFMA (32x32x16), fp32
 //             k_assign_fix   binary64 decision where fp32 cannot separate the two best
-//             k_sort         stable counting sort of each unit by cluster
+//             k_sort         stable counting sort of each unit by cluster (LSD radix in LDS
+//                            for segments of at most 16384 tokens)
 //             k_update       ordered fp32 member sums, correctly rounded means, bf16
 //                            centroids and norms; the last round also writes the
 //                            sorted K/V, inv_perm and the ordered fp32 value sums }
@@ -584,6 +585,144 @@ __global__ __launch_bounds__(SORT_THREADS) void k_sort(SeqArgs sa, const int32_t
   }
 }
 
+// ------------------------------------------------------------------ k_sort_radix
+// The same stable sort for units of at most RS_MAXL tokens, as an LSD radix sort
+// of the keys (cluster << 14 | position) held in LDS, RS_DB cluster bits per pass.
+// Element i of a pass is handled by thread i mod 1024 in tile i / 1024, so the
+// order (tile, wave, lane) is element order. Inside a wave the elements with
+// the same digit are matched with one ballot per digit bit; the per-(digit,
+// tile, wave) counts are scanned over the workgroup in digit-major order, which
+// makes every pass stable. After the passes the sorted keys give perm directly,
+// and each cluster's first slot is found by binary search.
+constexpr int RS_THREADS = 1024;
+constexpr int RS_MAXL = 16384;  // positions fit 14 bits
+constexpr int RS_DB = 5;
+constexpr int RS_ND = 1 << RS_DB;
+
+__device__ inline uint32_t rs_digit(uint32_t key, int pass) { return (key >> (14 + RS_DB * pass)) & (RS_ND - 1); }
+
+__global__ __launch_bounds__(RS_THREADS) void k_sort_radix(SeqArgs sa, const int32_t* __restrict__ assign,
+                                                           int32_t* __restrict__ sizes,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ perm) {
+  extern __shared__ uint8_t smem[];
+  const Unit U = unit_of(sa, blockIdx.x);
+  const int Kc = U.Kc, L = U.L;
+  const int E = (L + RS_THREADS - 1) / RS_THREADS;  // tiles
+  uint32_t* buf0 = reinterpret_cast<uint32_t*>(smem);
+  uint32_t* buf1 = buf0 + E * RS_THREADS;
+  __shared__ uint64_t scan[17];
+  __shared__ int32_t first[WAVE_MAX_CLUSTERS_PER_SEG + 1];  // first sorted slot of cluster c (c <= Kc)
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const uint64_t ltmask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int nbits = 0;
+  while ((1 << nbits) < Kc) ++nbits;
+  const int passes = (nbits + RS_DB - 1) / RS_DB;
+  // keys in element (= position) order; ids are in [0, Kc) by construction, the clamp keeps
+  // every sorted slot inside the segment even if they were not
+  for (int e = 0; e < E; ++e) {
+    const int i = e * RS_THREADS + tid;
+    const int ic = min(i, L - 1);
+    const int c = min(max(assign[U.row0 + ic] - U.cbase, 0), Kc - 1);
+    buf0[i] = ((uint32_t)c << 14) | (uint32_t)ic;
+  }
+  __syncthreads();
+  uint32_t* src = buf0;
+  uint32_t* dst = buf1;
+  const int nx = RS_ND * E * 16;           // (digit, tile, wave) counters, kept in dst
+  const int per = (nx + RS_THREADS - 1) / RS_THREADS;
+  for (int pass = 0; pass < passes; ++pass) {
+    int32_t* cnt = reinterpret_cast<int32_t*>(dst);
+    for (int x = tid; x < nx; x += RS_THREADS) cnt[x] = 0;
+    __syncthreads();
+    uint32_t dg[RS_MAXL / RS_THREADS];
+    int rk[RS_MAXL / RS_THREADS];
+#pragma unroll
+    for (int e = 0; e < RS_MAXL / RS_THREADS; ++e) {
+      if (e < E) {
+        const int i = e * RS_THREADS + tid;
+        const bool valid = i < L;
+        const uint32_t d = rs_digit(src[i], pass);
+        uint64_t m = __ballot(valid);
+#pragma unroll
+        for (int bt = 0; bt < RS_DB; ++bt) {
+          const uint64_t bb = __ballot((d >> bt) & 1u);
+          m &= ((d >> bt) & 1u) ? bb : ~bb;
+        }
+        dg[e] = d;
+        rk[e] = __popcll(m & ltmask);
+        if (valid && rk[e] == 0) cnt[((int)d * E + e) * 16 + wv] = __popcll(m);
+      }
+    }
+    __syncthreads();
+    // exclusive scan of the counters in (digit, tile, wave) order
+    {
+      const int x0 = min(tid * per, nx), x1 = min(x0 + per, nx);
+      uint64_t local = 0;
+      for (int x = x0; x < x1; ++x) local += (uint32_t)cnt[x];
+      uint64_t y = local;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint64_t t = __shfl_up(y, o, 64);
+        if (lane >= o) y += t;
+      }
+      if (lane == 63) scan[wv] = y;
+      __syncthreads();
+      if (wv == 0) {
+        const uint64_t v0 = lane < 16 ? scan[lane] : 0;
+        uint64_t tt = v0;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const uint64_t t = __shfl_up(tt, o, 64);
+          if (lane >= o) tt += t;
+        }
+        if (lane < 16) scan[lane] = tt - v0;
+      }
+      __syncthreads();
+      int run = (int)(scan[wv] + y - local);
+      for (int x = x0; x < x1; ++x) {
+        const int c = cnt[x];
+        cnt[x] = run;
+        run += c;
+      }
+    }
+    __syncthreads();
+    int pos[RS_MAXL / RS_THREADS];
+    uint32_t kv[RS_MAXL / RS_THREADS];
+#pragma unroll
+    for (int e = 0; e < RS_MAXL / RS_THREADS; ++e) {
+      if (e < E) {
+        const int i = e * RS_THREADS + tid;
+        kv[e] = src[i];
+        pos[e] = cnt[((int)dg[e] * E + e) * 16 + wv] + rk[e];
+      }
+    }
+    __syncthreads();  // the counters are read; dst takes the keys
+#pragma unroll
+    for (int e = 0; e < RS_MAXL / RS_THREADS; ++e)
+      if (e < E && e * RS_THREADS + tid < L) dst[pos[e]] = kv[e];
+    __syncthreads();
+    uint32_t* t = src;
+    src = dst;
+    dst = t;
+  }
+  // perm, and each cluster's first slot by binary search over the sorted keys
+  for (int i = tid; i < L; i += RS_THREADS) perm[U.brow + U.tok0 + i] = U.tok0 + (int32_t)(src[i] & 0x3FFFu);
+  for (int c = tid; c <= Kc; c += RS_THREADS) {
+    int lo = 0, hi = L;  // first index whose cluster is >= c
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((int)(src[mid] >> 14) < c) lo = mid + 1;
+      else hi = mid;
+    }
+    if (c < Kc) offsets[U.boff + U.cbase + c] = U.tok0 + lo;
+    first[c] = lo;
+  }
+  __syncthreads();
+  for (int c = tid; c < Kc; c += RS_THREADS) sizes[U.gclu + c] = first[c + 1] - first[c];
+  if (tid == 0 && U.tok0 + U.L == U.N) offsets[U.boff + U.C] = U.N;
+}
+
 // ------------------------------------------------------------------ k_update
 // Ordered fp32 sums of the members' keys (ascending position), correctly
 // rounded division by the count; empty clusters keep their centroid. One wave
@@ -682,6 +821,8 @@ hipError_t launch_build(const SeqArgs& sa, const void* Kv, const void* Vv, int32
                               sizeof(AssignLds));
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sort), hipFuncAttributeMaxDynamicSharedMemorySize,
                               16 * WAVE_MAX_CLUSTERS_PER_SEG * 4);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sort_radix),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 2 * RS_MAXL * 4);
     attrs = true;
   }
   const uint16_t* K = reinterpret_cast<const uint16_t*>(Kv);
@@ -690,6 +831,9 @@ hipError_t launch_build(const SeqArgs& sa, const void* Kv, const void* Vv, int32
   for (int b = 0; b < sa.B; ++b) nclu += (int64_t)sa.G * sa.C[b];
   const size_t init_lds = ((2 * (size_t)sa.seg_len + 15) & ~(size_t)15) + 4 * (size_t)sa.K_s;
   const size_t sort_lds = 16 * (size_t)sa.K_s * 4;
+  // two key buffers of E tiles; the counters (32 digits x E tiles x 16 waves) fit in one
+  const size_t radix_tiles = ((size_t)sa.seg_len + RS_THREADS - 1) / RS_THREADS;
+  const size_t radix_lds = 2 * radix_tiles * RS_THREADS * 4;
   const unsigned cgrid = (unsigned)((nclu + 3) / 4);
   uint16_t* chat = reinterpret_cast<uint16_t*>(ix.centroids_bf16);
   prof_begin("k_init", st);
@@ -711,8 +855,12 @@ hipError_t launch_build(const SeqArgs& sa, const void* Kv, const void* Vv, int32
       if (e != hipSuccess) return e;
     }
     prof_begin("k_sort", st);
-    hipLaunchKernelGGL(k_sort, dim3((unsigned)units), dim3(SORT_THREADS), sort_lds, st, sa, ix.assign, ws.rank,
-                       ix.sizes, ix.offsets, ix.perm);
+    if (sa.seg_len <= RS_MAXL)
+      hipLaunchKernelGGL(k_sort_radix, dim3((unsigned)units), dim3(RS_THREADS), radix_lds, st, sa, ix.assign, ix.sizes,
+                         ix.offsets, ix.perm);
+    else
+      hipLaunchKernelGGL(k_sort, dim3((unsigned)units), dim3(SORT_THREADS), sort_lds, st, sa, ix.assign, ws.rank,
+                         ix.sizes, ix.offsets, ix.perm);
     prof_end(st);
     prof_begin("k_update", st);
     if (it + 1 < iters)

@@ -58,6 +58,13 @@ def test_more_than_512_clusters_per_segment():
     _check_all("K_s=1024", K, V, 1, ctx, 2048, 1024, 2, 5)
 
 
+def test_long_segments_general_sort():
+    # segments longer than 16384 tokens take the ballot counting sort instead of the LDS radix sort
+    ctx = [45000]
+    K, V, _ = synth.kv(16, 1, 1, np.array(ctx), 20000)
+    _check_all("seg=20000", K, V, 1, ctx, 20000, 64, 2, 13)
+
+
 def test_duplicate_keys_and_ties():
     # many identical keys: exact distance ties go to the lowest id (binary64 decision path)
     ctx = [2048]
