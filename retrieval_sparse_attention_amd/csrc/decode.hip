@@ -7,18 +7,17 @@
 // (estimation zone). Four launches per call, all on the caller's stream:
 //   k_score  -- one pass over the centroid rows of a kv head: rank keys of the
 //               H/G q heads and eligibility
-//   k_topk   -- two roles in one grid: per (sequence, q head) the exact top-k by
-//               (key desc, id asc), selected ids and spans and steady-row
-//               corrections; and, on the remaining CUs meanwhile, the estimation
-//               term of every cluster (one pass over the value sums) as partial
-//               softmax states
-//   k_attend -- online-softmax attention over the selected clusters' sorted rows
-//               and over the steady rows; every row of a cluster whose centroid
-//               term was counted in k_score takes that term back out
+//   k_topk   -- per (sequence, q head): exact top-k by (key desc, id asc), the
+//               selected ids and spans, steady-row corrections
+//   k_attend -- two roles in one grid: online-softmax attention over the selected
+//               clusters' sorted rows and over the steady rows (every row of a
+//               cluster whose centroid term is counted takes that term back out);
+//               and the estimation term of every cluster (one pass over the value
+//               sums) as partial softmax states
 //   k_merge  -- log-sum-exp merge of the partials of every (sequence, q head)
 //
 // Estimation bookkeeping. The pages' estimation zone is E \ R with the value
-// sums and sizes of the clusters' non-steady members. k_topk adds the centroid
+// sums and sizes of the clusters' non-steady members. k_attend adds the centroid
 // term e^{s_j} (n_j, Vsum_j) of EVERY cluster; each member row t of a selected
 // cluster and each steady row t of a cluster that is not selected then adds
 // -e^{s_j} (1, v_t) in k_attend. Summed, this leaves exactly the centroid terms
@@ -32,7 +31,6 @@
 namespace wave {
 
 constexpr int SC = DEC_SCORE_CH;  // clusters per k_score workgroup
-constexpr int EC = DEC_EST_CH;    // clusters per estimation workgroup
 constexpr int SCORE_THREADS = 256;
 constexpr int TK_THREADS = 1024;
 constexpr int TK_CAP = 1024;      // candidates of the fast selection
@@ -185,130 +183,111 @@ __global__ __launch_bounds__(SCORE_THREADS) void k_score(SeqArgs sa, DecodeArgs 
 }
 
 // ------------------------------------------------------------------ estimation role
-// Workgroup (b, g, 512 clusters) of the k_topk grid: weights 2^(r tau log2(e) - m)
+// Workgroup (b, g, 128 clusters) of the k_attend grid: weights 2^(r tau log2(e) - m)
 // of every cluster for the GS q heads of kv head g, and one partial softmax state
-// per q head: (m, sum_j w_j n_j, sum_j w_j Vsum_j). Thread (sub, dq) takes dims
-// 4dq..4dq+3 of clusters sub + 32u (16 float4 loads in flight per thread, issued
-// after the keys and sizes, which the weights need first).
+// per q head: (m, sum_j w_j n_j, sum_j w_j Vsum_j). It runs beside the gathering
+// workgroups, whose memory latency it fills. Thread (sub, dq) takes dims
+// 4dq..4dq+3 of clusters sub + 8u (16 float4 loads in flight per thread), issued
+// after the keys and sizes, which the weights need first.
+template <int GS>
 struct EstLds {
-  float kw[WAVE_MAX_GROUP][EC];         // weights
-  float red[16][WAVE_MAX_GROUP][D / 2]; // per wave pair: half-width sums, reused for both halves
-  float hred[WAVE_MAX_GROUP][16][2];
-  int32_t nsz[EC];
+  float kw[GS][SC];    // weights
+  float red[4][GS][D]; // per wave: the q heads' weighted value sums
+  float hred[GS][2][2];
 };
 
-__device__ void est_role(const SeqArgs& sa, const DecodeArgs& da, const wave_index& ix, const DecodeWs& ws, int w,
-                         EstLds& S) {
+template <int GS>
+__device__ void est_role(const SeqArgs& sa, const DecodeArgs& da, const wave_index& ix, const DecodeWs& ws, int w) {
+  __shared__ EstLds<GS> S;
   int b = 0;
   for (;; ++b) {
-    const int nch = (sa.C[b] + EC - 1) / EC;
+    const int nch = (sa.C[b] + SC - 1) / SC;
     if (w < sa.G * nch) break;
     w -= sa.G * nch;
   }
   const SeqBase sb = seq_base(sa, b);
-  const int C = sb.C, GS = da.GS;
-  const int nch = (C + EC - 1) / EC;
+  const int C = sb.C;
+  const int nch = (C + SC - 1) / SC;
   const int g = w / nch, chunk = w % nch;
-  const int j0 = chunk * EC, nc = min(EC, C - j0);
+  const int j0 = chunk * SC, nc = min(SC, C - j0);
   const int64_t clu0 = sb.clu + (int64_t)g * C;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int sub = tid >> 5, dq = tid & 31;
   const float sc = da.tau * LOG2E;
-  // weights: thread jj < EC takes cluster jj for every head (keys and sizes loaded first)
+  // weights: thread jj < 128 takes cluster jj for every head (keys and sizes loaded first)
   const int jj = tid;
   const int jc = min(jj, nc - 1);
   const int n0 = ix.sizes[clu0 + j0 + jc];
   const float* kb = ws.keys + (int64_t)GS * sb.clu + (int64_t)g * GS * C + j0;
-  float kr[WAVE_MAX_GROUP];
+  float kr[GS];
 #pragma unroll
-  for (int hh = 0; hh < WAVE_MAX_GROUP; ++hh) kr[hh] = kb[(int64_t)min(hh, GS - 1) * C + jc];
-  float4 vreg[EC / 32];
+  for (int hh = 0; hh < GS; ++hh) kr[hh] = kb[(int64_t)hh * C + jc];
+  float4 vreg[SC / 8];
   {
     const float4* vsrc = reinterpret_cast<const float4*>(ix.vsum + (clu0 + j0) * D) + dq;
 #pragma unroll
-    for (int u = 0; u < EC / 32; ++u) vreg[u] = vsrc[(int64_t)min(sub + 32 * u, nc - 1) * (D / 4)];
+    for (int u = 0; u < SC / 8; ++u) vreg[u] = vsrc[(int64_t)min(sub + 8 * u, nc - 1) * (D / 4)];
   }
-  const int n = jj < nc ? n0 : 0;
-  float sv[WAVE_MAX_GROUP];
+  const bool live = jj < nc && n0 > 0;
+  float sv[GS];
+  if (tid < SC) {
 #pragma unroll
-  for (int hh = 0; hh < WAVE_MAX_GROUP; ++hh) sv[hh] = (hh < GS && jj < nc && n > 0) ? kr[hh] * sc : -INFINITY;
-  if (jj < EC) S.nsz[jj] = n;
-#pragma unroll
-  for (int hh = 0; hh < WAVE_MAX_GROUP; ++hh) {
-    if (hh < GS) {
+    for (int hh = 0; hh < GS; ++hh) {
+      sv[hh] = live ? kr[hh] * sc : -INFINITY;
       const float mx = wave_max(sv[hh]);
       if (lane == 0) S.hred[hh][wv][0] = mx;
     }
   }
   lds_barrier();
-  constexpr int EW = EC / 64;  // waves holding clusters
+  if (tid < SC) {
 #pragma unroll
-  for (int hh = 0; hh < WAVE_MAX_GROUP; ++hh) {
-    if (hh < GS) {
-      float M = -INFINITY;
-#pragma unroll
-      for (int w2 = 0; w2 < EW; ++w2) M = fmaxf(M, S.hred[hh][w2][0]);
+    for (int hh = 0; hh < GS; ++hh) {
+      const float M = fmaxf(S.hred[hh][0][0], S.hred[hh][1][0]);
       const float wgt = sv[hh] == -INFINITY ? 0.f : exp2f(sv[hh] - M);
-      if (jj < EC) S.kw[hh][jj] = wgt;
-      const float ls = wave_sum(wgt * (float)n);
+      S.kw[hh][tid] = wgt;
+      const float ls = wave_sum(wgt * (float)(live ? n0 : 0));
       if (lane == 0) S.hred[hh][wv][1] = ls;
     }
   }
   lds_barrier();
-  float acc[WAVE_MAX_GROUP][4];
+  float acc[GS][4];
 #pragma unroll
-  for (int hh = 0; hh < WAVE_MAX_GROUP; ++hh)
+  for (int hh = 0; hh < GS; ++hh)
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[hh][e] = 0.f;
 #pragma unroll
-  for (int u = 0; u < EC / 32; ++u) {
-    const int c = sub + 32 * u;
+  for (int u = 0; u < SC / 8; ++u) {
+    const int c = sub + 8 * u;
     const float4 v = vreg[u];
 #pragma unroll
-    for (int hh = 0; hh < WAVE_MAX_GROUP; ++hh) {
-      if (hh < GS) {
-        const float wgt = c < nc ? S.kw[hh][c] : 0.f;
-        acc[hh][0] = fmaf(wgt, v.x, acc[hh][0]);
-        acc[hh][1] = fmaf(wgt, v.y, acc[hh][1]);
-        acc[hh][2] = fmaf(wgt, v.z, acc[hh][2]);
-        acc[hh][3] = fmaf(wgt, v.w, acc[hh][3]);
-      }
+    for (int hh = 0; hh < GS; ++hh) {
+      const float wgt = c < nc ? S.kw[hh][c] : 0.f;
+      acc[hh][0] = fmaf(wgt, v.x, acc[hh][0]);
+      acc[hh][1] = fmaf(wgt, v.y, acc[hh][1]);
+      acc[hh][2] = fmaf(wgt, v.z, acc[hh][2]);
+      acc[hh][3] = fmaf(wgt, v.w, acc[hh][3]);
     }
   }
 #pragma unroll
-  for (int hh = 0; hh < WAVE_MAX_GROUP; ++hh)
+  for (int hh = 0; hh < GS; ++hh)
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[hh][e] += swap32(acc[hh][e]);
-  // 16 waves x (32 lanes x 4 dims): two passes of half the dims through red
-  float* o_base = ws.part + (((int64_t)b * da.H + g * GS) * da.NP + da.P + chunk) * PART;
+  if (lane < 32)
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    if (lane < 32 && (dq >> 4) == half)
+    for (int hh = 0; hh < GS; ++hh)
 #pragma unroll
-      for (int hh = 0; hh < WAVE_MAX_GROUP; ++hh)
-        if (hh < GS)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) S.red[wv][hh][(dq & 15) * 4 + e] = acc[hh][e];
-    lds_barrier();
-    for (int e = tid; e < GS * (D / 2); e += blockDim.x) {
-      const int hh = e / (D / 2), d = e % (D / 2);
-      float A = 0.f;
-#pragma unroll
-      for (int w2 = 0; w2 < 16; ++w2) A += S.red[w2][hh][d];
-      float* o = o_base + (int64_t)hh * da.NP * PART;
-      if (half == 0 && d == 0) {
-        float L = 0.f, Mx = -INFINITY;
-#pragma unroll
-        for (int w2 = 0; w2 < EW; ++w2) {
-          L += S.hred[hh][w2][1];
-          Mx = fmaxf(Mx, S.hred[hh][w2][0]);
-        }
-        o[0] = L > 0.f ? Mx : -INFINITY;
-        o[1] = L;
-      }
-      o[4 + half * (D / 2) + d] = A;
+      for (int e = 0; e < 4; ++e) S.red[wv][hh][dq * 4 + e] = acc[hh][e];
+  lds_barrier();
+  for (int e = tid; e < GS * D; e += blockDim.x) {
+    const int hh = e / D, d = e % D;
+    const float A = S.red[0][hh][d] + S.red[1][hh][d] + S.red[2][hh][d] + S.red[3][hh][d];
+    float* o = ws.part + (((int64_t)b * da.H + g * GS + hh) * da.NP + da.P + chunk) * PART;
+    if (d == 0) {
+      const float L = S.hred[hh][0][1] + S.hred[hh][1][1];
+      o[0] = L > 0.f ? fmaxf(S.hred[hh][0][0], S.hred[hh][1][0]) : -INFINITY;
+      o[1] = L;
     }
-    lds_barrier();
+    o[4 + d] = A;
   }
 }
 
@@ -365,8 +344,8 @@ __device__ inline void bitonic_desc(uint64_t* a, int n, bool global) {
 // R is the k = min(kreq, |E|) largest (u desc, id asc).
 //
 // Ids: wave w owns [w 64 NV, (w + 1) 64 NV); lane L holds ids
-// w0 + 256 blk + 4 L + e (blk < NV / 4, e < 4), so a wave's order of
-// (blk, lane, e) is id order. With NV <= 16 the keys stay in registers.
+// w0 + 64 v + L (v < NV): every load is 64 consecutive ids, and a wave's order
+// of (v, lane) is id order. With NV <= 16 the keys stay in registers.
 //
 // Fast path (keys in registers, k <= 1024): every wave finds the m-th largest
 // of its 64 lane maxima, t_w (m = ceil(kreq / 16)), by bisection over the 32
@@ -403,10 +382,6 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
   constexpr bool INREG = NVR > 0;
   constexpr int CHK = INREG ? NVR : 8;  // keys per lane per chunk
   extern __shared__ uint8_t smem[];
-  if ((int)blockIdx.x >= sa.B * da.H) {
-    est_role(sa, da, ix, ws, blockIdx.x - sa.B * da.H, *reinterpret_cast<EstLds*>(smem));
-    return;
-  }
   TopkLds& L = *reinterpret_cast<TopkLds*>(smem);
   const int NV = INREG ? NVR : da.NVg;
   const int bh = blockIdx.x;
@@ -427,7 +402,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
   const int32_t* sizes = ix.sizes + clu0;
   const int32_t* offs = ix.offsets + off0;
   const int w0 = wv * 64 * NV;
-  auto id_of = [&](int v) { return w0 + 256 * (v >> 2) + 4 * lane + (v & 3); };
+  auto id_of = [&](int v) { return w0 + 64 * v + lane; };
   const int nwords = (C + 31) >> 5;
   const bool lds_sel = nwords <= TK_SELW;
   int64_t wbase = 0;
@@ -683,49 +658,24 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
         szv[v] = sizes[j];
         kfv[v] = keys[j];
       }
-      // per block of 256 ids: lane-order prefix of (eq, selected) counts
+      // per 64 ids (one v): lane-order prefix of (eq, selected) counts by ballots
 #pragma unroll
-      for (int bb = 0; bb < CHK / 4; ++bb) {
-        int ce = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ce += (uc[4 * bb + e] == T);
-        int xe = ce;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_up(xe, o, 64);
-          if (lane >= o) xe += y;
+      for (int v = 0; v < CHK; ++v) {
+        const uint32_t x = uc[v];
+        const uint64_t em = __ballot(x == T);
+        const int er = eq_seen + __popcll(em & ltmask);
+        const bool sv = x > T || (x == T && er < k_eq);
+        const uint64_t sm = __ballot(sv);
+        if (sv) {
+          const int j = id_of(c0 + v);
+          const int p = pos + __popcll(sm & ltmask);
+          span[p] = make_int2(ofv[v], szv[v]);
+          skey[p] = kfv[v];
+          sb_[p] = ((uint64_t)x << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)j);
+          atomicOr(&selw[j >> 5], 1u << (j & 31));
         }
-        int er = eq_seen + xe - ce;
-        bool sel[4];
-        int cs = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t x = uc[4 * bb + e];
-          bool sv = x > T;
-          if (x == T) { sv = er < k_eq; ++er; }
-          sel[e] = sv;
-          cs += sv;
-        }
-        int xs = cs;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int y = __shfl_up(xs, o, 64);
-          if (lane >= o) xs += y;
-        }
-        int p = pos + xs - cs;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (sel[e]) {
-            const int j = id_of(c0 + 4 * bb + e);
-            span[p] = make_int2(ofv[4 * bb + e], szv[4 * bb + e]);
-            skey[p] = kfv[4 * bb + e];
-            sb_[p] = ((uint64_t)uc[4 * bb + e] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)j);
-            atomicOr(&selw[j >> 5], 1u << (j & 31));
-            ++p;
-          }
-        }
-        pos += __shfl(xs, 63, 64);
-        eq_seen += __shfl(xe, 63, 64);
+        pos += __popcll(sm);
+        eq_seen += __popcll(em);
       }
     }
     __threadfence_block();
@@ -858,6 +808,10 @@ template <int GS>
 __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs da, wave_index ix, DecodeWs ws,
                                                         const uint16_t* __restrict__ q) {
   __shared__ float red[4][PART];
+  if ((int)blockIdx.x >= sa.B * da.H * da.P) {
+    est_role<GS>(sa, da, ix, ws, blockIdx.x - sa.B * da.H * da.P);
+    return;
+  }
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, l16 = lane & 15, grp = lane >> 4;
   const int gi = wv * 4 + grp;  // 16-lane group in the workgroup
   const float sc = da.tau * LOG2E;
@@ -1023,7 +977,7 @@ __global__ __launch_bounds__(256) void k_merge(SeqArgs sa, DecodeArgs da, Decode
   __shared__ float mx[4];
   const int bh = blockIdx.x;
   const int b = bh / da.H;
-  const int npart = da.P + (sa.C[b] + EC - 1) / EC;
+  const int npart = da.P + (sa.C[b] + SC - 1) / SC;
   const float* pp = ws.part + (int64_t)bh * da.NP * PART;
   const int tid = threadIdx.x, dq = tid & 31, sub = tid >> 5;
   float M = -INFINITY;
@@ -1071,8 +1025,8 @@ static void launch_gs(const SeqArgs& sa, const DecodeArgs& da, const wave_index&
   hipLaunchKernelGGL(k_score<GS>, dim3(nscore), dim3(SCORE_THREADS), 0, st, sa, da, ix, q, ws);
   prof_end(st);
   prof_begin("k_topk", st);
-  const dim3 tg(sa.B * da.H + nest), tb(TK_THREADS);
-  const size_t tl = sizeof(TopkLds) > sizeof(EstLds) ? sizeof(TopkLds) : sizeof(EstLds);
+  const dim3 tg(sa.B * da.H), tb(TK_THREADS);
+  const size_t tl = sizeof(TopkLds);
   switch (da.NV) {
     case 4: hipLaunchKernelGGL(k_topk<4>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
     case 8: hipLaunchKernelGGL(k_topk<8>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
@@ -1081,7 +1035,7 @@ static void launch_gs(const SeqArgs& sa, const DecodeArgs& da, const wave_index&
   }
   prof_end(st);
   prof_begin("k_attend", st);
-  hipLaunchKernelGGL(k_attend<GS>, dim3(sa.B * da.H * da.P), dim3(ATT_THREADS), 0, st, sa, da, ix, ws, q);
+  hipLaunchKernelGGL(k_attend<GS>, dim3(sa.B * da.H * da.P + nest), dim3(ATT_THREADS), 0, st, sa, da, ix, ws, q);
   prof_end(st);
   prof_begin("k_merge", st);
   hipLaunchKernelGGL(k_merge, dim3(sa.B * da.H), dim3(256), 0, st, sa, da, ws, out, lse);
@@ -1092,7 +1046,7 @@ hipError_t launch_decode(const SeqArgs& sa, const DecodeArgs& da, const wave_ind
                          const uint16_t* q, float* out, int32_t* sel_ids, float* lse, hipStream_t st) {
   static bool attrs = false;
   if (!attrs) {
-    const size_t tl = sizeof(TopkLds) > sizeof(EstLds) ? sizeof(TopkLds) : sizeof(EstLds);
+    const size_t tl = sizeof(TopkLds);
     const void* fns[] = {reinterpret_cast<const void*>(&k_topk<0>), reinterpret_cast<const void*>(&k_topk<4>),
                          reinterpret_cast<const void*>(&k_topk<8>), reinterpret_cast<const void*>(&k_topk<16>)};
     for (const void* f : fns) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, tl);
@@ -1101,7 +1055,7 @@ hipError_t launch_decode(const SeqArgs& sa, const DecodeArgs& da, const wave_ind
   int nscore = 0, nest = 0;
   for (int b = 0; b < sa.B; ++b) {
     nscore += sa.G * ((sa.C[b] + SC - 1) / SC);
-    nest += sa.G * ((sa.C[b] + EC - 1) / EC);
+    nest += sa.G * ((sa.C[b] + SC - 1) / SC);
   }
   switch (da.GS) {
     case 1: launch_gs<1>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;

@@ -16,7 +16,7 @@ struct DecodeArgs {
   int32_t k_max;          // id columns of the output
   int32_t P;              // gathered-row workgroups per (b, h)
   int32_t NV;             // keys per lane of the register top-k (4, 8, 16), 0: keys read from memory
-  int32_t NP;             // partial slots per (b, h): P + max_b ceil(C_b / DEC_EST_CH)
+  int32_t NP;             // partial slots per (b, h): P + max_b ceil(C_b / DEC_SCORE_CH)
   int32_t scap;           // steady entries per (b, h)
   float tau;              // 1/sqrt(128)
   int32_t sort_stride;    // per-(b, h) entries of the global sort buffer
@@ -38,7 +38,6 @@ struct DecodeWs {
 };
 
 constexpr int DEC_SCORE_CH = 128;
-constexpr int DEC_EST_CH = 512;
 constexpr int DEC_PART = 132;
 constexpr int DEC_SORT_LDS = 4096;
 constexpr int DEC_ROWS_PER_WG = 256;

@@ -131,6 +131,7 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
   da.n_local = n_local;
   da.tau = (float)(1.0 / sqrt((double)WAVE_HEAD_DIM));
   int kmax = 0, Cmax = 0, nEmax = 0;
+
   int64_t sumC = 0, sumW = 0;
   for (int b = 0; b < sa.B; ++b) {
     const int64_t N = sa.N[b], C = sa.C[b];
@@ -140,7 +141,7 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
     da.kreq[b] = (int32_t)x;
     kmax = da.kreq[b] > kmax ? da.kreq[b] : kmax;
     Cmax = C > Cmax ? (int)C : Cmax;
-    const int nE = (int)((C + wave::DEC_EST_CH - 1) / wave::DEC_EST_CH);
+    const int nE = (int)((C + wave::DEC_SCORE_CH - 1) / wave::DEC_SCORE_CH);
     nEmax = nE > nEmax ? nE : nEmax;
     sumC += C;
     sumW += (C + 31) / 32;
