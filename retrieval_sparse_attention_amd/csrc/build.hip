@@ -201,24 +201,10 @@ constexpr int AS_GROUP = AS_WAVES * 64;  // centroids per pass
 // tile T runs in waves 0-1 while every wave already works on tile T + 1.
 struct AssignLds {
   u32x4 tile[2][AS_TT * 16];        // token rows, 16-byte chunk c of row t stored at slot t*16 + (c ^ (t & 15))
-  float red[2][AS_WAVES][AS_TT][3]; // per tile buffer and wave: best, id (bits), second best
+  float red[2][AS_WAVES][AS_TT][3]; // per tile buffer and wave: best, second best, winner's position (bits)
   float xnp[2][2][AS_TT];           // per tile buffer: two halves of |x|^2
   unsigned int rmax;                // max |c_j|^2 of the unit (float bits)
 };
-
-struct Best {
-  float b1, b2;
-  int i1;
-};
-
-__device__ __forceinline__ void best_merge(Best& a, const Best& o) {
-  // a keeps the larger best (lower id on equal values); second = largest of the rest
-  const bool take = (o.b1 > a.b1) || (o.b1 == a.b1 && o.i1 < a.i1);
-  const float lo = fminf(a.b1, o.b1);
-  const float s = fmaxf(lo, fmaxf(a.b2, o.b2));
-  if (take) { a.b1 = o.b1; a.i1 = o.i1; }
-  a.b2 = s;
-}
 
 __device__ inline void assign_wg_map(const SeqArgs& sa, int w, Unit& U, int& tok_begin) {
   // workgroups per unit: ceil(L / AS_TPW), units in (b, g, s) order
@@ -316,24 +302,29 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint
     const int t0 = tb0 + T * AS_TT;
     if (tid < AS_TT && t0 + tid < tend) {
       const int bi = T & 1;
-      Best bst;
-      bst.b1 = S.red[bi][0][tid][0];
-      bst.i1 = __float_as_int(S.red[bi][0][tid][1]);
-      bst.b2 = S.red[bi][0][tid][2];
+      float b1 = S.red[bi][0][tid][0], b2 = S.red[bi][0][tid][1];
+      uint32_t meta = __float_as_uint(S.red[bi][0][tid][2]);
+      int wbest = 0;
       for (int w2 = 1; w2 < AS_WAVES; ++w2) {
-        Best o;
-        o.b1 = S.red[bi][w2][tid][0];
-        o.i1 = __float_as_int(S.red[bi][w2][tid][1]);
-        o.b2 = S.red[bi][w2][tid][2];
-        best_merge(bst, o);
+        const float o1 = S.red[bi][w2][tid][0], o2 = S.red[bi][w2][tid][1];
+        const uint32_t om = __float_as_uint(S.red[bi][w2][tid][2]);
+        const bool take = o1 > b1;
+        b2 = fmaxf(fminf(b1, o1), fmaxf(b2, o2));
+        b1 = fmaxf(b1, o1);
+        meta = take ? om : meta;
+        wbest = take ? w2 : wbest;
       }
+      // id of the winner: group, wave, A tile r and row i of its 32x32 block, lane half
+      const int pbits = (int)(meta & 31u), hw = (int)((meta >> 5) & 1u), gw = (int)(meta >> 6);
+      const int best_id = gw * AS_GROUP + wbest * 64 + (pbits >> 4) * 32 + 8 * ((pbits & 15) >> 2) + 4 * hw +
+                          (pbits & 3);
       const int64_t row = U.row0 + t0 + tid;
       const float R2 = __uint_as_float(S.rmax);
       const float xn = sqrtf(S.xnp[bi][0][tid] + S.xnp[bi][1][tid]);
       const float margin = 0x1p-14f * (xn * sqrtf(R2) + R2) + 0x1p-100f;
-      assign[row] = U.cbase + bst.i1;
+      assign[row] = U.cbase + best_id;
       // also undecided: a best at the floor of the padding rows (values beyond fp32 range)
-      if (!(bst.b1 - bst.b2 > margin) || !(bst.b1 > -0x1p127f)) {
+      if (!(b1 - b2 > margin) || !(b1 > -0x1p127f)) {
         const int pos = atomicAdd(amb, 1);
         amb[1 + 2 * pos] = (int32_t)U.u;
         amb[2 + 2 * pos] = t0 + tid;
@@ -401,28 +392,28 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint
           b2 = fmaxf(lo, __builtin_amdgcn_fmed3f(hi, b1, b2));
           b1 = fmaxf(b1, hi);
         }
-        const int p = (int)(__float_as_uint(b1) & 31u);
-        Best bs;
-        bs.b1 = b1;
-        bs.b2 = b2;
-        bs.i1 = cb + (p >> 4) * 32 + 8 * ((p & 15) >> 2) + 4 * h + (p & 3);
-        Best o;
-        o.b1 = swap32(bs.b1);
-        o.b2 = swap32(bs.b2);
-        o.i1 = swap32(bs.i1);
-        best_merge(bs, o);
+        // merge the two half-waves (the lanes of one token); exact ties need no order here:
+        // their gap is 0, so the token is re-decided in binary64
+        const float ob1 = swap32(b1), ob2 = swap32(b2);
+        const bool take = ob1 > b1;
+        const float nb2 = fmaxf(fminf(b1, ob1), fmaxf(b2, ob2));
+        const float nb1 = fmaxf(b1, ob1);
+        // the winner's position: its packed 5 bits, its half, the centroid group
+        const uint32_t meta = ((uint32_t)grp << 6) | ((uint32_t)(take ? h ^ 1 : h) << 5) | (__float_as_uint(nb1) & 31u);
         if (h == 0) {
           float* rd = S.red[bi][wv][t];
           if (grp > 0) {
-            Best prev;
-            prev.b1 = rd[0];
-            prev.i1 = __float_as_int(rd[1]);
-            prev.b2 = rd[2];
-            best_merge(bs, prev);
+            const float pb1 = rd[0], pb2 = rd[1];
+            const uint32_t pm = __float_as_uint(rd[2]);
+            const bool keep = !(nb1 > pb1);
+            rd[0] = fmaxf(pb1, nb1);
+            rd[1] = fmaxf(fminf(pb1, nb1), fmaxf(pb2, nb2));
+            rd[2] = __uint_as_float(keep ? pm : meta);
+          } else {
+            rd[0] = nb1;
+            rd[1] = nb2;
+            rd[2] = __uint_as_float(meta);
           }
-          rd[0] = bs.b1;
-          rd[1] = __int_as_float(bs.i1);
-          rd[2] = bs.b2;
         }
       }
     }
