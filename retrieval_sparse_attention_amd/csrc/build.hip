@@ -16,6 +16,8 @@
 //                            sorted K/V, inv_perm and the ordered fp32 value sums }
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -24,6 +26,7 @@ namespace wave {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr uint64_t GAMMA = 0x9E3779B97F4A7C15ULL;
 
@@ -174,47 +177,75 @@ __global__ __launch_bounds__(INIT_THREADS) void k_init(SeqArgs sa, uint64_t seed
 // ------------------------------------------------------------------ k_assign (bf16 MFMA)
 // For a key x and bf16 centroids c_j the nearest centroid maximises
 // f_j = x.c_j - |c_j|^2 / 2. D[centroid][token] = C . X^T is computed with
-// v_mfma_f32_32x32x16_bf16: every wave keeps 64 centroid rows (two 32-row A
-// tiles, all 128 dims) in registers; token tiles (B operand) stream through
-// LDS; the accumulator starts at -|c_j|^2/2. A lane of the 32x32 result holds
-// one token (column) and 16 centroid rows of each A tile.
+// v_mfma_f32_32x32x16_bf16. A workgroup is 4 waves, one per SIMD, so each wave
+// has the whole register file: it keeps 128 centroid rows (four 32-row A
+// tiles, all 128 dims) resident, the token tiles (B operand) stream through
+// LDS, and the accumulator starts at -|c_j|^2/2. A lane of a 32x32 result holds
+// one token (column) and 16 centroid rows of its A tile.
 //
-// Selection per lane: the 5-bit position of each of its 32 values is written
-// into the value's low mantissa bits, so the best and second best of the 32
-// come from max3/med3 over triples (about 2.7 VALU operations per value) and the
-// best's position is read back from its bits. The packing moves a value by less
-// than 2^-18 |f|. The running best, its id and the second best are then merged
-// across the two half-waves and the 8 waves. When the gap between best and
-// second best is within 2^-14 (|x| R + R^2), R = max_j |c_j|, plus 2^-100 for
-// denormal flushing, the token goes to the exact binary64 decision
-// (k_assign_fix): that margin is more than twice the fp32 accumulation error of
-// a 128-term dot product and a norm (each below 2^-17 of those magnitudes) plus
-// the packing error, so every token not sent there has the exact argmin.
-constexpr int AS_WAVES = 8;
+// Software pipeline: the 32 MFMAs of a 32-token block run as two halves of 16
+// (A tiles 0-1, then 2-3); while one half runs on the matrix core, the same
+// wave selects over the other half's results on the vector ALU, so one wave
+// keeps both pipes busy. Units with more than 512 clusters (MULTI) take the
+// centroids in groups of 512, reloaded per tile.
+//
+// Selection per lane: the 6-bit position of each of its 64 values is written
+// into the value's low mantissa bits, so the best and second best come from
+// max3/med3 over triples and the best's position is read back from its bits.
+// The packing moves a value by less than 2^-17 |f|. The best, its position and
+// the second best are then merged across the two half-waves and the 4 waves.
+// When the gap between best and second best is within 2^-14 (|x| R + R^2),
+// R = max_j |c_j|, plus 2^-100 for denormal flushing, the token goes to the
+// exact binary64 decision (k_assign_fix): each value is off by less than the
+// fp32 accumulation error of a 128-term dot product and a norm (each below
+// 2^-17 of those magnitudes) plus the packing error, i.e. by less than
+// 2^-16 (|x| R + R^2), so the margin is twice what two values can move and
+// every token not sent there has the exact argmin.
+// scheduling of one pipeline step (see tile() in k_assign): nds LDS reads, then 16 x
+// (1 MFMA, 6 vector-ALU operations); nothing moves across the step's end
+#define AS_STEP(nds)                                                              \
+  do {                                                                            \
+    if ((nds) > 0) __builtin_amdgcn_sched_group_barrier(0x100, (nds), 0);         \
+    _Pragma("unroll") for (int i_ = 0; i_ < 16; ++i_) {                           \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          \
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);                          \
+    }                                                                             \
+    __builtin_amdgcn_sched_barrier(0);                                            \
+  } while (0)
+
+constexpr int AS_WAVES = 4;
 constexpr int AS_THREADS = AS_WAVES * 64;
-constexpr int AS_TT = 128;     // tokens per LDS tile
-constexpr int AS_TPW = 1024;   // tokens per workgroup
-constexpr int AS_GROUP = AS_WAVES * 64;  // centroids per pass
+constexpr int AS_TT = 128;                   // tokens per LDS tile (4 blocks of 32)
+constexpr int AS_CPW = 128;                  // centroids per wave
+constexpr int AS_GROUP = AS_WAVES * AS_CPW;  // centroids per pass
+constexpr int AS_MAXTPW = 16384;             // tokens per workgroup at most
 
 // Token tiles are double buffered and loaded straight into LDS (global_load_lds,
-// 16 bytes per lane); one barrier per tile. The reduction over the 8 waves of
-// tile T runs in waves 0-1 while every wave already works on tile T + 1.
+// 16 bytes per lane); one barrier per tile. The work of a tile's start (the
+// previous tile's decisions, this tile's key norms, the next tile's loads) is
+// straight-line code, so it overlaps the first MFMAs of the tile.
 struct AssignLds {
-  u32x4 tile[2][AS_TT * 16];        // token rows, 16-byte chunk c of row t stored at slot t*16 + (c ^ (t & 15))
-  float red[2][AS_WAVES][AS_TT][3]; // per tile buffer and wave: best, second best, winner's position (bits)
-  float xnp[2][2][AS_TT];           // per tile buffer: two halves of |x|^2
-  unsigned int rmax;                // max |c_j|^2 of the unit (float bits)
+  u32x4 tile[2][AS_TT * 16];         // token rows, 16-byte chunk c of row t stored at slot t*16 + (c ^ (t & 15))
+  float red[2][AS_WAVES][AS_TT][3];  // per tile buffer and wave: best, second best, winner's position (bits)
+  // near-tie flag of token i of the range at ambf[AS_TT + i]; the first AS_TT bytes
+  // take the flags of the empty decision pass before the first tile
+  uint8_t ambf[AS_MAXTPW + AS_TT];
+  float4 nrm[WAVE_MAX_CLUSTERS_PER_SEG / 4];  // |c_j|^2 of the unit's centroids
+  int32_t scan[AS_THREADS];
+  float rmx[AS_WAVES];               // per wave: max |c_j|^2
+  int32_t amb_base;
 };
 
-__device__ inline void assign_wg_map(const SeqArgs& sa, int w, Unit& U, int& tok_begin) {
-  // workgroups per unit: ceil(L / AS_TPW), units in (b, g, s) order
+// Workgroups per unit: ceil(L / tpw) with tpw tokens per workgroup (a multiple of
+// AS_TT chosen by the host); units in (b, g, s) order.
+__device__ inline void assign_wg_map(const SeqArgs& sa, int tpw, int w, Unit& U, int& tok_begin) {
   int64_t u = 0;
   int b = 0;
   for (;; ++b) {
     const int64_t N = sa.N[b];
     const int64_t nseg = (N + sa.seg_len - 1) / sa.seg_len;
     const int64_t last = N - (nseg - 1) * sa.seg_len;
-    const int wf = (sa.seg_len + AS_TPW - 1) / AS_TPW, wl = (int)((last + AS_TPW - 1) / AS_TPW);
+    const int wf = (sa.seg_len + tpw - 1) / tpw, wl = (int)((last + tpw - 1) / tpw);
     const int64_t per_g = (nseg - 1) * wf + wl;
     if (w < sa.G * per_g) {
       const int g = (int)(w / per_g);
@@ -223,7 +254,7 @@ __device__ inline void assign_wg_map(const SeqArgs& sa, int w, Unit& U, int& tok
       int64_t k = r % wf;
       if (s >= nseg - 1) { s = nseg - 1; k = r - (nseg - 1) * wf; }
       U = unit_of(sa, u + (int64_t)g * nseg + s);
-      tok_begin = (int)(k * AS_TPW);
+      tok_begin = (int)(k * tpw);
       return;
     }
     w -= (int)(sa.G * per_g);
@@ -231,12 +262,33 @@ __device__ inline void assign_wg_map(const SeqArgs& sa, int w, Unit& U, int& tok
   }
 }
 
-// value with its position p (0..31) in the low 5 mantissa bits
-__device__ __forceinline__ float pack5(float v, int p) {
-  return __uint_as_float((__float_as_uint(v) & ~31u) | (unsigned)p);
+// value with its position p (0..63) in the low 6 mantissa bits
+__device__ __forceinline__ float pack6(float v, int p) {
+  return __uint_as_float((__float_as_uint(v) & ~63u) | (unsigned)p);
 }
 
-__global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint16_t* __restrict__ K,
+// Best and second best of v[0..n) folded into (b1, b2); max3/med3 over triples.
+template <int n>
+__device__ __forceinline__ void top2_fold(const float* v, float& b1, float& b2) {
+#pragma unroll
+  for (int k3 = 0; k3 + 3 <= n; k3 += 3) {
+    const float x = v[k3], y = v[k3 + 1], z = v[k3 + 2];
+    const float m = fmaxf(fmaxf(x, y), z), md = __builtin_amdgcn_fmed3f(x, y, z);
+    b2 = fmaxf(md, __builtin_amdgcn_fmed3f(m, b1, b2));
+    b1 = fmaxf(b1, m);
+  }
+  if constexpr (n % 3 == 2) {
+    const float hi = fmaxf(v[n - 2], v[n - 1]), lo = fminf(v[n - 2], v[n - 1]);
+    b2 = fmaxf(lo, __builtin_amdgcn_fmed3f(hi, b1, b2));
+    b1 = fmaxf(b1, hi);
+  } else if constexpr (n % 3 == 1) {
+    b2 = __builtin_amdgcn_fmed3f(v[n - 1], b1, b2);
+    b1 = fmaxf(b1, v[n - 1]);
+  }
+}
+
+template <bool MULTI>
+__global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, const uint16_t* __restrict__ K,
                                                           const uint16_t* __restrict__ chat,
                                                           const float* __restrict__ norm,
                                                           int32_t* __restrict__ assign, int32_t* __restrict__ amb) {
@@ -244,182 +296,284 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, const uint
   AssignLds& S = *reinterpret_cast<AssignLds*>(smem);
   Unit U;
   int tb0;
-  assign_wg_map(sa, xcd_linear(blockIdx.x, gridDim.x), U, tb0);
-  const int tend = min(tb0 + AS_TPW, U.L);
-  const int ntiles = (tend - tb0 + AS_TT - 1) / AS_TT;
+  assign_wg_map(sa, tpw, xcd_linear(blockIdx.x, gridDim.x), U, tb0);
+  const int nrow = min(tpw, U.L - tb0);  // rows of the workgroup's range
+  const int ntiles = (nrow + AS_TT - 1) / AS_TT;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, h = lane >> 5, col = lane & 31;
-  // tile T -> buffer T & 1: wave wv fills slots [(4 wv + m) * 64, +64), m < 4; lane i of a
-  // load writes slot base + i, i.e. token t = slot / 16, chunk (slot % 16) ^ (t % 16).
-  // Rows past the segment end repeat its last row; their results are never stored.
-  auto issue = [&](int T) {
-    const int t0 = tb0 + T * AS_TT;
+  const uint16_t* Kr = K + (U.row0 + tb0) * D;  // first row of the range
+  // rows of tile T into buffer bi: wave wv fills slots [(8 wv + m) * 64, +64), m < 8; lane i of
+  // a load writes slot base + i, i.e. token t = slot / 16, chunk (slot % 16) ^ (t % 16).
+  // Rows past the range end repeat its last row: their results equal that row's.
+  auto issue = [&](int T, int bi) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int s0 = (wv * 4 + m) * 64;
+    for (int m = 0; m < 8; ++m) {
+      const int s0 = (wv * 8 + m) * 64;
       const int slot = s0 + lane;
       const int t = slot >> 4, c = (slot & 15) ^ (t & 15);
-      const int tt = min(t0 + t, tend - 1);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(K + (U.row0 + tt) * D + c * 8),
-          (__attribute__((address_space(3))) void*)(&S.tile[T & 1][s0]), 16, 0, 0);
+      const int tt = min(T * AS_TT + t, nrow - 1);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(Kr + tt * D + c * 8),
+                                       (__attribute__((address_space(3))) void*)(&S.tile[bi][s0]), 16, 0, 0);
     }
   };
-  issue(0);
-  // largest squared centroid norm of the unit (all norms are >= 0)
-  if (tid == 0) S.rmax = 0u;
-  __syncthreads();
-  {
-    unsigned int m = 0u;
-    for (int j = tid; j < U.Kc; j += AS_THREADS) m = max(m, __float_as_uint(norm[U.gclu + j]));
-    atomicMax(&S.rmax, m);
-  }
+  issue(0, 0);
   const int ngroups = (U.Kc + AS_GROUP - 1) / AS_GROUP;
-  bf16x8_t A[2][8];
-  floatx16 nh[2];
-  auto load_group = [&](int grp) {
-    const int cb = grp * AS_GROUP + wv * 64;
+  // A fragments live in the accumulation registers (AGPRs), which the MFMA reads as
+  // its A operand directly; the architectural VGPRs hold accumulators, B fragments and
+  // the selection. The empty asm only fixes the register class of its tied operand.
+  u32x4 A[4][8];
+  floatx16 nh[4];
+  auto load_a = [&](int grp) {
+    const int cb = grp * AS_GROUP + wv * AS_CPW;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
+    for (int r = 0; r < 4; ++r) {
       const int row = cb + r * 32 + col;
       const int rc = min(row, U.Kc - 1);
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(chat + (U.gclu + rc) * D + (2 * st + h) * 8);
-        A[r][st] = __builtin_bit_cast(bf16x8_t, row < U.Kc ? v : u32x4{0u, 0u, 0u, 0u});
+        const u32x4 z = row < U.Kc ? v : u32x4{0u, 0u, 0u, 0u};
+        asm volatile("" : "=a"(A[r][st]) : "0"(z));
       }
+    }
+  };
+  // accumulator start -|c_j|^2 / 2 of the rows a lane's results hold (from the LDS copy)
+  auto load_nh = [&](int grp) {
+    const int cb = grp * AS_GROUP + wv * AS_CPW;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int rr = cb + r * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
-        const float nv = norm[U.gclu + min(rr, U.Kc - 1)];
-        // rows past the unit's clusters: a finite floor that every real value beats
-        nh[r][i] = rr < U.Kc ? -0.5f * nv : -__FLT_MAX__;
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int r0 = cb + r * 32 + 8 * a4 + 4 * h;
+        const float4 nv = S.nrm[r0 >> 2];
+        const float f[4] = {nv.x, nv.y, nv.z, nv.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          // rows past the unit's clusters: a finite floor that every real value beats
+          nh[r][4 * a4 + k] = r0 + k < U.Kc ? -0.5f * f[k] : -__FLT_MAX__;
+      }
+  };
+  if (!MULTI) load_a(0);
+  // the unit's squared centroid norms into LDS, and their maximum (all are >= 0)
+  {
+    float m = 0.f;
+    float* nr = reinterpret_cast<float*>(S.nrm);
+    for (int j = tid; j < U.Kc; j += AS_THREADS) {
+      const float v = norm[U.gclu + j];
+      nr[j] = v;
+      m = fmaxf(m, v);
+    }
+    m = wave_max(m);
+    if (lane == 0) S.rmx[wv] = m;
+  }
+  // red buffer 1 holds the empty decision pass before the first tile
+  for (int i = tid; i < AS_WAVES * AS_TT; i += AS_THREADS) {
+    float* rd = S.red[1][i / AS_TT][i % AS_TT];
+    rd[0] = -INFINITY;
+    rd[1] = -INFINITY;
+    rd[2] = 0.f;
+  }
+  __syncthreads();
+  if (!MULTI) load_nh(0);
+  const float R2 = fmaxf(fmaxf(S.rmx[0], S.rmx[1]), fmaxf(S.rmx[2], S.rmx[3])), R = __builtin_amdgcn_sqrtf(R2);
+  // Decisions for tile Tm (Tm = -1: the empty pass, whose stores go to rows of tile 0 and
+  // are overwritten by the real ones): wave wv takes tokens 32 wv .. 32 wv + 31, both
+  // lane halves the same token; merge the 4 waves, store, flag near ties. x2: |x|^2.
+  auto reduce = [&](int Tm, float x2) {
+    const int bi = Tm & 1;
+    const int tk = wv * 32 + col;
+    float b1 = S.red[bi][0][tk][0], b2 = S.red[bi][0][tk][1];
+    uint32_t meta = __float_as_uint(S.red[bi][0][tk][2]);
+    int wbest = 0;
+#pragma unroll
+    for (int w2 = 1; w2 < AS_WAVES; ++w2) {
+      const float o1 = S.red[bi][w2][tk][0], o2 = S.red[bi][w2][tk][1];
+      const uint32_t om = __float_as_uint(S.red[bi][w2][tk][2]);
+      const bool take = o1 > b1;
+      b2 = fmaxf(fminf(b1, o1), fmaxf(b2, o2));
+      b1 = fmaxf(b1, o1);
+      meta = take ? om : meta;
+      wbest = take ? w2 : wbest;
+    }
+    // id of the winner: group, wave, A tile and row i of its 32x32 block, lane half
+    const int p = (int)(meta & 63u), hw = (int)((meta >> 6) & 1u), gw = (int)(meta >> 7);
+    const int best_id = gw * AS_GROUP + wbest * AS_CPW + (p >> 4) * 32 + 8 * ((p & 15) >> 2) + 4 * hw + (p & 3);
+    const int tr = Tm * AS_TT + tk;
+    assign[U.row0 + tb0 + min(max(tr, tk), nrow - 1)] = U.cbase + best_id;
+    const float margin = 0x1p-14f * (__builtin_amdgcn_sqrtf(x2) * R + R2) + 0x1p-100f;
+    // also undecided: a best at the floor of the padding rows (values beyond fp32 range)
+    const bool near = !(b1 - b2 > margin) || !(b1 > -0x1p127f);
+    S.ambf[AS_TT + tr] = (near && tr < nrow) ? 1 : 0;
+  };
+  // |x|^2 of this wave's tokens of a tile: lane (col, h) sums the 64 dims of half h
+  auto xnorm = [&](int bi) {
+    const int t = wv * 32 + col;
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const u32x4 w = S.tile[bi][t * 16 + ((8 * h + q) ^ (t & 15))];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2_t x = __builtin_bit_cast(bf16x2_t, w[e]);
+        s = __builtin_amdgcn_fdot2_f32_bf16(x, x, s, false);
       }
     }
+    return s + swap32(s);
   };
-  if (ngroups == 1) load_group(0);
-  // the 128 tokens of tile T: merge the 8 waves, decide or defer, store
-  auto reduce = [&](int T) {
-    const int t0 = tb0 + T * AS_TT;
-    if (tid < AS_TT && t0 + tid < tend) {
-      const int bi = T & 1;
-      float b1 = S.red[bi][0][tid][0], b2 = S.red[bi][0][tid][1];
-      uint32_t meta = __float_as_uint(S.red[bi][0][tid][2]);
-      int wbest = 0;
-      for (int w2 = 1; w2 < AS_WAVES; ++w2) {
-        const float o1 = S.red[bi][w2][tid][0], o2 = S.red[bi][w2][tid][1];
-        const uint32_t om = __float_as_uint(S.red[bi][w2][tid][2]);
-        const bool take = o1 > b1;
-        b2 = fmaxf(fminf(b1, o1), fmaxf(b2, o2));
-        b1 = fmaxf(b1, o1);
-        meta = take ? om : meta;
-        wbest = take ? w2 : wbest;
-      }
-      // id of the winner: group, wave, A tile r and row i of its 32x32 block, lane half
-      const int pbits = (int)(meta & 31u), hw = (int)((meta >> 5) & 1u), gw = (int)(meta >> 6);
-      const int best_id = gw * AS_GROUP + wbest * 64 + (pbits >> 4) * 32 + 8 * ((pbits & 15) >> 2) + 4 * hw +
-                          (pbits & 3);
-      const int64_t row = U.row0 + t0 + tid;
-      const float R2 = __uint_as_float(S.rmax);
-      const float xn = sqrtf(S.xnp[bi][0][tid] + S.xnp[bi][1][tid]);
-      const float margin = 0x1p-14f * (xn * sqrtf(R2) + R2) + 0x1p-100f;
-      assign[row] = U.cbase + best_id;
-      // also undecided: a best at the floor of the padding rows (values beyond fp32 range)
-      if (!(b1 - b2 > margin) || !(b1 > -0x1p127f)) {
-        const int pos = atomicAdd(amb, 1);
-        amb[1 + 2 * pos] = (int32_t)U.u;
-        amb[2 + 2 * pos] = t0 + tid;
-      }
+  // B fragments of 32-token block tb of a tile: lane (col, h) holds chunks 2 st + h of token col
+  auto load_b = [&](const u32x4* tl, int tb, bf16x8_t (&Bv)[8]) {
+    const int t = tb * 32 + col;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) Bv[st] = __builtin_bit_cast(bf16x8_t, tl[t * 16 + ((2 * st + h) ^ (t & 15))]);
+  };
+  // the 16 MFMAs of A tiles 2 hb, 2 hb + 1 against one token block
+  auto mma_half = [&](const bf16x8_t (&Bv)[8], int hb, floatx16 (&acc)[2]) {
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, A[2 * hb + r][st]), Bv[st],
+                                                         st == 0 ? nh[2 * hb + r] : acc[r], 0, 0, 0);
+  };
+  // fold the 32 values of a half block into (b1, b2); positions 32 hb + 16 r + i
+  auto sel_half = [&](floatx16 (&acc)[2], int hb, float& b1, float& b2) {
+    float v[32];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[16 * r + i] = pack6(acc[r][i], 32 * hb + 16 * r + i);
+    if (hb == 0) {
+      b1 = -INFINITY;
+      b2 = -INFINITY;
+    }
+    top2_fold<32>(v, b1, b2);
+  };
+  // merge the two half-waves (the lanes of one token) and store the wave's result for the
+  // block. Both halves store the same values, up to exact ties, which need no order here:
+  // their gap is 0, so the token is re-decided in binary64.
+  auto finish = [&](int tb, int bi, int grp, float b1, float b2) {
+    const float ob1 = swap32(b1), ob2 = swap32(b2);
+    const bool take = ob1 > b1;
+    const float nb2 = fmaxf(fminf(b1, ob1), fmaxf(b2, ob2));
+    const float nb1 = fmaxf(b1, ob1);
+    // the winner's position: its packed 6 bits, its half, the centroid group
+    const uint32_t meta = ((uint32_t)grp << 7) | ((uint32_t)(take ? h ^ 1 : h) << 6) | (__float_as_uint(nb1) & 63u);
+    float* rd = S.red[bi][wv][tb * 32 + col];
+    if (MULTI && grp > 0) {
+      const float pb1 = rd[0], pb2 = rd[1];
+      const uint32_t pm = __float_as_uint(rd[2]);
+      const bool keep = !(nb1 > pb1);
+      rd[0] = fmaxf(pb1, nb1);
+      rd[1] = fmaxf(fminf(pb1, nb1), fmaxf(pb2, nb2));
+      rd[2] = __uint_as_float(keep ? pm : meta);
+    } else {
+      rd[0] = nb1;
+      rd[1] = nb2;
+      rd[2] = __uint_as_float(meta);
     }
   };
-  // |x|^2 of 32-token block (wv & 3) of a tile, half (wv >> 2) of the dims, from the B fragments
-  const int xtb = wv & 3, xhalf = wv >> 2;
+  // one tile against one centroid group: 8 half-block steps, the selection of step j - 1
+  // next to the MFMAs of step j. Each step is its own scheduling region: first the LDS
+  // reads of a later block's B fragments, then one MFMA followed by up to 6 vector-ALU
+  // operations, 16 times (the matrix core takes 32 cycles per MFMA, in which this wave
+  // issues the selection work).
+  auto tile = [&](int bi, int grp) {
+    const u32x4* tl = S.tile[bi];
+    bf16x8_t B0[8], B1[8];
+    floatx16 accA[2], accB[2];
+    float b1 = -INFINITY, b2 = -INFINITY;
+    load_b(tl, 0, B0);
+    load_b(tl, 1, B1);
+    mma_half(B0, 0, accA);
+    AS_STEP(16);
+    mma_half(B0, 1, accB);
+    sel_half(accA, 0, b1, b2);
+    AS_STEP(0);
+    mma_half(B1, 0, accA);
+    sel_half(accB, 1, b1, b2);
+    finish(0, bi, grp, b1, b2);
+    AS_STEP(0);
+    load_b(tl, 2, B0);
+    mma_half(B1, 1, accB);
+    sel_half(accA, 0, b1, b2);
+    AS_STEP(8);
+    mma_half(B0, 0, accA);
+    sel_half(accB, 1, b1, b2);
+    finish(1, bi, grp, b1, b2);
+    AS_STEP(0);
+    load_b(tl, 3, B1);
+    mma_half(B0, 1, accB);
+    sel_half(accA, 0, b1, b2);
+    AS_STEP(8);
+    mma_half(B1, 0, accA);
+    sel_half(accB, 1, b1, b2);
+    finish(2, bi, grp, b1, b2);
+    AS_STEP(0);
+    mma_half(B1, 1, accB);
+    sel_half(accA, 0, b1, b2);
+    AS_STEP(0);
+    sel_half(accB, 1, b1, b2);
+    finish(3, bi, grp, b1, b2);
+  };
+  float xn = 0.f;  // |x|^2 of this wave's tokens of the previous tile
   for (int T = 0; T < ntiles; ++T) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of tile T have landed
     __syncthreads();  // tile T is in LDS; red[(T - 1) & 1] is complete
-    if (T + 1 < ntiles) issue(T + 1);  // into the buffer of tile T - 1, which every wave has finished
-    if (T > 0) reduce(T - 1);
     const int bi = T & 1;
-    const u32x4* tl = S.tile[bi];
-    for (int grp = 0; grp < ngroups; ++grp) {
-      if (ngroups > 1) load_group(grp);
-      const int cb = grp * AS_GROUP + wv * 64;
-#pragma unroll 2
-      for (int tb = 0; tb < AS_TT / 32; ++tb) {
-        const int t = tb * 32 + col;
-        bf16x8_t Bv[8];
-#pragma unroll
-        for (int st = 0; st < 8; ++st) Bv[st] = __builtin_bit_cast(bf16x8_t, tl[t * 16 + ((2 * st + h) ^ (t & 15))]);
-        if (grp == 0 && tb == xtb) {
-          float s2 = 0.f;
-          auto sq = [&](const bf16x8_t& f) {
-            const u32x4 w = __builtin_bit_cast(u32x4, f);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float a = bf16_lo(w[e]), b = bf16_hi(w[e]);
-              s2 = fmaf(a, a, s2);
-              s2 = fmaf(b, b, s2);
-            }
-          };
-          if (xhalf == 0) {
-            sq(Bv[0]); sq(Bv[1]); sq(Bv[2]); sq(Bv[3]);
-          } else {
-            sq(Bv[4]); sq(Bv[5]); sq(Bv[6]); sq(Bv[7]);
-          }
-          s2 += swap32(s2);
-          if (h == 0) S.xnp[bi][xhalf][t] = s2;
-        }
-        floatx16 acc[2];
-#pragma unroll
-        for (int st = 0; st < 8; ++st)
-#pragma unroll
-          for (int r = 0; r < 2; ++r)
-            acc[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[r][st], Bv[st], st == 0 ? nh[r] : acc[r], 0, 0, 0);
-        float v[32];
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) v[16 * r + i] = pack5(acc[r][i], 16 * r + i);
-        float b1 = -INFINITY, b2 = -INFINITY;
-#pragma unroll
-        for (int k3 = 0; k3 < 10; ++k3) {
-          const float x = v[3 * k3], y = v[3 * k3 + 1], z = v[3 * k3 + 2];
-          const float m = fmaxf(fmaxf(x, y), z), md = __builtin_amdgcn_fmed3f(x, y, z);
-          b2 = fmaxf(md, __builtin_amdgcn_fmed3f(m, b1, b2));
-          b1 = fmaxf(b1, m);
-        }
-        {
-          const float hi = fmaxf(v[30], v[31]), lo = fminf(v[30], v[31]);
-          b2 = fmaxf(lo, __builtin_amdgcn_fmed3f(hi, b1, b2));
-          b1 = fmaxf(b1, hi);
-        }
-        // merge the two half-waves (the lanes of one token); exact ties need no order here:
-        // their gap is 0, so the token is re-decided in binary64
-        const float ob1 = swap32(b1), ob2 = swap32(b2);
-        const bool take = ob1 > b1;
-        const float nb2 = fmaxf(fminf(b1, ob1), fmaxf(b2, ob2));
-        const float nb1 = fmaxf(b1, ob1);
-        // the winner's position: its packed 5 bits, its half, the centroid group
-        const uint32_t meta = ((uint32_t)grp << 6) | ((uint32_t)(take ? h ^ 1 : h) << 5) | (__float_as_uint(nb1) & 31u);
-        if (h == 0) {
-          float* rd = S.red[bi][wv][t];
-          if (grp > 0) {
-            const float pb1 = rd[0], pb2 = rd[1];
-            const uint32_t pm = __float_as_uint(rd[2]);
-            const bool keep = !(nb1 > pb1);
-            rd[0] = fmaxf(pb1, nb1);
-            rd[1] = fmaxf(fminf(pb1, nb1), fmaxf(pb2, nb2));
-            rd[2] = __uint_as_float(keep ? pm : meta);
-          } else {
-            rd[0] = nb1;
-            rd[1] = nb2;
-            rd[2] = __uint_as_float(meta);
-          }
-        }
+    // into the buffer of tile T - 1, which every wave has finished; after the last tile a
+    // harmless reload of it
+    issue(min(T + 1, ntiles - 1), bi ^ 1);
+    reduce(T - 1, xn);
+    xn = xnorm(bi);
+    if (!MULTI) {
+      tile(bi, 0);
+    } else {
+      for (int grp = 0; grp < ngroups; ++grp) {
+        load_a(grp);
+        load_nh(grp);
+        tile(bi, grp);
       }
     }
   }
   __syncthreads();
-  reduce(ntiles - 1);
+  reduce(ntiles - 1, xn);
+  __syncthreads();
+  // near-tie tokens to the global list: flags counted per thread (4 per word), a
+  // workgroup scan, one atomic
+  const uint32_t* fw = reinterpret_cast<const uint32_t*>(S.ambf + AS_TT);
+  const int nw = ntiles * (AS_TT / 4), per = (nw + AS_THREADS - 1) / AS_THREADS;
+  const int w0 = min(tid * per, nw), w1 = min(w0 + per, nw);
+  int cnt = 0;
+  for (int i = w0; i < w1; ++i) cnt += __builtin_popcount(fw[i]);
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) S.scan[wv] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < AS_WAVES; ++w2) {
+    const int c = S.scan[w2];
+    before += w2 < wv ? c : 0;
+    total += c;
+  }
+  if (total > 0) {
+    if (tid == 0) S.amb_base = atomicAdd(amb, total);
+    __syncthreads();
+    int pos = S.amb_base + before + incl - cnt;
+    for (int i = w0; i < w1; ++i) {
+      uint32_t f = fw[i];
+      while (f != 0u) {
+        const int b = __builtin_ctz(f);
+        f &= f - 1u;
+        amb[1 + 2 * pos] = (int32_t)U.u;
+        amb[2 + 2 * pos] = tb0 + 4 * i + (b >> 3);
+        ++pos;
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------------ k_assign_fix
@@ -789,13 +943,23 @@ __global__ __launch_bounds__(256) void k_update(SeqArgs sa, int64_t nclu, const 
 }
 
 // ------------------------------------------------------------------ host side
-static int64_t assign_grid(const SeqArgs& sa) {
+// Tokens per k_assign workgroup: enough workgroups per segment that the units fill
+// the 256 compute units once (one workgroup per CU: its LDS and registers take the CU),
+// in whole tiles.
+static int assign_tpw(const SeqArgs& sa, int64_t units) {
+  const int64_t per = std::max<int64_t>(1, (256 + units - 1) / units);
+  int64_t t = (sa.seg_len + per - 1) / per;
+  t = (t + AS_TT - 1) / AS_TT * AS_TT;
+  return (int)std::min<int64_t>(AS_MAXTPW, std::max<int64_t>(AS_TT, t));
+}
+
+static int64_t assign_grid(const SeqArgs& sa, int tpw) {
   int64_t n = 0;
   for (int b = 0; b < sa.B; ++b) {
     const int64_t N = sa.N[b];
     const int64_t nseg = (N + sa.seg_len - 1) / sa.seg_len;
     const int64_t last = N - (nseg - 1) * sa.seg_len;
-    const int64_t wf = (sa.seg_len + AS_TPW - 1) / AS_TPW, wl = (last + AS_TPW - 1) / AS_TPW;
+    const int64_t wf = (sa.seg_len + tpw - 1) / tpw, wl = (last + tpw - 1) / tpw;
     n += (int64_t)sa.G * ((nseg - 1) * wf + wl);
   }
   return n;
@@ -808,8 +972,10 @@ hipError_t launch_build(const SeqArgs& sa, const void* Kv, const void* Vv, int32
   if (!attrs) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_init), hipFuncAttributeMaxDynamicSharedMemorySize,
                               160 * 1024);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_assign), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              sizeof(AssignLds));
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_assign<false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(AssignLds));
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_assign<true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(AssignLds));
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sort), hipFuncAttributeMaxDynamicSharedMemorySize,
                               16 * WAVE_MAX_CLUSTERS_PER_SEG * 4);
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sort_radix),
@@ -831,11 +997,16 @@ hipError_t launch_build(const SeqArgs& sa, const void* Kv, const void* Vv, int32
   hipLaunchKernelGGL(k_init, dim3((unsigned)units), dim3(INIT_THREADS), init_lds, st, sa, seed, K, ix.centroids, chat,
                      ws.norm, ws.amb);
   prof_end(st);
-  const int64_t agrid = assign_grid(sa);
+  const int tpw = assign_tpw(sa, units);
+  const int64_t agrid = assign_grid(sa, tpw);
   for (int it = 0; it < iters; ++it) {
     prof_begin("k_assign", st);
-    hipLaunchKernelGGL(k_assign, dim3((unsigned)agrid), dim3(AS_THREADS), sizeof(AssignLds), st, sa, K, chat, ws.norm,
-                       ix.assign, ws.amb);
+    if (sa.K_s > AS_GROUP)
+      hipLaunchKernelGGL(k_assign<true>, dim3((unsigned)agrid), dim3(AS_THREADS), sizeof(AssignLds), st, sa, tpw, K,
+                         chat, ws.norm, ix.assign, ws.amb);
+    else
+      hipLaunchKernelGGL(k_assign<false>, dim3((unsigned)agrid), dim3(AS_THREADS), sizeof(AssignLds), st, sa, tpw, K,
+                         chat, ws.norm, ix.assign, ws.amb);
     prof_end(st);
     prof_begin("k_assign_fix", st);
     hipLaunchKernelGGL(k_assign_fix, dim3(512), dim3(FIX_THREADS), 0, st, sa, K, chat, ix.assign, ws.amb);
