@@ -218,7 +218,7 @@ constexpr int AS_THREADS = AS_WAVES * 64;
 constexpr int AS_TT = 128;                   // tokens per LDS tile (4 blocks of 32)
 constexpr int AS_CPW = 128;                  // centroids per wave
 constexpr int AS_GROUP = AS_WAVES * AS_CPW;  // centroids per pass
-constexpr int AS_MAXTPW = 16384;             // tokens per workgroup at most
+constexpr int AS_MAXTPW = 8192;              // tokens per workgroup at most (the near-tie list fits a tile buffer)
 
 // Token tiles are double buffered and loaded straight into LDS (global_load_lds,
 // 16 bytes per lane); one barrier per tile. The work of a tile's start (the
@@ -231,6 +231,8 @@ struct AssignLds {
   // take the flags of the empty decision pass before the first tile
   uint8_t ambf[AS_MAXTPW + AS_TT];
   float4 nrm[WAVE_MAX_CLUSTERS_PER_SEG / 4];  // |c_j|^2 of the unit's centroids
+  unsigned long long fd[32];         // exact decision: per token the least D_j (bits), then its id
+  int32_t fj[32];
   int32_t scan[AS_THREADS];
   float rmx[AS_WAVES];               // per wave: max |c_j|^2
   int32_t amb_base;
@@ -413,7 +415,10 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
       const u32x4 w = S.tile[bi][t * 16 + ((8 * h + q) ^ (t & 15))];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const bf16x2_t x = __builtin_bit_cast(bf16x2_t, w[e]);
+        // bit-cast a named scalar: hipcc lowers a bit-cast of a vector element
+        // expression inside a loop to element 0 for every iteration
+        const uint32_t we = w[e];
+        const bf16x2_t x = __builtin_bit_cast(bf16x2_t, we);
         s = __builtin_amdgcn_fdot2_f32_bf16(x, x, s, false);
       }
     }
@@ -534,11 +539,11 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
       }
     }
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the trailing reload has landed: the buffers are free
   __syncthreads();
   reduce(ntiles - 1, xn);
   __syncthreads();
-  // near-tie tokens to the global list: flags counted per thread (4 per word), a
-  // workgroup scan, one atomic
+  // near-tie tokens: flags counted per thread (4 per word) and a workgroup scan
   const uint32_t* fw = reinterpret_cast<const uint32_t*>(S.ambf + AS_TT);
   const int nw = ntiles * (AS_TT / 4), per = (nw + AS_THREADS - 1) / AS_THREADS;
   const int w0 = min(tid * per, nw), w1 = min(w0 + per, nw);
@@ -559,7 +564,9 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
     before += w2 < wv ? c : 0;
     total += c;
   }
-  if (total > 0) {
+  if (total == 0) return;
+  if (MULTI) {
+    // to the global list, for k_assign_fix: one atomic
     if (tid == 0) S.amb_base = atomicAdd(amb, total);
     __syncthreads();
     int pos = S.amb_base + before + incl - cnt;
@@ -573,47 +580,203 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
         ++pos;
       }
     }
+    return;
+  }
+  // Exact decision in the workgroup, 32 tokens at a time: their rows go through the
+  // MFMAs again; every centroid within 2^-14 (|x| R + R^2) + 2^-40 (|x| + R)^2 +
+  // 2^-100 of the best fp32 value (two fp32 errors and two binary64 rounding errors
+  // of the sums) gets D_j = sum_i (x_i - c_j,i)^2 in binary64, dims in order, each
+  // operation rounded; argmin with the lowest id on ties.
+  int32_t* fl = reinterpret_cast<int32_t*>(S.tile[1]);  // the list (the buffer is free now)
+  {
+    int pos = before + incl - cnt;
+    for (int i = w0; i < w1; ++i) {
+      uint32_t f = fw[i];
+      while (f != 0u) {
+        const int b = __builtin_ctz(f);
+        f &= f - 1u;
+        fl[pos++] = 4 * i + (b >> 3);
+      }
+    }
+  }
+  __syncthreads();
+  for (int f0 = 0; f0 < total; f0 += 32) {
+    const int nb = min(32, total - f0);
+    // rows of the batch into buffer 0 as block 0 of a tile; past nb the last row again
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int slot = tid + AS_THREADS * m;
+      const int t = slot >> 4, c = (slot & 15) ^ (t & 15);
+      S.tile[0][slot] = *reinterpret_cast<const u32x4*>(Kr + fl[f0 + min(t, nb - 1)] * D + c * 8);
+    }
+    if (tid < 32) {
+      S.fd[tid] = ~0ull;
+      S.fj[tid] = 0x7FFFFFFF;
+    }
+    __syncthreads();
+    bf16x8_t B[8];
+    load_b(S.tile[0], 0, B);
+    floatx16 a0[2], a1[2];
+    mma_half(B, 0, a0);
+    mma_half(B, 1, a1);
+    // |x|^2 of token col in fp32
+    float s2 = 0.f;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const u32x4 w = __builtin_bit_cast(u32x4, B[st]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t we = w[e];
+        const float a = bf16_lo(we), b = bf16_hi(we);
+        s2 = fmaf(a, a, s2);
+        s2 = fmaf(b, b, s2);
+      }
+    }
+    s2 += swap32(s2);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(a0[r][i], a1[r][i]));
+    mx = fmaxf(mx, swap32(mx));
+    if (h == 0) S.red[0][wv][col][0] = mx;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(S.red[0][0][col][0], S.red[0][1][col][0]), fmaxf(S.red[0][2][col][0], S.red[0][3][col][0]));
+    const float X = sqrtf(s2);
+    const float thr = M - (0x1p-14f * (X * R + R2) + 0x1p-40f * (X + R) * (X + R) + 0x1p-100f);
+    uint64_t cm = 0ull;  // candidates among this lane's 64 values: bit 32 hb + 16 r + i
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        cm |= (uint64_t)(a0[r][i] >= thr) << (16 * r + i);
+        cm |= (uint64_t)(a1[r][i] >= thr) << (32 + 16 * r + i);
+      }
+    const u32x4* xr = S.tile[0] + col * 16;
+    double best = INFINITY;
+    int bj = 0x7FFFFFFF;
+    while (cm != 0ull) {
+      const int q = __builtin_ctzll(cm);
+      cm &= cm - 1ull;
+      const int i = q & 15;
+      const int j = wv * AS_CPW + 32 * (q >> 4) + 8 * (i >> 2) + 4 * h + (i & 3);
+      if (j >= U.Kc) continue;
+      const u32x4* cj = reinterpret_cast<const u32x4*>(chat + (U.gclu + j) * D);
+      double acc = 0.0;
+      for (int c = 0; c < 16; ++c) {
+        const u32x4 xv = xr[c ^ (col & 15)], cv = cj[c];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t xe = xv[e], ce = cv[e];
+          const double d0 = __dsub_rn((double)bf16_lo(xe), (double)bf16_lo(ce));
+          acc = __dadd_rn(acc, __dmul_rn(d0, d0));
+          const double d1 = __dsub_rn((double)bf16_hi(xe), (double)bf16_hi(ce));
+          acc = __dadd_rn(acc, __dmul_rn(d1, d1));
+        }
+      }
+      if (acc < best || (acc == best && j < bj)) {
+        best = acc;
+        bj = j;
+      }
+    }
+    // D >= 0: its bits order as its values
+    const unsigned long long bd = (unsigned long long)__double_as_longlong(best);
+    if (bj != 0x7FFFFFFF) atomicMin(&S.fd[col], bd);
+    __syncthreads();
+    if (bj != 0x7FFFFFFF && bd == S.fd[col]) atomicMin(&S.fj[col], bj);
+    __syncthreads();
+    if (tid < nb) assign[U.row0 + tb0 + fl[f0 + tid]] = U.cbase + S.fj[tid];
+    __syncthreads();
   }
 }
 
 // ------------------------------------------------------------------ k_assign_fix
 // Exact decision for the listed tokens: D_j = sum_i (x_i - c_j,i)^2 in binary64,
 // dims in order, each operation rounded (no fused multiply-add), argmin with
-// the lowest id on ties. One workgroup per token; thread t takes centroids
-// j = t, t + 256, ...
+// the lowest id on ties. One wave per token; the waves of the grid take
+// contiguous runs of the list (a run is mostly one unit, whose centroids then
+// come from L2).
+//
+// Screening: every lane scores its centroids j = lane, lane + 64, ... in fp32,
+// f_j = x.c_j - |c_j|^2 / 2 (bf16 pair dot products, fp32 accumulation), and only
+// those within 2^-11 (|x| R + R^2) + 2^-40 (|x| + R)^2 + 2^-100 of the wave's best
+// get the binary64 sum. The pair dot product (v_dot2_f32_bf16) is not correctly
+// rounded: its error is at most 2.25 units in the last place of its largest
+// operand (measured over 2^20 random operands), i.e. at most 2.25 * 2^-23 |x| R
+// per step and 2^-15 (|x| R + R^2) over the 64 steps and the norm. A centroid
+// outside the window has f_j below the best by more than eight such errors plus
+// two binary64 rounding errors of the sums (each under 2^-45 (|x| + R)^2 in f
+// units), so its D_j exceeds the best candidate's and it cannot be the argmin.
 constexpr int FIX_THREADS = 256;
 
 __global__ __launch_bounds__(FIX_THREADS) void k_assign_fix(SeqArgs sa, const uint16_t* __restrict__ K,
                                                             const uint16_t* __restrict__ chat,
+                                                            const float* __restrict__ norm,
                                                             int32_t* __restrict__ assign,
                                                             const int32_t* __restrict__ amb) {
-  __shared__ double xs[D];
-  __shared__ double rb[FIX_THREADS / 64];
-  __shared__ int ri[FIX_THREADS / 64];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ uint32_t xw[FIX_THREADS / 64][D / 2];  // the wave's token, bf16 pairs
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int count = amb[0];
-  for (int item = blockIdx.x; item < count; item += gridDim.x) {
+  const int nwave = gridDim.x * (FIX_THREADS / 64), gw = blockIdx.x * (FIX_THREADS / 64) + wv;
+  const int it0 = (int)((int64_t)count * gw / nwave), it1 = (int)((int64_t)count * (gw + 1) / nwave);
+  const u32x4* xq = reinterpret_cast<const u32x4*>(xw[wv]);
+  for (int item = it0; item < it1; ++item) {
     const Unit U = unit_of(sa, amb[1 + 2 * item]);
     const int64_t row = U.row0 + amb[2 + 2 * item];
-    if (tid < D) xs[tid] = (double)bf16_to_f(K[row * D + tid]);
-    __syncthreads();
+    const uint32_t xv = reinterpret_cast<const uint32_t*>(K + row * D)[lane];
+    xw[wv][lane] = xv;
+    const float x0 = bf16_lo(xv), x1 = bf16_hi(xv);
+    const float X = sqrtf(wave_sum(fmaf(x0, x0, x1 * x1)));
+    float r2 = 0.f;
+    for (int j = lane; j < U.Kc; j += 64) r2 = fmaxf(r2, norm[U.gclu + j]);
+    const float R2 = wave_max(r2), R = sqrtf(R2);
+    // fp32 screening
+    float fb = -INFINITY;
+    float fj[WAVE_MAX_CLUSTERS_PER_SEG / 64];
+#pragma unroll
+    for (int q = 0; q < WAVE_MAX_CLUSTERS_PER_SEG / 64; ++q) {
+      const int j = lane + 64 * q;
+      fj[q] = -INFINITY;
+      if (64 * q < U.Kc && j < U.Kc) {
+        const u32x4* c = reinterpret_cast<const u32x4*>(chat + (U.gclu + j) * D);
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const u32x4 cv = c[e], xx = xq[e];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t xs = xx[w], cs = cv[w];  // named scalars (see xnorm in k_assign)
+            s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xs), __builtin_bit_cast(bf16x2_t, cs), s,
+                                                false);
+          }
+        }
+        fj[q] = s - 0.5f * norm[U.gclu + j];
+        fb = fmaxf(fb, fj[q]);
+      }
+    }
+    const float thr = wave_max(fb) - (0x1p-11f * (X * R + R2) + 0x1p-40f * (X + R) * (X + R) + 0x1p-100f);
+    // binary64 sums of the candidates, dims in order
     double best = INFINITY;
     int bi = 0x7FFFFFFF;
-    for (int j = tid; j < U.Kc; j += FIX_THREADS) {
-      const u32x4* c = reinterpret_cast<const u32x4*>(chat + (U.gclu + j) * D);
-      double acc = 0.0;
+#pragma unroll 1
+    for (int q = 0; q < WAVE_MAX_CLUSTERS_PER_SEG / 64; ++q) {
+      if (64 * q >= U.Kc) break;
+      const int j = lane + 64 * q;
+      if (j < U.Kc && fj[q] >= thr) {
+        const u32x4* c = reinterpret_cast<const u32x4*>(chat + (U.gclu + j) * D);
+        double acc = 0.0;
+        for (int e = 0; e < 16; ++e) {
+          const u32x4 cv = c[e], xx = xq[e];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const u32x4 cv = c[e];
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const double d0 = __dsub_rn(xs[8 * e + 2 * w], (double)bf16_lo(cv[w]));
-          acc = __dadd_rn(acc, __dmul_rn(d0, d0));
-          const double d1 = __dsub_rn(xs[8 * e + 2 * w + 1], (double)bf16_hi(cv[w]));
-          acc = __dadd_rn(acc, __dmul_rn(d1, d1));
+          for (int w = 0; w < 4; ++w) {
+            const double d0 = __dsub_rn((double)bf16_lo(xx[w]), (double)bf16_lo(cv[w]));
+            acc = __dadd_rn(acc, __dmul_rn(d0, d0));
+            const double d1 = __dsub_rn((double)bf16_hi(xx[w]), (double)bf16_hi(cv[w]));
+            acc = __dadd_rn(acc, __dmul_rn(d1, d1));
+          }
         }
+        if (acc < best) { best = acc; bi = j; }
       }
-      if (acc < best) { best = acc; bi = j; }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -621,14 +784,7 @@ __global__ __launch_bounds__(FIX_THREADS) void k_assign_fix(SeqArgs sa, const ui
       const int oi = __shfl_xor(bi, o, 64);
       if (ob < best || (ob == best && oi < bi)) { best = ob; bi = oi; }
     }
-    if (lane == 0) { rb[wv] = best; ri[wv] = bi; }
-    __syncthreads();
-    if (tid == 0) {
-      for (int w = 1; w < FIX_THREADS / 64; ++w)
-        if (rb[w] < best || (rb[w] == best && ri[w] < bi)) { best = rb[w]; bi = ri[w]; }
-      assign[row] = U.cbase + bi;
-    }
-    __syncthreads();
+    if (lane == 0) assign[row] = U.cbase + bi;
   }
 }
 
@@ -1008,9 +1164,11 @@ hipError_t launch_build(const SeqArgs& sa, const void* Kv, const void* Vv, int32
       hipLaunchKernelGGL(k_assign<false>, dim3((unsigned)agrid), dim3(AS_THREADS), sizeof(AssignLds), st, sa, tpw, K,
                          chat, ws.norm, ix.assign, ws.amb);
     prof_end(st);
-    prof_begin("k_assign_fix", st);
-    hipLaunchKernelGGL(k_assign_fix, dim3(512), dim3(FIX_THREADS), 0, st, sa, K, chat, ix.assign, ws.amb);
-    prof_end(st);
+    if (sa.K_s > AS_GROUP) {  // k_assign decides its own near ties otherwise
+      prof_begin("k_assign_fix", st);
+      hipLaunchKernelGGL(k_assign_fix, dim3(512), dim3(FIX_THREADS), 0, st, sa, K, chat, ws.norm, ix.assign, ws.amb);
+      prof_end(st);
+    }
     if (trace != nullptr) {
       hipError_t e = hipMemcpyAsync(trace + (int64_t)it * rows, ix.assign, sizeof(int32_t) * (size_t)rows,
                                     hipMemcpyDeviceToDevice, st);

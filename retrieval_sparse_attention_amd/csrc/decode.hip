@@ -871,7 +871,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
     }
     load_window(lo);
   }
-  constexpr int U = 4;
+  constexpr int U = 8;
   // members of the selected clusters: rows [s0, min(s1, M))
   const int r1 = min(s1, M);
   for (int r = s0; r < r1; r += U) {
