@@ -303,7 +303,7 @@ def main():
     # algorithmic HBM bytes per launch: every byte a kernel must read or write once
     steady = ns + nl
     k_sel = k_max                                 # clusters selected per q head
-    n_est = -(-C // 512)                          # estimation chunks per kv head
+    n_est = -(-C // 128)                          # estimation chunks (workgroups) per kv head
     P = (int(rows_per_dec / H) + steady + 255) // 256
     part = 132 * 4                                # one partial softmax state
     rows = B * N * G                              # index rows
@@ -312,13 +312,14 @@ def main():
                    + H * C * 8)                   # rank keys + sortable keys out
     topk_bytes = (H * C * 4 + G * C * 8           # sortable keys; sizes + offsets
                   + H * k_sel * (4 + 8 + 4 + 4)   # ids, spans, keys, member prefix out
-                  + G * C * (128 * 4 + 4)         # estimation: value sums + sizes
-                  + H * C * 4                     # estimation: rank keys
-                  + H * n_est * part)             # estimation partials out
+                  + H * steady * 8)               # steady rows: cluster ids in, corrections out
     attend_bytes = (rows_per_dec * (2 * 128 * 2 + 4)       # K, V and perm of the retrieved rows
                     + H * steady * (2 * 128 * 2 + 4 + 4)   # steady rows: K, V, inv_perm, correction
                     + H * k_sel * 16                       # window metadata
-                    + B * H * 128 * 2 + H * P * part)      # q, partials out
+                    + B * H * 128 * 2 + H * P * part       # q, row partials out
+                    + G * C * (128 * 4 + 4)                # estimation: value sums + sizes
+                    + H * C * 4                            # estimation: rank keys
+                    + H * n_est * part)                    # estimation partials out
     merge_bytes = H * (P + n_est) * part + B * H * (128 * 4 + 4)
     step_bytes = score_bytes + topk_bytes + attend_bytes + merge_bytes
     assign_flops = 2.0 * B * N * K_s * 128 * G    # per launch (one k-means round)
