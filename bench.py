@@ -11,6 +11,10 @@ One step = the whole hot path over one batch of input: the index build of one la
 per second of that whole job.  Inputs are resident in HBM before timing.  L = 32 layers
 live in HBM at distinct addresses; step i rebuilds layer i mod L and its 64 queries visit
 the layers round robin, so no decode reuses the 256 MB Infinity Cache.
+
+`--workload` runs one of the method's other workloads instead (16k, 1m, batched: decode
+steps/s of the whole job; stress: index-build tokens/s of the clustering on 1M heavy-tailed
+keys per kv head); the default line is the 128K one.
 """
 import argparse
 import hashlib
@@ -30,6 +34,34 @@ WORKLOAD = dict(workload="llama3-8b-attention-layer-128k", batch=1, q_heads=32, 
                 ctx=131072, seg_len=8192, clusters_per_seg=512, kmeans_iters=10, n_sink=4, n_local=64,
                 topk_frac=0.02, decode_queries_per_step=64, layers=32, seed_data=2, seed_build=1234,
                 seed_query=102)
+# the other workloads of the method's evaluation (reported with --workload; the default line is
+# the 128K one): a small parity-size layer, the 1M-token layer, a ragged batch of 16 sequences
+# of 64K..128K tokens, and the clustering alone on 1M heavy-tailed keys per kv head
+WORKLOADS = {
+    "128k": WORKLOAD,
+    "16k": dict(workload="attention-layer-16k", batch=1, q_heads=8, kv_heads=2, head_dim=128, ctx=16384,
+                seg_len=8192, clusters_per_seg=512, kmeans_iters=10, n_sink=4, n_local=64, topk_frac=0.05,
+                decode_queries_per_step=64, layers=64, seed_data=1, seed_build=1234, seed_query=101),
+    "1m": dict(workload="llama3-8b-attention-layer-1m", batch=1, q_heads=32, kv_heads=8, head_dim=128,
+               ctx=1048576, seg_len=16384, clusters_per_seg=1024, kmeans_iters=10, n_sink=4, n_local=512,
+               topk_frac=0.018, decode_queries_per_step=32, layers=2, seed_data=3, seed_build=1234,
+               seed_query=103),
+    "batched": dict(workload="batched-decode-16-ragged-64k-128k", batch=16, q_heads=32, kv_heads=8, head_dim=128,
+                    ctx=[65536, 131072], seg_len=8192, clusters_per_seg=512, kmeans_iters=10, n_sink=4,
+                    n_local=64, topk_frac=0.02, decode_queries_per_step=64, layers=2, seed_data=4,
+                    seed_build=1234, seed_query=104),
+    "stress": dict(workload="index-build-1m-keys-student-t", batch=1, q_heads=8, kv_heads=8, head_dim=128,
+                   ctx=1048576, seg_len=8192, clusters_per_seg=512, kmeans_iters=10, heavy_tailed=True,
+                   n_sink=4, n_local=64, topk_frac=0.02, decode_queries_per_step=0, layers=1, seed_data=5,
+                   seed_build=1234, seed_query=105),
+}
+
+
+def num_clusters(n, seg, ks):
+    """Clusters of a sequence of n tokens: K_s per full segment, ceil(L K_s / L_s) for a short last one."""
+    nseg = -(-n // seg)
+    last = n - (nseg - 1) * seg
+    return (nseg - 1) * ks + (ks if last >= seg else -(-last * ks // seg))
 
 
 def parse():
@@ -37,7 +69,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--layers", type=int, default=WORKLOAD["layers"])
+    p.add_argument("--workload", choices=sorted(WORKLOADS), default="128k",
+                   help="workload of the line (default: the 128K layer, the headline one)")
+    p.add_argument("--layers", type=int, default=None, help="layer indexes in HBM (default: the workload's)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the oracle timing sample")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -183,17 +217,23 @@ def main():
         print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "launches": 3}))
         return
 
-    W = dict(WORKLOAD)
-    W["layers"] = args.layers
-    B, H, G, N = W["batch"], W["q_heads"], W["kv_heads"], W["ctx"]
+    W = dict(WORKLOADS[args.workload])
+    if args.layers is not None:
+        W["layers"] = args.layers
+    headline = args.workload == "128k"
+    B, H, G = W["batch"], W["q_heads"], W["kv_heads"]
     seg, K_s, iters = W["seg_len"], W["clusters_per_seg"], W["kmeans_iters"]
     ns, nl, frac, QPS = W["n_sink"], W["n_local"], W["topk_frac"], W["decode_queries_per_step"]
-    L = args.layers
-    ctx = np.array([N] * B, np.int64)
+    L = W["layers"]
+    if isinstance(W["ctx"], list):  # ragged: N_b ~ U{lo..hi} from the data seed
+        ctx = synth.ctx_lengths(W["seed_data"], B, W["ctx"][0], W["ctx"][1])
+    else:
+        ctx = np.array([W["ctx"]] * B, np.int64)
+    N = int(ctx.max())
 
     print("generating inputs", file=sys.stderr, flush=True)
-    K, V, _ = synth.kv(W["seed_data"], B, G, ctx, seg)
-    nq = QPS * 4
+    K, V, _ = synth.kv(W["seed_data"], B, G, ctx, seg, heavy=W.get("heavy_tailed", False))
+    nq = max(QPS, 1) * 4
     q, _ = synth.queries(W["seed_query"], nq, B, H, G, ctx, K)
     Kd0 = torch.from_numpy(K.view(np.int16)).to(dev).view(torch.bfloat16)
     Vd0 = torch.from_numpy(V.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -228,7 +268,7 @@ def main():
             rsa.wave_attn_decode(idxs[lay], qd[qi], ns, nl, frac, ws=dws, out=out, sel_ids=ids, lse=lse)
 
     # the step pattern repeats with period P: one captured HIP graph per phase
-    P = math.lcm(L, max(1, nq // math.gcd(nq, QPS)))
+    P = math.lcm(L, max(1, nq // math.gcd(nq, max(QPS, 1))))
     print("warmup (eager)%s" % ("" if args.eager else " and capture of %d step graphs" % P), file=sys.stderr,
           flush=True)
     for i in range(max(1, args.warmup)):
@@ -241,10 +281,11 @@ def main():
             with torch.cuda.graph(g):
                 job(ph)
             graphs.append(g)
-            g2 = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g2):
-                job(ph, build=False)
-            dgraphs.append(g2)
+            if QPS > 0:
+                g2 = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g2):
+                    job(ph, build=False)
+                dgraphs.append(g2)
         torch.cuda.synchronize()
         for i in range(args.warmup):
             graphs[i % P].replay()
@@ -267,12 +308,14 @@ def main():
     t_plain = e0.elapsed_time(e1)
     print("timed %d steps: %.3f ms" % (args.steps, t_plain), file=sys.stderr, flush=True)
     # decode queries alone (same 64 per step, no build)
-    e0.record()
-    for i in range(args.warmup, args.warmup + args.steps):
-        run(i, build=False)
-    e1.record()
-    torch.cuda.synchronize()
-    t_dec = e0.elapsed_time(e1)
+    t_dec = None
+    if QPS > 0:
+        e0.record()
+        for i in range(args.warmup, args.warmup + args.steps):
+            run(i, build=False)
+        e1.record()
+        torch.cuda.synchronize()
+        t_dec = e0.elapsed_time(e1)
 
     # ---- the same steps once more, eagerly, with HIP events around every kernel on its
     # launch stream: per-kernel durations for the roofline, and the selected ids
@@ -289,53 +332,67 @@ def main():
     t_ms = e0.elapsed_time(e1)
 
     # ---- algorithmic work per launch (actual sizes of the selected clusters)
-    sizes = [ix.sizes.cpu().numpy() for ix in idxs[:1]][0]  # every layer holds the same clustering
-    C = sizes.shape[0] // G
-    ids_h = ids_log[:, :, :, :k_max].cpu().numpy().reshape(args.steps * QPS, B * H, k_max)
-    retrieved_rows = 0
-    for qq in range(ids_h.shape[0]):
-        for h in range(H):
-            g = h * G // H
-            sel = ids_h[qq, h]
-            sel = sel[sel >= 0]
-            retrieved_rows += int(sizes[g * C + sel].sum())
-    rows_per_dec = retrieved_rows / ids_h.shape[0]
+    sizes = idxs[0].sizes.cpu().numpy()  # every layer holds the same clustering
+    Cb = [num_clusters(int(n), seg, K_s) for n in ctx]
+    Ctot = sum(Cb)
+    cbase = np.concatenate([[0], np.cumsum([G * c for c in Cb])]).astype(np.int64)
+    nq_t = args.steps * QPS
+    retrieved_rows, n_sel = 0, 0
+    if nq_t > 0:
+        ids_h = ids_log[:, :, :, :k_max].cpu().numpy()  # [queries, B, H, k_max]
+        for qq in range(nq_t):
+            for b in range(B):
+                for h in range(H):
+                    sel = ids_h[qq, b, h]
+                    sel = sel[sel >= 0]
+                    n_sel += len(sel)
+                    retrieved_rows += int(sizes[cbase[b] + (h * G // H) * Cb[b] + sel].sum())
+    rows_per_dec = retrieved_rows / max(nq_t, 1)
+    sel_per_dec = n_sel / max(nq_t, 1)             # clusters selected per decode call, all (b, h)
     # algorithmic HBM bytes per launch: every byte a kernel must read or write once
     steady = ns + nl
-    k_sel = k_max                                 # clusters selected per q head
-    n_est = -(-C // 128)                          # estimation chunks (workgroups) per kv head
-    P = (int(rows_per_dec / H) + steady + 255) // 256
+    n_est = sum(-(-c // 128) for c in Cb)          # estimation chunks (workgroups) per kv head
+    P = (int(rows_per_dec / (B * H)) + steady + 255) // 256
     part = 132 * 4                                # one partial softmax state
-    rows = B * N * G                              # index rows
-    score_bytes = (G * C * (128 * 2 + 4)          # bf16 centroid rows + sizes
+    rows = G * int(ctx.sum())                     # index rows
+    score_bytes = (G * Ctot * (128 * 2 + 4)       # bf16 centroid rows + sizes
                    + B * H * 128 * 2              # q
-                   + H * C * 8)                   # rank keys + sortable keys out
-    topk_bytes = (H * C * 4 + G * C * 8           # sortable keys; sizes + offsets
-                  + H * k_sel * (4 + 8 + 4 + 4)   # ids, spans, keys, member prefix out
-                  + H * steady * 8)               # steady rows: cluster ids in, corrections out
-    attend_bytes = (rows_per_dec * (2 * 128 * 2 + 4)       # K, V and perm of the retrieved rows
-                    + H * steady * (2 * 128 * 2 + 4 + 4)   # steady rows: K, V, inv_perm, correction
-                    + H * k_sel * 16                       # window metadata
-                    + B * H * 128 * 2 + H * P * part       # q, row partials out
-                    + G * C * (128 * 4 + 4)                # estimation: value sums + sizes
-                    + H * C * 4                            # estimation: rank keys
-                    + H * n_est * part)                    # estimation partials out
-    merge_bytes = H * (P + n_est) * part + B * H * (128 * 4 + 4)
+                   + H * Ctot * 8)                # rank keys + sortable keys out
+    topk_bytes = (H * Ctot * 4 + G * Ctot * 8     # sortable keys; sizes + offsets
+                  + sel_per_dec * (4 + 8 + 4 + 4)  # ids, spans, keys, member prefix out
+                  + B * H * steady * 8)           # steady rows: cluster ids in, corrections out
+    attend_bytes = (rows_per_dec * (2 * 128 * 2 + 4)         # K, V and perm of the retrieved rows
+                    + B * H * steady * (2 * 128 * 2 + 4 + 4)  # steady rows: K, V, inv_perm, correction
+                    + sel_per_dec * 16                        # window metadata
+                    + B * H * 128 * 2 + B * H * P * part      # q, row partials out
+                    + G * Ctot * (128 * 4 + 4)                # estimation: value sums + sizes
+                    + H * Ctot * 4                            # estimation: rank keys
+                    + H * n_est * part)                       # estimation partials out
+    merge_bytes = B * H * P * part + H * n_est * part + B * H * (128 * 4 + 4)
     step_bytes = score_bytes + topk_bytes + attend_bytes + merge_bytes
-    assign_flops = 2.0 * B * N * K_s * 128 * G    # per launch (one k-means round)
-    assign_bytes = rows * (128 * 2 + 4) + G * C * (128 * 2 + 4)
-    update_bytes = ((iters - 1) * (rows * (128 * 2 + 4) + G * C * (128 * 4 + 128 * 2 + 4))
-                    + rows * (4 * 128 * 2 + 3 * 4) + G * C * (2 * 128 * 4 + 128 * 2 + 4)) / iters
-    sort_bytes = rows * 12 + G * C * 8
-    init_bytes = G * C * (128 * 2 + 128 * 4 + 128 * 2 + 4)
+    # per launch (one k-means round): every unit's tokens against its own clusters
+    tok_clu = 0
+    for n in ctx:
+        n = int(n)
+        nseg = -(-n // seg)
+        for si in range(nseg):
+            ls = min(seg, n - si * seg)
+            tok_clu += ls * (K_s if ls >= seg else -(-ls * K_s // seg))
+    assign_flops = 2.0 * 128 * G * tok_clu
+    assign_bytes = rows * (128 * 2 + 4) + G * Ctot * (128 * 2 + 4)
+    update_bytes = ((iters - 1) * (rows * (128 * 2 + 4) + G * Ctot * (128 * 4 + 128 * 2 + 4))
+                    + rows * (4 * 128 * 2 + 3 * 4) + G * Ctot * (2 * 128 * 4 + 128 * 2 + 4)) / iters
+    sort_bytes = rows * 12 + G * Ctot * 8
+    init_bytes = G * Ctot * (128 * 2 + 128 * 4 + 128 * 2 + 4)
     hbm_bytes = {"k_score": score_bytes, "k_topk": topk_bytes, "k_attend": attend_bytes, "k_merge": merge_bytes,
                  "k_update": update_bytes, "k_sort": sort_bytes, "k_init": init_bytes}
 
     kern = {}
     for name, (cnt, ms) in prof.items():
         kern[name] = {"launches": cnt, "avg_us": 1000.0 * ms / cnt, "total_ms": ms}
-    sha = source_sha(SOURCES)
-    dom = max(kern, key=lambda k: kern[k]["total_ms"])
+    # the committed counter summaries are of the 128K workload
+    sha = source_sha(SOURCES) if headline else "not-the-128k-workload"
+    dom = max((k for k in kern if k in hbm_bytes or k == "k_assign"), key=lambda k: kern[k]["total_ms"])
     if dom == "k_assign":
         ach = assign_flops / (kern[dom]["avg_us"] * 1e-6) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
@@ -361,12 +418,22 @@ def main():
                              "traffic": counter_traffic("k_assign", sha)}
 
     decodes = args.steps * QPS
-    value = decodes / (t_plain / 1000.0)
     build_ms = sum(kern[k]["total_ms"] for k in kern if k not in ("k_score", "k_topk", "k_attend", "k_merge"))
+    build_tps = args.steps * int(ctx.sum()) / (build_ms / 1000.0)
+    if QPS > 0:
+        metric = ("sparse decode-attn steps/s (whole job: index build + %d decode queries per step), %s"
+                  % (QPS, "8B-shape layer at 128K ctx" if headline else W["workload"]))
+        value, unit = decodes / (t_plain / 1000.0), "decode steps/s"
+    else:
+        metric = "index-build tokens/s (segmented k-means + layout), %s" % W["workload"]
+        value, unit = args.steps * int(ctx.sum()) / (t_plain / 1000.0), "tokens/s"
+    cfg = dict(W)
+    if isinstance(W["ctx"], list):
+        cfg["ctx_per_sequence"] = [int(n) for n in ctx]
     result = {
-        "metric": "sparse decode-attn steps/s (whole job: index build + 64 decode queries per step), 8B-shape layer at 128K ctx",
+        "metric": metric,
         "value": round(value, 1),
-        "unit": "decode steps/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -376,20 +443,20 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": W,
+        "config": cfg,
         "roofline": roof,
-        "decode_only_steps_per_s": round(decodes / (t_dec / 1000.0), 1),
-        "decode_only_us_per_query": round(1000.0 * t_dec / decodes, 2),
-        "decode_only_effective_GBs": round(step_bytes * decodes / (t_dec / 1000.0) / 1e9, 1),
-        "decode_bytes_per_query": int(step_bytes),
-        "build_tokens_per_s": round(args.steps * B * N / (build_ms / 1000.0), 1),
+        "decode_only_steps_per_s": round(decodes / (t_dec / 1000.0), 1) if QPS > 0 else None,
+        "decode_only_us_per_query": round(1000.0 * t_dec / decodes, 2) if QPS > 0 else None,
+        "decode_only_effective_GBs": round(step_bytes * decodes / (t_dec / 1000.0) / 1e9, 1) if QPS > 0 else None,
+        "decode_bytes_per_query": int(step_bytes) if QPS > 0 else None,
+        "build_tokens_per_s": round(build_tps, 1),
         "timing": "eager launches" if args.eager else "HIP graph replays",
         "eager_with_kernel_events_ms_per_step": round(t_ms / args.steps, 4),
         "kernels": {k: {"launches": v["launches"], "avg_us": round(v["avg_us"], 2)} for k, v in kern.items()},
         "kernel_roofline": extra,
         "source_sha": sha,
     }
-    if not args.no_cpu_baseline:
+    if headline and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(W, K, V, ctx, q, args.cpu_seconds)
     print(json.dumps(result))
 

@@ -1028,6 +1028,8 @@ static void launch_gs(const SeqArgs& sa, const DecodeArgs& da, const wave_index&
   const dim3 tg(sa.B * da.H), tb(TK_THREADS);
   const size_t tl = sizeof(TopkLds);
   switch (da.NV) {
+    case 1: hipLaunchKernelGGL(k_topk<1>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
+    case 2: hipLaunchKernelGGL(k_topk<2>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
     case 4: hipLaunchKernelGGL(k_topk<4>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
     case 8: hipLaunchKernelGGL(k_topk<8>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
     case 16: hipLaunchKernelGGL(k_topk<16>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
@@ -1047,7 +1049,8 @@ hipError_t launch_decode(const SeqArgs& sa, const DecodeArgs& da, const wave_ind
   static bool attrs = false;
   if (!attrs) {
     const size_t tl = sizeof(TopkLds);
-    const void* fns[] = {reinterpret_cast<const void*>(&k_topk<0>), reinterpret_cast<const void*>(&k_topk<4>),
+    const void* fns[] = {reinterpret_cast<const void*>(&k_topk<0>), reinterpret_cast<const void*>(&k_topk<1>),
+                         reinterpret_cast<const void*>(&k_topk<2>), reinterpret_cast<const void*>(&k_topk<4>),
                          reinterpret_cast<const void*>(&k_topk<8>), reinterpret_cast<const void*>(&k_topk<16>)};
     for (const void* f : fns) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, tl);
     attrs = true;
