@@ -187,7 +187,8 @@ __global__ __launch_bounds__(INIT_THREADS) void k_init(SeqArgs sa, uint64_t seed
 // (A tiles 0-1, then 2-3); while one half runs on the matrix core, the same
 // wave selects over the other half's results on the vector ALU, so one wave
 // keeps both pipes busy. Units with more than 512 clusters (MULTI) take the
-// centroids in groups of 512, reloaded per tile.
+// centroids in groups of 512, one pass over the range's token tiles per group, the
+// running best / second best / id of every token kept in LDS between passes.
 //
 // Selection per lane: the 6-bit position of each of its 64 values is written
 // into the value's low mantissa bits, so the best and second best come from
@@ -219,6 +220,7 @@ constexpr int AS_TT = 128;                   // tokens per LDS tile (4 blocks of
 constexpr int AS_CPW = 128;                  // centroids per wave
 constexpr int AS_GROUP = AS_WAVES * AS_CPW;  // centroids per pass
 constexpr int AS_MAXTPW = 8192;              // tokens per workgroup at most (the near-tie list fits a tile buffer)
+constexpr int AS_MAXTPW_M = 4096;            // the same with more than AS_GROUP clusters (the running bests fit LDS)
 
 // Token tiles are double buffered and loaded straight into LDS (global_load_lds,
 // 16 bytes per lane); one barrier per tile. The work of a tile's start (the
@@ -231,6 +233,8 @@ struct AssignLds {
   // take the flags of the empty decision pass before the first tile
   uint8_t ambf[AS_MAXTPW + AS_TT];
   float4 nrm[WAVE_MAX_CLUSTERS_PER_SEG / 4];  // |c_j|^2 of the unit's centroids
+  float part[AS_MAXTPW_M + AS_TT][3]; // more than AS_GROUP clusters: running best, second best, id per token
+                                     // of the range over the centroid groups so far (+ spare slots)
   unsigned long long fd[32];         // exact decision: per token the least D_j (bits), then its id
   int32_t fj[32];
   int32_t scan[AS_THREADS];
@@ -354,7 +358,7 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
           nh[r][4 * a4 + k] = r0 + k < U.Kc ? -0.5f * f[k] : -__FLT_MAX__;
       }
   };
-  if (!MULTI) load_a(0);
+  load_a(0);
   // the unit's squared centroid norms into LDS, and their maximum (all are >= 0)
   {
     float m = 0.f;
@@ -375,12 +379,12 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
     rd[2] = 0.f;
   }
   __syncthreads();
-  if (!MULTI) load_nh(0);
+  load_nh(0);
   const float R2 = fmaxf(fmaxf(S.rmx[0], S.rmx[1]), fmaxf(S.rmx[2], S.rmx[3])), R = __builtin_amdgcn_sqrtf(R2);
   // Decisions for tile Tm (Tm = -1: the empty pass, whose stores go to rows of tile 0 and
   // are overwritten by the real ones): wave wv takes tokens 32 wv .. 32 wv + 31, both
   // lane halves the same token; merge the 4 waves, store, flag near ties. x2: |x|^2.
-  auto reduce = [&](int Tm, float x2) {
+  auto reduce = [&](int Tm, float x2, int grp, bool last) {
     const int bi = Tm & 1;
     const int tk = wv * 32 + col;
     float b1 = S.red[bi][0][tk][0], b2 = S.red[bi][0][tk][1];
@@ -398,8 +402,24 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
     }
     // id of the winner: group, wave, A tile and row i of its 32x32 block, lane half
     const int p = (int)(meta & 63u), hw = (int)((meta >> 6) & 1u), gw = (int)(meta >> 7);
-    const int best_id = gw * AS_GROUP + wbest * AS_CPW + (p >> 4) * 32 + 8 * ((p & 15) >> 2) + 4 * hw + (p & 3);
+    int best_id = gw * AS_GROUP + wbest * AS_CPW + (p >> 4) * 32 + 8 * ((p & 15) >> 2) + 4 * hw + (p & 3);
     const int tr = Tm * AS_TT + tk;
+    if constexpr (MULTI) {
+      // running best over the centroid groups (the empty pass before tile 0 uses spare slots)
+      float* pp = S.part[Tm < 0 ? AS_MAXTPW_M + tk : tr];
+      if (grp > 0) {
+        const float q1 = pp[0], q2 = pp[1];
+        const int qid = __float_as_int(pp[2]);
+        const bool keep = !(b1 > q1);  // equal bests: a gap of 0, decided in binary64
+        b2 = fmaxf(fminf(q1, b1), fmaxf(q2, b2));
+        b1 = fmaxf(q1, b1);
+        best_id = keep ? qid : best_id;
+      }
+      pp[0] = b1;
+      pp[1] = b2;
+      pp[2] = __int_as_float(best_id);
+      if (!last) return;
+    }
     assign[U.row0 + tb0 + min(max(tr, tk), nrow - 1)] = U.cbase + best_id;
     const float margin = 0x1p-14f * (__builtin_amdgcn_sqrtf(x2) * R + R2) + 0x1p-100f;
     // also undecided: a best at the floor of the padding rows (values beyond fp32 range)
@@ -463,18 +483,9 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
     // the winner's position: its packed 6 bits, its half, the centroid group
     const uint32_t meta = ((uint32_t)grp << 7) | ((uint32_t)(take ? h ^ 1 : h) << 6) | (__float_as_uint(nb1) & 63u);
     float* rd = S.red[bi][wv][tb * 32 + col];
-    if (MULTI && grp > 0) {
-      const float pb1 = rd[0], pb2 = rd[1];
-      const uint32_t pm = __float_as_uint(rd[2]);
-      const bool keep = !(nb1 > pb1);
-      rd[0] = fmaxf(pb1, nb1);
-      rd[1] = fmaxf(fminf(pb1, nb1), fmaxf(pb2, nb2));
-      rd[2] = __uint_as_float(keep ? pm : meta);
-    } else {
-      rd[0] = nb1;
-      rd[1] = nb2;
-      rd[2] = __uint_as_float(meta);
-    }
+    rd[0] = nb1;
+    rd[1] = nb2;
+    rd[2] = __uint_as_float(meta);
   };
   // one tile against one centroid group: 8 half-block steps, the selection of step j - 1
   // next to the MFMAs of step j. Each step is its own scheduling region: first the LDS
@@ -519,30 +530,38 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
     sel_half(accB, 1, b1, b2);
     finish(3, bi, grp, b1, b2);
   };
-  float xn = 0.f;  // |x|^2 of this wave's tokens of the previous tile
-  for (int T = 0; T < ntiles; ++T) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of tile T have landed
-    __syncthreads();  // tile T is in LDS; red[(T - 1) & 1] is complete
-    const int bi = T & 1;
-    // into the buffer of tile T - 1, which every wave has finished; after the last tile a
-    // harmless reload of it
-    issue(min(T + 1, ntiles - 1), bi ^ 1);
-    reduce(T - 1, xn);
-    xn = xnorm(bi);
-    if (!MULTI) {
-      tile(bi, 0);
-    } else {
-      for (int grp = 0; grp < ngroups; ++grp) {
+  // one pass of the range's tiles against centroid group grp; the decisions in the last
+  auto pass = [&](int grp, bool last) {
+    float xn = 0.f;  // |x|^2 of this wave's tokens of the previous tile
+    for (int T = 0; T < ntiles; ++T) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of tile T have landed
+      __syncthreads();  // tile T is in LDS; red[(T - 1) & 1] is complete
+      const int bi = T & 1;
+      // into the buffer of tile T - 1, which every wave has finished; after the last tile a
+      // harmless reload of it
+      issue(min(T + 1, ntiles - 1), bi ^ 1);
+      reduce(T - 1, xn, grp, last);
+      xn = xnorm(bi);
+      tile(bi, grp);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the trailing reload has landed: the buffers are free
+    __syncthreads();
+    reduce(ntiles - 1, xn, grp, last);
+    __syncthreads();
+  };
+  if (!MULTI) {
+    pass(0, true);
+  } else {
+    // more than AS_GROUP clusters: a pass per group of them, the token tiles streamed again
+    for (int grp = 0; grp < ngroups; ++grp) {
+      if (grp > 0) {
         load_a(grp);
         load_nh(grp);
-        tile(bi, grp);
+        issue(0, 0);
       }
+      pass(grp, grp == ngroups - 1);
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the trailing reload has landed: the buffers are free
-  __syncthreads();
-  reduce(ntiles - 1, xn);
-  __syncthreads();
   // near-tie tokens: flags counted per thread (4 per word) and a workgroup scan
   const uint32_t* fw = reinterpret_cast<const uint32_t*>(S.ambf + AS_TT);
   const int nw = ntiles * (AS_TT / 4), per = (nw + AS_THREADS - 1) / AS_THREADS;
@@ -1106,7 +1125,7 @@ static int assign_tpw(const SeqArgs& sa, int64_t units) {
   const int64_t per = std::max<int64_t>(1, (256 + units - 1) / units);
   int64_t t = (sa.seg_len + per - 1) / per;
   t = (t + AS_TT - 1) / AS_TT * AS_TT;
-  return (int)std::min<int64_t>(AS_MAXTPW, std::max<int64_t>(AS_TT, t));
+  return (int)std::min<int64_t>(sa.K_s > AS_GROUP ? AS_MAXTPW_M : AS_MAXTPW, std::max<int64_t>(AS_TT, t));
 }
 
 static int64_t assign_grid(const SeqArgs& sa, int tpw) {

@@ -345,7 +345,8 @@ __device__ inline void bitonic_desc(uint64_t* a, int n, bool global) {
 //
 // Ids: wave w owns [w 64 NV, (w + 1) 64 NV); lane L holds ids
 // w0 + 64 v + L (v < NV): every load is 64 consecutive ids, and a wave's order
-// of (v, lane) is id order. With NV <= 16 the keys stay in registers.
+// of (v, lane) is id order. With NV <= 32 the keys stay in registers (the fast
+// path below takes NV <= 16).
 //
 // Fast path (keys in registers, k <= 1024): every wave finds the m-th largest
 // of its 64 lane maxima, t_w (m = ceil(kreq / 16)), by bisection over the 32
@@ -380,7 +381,7 @@ template <int NVR>
 __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, wave_index ix, DecodeWs ws,
                                                      int32_t* __restrict__ sel_ids) {
   constexpr bool INREG = NVR > 0;
-  constexpr int CHK = INREG ? NVR : 8;  // keys per lane per chunk
+  constexpr int CHK = INREG ? (NVR < 16 ? NVR : 16) : 8;  // keys per lane per chunk
   extern __shared__ uint8_t smem[];
   TopkLds& L = *reinterpret_cast<TopkLds*>(smem);
   const int NV = INREG ? NVR : da.NVg;
@@ -521,9 +522,10 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
   X = max(X, 1u);
 
   // 2. fast path: candidates u >= X; rank and size prefix by counting
-  bool fast = INREG && k > 0 && k <= TK_CAP;
+  // (32 keys per lane: the general path only, the keys in registers)
+  bool fast = INREG && NVR <= 16 && k > 0 && k <= TK_CAP;
   if (fast) {
-    if constexpr (INREG) {
+    if constexpr (INREG && NVR <= 16) {
       uint64_t bal[NVR];
       int tot = 0;
 #pragma unroll
@@ -649,16 +651,8 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
     for (int c0 = 0; c0 < NV; c0 += CHK) {
       uint32_t uc[CHK];
       chunk_keys(c0, uc);
-      int ofv[CHK], szv[CHK];
-      float kfv[CHK];
-#pragma unroll
-      for (int v = 0; v < CHK; ++v) {
-        const int j = min(id_of(c0 + v), C - 1);
-        ofv[v] = offs[j];
-        szv[v] = sizes[j];
-        kfv[v] = keys[j];
-      }
-      // per 64 ids (one v): lane-order prefix of (eq, selected) counts by ballots
+      // per 64 ids (one v): lane-order prefix of (eq, selected) counts by ballots; the
+      // selected keys' offsets, sizes and rank keys are loaded where they are selected
 #pragma unroll
       for (int v = 0; v < CHK; ++v) {
         const uint32_t x = uc[v];
@@ -669,8 +663,8 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
         if (sv) {
           const int j = id_of(c0 + v);
           const int p = pos + __popcll(sm & ltmask);
-          span[p] = make_int2(ofv[v], szv[v]);
-          skey[p] = kfv[v];
+          span[p] = make_int2(offs[j], sizes[j]);
+          skey[p] = keys[j];
           sb_[p] = ((uint64_t)x << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)j);
           atomicOr(&selw[j >> 5], 1u << (j & 31));
         }
@@ -1033,6 +1027,7 @@ static void launch_gs(const SeqArgs& sa, const DecodeArgs& da, const wave_index&
     case 4: hipLaunchKernelGGL(k_topk<4>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
     case 8: hipLaunchKernelGGL(k_topk<8>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
     case 16: hipLaunchKernelGGL(k_topk<16>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
+    case 32: hipLaunchKernelGGL(k_topk<32>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
     default: hipLaunchKernelGGL(k_topk<0>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
   }
   prof_end(st);
@@ -1049,9 +1044,10 @@ hipError_t launch_decode(const SeqArgs& sa, const DecodeArgs& da, const wave_ind
   static bool attrs = false;
   if (!attrs) {
     const size_t tl = sizeof(TopkLds);
-    const void* fns[] = {reinterpret_cast<const void*>(&k_topk<0>), reinterpret_cast<const void*>(&k_topk<1>),
-                         reinterpret_cast<const void*>(&k_topk<2>), reinterpret_cast<const void*>(&k_topk<4>),
-                         reinterpret_cast<const void*>(&k_topk<8>), reinterpret_cast<const void*>(&k_topk<16>)};
+    const void* fns[] = {reinterpret_cast<const void*>(&k_topk<0>),  reinterpret_cast<const void*>(&k_topk<1>),
+                         reinterpret_cast<const void*>(&k_topk<2>),  reinterpret_cast<const void*>(&k_topk<4>),
+                         reinterpret_cast<const void*>(&k_topk<8>),  reinterpret_cast<const void*>(&k_topk<16>),
+                         reinterpret_cast<const void*>(&k_topk<32>)};
     for (const void* f : fns) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, tl);
     attrs = true;
   }

@@ -15,7 +15,7 @@ struct DecodeArgs {
   int32_t n_sink, n_local;
   int32_t k_max;          // id columns of the output
   int32_t P;              // gathered-row workgroups per (b, h)
-  int32_t NV;             // keys per lane of the register top-k (1, 2, 4, 8, 16), 0: keys read from memory
+  int32_t NV;             // keys per lane of the register top-k (1, 2, ..., 32), 0: keys read from memory
   int32_t NP;             // partial slots per (b, h): P + max_b ceil(C_b / DEC_SCORE_CH)
   int32_t scap;           // steady entries per (b, h)
   float tau;              // 1/sqrt(128)

@@ -174,7 +174,7 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
   // keys per lane of the top-k (16 waves x 64 lanes): the fewest that hold every key, so
   // that every wave holds keys (its thresholds then bound the selection); 0: beyond registers
   da.NV = 0;
-  for (int nv = 1; nv <= 16; nv *= 2)
+  for (int nv = 1; nv <= 32; nv *= 2)
     if (16 * 64 * nv >= Cmax) { da.NV = nv; break; }
   da.NVg = (int32_t)(((Cmax + 16 * 64 * 16 - 1) / (16 * 64 * 16)) * 16);
   int sort_stride = 0;
