@@ -180,6 +180,40 @@ __global__ __launch_bounds__(SCORE_THREADS) void k_score(SeqArgs sa, DecodeArgs 
       ws.key32[kb + (int64_t)hh * C + jj] = elig ? float_sortable(key) : 0u;
     }
   }
+  // per q head (a wave each): the chunk's 4 largest sortable keys (a multiset) and its
+  // eligible count, from which the top-k takes a threshold when its keys do not fit
+  // registers (da.NV == 0)
+  const int chm = da.NP - da.P;
+  for (int hh = wv; da.NV == 0 && hh < GS; hh += SCORE_THREADS / 64) {
+    uint32_t u[2];
+    int ne = 0;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int jj = lane + 64 * r;
+      const int n = jj < nc ? S.nsz[jj] : 0;
+      const bool elig = jj < nc && !sz.all && n > 0 && S.scnt[jj] < n;
+      u[r] = elig ? float_sortable(S.kw[hh][jj]) : 0u;
+      ne += elig;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ne += __shfl_xor(ne, o, 64);
+    uint32_t* ct = ws.ctop + ((int64_t)(b * da.H + g * GS + hh) * chm + chunk) * 8;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      uint32_t mx = max(u[0], u[1]);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+      const uint64_t b0 = __ballot(u[0] == mx), b1 = __ballot(u[1] == mx);
+      // take out one instance: the lowest lane's
+      if (b0 != 0ull) {
+        if (lane == __ffsll((unsigned long long)b0) - 1) u[0] = 0u;
+      } else if (lane == __ffsll((unsigned long long)b1) - 1) {
+        u[1] = 0u;
+      }
+      if (lane == 0) ct[r4] = mx;
+    }
+    if (lane == 0) ct[4] = (uint32_t)ne;
+  }
 }
 
 // ------------------------------------------------------------------ estimation role
@@ -371,6 +405,7 @@ struct TopkLds {
   uint32_t selw[TK_SELW];       // selection bitmap (C <= 65536)
   uint64_t scan[17];
   uint32_t bis[34];             // block counts of the bisection, then of keys above T
+  uint32_t cbis[32];            // block counts of the bisection over the chunks' top keys
   int32_t wE[16];
   uint32_t wt[16];
   int32_t tcnt[16];             // keys >= wt[i] over the workgroup
@@ -456,6 +491,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
     L.u.c.pre[tid] = 0;
   }
   if (tid < 34) L.bis[tid] = 0u;
+  if (tid < 32) L.cbis[tid] = 0u;
   if (tid < 8) L.misc[tid] = 0;
   if (tid < 16) L.tcnt[tid] = 0;
 
@@ -478,12 +514,14 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
       }
     }
   } else {
-    for (int c0 = 0; c0 < NV; c0 += CHK) {
-      uint32_t uc[CHK];
-      chunk_keys(c0, uc);
+    // eligible keys from k_score's chunk summaries (thread t adds chunks t, t + 1024, ...)
+    const int nch = (C + SC - 1) / SC;
+    const uint32_t* ct = ws.ctop + (int64_t)bh * (da.NP - da.P) * 8;
+    int e = 0;
+    for (int i = tid; i < nch; i += nt) e += (int)ct[(int64_t)i * 8 + 4];
 #pragma unroll
-      for (int v = 0; v < CHK; ++v) Ew += __popcll(__ballot(uc[v] != 0u));
-    }
+    for (int o = 32; o > 0; o >>= 1) e += __shfl_xor(e, o, 64);
+    Ew = e;
   }
   // rank keys of the steady tokens' clusters, for the corrections at the end
   float kjr[2];
@@ -602,8 +640,75 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
     }
   }
 
+  // 3a. keys read from memory: a threshold t from the chunks' top-4 keys (the k-th largest
+  // of them is at most the k-th largest key, so the keys >= t hold the selection), one
+  // pass collecting those keys into LDS, and a sort of them
+  bool done = false;
+  if constexpr (!INREG) {
+    const int nch = (C + SC - 1) / SC;
+    const uint32_t* ct = ws.ctop + (int64_t)bh * (da.NP - da.P) * 8;
+    if (k > 0 && k <= 4 * nch && nch <= TK_THREADS) {
+      uint32_t tv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tv[r] = tid < nch ? ct[(int64_t)tid * 8 + r] : 0u;
+      uint32_t t = 0u;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = t | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cnt += __popcll(__ballot(tv[r] >= c));
+        if (lane == 0) atomicAdd(&L.cbis[bit], (uint32_t)cnt);
+        lds_barrier();
+        if (L.cbis[bit] >= (uint32_t)k) t = c;
+      }
+      if (t > 0u) {
+        uint64_t* cb = L.u.sortbuf;
+        for (int c0 = 0; c0 < NV; c0 += CHK) {
+          uint32_t uc[CHK];
+          chunk_keys(c0, uc);
+          uint64_t bal[CHK];
+          int tot = 0;
+#pragma unroll
+          for (int v = 0; v < CHK; ++v) {
+            bal[v] = __ballot(uc[v] >= t);
+            tot += __popcll(bal[v]);
+          }
+          int base = 0;
+          if (lane == 0 && tot > 0) base = atomicAdd(&L.misc[1], tot);
+          base = __shfl(base, 0, 64);
+#pragma unroll
+          for (int v = 0; v < CHK; ++v) {
+            if (uc[v] >= t) {
+              const int p = base + __popcll(bal[v] & ltmask);
+              if (p < TK_SORT) cb[p] = ((uint64_t)uc[v] << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)id_of(c0 + v));
+            }
+            base += __popcll(bal[v]);
+          }
+        }
+        lds_barrier();
+        const int nc = L.misc[1];
+        if (nc <= TK_SORT) {
+          int P2 = 1;
+          while (P2 < nc) P2 <<= 1;
+          for (int i = nc + tid; i < P2; i += nt) cb[i] = 0ull;
+          __syncthreads();
+          bitonic_desc(cb, P2, false);
+          // (key desc, id asc): the first k are the selection in rank order
+          for (int r = tid; r < k; r += nt) {
+            const int id = (int)(0xFFFFFFFFu - (uint32_t)(cb[r] & 0xFFFFFFFFu));
+            out[r] = id;
+            span[r] = make_int2(offs[id], sizes[id]);
+            skey[r] = keys[id];
+            atomicOr(&selw[id >> 5], 1u << (id & 31));
+          }
+          done = true;
+        }
+      }
+    }
+  }
+
   // 3. general path: exact k-th key T by bisection, selection in id order, rank-order sort
-  if (!fast && k > 0) {
+  if (!fast && !done && k > 0) {
     uint32_t T = 0u;
     auto block_count = [&](uint32_t c, uint32_t* slot) {  // keys >= c over the workgroup
       int cnt = 0;

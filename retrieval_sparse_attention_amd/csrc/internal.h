@@ -34,6 +34,7 @@ struct DecodeWs {
   float* corr;       // [B*H*scap] rank key of a steady row's cluster if it is not selected, else NaN
   int32_t* counts;   // [B*H*4] rows of the selected clusters, k, steady rows, 0
   float* part;       // [B*H*NP*132] partial softmax states
+  uint32_t* ctop;    // [B*H*(NP-P)*8] per 128-cluster chunk of a (b, h): its 4 largest sortable keys, eligible count
   uint64_t* sortg;   // [B*H*pow2(C_max)] global sort buffer (only when k_max > 4096)
 };
 

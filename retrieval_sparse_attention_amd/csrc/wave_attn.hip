@@ -107,7 +107,7 @@ wave_status hip_device_ok() {
 // ------------------------------------------------------------------ decode sizes
 struct DecodePlan {
   wave::DecodeArgs da;
-  size_t keys, key32, span, skey, selpre, selw, corr, counts, part, sortg, total;
+  size_t keys, key32, span, skey, selpre, selw, corr, counts, part, ctop, sortg, total;
 };
 
 wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t n_local, double frac,
@@ -194,6 +194,7 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
   P->corr = o;   o += align256(4 * (size_t)(BH * da.scap));
   P->counts = o; o += align256(4 * (size_t)(BH * 4));
   P->part = o;   o += align256(4 * (size_t)(BH * da.NP * wave::DEC_PART));
+  P->ctop = o;   o += align256(4 * (size_t)(BH * (da.NP - da.P) * 8));
   P->sortg = o;  o += align256(8 * (size_t)(BH * sort_stride));
   P->total = o;
   return WAVE_OK;
@@ -330,6 +331,7 @@ wave_status wave_attn_decode(const wave_index* index, const void* q, int32_t n_q
   dw.corr = reinterpret_cast<float*>(w + P.corr);
   dw.counts = reinterpret_cast<int32_t*>(w + P.counts);
   dw.part = reinterpret_cast<float*>(w + P.part);
+  dw.ctop = reinterpret_cast<uint32_t*>(w + P.ctop);
   dw.sortg = reinterpret_cast<uint64_t*>(w + P.sortg);
   hipError_t e = wave::launch_decode(sa, P.da, *index, dw, reinterpret_cast<const uint16_t*>(q), out, sel_ids, lse,
                                      reinterpret_cast<hipStream_t>(stream));
