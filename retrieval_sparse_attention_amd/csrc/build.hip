@@ -7,8 +7,8 @@
 // problem ("unit") per (sequence b, kv head g, segment s), enumerated in that
 // order. Launch sequence, all on the caller's stream:
 //   k_init                   seeded choice of K(s) tokens per unit (bf16 centroids, norms)
-//   iters x { k_assign       nearest centroid on bf16 MFMA (32x32x16), fp32
-//             k_assign_fix   binary64 decision where fp32 cannot separate the two best
+//   iters x { k_assign       nearest centroid on bf16 MFMA (32x32x16), fp32, and the
+//                            binary64 decision where fp32 cannot separate the two best
 //             k_sort         stable counting sort of each unit by cluster (LSD radix in LDS
 //                            for segments of at most 16384 tokens)
 //             k_update       ordered fp32 member sums, correctly rounded means, bf16
@@ -118,13 +118,12 @@ constexpr int INIT_THREADS = 1024;
 
 __global__ __launch_bounds__(INIT_THREADS) void k_init(SeqArgs sa, uint64_t seed, const uint16_t* __restrict__ K,
                                                        float* __restrict__ cent, uint16_t* __restrict__ chat,
-                                                       float* __restrict__ norm, int32_t* __restrict__ amb) {
+                                                       float* __restrict__ norm) {
   extern __shared__ uint8_t smem[];
   const Unit U = unit_of(sa, blockIdx.x);
   uint16_t* idx = reinterpret_cast<uint16_t*>(smem);
   int32_t* jsel = reinterpret_cast<int32_t*>(smem + ((2 * (size_t)U.L + 15) & ~(size_t)15));
   const uint64_t st0 = seed + GAMMA * (uint64_t)(U.u + 1);
-  if (blockIdx.x == 0 && threadIdx.x == 0) amb[0] = 0;
   for (int i = threadIdx.x; i < U.L; i += blockDim.x) idx[i] = (uint16_t)i;
   for (int i = threadIdx.x; i < U.Kc; i += blockDim.x) {
     const uint64_t r = sm64_mix(st0 + GAMMA * (uint64_t)(i + 1));
@@ -197,11 +196,12 @@ __global__ __launch_bounds__(INIT_THREADS) void k_init(SeqArgs sa, uint64_t seed
 // the second best are then merged across the two half-waves and the 4 waves.
 // When the gap between best and second best is within 2^-14 (|x| R + R^2),
 // R = max_j |c_j|, plus 2^-100 for denormal flushing, the token goes to the
-// exact binary64 decision (k_assign_fix): each value is off by less than the
-// fp32 accumulation error of a 128-term dot product and a norm (each below
-// 2^-17 of those magnitudes) plus the packing error, i.e. by less than
+// exact binary64 decision at the end of the workgroup: each value is off by less
+// than the fp32 accumulation error of a 128-term dot product and a norm (each
+// below 2^-17 of those magnitudes) plus the packing error, i.e. by less than
 // 2^-16 (|x| R + R^2), so the margin is twice what two values can move and
 // every token not sent there has the exact argmin.
+
 // scheduling of one pipeline step (see tile() in k_assign): nds LDS reads, then 16 x
 // (1 MFMA, 6 vector-ALU operations); nothing moves across the step's end
 #define AS_STEP(nds)                                                              \
@@ -239,7 +239,6 @@ struct AssignLds {
   int32_t fj[32];
   int32_t scan[AS_THREADS];
   float rmx[AS_WAVES];               // per wave: max |c_j|^2
-  int32_t amb_base;
 };
 
 // Workgroups per unit: ceil(L / tpw) with tpw tokens per workgroup (a multiple of
@@ -297,7 +296,7 @@ template <bool MULTI>
 __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, const uint16_t* __restrict__ K,
                                                           const uint16_t* __restrict__ chat,
                                                           const float* __restrict__ norm,
-                                                          int32_t* __restrict__ assign, int32_t* __restrict__ amb) {
+                                                          int32_t* __restrict__ assign) {
   extern __shared__ uint8_t smem[];
   AssignLds& S = *reinterpret_cast<AssignLds*>(smem);
   Unit U;
@@ -584,28 +583,13 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
     total += c;
   }
   if (total == 0) return;
-  if (MULTI) {
-    // to the global list, for k_assign_fix: one atomic
-    if (tid == 0) S.amb_base = atomicAdd(amb, total);
-    __syncthreads();
-    int pos = S.amb_base + before + incl - cnt;
-    for (int i = w0; i < w1; ++i) {
-      uint32_t f = fw[i];
-      while (f != 0u) {
-        const int b = __builtin_ctz(f);
-        f &= f - 1u;
-        amb[1 + 2 * pos] = (int32_t)U.u;
-        amb[2 + 2 * pos] = tb0 + 4 * i + (b >> 3);
-        ++pos;
-      }
-    }
-    return;
-  }
   // Exact decision in the workgroup, 32 tokens at a time: their rows go through the
-  // MFMAs again; every centroid within 2^-14 (|x| R + R^2) + 2^-40 (|x| + R)^2 +
-  // 2^-100 of the best fp32 value (two fp32 errors and two binary64 rounding errors
-  // of the sums) gets D_j = sum_i (x_i - c_j,i)^2 in binary64, dims in order, each
-  // operation rounded; argmin with the lowest id on ties.
+  // MFMAs again, group by group (the last pass's group first, its centroids are still
+  // loaded); every centroid within 2^-14 (|x| R + R^2) + 2^-40 (|x| + R)^2 + 2^-100 of
+  // the best fp32 value so far (two fp32 errors and two binary64 rounding errors of the
+  // sums; the best so far is at most the final best, so no centroid within the window of
+  // the final best is missed) gets D_j = sum_i (x_i - c_j,i)^2 in binary64, dims in
+  // order, each operation rounded; argmin with the lowest id on ties.
   int32_t* fl = reinterpret_cast<int32_t*>(S.tile[1]);  // the list (the buffer is free now)
   {
     int pos = before + incl - cnt;
@@ -635,9 +619,6 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
     __syncthreads();
     bf16x8_t B[8];
     load_b(S.tile[0], 0, B);
-    floatx16 a0[2], a1[2];
-    mma_half(B, 0, a0);
-    mma_half(B, 1, a1);
     // |x|^2 of token col in fp32
     float s2 = 0.f;
 #pragma unroll
@@ -652,50 +633,64 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
       }
     }
     s2 += swap32(s2);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(a0[r][i], a1[r][i]));
-    mx = fmaxf(mx, swap32(mx));
-    if (h == 0) S.red[0][wv][col][0] = mx;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(S.red[0][0][col][0], S.red[0][1][col][0]), fmaxf(S.red[0][2][col][0], S.red[0][3][col][0]));
     const float X = sqrtf(s2);
-    const float thr = M - (0x1p-14f * (X * R + R2) + 0x1p-40f * (X + R) * (X + R) + 0x1p-100f);
-    uint64_t cm = 0ull;  // candidates among this lane's 64 values: bit 32 hb + 16 r + i
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        cm |= (uint64_t)(a0[r][i] >= thr) << (16 * r + i);
-        cm |= (uint64_t)(a1[r][i] >= thr) << (32 + 16 * r + i);
-      }
+    const float win = 0x1p-14f * (X * R + R2) + 0x1p-40f * (X + R) * (X + R) + 0x1p-100f;
     const u32x4* xr = S.tile[0] + col * 16;
+    float M = -INFINITY;  // best fp32 value of token col so far
     double best = INFINITY;
     int bj = 0x7FFFFFFF;
-    while (cm != 0ull) {
-      const int q = __builtin_ctzll(cm);
-      cm &= cm - 1ull;
-      const int i = q & 15;
-      const int j = wv * AS_CPW + 32 * (q >> 4) + 8 * (i >> 2) + 4 * h + (i & 3);
-      if (j >= U.Kc) continue;
-      const u32x4* cj = reinterpret_cast<const u32x4*>(chat + (U.gclu + j) * D);
-      double acc = 0.0;
-      for (int c = 0; c < 16; ++c) {
-        const u32x4 xv = xr[c ^ (col & 15)], cv = cj[c];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t xe = xv[e], ce = cv[e];
-          const double d0 = __dsub_rn((double)bf16_lo(xe), (double)bf16_lo(ce));
-          acc = __dadd_rn(acc, __dmul_rn(d0, d0));
-          const double d1 = __dsub_rn((double)bf16_hi(xe), (double)bf16_hi(ce));
-          acc = __dadd_rn(acc, __dmul_rn(d1, d1));
-        }
+    for (int gi = 0; gi < ngroups; ++gi) {
+      const int grp = ngroups - 1 - gi;
+      if (gi > 0) {
+        load_a(grp);
+        load_nh(grp);
       }
-      if (acc < best || (acc == best && j < bj)) {
-        best = acc;
-        bj = j;
+      floatx16 a0[2], a1[2];
+      mma_half(B, 0, a0);
+      mma_half(B, 1, a1);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(a0[r][i], a1[r][i]));
+      mx = fmaxf(mx, swap32(mx));
+      if (h == 0) S.red[0][wv][col][0] = mx;
+      __syncthreads();
+      M = fmaxf(M, fmaxf(fmaxf(S.red[0][0][col][0], S.red[0][1][col][0]),
+                         fmaxf(S.red[0][2][col][0], S.red[0][3][col][0])));
+      __syncthreads();  // red[0] is read before the next group writes it
+      const float thr = M - win;
+      uint64_t cm = 0ull;  // candidates among this lane's 64 values: bit 32 hb + 16 r + i
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          cm |= (uint64_t)(a0[r][i] >= thr) << (16 * r + i);
+          cm |= (uint64_t)(a1[r][i] >= thr) << (32 + 16 * r + i);
+        }
+      while (cm != 0ull) {
+        const int q = __builtin_ctzll(cm);
+        cm &= cm - 1ull;
+        const int i = q & 15;
+        const int j = grp * AS_GROUP + wv * AS_CPW + 32 * (q >> 4) + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (j >= U.Kc) continue;
+        const u32x4* cj = reinterpret_cast<const u32x4*>(chat + (U.gclu + j) * D);
+        double acc = 0.0;
+        for (int c = 0; c < 16; ++c) {
+          const u32x4 xv = xr[c ^ (col & 15)], cv = cj[c];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t xe = xv[e], ce = cv[e];
+            const double d0 = __dsub_rn((double)bf16_lo(xe), (double)bf16_lo(ce));
+            acc = __dadd_rn(acc, __dmul_rn(d0, d0));
+            const double d1 = __dsub_rn((double)bf16_hi(xe), (double)bf16_hi(ce));
+            acc = __dadd_rn(acc, __dmul_rn(d1, d1));
+          }
+        }
+        if (acc < best || (acc == best && j < bj)) {
+          best = acc;
+          bj = j;
+        }
       }
     }
     // D >= 0: its bits order as its values
@@ -706,104 +701,10 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
     __syncthreads();
     if (tid < nb) assign[U.row0 + tb0 + fl[f0 + tid]] = U.cbase + S.fj[tid];
     __syncthreads();
-  }
-}
-
-// ------------------------------------------------------------------ k_assign_fix
-// Exact decision for the listed tokens: D_j = sum_i (x_i - c_j,i)^2 in binary64,
-// dims in order, each operation rounded (no fused multiply-add), argmin with
-// the lowest id on ties. One wave per token; the waves of the grid take
-// contiguous runs of the list (a run is mostly one unit, whose centroids then
-// come from L2).
-//
-// Screening: every lane scores its centroids j = lane, lane + 64, ... in fp32,
-// f_j = x.c_j - |c_j|^2 / 2 (bf16 pair dot products, fp32 accumulation), and only
-// those within 2^-11 (|x| R + R^2) + 2^-40 (|x| + R)^2 + 2^-100 of the wave's best
-// get the binary64 sum. The pair dot product (v_dot2_f32_bf16) is not correctly
-// rounded: its error is at most 2.25 units in the last place of its largest
-// operand (measured over 2^20 random operands), i.e. at most 2.25 * 2^-23 |x| R
-// per step and 2^-15 (|x| R + R^2) over the 64 steps and the norm. A centroid
-// outside the window has f_j below the best by more than eight such errors plus
-// two binary64 rounding errors of the sums (each under 2^-45 (|x| + R)^2 in f
-// units), so its D_j exceeds the best candidate's and it cannot be the argmin.
-constexpr int FIX_THREADS = 256;
-
-__global__ __launch_bounds__(FIX_THREADS) void k_assign_fix(SeqArgs sa, const uint16_t* __restrict__ K,
-                                                            const uint16_t* __restrict__ chat,
-                                                            const float* __restrict__ norm,
-                                                            int32_t* __restrict__ assign,
-                                                            const int32_t* __restrict__ amb) {
-  __shared__ uint32_t xw[FIX_THREADS / 64][D / 2];  // the wave's token, bf16 pairs
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int count = amb[0];
-  const int nwave = gridDim.x * (FIX_THREADS / 64), gw = blockIdx.x * (FIX_THREADS / 64) + wv;
-  const int it0 = (int)((int64_t)count * gw / nwave), it1 = (int)((int64_t)count * (gw + 1) / nwave);
-  const u32x4* xq = reinterpret_cast<const u32x4*>(xw[wv]);
-  for (int item = it0; item < it1; ++item) {
-    const Unit U = unit_of(sa, amb[1 + 2 * item]);
-    const int64_t row = U.row0 + amb[2 + 2 * item];
-    const uint32_t xv = reinterpret_cast<const uint32_t*>(K + row * D)[lane];
-    xw[wv][lane] = xv;
-    const float x0 = bf16_lo(xv), x1 = bf16_hi(xv);
-    const float X = sqrtf(wave_sum(fmaf(x0, x0, x1 * x1)));
-    float r2 = 0.f;
-    for (int j = lane; j < U.Kc; j += 64) r2 = fmaxf(r2, norm[U.gclu + j]);
-    const float R2 = wave_max(r2), R = sqrtf(R2);
-    // fp32 screening
-    float fb = -INFINITY;
-    float fj[WAVE_MAX_CLUSTERS_PER_SEG / 64];
-#pragma unroll
-    for (int q = 0; q < WAVE_MAX_CLUSTERS_PER_SEG / 64; ++q) {
-      const int j = lane + 64 * q;
-      fj[q] = -INFINITY;
-      if (64 * q < U.Kc && j < U.Kc) {
-        const u32x4* c = reinterpret_cast<const u32x4*>(chat + (U.gclu + j) * D);
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const u32x4 cv = c[e], xx = xq[e];
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const uint32_t xs = xx[w], cs = cv[w];  // named scalars (see xnorm in k_assign)
-            s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xs), __builtin_bit_cast(bf16x2_t, cs), s,
-                                                false);
-          }
-        }
-        fj[q] = s - 0.5f * norm[U.gclu + j];
-        fb = fmaxf(fb, fj[q]);
-      }
+    if (MULTI && f0 + 32 < total) {  // the next batch starts from the last group again
+      load_a(ngroups - 1);
+      load_nh(ngroups - 1);
     }
-    const float thr = wave_max(fb) - (0x1p-11f * (X * R + R2) + 0x1p-40f * (X + R) * (X + R) + 0x1p-100f);
-    // binary64 sums of the candidates, dims in order
-    double best = INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll 1
-    for (int q = 0; q < WAVE_MAX_CLUSTERS_PER_SEG / 64; ++q) {
-      if (64 * q >= U.Kc) break;
-      const int j = lane + 64 * q;
-      if (j < U.Kc && fj[q] >= thr) {
-        const u32x4* c = reinterpret_cast<const u32x4*>(chat + (U.gclu + j) * D);
-        double acc = 0.0;
-        for (int e = 0; e < 16; ++e) {
-          const u32x4 cv = c[e], xx = xq[e];
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const double d0 = __dsub_rn((double)bf16_lo(xx[w]), (double)bf16_lo(cv[w]));
-            acc = __dadd_rn(acc, __dmul_rn(d0, d0));
-            const double d1 = __dsub_rn((double)bf16_hi(xx[w]), (double)bf16_hi(cv[w]));
-            acc = __dadd_rn(acc, __dmul_rn(d1, d1));
-          }
-        }
-        if (acc < best) { best = acc; bi = j; }
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const double ob = __shfl_xor(best, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ob < best || (ob == best && oi < bi)) { best = ob; bi = oi; }
-    }
-    if (lane == 0) assign[row] = U.cbase + bi;
   }
 }
 
@@ -1053,10 +954,9 @@ __global__ __launch_bounds__(RS_THREADS) void k_sort_radix(SeqArgs sa, const int
 template <bool FINAL>
 __global__ __launch_bounds__(256) void k_update(SeqArgs sa, int64_t nclu, const uint16_t* __restrict__ K,
                                                 const uint16_t* __restrict__ V, wave_index ix,
-                                                float* __restrict__ norm, int32_t* __restrict__ amb) {
+                                                float* __restrict__ norm) {
   const int64_t F = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (blockIdx.x == 0 && threadIdx.x == 0) amb[0] = 0;  // the next round's near-tie list
   if (F >= nclu) return;
   const int n = ix.sizes[F];
   if (n == 0) {
@@ -1170,7 +1070,7 @@ hipError_t launch_build(const SeqArgs& sa, const void* Kv, const void* Vv, int32
   uint16_t* chat = reinterpret_cast<uint16_t*>(ix.centroids_bf16);
   prof_begin("k_init", st);
   hipLaunchKernelGGL(k_init, dim3((unsigned)units), dim3(INIT_THREADS), init_lds, st, sa, seed, K, ix.centroids, chat,
-                     ws.norm, ws.amb);
+                     ws.norm);
   prof_end(st);
   const int tpw = assign_tpw(sa, units);
   const int64_t agrid = assign_grid(sa, tpw);
@@ -1178,16 +1078,11 @@ hipError_t launch_build(const SeqArgs& sa, const void* Kv, const void* Vv, int32
     prof_begin("k_assign", st);
     if (sa.K_s > AS_GROUP)
       hipLaunchKernelGGL(k_assign<true>, dim3((unsigned)agrid), dim3(AS_THREADS), sizeof(AssignLds), st, sa, tpw, K,
-                         chat, ws.norm, ix.assign, ws.amb);
+                         chat, ws.norm, ix.assign);
     else
       hipLaunchKernelGGL(k_assign<false>, dim3((unsigned)agrid), dim3(AS_THREADS), sizeof(AssignLds), st, sa, tpw, K,
-                         chat, ws.norm, ix.assign, ws.amb);
+                         chat, ws.norm, ix.assign);
     prof_end(st);
-    if (sa.K_s > AS_GROUP) {  // k_assign decides its own near ties otherwise
-      prof_begin("k_assign_fix", st);
-      hipLaunchKernelGGL(k_assign_fix, dim3(512), dim3(FIX_THREADS), 0, st, sa, K, chat, ws.norm, ix.assign, ws.amb);
-      prof_end(st);
-    }
     if (trace != nullptr) {
       hipError_t e = hipMemcpyAsync(trace + (int64_t)it * rows, ix.assign, sizeof(int32_t) * (size_t)rows,
                                     hipMemcpyDeviceToDevice, st);
@@ -1203,9 +1098,9 @@ hipError_t launch_build(const SeqArgs& sa, const void* Kv, const void* Vv, int32
     prof_end(st);
     prof_begin("k_update", st);
     if (it + 1 < iters)
-      hipLaunchKernelGGL(k_update<false>, dim3(cgrid), dim3(256), 0, st, sa, nclu, K, V, ix, ws.norm, ws.amb);
+      hipLaunchKernelGGL(k_update<false>, dim3(cgrid), dim3(256), 0, st, sa, nclu, K, V, ix, ws.norm);
     else
-      hipLaunchKernelGGL(k_update<true>, dim3(cgrid), dim3(256), 0, st, sa, nclu, K, V, ix, ws.norm, ws.amb);
+      hipLaunchKernelGGL(k_update<true>, dim3(cgrid), dim3(256), 0, st, sa, nclu, K, V, ix, ws.norm);
     prof_end(st);
   }
   return hipGetLastError();

@@ -49,7 +49,6 @@ hipError_t launch_decode(const SeqArgs& sa, const DecodeArgs& da, const wave_ind
 // ------------------------------------------------------------------ build
 struct BuildWs {
   float* norm;        // [clusters] |chat_j|^2 (fp32) of the current round
-  int32_t* amb;       // [1 + rows] count, then rows whose nearest centroid needs the exact decision
   int32_t* rank;      // [rows] scratch of the counting sort
 };
 

@@ -84,14 +84,13 @@ void index_sizes(const wave::SeqArgs& sa, wave_index_sizes* o) {
 }
 
 struct BuildLayout {
-  size_t norm, amb, rank, total;
+  size_t norm, rank, total;
 };
 
 BuildLayout build_layout(const wave_index_sizes& z) {
   BuildLayout L;
   size_t o = 0;
   L.norm = o;  o += align256(sizeof(float) * (size_t)z.clusters);
-  L.amb = o;   o += align256(sizeof(int32_t) * (size_t)(1 + 2 * z.rows));
   L.rank = o;  o += align256(sizeof(int32_t) * (size_t)z.rows);
   L.total = o;
   return L;
@@ -281,7 +280,6 @@ wave_status wave_index_build(const wave_shape* shape, const void* K, const void*
   uint8_t* w = reinterpret_cast<uint8_t*>(ws);
   wave::BuildWs bw;
   bw.norm = reinterpret_cast<float*>(w + L.norm);
-  bw.amb = reinterpret_cast<int32_t*>(w + L.amb);
   bw.rank = reinterpret_cast<int32_t*>(w + L.rank);
   hipError_t e = wave::launch_build(sa, K, V, iters, seed, *out, bw, z.units, assign_trace, z.rows,
                                     reinterpret_cast<hipStream_t>(stream));
