@@ -352,7 +352,13 @@ def main():
     # algorithmic HBM bytes per launch: every byte a kernel must read or write once
     steady = ns + nl
     n_est = sum(-(-c // 128) for c in Cb)          # estimation chunks (workgroups) per kv head
-    P = (int(rows_per_dec / (B * H)) + steady + 255) // 256
+    # row workgroups per (b, h), as the library plans them: 176 rows each at the average
+    # cluster size if the grid then fits 1024 resident workgroups, else 256
+    est_rows = k_max * -(-seg // K_s) + steady
+    P = -(-est_rows // 176)
+    if B * H * P + G * n_est > 1024:
+        P = -(-est_rows // 256)
+    P = max(1, min(4096, P))
     part = 132 * 4                                # one partial softmax state
     rows = G * int(ctx.sum())                     # index rows
     score_bytes = (G * Ctot * (128 * 2 + 4)       # bf16 centroid rows + sizes

@@ -38,6 +38,8 @@ constexpr int TK_SORT = DEC_SORT_LDS;
 constexpr int TK_SELW = 2048;     // selection bitmap words kept in LDS (C <= 65536)
 constexpr int TK_RANK_SMALL = 512;
 constexpr int ATT_THREADS = 256;
+constexpr int ATT_KCAP = 4 * ATT_THREADS;  // selections whose metadata k_attend stages in LDS
+constexpr int ATT_SCAP = 2 * ATT_THREADS;  // steady rows likewise
 constexpr int PART = DEC_PART;    // floats per partial: m, l, 2 pad, acc[128]
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -258,9 +260,13 @@ __device__ void est_role(const SeqArgs& sa, const DecodeArgs& da, const wave_ind
   for (int hh = 0; hh < GS; ++hh) kr[hh] = kb[(int64_t)hh * C + jc];
   float4 vreg[SC / 8];
   {
-    const float4* vsrc = reinterpret_cast<const float4*>(ix.vsum + (clu0 + j0) * D) + dq;
+    // a uniform base and 32-bit lane offsets: one address register per load
+    const char* vsrc = reinterpret_cast<const char*>(ix.vsum + (clu0 + j0) * D);
 #pragma unroll
-    for (int u = 0; u < SC / 8; ++u) vreg[u] = vsrc[(int64_t)min(sub + 8 * u, nc - 1) * (D / 4)];
+    for (int u = 0; u < SC / 8; ++u) {
+      const uint32_t off = (uint32_t)(min(sub + 8 * u, nc - 1) * (D * 4) + dq * 16);
+      vreg[u] = *reinterpret_cast<const float4*>(vsrc + off);
+    }
   }
   const bool live = jj < nc && n0 > 0;
   float sv[GS];
@@ -295,7 +301,7 @@ __device__ void est_role(const SeqArgs& sa, const DecodeArgs& da, const wave_ind
     const float4 v = vreg[u];
 #pragma unroll
     for (int hh = 0; hh < GS; ++hh) {
-      const float wgt = c < nc ? S.kw[hh][c] : 0.f;
+      const float wgt = S.kw[hh][c];  // 0 for c >= nc (not live)
       acc[hh][0] = fmaf(wgt, v.x, acc[hh][0]);
       acc[hh][1] = fmaf(wgt, v.y, acc[hh][1]);
       acc[hh][2] = fmaf(wgt, v.z, acc[hh][2]);
@@ -440,12 +446,21 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
   const int w0 = wv * 64 * NV;
   auto id_of = [&](int v) { return w0 + 64 * v + lane; };
   const int nwords = (C + 31) >> 5;
-  const bool lds_sel = nwords <= TK_SELW;
+  const bool lds_sel = INREG || nwords <= TK_SELW;  // keys in registers: C <= 32768
   int64_t wbase = 0;
   for (int i = 0; i < b; ++i) wbase += (int64_t)da.H * ((sa.C[i] + 31) >> 5);
   uint32_t* selw = lds_sel ? L.selw : ws.selw + wbase + (int64_t)h * nwords;
 
-  // 0. keys and the steady tokens' clusters in flight; LDS init
+  // 0. the steady tokens' clusters (first: they come from HBM) and the keys in flight;
+  // LDS init
+  const Steady sz = steady_of(da, N);
+  // loads at a clamped position, without a branch (a value merged after a divergent
+  // load would make the wave wait for every load in flight); entries i >= nS unused
+  int32_t sjr[2];
+  sjr[0] = ix.assign[row0 + min(steady_pos(sz, min(tid, max(sz.nS - 1, 0))), (int64_t)N - 1)];
+  sjr[1] = 0;
+  if (sz.nS > TK_THREADS)
+    sjr[1] = ix.assign[row0 + min(steady_pos(sz, min(tid + TK_THREADS, sz.nS - 1)), (int64_t)N - 1)];
   constexpr bool PRE = INREG && NVR <= 8;  // sizes and offsets of every key prefetched
   uint32_t ureg[INREG ? NVR : 1];
   int32_t nreg[PRE ? NVR : 1], oreg[PRE ? NVR : 1];
@@ -478,14 +493,11 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
       }
     }
   };
-  const Steady sz = steady_of(da, N);
-  int32_t sjr[2] = {0, 0};
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int i = tid + r * TK_THREADS;
-    if (i < sz.nS) sjr[r] = ix.assign[row0 + steady_pos(sz, i)];
+  if (lds_sel) {
+    for (int i = tid; i < nwords; i += nt) L.selw[i] = 0u;
+  } else {
+    for (int i = tid; i < nwords; i += nt) selw[i] = 0u;
   }
-  for (int i = tid; i < nwords; i += nt) selw[i] = 0u;
   if constexpr (INREG) {
     L.u.c.rank[tid] = 0;
     L.u.c.pre[tid] = 0;
@@ -552,8 +564,11 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
       if (lane < 16) atomicAdd(&L.tcnt[lane], mine);
       lds_barrier();
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (L.tcnt[i] >= k) X = max(X, L.wt[i]);
+      for (int i = 0; i < 16; ++i) {
+        const int tc = L.tcnt[i];  // both read unconditionally: no serial LDS round trips
+        const uint32_t ti = L.wt[i];
+        X = tc >= k ? max(X, ti) : X;
+      }
     }
   }
   if (k < kreq) X = 1u;
@@ -573,7 +588,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
       }
       int base = 0;
       if (lane == 0) base = atomicAdd(&L.misc[0], tot);
-      base = __shfl(base, 0, 64);
+      base = __builtin_amdgcn_readfirstlane(base);
 #pragma unroll
       for (int v = 0; v < NVR; ++v) {
         if (ureg[v] >= X) {
@@ -938,6 +953,61 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
   const int2* span = ws.span + kbase;
   const float* skey = ws.skey + kbase;
   const float* corr = ws.corr + (int64_t)bh * da.scap;
+  // The selection's metadata (member prefix, span, rank key of up to kreq clusters)
+  // and the steady rows' sorted slots and corrections, loaded into LDS in the same
+  // round trip as the counts and q: the searches and windows below then cost LDS
+  // latency instead of one dependent global round trip each.
+  __shared__ int32_t m_pre[ATT_KCAP + 1];
+  __shared__ int2 m_span[ATT_KCAP];
+  __shared__ float m_key[ATT_KCAP];
+  __shared__ int32_t m_sp[ATT_SCAP];
+  __shared__ float m_corr[ATT_SCAP];
+  const int kq = da.kreq[b];  // k <= kq <= C: entries up to kq are this head's
+  const bool lds_meta = kq <= ATT_KCAP && sz.nS <= ATT_SCAP;
+  if (lds_meta) {
+    const int tid = threadIdx.x;
+    int32_t rp[ATT_KCAP / ATT_THREADS + 1];
+    int2 rs[ATT_KCAP / ATT_THREADS];
+    float rk[ATT_KCAP / ATT_THREADS];
+    int32_t rq[ATT_SCAP / ATT_THREADS];
+    float rc[ATT_SCAP / ATT_THREADS];
+#pragma unroll
+    for (int u = 0; u <= ATT_KCAP / ATT_THREADS; ++u) {
+      const int c = tid + u * ATT_THREADS;
+      if (c <= kq) rp[u] = selpre[c];
+      if (u < ATT_KCAP / ATT_THREADS && c < kq) {
+        rs[u] = span[c];
+        rk[u] = skey[c];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < ATT_SCAP / ATT_THREADS; ++u) {
+      const int e = tid + u * ATT_THREADS;
+      if (e < sz.nS) {
+        rq[u] = ix.inv_perm[row0 + steady_pos(sz, e)];
+        rc[u] = corr[e];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u <= ATT_KCAP / ATT_THREADS; ++u) {
+      const int c = tid + u * ATT_THREADS;
+      if (c <= kq) m_pre[c] = rp[u];
+      if (u < ATT_KCAP / ATT_THREADS && c < kq) {
+        m_span[c] = rs[u];
+        m_key[c] = rk[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < ATT_SCAP / ATT_THREADS; ++u) {
+      const int e = tid + u * ATT_THREADS;
+      if (e < sz.nS) {
+        m_sp[e] = rq[u];
+        m_corr[e] = rc[u];
+      }
+    }
+    __syncthreads();
+  }
+  auto pre_of = [&](int c) { return lds_meta ? m_pre[c] : selpre[c]; };
   RowState st;
   st.m = -INFINITY;
   st.l = 0.f;
@@ -951,10 +1021,10 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
   auto load_window = [&](int c0) {
     ci0 = c0;
     const int c = c0 + l16;
-    wpre = c <= k ? selpre[c] : 0x7FFFFFFF;
-    wsx = c < k ? span[c].x : 0;
-    wkey = c < k ? skey[c] * sc : -INFINITY;
-    wend = __shfl(c0 + 16 <= k ? selpre[min(c0 + 16, k)] : 0x7FFFFFFF, gbase, 64);
+    wpre = c <= k ? pre_of(c) : 0x7FFFFFFF;
+    wsx = c < k ? (lds_meta ? m_span[c].x : span[c].x) : 0;
+    wkey = c < k ? (lds_meta ? m_key[c] : skey[c]) * sc : -INFINITY;
+    wend = __shfl(c0 + 16 <= k ? pre_of(min(c0 + 16, k)) : 0x7FFFFFFF, gbase, 64);
   };
   if (s0 < min(s1, M)) {
     // 16-ary search for the last cluster whose first row is <= s0
@@ -962,7 +1032,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
     while (hi - lo > 1) {
       const int step = (hi - lo + 15) / 16;
       const int c = lo + l16 * step;
-      const int v = c < hi ? selpre[c] : 0x7FFFFFFF;
+      const int v = c < hi ? pre_of(c) : 0x7FFFFFFF;
       const uint32_t m = (uint32_t)(__ballot(v <= s0) >> gbase) & 0xFFFFu;
       const int cnt = __popc(m);
       lo = lo + (cnt - 1) * step;
@@ -1013,8 +1083,8 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int e = min(r + u, s1 - 1) - M;
-      p[u] = ix.inv_perm[row0 + steady_pos(sz, e)];
-      cvv[u] = corr[e];
+      p[u] = lds_meta ? m_sp[e] : ix.inv_perm[row0 + steady_pos(sz, e)];
+      cvv[u] = lds_meta ? m_corr[e] : corr[e];
     }
     uint4 kv[U], vv[U];
 #pragma unroll

@@ -41,7 +41,16 @@ struct DecodeWs {
 constexpr int DEC_SCORE_CH = 128;
 constexpr int DEC_PART = 132;
 constexpr int DEC_SORT_LDS = 4096;
+// Rows per gathering workgroup of k_attend. With fewer rows per workgroup each 16-lane
+// group needs fewer dependent load rounds, which pays while the whole grid (row and
+// estimation workgroups) is resident at once: DEC_ROWS_SMALL then, DEC_ROWS_PER_WG when
+// the grid takes several rounds anyway (measured: a 32-head 128K layer 17.6 -> 14.0 us
+// per launch at 176; the 1M and batched layers about 3% slower at 176 than at 256).
+// DEC_ATT_SLOTS: k_attend workgroups resident at once on 256 CUs (4 each: 256 threads
+// and at most 128 registers per lane for up to 4 q heads per kv head).
+constexpr int DEC_ROWS_SMALL = 176;
 constexpr int DEC_ROWS_PER_WG = 256;
+constexpr int DEC_ATT_SLOTS = 1024;
 
 hipError_t launch_decode(const SeqArgs& sa, const DecodeArgs& da, const wave_index& ix, const DecodeWs& ws,
                          const uint16_t* q, float* out, int32_t* sel_ids, float* lse, hipStream_t st);

@@ -161,11 +161,16 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
     nSmax = nS > nSmax ? nS : nSmax;
   }
   da.scap = (int32_t)(nSmax > 0 ? nSmax : 1);
-  // gathered-row workgroups per (b, h): about DEC_ROWS_PER_WG rows each at the
-  // average cluster size
+  // gathered-row workgroups per (b, h) at the average cluster size: DEC_ROWS_SMALL rows
+  // each if the k_attend grid (with one estimation workgroup per 128 clusters and kv
+  // head) is then resident at once, else DEC_ROWS_PER_WG
   const int64_t avg = (ix->seg_len + ix->clusters_per_seg - 1) / ix->clusters_per_seg;
   int64_t est = (int64_t)kmax * avg + nSmax;
-  int64_t Pw = (est + wave::DEC_ROWS_PER_WG - 1) / wave::DEC_ROWS_PER_WG;
+  int64_t nest = 0;
+  for (int b = 0; b < sa.B; ++b) nest += (int64_t)G * ((sa.C[b] + wave::DEC_SCORE_CH - 1) / wave::DEC_SCORE_CH);
+  int64_t Pw = (est + wave::DEC_ROWS_SMALL - 1) / wave::DEC_ROWS_SMALL;
+  if ((int64_t)sa.B * H * Pw + nest > wave::DEC_ATT_SLOTS)
+    Pw = (est + wave::DEC_ROWS_PER_WG - 1) / wave::DEC_ROWS_PER_WG;
   if (Pw < 1) Pw = 1;
   if (Pw > 4096) Pw = 4096;
   da.P = (int32_t)Pw;

@@ -50,7 +50,7 @@ def test_index_plan_sizes():
         assert z.offsets_len == G * sum(c + 1 for c in C)
         assert z.units == G * sum(-(-n // L) for n in ctx)
         assert z.max_clusters == max(C)
-        assert z.build_ws_bytes >= 4 * (z.clusters + 3 * z.rows)
+        assert z.build_ws_bytes >= 4 * (z.clusters + z.rows)  # squared norms, sort ranks
 
 
 @pytest.mark.parametrize("args,status", [
