@@ -102,8 +102,29 @@ __global__ __launch_bounds__(SCORE_THREADS) void k_score(SeqArgs sa, DecodeArgs 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, grp = lane >> 4;
   const int gi = wv * 4 + grp;
 
+  // Loads in the order their values are needed: q, the centroid rows, then the sizes and
+  // the steady tokens' clusters. The load counter drains in issue order, so the rank key
+  // of row it is computed as soon as q and rows 0..it have landed, overlapping the rest.
+  float qf[GS][8];
+#pragma unroll
+  for (int hh = 0; hh < GS; ++hh) {
+    const uint4 v = *reinterpret_cast<const uint4*>(q + ((int64_t)b * da.H + g * GS + hh) * D + l16 * 8);
+    qf[hh][0] = bf16_lo(v.x); qf[hh][1] = bf16_hi(v.x);
+    qf[hh][2] = bf16_lo(v.y); qf[hh][3] = bf16_hi(v.y);
+    qf[hh][4] = bf16_lo(v.z); qf[hh][5] = bf16_hi(v.z);
+    qf[hh][6] = bf16_lo(v.w); qf[hh][7] = bf16_hi(v.w);
+  }
+  // 1. centroid rows: group gi takes clusters gi + 16 it
+  uint4 cv[SC / 16];
+  {
+    const uint16_t* cb = reinterpret_cast<const uint16_t*>(ix.centroids_bf16) + (clu0 + j0) * D + l16 * 8;
+#pragma unroll
+    for (int it = 0; it < SC / 16; ++it)
+      cv[it] = *reinterpret_cast<const uint4*>(cb + (int64_t)min(gi + 16 * it, nc - 1) * D);
+  }
+  const int nsz = ix.sizes[clu0 + j0 + min(tid, nc - 1)];
   // steady tokens whose clusters may lie in this chunk (the first and the last segments):
-  // their clusters, up to 4 per thread in registers, loaded first
+  // their clusters, up to 4 per thread in registers
   const Steady sz = steady_of(da, N);
   bool need = false;
   if (!sz.all && sz.nS > 0) {
@@ -114,33 +135,13 @@ __global__ __launch_bounds__(SCORE_THREADS) void k_score(SeqArgs sa, DecodeArgs 
   }
   constexpr int SQ = 4;
   int32_t sjr[SQ];
+  if (need) {
+    // clamped loads without a per-lane branch; entries i >= nS are masked below
 #pragma unroll
-  for (int r = 0; r < SQ; ++r) {
-    const int i = tid + r * SCORE_THREADS;
-    sjr[r] = (need && i < sz.nS) ? ix.assign[row0 + steady_pos(sz, i)] : -1;
+    for (int r = 0; r < SQ; ++r)
+      sjr[r] = ix.assign[row0 + min(steady_pos(sz, min(tid + r * SCORE_THREADS, sz.nS - 1)), (int64_t)N - 1)];
   }
-  // 1. centroid rows: group gi takes clusters gi + 16 it
-  uint4 cv[SC / 16];
-  {
-    const uint16_t* cb = reinterpret_cast<const uint16_t*>(ix.centroids_bf16) + (clu0 + j0) * D + l16 * 8;
-#pragma unroll
-    for (int it = 0; it < SC / 16; ++it)
-      cv[it] = *reinterpret_cast<const uint4*>(cb + (int64_t)min(gi + 16 * it, nc - 1) * D);
-  }
-  float qf[GS][8];
-#pragma unroll
-  for (int hh = 0; hh < GS; ++hh) {
-    const uint4 v = *reinterpret_cast<const uint4*>(q + ((int64_t)b * da.H + g * GS + hh) * D + l16 * 8);
-    qf[hh][0] = bf16_lo(v.x); qf[hh][1] = bf16_hi(v.x);
-    qf[hh][2] = bf16_lo(v.y); qf[hh][3] = bf16_hi(v.y);
-    qf[hh][4] = bf16_lo(v.z); qf[hh][5] = bf16_hi(v.z);
-    qf[hh][6] = bf16_lo(v.w); qf[hh][7] = bf16_hi(v.w);
-  }
-  if (tid < SC) {
-    S.nsz[tid] = tid < nc ? ix.sizes[clu0 + j0 + tid] : 0;
-    S.scnt[tid] = 0;
-  }
-  lds_barrier();
+  if (tid < SC) S.scnt[tid] = 0;
   // 2. rank keys
 #pragma unroll
   for (int it = 0; it < SC / 16; ++it) {
@@ -157,12 +158,14 @@ __global__ __launch_bounds__(SCORE_THREADS) void k_score(SeqArgs sa, DecodeArgs 
       if (l16 == hh) S.kw[hh][jj] = u + 0.0f;
     }
   }
+  if (tid < SC) S.nsz[tid] = tid < nc ? nsz : 0;
+  lds_barrier();
   // steady members per cluster of the chunk
   if (need) {
 #pragma unroll
     for (int r = 0; r < SQ; ++r) {
       const int j = sjr[r] - j0;
-      if (sjr[r] >= 0 && j >= 0 && j < nc) atomicAdd(&S.scnt[j], 1);
+      if (tid + r * SCORE_THREADS < sz.nS && j >= 0 && j < nc) atomicAdd(&S.scnt[j], 1);
     }
     for (int i = tid + SQ * SCORE_THREADS; i < sz.nS; i += SCORE_THREADS) {
       const int j = ix.assign[row0 + steady_pos(sz, i)] - j0;
@@ -451,16 +454,8 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
   for (int i = 0; i < b; ++i) wbase += (int64_t)da.H * ((sa.C[i] + 31) >> 5);
   uint32_t* selw = lds_sel ? L.selw : ws.selw + wbase + (int64_t)h * nwords;
 
-  // 0. the steady tokens' clusters (first: they come from HBM) and the keys in flight;
-  // LDS init
-  const Steady sz = steady_of(da, N);
-  // loads at a clamped position, without a branch (a value merged after a divergent
-  // load would make the wave wait for every load in flight); entries i >= nS unused
-  int32_t sjr[2];
-  sjr[0] = ix.assign[row0 + min(steady_pos(sz, min(tid, max(sz.nS - 1, 0))), (int64_t)N - 1)];
-  sjr[1] = 0;
-  if (sz.nS > TK_THREADS)
-    sjr[1] = ix.assign[row0 + min(steady_pos(sz, min(tid + TK_THREADS, sz.nS - 1)), (int64_t)N - 1)];
+  // 0. loads in the order their values are needed (the load counter drains in issue
+  // order): the keys, their sizes and offsets, then the steady tokens' clusters; LDS init
   constexpr bool PRE = INREG && NVR <= 8;  // sizes and offsets of every key prefetched
   uint32_t ureg[INREG ? NVR : 1];
   int32_t nreg[PRE ? NVR : 1], oreg[PRE ? NVR : 1];
@@ -480,6 +475,14 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
       oreg[v] = offs[j];
     }
   }
+  const Steady sz = steady_of(da, N);
+  // loads at a clamped position, without a branch (a value merged after a divergent
+  // load would make the wave wait for every load in flight); entries i >= nS unused
+  int32_t sjr[2];
+  sjr[0] = ix.assign[row0 + min(steady_pos(sz, min(tid, max(sz.nS - 1, 0))), (int64_t)N - 1)];
+  sjr[1] = 0;
+  if (sz.nS > TK_THREADS)
+    sjr[1] = ix.assign[row0 + min(steady_pos(sz, min(tid + TK_THREADS, sz.nS - 1)), (int64_t)N - 1)];
   auto chunk_keys = [&](int c0, uint32_t* uc) {  // the lane's CHK keys of chunk c0
     if constexpr (INREG) {
 #pragma unroll
