@@ -85,6 +85,9 @@ def parse():
                    help="print HBM bytes per launch of KERNEL from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv "
                         "runs of the benchmark and of --calibrate-copy, and exit")
     p.add_argument("--command", default="", help="command line recorded in a summary")
+    p.add_argument("--accuracy", action="store_true",
+                   help="only measure the error of the wave attention against dense attention over a grid of "
+                        "budgets (top-k fraction, local window, clusters per segment) on the 128K layer")
     return p.parse_args()
 
 
@@ -185,6 +188,70 @@ SOURCES = ["retrieval_sparse_attention_amd/csrc/decode.hip", "retrieval_sparse_a
            "retrieval_sparse_attention_amd/csrc/wave_attn.hip"]
 
 
+def accuracy(dev):
+    """Error of the wave attention against dense softmax attention over the budgets.
+
+    The 128K layer's generator (drifting Gaussian mixture keys and values, queries near a
+    uniformly drawn key), 16 queries per q head. For each clusters_per_seg (a new index),
+    topk_frac and n_local: relative L2 error |o - o_dense| / |o_dense| per (query, q head),
+    mean and maximum, and the share of tokens read exactly (retrieved plus steady). The
+    dense reference is float32 softmax attention in PyTorch over all N keys.
+    """
+    import numpy as np
+    import torch
+
+    import retrieval_sparse_attention_amd as rsa
+    import synth
+
+    W = WORKLOAD
+    B, H, G, N, seg = 1, W["q_heads"], W["kv_heads"], W["ctx"], W["seg_len"]
+    ns, iters, nq = W["n_sink"], W["kmeans_iters"], 16
+    ctx = np.array([N], np.int64)
+    print("generating inputs", file=sys.stderr, flush=True)
+    K, V, _ = synth.kv(W["seed_data"], B, G, ctx, seg)
+    q, _ = synth.queries(W["seed_query"], nq, B, H, G, ctx, K)
+    Kd = torch.from_numpy(K.view(np.int16)).to(dev).view(torch.bfloat16)
+    Vd = torch.from_numpy(V.view(np.int16)).to(dev).view(torch.bfloat16)
+    qd = torch.from_numpy(q.view(np.int16)).to(dev).view(torch.bfloat16)  # [nq, 1, H, 128]
+    tau = 1.0 / math.sqrt(128.0)
+    Kf = Kd.view(G, N, 128).float()
+    Vf = Vd.view(G, N, 128).float()
+    qf = qd.view(nq, G, H // G, 128).float()
+    ref = torch.empty((nq, G, H // G, 128), dtype=torch.float32, device=dev)
+    for g in range(G):
+        s = torch.matmul(qf[:, g].reshape(-1, 128), Kf[g].t().contiguous()) * tau  # [nq * H/G, N]
+        ref[:, g] = torch.matmul(torch.softmax(s, dim=1), Vf[g]).view(nq, H // G, 128)
+    ref = ref.view(nq, H, 128)
+    rows = []
+    for ks in (256, 512, 1024):
+        idx = rsa.wave_index_build(Kd, Vd, G, [N], seg, ks, iters, W["seed_build"])
+        sizes = idx.arrays["sizes"].cpu().numpy()
+        C = sizes.size // G
+        for nl in (0, 64, 512):
+            for frac in (0.005, 0.01, 0.02, 0.05, 0.1):
+                err, exact = [], []
+                for t in range(nq):
+                    o, ids, _ = rsa.wave_attn_decode(idx, qd[t], ns, nl, frac)
+                    e = (o[0] - ref[t]).norm(dim=1) / ref[t].norm(dim=1)
+                    err.append(e.cpu().numpy())
+                    ih = ids[0].cpu().numpy()
+                    for h in range(H):
+                        sel = ih[h][ih[h] >= 0]
+                        exact.append((sizes[(h * G // H) * C + sel].sum() + ns + nl) / N)
+                err = np.concatenate(err)
+                rows.append({"clusters_per_seg": ks, "n_local": nl, "topk_frac": frac,
+                             "rel_err_mean": round(float(err.mean()), 5), "rel_err_p90": round(float(np.quantile(err, 0.9)), 5),
+                             "rel_err_max": round(float(err.max()), 5),
+                             "exact_token_share": round(float(np.mean(exact)), 4)})
+                print("K_s %4d n_local %3d frac %.3f: rel err mean %.4f max %.4f, exact tokens %.3f" % (
+                    ks, nl, frac, rows[-1]["rel_err_mean"], rows[-1]["rel_err_max"], rows[-1]["exact_token_share"]),
+                    file=sys.stderr, flush=True)
+        del idx
+    print(json.dumps({"metric": "relative L2 error of wave attention vs dense attention",
+                      "workload": W["workload"], "queries_per_head": nq, "q_heads": H, "n_sink": ns,
+                      "data": "synthetic", "reference": "float32 dense softmax attention (PyTorch)", "rows": rows}))
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -215,6 +282,10 @@ def main():
             torch.neg(x, out=y)
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "launches": 3}))
+        return
+
+    if args.accuracy:
+        accuracy(dev)
         return
 
     W = dict(WORKLOADS[args.workload])
