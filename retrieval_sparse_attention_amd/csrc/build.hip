@@ -296,7 +296,8 @@ template <bool MULTI>
 __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, const uint16_t* __restrict__ K,
                                                           const uint16_t* __restrict__ chat,
                                                           const float* __restrict__ norm,
-                                                          int32_t* __restrict__ assign) {
+                                                          int32_t* __restrict__ assign, float* __restrict__ xn2,
+                                                          int first) {
   extern __shared__ uint8_t smem[];
   AssignLds& S = *reinterpret_cast<AssignLds*>(smem);
   Unit U;
@@ -529,9 +530,16 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
     sel_half(accB, 1, b1, b2);
     finish(3, bi, grp, b1, b2);
   };
-  // one pass of the range's tiles against centroid group grp; the decisions in the last
+  // one pass of the range's tiles against centroid group grp; the decisions in the last.
+  // The keys' |x|^2 (for the margins) are the same in every round: the first round's first
+  // pass computes them from the tiles in LDS and stores them; later passes load them with
+  // the tile loads, a tile ahead (the serial LDS reads of the computation cost a tenth of
+  // the launch).
+  auto xrow = [&](int T) { return U.row0 + tb0 + min(T * AS_TT + wv * 32 + col, nrow - 1); };
   auto pass = [&](int grp, bool last) {
-    float xn = 0.f;  // |x|^2 of this wave's tokens of the previous tile
+    const bool fresh = first && grp == 0;
+    float xn = 0.f;                                 // |x|^2 of this wave's tokens of the previous tile
+    float xc = fresh ? 0.f : xn2[xrow(0)];          // and of tile T, loaded with it
     for (int T = 0; T < ntiles; ++T) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of tile T have landed
       __syncthreads();  // tile T is in LDS; red[(T - 1) & 1] is complete
@@ -539,8 +547,15 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
       // into the buffer of tile T - 1, which every wave has finished; after the last tile a
       // harmless reload of it
       issue(min(T + 1, ntiles - 1), bi ^ 1);
+      const float xnext = fresh ? 0.f : xn2[xrow(min(T + 1, ntiles - 1))];
       reduce(T - 1, xn, grp, last);
-      xn = xnorm(bi);
+      if (fresh) {
+        xn = xnorm(bi);
+        if (h == 0 && T * AS_TT + wv * 32 + col < nrow) xn2[xrow(T)] = xn;
+      } else {
+        xn = xc;
+      }
+      xc = xnext;
       tile(bi, grp);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the trailing reload has landed: the buffers are free
@@ -1078,10 +1093,10 @@ hipError_t launch_build(const SeqArgs& sa, const void* Kv, const void* Vv, int32
     prof_begin("k_assign", st);
     if (sa.K_s > AS_GROUP)
       hipLaunchKernelGGL(k_assign<true>, dim3((unsigned)agrid), dim3(AS_THREADS), sizeof(AssignLds), st, sa, tpw, K,
-                         chat, ws.norm, ix.assign);
+                         chat, ws.norm, ix.assign, ws.xn2, it == 0 ? 1 : 0);
     else
       hipLaunchKernelGGL(k_assign<false>, dim3((unsigned)agrid), dim3(AS_THREADS), sizeof(AssignLds), st, sa, tpw, K,
-                         chat, ws.norm, ix.assign);
+                         chat, ws.norm, ix.assign, ws.xn2, it == 0 ? 1 : 0);
     prof_end(st);
     if (trace != nullptr) {
       hipError_t e = hipMemcpyAsync(trace + (int64_t)it * rows, ix.assign, sizeof(int32_t) * (size_t)rows,

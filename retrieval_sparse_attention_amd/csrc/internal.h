@@ -59,6 +59,7 @@ hipError_t launch_decode(const SeqArgs& sa, const DecodeArgs& da, const wave_ind
 struct BuildWs {
   float* norm;        // [clusters] |chat_j|^2 (fp32) of the current round
   int32_t* rank;      // [rows] scratch of the counting sort
+  float* xn2;         // [rows] |x|^2 of every key (written by the first k_assign round)
 };
 
 hipError_t launch_build(const SeqArgs& sa, const void* K, const void* V, int32_t iters, uint64_t seed,

@@ -84,7 +84,7 @@ void index_sizes(const wave::SeqArgs& sa, wave_index_sizes* o) {
 }
 
 struct BuildLayout {
-  size_t norm, rank, total;
+  size_t norm, rank, xn2, total;
 };
 
 BuildLayout build_layout(const wave_index_sizes& z) {
@@ -92,6 +92,7 @@ BuildLayout build_layout(const wave_index_sizes& z) {
   size_t o = 0;
   L.norm = o;  o += align256(sizeof(float) * (size_t)z.clusters);
   L.rank = o;  o += align256(sizeof(int32_t) * (size_t)z.rows);
+  L.xn2 = o;   o += align256(sizeof(float) * (size_t)z.rows);
   L.total = o;
   return L;
 }
@@ -286,6 +287,7 @@ wave_status wave_index_build(const wave_shape* shape, const void* K, const void*
   wave::BuildWs bw;
   bw.norm = reinterpret_cast<float*>(w + L.norm);
   bw.rank = reinterpret_cast<int32_t*>(w + L.rank);
+  bw.xn2 = reinterpret_cast<float*>(w + L.xn2);
   hipError_t e = wave::launch_build(sa, K, V, iters, seed, *out, bw, z.units, assign_trace, z.rows,
                                     reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(WAVE_ERR_HIP, "build launch failed: %s", hipGetErrorString(e));
