@@ -61,6 +61,9 @@ def _load():
         lib.ref_select.argtypes = [P, P, i32, i32, P]
         lib.ref_decode.argtypes = [i32, i32, i32, P, i32, i32, P, P, P, P, P, P, i32, i32, f64, i32, P, P, P, P]
         lib.ref_decode.restype = ctypes.c_int
+        lib.ref_decode_topk.argtypes = [i32, i32, i32, P, i32, i32, P, P, P, P, P, i32, i32, f64, i32, P, P, P, P]
+        lib.ref_decode_topk.restype = ctypes.c_int
+        lib.ref_block_assign.argtypes = [i32, i32, P, i32, i32, P]
         lib.ref_full_attention.argtypes = [i32, i32, i32, P, P, P, P, P, P]
         _lib = lib
     return _lib
@@ -187,6 +190,21 @@ def index_from_assign(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, seed, as
     return idx
 
 
+def block_assign(n_kv_heads, ctx, seg_len, clusters_per_seg):
+    """Block ids of every row for the block baseline: token i of a segment of L tokens with K(s) blocks is in
+    block floor(i K(s) / L) (Vortex technical summary, section A)."""
+    ctx = _c(ctx, np.int64)
+    a = np.empty(int(n_kv_heads * ctx.sum()), np.int32)
+    _load().ref_block_assign(len(ctx), n_kv_heads, _p(ctx), seg_len, clusters_per_seg, _p(a))
+    return a
+
+
+def build_blocks(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg):
+    """Index of the block baseline: the layout, means and value sums over the block clustering."""
+    return index_from_assign(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, 0,
+                             block_assign(n_kv_heads, ctx, seg_len, clusters_per_seg))
+
+
 # ---------------------------------------------------------------- decode
 def rank_key(q, c):
     return _load().ref_rank_key(_p(_c(q, np.uint16)), _p(_c(c, np.uint16)))
@@ -218,6 +236,24 @@ def decode(index, K, V, q, n_sink, n_local, topk_frac, k_max=None):
                             n_sink, n_local, topk_frac, k_max, _p(out), _p(lse), _p(ids), _p(kc))
     if rc != 0:
         raise ValueError("ref_decode rejected its arguments (rc=%d)" % rc)
+    return out, lse, ids[:, :, :k_max], kc
+
+
+def decode_topk(index, K, V, q, n_sink, n_local, topk_frac, k_max=None):
+    """Top-k retrieval without the estimation zone (steady zone + the selected clusters' tokens, exact)."""
+    q = _c(q, np.uint16)
+    B, H = q.shape[0], q.shape[1]
+    if k_max is None:
+        k_max = decode_k_max(index.C, topk_frac)
+    out = np.empty((B, H, D), np.float64)
+    lse = np.empty((B, H), np.float64)
+    ids = np.empty((B, H, max(k_max, 1)), np.int32)
+    kc = np.empty((B, H), np.int32)
+    rc = _load().ref_decode_topk(B, H, index.G, _p(index.ctx), index.seg_len, index.K_s, _p(_c(K, np.uint16)),
+                                 _p(_c(V, np.uint16)), _p(index.assign), _p(index.centroids_bf16), _p(q),
+                                 n_sink, n_local, topk_frac, k_max, _p(out), _p(lse), _p(ids), _p(kc))
+    if rc != 0:
+        raise ValueError("ref_decode_topk rejected its arguments (rc=%d)" % rc)
     return out, lse, ids[:, :, :k_max], kc
 
 

@@ -416,6 +416,28 @@ int ref_index_from_assign(int32_t B, int32_t G, const int64_t* ctx, const uint16
                     offsets, sizes, centroids, centroids_bf16, vsum, NULL);
 }
 
+/*
+ * Block clustering of the block top-k baseline (Vortex technical summary,
+ * section A, vFlow: a query-independent phase builds per-block summaries such as
+ * block centroids, a query-dependent phase scores the blocks, keeps the top-k and
+ * attends to them; its results name block top-k as a workload). Reading: the
+ * blocks are contiguous runs of tokens inside the same segments and id space as
+ * the clusters, local token i of a segment of L tokens with K(s) clusters in block
+ * floor(i * K(s) / L) (balanced; L_s / K_s tokens each when K_s divides L_s).
+ * Writes the block-level ids (segment base + local block) of every row.
+ */
+void ref_block_assign(int32_t B, int32_t G, const int64_t* ctx, int32_t seg_len, int32_t K_s, int32_t* assign) {
+  int64_t row = 0;
+  for (int32_t b = 0; b < B; ++b)
+    for (int32_t g = 0; g < G; ++g)
+      for (int64_t t = 0; t < ctx[b]; ++t) {
+        int64_t s = t / seg_len, i = t - s * seg_len;
+        int64_t L = ctx[b] - s * seg_len < seg_len ? ctx[b] - s * seg_len : seg_len;
+        int64_t Kc = ref_segment_clusters(L, seg_len, K_s);
+        assign[row++] = (int32_t)(s * K_s + i * Kc / L);
+      }
+}
+
 /* ------------------------------------------------------------------ */
 /*
  * Rank key of a cluster for retrieval [bit-defined]. The retrieval zone ranks
@@ -489,10 +511,10 @@ void ref_select(const float* keys, const int32_t* cand, int32_t n, int32_t k, in
  * index, q [B][H][128]. Outputs: out [B][H][128], lse [B][H], ids [B][H][k_max]
  * (rank order, -1 padded). Returns k_b per (b, h) in kcount (nullable).
  */
-int ref_decode(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int32_t seg_len, int32_t K_s, const uint16_t* K,
-               const uint16_t* V, const int32_t* assign, const uint16_t* chat, const float* vsum, const uint16_t* q,
-               int32_t n_sink, int32_t n_local, double topk_frac, int32_t k_max, double* out, double* lse,
-               int32_t* ids, int32_t* kcount) {
+static int decode_impl(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int32_t seg_len, int32_t K_s,
+                       const uint16_t* K, const uint16_t* V, const int32_t* assign, const uint16_t* chat,
+                       const float* vsum, const uint16_t* q, int32_t n_sink, int32_t n_local, double topk_frac,
+                       int32_t k_max, double* out, double* lse, int32_t* ids, int32_t* kcount, int estimate) {
   if (B < 1 || G < 1 || H < 1 || H % G != 0 || n_sink < 0 || n_local < 0 || !(topk_frac >= 0.0 && topk_frac <= 1.0))
     return -1;
   seq_base* sb = make_bases(B, G, ctx, seg_len, K_s);
@@ -560,7 +582,7 @@ int ref_decode(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int32_t seg_
     }
     double* sj = (double*)malloc(sizeof(double) * (size_t)(C > 0 ? C : 1));
     for (int64_t j = 0; j < C; ++j) {
-      if (np[j] > 0 && !inR[j]) {
+      if (estimate && np[j] > 0 && !inR[j]) {
         double s = 0.0;
         for (int i = 0; i < D; ++i) s += qd[i] * (double)ref_bf16_to_f32(chat[(clu0 + j) * D + i]);
         sj[j] = tau * s;
@@ -578,7 +600,7 @@ int ref_decode(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int32_t seg_
       }
     }
     for (int64_t j = 0; j < C; ++j) {
-      if (np[j] > 0 && !inR[j]) {
+      if (estimate && np[j] > 0 && !inR[j]) {
         double w = exp(sj[j] - m);
         den += w * (double)np[j];
         for (int i = 0; i < D; ++i) num[i] += w * vs[j * D + i];
@@ -597,6 +619,34 @@ int ref_decode(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int32_t seg_
     free(np);
   }
   free(sb);
+  return rc;
+}
+
+int ref_decode(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int32_t seg_len, int32_t K_s, const uint16_t* K,
+               const uint16_t* V, const int32_t* assign, const uint16_t* chat, const float* vsum, const uint16_t* q,
+               int32_t n_sink, int32_t n_local, double topk_frac, int32_t k_max, double* out, double* lse,
+               int32_t* ids, int32_t* kcount) {
+  return decode_impl(B, H, G, ctx, seg_len, K_s, K, V, assign, chat, vsum, q, n_sink, n_local, topk_frac, k_max, out,
+                     lse, ids, kcount, 1);
+}
+
+/*
+ * Top-k retrieval without the estimation zone (the block top-k baseline of the
+ * Vortex technical summary, section A: score the blocks, keep the top-k, attend
+ * to them): the same steady zone, E, k and R as ref_decode, and
+ * o = softmax over the steady tokens and the non-steady members of R only.
+ */
+int ref_decode_topk(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int32_t seg_len, int32_t K_s,
+                    const uint16_t* K, const uint16_t* V, const int32_t* assign, const uint16_t* chat,
+                    const uint16_t* q, int32_t n_sink, int32_t n_local, double topk_frac, int32_t k_max, double* out,
+                    double* lse, int32_t* ids, int32_t* kcount) {
+  int64_t clusters = 0;
+  for (int32_t b = 0; b < B; ++b) clusters += (int64_t)G * ref_num_clusters(ctx[b], seg_len, K_s);
+  /* the value sums are not read without the estimation zone; a zero array stands in */
+  float* vz = (float*)calloc((size_t)(clusters > 0 ? clusters : 1) * D, sizeof(float));
+  int rc = decode_impl(B, H, G, ctx, seg_len, K_s, K, V, assign, chat, vz, q, n_sink, n_local, topk_frac, k_max, out,
+                       lse, ids, kcount, 0);
+  free(vz);
   return rc;
 }
 

@@ -485,3 +485,100 @@ def test_decode_selection_brute_force():
             assert ids[b, h, :k].tolist() == want
         row += idx.G * N
         clu += idx.G * C
+
+
+# ------------------------------------------------------------- block baseline
+def test_block_assign_closed_form():
+    # token i of a segment of L tokens with K(s) blocks is in block floor(i K(s) / L):
+    # contiguous, ascending, block j holds ceil((j+1) L / K) - ceil(j L / K) tokens
+    G, seg, K_s = 2, 1000, 64
+    ctx = np.array([2500, 999, 1], np.int64)
+    a = oracle.block_assign(G, ctx, seg, K_s)
+    row = 0
+    for N in ctx:
+        for g in range(G):
+            blk = a[row: row + N]
+            for s0 in range(0, N, seg):
+                L = min(seg, N - s0)
+                Kc = oracle.segment_clusters(L, seg, K_s)
+                loc = blk[s0: s0 + L] - (s0 // seg) * K_s
+                assert np.all(np.diff(loc) >= 0) and loc[0] == 0 and loc[-1] == Kc - 1
+                cnt = np.bincount(loc, minlength=Kc)
+                want = [-(-(j + 1) * L // Kc) - -(-j * L // Kc) for j in range(Kc)]
+                assert cnt.tolist() == want
+            row += N
+
+
+def test_block_index_is_identity_layout_with_block_means():
+    ctx = np.array([1500, 700], np.int64)
+    G, seg, K_s = 2, 512, 32
+    K, V, _ = synth.kv(41, 2, G, ctx, seg)
+    idx = oracle.build_blocks(K, V, G, ctx, seg, K_s)
+    assert np.array_equal(idx.perm, np.concatenate([np.arange(N) for N in ctx for _ in range(G)]))
+    assert np.array_equal(idx.k_sorted, K) and np.array_equal(idx.v_sorted, V)
+    # centroid = ordered fp32 mean of the block's keys (numpy float32 cumulative sum in order)
+    a = oracle.block_assign(G, ctx, seg, K_s)
+    row = clu = 0
+    for N in ctx:
+        C = oracle.num_clusters(int(N), seg, K_s)
+        for g in range(G):
+            for j in (0, 7, C - 1):
+                m = np.nonzero(a[row: row + N] == j)[0]
+                x = oracle.bf16_to_f32(K[row + m]).astype(np.float32)
+                acc = np.zeros(D, np.float32)
+                for r in x:
+                    acc = (acc + r).astype(np.float32)
+                assert np.array_equal(idx.centroids[clu + j], (acc / np.float32(len(m))).astype(np.float32))
+            row += N
+            clu += C
+
+
+def _masked_attention(K, V, q, G, ctx, keep):
+    """Softmax attention of every (b, h) over the rows keep[b][h] (boolean per token), float64."""
+    B, H = q.shape[:2]
+    out = np.zeros((B, H, D))
+    row = 0
+    for b, N in enumerate(ctx):
+        for h in range(H):
+            g = h * G // H
+            sl = slice(row + g * N, row + (g + 1) * N)
+            Kf = oracle.bf16_to_f32(K[sl]).astype(np.float64)[keep[b][h]]
+            Vf = oracle.bf16_to_f32(V[sl]).astype(np.float64)[keep[b][h]]
+            w = scipy.special.softmax(Kf @ oracle.bf16_to_f32(q[b, h]).astype(np.float64) / math.sqrt(D))
+            out[b, h] = w @ Vf
+        row += G * N
+    return out
+
+
+@pytest.mark.parametrize("blocks", [False, True])
+def test_decode_topk_only_is_masked_attention(blocks):
+    # without the estimation zone the output is softmax attention restricted to the steady
+    # tokens and the members of the selected clusters (brute force with scipy's softmax)
+    K, V, ctx, idx, q = _setup_decode()
+    if blocks:
+        idx = oracle.build_blocks(K, V, idx.G, ctx, idx.seg_len, idx.K_s)
+    ns, nl, frac = 4, 64, 0.1
+    o, lse, ids, kc = oracle.decode_topk(idx, K, V, q, ns, nl, frac)
+    _, _, ids_w, kc_w = oracle.decode(idx, K, V, q, ns, nl, frac)
+    assert np.array_equal(ids, ids_w) and np.array_equal(kc, kc_w)  # same selection as the wave decode
+    keep, row = [], 0
+    for b, N in enumerate(ctx):
+        keep.append([])
+        for h in range(q.shape[1]):
+            g = h * idx.G // q.shape[1]
+            a = idx.assign[row + g * N: row + (g + 1) * N]
+            t = np.arange(N)
+            keep[b].append(((t < ns) | (t >= N - nl)) | np.isin(a, ids[b, h, :kc[b, h]]))
+        row += idx.G * N
+    np.testing.assert_allclose(o, _masked_attention(K, V, q, idx.G, ctx, keep), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("n_sink,n_local", [(0, 0), (4, 64)])
+def test_decode_topk_only_all_selected_equals_full_attention(n_sink, n_local):
+    K, V, ctx, idx, q = _setup_decode()
+    idxb = oracle.build_blocks(K, V, idx.G, ctx, idx.seg_len, idx.K_s)
+    of, lf = oracle.full_attention(K, V, q, idx.G, ctx)
+    for ix in (idx, idxb):
+        o, lse, _, _ = oracle.decode_topk(ix, K, V, q, n_sink, n_local, 1.0)
+        np.testing.assert_allclose(o, of, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse, lf, rtol=1e-12, atol=1e-12)
