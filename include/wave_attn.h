@@ -169,6 +169,35 @@ wave_status wave_attn_decode(const wave_index* index, const void* q, int32_t n_q
                              int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse, void* ws,
                              size_t ws_bytes, wave_stream_t stream);
 
+/*
+ * wave_index_build_blocks -- the index of the block top-k baseline (Vortex
+ * technical summary, section A, vFlow: a query-independent phase summarises
+ * fixed blocks of the KV cache by their centroids; the query-dependent phase
+ * scores the blocks, keeps the top-k and attends to them). Clusters are
+ * contiguous blocks instead of k-means clusters: token i of a segment of L
+ * tokens with K(s) clusters (as in wave_index_plan) belongs to block
+ * floor(i*K(s)/L), so full segments have blocks of L_s/K_s tokens when K_s
+ * divides L_s. The arrays are those wave_index_build fills, for that
+ * assignment: identity order (perm, inv_perm), sizes, offsets, member means
+ * (centroids), their bf16 rounding and the value sums. Arguments, ownership
+ * and errors as wave_index_build (no iters, seed or trace).
+ */
+wave_status wave_index_build_blocks(const wave_shape* shape, const void* K, const void* V, int32_t seg_len,
+                                    int32_t clusters_per_seg, wave_index* out, void* ws, size_t ws_bytes,
+                                    wave_stream_t stream);
+
+/*
+ * wave_attn_decode_topk -- top-k retrieval without the estimation zone (the
+ * block top-k baseline's decode; Vortex technical summary, section A): S, E,
+ * k_b and R exactly as wave_attn_decode (same ids), and out / lse = exact
+ * softmax attention over the steady tokens and the non-steady members of R
+ * only. Arguments, workspace (wave_attn_decode_plan) and errors as
+ * wave_attn_decode (index->vsum is validated like the other arrays but not read).
+ */
+wave_status wave_attn_decode_topk(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
+                                  int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse,
+                                  void* ws, size_t ws_bytes, wave_stream_t stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* wave_last_error(void);
 

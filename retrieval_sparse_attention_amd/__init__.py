@@ -66,12 +66,15 @@ def lib():
         L.wave_attn_decode_plan.argtypes = [ctypes.POINTER(_Index), i32, i32, i32, ctypes.c_double,
                                             ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_size_t)]
         L.wave_attn_decode.argtypes = [ctypes.POINTER(_Index), P, i32, i32, i32, ctypes.c_double, P, P, P, P, sz, P]
+        L.wave_attn_decode_topk.argtypes = L.wave_attn_decode.argtypes
+        L.wave_index_build_blocks.argtypes = [ctypes.POINTER(_Shape), P, P, i32, i32, ctypes.POINTER(_Index), P, sz,
+                                              P]
         L.wave_last_error.restype = ctypes.c_char_p
         L.wave_profiler_enable.argtypes = [i32]
         L.wave_profiler_read.argtypes = [ctypes.c_char_p, P, P, i32]
         L.wave_profiler_read.restype = i32
         for f in ("wave_index_plan", "wave_index_build", "wave_attn_decode_plan", "wave_attn_decode",
-                  "wave_profiler_enable"):
+                  "wave_profiler_enable", "wave_index_build_blocks", "wave_attn_decode_topk"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -167,6 +170,21 @@ def wave_index_build(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, iters, se
     return (index, tr) if assign_trace else index
 
 
+def wave_index_build_blocks(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, stream=None, index=None, ws=None):
+    """Index of the block top-k baseline: contiguous blocks in place of the k-means clusters."""
+    if index is None:
+        index, z = WaveIndex.allocate(n_kv_heads, ctx, seg_len, clusters_per_seg, device=K.device)
+    else:
+        z = wave_index_plan(n_kv_heads, ctx, seg_len, clusters_per_seg)
+    if ws is None:
+        ws = torch.empty(max(int(z["build_ws_bytes"]), 16), dtype=torch.uint8, device=K.device)
+    sh = _Shape()
+    ctypes.pointer(sh)[0] = index.c.shape
+    _check(lib().wave_index_build_blocks(ctypes.byref(sh), _ptr(K), _ptr(V), int(seg_len), int(clusters_per_seg),
+                                         ctypes.byref(index.c), _ptr(ws), ws.numel(), _stream(stream)))
+    return index
+
+
 def wave_attn_decode_plan(index, n_q_heads, n_sink, n_local, topk_frac):
     """(k_max, workspace bytes) of a decode call."""
     k = ctypes.c_int32()
@@ -177,7 +195,7 @@ def wave_attn_decode_plan(index, n_q_heads, n_sink, n_local, topk_frac):
 
 
 def wave_attn_decode(index, q, n_sink, n_local, topk_frac, ws=None, out=None, sel_ids=None, lse=None,
-                     stream=None):
+                     stream=None, estimate=True):
     """One decode query per (sequence, q head): q bf16 [B, H, 128] on the device.
 
     Returns (out fp32 [B, H, 128], sel_ids int32 [B, H, k_max], lse fp32 [B, H]).
@@ -193,9 +211,16 @@ def wave_attn_decode(index, q, n_sink, n_local, topk_frac, ws=None, out=None, se
         sel_ids = torch.empty((B, H, max(k_max, 1)), dtype=torch.int32, device=dev)
     if lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-    _check(lib().wave_attn_decode(ctypes.byref(index.c), _ptr(q), H, int(n_sink), int(n_local), float(topk_frac),
-                                  _ptr(out), _ptr(sel_ids), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+    fn = lib().wave_attn_decode if estimate else lib().wave_attn_decode_topk
+    _check(fn(ctypes.byref(index.c), _ptr(q), H, int(n_sink), int(n_local), float(topk_frac), _ptr(out), _ptr(sel_ids),
+              _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
     return out, sel_ids[:, :, :k_max], lse
+
+
+def wave_attn_decode_topk(index, q, n_sink, n_local, topk_frac, ws=None, out=None, sel_ids=None, lse=None,
+                          stream=None):
+    """Top-k retrieval without the estimation zone (the block baseline's decode); as wave_attn_decode."""
+    return wave_attn_decode(index, q, n_sink, n_local, topk_frac, ws, out, sel_ids, lse, stream, estimate=False)
 
 
 def wave_profiler_enable(on=True):

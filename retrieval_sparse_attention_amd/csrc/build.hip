@@ -1032,6 +1032,17 @@ __global__ __launch_bounds__(256) void k_update(SeqArgs sa, int64_t nclu, const 
   if (FINAL) *reinterpret_cast<float2*>(ix.vsum + F * D + 2 * lane) = make_float2(w0, w1);
 }
 
+// ------------------------------------------------------------------ k_block_assign
+// Block clustering of the block top-k baseline (Vortex technical summary, section A:
+// per-block summaries built once, blocks scored and the top-k attended per query):
+// token i of a unit of L tokens and Kc clusters goes to block floor(i Kc / L), the
+// contiguous balanced blocks in the clusters' id space. One workgroup per unit.
+__global__ __launch_bounds__(1024) void k_block_assign(SeqArgs sa, int32_t* __restrict__ assign) {
+  const Unit U = unit_of(sa, blockIdx.x);
+  for (int i = threadIdx.x; i < U.L; i += blockDim.x)
+    assign[U.row0 + i] = U.cbase + (int32_t)((int64_t)i * U.Kc / U.L);
+}
+
 // ------------------------------------------------------------------ host side
 // Tokens per k_assign workgroup: enough workgroups per segment that the units fill
 // the 256 compute units once (one workgroup per CU: its LDS and registers take the CU),
@@ -1118,6 +1129,43 @@ hipError_t launch_build(const SeqArgs& sa, const void* Kv, const void* Vv, int32
       hipLaunchKernelGGL(k_update<true>, dim3(cgrid), dim3(256), 0, st, sa, nclu, K, V, ix, ws.norm);
     prof_end(st);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_build_blocks(const SeqArgs& sa, const void* Kv, const void* Vv, const wave_index& ix,
+                               const BuildWs& ws, int64_t units, hipStream_t st) {
+  static bool attrs = false;
+  if (!attrs) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sort), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              16 * WAVE_MAX_CLUSTERS_PER_SEG * 4);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sort_radix),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 2 * RS_MAXL * 4);
+    attrs = true;
+  }
+  const uint16_t* K = reinterpret_cast<const uint16_t*>(Kv);
+  const uint16_t* V = reinterpret_cast<const uint16_t*>(Vv);
+  int64_t nclu = 0;
+  for (int b = 0; b < sa.B; ++b) nclu += (int64_t)sa.G * sa.C[b];
+  const size_t sort_lds = 16 * (size_t)sa.K_s * 4;
+  const size_t radix_tiles = ((size_t)sa.seg_len + RS_THREADS - 1) / RS_THREADS;
+  const size_t radix_lds = 2 * radix_tiles * RS_THREADS * 4;
+  const unsigned cgrid = (unsigned)((nclu + 3) / 4);
+  prof_begin("k_block_assign", st);
+  hipLaunchKernelGGL(k_block_assign, dim3((unsigned)units), dim3(1024), 0, st, sa, ix.assign);
+  prof_end(st);
+  // the layout pass of the k-means build over the block labels: counts, offsets, the
+  // (identity) order, member means, bf16 centroids, value sums
+  prof_begin("k_sort", st);
+  if (sa.seg_len <= RS_MAXL)
+    hipLaunchKernelGGL(k_sort_radix, dim3((unsigned)units), dim3(RS_THREADS), radix_lds, st, sa, ix.assign, ix.sizes,
+                       ix.offsets, ix.perm);
+  else
+    hipLaunchKernelGGL(k_sort, dim3((unsigned)units), dim3(SORT_THREADS), sort_lds, st, sa, ix.assign, ws.rank,
+                       ix.sizes, ix.offsets, ix.perm);
+  prof_end(st);
+  prof_begin("k_update", st);
+  hipLaunchKernelGGL(k_update<true>, dim3(cgrid), dim3(256), 0, st, sa, nclu, K, V, ix, ws.norm);
+  prof_end(st);
   return hipGetLastError();
 }
 

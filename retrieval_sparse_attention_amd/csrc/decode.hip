@@ -1075,7 +1075,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
       const bool valid = r + u < r1;
       const bool steady = t[u] < sz.a_end || t[u] >= sz.c_beg;  // counted exactly with the steady rows
       sv[u] = (valid && !steady) ? x : -INFINITY;
-      cs[u] = valid ? ck[u] : -INFINITY;
+      cs[u] = (valid && da.est) ? ck[u] : -INFINITY;  // no centroid term to take back without estimation
     }
     softmax_rows<U>(st, sv, cs, vv);
   }
@@ -1101,7 +1101,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
       const float x = dot8(qf, kv[u]);
       const bool valid = r + u < s1;
       sv[u] = valid ? x : -INFINITY;
-      cs[u] = (valid && cvv[u] == cvv[u]) ? cvv[u] * sc : -INFINITY;
+      cs[u] = (valid && da.est && cvv[u] == cvv[u]) ? cvv[u] * sc : -INFINITY;
     }
     softmax_rows<U>(st, sv, cs, vv);
   }
@@ -1149,7 +1149,7 @@ __global__ __launch_bounds__(256) void k_merge(SeqArgs sa, DecodeArgs da, Decode
   __shared__ float mx[4];
   const int bh = blockIdx.x;
   const int b = bh / da.H;
-  const int npart = da.P + (sa.C[b] + SC - 1) / SC;
+  const int npart = da.P + (da.est ? (sa.C[b] + SC - 1) / SC : 0);
   const float* pp = ws.part + (int64_t)bh * da.NP * PART;
   const int tid = threadIdx.x, dq = tid & 31, sub = tid >> 5;
   float M = -INFINITY;
@@ -1210,7 +1210,8 @@ static void launch_gs(const SeqArgs& sa, const DecodeArgs& da, const wave_index&
   }
   prof_end(st);
   prof_begin("k_attend", st);
-  hipLaunchKernelGGL(k_attend<GS>, dim3(sa.B * da.H * da.P + nest), dim3(ATT_THREADS), 0, st, sa, da, ix, ws, q);
+  hipLaunchKernelGGL(k_attend<GS>, dim3(sa.B * da.H * da.P + (da.est ? nest : 0)), dim3(ATT_THREADS), 0, st, sa, da,
+                     ix, ws, q);
   prof_end(st);
   prof_begin("k_merge", st);
   hipLaunchKernelGGL(k_merge, dim3(sa.B * da.H), dim3(256), 0, st, sa, da, ws, out, lse);

@@ -21,6 +21,7 @@ struct DecodeArgs {
   float tau;              // 1/sqrt(128)
   int32_t sort_stride;    // per-(b, h) entries of the global sort buffer
   int32_t NVg;            // keys per lane when NV == 0 (a multiple of 16)
+  int32_t est;            // 1: the estimation zone (wave attention); 0: top-k retrieval only
   int32_t kreq[MAXB];     // min(ceil(topk_frac * C_b), C_b), binary64 on the host
 };
 
@@ -65,6 +66,8 @@ struct BuildWs {
 hipError_t launch_build(const SeqArgs& sa, const void* K, const void* V, int32_t iters, uint64_t seed,
                         const wave_index& ix, const BuildWs& ws, int64_t units, int32_t* trace, int64_t rows,
                         hipStream_t st);
+hipError_t launch_build_blocks(const SeqArgs& sa, const void* K, const void* V, const wave_index& ix,
+                               const BuildWs& ws, int64_t units, hipStream_t st);
 
 // ------------------------------------------------------------------ kernel timing hook
 void prof_begin(const char* name, hipStream_t st);

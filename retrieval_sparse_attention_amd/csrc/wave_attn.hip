@@ -130,6 +130,7 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
   da.n_sink = n_sink;
   da.n_local = n_local;
   da.tau = (float)(1.0 / sqrt((double)WAVE_HEAD_DIM));
+  da.est = 1;
   int kmax = 0, Cmax = 0, nEmax = 0;
 
   int64_t sumC = 0, sumW = 0;
@@ -294,6 +295,44 @@ wave_status wave_index_build(const wave_shape* shape, const void* K, const void*
   return ok();
 }
 
+wave_status wave_index_build_blocks(const wave_shape* shape, const void* K, const void* V, int32_t seg_len,
+                                    int32_t clusters_per_seg, wave_index* out, void* ws, size_t ws_bytes,
+                                    wave_stream_t stream) {
+  wave_status st = check_shape(shape);
+  if (st != WAVE_OK) return st;
+  st = check_seg(seg_len, clusters_per_seg);
+  if (st != WAVE_OK) return st;
+  if (K == nullptr || V == nullptr || out == nullptr || ws == nullptr)
+    return fail(WAVE_ERR_ARG, "K, V, out and ws must be non-NULL");
+  const void* ptrs[] = {out->k_sorted, out->v_sorted, out->perm, out->inv_perm, out->assign, out->offsets,
+                        out->sizes, out->centroids, out->centroids_bf16, out->vsum};
+  for (const void* p : ptrs)
+    if (p == nullptr) return fail(WAVE_ERR_ARG, "an index array pointer is NULL");
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(WAVE_ERR_ALIGN, "index arrays must be 16-byte aligned");
+  if (!aligned16(K) || !aligned16(V) || !aligned16(ws))
+    return fail(WAVE_ERR_ALIGN, "K, V and ws must be 16-byte aligned");
+  wave_index_sizes z;
+  const wave::SeqArgs sa = make_seq(shape, seg_len, clusters_per_seg);
+  index_sizes(sa, &z);
+  const BuildLayout L = build_layout(z);
+  if (ws_bytes < L.total)
+    return fail(WAVE_ERR_WORKSPACE, "build workspace %zu bytes < %zu", ws_bytes, L.total);
+  st = hip_device_ok();
+  if (st != WAVE_OK) return st;
+  out->shape = *shape;
+  out->seg_len = seg_len;
+  out->clusters_per_seg = clusters_per_seg;
+  uint8_t* w = reinterpret_cast<uint8_t*>(ws);
+  wave::BuildWs bw;
+  bw.norm = reinterpret_cast<float*>(w + L.norm);
+  bw.rank = reinterpret_cast<int32_t*>(w + L.rank);
+  bw.xn2 = reinterpret_cast<float*>(w + L.xn2);
+  hipError_t e = wave::launch_build_blocks(sa, K, V, *out, bw, z.units, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(WAVE_ERR_HIP, "block build launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 wave_status wave_attn_decode_plan(const wave_index* index, int32_t n_q_heads, int32_t n_sink, int32_t n_local,
                                   double topk_frac, int32_t* k_max, size_t* ws_bytes) {
   DecodePlan P;
@@ -304,12 +343,13 @@ wave_status wave_attn_decode_plan(const wave_index* index, int32_t n_q_heads, in
   return ok();
 }
 
-wave_status wave_attn_decode(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
-                             int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse, void* ws,
-                             size_t ws_bytes, wave_stream_t stream) {
+static wave_status decode_call(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
+                               int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse, void* ws,
+                               size_t ws_bytes, wave_stream_t stream, int est) {
   DecodePlan P;
   wave_status st = decode_plan(index, n_q_heads, n_sink, n_local, topk_frac, &P);
   if (st != WAVE_OK) return st;
+  P.da.est = est;
   if (q == nullptr || out == nullptr || ws == nullptr) return fail(WAVE_ERR_ARG, "q, out and ws must be non-NULL");
   if (P.da.k_max > 0 && sel_ids == nullptr) return fail(WAVE_ERR_ARG, "sel_ids is NULL but k_max = %d", P.da.k_max);
   const void* ptrs[] = {index->k_sorted, index->v_sorted, index->perm, index->inv_perm, index->assign,
@@ -342,6 +382,18 @@ wave_status wave_attn_decode(const wave_index* index, const void* q, int32_t n_q
                                      reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(WAVE_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+wave_status wave_attn_decode(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
+                             int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse, void* ws,
+                             size_t ws_bytes, wave_stream_t stream) {
+  return decode_call(index, q, n_q_heads, n_sink, n_local, topk_frac, out, sel_ids, lse, ws, ws_bytes, stream, 1);
+}
+
+wave_status wave_attn_decode_topk(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
+                                  int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse,
+                                  void* ws, size_t ws_bytes, wave_stream_t stream) {
+  return decode_call(index, q, n_q_heads, n_sink, n_local, topk_frac, out, sel_ids, lse, ws, ws_bytes, stream, 0);
 }
 
 wave_status wave_profiler_enable(int32_t on) {

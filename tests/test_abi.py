@@ -165,3 +165,26 @@ def test_calls_fail_cleanly_without_device():
     bad = list(dargs)
     bad[1] = ctypes.c_void_p(0x4008)
     assert L.wave_attn_decode(*bad) == ALIGN
+    # the block baseline's entry points check the same way
+    bargs = [ctypes.byref(sh), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), 1024, 64, ctypes.byref(ix),
+             ctypes.c_void_p(0x3000), z.build_ws_bytes, None]
+    assert L.wave_index_build_blocks(*bargs) == HIP
+    bad = list(bargs)
+    bad[2] = None
+    assert L.wave_index_build_blocks(*bad) == ARG
+    bad = list(bargs)
+    bad[6] = ctypes.c_void_p(0x3004)
+    assert L.wave_index_build_blocks(*bad) == ALIGN
+    bad = list(bargs)
+    bad[7] = z.build_ws_bytes - 1
+    assert L.wave_index_build_blocks(*bad) == WS
+    bad = list(bargs)
+    bad[4] = 2048
+    assert L.wave_index_build_blocks(*bad) == SHAPE
+    assert L.wave_attn_decode_topk(*dargs) == HIP
+    bad = list(dargs)
+    bad[10] = w - 1
+    assert L.wave_attn_decode_topk(*bad) == WS
+    bad = list(dargs)
+    bad[6] = None
+    assert L.wave_attn_decode_topk(*bad) == ARG
