@@ -36,7 +36,8 @@ WORKLOAD = dict(workload="llama3-8b-attention-layer-128k", batch=1, q_heads=32, 
                 seed_query=102)
 # the other workloads of the method's evaluation (reported with --workload; the default line is
 # the 128K one): a small parity-size layer, the 1M-token layer, a ragged batch of 16 sequences
-# of 64K..128K tokens, and the clustering alone on 1M heavy-tailed keys per kv head
+# of 64K..128K tokens, the block top-k baseline on the 128K layer, and the clustering alone on
+# 1M heavy-tailed keys per kv head
 WORKLOADS = {
     "128k": WORKLOAD,
     "16k": dict(workload="attention-layer-16k", batch=1, q_heads=8, kv_heads=2, head_dim=128, ctx=16384,
@@ -50,6 +51,9 @@ WORKLOADS = {
                     ctx=[65536, 131072], seg_len=8192, clusters_per_seg=512, kmeans_iters=10, n_sink=4,
                     n_local=64, topk_frac=0.02, decode_queries_per_step=64, layers=2, seed_data=4,
                     seed_build=1234, seed_query=104),
+    # the block top-k baseline on the 128K layer: contiguous blocks of 16 tokens instead of the
+    # k-means clusters and no estimation zone (a same-hardware comparison point)
+    "blocks": dict(WORKLOAD, workload="block-topk-baseline-128k", blocks=True, kmeans_iters=0),
     "stress": dict(workload="index-build-1m-keys-student-t", batch=1, q_heads=8, kv_heads=8, head_dim=128,
                    ctx=1048576, seg_len=8192, clusters_per_seg=512, kmeans_iters=10, heavy_tailed=True,
                    n_sink=4, n_local=64, topk_frac=0.02, decode_queries_per_step=0, layers=1, seed_data=5,
@@ -189,13 +193,15 @@ SOURCES = ["retrieval_sparse_attention_amd/csrc/decode.hip", "retrieval_sparse_a
 
 
 def accuracy(dev):
-    """Error of the wave attention against dense softmax attention over the budgets.
+    """Error of the wave attention and of two baselines against dense softmax attention.
 
     The 128K layer's generator (drifting Gaussian mixture keys and values, queries near a
-    uniformly drawn key), 16 queries per q head. For each clusters_per_seg (a new index),
-    topk_frac and n_local: relative L2 error |o - o_dense| / |o_dense| per (query, q head),
-    mean and maximum, and the share of tokens read exactly (retrieved plus steady). The
-    dense reference is float32 softmax attention in PyTorch over all N keys.
+    uniformly drawn key), 16 queries per q head. For each clusters_per_seg, topk_frac and
+    n_local: relative L2 error |o - o_dense| / |o_dense| per (query, q head) (mean, 90th
+    percentile, maximum) and the share of tokens read exactly (retrieved plus steady), for
+    the wave attention over the k-means index, the same selection without the estimation
+    zone, and the block top-k baseline (contiguous blocks, no estimation). The dense
+    reference is float32 softmax attention in PyTorch over all N keys.
     """
     import numpy as np
     import torch
@@ -223,15 +229,22 @@ def accuracy(dev):
         ref[:, g] = torch.matmul(torch.softmax(s, dim=1), Vf[g]).view(nq, H // G, 128)
     ref = ref.view(nq, H, 128)
     rows = []
+    # the wave attention over the k-means index at every budget; for a local window of 64 also
+    # the same selection without the estimation zone, and the block top-k baseline (contiguous
+    # blocks, no estimation)
+    runs = [("wave", False, True, nl) for nl in (0, 64, 512)] + [("kmeans-topk-only", False, False, 64),
+                                                                  ("block-topk", True, False, 64)]
     for ks in (256, 512, 1024):
-        idx = rsa.wave_index_build(Kd, Vd, G, [N], seg, ks, iters, W["seed_build"])
-        sizes = idx.arrays["sizes"].cpu().numpy()
-        C = sizes.size // G
-        for nl in (0, 64, 512):
+        kidx = rsa.wave_index_build(Kd, Vd, G, [N], seg, ks, iters, W["seed_build"])
+        bidx = rsa.wave_index_build_blocks(Kd, Vd, G, [N], seg, ks)
+        for method, blocks, estimate, nl in runs:
+            idx = bidx if blocks else kidx
+            sizes = idx.arrays["sizes"].cpu().numpy()
+            C = sizes.size // G
             for frac in (0.005, 0.01, 0.02, 0.05, 0.1):
                 err, exact = [], []
                 for t in range(nq):
-                    o, ids, _ = rsa.wave_attn_decode(idx, qd[t], ns, nl, frac)
+                    o, ids, _ = rsa.wave_attn_decode(idx, qd[t], ns, nl, frac, estimate=estimate)
                     e = (o[0] - ref[t]).norm(dim=1) / ref[t].norm(dim=1)
                     err.append(e.cpu().numpy())
                     ih = ids[0].cpu().numpy()
@@ -239,15 +252,16 @@ def accuracy(dev):
                         sel = ih[h][ih[h] >= 0]
                         exact.append((sizes[(h * G // H) * C + sel].sum() + ns + nl) / N)
                 err = np.concatenate(err)
-                rows.append({"clusters_per_seg": ks, "n_local": nl, "topk_frac": frac,
-                             "rel_err_mean": round(float(err.mean()), 5), "rel_err_p90": round(float(np.quantile(err, 0.9)), 5),
+                rows.append({"method": method, "clusters_per_seg": ks, "n_local": nl, "topk_frac": frac,
+                             "rel_err_mean": round(float(err.mean()), 5),
+                             "rel_err_p90": round(float(np.quantile(err, 0.9)), 5),
                              "rel_err_max": round(float(err.max()), 5),
                              "exact_token_share": round(float(np.mean(exact)), 4)})
-                print("K_s %4d n_local %3d frac %.3f: rel err mean %.4f max %.4f, exact tokens %.3f" % (
-                    ks, nl, frac, rows[-1]["rel_err_mean"], rows[-1]["rel_err_max"], rows[-1]["exact_token_share"]),
-                    file=sys.stderr, flush=True)
-        del idx
-    print(json.dumps({"metric": "relative L2 error of wave attention vs dense attention",
+                print("%-16s K_s %4d n_local %3d frac %.3f: rel err mean %.4f max %.4f, exact tokens %.3f" % (
+                    method, ks, nl, frac, rows[-1]["rel_err_mean"], rows[-1]["rel_err_max"],
+                    rows[-1]["exact_token_share"]), file=sys.stderr, flush=True)
+        del kidx, bidx
+    print(json.dumps({"metric": "relative L2 error against dense attention (wave attention and baselines)",
                       "workload": W["workload"], "queries_per_head": nq, "q_heads": H, "n_sink": ns,
                       "data": "synthetic", "reference": "float32 dense softmax attention (PyTorch)", "rows": rows}))
 
@@ -296,6 +310,7 @@ def main():
     seg, K_s, iters = W["seg_len"], W["clusters_per_seg"], W["kmeans_iters"]
     ns, nl, frac, QPS = W["n_sink"], W["n_local"], W["topk_frac"], W["decode_queries_per_step"]
     L = W["layers"]
+    blocks = W.get("blocks", False)
     if isinstance(W["ctx"], list):  # ragged: N_b ~ U{lo..hi} from the data seed
         ctx = synth.ctx_lengths(W["seed_data"], B, W["ctx"][0], W["ctx"][1])
     else:
@@ -316,8 +331,15 @@ def main():
     idxs = [rsa.WaveIndex.allocate(G, ctx.tolist(), seg, K_s, device=dev)[0] for _ in range(L)]
     bws = torch.empty(int(z["build_ws_bytes"]), dtype=torch.uint8, device=dev)
     print("building %d layer indexes" % L, file=sys.stderr, flush=True)
+    def build_layer(l):
+        if blocks:
+            rsa.wave_index_build_blocks(Ks[l], Vs[l], G, ctx.tolist(), seg, K_s, index=idxs[l], ws=bws)
+        else:
+            rsa.wave_index_build(Ks[l], Vs[l], G, ctx.tolist(), seg, K_s, iters, W["seed_build"], index=idxs[l],
+                                 ws=bws)
+
     for l in range(L):
-        rsa.wave_index_build(Ks[l], Vs[l], G, ctx.tolist(), seg, K_s, iters, W["seed_build"], index=idxs[l], ws=bws)
+        build_layer(l)
     torch.cuda.synchronize()
     k_max, dwsb = rsa.wave_attn_decode_plan(idxs[0], H, ns, nl, frac)
     dws = torch.empty(dwsb, dtype=torch.uint8, device=dev)
@@ -330,13 +352,13 @@ def main():
         """One step: rebuild layer (step mod L), then 64 queries over the layers round robin."""
         l = step % L
         if build:
-            rsa.wave_index_build(Ks[l], Vs[l], G, ctx.tolist(), seg, K_s, iters, W["seed_build"], index=idxs[l],
-                                 ws=bws)
+            build_layer(l)
         for s in range(QPS):
             lay = (step * QPS + s) % L
             qi = (step * QPS + s) % nq
             ids = ids_log[s] if ids_log is not None else ids_buf
-            rsa.wave_attn_decode(idxs[lay], qd[qi], ns, nl, frac, ws=dws, out=out, sel_ids=ids, lse=lse)
+            rsa.wave_attn_decode(idxs[lay], qd[qi], ns, nl, frac, ws=dws, out=out, sel_ids=ids, lse=lse,
+                                 estimate=not blocks)
 
     # the step pattern repeats with period P: one captured HIP graph per phase
     P = math.lcm(L, max(1, nq // math.gcd(nq, max(QPS, 1))))
@@ -441,11 +463,12 @@ def main():
     attend_bytes = (rows_per_dec * (2 * 128 * 2 + 4)         # K, V and perm of the retrieved rows
                     + B * H * steady * (2 * 128 * 2 + 4 + 4)  # steady rows: K, V, inv_perm, correction
                     + sel_per_dec * 16                        # window metadata
-                    + B * H * 128 * 2 + B * H * P * part      # q, row partials out
-                    + G * Ctot * (128 * 4 + 4)                # estimation: value sums + sizes
-                    + H * Ctot * 4                            # estimation: rank keys
-                    + H * n_est * part)                       # estimation partials out
-    merge_bytes = B * H * P * part + H * n_est * part + B * H * (128 * 4 + 4)
+                    + B * H * 128 * 2 + B * H * P * part)     # q, row partials out
+    if not blocks:
+        attend_bytes += (G * Ctot * (128 * 4 + 4)             # estimation: value sums + sizes
+                         + H * Ctot * 4                       # estimation: rank keys
+                         + H * n_est * part)                  # estimation partials out
+    merge_bytes = B * H * P * part + (0 if blocks else H * n_est * part) + B * H * (128 * 4 + 4)
     step_bytes = score_bytes + topk_bytes + attend_bytes + merge_bytes
     # per launch (one k-means round): every unit's tokens against its own clusters
     tok_clu = 0
@@ -457,12 +480,13 @@ def main():
             tok_clu += ls * (K_s if ls >= seg else -(-ls * K_s // seg))
     assign_flops = 2.0 * 128 * G * tok_clu
     assign_bytes = rows * (128 * 2 + 4) + G * Ctot * (128 * 2 + 4)
-    update_bytes = ((iters - 1) * (rows * (128 * 2 + 4) + G * Ctot * (128 * 4 + 128 * 2 + 4))
-                    + rows * (4 * 128 * 2 + 3 * 4) + G * Ctot * (2 * 128 * 4 + 128 * 2 + 4)) / iters
+    final_update = rows * (4 * 128 * 2 + 3 * 4) + G * Ctot * (2 * 128 * 4 + 128 * 2 + 4)
+    update_bytes = (final_update if blocks else
+                    ((iters - 1) * (rows * (128 * 2 + 4) + G * Ctot * (128 * 4 + 128 * 2 + 4)) + final_update) / iters)
     sort_bytes = rows * 12 + G * Ctot * 8
     init_bytes = G * Ctot * (128 * 2 + 128 * 4 + 128 * 2 + 4)
     hbm_bytes = {"k_score": score_bytes, "k_topk": topk_bytes, "k_attend": attend_bytes, "k_merge": merge_bytes,
-                 "k_update": update_bytes, "k_sort": sort_bytes, "k_init": init_bytes}
+                 "k_update": update_bytes, "k_sort": sort_bytes, "k_init": init_bytes, "k_block_assign": rows * 4}
 
     kern = {}
     for name, (cnt, ms) in prof.items():
