@@ -364,6 +364,45 @@ __device__ inline uint64_t block_scan_excl(uint64_t v, uint64_t* tmp, uint64_t* 
   return r;
 }
 
+// descending bitonic sort of n (power of two) unique u64 keys in LDS. Each wave owns a
+// contiguous region of R = n / waves keys; a compare-exchange step with distance j < R stays
+// inside the regions, so it needs no workgroup barrier: the wave's LDS operations complete in
+// order (a wait on the LDS counter between steps), and only the steps with j >= R (10 of
+// the 66 for n = 2048) synchronise the workgroup.
+__device__ inline void bitonic_desc_lds(uint64_t* a, int n) {
+  const int nw = blockDim.x >> 6, wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int R = n / nw;
+  bool waved = false;  // the previous step was wave-local
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= R || R < 2) {
+        if (waved) __syncthreads();
+        waved = false;
+        for (int i = threadIdx.x; i < n; i += blockDim.x) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const uint64_t x = a[i], y = a[ixj];
+            const bool desc = (i & k) == 0;
+            if (desc ? (x < y) : (x > y)) { a[i] = y; a[ixj] = x; }
+          }
+        }
+        __syncthreads();
+      } else {
+        // pairs (i, i + j) of the wave's region, i with bit j clear
+        for (int q = lane; q < R / 2; q += 64) {
+          const int i = wv * R + ((q / j) * 2 * j) + (q % j), ixj = i + j;
+          const uint64_t x = a[i], y = a[ixj];
+          const bool desc = (i & k) == 0;
+          if (desc ? (x < y) : (x > y)) { a[i] = y; a[ixj] = x; }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        waved = true;
+      }
+    }
+  }
+  if (waved) __syncthreads();
+}
+
 // descending bitonic sort of n (power of two) unique u64 keys (LDS or global)
 __device__ inline void bitonic_desc(uint64_t* a, int n, bool global) {
   for (int k = 2; k <= n; k <<= 1) {
@@ -414,7 +453,8 @@ struct TopkLds {
   uint32_t selw[TK_SELW];       // selection bitmap (C <= 65536)
   uint64_t scan[17];
   uint32_t bis[34];             // block counts of the bisection, then of keys above T
-  uint32_t cbis[32];            // block counts of the bisection over the chunks' top keys
+  uint32_t rhist[2][256];       // digit counts of the radix select over the chunks' top keys
+  uint32_t rsel[2];             // its digit and the count above it
   int32_t wE[16];
   uint32_t wt[16];
   int32_t tcnt[16];             // keys >= wt[i] over the workgroup
@@ -506,7 +546,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
     L.u.c.pre[tid] = 0;
   }
   if (tid < 34) L.bis[tid] = 0u;
-  if (tid < 32) L.cbis[tid] = 0u;
+  if (tid < 256) L.rhist[0][tid] = 0u;
   if (tid < 8) L.misc[tid] = 0;
   if (tid < 16) L.tcnt[tid] = 0;
 
@@ -669,21 +709,76 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
       uint32_t tv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) tv[r] = tid < nch ? ct[(int64_t)tid * 8 + r] : 0u;
+      // t = the k-th largest of them (zeros included): a radix select, 8 bits a pass from
+      // the top; a wave counts equal digits by matching the 8 digit bits with ballots and
+      // the lowest lane of each match adds the count (one LDS atomic per distinct digit)
       uint32_t t = 0u;
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t c = t | (1u << bit);
-        int cnt = 0;
+      {
+        uint32_t pre = 0u, msk = 0u;
+        int kr = k;
+        for (int pass = 0; pass < 4; ++pass) {
+          const int sh = 24 - 8 * pass;
+          uint32_t* hist = L.rhist[pass & 1];
+          if (tid < 256) L.rhist[(pass + 1) & 1][tid] = 0u;  // for the next pass (read two barriers ago)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) cnt += __popcll(__ballot(tv[r] >= c));
-        if (lane == 0) atomicAdd(&L.cbis[bit], (uint32_t)cnt);
-        lds_barrier();
-        if (L.cbis[bit] >= (uint32_t)k) t = c;
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t d = (tv[r] >> sh) & 255u;
+            uint64_t m = __ballot((tv[r] & msk) == pre);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+              const uint64_t bb = __ballot((d >> b) & 1u);
+              m &= ((d >> b) & 1u) ? bb : ~bb;
+            }
+            if ((tv[r] & msk) == pre && (m & ltmask) == 0ull) atomicAdd(&hist[d], (uint32_t)__popcll(m));
+          }
+          lds_barrier();
+          if (wv == 0) {
+            // lane l: digits 4l..4l+3; suffix sums over the lanes give the count at or above
+            const uint4 h4 = reinterpret_cast<const uint4*>(hist)[lane];
+            const int s4 = (int)(h4.x + h4.y + h4.z + h4.w);
+            int suf = s4;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+              const int v = __shfl_down(suf, o, 64);
+              if (lane + o < 64) suf += v;
+            }
+            const int above = suf - s4;  // digits >= 4l + 4
+            if (above < kr && kr <= suf) {
+              int gt = above, d = 4 * lane + 3;
+              if (gt + (int)h4.w < kr) {
+                gt += (int)h4.w;
+                d = 4 * lane + 2;
+                if (gt + (int)h4.z < kr) {
+                  gt += (int)h4.z;
+                  d = 4 * lane + 1;
+                  if (gt + (int)h4.y < kr) {
+                    gt += (int)h4.y;
+                    d = 4 * lane;
+                  }
+                }
+              }
+              L.rsel[0] = (uint32_t)d;
+              L.rsel[1] = (uint32_t)gt;
+            }
+          }
+          lds_barrier();
+          pre |= L.rsel[0] << sh;
+          msk |= 255u << sh;
+          kr -= (int)L.rsel[1];
+        }
+        t = pre;
       }
       if (t > 0u) {
         uint64_t* cb = L.u.sortbuf;
+        // the keys a chunk ahead in flight (the loads of a chunk otherwise wait for the
+        // previous chunk's collection)
+        uint32_t un[CHK];
+        chunk_keys(0, un);
         for (int c0 = 0; c0 < NV; c0 += CHK) {
           uint32_t uc[CHK];
-          chunk_keys(c0, uc);
+#pragma unroll
+          for (int v = 0; v < CHK; ++v) uc[v] = un[v];
+          if (c0 + CHK < NV) chunk_keys(c0 + CHK, un);
           uint64_t bal[CHK];
           int tot = 0;
 #pragma unroll
@@ -710,7 +805,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
           while (P2 < nc) P2 <<= 1;
           for (int i = nc + tid; i < P2; i += nt) cb[i] = 0ull;
           __syncthreads();
-          bitonic_desc(cb, P2, false);
+          bitonic_desc_lds(cb, P2);
           // (key desc, id asc): the first k are the selection in rank order
           for (int r = tid; r < k; r += nt) {
             const int id = (int)(0xFFFFFFFFu - (uint32_t)(cb[r] & 0xFFFFFFFFu));
