@@ -830,6 +830,12 @@ __global__ __launch_bounds__(SORT_THREADS) void k_sort(SeqArgs sa, const int32_t
 // tile, wave) counts are scanned over the workgroup in digit-major order, which
 // makes every pass stable. After the passes the sorted keys give perm directly,
 // and each cluster's first slot is found by binary search.
+//
+// With parts = 2 (the units alone would leave half the CUs idle) a unit's tokens are
+// split between two workgroups at position Lp = ceil(L / 2): each counts the clusters of
+// both halves, so that member j of cluster c in half 1 goes to slot off[c] + (members of c
+// in half 0) + j, sorts its own half and writes those slots; half 0 writes sizes and
+// offsets.
 constexpr int RS_THREADS = 1024;
 constexpr int RS_MAXL = 16384;  // positions fit 14 bits
 constexpr int RS_DB = 5;
@@ -837,29 +843,79 @@ constexpr int RS_ND = 1 << RS_DB;
 
 __device__ inline uint32_t rs_digit(uint32_t key, int pass) { return (key >> (14 + RS_DB * pass)) & (RS_ND - 1); }
 
-__global__ __launch_bounds__(RS_THREADS) void k_sort_radix(SeqArgs sa, const int32_t* __restrict__ assign,
+// LDS slot of counter x: the counters of one (tile, wave) for the 32 digits lie 16 E words
+// apart, i.e. in one bank; xor-ing bits 6.. into the bank bits spreads them over 32 banks
+// (a bijection inside every 64-word block)
+__device__ __forceinline__ int rs_cx(int x) { return x ^ ((x >> 6) & 63); }
+
+// exclusive scan of one u64 per thread over a workgroup of RS_THREADS; *total gets the sum
+__device__ inline uint64_t block_scan_u64(uint64_t v, uint64_t* tmp, uint64_t* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint64_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) tmp[wv] = x;
+  __syncthreads();
+  if (wv == 0) {
+    const uint64_t t = lane < RS_THREADS / 64 ? tmp[lane] : 0ull;
+    uint64_t tt = t;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const uint64_t y = __shfl_up(tt, o, 64);
+      if (lane >= o) tt += y;
+    }
+    if (lane < RS_THREADS / 64) tmp[lane] = tt - t;
+    if (lane == RS_THREADS / 64 - 1) tmp[16] = tt;
+  }
+  __syncthreads();
+  const uint64_t r = tmp[wv] + x - v;
+  *total = tmp[16];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(RS_THREADS) void k_sort_radix(SeqArgs sa, int parts, const int32_t* __restrict__ assign,
                                                            int32_t* __restrict__ sizes,
                                                            int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ perm) {
   extern __shared__ uint8_t smem[];
-  const Unit U = unit_of(sa, blockIdx.x);
-  const int Kc = U.Kc, L = U.L;
-  const int E = (L + RS_THREADS - 1) / RS_THREADS;  // tiles
+  const Unit U = unit_of(sa, blockIdx.x / parts);
+  const int part = (int)(blockIdx.x % parts);
+  const int Kc = U.Kc, Lp = (U.L + parts - 1) / parts, p0 = part * Lp;
+  const int L = min(Lp, U.L - p0);                   // this workgroup's positions [p0, p0 + L)
+  const int E = (Lp + RS_THREADS - 1) / RS_THREADS;  // tiles
   uint32_t* buf0 = reinterpret_cast<uint32_t*>(smem);
   uint32_t* buf1 = buf0 + E * RS_THREADS;
   __shared__ uint64_t scan[17];
   __shared__ int32_t first[WAVE_MAX_CLUSTERS_PER_SEG + 1];  // first sorted slot of cluster c (c <= Kc)
+  __shared__ int32_t hist1[WAVE_MAX_CLUSTERS_PER_SEG];      // parts = 2: members of c in half 1
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const uint64_t ltmask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int nbits = 0;
   while ((1 << nbits) < Kc) ++nbits;
   const int passes = (nbits + RS_DB - 1) / RS_DB;
+  if (parts > 1) {
+    // members per cluster in each half (first[] holds half 0's counts for now)
+    for (int c = tid; c < Kc; c += RS_THREADS) {
+      first[c] = 0;
+      hist1[c] = 0;
+    }
+    __syncthreads();
+    for (int i = tid; i < U.L; i += RS_THREADS) {
+      const int c = min(max(assign[U.row0 + i] - U.cbase, 0), Kc - 1);
+      atomicAdd(i < Lp ? &first[c] : &hist1[c], 1);
+    }
+    __syncthreads();
+  }
   // keys in element (= position) order; ids are in [0, Kc) by construction, the clamp keeps
   // every sorted slot inside the segment even if they were not
   for (int e = 0; e < E; ++e) {
     const int i = e * RS_THREADS + tid;
     const int ic = min(i, L - 1);
-    const int c = min(max(assign[U.row0 + ic] - U.cbase, 0), Kc - 1);
+    const int c = min(max(assign[U.row0 + p0 + ic] - U.cbase, 0), Kc - 1);
     buf0[i] = ((uint32_t)c << 14) | (uint32_t)ic;
   }
   __syncthreads();
@@ -887,7 +943,7 @@ __global__ __launch_bounds__(RS_THREADS) void k_sort_radix(SeqArgs sa, const int
         }
         dg[e] = d;
         rk[e] = __popcll(m & ltmask);
-        if (valid && rk[e] == 0) cnt[((int)d * E + e) * 16 + wv] = __popcll(m);
+        if (valid && rk[e] == 0) cnt[rs_cx(((int)d * E + e) * 16 + wv)] = __popcll(m);
       }
     }
     __syncthreads();
@@ -895,7 +951,7 @@ __global__ __launch_bounds__(RS_THREADS) void k_sort_radix(SeqArgs sa, const int
     {
       const int x0 = min(tid * per, nx), x1 = min(x0 + per, nx);
       uint64_t local = 0;
-      for (int x = x0; x < x1; ++x) local += (uint32_t)cnt[x];
+      for (int x = x0; x < x1; ++x) local += (uint32_t)cnt[rs_cx(x)];
       uint64_t y = local;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -917,8 +973,8 @@ __global__ __launch_bounds__(RS_THREADS) void k_sort_radix(SeqArgs sa, const int
       __syncthreads();
       int run = (int)(scan[wv] + y - local);
       for (int x = x0; x < x1; ++x) {
-        const int c = cnt[x];
-        cnt[x] = run;
+        const int c = cnt[rs_cx(x)];
+        cnt[rs_cx(x)] = run;
         run += c;
       }
     }
@@ -930,7 +986,7 @@ __global__ __launch_bounds__(RS_THREADS) void k_sort_radix(SeqArgs sa, const int
       if (e < E) {
         const int i = e * RS_THREADS + tid;
         kv[e] = src[i];
-        pos[e] = cnt[((int)dg[e] * E + e) * 16 + wv] + rk[e];
+        pos[e] = cnt[rs_cx(((int)dg[e] * E + e) * 16 + wv)] + rk[e];
       }
     }
     __syncthreads();  // the counters are read; dst takes the keys
@@ -941,6 +997,44 @@ __global__ __launch_bounds__(RS_THREADS) void k_sort_radix(SeqArgs sa, const int
     uint32_t* t = src;
     src = dst;
     dst = t;
+  }
+  if (parts > 1) {
+    // slot of sorted element s of cluster c: off[c] + (half 1: members of c in half 0) +
+    // (s - first element of c in this half). One scan of (total, this half's count) pairs
+    // over the clusters, 2 per thread.
+    const int c0 = 2 * tid;
+    uint64_t v[2] = {0ull, 0ull};
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      if (c0 + r < Kc) {
+        const uint64_t h0 = (uint32_t)first[c0 + r], h1 = (uint32_t)hist1[c0 + r];
+        v[r] = ((h0 + h1) << 32) | (part == 0 ? h0 : h1);
+      }
+    uint64_t tot;
+    const uint64_t ex = block_scan_u64(v[0] + v[1], scan, &tot);
+    int32_t delta[2];
+    uint64_t run = ex;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int off = (int)(run >> 32), fmy = (int)(run & 0xFFFFFFFFu);
+      delta[r] = off + (part == 1 && c0 + r < Kc ? first[c0 + r] : 0) - fmy;
+      if (part == 0 && c0 + r < Kc) {
+        offsets[U.boff + U.cbase + c0 + r] = U.tok0 + off;
+        sizes[U.gclu + c0 + r] = (int32_t)(v[r] >> 32);
+      }
+      run += v[r];
+    }
+    __syncthreads();  // first[] and hist1[] are read
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      if (c0 + r < Kc) first[c0 + r] = delta[r];
+    __syncthreads();
+    for (int i = tid; i < L; i += RS_THREADS) {
+      const uint32_t key = src[i];
+      perm[U.brow + U.tok0 + first[key >> 14] + i] = U.tok0 + p0 + (int32_t)(key & 0x3FFFu);
+    }
+    if (part == 0 && tid == 0 && U.tok0 + U.L == U.N) offsets[U.boff + U.C] = U.N;
+    return;
   }
   // perm, and each cluster's first slot by binary search over the sorted keys
   for (int i = tid; i < L; i += RS_THREADS) perm[U.brow + U.tok0 + i] = U.tok0 + (int32_t)(src[i] & 0x3FFFu);
@@ -1044,6 +1138,20 @@ __global__ __launch_bounds__(1024) void k_block_assign(SeqArgs sa, int32_t* __re
 }
 
 // ------------------------------------------------------------------ host side
+// Workgroups per unit of the LDS radix sort: 2 when the units alone would leave more than
+// half of the compute units idle (one 1024-thread workgroup per CU), else 1.
+static int sort_parts(int64_t units) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cus = n;
+    else
+      cus = 256;
+  }
+  return 2 * units <= cus ? 2 : 1;
+}
 // Tokens per k_assign workgroup: enough workgroups per segment that the units fill
 // the 256 compute units once (one workgroup per CU: its LDS and registers take the CU),
 // in whole tiles.
@@ -1090,7 +1198,8 @@ hipError_t launch_build(const SeqArgs& sa, const void* Kv, const void* Vv, int32
   const size_t init_lds = ((2 * (size_t)sa.seg_len + 15) & ~(size_t)15) + 4 * (size_t)sa.K_s;
   const size_t sort_lds = 16 * (size_t)sa.K_s * 4;
   // two key buffers of E tiles; the counters (32 digits x E tiles x 16 waves) fit in one
-  const size_t radix_tiles = ((size_t)sa.seg_len + RS_THREADS - 1) / RS_THREADS;
+  const int sparts = sort_parts(units);
+  const size_t radix_tiles = ((size_t)(sa.seg_len + sparts - 1) / sparts + RS_THREADS - 1) / RS_THREADS;
   const size_t radix_lds = 2 * radix_tiles * RS_THREADS * 4;
   const unsigned cgrid = (unsigned)((nclu + 3) / 4);
   uint16_t* chat = reinterpret_cast<uint16_t*>(ix.centroids_bf16);
@@ -1116,8 +1225,8 @@ hipError_t launch_build(const SeqArgs& sa, const void* Kv, const void* Vv, int32
     }
     prof_begin("k_sort", st);
     if (sa.seg_len <= RS_MAXL)
-      hipLaunchKernelGGL(k_sort_radix, dim3((unsigned)units), dim3(RS_THREADS), radix_lds, st, sa, ix.assign, ix.sizes,
-                         ix.offsets, ix.perm);
+      hipLaunchKernelGGL(k_sort_radix, dim3((unsigned)(units * sparts)), dim3(RS_THREADS), radix_lds, st, sa, sparts,
+                         ix.assign, ix.sizes, ix.offsets, ix.perm);
     else
       hipLaunchKernelGGL(k_sort, dim3((unsigned)units), dim3(SORT_THREADS), sort_lds, st, sa, ix.assign, ws.rank,
                          ix.sizes, ix.offsets, ix.perm);
@@ -1147,7 +1256,8 @@ hipError_t launch_build_blocks(const SeqArgs& sa, const void* Kv, const void* Vv
   int64_t nclu = 0;
   for (int b = 0; b < sa.B; ++b) nclu += (int64_t)sa.G * sa.C[b];
   const size_t sort_lds = 16 * (size_t)sa.K_s * 4;
-  const size_t radix_tiles = ((size_t)sa.seg_len + RS_THREADS - 1) / RS_THREADS;
+  const int sparts = sort_parts(units);
+  const size_t radix_tiles = ((size_t)(sa.seg_len + sparts - 1) / sparts + RS_THREADS - 1) / RS_THREADS;
   const size_t radix_lds = 2 * radix_tiles * RS_THREADS * 4;
   const unsigned cgrid = (unsigned)((nclu + 3) / 4);
   prof_begin("k_block_assign", st);
@@ -1157,8 +1267,8 @@ hipError_t launch_build_blocks(const SeqArgs& sa, const void* Kv, const void* Vv
   // (identity) order, member means, bf16 centroids, value sums
   prof_begin("k_sort", st);
   if (sa.seg_len <= RS_MAXL)
-    hipLaunchKernelGGL(k_sort_radix, dim3((unsigned)units), dim3(RS_THREADS), radix_lds, st, sa, ix.assign, ix.sizes,
-                       ix.offsets, ix.perm);
+    hipLaunchKernelGGL(k_sort_radix, dim3((unsigned)(units * sparts)), dim3(RS_THREADS), radix_lds, st, sa, sparts,
+                       ix.assign, ix.sizes, ix.offsets, ix.perm);
   else
     hipLaunchKernelGGL(k_sort, dim3((unsigned)units), dim3(SORT_THREADS), sort_lds, st, sa, ix.assign, ws.rank,
                        ix.sizes, ix.offsets, ix.perm);
