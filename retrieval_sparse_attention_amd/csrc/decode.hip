@@ -32,7 +32,8 @@ namespace wave {
 
 constexpr int SC = DEC_SCORE_CH;  // clusters per k_score workgroup
 constexpr int SCORE_THREADS = 256;
-constexpr int TK_THREADS = 1024;
+constexpr int TK_WAVES = DEC_TK_WAVES;
+constexpr int TK_THREADS = 64 * TK_WAVES;
 constexpr int TK_CAP = 1024;      // candidates of the fast selection
 constexpr int TK_SORT = DEC_SORT_LDS;
 constexpr int TK_SELW = 2048;     // selection bitmap words kept in LDS (C <= 65536)
@@ -431,9 +432,9 @@ __device__ inline void bitonic_desc(uint64_t* a, int n, bool global) {
 // path below takes NV <= 16).
 //
 // Fast path (keys in registers, k <= 1024): every wave finds the m-th largest
-// of its 64 lane maxima, t_w (m = ceil(kreq / 16)), by bisection over the 32
-// key bits with ballots, no barrier; at least m keys of the wave are >= t_w, so
-// at least 16 m >= k keys are >= min_w t_w. A lane whose maximum is >= t holds a
+// of its 64 lane maxima, t_w (m = ceil(kreq / W) for W waves), by bisection over
+// the 32 key bits with ballots, no barrier; at least m keys of the wave are >= t_w,
+// so at least W m >= k keys are >= min_w t_w. A lane whose maximum is >= t holds a
 // key >= t, so counting lane maxima >= each t_w bounds the keys >= t_w from below:
 // X is the largest t_w with at least k lane maxima at or above it, and the keys
 // >= X contain R. When there are at most 1024 of them, each one's rank and
@@ -496,7 +497,8 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
 
   // 0. loads in the order their values are needed (the load counter drains in issue
   // order): the keys, their sizes and offsets, then the steady tokens' clusters; LDS init
-  constexpr bool PRE = INREG && NVR <= 8;  // sizes and offsets of every key prefetched
+  // sizes and offsets of every key prefetched (as registers allow)
+  constexpr bool PRE = INREG && NVR <= (TK_WAVES <= 8 ? 16 : 8);
   uint32_t ureg[INREG ? NVR : 1];
   int32_t nreg[PRE ? NVR : 1], oreg[PRE ? NVR : 1];
   if constexpr (INREG) {
@@ -542,8 +544,10 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
     for (int i = tid; i < nwords; i += nt) selw[i] = 0u;
   }
   if constexpr (INREG) {
-    L.u.c.rank[tid] = 0;
-    L.u.c.pre[tid] = 0;
+    for (int i = tid; i < TK_CAP; i += nt) {
+      L.u.c.rank[i] = 0;
+      L.u.c.pre[i] = 0;
+    }
   }
   if (tid < 34) L.bis[tid] = 0u;
   if (tid < 256) L.rhist[0][tid] = 0u;
@@ -552,7 +556,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
 
   // 1. per wave: eligible keys and (keys in registers) the m-th largest key
   const int kreq = da.kreq[b];
-  const int m = (kreq + 15) / 16;
+  const int m = (kreq + TK_WAVES - 1) / TK_WAVES;
   int Ew = 0;
   uint32_t tw = 0u;
   uint32_t lmax = 0u;
@@ -569,7 +573,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
       }
     }
   } else {
-    // eligible keys from k_score's chunk summaries (thread t adds chunks t, t + 1024, ...)
+    // eligible keys from k_score's chunk summaries (thread t adds chunks t, t + TK_THREADS, ...)
     const int nch = (C + SC - 1) / SC;
     const uint32_t* ct = ws.ctop + (int64_t)bh * (da.NP - da.P) * 8;
     int e = 0;
@@ -590,24 +594,24 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
   int nE = 0;
   uint32_t X = 0xFFFFFFFFu;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < TK_WAVES; ++i) {
     nE += L.wE[i];
     X = min(X, L.wt[i]);
   }
   const int k = min(kreq, nE);
   if constexpr (INREG) {
     if (k > 0 && k == kreq && X > 0u) {
-      // lane maxima >= each wave threshold; lane i < 16 of every wave adds its count for wt[i]
+      // lane maxima >= each wave threshold; lane i < TK_WAVES of every wave adds its count for wt[i]
       int mine = 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < TK_WAVES; ++i) {
         const int cnt = __popcll(__ballot(lmax >= L.wt[i]));
         mine = (lane == i) ? cnt : mine;
       }
-      if (lane < 16) atomicAdd(&L.tcnt[lane], mine);
+      if (lane < TK_WAVES) atomicAdd(&L.tcnt[lane], mine);
       lds_barrier();
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < TK_WAVES; ++i) {
         const int tc = L.tcnt[i];  // both read unconditionally: no serial LDS round trips
         const uint32_t ti = L.wt[i];
         X = tc >= k ? max(X, ti) : X;
@@ -658,10 +662,10 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
     const int nc = L.misc[0];
     fast = nc <= TK_CAP;
     if (fast) {
-      // candidate i = tid mod nc counts over the part (tid / nc) of the candidates
+      // item x = (part, candidate i) counts over that part of the candidates
       const int P = max(1, TK_THREADS / nc);
-      const int i = tid % nc, part = tid / nc;
-      if (part < P) {
+      for (int x = tid; x < nc * P; x += nt) {
+        const int i = x % nc, part = x / nc;
         const uint4 ri = L.u.c.rec[i];
         const uint64_t c = ((uint64_t)ri.y << 32) | ri.x;
         const int j0 = nc * part / P, j1 = nc * (part + 1) / P;  // nc <= 1024: no overflow
@@ -678,12 +682,12 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
       }
       lds_barrier();
       int32_t* selpre = ws.selpre + kbase + bh;  // k + 1 entries per (b, h)
-      if (tid < nc) {
-        const int rank = L.u.c.rank[tid];
+      for (int ci = tid; ci < nc; ci += nt) {
+        const int rank = L.u.c.rank[ci];
         if (rank < k) {
-          const uint4 r = L.u.c.rec[tid];
+          const uint4 r = L.u.c.rec[ci];
           const int id = (int)(0xFFFFFFFFu - r.x);
-          const int n = (int)r.z, pre = L.u.c.pre[tid];
+          const int n = (int)r.z, pre = L.u.c.pre[ci];
           out[rank] = id;
           span[rank] = make_int2((int)r.w, n);
           skey[rank] = sortable_float(r.y);

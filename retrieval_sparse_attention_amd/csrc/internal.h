@@ -40,6 +40,7 @@ struct DecodeWs {
 };
 
 constexpr int DEC_SCORE_CH = 128;
+constexpr int DEC_TK_WAVES = 16;  // waves of a k_topk workgroup (one per (sequence, q head))
 constexpr int DEC_PART = 132;
 constexpr int DEC_SORT_LDS = 4096;
 // Rows per gathering workgroup of k_attend. With fewer rows per workgroup each 16-lane

@@ -181,8 +181,9 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
   // that every wave holds keys (its thresholds then bound the selection); 0: beyond registers
   da.NV = 0;
   for (int nv = 1; nv <= 32; nv *= 2)
-    if (16 * 64 * nv >= Cmax) { da.NV = nv; break; }
-  da.NVg = (int32_t)(((Cmax + 16 * 64 * 16 - 1) / (16 * 64 * 16)) * 16);
+    if (wave::DEC_TK_WAVES * 64 * nv >= Cmax) { da.NV = nv; break; }
+  constexpr int64_t NVG_Q = (int64_t)wave::DEC_TK_WAVES * 64 * 16;  // keys per 16 a lane
+  da.NVg = (int32_t)(((Cmax + NVG_Q - 1) / NVG_Q) * 16);
   int sort_stride = 0;
   if (kmax > wave::DEC_SORT_LDS) {
     sort_stride = 1;
