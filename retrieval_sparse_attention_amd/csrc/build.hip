@@ -191,7 +191,7 @@ __global__ __launch_bounds__(INIT_THREADS) void k_init(SeqArgs sa, uint64_t seed
 //
 // Selection per lane: the 6-bit position of each of its 64 values is written
 // into the value's low mantissa bits, so the best and second best come from
-// max3/med3 over triples and the best's position is read back from its bits.
+// a tournament of triples (max3/med3) and the best's position is read back from its bits.
 // The packing moves a value by less than 2^-17 |f|. The best, its position and
 // the second best are then merged across the two half-waves and the 4 waves.
 // When the gap between best and second best is within 2^-14 (|x| R + R^2),
@@ -272,24 +272,47 @@ __device__ __forceinline__ float pack6(float v, int p) {
   return __uint_as_float((__float_as_uint(v) & ~63u) | (unsigned)p);
 }
 
-// Best and second best of v[0..n) folded into (b1, b2); max3/med3 over triples.
-template <int n>
-__device__ __forceinline__ void top2_fold(const float* v, float& b1, float& b2) {
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// Best and second best of the 32 values v and a running pair b1 >= b2 (FRESH: none yet),
+// by a tournament of triples: a triple's maximum goes up a level, its median is kept.
+// The second best overall is the median of the triple where its path meets the best's
+// (the best and it are the two largest of that triple), and no median exceeds it (a
+// median is below its triple's maximum), so it is the largest median; the running pair
+// enters as one more player (b1) and one more median (b2). 40 operations for 32 values,
+// where folding each triple into the running pair takes 54.
+template <bool FRESH>
+__device__ __forceinline__ void top2_tree32(const float (&v)[32], float& b1, float& b2) {
+  float up[12], md[17];
 #pragma unroll
-  for (int k3 = 0; k3 + 3 <= n; k3 += 3) {
-    const float x = v[k3], y = v[k3 + 1], z = v[k3 + 2];
-    const float m = fmaxf(fmaxf(x, y), z), md = __builtin_amdgcn_fmed3f(x, y, z);
-    b2 = fmaxf(md, __builtin_amdgcn_fmed3f(m, b1, b2));
-    b1 = fmaxf(b1, m);
+  for (int k = 0; k < 10; ++k) {
+    up[k] = max3f(v[3 * k], v[3 * k + 1], v[3 * k + 2]);
+    md[k] = __builtin_amdgcn_fmed3f(v[3 * k], v[3 * k + 1], v[3 * k + 2]);
   }
-  if constexpr (n % 3 == 2) {
-    const float hi = fmaxf(v[n - 2], v[n - 1]), lo = fminf(v[n - 2], v[n - 1]);
-    b2 = fmaxf(lo, __builtin_amdgcn_fmed3f(hi, b1, b2));
-    b1 = fmaxf(b1, hi);
-  } else if constexpr (n % 3 == 1) {
-    b2 = __builtin_amdgcn_fmed3f(v[n - 1], b1, b2);
-    b1 = fmaxf(b1, v[n - 1]);
+  up[10] = v[30];
+  up[11] = v[31];
+  float u2[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    u2[k] = max3f(up[3 * k], up[3 * k + 1], up[3 * k + 2]);
+    md[10 + k] = __builtin_amdgcn_fmed3f(up[3 * k], up[3 * k + 1], up[3 * k + 2]);
   }
+  const float u3 = max3f(u2[0], u2[1], u2[2]);
+  md[14] = __builtin_amdgcn_fmed3f(u2[0], u2[1], u2[2]);
+  constexpr int n = FRESH ? 16 : 17;
+  if constexpr (FRESH) {
+    b1 = fmaxf(u3, u2[3]);
+    md[15] = fminf(u3, u2[3]);
+  } else {
+    md[15] = __builtin_amdgcn_fmed3f(u3, u2[3], b1);
+    md[16] = b2;
+    b1 = max3f(u3, u2[3], b1);
+  }
+  float s = max3f(md[0], md[1], md[2]);
+#pragma unroll
+  for (int k = 3; k + 2 <= n; k += 2) s = max3f(s, md[k], md[k + 1]);
+  if constexpr ((n - 3) % 2 == 1) s = fmaxf(s, md[n - 1]);
+  b2 = s;
 }
 
 template <bool MULTI>
@@ -422,8 +445,9 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
     }
     assign[U.row0 + tb0 + min(max(tr, tk), nrow - 1)] = U.cbase + best_id;
     const float margin = 0x1p-14f * (__builtin_amdgcn_sqrtf(x2) * R + R2) + 0x1p-100f;
-    // also undecided: a best at the floor of the padding rows (values beyond fp32 range)
-    const bool near = !(b1 - b2 > margin) || !(b1 > -0x1p127f);
+    // also undecided: a best at the floor of the padding rows, and keys or centroids so large
+    // that a value may leave the fp32 range (|f| < |x| R + R^2 / 2 < 2^114 otherwise)
+    const bool near = !(b1 - b2 > margin) || !(b1 > -0x1p127f) || !(margin < 0x1p100f);
     S.ambf[AS_TT + tr] = (near && tr < nrow) ? 1 : 0;
   };
   // |x|^2 of this wave's tokens of a tile: lane (col, h) sums the 64 dims of half h
@@ -466,11 +490,10 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
     for (int r = 0; r < 2; ++r)
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[16 * r + i] = pack6(acc[r][i], 32 * hb + 16 * r + i);
-    if (hb == 0) {
-      b1 = -INFINITY;
-      b2 = -INFINITY;
-    }
-    top2_fold<32>(v, b1, b2);
+    if (hb == 0)
+      top2_tree32<true>(v, b1, b2);
+    else
+      top2_tree32<false>(v, b1, b2);
   };
   // merge the two half-waves (the lanes of one token) and store the wave's result for the
   // block. Both halves store the same values, up to exact ties, which need no order here:
@@ -680,8 +703,9 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
       for (int r = 0; r < 2; ++r)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          cm |= (uint64_t)(a0[r][i] >= thr) << (16 * r + i);
-          cm |= (uint64_t)(a1[r][i] >= thr) << (32 + 16 * r + i);
+          // a NaN window or value (fp32 overflow) makes every centroid a candidate
+          cm |= (uint64_t)!(a0[r][i] < thr) << (16 * r + i);
+          cm |= (uint64_t)!(a1[r][i] < thr) << (32 + 16 * r + i);
         }
       while (cm != 0ull) {
         const int q = __builtin_ctzll(cm);
