@@ -61,6 +61,8 @@ def _load():
         lib.ref_select.argtypes = [P, P, i32, i32, P]
         lib.ref_decode.argtypes = [i32, i32, i32, P, i32, i32, P, P, P, P, P, P, i32, i32, f64, i32, P, P, P, P]
         lib.ref_decode.restype = ctypes.c_int
+        lib.ref_decode_shared.argtypes = lib.ref_decode.argtypes
+        lib.ref_decode_shared.restype = ctypes.c_int
         lib.ref_decode_topk.argtypes = [i32, i32, i32, P, i32, i32, P, P, P, P, P, i32, i32, f64, i32, P, P, P, P]
         lib.ref_decode_topk.restype = ctypes.c_int
         lib.ref_block_assign.argtypes = [i32, i32, P, i32, i32, P]
@@ -221,8 +223,9 @@ def decode_k_max(C_list, topk_frac):
     return max([k_from_frac(topk_frac, int(C)) for C in C_list] + [0])
 
 
-def decode(index, K, V, q, n_sink, n_local, topk_frac, k_max=None):
-    """Wave-index decode for q [B][H][128] against `index`. Returns (out [B,H,128] f64, lse [B,H], ids, k [B,H])."""
+def decode(index, K, V, q, n_sink, n_local, topk_frac, k_max=None, shared=False):
+    """Wave-index decode for q [B][H][128] against `index`. Returns (out [B,H,128] f64, lse [B,H], ids, k [B,H]).
+    shared: one retrieval set per kv head, chosen by the group key (ref_decode_shared)."""
     q = _c(q, np.uint16)
     B, H = q.shape[0], q.shape[1]
     if k_max is None:
@@ -231,9 +234,10 @@ def decode(index, K, V, q, n_sink, n_local, topk_frac, k_max=None):
     lse = np.empty((B, H), np.float64)
     ids = np.empty((B, H, max(k_max, 1)), np.int32)
     kc = np.empty((B, H), np.int32)
-    rc = _load().ref_decode(B, H, index.G, _p(index.ctx), index.seg_len, index.K_s, _p(_c(K, np.uint16)),
-                            _p(_c(V, np.uint16)), _p(index.assign), _p(index.centroids_bf16), _p(index.vsum), _p(q),
-                            n_sink, n_local, topk_frac, k_max, _p(out), _p(lse), _p(ids), _p(kc))
+    fn = _load().ref_decode_shared if shared else _load().ref_decode
+    rc = fn(B, H, index.G, _p(index.ctx), index.seg_len, index.K_s, _p(_c(K, np.uint16)),
+            _p(_c(V, np.uint16)), _p(index.assign), _p(index.centroids_bf16), _p(index.vsum), _p(q),
+            n_sink, n_local, topk_frac, k_max, _p(out), _p(lse), _p(ids), _p(kc))
     if rc != 0:
         raise ValueError("ref_decode rejected its arguments (rc=%d)" % rc)
     return out, lse, ids[:, :, :k_max], kc

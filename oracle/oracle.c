@@ -510,11 +510,14 @@ void ref_select(const float* keys, const int32_t* cand, int32_t n, int32_t k, in
  * Inputs: original K, V rows, block-level assignment, chat and vsum of the
  * index, q [B][H][128]. Outputs: out [B][H][128], lse [B][H], ids [B][H][k_max]
  * (rank order, -1 padded). Returns k_b per (b, h) in kcount (nullable).
+ * shared: R is chosen once per kv head by the group key of each cluster (see
+ * ref_decode_shared); the zones of every q head then follow from that R.
  */
 static int decode_impl(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int32_t seg_len, int32_t K_s,
                        const uint16_t* K, const uint16_t* V, const int32_t* assign, const uint16_t* chat,
                        const float* vsum, const uint16_t* q, int32_t n_sink, int32_t n_local, double topk_frac,
-                       int32_t k_max, double* out, double* lse, int32_t* ids, int32_t* kcount, int estimate) {
+                       int32_t k_max, double* out, double* lse, int32_t* ids, int32_t* kcount, int estimate,
+                       int shared) {
   if (B < 1 || G < 1 || H < 1 || H % G != 0 || n_sink < 0 || n_local < 0 || !(topk_frac >= 0.0 && topk_frac <= 1.0))
     return -1;
   seq_base* sb = make_bases(B, G, ctx, seg_len, K_s);
@@ -548,10 +551,19 @@ static int decode_impl(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int3
     int32_t* cand = (int32_t*)malloc(sizeof(int32_t) * (size_t)(C > 0 ? C : 1));
     float* keys = (float*)malloc(sizeof(float) * (size_t)(C > 0 ? C : 1));
     int32_t nE = 0;
+    const int32_t GS = H / G;
     for (int64_t j = 0; j < C; ++j)
       if (np[j] > 0) {
         cand[nE] = (int32_t)j;
-        keys[nE] = ref_rank_key(qh, chat + (clu0 + j) * D);
+        if (!shared) {
+          keys[nE] = ref_rank_key(qh, chat + (clu0 + j) * D);
+        } else {
+          /* group key: the rank keys of the kv head's q heads added in head order in fp32 */
+          float gk = ref_rank_key(q + ((int64_t)b * H + (int64_t)g * GS) * D, chat + (clu0 + j) * D);
+          for (int32_t i = 1; i < GS; ++i)
+            gk = gk + ref_rank_key(q + ((int64_t)b * H + (int64_t)g * GS + i) * D, chat + (clu0 + j) * D);
+          keys[nE] = gk + 0.0f;
+        }
         ++nE;
       }
     int64_t kreq = ref_k_from_frac(topk_frac, C);
@@ -627,7 +639,28 @@ int ref_decode(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int32_t seg_
                int32_t n_sink, int32_t n_local, double topk_frac, int32_t k_max, double* out, double* lse,
                int32_t* ids, int32_t* kcount) {
   return decode_impl(B, H, G, ctx, seg_len, K_s, K, V, assign, chat, vsum, q, n_sink, n_local, topk_frac, k_max, out,
-                     lse, ids, kcount, 1);
+                     lse, ids, kcount, 1, 0);
+}
+
+/*
+ * Wave attention with the retrieval set shared by the q heads of a kv head. The
+ * pages select the clusters most similar to "the current query"; with grouped
+ * query attention every q head of a kv head reads the same clusters, so one
+ * selection per kv head lets them share the retrieved rows. The group's key of
+ * cluster j is its q heads' rank keys r_{h,j} added in fp32 in head order (the
+ * inner product of their summed queries with chat_j, rounded in a fixed order):
+ * R_{b,g} = the k members of E with the largest group keys (ties: lower id), the
+ * same k and E as ref_decode. Every q head then has its own retrieval zone
+ * (exact terms of R's non-steady members), steady zone and estimation zone
+ * (E \ R by its own s_j), exactly as in ref_decode. ids [B][H][k_max] repeat the
+ * group's selection for each of its q heads.
+ */
+int ref_decode_shared(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int32_t seg_len, int32_t K_s,
+                      const uint16_t* K, const uint16_t* V, const int32_t* assign, const uint16_t* chat,
+                      const float* vsum, const uint16_t* q, int32_t n_sink, int32_t n_local, double topk_frac,
+                      int32_t k_max, double* out, double* lse, int32_t* ids, int32_t* kcount) {
+  return decode_impl(B, H, G, ctx, seg_len, K_s, K, V, assign, chat, vsum, q, n_sink, n_local, topk_frac, k_max, out,
+                     lse, ids, kcount, 1, 1);
 }
 
 /*
@@ -645,7 +678,7 @@ int ref_decode_topk(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int32_t
   /* the value sums are not read without the estimation zone; a zero array stands in */
   float* vz = (float*)calloc((size_t)(clusters > 0 ? clusters : 1) * D, sizeof(float));
   int rc = decode_impl(B, H, G, ctx, seg_len, K_s, K, V, assign, chat, vz, q, n_sink, n_local, topk_frac, k_max, out,
-                       lse, ids, kcount, 0);
+                       lse, ids, kcount, 0, 0);
   free(vz);
   return rc;
 }

@@ -582,3 +582,80 @@ def test_decode_topk_only_all_selected_equals_full_attention(n_sink, n_local):
         o, lse, _, _ = oracle.decode_topk(ix, K, V, q, n_sink, n_local, 1.0)
         np.testing.assert_allclose(o, of, rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(lse, lf, rtol=1e-12, atol=1e-12)
+
+
+# -------------------------------------------------- selection shared by a kv head
+def test_decode_shared_one_q_head_per_kv_head_is_decode():
+    # with one q head per kv head the group key is that head's rank key
+    K, V, ctx, idx, q = _setup_decode(H=2, G=2)
+    for frac, ns, nl in [(0.05, 4, 64), (0.2, 0, 0), (0.5, 7, 0)]:
+        a = oracle.decode(idx, K, V, q, ns, nl, frac)
+        s = oracle.decode(idx, K, V, q, ns, nl, frac, shared=True)
+        for x, y in zip(a, s):
+            assert np.array_equal(x, y)
+
+
+def test_decode_shared_equal_q_heads_is_decode():
+    # two equal q heads per kv head: the group key is 2 r (exact), which orders the
+    # clusters as r does, so the selection and every output equal the per-head decode
+    K, V, ctx, idx, q = _setup_decode(H=4, G=2)
+    q2 = q.copy()
+    q2[:, 1] = q2[:, 0]
+    q2[:, 3] = q2[:, 2]
+    for frac, ns, nl in [(0.05, 4, 64), (0.3, 0, 17)]:
+        a = oracle.decode(idx, K, V, q2, ns, nl, frac)
+        s = oracle.decode(idx, K, V, q2, ns, nl, frac, shared=True)
+        for x, y in zip(a, s):
+            assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("n_sink,n_local", [(0, 0), (4, 64)])
+def test_decode_shared_all_and_none(n_sink, n_local):
+    # everything or nothing retrieved: the selection no longer matters
+    K, V, ctx, idx, q = _setup_decode()
+    o, lse, _, _ = oracle.decode(idx, K, V, q, n_sink, n_local, 1.0, shared=True)
+    of, lf = oracle.full_attention(K, V, q, idx.G, ctx)
+    np.testing.assert_allclose(o, of, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, lf, rtol=1e-12, atol=1e-12)
+    a = oracle.decode(idx, K, V, q, n_sink, n_local, 0.0)
+    s = oracle.decode(idx, K, V, q, n_sink, n_local, 0.0, shared=True)
+    for x, y in zip(a, s):
+        assert np.array_equal(x, y)
+
+
+def test_decode_shared_selection_is_top_k_of_summed_queries():
+    # the group key equals (sum of the group's q) . chat_j up to the fp32 rounding of the
+    # rank keys and of their sum (below 2^-20 of sum_h |q_h| |chat_j| here); so the selected
+    # clusters' binary64 group scores are, up to that bound, the k largest over E, in
+    # descending order, and every q head of a kv head has the same ids
+    K, V, ctx, idx, q = _setup_decode(H=8, G=2)
+    ns, nl, frac = 4, 64, 0.1
+    _, _, ids, kc = oracle.decode(idx, K, V, q, ns, nl, frac, shared=True)
+    H = q.shape[1]
+    GS = H // idx.G
+    row = clu = 0
+    for b, N in enumerate(ctx):
+        C = int(idx.C[b])
+        for g in range(idx.G):
+            hs = list(range(g * GS, (g + 1) * GS))
+            for h in hs[1:]:
+                assert ids[b, h].tolist() == ids[b, hs[0]].tolist() and kc[b, h] == kc[b, hs[0]]
+            a = idx.assign[row + g * N: row + (g + 1) * N]
+            t = np.arange(N)
+            elig = np.unique(a[~((t < ns) | (t >= N - nl))])
+            qf = oracle.bf16_to_f32(q[b, hs]).astype(np.float64)
+            ch = oracle.bf16_to_f32(idx.centroids_bf16[clu + g * C: clu + (g + 1) * C]).astype(np.float64)
+            score = ch[elig] @ qf.sum(0)
+            bound = 2.0 ** -20 * (np.abs(ch[elig]) @ np.abs(qf).sum(0))
+            k = min(oracle.k_from_frac(frac, C), len(elig))
+            assert kc[b, hs[0]] == k
+            sel = ids[b, hs[0], :k]
+            pos = {j: i for i, j in enumerate(elig.tolist())}
+            si = np.array([pos[j] for j in sel.tolist()])
+            rest = np.setdiff1d(np.arange(len(elig)), si)
+            assert len(set(sel.tolist())) == k
+            if len(rest):
+                assert np.all(score[si] + bound[si] >= score[rest].max() - bound[rest].max())
+            assert np.all(score[si][:-1] + bound[si][:-1] >= score[si][1:] - bound[si][1:])
+        row += idx.G * N
+        clu += idx.G * C
