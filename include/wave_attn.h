@@ -170,6 +170,26 @@ wave_status wave_attn_decode(const wave_index* index, const void* q, int32_t n_q
                              size_t ws_bytes, wave_stream_t stream);
 
 /*
+ * wave_attn_decode_shared -- wave attention with one retrieval set per kv head.
+ * The RetroInfer page (section 2.A) retrieves the clusters most similar to the
+ * query; under grouped-query attention the q heads of a kv head read the same
+ * key/value rows, and the Vortex summary (section A) names GQA backends as the
+ * attention it routes to. Here the q heads of kv head g choose their clusters
+ * together: the group key of cluster j is the rank keys of g's q heads (as in
+ * wave_attn_decode) added in fp32 in head order, and R_{b,g} = the k_b members
+ * of E with the largest group keys (ties: lower id), with S, E and k_b as in
+ * wave_attn_decode. Each q head then attends exactly to the steady tokens and
+ * to the non-steady members of R_{b,g}, and estimates E \ R_{b,g} from its own
+ * centroid scores; sel_ids repeats R_{b,g} for every q head of g. The q heads
+ * of a kv head read the same rows, which their workgroups share through the
+ * L2 cache. Arguments, workspace (wave_attn_decode_plan) and errors as
+ * wave_attn_decode.
+ */
+wave_status wave_attn_decode_shared(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
+                                    int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse,
+                                    void* ws, size_t ws_bytes, wave_stream_t stream);
+
+/*
  * wave_index_build_blocks -- the index of the block top-k baseline (Vortex
  * technical summary, section A, vFlow: a query-independent phase summarises
  * fixed blocks of the KV cache by their centroids; the query-dependent phase

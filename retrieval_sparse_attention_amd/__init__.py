@@ -67,6 +67,7 @@ def lib():
                                             ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_size_t)]
         L.wave_attn_decode.argtypes = [ctypes.POINTER(_Index), P, i32, i32, i32, ctypes.c_double, P, P, P, P, sz, P]
         L.wave_attn_decode_topk.argtypes = L.wave_attn_decode.argtypes
+        L.wave_attn_decode_shared.argtypes = L.wave_attn_decode.argtypes
         L.wave_index_build_blocks.argtypes = [ctypes.POINTER(_Shape), P, P, i32, i32, ctypes.POINTER(_Index), P, sz,
                                               P]
         L.wave_last_error.restype = ctypes.c_char_p
@@ -74,7 +75,8 @@ def lib():
         L.wave_profiler_read.argtypes = [ctypes.c_char_p, P, P, i32]
         L.wave_profiler_read.restype = i32
         for f in ("wave_index_plan", "wave_index_build", "wave_attn_decode_plan", "wave_attn_decode",
-                  "wave_profiler_enable", "wave_index_build_blocks", "wave_attn_decode_topk"):
+                  "wave_profiler_enable", "wave_index_build_blocks", "wave_attn_decode_topk",
+                  "wave_attn_decode_shared"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -195,10 +197,12 @@ def wave_attn_decode_plan(index, n_q_heads, n_sink, n_local, topk_frac):
 
 
 def wave_attn_decode(index, q, n_sink, n_local, topk_frac, ws=None, out=None, sel_ids=None, lse=None,
-                     stream=None, estimate=True):
+                     stream=None, estimate=True, shared=False):
     """One decode query per (sequence, q head): q bf16 [B, H, 128] on the device.
 
     Returns (out fp32 [B, H, 128], sel_ids int32 [B, H, k_max], lse fp32 [B, H]).
+    estimate=False: top-k retrieval only (wave_attn_decode_topk); shared=True: one
+    selection per kv head (wave_attn_decode_shared).
     """
     B, H = q.shape[0], q.shape[1]
     k_max, wsb = wave_attn_decode_plan(index, H, n_sink, n_local, topk_frac)
@@ -211,7 +215,9 @@ def wave_attn_decode(index, q, n_sink, n_local, topk_frac, ws=None, out=None, se
         sel_ids = torch.empty((B, H, max(k_max, 1)), dtype=torch.int32, device=dev)
     if lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
-    fn = lib().wave_attn_decode if estimate else lib().wave_attn_decode_topk
+    if shared and not estimate:
+        raise ValueError("the shared selection is a variant of wave attention (estimate=True)")
+    fn = lib().wave_attn_decode_shared if shared else (lib().wave_attn_decode if estimate else lib().wave_attn_decode_topk)
     _check(fn(ctypes.byref(index.c), _ptr(q), H, int(n_sink), int(n_local), float(topk_frac), _ptr(out), _ptr(sel_ids),
               _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
     return out, sel_ids[:, :, :k_max], lse
@@ -221,6 +227,12 @@ def wave_attn_decode_topk(index, q, n_sink, n_local, topk_frac, ws=None, out=Non
                           stream=None):
     """Top-k retrieval without the estimation zone (the block baseline's decode); as wave_attn_decode."""
     return wave_attn_decode(index, q, n_sink, n_local, topk_frac, ws, out, sel_ids, lse, stream, estimate=False)
+
+
+def wave_attn_decode_shared(index, q, n_sink, n_local, topk_frac, ws=None, out=None, sel_ids=None, lse=None,
+                            stream=None):
+    """Wave attention with one retrieval set per kv head (group key); as wave_attn_decode."""
+    return wave_attn_decode(index, q, n_sink, n_local, topk_frac, ws, out, sel_ids, lse, stream, shared=True)
 
 
 def wave_profiler_enable(on=True):

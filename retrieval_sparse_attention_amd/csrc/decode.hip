@@ -174,7 +174,14 @@ __global__ __launch_bounds__(SCORE_THREADS) void k_score(SeqArgs sa, DecodeArgs 
     }
   }
   lds_barrier();
-  // 3. keys and eligibility out
+  // 3. keys and eligibility out. Selection shared by the kv head: the sortable keys are the
+  // group keys (the q heads' rank keys added in head order in fp32), in the first q head's slot.
+  auto group_key = [&](int jj) {
+    float s = S.kw[0][jj];
+#pragma unroll
+    for (int hh = 1; hh < GS; ++hh) s = s + S.kw[hh][jj];
+    return s + 0.0f;
+  };
   const int64_t kb = (int64_t)GS * sb.clu + (int64_t)g * GS * C + j0;
   for (int e = tid; e < GS * SC; e += SCORE_THREADS) {
     const int hh = e / SC, jj = e % SC;
@@ -183,14 +190,18 @@ __global__ __launch_bounds__(SCORE_THREADS) void k_score(SeqArgs sa, DecodeArgs 
       const int n = S.nsz[jj];
       const bool elig = !sz.all && n > 0 && S.scnt[jj] < n;
       ws.keys[kb + (int64_t)hh * C + jj] = key;
-      ws.key32[kb + (int64_t)hh * C + jj] = elig ? float_sortable(key) : 0u;
+      if (!da.shared)
+        ws.key32[kb + (int64_t)hh * C + jj] = elig ? float_sortable(key) : 0u;
+      else if (hh == 0)
+        ws.key32[kb + jj] = elig ? float_sortable(group_key(jj)) : 0u;
     }
   }
   // per q head (a wave each): the chunk's 4 largest sortable keys (a multiset) and its
   // eligible count, from which the top-k takes a threshold when its keys do not fit
   // registers (da.NV == 0)
   const int chm = da.NP - da.P;
-  for (int hh = wv; da.NV == 0 && hh < GS; hh += SCORE_THREADS / 64) {
+  const int nsel = da.shared ? 1 : GS;  // rows of sortable keys
+  for (int hh = wv; da.NV == 0 && hh < nsel; hh += SCORE_THREADS / 64) {
     uint32_t u[2];
     int ne = 0;
 #pragma unroll
@@ -198,7 +209,7 @@ __global__ __launch_bounds__(SCORE_THREADS) void k_score(SeqArgs sa, DecodeArgs 
       const int jj = lane + 64 * r;
       const int n = jj < nc ? S.nsz[jj] : 0;
       const bool elig = jj < nc && !sz.all && n > 0 && S.scnt[jj] < n;
-      u[r] = elig ? float_sortable(S.kw[hh][jj]) : 0u;
+      u[r] = elig ? float_sortable(da.shared ? group_key(jj) : S.kw[hh][jj]) : 0u;
       ne += elig;
     }
 #pragma unroll
@@ -478,9 +489,12 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
   const int64_t clu0 = sb.clu + (int64_t)g * C;
   const int64_t off0 = sb.off + (int64_t)g * (C + 1);
   const int64_t kbase = (int64_t)da.GS * sb.clu + (int64_t)h * C;
+  // sortable keys of the selection: the head's own, or its kv head's group keys (first q head's slot)
+  const int hs = da.shared ? g * da.GS : h;
+  const int64_t bhs = (int64_t)b * da.H + hs;
   const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wv = tid >> 6;
   const uint64_t ltmask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const uint32_t* key32 = ws.key32 + kbase;
+  const uint32_t* key32 = ws.key32 + (int64_t)da.GS * sb.clu + (int64_t)hs * C;
   const float* keys = ws.keys + kbase;
   int2* span = ws.span + kbase;
   float* skey = ws.skey + kbase;
@@ -575,7 +589,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
   } else {
     // eligible keys from k_score's chunk summaries (thread t adds chunks t, t + TK_THREADS, ...)
     const int nch = (C + SC - 1) / SC;
-    const uint32_t* ct = ws.ctop + (int64_t)bh * (da.NP - da.P) * 8;
+    const uint32_t* ct = ws.ctop + bhs * (da.NP - da.P) * 8;
     int e = 0;
     for (int i = tid; i < nch; i += nt) e += (int)ct[(int64_t)i * 8 + 4];
 #pragma unroll
@@ -690,7 +704,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
           const int n = (int)r.z, pre = L.u.c.pre[ci];
           out[rank] = id;
           span[rank] = make_int2((int)r.w, n);
-          skey[rank] = sortable_float(r.y);
+          skey[rank] = da.shared ? keys[id] : sortable_float(r.y);  // the head's own rank key
           selpre[rank] = pre;
           atomicOr(&L.selw[id >> 5], 1u << (id & 31));
           if (rank == k - 1) {
@@ -708,7 +722,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
   bool done = false;
   if constexpr (!INREG) {
     const int nch = (C + SC - 1) / SC;
-    const uint32_t* ct = ws.ctop + (int64_t)bh * (da.NP - da.P) * 8;
+    const uint32_t* ct = ws.ctop + bhs * (da.NP - da.P) * 8;
     if (k > 0 && k <= 4 * nch && nch <= TK_THREADS) {
       uint32_t tv[4];
 #pragma unroll

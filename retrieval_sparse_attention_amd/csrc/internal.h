@@ -22,6 +22,7 @@ struct DecodeArgs {
   int32_t sort_stride;    // per-(b, h) entries of the global sort buffer
   int32_t NVg;            // keys per lane when NV == 0 (a multiple of 16)
   int32_t est;            // 1: the estimation zone (wave attention); 0: top-k retrieval only
+  int32_t shared;         // 1: one selection per kv head, by the sum of its q heads' rank keys
   int32_t kreq[MAXB];     // min(ceil(topk_frac * C_b), C_b), binary64 on the host
 };
 

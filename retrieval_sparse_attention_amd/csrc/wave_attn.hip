@@ -346,11 +346,12 @@ wave_status wave_attn_decode_plan(const wave_index* index, int32_t n_q_heads, in
 
 static wave_status decode_call(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
                                int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse, void* ws,
-                               size_t ws_bytes, wave_stream_t stream, int est) {
+                               size_t ws_bytes, wave_stream_t stream, int est, int shared) {
   DecodePlan P;
   wave_status st = decode_plan(index, n_q_heads, n_sink, n_local, topk_frac, &P);
   if (st != WAVE_OK) return st;
   P.da.est = est;
+  P.da.shared = shared;
   if (q == nullptr || out == nullptr || ws == nullptr) return fail(WAVE_ERR_ARG, "q, out and ws must be non-NULL");
   if (P.da.k_max > 0 && sel_ids == nullptr) return fail(WAVE_ERR_ARG, "sel_ids is NULL but k_max = %d", P.da.k_max);
   const void* ptrs[] = {index->k_sorted, index->v_sorted, index->perm, index->inv_perm, index->assign,
@@ -388,13 +389,19 @@ static wave_status decode_call(const wave_index* index, const void* q, int32_t n
 wave_status wave_attn_decode(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
                              int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse, void* ws,
                              size_t ws_bytes, wave_stream_t stream) {
-  return decode_call(index, q, n_q_heads, n_sink, n_local, topk_frac, out, sel_ids, lse, ws, ws_bytes, stream, 1);
+  return decode_call(index, q, n_q_heads, n_sink, n_local, topk_frac, out, sel_ids, lse, ws, ws_bytes, stream, 1, 0);
+}
+
+wave_status wave_attn_decode_shared(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
+                                    int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse,
+                                    void* ws, size_t ws_bytes, wave_stream_t stream) {
+  return decode_call(index, q, n_q_heads, n_sink, n_local, topk_frac, out, sel_ids, lse, ws, ws_bytes, stream, 1, 1);
 }
 
 wave_status wave_attn_decode_topk(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
                                   int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse,
                                   void* ws, size_t ws_bytes, wave_stream_t stream) {
-  return decode_call(index, q, n_q_heads, n_sink, n_local, topk_frac, out, sel_ids, lse, ws, ws_bytes, stream, 0);
+  return decode_call(index, q, n_q_heads, n_sink, n_local, topk_frac, out, sel_ids, lse, ws, ws_bytes, stream, 0, 0);
 }
 
 wave_status wave_profiler_enable(int32_t on) {

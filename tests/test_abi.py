@@ -22,7 +22,7 @@ def _declared():
 def test_exports_every_declared_symbol():
     names = _declared()
     assert {"wave_index_plan", "wave_index_build", "wave_attn_decode_plan", "wave_attn_decode",
-            "wave_last_error"} <= set(names)
+            "wave_last_error", "wave_attn_decode_shared"} <= set(names)
     L = rsa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -188,3 +188,10 @@ def test_calls_fail_cleanly_without_device():
     bad = list(dargs)
     bad[6] = None
     assert L.wave_attn_decode_topk(*bad) == ARG
+    assert L.wave_attn_decode_shared(*dargs) == HIP
+    bad = list(dargs)
+    bad[10] = w - 1
+    assert L.wave_attn_decode_shared(*bad) == WS
+    bad = list(dargs)
+    bad[2] = 7  # not a multiple of the 2 kv heads
+    assert L.wave_attn_decode_shared(*bad) == SHAPE
