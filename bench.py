@@ -13,7 +13,8 @@ live in HBM at distinct addresses; step i rebuilds layer i mod L and its 64 quer
 the layers round robin, so no decode reuses the 256 MB Infinity Cache.
 
 `--workload` runs one of the method's other workloads instead (16k, 1m, batched: decode
-steps/s of the whole job; stress: index-build tokens/s of the clustering on 1M heavy-tailed
+steps/s of the whole job; blocks: the block top-k baseline; shared: the 128K layer with one
+retrieval set per kv head; stress: index-build tokens/s of the clustering on 1M heavy-tailed
 keys per kv head); the default line is the 128K one.
 """
 import argparse
@@ -54,6 +55,8 @@ WORKLOADS = {
     # the block top-k baseline on the 128K layer: contiguous blocks of 16 tokens instead of the
     # k-means clusters and no estimation zone (a same-hardware comparison point)
     "blocks": dict(WORKLOAD, workload="block-topk-baseline-128k", blocks=True, kmeans_iters=0),
+    # the 128K layer with one retrieval set per kv head (wave_attn_decode_shared)
+    "shared": dict(WORKLOAD, workload="llama3-8b-attention-layer-128k-shared-selection", shared=True),
     "stress": dict(workload="index-build-1m-keys-student-t", batch=1, q_heads=8, kv_heads=8, head_dim=128,
                    ctx=1048576, seg_len=8192, clusters_per_seg=512, kmeans_iters=10, heavy_tailed=True,
                    n_sink=4, n_local=64, topk_frac=0.02, decode_queries_per_step=0, layers=1, seed_data=5,
@@ -199,8 +202,9 @@ def accuracy(dev):
     uniformly drawn key), 16 queries per q head. For each clusters_per_seg, topk_frac and
     n_local: relative L2 error |o - o_dense| / |o_dense| per (query, q head) (mean, 90th
     percentile, maximum) and the share of tokens read exactly (retrieved plus steady), for
-    the wave attention over the k-means index, the same selection without the estimation
-    zone, and the block top-k baseline (contiguous blocks, no estimation). The dense
+    the wave attention over the k-means index, the same with one selection per kv head
+    (wave-shared), the same selection without the estimation zone, and the block top-k
+    baseline (contiguous blocks, no estimation). The dense
     reference is float32 softmax attention in PyTorch over all N keys.
     """
     import numpy as np
@@ -232,7 +236,8 @@ def accuracy(dev):
     # the wave attention over the k-means index at every budget; for a local window of 64 also
     # the same selection without the estimation zone, and the block top-k baseline (contiguous
     # blocks, no estimation)
-    runs = [("wave", False, True, nl) for nl in (0, 64, 512)] + [("kmeans-topk-only", False, False, 64),
+    runs = [("wave", False, True, nl) for nl in (0, 64, 512)] + [("wave-shared", False, True, 64),
+                                                                  ("kmeans-topk-only", False, False, 64),
                                                                   ("block-topk", True, False, 64)]
     for ks in (256, 512, 1024):
         kidx = rsa.wave_index_build(Kd, Vd, G, [N], seg, ks, iters, W["seed_build"])
@@ -244,7 +249,8 @@ def accuracy(dev):
             for frac in (0.005, 0.01, 0.02, 0.05, 0.1):
                 err, exact = [], []
                 for t in range(nq):
-                    o, ids, _ = rsa.wave_attn_decode(idx, qd[t], ns, nl, frac, estimate=estimate)
+                    o, ids, _ = rsa.wave_attn_decode(idx, qd[t], ns, nl, frac, estimate=estimate,
+                                                     shared=method == "wave-shared")
                     e = (o[0] - ref[t]).norm(dim=1) / ref[t].norm(dim=1)
                     err.append(e.cpu().numpy())
                     ih = ids[0].cpu().numpy()
@@ -311,6 +317,7 @@ def main():
     ns, nl, frac, QPS = W["n_sink"], W["n_local"], W["topk_frac"], W["decode_queries_per_step"]
     L = W["layers"]
     blocks = W.get("blocks", False)
+    shared = W.get("shared", False)
     if isinstance(W["ctx"], list):  # ragged: N_b ~ U{lo..hi} from the data seed
         ctx = synth.ctx_lengths(W["seed_data"], B, W["ctx"][0], W["ctx"][1])
     else:
@@ -358,7 +365,7 @@ def main():
             qi = (step * QPS + s) % nq
             ids = ids_log[s] if ids_log is not None else ids_buf
             rsa.wave_attn_decode(idxs[lay], qd[qi], ns, nl, frac, ws=dws, out=out, sel_ids=ids, lse=lse,
-                                 estimate=not blocks)
+                                 estimate=not blocks, shared=shared)
 
     # the step pattern repeats with period P: one captured HIP graph per phase
     P = math.lcm(L, max(1, nq // math.gcd(nq, max(QPS, 1))))
@@ -439,7 +446,9 @@ def main():
                     sel = ids_h[qq, b, h]
                     sel = sel[sel >= 0]
                     n_sel += len(sel)
-                    retrieved_rows += int(sizes[cbase[b] + (h * G // H) * Cb[b] + sel].sum())
+                    # a shared selection's rows are read once for the kv head's q heads
+                    if not shared or h % (H // G) == 0:
+                        retrieved_rows += int(sizes[cbase[b] + (h * G // H) * Cb[b] + sel].sum())
     rows_per_dec = retrieved_rows / max(nq_t, 1)
     sel_per_dec = n_sel / max(nq_t, 1)             # clusters selected per decode call, all (b, h)
     # algorithmic HBM bytes per launch: every byte a kernel must read or write once
@@ -461,7 +470,8 @@ def main():
                   + sel_per_dec * (4 + 8 + 4 + 4)  # ids, spans, keys, member prefix out
                   + B * H * steady * 8)           # steady rows: cluster ids in, corrections out
     attend_bytes = (rows_per_dec * (2 * 128 * 2 + 4)         # K, V and perm of the retrieved rows
-                    + B * H * steady * (2 * 128 * 2 + 4 + 4)  # steady rows: K, V, inv_perm, correction
+                    + B * G * steady * (2 * 128 * 2 + 4)      # steady rows (a kv head's): K, V, inv_perm
+                    + B * H * steady * 4                      # their corrections per q head
                     + sel_per_dec * 16                        # window metadata
                     + B * H * 128 * 2 + B * H * P * part)     # q, row partials out
     if not blocks:
@@ -592,7 +602,7 @@ def cpu_baseline(W, K, V, ctx, q, budget_s):
     t2 = time.time()
     n_dec = 0
     while n_dec < min(q.shape[0], W["decode_queries_per_step"]) and (n_dec == 0 or time.time() - t2 < 0.5 * budget_s):
-        oracle.decode(idx, K, V, q[n_dec], W["n_sink"], W["n_local"], W["topk_frac"])
+        oracle.decode(idx, K, V, q[n_dec], W["n_sink"], W["n_local"], W["topk_frac"], shared=W.get("shared", False))
         n_dec += 1
     t_dec = (time.time() - t2) / n_dec
     step_s = units_total * t_unit + t_layout + W["decode_queries_per_step"] * t_dec
