@@ -349,18 +349,27 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
   // A fragments live in the accumulation registers (AGPRs), which the MFMA reads as
   // its A operand directly; the architectural VGPRs hold accumulators, B fragments and
   // the selection. The empty asm only fixes the register class of its tied operand.
+  // All 32 loads are issued before the first move into the accumulation registers: moved
+  // one by one, each load waited for its own round trip (32 serial round trips, 13 us of
+  // a 128K launch).
   u32x4 A[4][8];
   floatx16 nh[4];
   auto load_a = [&](int grp) {
     const int cb = grp * AS_GROUP + wv * AS_CPW;
+    u32x4 ld[4][8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = cb + r * 32 + col;
-      const int rc = min(row, U.Kc - 1);
+      const int rc = min(cb + r * 32 + col, U.Kc - 1);
+#pragma unroll
+      for (int st = 0; st < 8; ++st)
+        ld[r][st] = *reinterpret_cast<const u32x4*>(chat + (U.gclu + rc) * D + (2 * st + h) * 8);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const bool in = cb + r * 32 + col < U.Kc;
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(chat + (U.gclu + rc) * D + (2 * st + h) * 8);
-        const u32x4 z = row < U.Kc ? v : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 z = in ? ld[r][st] : u32x4{0u, 0u, 0u, 0u};
         asm volatile("" : "=a"(A[r][st]) : "0"(z));
       }
     }
