@@ -62,6 +62,9 @@ def _load():
         lib.ref_decode.argtypes = [i32, i32, i32, P, i32, i32, P, P, P, P, P, P, i32, i32, f64, i32, P, P, P, P]
         lib.ref_decode.restype = ctypes.c_int
         lib.ref_decode_shared.argtypes = lib.ref_decode.argtypes
+        lib.ref_decode_tail.argtypes = [i32, i32, i32, P, i32, i32, P, P, P, P, P, P, i32, i32, f64, P, P, i32, P,
+                                        i32, P, P, P, P]
+        lib.ref_decode_tail.restype = ctypes.c_int
         lib.ref_decode_shared.restype = ctypes.c_int
         lib.ref_decode_topk.argtypes = [i32, i32, i32, P, i32, i32, P, P, P, P, P, i32, i32, f64, i32, P, P, P, P]
         lib.ref_decode_topk.restype = ctypes.c_int
@@ -240,6 +243,30 @@ def decode(index, K, V, q, n_sink, n_local, topk_frac, k_max=None, shared=False)
             n_sink, n_local, topk_frac, k_max, _p(out), _p(lse), _p(ids), _p(kc))
     if rc != 0:
         raise ValueError("ref_decode rejected its arguments (rc=%d)" % rc)
+    return out, lse, ids[:, :, :k_max], kc
+
+
+def decode_tail(index, K, V, q, n_sink, n_local, topk_frac, Kt, Vt, tail_len, k_max=None):
+    """Wave-index decode plus the tokens appended after the build (exact): Kt, Vt [B][G][cap][128] bf16 bits,
+    tail_len [B] <= cap. Returns as decode()."""
+    q = _c(q, np.uint16)
+    B, H = q.shape[0], q.shape[1]
+    Kt = _c(Kt, np.uint16)
+    Vt = _c(Vt, np.uint16)
+    cap = Kt.shape[2]
+    tl = _c(np.asarray(tail_len), np.int32)
+    if k_max is None:
+        k_max = decode_k_max(index.C, topk_frac)
+    out = np.empty((B, H, D), np.float64)
+    lse = np.empty((B, H), np.float64)
+    ids = np.empty((B, H, max(k_max, 1)), np.int32)
+    kc = np.empty((B, H), np.int32)
+    rc = _load().ref_decode_tail(B, H, index.G, _p(index.ctx), index.seg_len, index.K_s, _p(_c(K, np.uint16)),
+                                 _p(_c(V, np.uint16)), _p(index.assign), _p(index.centroids_bf16), _p(index.vsum),
+                                 _p(q), n_sink, n_local, topk_frac, _p(Kt), _p(Vt), cap, _p(tl), k_max, _p(out),
+                                 _p(lse), _p(ids), _p(kc))
+    if rc != 0:
+        raise ValueError("ref_decode_tail rejected its arguments (rc=%d)" % rc)
     return out, lse, ids[:, :, :k_max], kc
 
 

@@ -517,7 +517,8 @@ static int decode_impl(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int3
                        const uint16_t* K, const uint16_t* V, const int32_t* assign, const uint16_t* chat,
                        const float* vsum, const uint16_t* q, int32_t n_sink, int32_t n_local, double topk_frac,
                        int32_t k_max, double* out, double* lse, int32_t* ids, int32_t* kcount, int estimate,
-                       int shared) {
+                       int shared, const uint16_t* Kt, const uint16_t* Vt, int32_t tail_cap,
+                       const int32_t* tail_len) {
   if (B < 1 || G < 1 || H < 1 || H % G != 0 || n_sink < 0 || n_local < 0 || !(topk_frac >= 0.0 && topk_frac <= 1.0))
     return -1;
   seq_base* sb = make_bases(B, G, ctx, seg_len, K_s);
@@ -592,6 +593,16 @@ static int decode_impl(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int3
         if (st[t] > m) m = st[t];
       }
     }
+    /* tokens appended after the index was built: exact, like the steady zone */
+    const int64_t nT = Kt ? tail_len[b] : 0;
+    const int64_t trow0 = ((int64_t)b * G + g) * tail_cap;
+    double* tt = (double*)malloc(sizeof(double) * (size_t)(nT > 0 ? nT : 1));
+    for (int64_t t = 0; t < nT; ++t) {
+      double s = 0.0;
+      for (int i = 0; i < D; ++i) s += qd[i] * (double)ref_bf16_to_f32(Kt[(trow0 + t) * D + i]);
+      tt[t] = tau * s;
+      if (tt[t] > m) m = tt[t];
+    }
     double* sj = (double*)malloc(sizeof(double) * (size_t)(C > 0 ? C : 1));
     for (int64_t j = 0; j < C; ++j) {
       if (estimate && np[j] > 0 && !inR[j]) {
@@ -618,6 +629,12 @@ static int decode_impl(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int3
         for (int i = 0; i < D; ++i) num[i] += w * vs[j * D + i];
       }
     }
+    for (int64_t t = 0; t < nT; ++t) {
+      double w = exp(tt[t] - m);
+      den += w;
+      for (int i = 0; i < D; ++i) num[i] += w * (double)ref_bf16_to_f32(Vt[(trow0 + t) * D + i]);
+    }
+    free(tt);
     for (int i = 0; i < D; ++i) out[bh * D + i] = num[i] / den;
     if (lse) lse[bh] = m + log(den);
     free(sj);
@@ -639,7 +656,28 @@ int ref_decode(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int32_t seg_
                int32_t n_sink, int32_t n_local, double topk_frac, int32_t k_max, double* out, double* lse,
                int32_t* ids, int32_t* kcount) {
   return decode_impl(B, H, G, ctx, seg_len, K_s, K, V, assign, chat, vsum, q, n_sink, n_local, topk_frac, k_max, out,
-                     lse, ids, kcount, 1, 0);
+                     lse, ids, kcount, 1, 0, NULL, NULL, 0, NULL);
+}
+
+/*
+ * Wave attention over an index plus the tokens appended after it was built (the
+ * RetroInfer page, section 2.A: the steady zone keeps the recent tokens exact, and
+ * the index is built segment by segment, so decoded tokens wait in the recent window
+ * until they fill a segment). Sequence b has tail_len[b] <= tail_cap such tokens, K/V
+ * rows Kt, Vt [B][G][tail_cap][128] (bf16), positions N_b, N_b + 1, ...; every one is
+ * attended exactly, next to ref_decode's three zones over the N_b indexed tokens
+ * (whose steady zone is still the first n_sink and the last n_local of them).
+ */
+int ref_decode_tail(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int32_t seg_len, int32_t K_s,
+                    const uint16_t* K, const uint16_t* V, const int32_t* assign, const uint16_t* chat,
+                    const float* vsum, const uint16_t* q, int32_t n_sink, int32_t n_local, double topk_frac,
+                    const uint16_t* Kt, const uint16_t* Vt, int32_t tail_cap, const int32_t* tail_len,
+                    int32_t k_max, double* out, double* lse, int32_t* ids, int32_t* kcount) {
+  if (!Kt || !Vt || !tail_len || tail_cap < 0) return -1;
+  for (int32_t b = 0; b < B; ++b)
+    if (tail_len[b] < 0 || tail_len[b] > tail_cap) return -1;
+  return decode_impl(B, H, G, ctx, seg_len, K_s, K, V, assign, chat, vsum, q, n_sink, n_local, topk_frac, k_max, out,
+                     lse, ids, kcount, 1, 0, Kt, Vt, tail_cap, tail_len);
 }
 
 /*
@@ -660,7 +698,7 @@ int ref_decode_shared(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int32
                       const float* vsum, const uint16_t* q, int32_t n_sink, int32_t n_local, double topk_frac,
                       int32_t k_max, double* out, double* lse, int32_t* ids, int32_t* kcount) {
   return decode_impl(B, H, G, ctx, seg_len, K_s, K, V, assign, chat, vsum, q, n_sink, n_local, topk_frac, k_max, out,
-                     lse, ids, kcount, 1, 1);
+                     lse, ids, kcount, 1, 1, NULL, NULL, 0, NULL);
 }
 
 /*
@@ -678,7 +716,7 @@ int ref_decode_topk(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int32_t
   /* the value sums are not read without the estimation zone; a zero array stands in */
   float* vz = (float*)calloc((size_t)(clusters > 0 ? clusters : 1) * D, sizeof(float));
   int rc = decode_impl(B, H, G, ctx, seg_len, K_s, K, V, assign, chat, vz, q, n_sink, n_local, topk_frac, k_max, out,
-                       lse, ids, kcount, 0, 0);
+                       lse, ids, kcount, 0, 0, NULL, NULL, 0, NULL);
   free(vz);
   return rc;
 }

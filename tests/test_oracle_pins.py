@@ -659,3 +659,84 @@ def test_decode_shared_selection_is_top_k_of_summed_queries():
             assert np.all(score[si][:-1] + bound[si][:-1] >= score[si][1:] - bound[si][1:])
         row += idx.G * N
         clu += idx.G * C
+
+
+# ------------------------------------------- tokens appended after the index was built
+def _split_tail(Kf, Vf, ctx_full, tail, G, cap):
+    """Split [b][g][t] rows of ctx_full into the first ctx_full - tail tokens of every (b, g)
+    (index input) and the rest as tails [B][G][cap][128] (zero padded)."""
+    B = len(ctx_full)
+    ctx_idx = np.array([n - t for n, t in zip(ctx_full, tail)], np.int64)
+    Ki, Vi, Kt, Vt = [], [], np.zeros((B, G, cap, D), np.uint16), np.zeros((B, G, cap, D), np.uint16)
+    row = 0
+    for b, (N, T) in enumerate(zip(ctx_full, tail)):
+        for g in range(G):
+            r = row + g * N
+            Ki.append(Kf[r:r + N - T])
+            Vi.append(Vf[r:r + N - T])
+            Kt[b, g, :T] = Kf[r + N - T:r + N]
+            Vt[b, g, :T] = Vf[r + N - T:r + N]
+        row += G * N
+    return np.concatenate(Ki), np.concatenate(Vi), ctx_idx, Kt, Vt
+
+
+def _tail_setup(tail=(40, 0), cap=64, seed=41):
+    G, H, seg, K_s = 2, 4, 1024, 64
+    ctx_full = np.array([3000 + tail[0], 1700 + tail[1]], np.int64)
+    Kf, Vf, _ = synth.kv(seed, 2, G, ctx_full, seg)
+    Ki, Vi, ctx, Kt, Vt = _split_tail(Kf, Vf, ctx_full, tail, G, cap)
+    idx = oracle.build(Ki, Vi, G, ctx, seg, K_s, 3, 1234)
+    q, _ = synth.queries(seed + 1, 1, 2, H, G, ctx_full, Kf)
+    return Kf, Vf, ctx_full, Ki, Vi, ctx, Kt, Vt, idx, q[0]
+
+
+def test_decode_tail_empty_is_decode():
+    Kf, Vf, cf, Ki, Vi, ctx, Kt, Vt, idx, q = _tail_setup()
+    a = oracle.decode(idx, Ki, Vi, q, 4, 64, 0.05)
+    t = oracle.decode_tail(idx, Ki, Vi, q, 4, 64, 0.05, Kt, Vt, [0, 0])
+    for x, y in zip(a, t):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("frac,ns,nl", [(1.0, 4, 64), (1.0, 0, 0), (0.05, 1500, 1500)])
+def test_decode_tail_everything_exact_is_full_attention(frac, ns, nl):
+    # every indexed token exact (all clusters retrieved, or all steady) and the tail exact:
+    # dense attention over the indexed tokens followed by the appended ones
+    Kf, Vf, cf, Ki, Vi, ctx, Kt, Vt, idx, q = _tail_setup(tail=(40, 7))
+    o, lse, _, _ = oracle.decode_tail(idx, Ki, Vi, q, ns, nl, frac, Kt, Vt, [40, 7])
+    of, lf = oracle.full_attention(Kf, Vf, q, idx.G, cf)
+    np.testing.assert_allclose(o, of, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, lf, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_tail_estimation_only_closed_form():
+    # topk_frac = 0, no steady tokens: the centroid terms of every cluster plus the exact tail
+    Kf, Vf, cf, Ki, Vi, ctx, Kt, Vt, idx, q = _tail_setup(tail=(33, 64))
+    tl = [33, 64]
+    o, lse, _, _ = oracle.decode_tail(idx, Ki, Vi, q, 0, 0, 0.0, Kt, Vt, tl)
+    clu = 0
+    for b, N in enumerate(ctx):
+        C = int(idx.C[b])
+        for h in range(q.shape[1]):
+            g = h * idx.G // q.shape[1]
+            cs = slice(clu + g * C, clu + (g + 1) * C)
+            n = idx.sizes[cs].astype(np.float64)
+            qf = oracle.bf16_to_f32(q[b, h]).astype(np.float64)
+            chat = oracle.bf16_to_f32(idx.centroids_bf16[cs]).astype(np.float64)
+            s = np.where(n > 0, chat @ qf / math.sqrt(D), -np.inf)
+            kt = oracle.bf16_to_f32(Kt[b, g, :tl[b]]).astype(np.float64)
+            vt = oracle.bf16_to_f32(Vt[b, g, :tl[b]]).astype(np.float64)
+            st = kt @ qf / math.sqrt(D)
+            m = max(s.max(), st.max())
+            w, wt = np.exp(s - m), np.exp(st - m)
+            num = (w[:, None] * idx.vsum[cs].astype(np.float64)).sum(0) + wt @ vt
+            den = (w * n).sum() + wt.sum()
+            np.testing.assert_allclose(o[b, h], num / den, rtol=1e-10, atol=1e-10)
+            assert abs(lse[b, h] - (m + math.log(den))) < 1e-10
+        clu += idx.G * C
+
+
+def test_decode_tail_rejects_lengths_beyond_capacity():
+    Kf, Vf, cf, Ki, Vi, ctx, Kt, Vt, idx, q = _tail_setup()
+    with pytest.raises(ValueError):
+        oracle.decode_tail(idx, Ki, Vi, q, 4, 64, 0.05, Kt, Vt, [65, 0])
