@@ -46,6 +46,7 @@ typedef struct ihipStream_t* wave_stream_t; /* same type as hipStream_t */
 #define WAVE_MAX_CLUSTERS_PER_SEG 2048
 #define WAVE_MAX_STEADY 2048   /* steady tokens per sequence unless they cover it all */
 #define WAVE_MAX_GROUP 8       /* q heads per kv head */
+#define WAVE_MAX_TAIL 65536    /* tokens appended after a build (wave_attn_decode_tail) */
 
 typedef enum wave_status {
   WAVE_OK = 0,
@@ -168,6 +169,34 @@ wave_status wave_attn_decode_plan(const wave_index* index, int32_t n_q_heads, in
 wave_status wave_attn_decode(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
                              int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse, void* ws,
                              size_t ws_bytes, wave_stream_t stream);
+
+/*
+ * wave_attn_decode_tail -- wave attention over an index plus the tokens decoded
+ * after it was built. RetroInfer page, section 2.A: the steady zone keeps the
+ * recent tokens exact, and the index grows segment by segment (the segments are
+ * clustered independently), so a decoded token waits among the recent tokens
+ * until a full segment of them can be clustered (then a wave_index_build over
+ * the longer context takes them in). Sequence b has tail_len[b] such tokens after
+ * its N_b indexed ones; each is attended exactly by every q head of its kv head,
+ * beside wave_attn_decode's three zones over the indexed tokens (whose steady zone
+ * is still the first n_sink and the last n_local indexed tokens). S, E, k_b, R
+ * and sel_ids are those of wave_attn_decode.
+ *  k_tail, v_tail: device bf16 [B][G][tail_cap][128], row (b, g, t) at element
+ *            128 * ((b * G + g) * tail_cap + t); rows t < tail_len[b] are read.
+ *            Caller-owned, read only, 16-byte aligned.
+ *  tail_cap: 1..WAVE_MAX_TAIL.
+ *  tail_len: device int32 [B]; a value outside [0, tail_cap] is clamped to it.
+ *  ws:       at least wave_attn_decode_tail_plan's size for this tail_cap (the
+ *            row workgroups are planned for tail_cap appended tokens).
+ * Other arguments and errors as wave_attn_decode; ARG also for a tail_cap out of
+ * range or a NULL tail pointer, ALIGN for a misaligned one.
+ */
+wave_status wave_attn_decode_tail_plan(const wave_index* index, int32_t n_q_heads, int32_t n_sink, int32_t n_local,
+                                       double topk_frac, int32_t tail_cap, int32_t* k_max, size_t* ws_bytes);
+wave_status wave_attn_decode_tail(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
+                                  int32_t n_local, double topk_frac, const void* k_tail, const void* v_tail,
+                                  int32_t tail_cap, const int32_t* tail_len, float* out, int32_t* sel_ids,
+                                  float* lse, void* ws, size_t ws_bytes, wave_stream_t stream);
 
 /*
  * wave_attn_decode_shared -- wave attention with one retrieval set per kv head.

@@ -68,6 +68,10 @@ def lib():
         L.wave_attn_decode.argtypes = [ctypes.POINTER(_Index), P, i32, i32, i32, ctypes.c_double, P, P, P, P, sz, P]
         L.wave_attn_decode_topk.argtypes = L.wave_attn_decode.argtypes
         L.wave_attn_decode_shared.argtypes = L.wave_attn_decode.argtypes
+        L.wave_attn_decode_tail_plan.argtypes = [ctypes.POINTER(_Index), i32, i32, i32, ctypes.c_double, i32,
+                                                 ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_size_t)]
+        L.wave_attn_decode_tail.argtypes = [ctypes.POINTER(_Index), P, i32, i32, i32, ctypes.c_double, P, P, i32, P,
+                                            P, P, P, P, sz, P]
         L.wave_index_build_blocks.argtypes = [ctypes.POINTER(_Shape), P, P, i32, i32, ctypes.POINTER(_Index), P, sz,
                                               P]
         L.wave_last_error.restype = ctypes.c_char_p
@@ -76,7 +80,7 @@ def lib():
         L.wave_profiler_read.restype = i32
         for f in ("wave_index_plan", "wave_index_build", "wave_attn_decode_plan", "wave_attn_decode",
                   "wave_profiler_enable", "wave_index_build_blocks", "wave_attn_decode_topk",
-                  "wave_attn_decode_shared"):
+                  "wave_attn_decode_shared", "wave_attn_decode_tail_plan", "wave_attn_decode_tail"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -227,6 +231,41 @@ def wave_attn_decode_topk(index, q, n_sink, n_local, topk_frac, ws=None, out=Non
                           stream=None):
     """Top-k retrieval without the estimation zone (the block baseline's decode); as wave_attn_decode."""
     return wave_attn_decode(index, q, n_sink, n_local, topk_frac, ws, out, sel_ids, lse, stream, estimate=False)
+
+
+def wave_attn_decode_tail_plan(index, n_q_heads, n_sink, n_local, topk_frac, tail_cap):
+    """(k_max, workspace bytes) of a decode call with up to tail_cap appended tokens."""
+    k = ctypes.c_int32()
+    w = ctypes.c_size_t()
+    _check(lib().wave_attn_decode_tail_plan(ctypes.byref(index.c), int(n_q_heads), int(n_sink), int(n_local),
+                                            float(topk_frac), int(tail_cap), ctypes.byref(k), ctypes.byref(w)))
+    return k.value, w.value
+
+
+def wave_attn_decode_tail(index, q, n_sink, n_local, topk_frac, k_tail, v_tail, tail_len, ws=None, out=None,
+                          sel_ids=None, lse=None, stream=None):
+    """Wave attention plus the tokens appended after the build: k_tail, v_tail bf16 [B, G, cap, 128] and
+    tail_len int32 [B] on the device. Returns as wave_attn_decode."""
+    B, H = q.shape[0], q.shape[1]
+    cap = int(k_tail.shape[2])
+    if tuple(v_tail.shape) != tuple(k_tail.shape) or tuple(k_tail.shape[:2]) != (B, index.n_kv_heads) or k_tail.shape[3] != 128:
+        raise ValueError("k_tail and v_tail must be [B, G, cap, 128]")
+    if tail_len.dtype != torch.int32 or tail_len.numel() != B:
+        raise ValueError("tail_len must be int32 [B]")
+    k_max, wsb = wave_attn_decode_tail_plan(index, H, n_sink, n_local, topk_frac, cap)
+    dev = q.device
+    if ws is None:
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((B, H, HEAD_DIM), dtype=torch.float32, device=dev)
+    if sel_ids is None:
+        sel_ids = torch.empty((B, H, max(k_max, 1)), dtype=torch.int32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _check(lib().wave_attn_decode_tail(ctypes.byref(index.c), _ptr(q), H, int(n_sink), int(n_local), float(topk_frac),
+                                       _ptr(k_tail), _ptr(v_tail), cap, _ptr(tail_len), _ptr(out), _ptr(sel_ids),
+                                       _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+    return out, sel_ids[:, :, :k_max], lse
 
 
 def wave_attn_decode_shared(index, q, n_sink, n_local, topk_frac, ws=None, out=None, sel_ids=None, lse=None,

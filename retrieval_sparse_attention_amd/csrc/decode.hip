@@ -1032,7 +1032,7 @@ __device__ __forceinline__ void softmax_rows(RowState& st, const float* s, const
 }
 
 // Rows of one (b, h): the members of the selected clusters in selection order,
-// then the steady rows. Workgroup `part` takes rows [part*T/P, (part+1)*T/P),
+// then the steady rows, then the tokens appended after the build (if any). Workgroup `part` takes rows [part*T/P, (part+1)*T/P),
 // each 16-lane group a contiguous 1/16 of that.
 template <int GS>
 __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs da, wave_index ix, DecodeWs ws,
@@ -1053,7 +1053,10 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
   const int64_t row0 = sb.row + (int64_t)g * N;
   const int64_t kbase = (int64_t)da.GS * sb.clu + (int64_t)h * sb.C;
   const int M = ws.counts[4 * bh + 0], k = ws.counts[4 * bh + 1], nS = ws.counts[4 * bh + 2];
-  const int T = M + nS;
+  // rows: the selected clusters' members [0, M), the steady rows [M, M + nS), then the
+  // tokens appended after the build [M + nS, T)
+  const int nT = da.kt != nullptr ? min(max(da.tail_len[b], 0), da.tail_cap) : 0;
+  const int T = M + nS + nT;
   const Steady sz = steady_of(da, N);
   const int i0 = (int)((int64_t)T * part / per_bh), i1 = (int)((int64_t)T * (part + 1) / per_bh);
   const int s0 = i0 + (int)((int64_t)(i1 - i0) * gi / 16), s1 = i0 + (int)((int64_t)(i1 - i0) * (gi + 1) / 16);
@@ -1192,13 +1195,14 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
     }
     softmax_rows<U>(st, sv, cs, vv);
   }
-  // steady rows: entries e = row - M for rows [max(s0, M), s1)
-  for (int r = max(s0, M); r < s1; r += U) {
+  // steady rows: entries e = row - M for rows [max(s0, M), min(s1, M + nS))
+  const int r2 = min(s1, M + nS);
+  for (int r = max(s0, M); r < r2; r += U) {
     int32_t p[U];
     float cvv[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int e = min(r + u, s1 - 1) - M;
+      const int e = min(r + u, r2 - 1) - M;
       p[u] = lds_meta ? m_sp[e] : ix.inv_perm[row0 + steady_pos(sz, e)];
       cvv[u] = lds_meta ? m_corr[e] : corr[e];
     }
@@ -1212,11 +1216,34 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const float x = dot8(qf, kv[u]);
-      const bool valid = r + u < s1;
+      const bool valid = r + u < r2;
       sv[u] = valid ? x : -INFINITY;
       cs[u] = (valid && da.est && cvv[u] == cvv[u]) ? cvv[u] * sc : -INFINITY;
     }
     softmax_rows<U>(st, sv, cs, vv);
+  }
+  // appended tokens: entries e = row - M - nS for rows [max(s0, M + nS), s1), exact, in no
+  // cluster (no centroid term to take back)
+  if (s1 > M + nS) {
+    const uint16_t* Kt = da.kt + (int64_t)(b * sa.G + g) * da.tail_cap * D + l16 * 8;
+    const uint16_t* Vt = da.vt + (int64_t)(b * sa.G + g) * da.tail_cap * D + l16 * 8;
+    for (int r = max(s0, M + nS); r < s1; r += U) {
+      uint4 kv[U], vv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t e = min(r + u, s1 - 1) - (M + nS);
+        kv[u] = *reinterpret_cast<const uint4*>(Kt + e * D);
+        vv[u] = *reinterpret_cast<const uint4*>(Vt + e * D);
+      }
+      float sv[U], cs[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float x = dot8(qf, kv[u]);
+        sv[u] = r + u < s1 ? x : -INFINITY;
+        cs[u] = -INFINITY;
+      }
+      softmax_rows<U>(st, sv, cs, vv);
+    }
   }
   // merge the 4 groups of the wave, then the 4 waves
 #pragma unroll

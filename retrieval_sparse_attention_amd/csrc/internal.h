@@ -23,6 +23,10 @@ struct DecodeArgs {
   int32_t NVg;            // keys per lane when NV == 0 (a multiple of 16)
   int32_t est;            // 1: the estimation zone (wave attention); 0: top-k retrieval only
   int32_t shared;         // 1: one selection per kv head, by the sum of its q heads' rank keys
+  const uint16_t* kt;     // tokens appended after the build, keys [B][G][tail_cap][128] (nullptr: none)
+  const uint16_t* vt;     // and values
+  const int32_t* tail_len;  // device [B]: appended tokens of sequence b (clamped to [0, tail_cap])
+  int32_t tail_cap;
   int32_t kreq[MAXB];     // min(ceil(topk_frac * C_b), C_b), binary64 on the host
 };
 

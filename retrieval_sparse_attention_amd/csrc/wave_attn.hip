@@ -111,7 +111,7 @@ struct DecodePlan {
 };
 
 wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t n_local, double frac,
-                        DecodePlan* P) {
+                        DecodePlan* P, int32_t tail_cap = 0) {
   if (ix == nullptr) return fail(WAVE_ERR_ARG, "index is NULL");
   wave_status st = check_shape(&ix->shape);
   if (st != WAVE_OK) return st;
@@ -167,7 +167,7 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
   // each if the k_attend grid (with one estimation workgroup per 128 clusters and kv
   // head) is then resident at once, else DEC_ROWS_PER_WG
   const int64_t avg = (ix->seg_len + ix->clusters_per_seg - 1) / ix->clusters_per_seg;
-  int64_t est = (int64_t)kmax * avg + nSmax;
+  int64_t est = (int64_t)kmax * avg + nSmax + tail_cap;
   int64_t nest = 0;
   for (int b = 0; b < sa.B; ++b) nest += (int64_t)G * ((sa.C[b] + wave::DEC_SCORE_CH - 1) / wave::DEC_SCORE_CH);
   int64_t Pw = (est + wave::DEC_ROWS_SMALL - 1) / wave::DEC_ROWS_SMALL;
@@ -346,12 +346,18 @@ wave_status wave_attn_decode_plan(const wave_index* index, int32_t n_q_heads, in
 
 static wave_status decode_call(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
                                int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse, void* ws,
-                               size_t ws_bytes, wave_stream_t stream, int est, int shared) {
+                               size_t ws_bytes, wave_stream_t stream, int est, int shared,
+                               const void* k_tail = nullptr, const void* v_tail = nullptr, int32_t tail_cap = 0,
+                               const int32_t* tail_len = nullptr) {
   DecodePlan P;
-  wave_status st = decode_plan(index, n_q_heads, n_sink, n_local, topk_frac, &P);
+  wave_status st = decode_plan(index, n_q_heads, n_sink, n_local, topk_frac, &P, tail_cap);
   if (st != WAVE_OK) return st;
   P.da.est = est;
   P.da.shared = shared;
+  P.da.kt = reinterpret_cast<const uint16_t*>(k_tail);
+  P.da.vt = reinterpret_cast<const uint16_t*>(v_tail);
+  P.da.tail_len = tail_len;
+  P.da.tail_cap = tail_cap;
   if (q == nullptr || out == nullptr || ws == nullptr) return fail(WAVE_ERR_ARG, "q, out and ws must be non-NULL");
   if (P.da.k_max > 0 && sel_ids == nullptr) return fail(WAVE_ERR_ARG, "sel_ids is NULL but k_max = %d", P.da.k_max);
   const void* ptrs[] = {index->k_sorted, index->v_sorted, index->perm, index->inv_perm, index->assign,
@@ -390,6 +396,33 @@ wave_status wave_attn_decode(const wave_index* index, const void* q, int32_t n_q
                              int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse, void* ws,
                              size_t ws_bytes, wave_stream_t stream) {
   return decode_call(index, q, n_q_heads, n_sink, n_local, topk_frac, out, sel_ids, lse, ws, ws_bytes, stream, 1, 0);
+}
+
+wave_status wave_attn_decode_tail_plan(const wave_index* index, int32_t n_q_heads, int32_t n_sink, int32_t n_local,
+                                       double topk_frac, int32_t tail_cap, int32_t* k_max, size_t* ws_bytes) {
+  if (tail_cap < 1 || tail_cap > WAVE_MAX_TAIL)
+    return fail(WAVE_ERR_ARG, "tail_cap %d outside [1, %d]", tail_cap, WAVE_MAX_TAIL);
+  if (k_max == nullptr || ws_bytes == nullptr) return fail(WAVE_ERR_ARG, "k_max and ws_bytes must be non-NULL");
+  DecodePlan P;
+  wave_status st = decode_plan(index, n_q_heads, n_sink, n_local, topk_frac, &P, tail_cap);
+  if (st != WAVE_OK) return st;
+  *k_max = P.da.k_max;
+  *ws_bytes = P.total;
+  return ok();
+}
+
+wave_status wave_attn_decode_tail(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
+                                  int32_t n_local, double topk_frac, const void* k_tail, const void* v_tail,
+                                  int32_t tail_cap, const int32_t* tail_len, float* out, int32_t* sel_ids,
+                                  float* lse, void* ws, size_t ws_bytes, wave_stream_t stream) {
+  if (tail_cap < 1 || tail_cap > WAVE_MAX_TAIL)
+    return fail(WAVE_ERR_ARG, "tail_cap %d outside [1, %d]", tail_cap, WAVE_MAX_TAIL);
+  if (k_tail == nullptr || v_tail == nullptr || tail_len == nullptr)
+    return fail(WAVE_ERR_ARG, "k_tail, v_tail and tail_len must be non-NULL");
+  if (!aligned16(k_tail) || !aligned16(v_tail) || (reinterpret_cast<uintptr_t>(tail_len) & 3) != 0)
+    return fail(WAVE_ERR_ALIGN, "k_tail and v_tail must be 16-byte aligned, tail_len 4-byte aligned");
+  return decode_call(index, q, n_q_heads, n_sink, n_local, topk_frac, out, sel_ids, lse, ws, ws_bytes, stream, 1, 0,
+                     k_tail, v_tail, tail_cap, tail_len);
 }
 
 wave_status wave_attn_decode_shared(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,

@@ -22,7 +22,7 @@ def _declared():
 def test_exports_every_declared_symbol():
     names = _declared()
     assert {"wave_index_plan", "wave_index_build", "wave_attn_decode_plan", "wave_attn_decode",
-            "wave_last_error", "wave_attn_decode_shared"} <= set(names)
+            "wave_last_error", "wave_attn_decode_shared", "wave_attn_decode_tail"} <= set(names)
     L = rsa.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -188,6 +188,27 @@ def test_calls_fail_cleanly_without_device():
     bad = list(dargs)
     bad[6] = None
     assert L.wave_attn_decode_topk(*bad) == ARG
+    k2 = ctypes.c_int32()
+    w2 = ctypes.c_size_t()
+    assert L.wave_attn_decode_tail_plan(ctypes.byref(ix), 8, 4, 64, 0.05, 512, ctypes.byref(k2), ctypes.byref(w2)) == OK
+    assert k2.value == k and w2.value >= w  # the tail's rows may take more row workgroups
+    assert L.wave_attn_decode_tail_plan(ctypes.byref(ix), 8, 4, 64, 0.05, 0, ctypes.byref(k2), ctypes.byref(w2)) == ARG
+    targs = [ctypes.byref(ix), ctypes.c_void_p(0x4000), 8, 4, 64, 0.05, ctypes.c_void_p(0x8000),
+             ctypes.c_void_p(0x9000), 512, ctypes.c_void_p(0xA000), ctypes.c_void_p(0x5000), ctypes.c_void_p(0x6000),
+             None, ctypes.c_void_p(0x7000), w2.value, None]
+    assert L.wave_attn_decode_tail(*targs) == HIP
+    bad = list(targs)
+    bad[6] = None
+    assert L.wave_attn_decode_tail(*bad) == ARG
+    bad = list(targs)
+    bad[7] = ctypes.c_void_p(0x9004)
+    assert L.wave_attn_decode_tail(*bad) == ALIGN
+    bad = list(targs)
+    bad[8] = 65537
+    assert L.wave_attn_decode_tail(*bad) == ARG
+    bad = list(targs)
+    bad[14] = w2.value - 1
+    assert L.wave_attn_decode_tail(*bad) == WS
     assert L.wave_attn_decode_shared(*dargs) == HIP
     bad = list(dargs)
     bad[10] = w - 1
