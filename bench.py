@@ -14,7 +14,7 @@ the layers round robin, so no decode reuses the 256 MB Infinity Cache.
 
 `--workload` runs one of the method's other workloads instead (16k, 1m, batched: decode
 steps/s of the whole job; blocks: the block top-k baseline; shared: the 128K layer with one
-retrieval set per kv head; stress: index-build tokens/s of the clustering on 1M heavy-tailed
+retrieval set per kv head; tail: the 128K layer with 4096 tokens decoded after its build; stress: index-build tokens/s of the clustering on 1M heavy-tailed
 keys per kv head); the default line is the 128K one.
 """
 import argparse
@@ -55,6 +55,8 @@ WORKLOADS = {
     # the block top-k baseline on the 128K layer: contiguous blocks of 16 tokens instead of the
     # k-means clusters and no estimation zone (a same-hardware comparison point)
     "blocks": dict(WORKLOAD, workload="block-topk-baseline-128k", blocks=True, kmeans_iters=0),
+    # the 128K layer with half a segment of tokens decoded after its build (wave_attn_decode_tail)
+    "tail": dict(WORKLOAD, workload="llama3-8b-attention-layer-128k-plus-4096-decoded", tail=4096),
     # the 128K layer with one retrieval set per kv head (wave_attn_decode_shared)
     "shared": dict(WORKLOAD, workload="llama3-8b-attention-layer-128k-shared-selection", shared=True),
     "stress": dict(workload="index-build-1m-keys-student-t", batch=1, q_heads=8, kv_heads=8, head_dim=128,
@@ -348,7 +350,16 @@ def main():
     for l in range(L):
         build_layer(l)
     torch.cuda.synchronize()
-    k_max, dwsb = rsa.wave_attn_decode_plan(idxs[0], H, ns, nl, frac)
+    n_tail = int(W.get("tail", 0))
+    if n_tail:
+        # the decoded tokens' K/V rows: the generator's next n_tail tokens of each (b, g)
+        Kx, Vx, _ = synth.kv(W["seed_data"] + 1, B, G, np.array([n_tail] * B, np.int64), seg)
+        k_tail = torch.from_numpy(Kx.view(np.int16)).to(dev).view(torch.bfloat16).view(B, G, n_tail, 128)
+        v_tail = torch.from_numpy(Vx.view(np.int16)).to(dev).view(torch.bfloat16).view(B, G, n_tail, 128)
+        tail_len = torch.full((B,), n_tail, dtype=torch.int32, device=dev)
+        k_max, dwsb = rsa.wave_attn_decode_tail_plan(idxs[0], H, ns, nl, frac, n_tail)
+    else:
+        k_max, dwsb = rsa.wave_attn_decode_plan(idxs[0], H, ns, nl, frac)
     dws = torch.empty(dwsb, dtype=torch.uint8, device=dev)
     out = torch.empty((B, H, 128), dtype=torch.float32, device=dev)
     lse = torch.empty((B, H), dtype=torch.float32, device=dev)
@@ -364,8 +375,12 @@ def main():
             lay = (step * QPS + s) % L
             qi = (step * QPS + s) % nq
             ids = ids_log[s] if ids_log is not None else ids_buf
-            rsa.wave_attn_decode(idxs[lay], qd[qi], ns, nl, frac, ws=dws, out=out, sel_ids=ids, lse=lse,
-                                 estimate=not blocks, shared=shared)
+            if n_tail:
+                rsa.wave_attn_decode_tail(idxs[lay], qd[qi], ns, nl, frac, k_tail, v_tail, tail_len, ws=dws,
+                                          out=out, sel_ids=ids, lse=lse)
+            else:
+                rsa.wave_attn_decode(idxs[lay], qd[qi], ns, nl, frac, ws=dws, out=out, sel_ids=ids, lse=lse,
+                                     estimate=not blocks, shared=shared)
 
     # the step pattern repeats with period P: one captured HIP graph per phase
     P = math.lcm(L, max(1, nq // math.gcd(nq, max(QPS, 1))))
@@ -456,7 +471,7 @@ def main():
     n_est = sum(-(-c // 128) for c in Cb)          # estimation chunks (workgroups) per kv head
     # row workgroups per (b, h), as the library plans them: 176 rows each at the average
     # cluster size if the grid then fits 1024 resident workgroups, else 256
-    est_rows = k_max * -(-seg // K_s) + steady
+    est_rows = k_max * -(-seg // K_s) + steady + n_tail
     P = -(-est_rows // 176)
     if B * H * P + G * n_est > 1024:
         P = -(-est_rows // 256)
@@ -473,6 +488,7 @@ def main():
                     + B * G * steady * (2 * 128 * 2 + 4)      # steady rows (a kv head's): K, V, inv_perm
                     + B * H * steady * 4                      # their corrections per q head
                     + sel_per_dec * 16                        # window metadata
+                    + B * G * n_tail * 2 * 128 * 2            # appended tokens' K, V
                     + B * H * 128 * 2 + B * H * P * part)     # q, row partials out
     if not blocks:
         attend_bytes += (G * Ctot * (128 * 4 + 4)             # estimation: value sums + sizes
@@ -599,10 +615,21 @@ def cpu_baseline(W, K, V, ctx, q, budget_s):
     t1 = time.time()
     idx = oracle.index_from_assign(K, V, G, ctx, seg, K_s, W["seed_build"], lab.astype(np.int32))
     t_layout = time.time() - t1
+    n_tail = int(W.get("tail", 0))
+    if n_tail:  # the decoded tokens of the GPU run
+        import synth
+        Kx, Vx, _ = synth.kv(W["seed_data"] + 1, len(ctx), G, np.array([n_tail] * len(ctx), np.int64), seg)
+        Kx = Kx.reshape(len(ctx), G, n_tail, 128)
+        Vx = Vx.reshape(len(ctx), G, n_tail, 128)
     t2 = time.time()
     n_dec = 0
     while n_dec < min(q.shape[0], W["decode_queries_per_step"]) and (n_dec == 0 or time.time() - t2 < 0.5 * budget_s):
-        oracle.decode(idx, K, V, q[n_dec], W["n_sink"], W["n_local"], W["topk_frac"], shared=W.get("shared", False))
+        if n_tail:
+            oracle.decode_tail(idx, K, V, q[n_dec], W["n_sink"], W["n_local"], W["topk_frac"], Kx, Vx,
+                               [n_tail] * len(ctx))
+        else:
+            oracle.decode(idx, K, V, q[n_dec], W["n_sink"], W["n_local"], W["topk_frac"],
+                          shared=W.get("shared", False))
         n_dec += 1
     t_dec = (time.time() - t2) / n_dec
     step_s = units_total * t_unit + t_layout + W["decode_queries_per_step"] * t_dec
