@@ -471,7 +471,8 @@ def main():
     n_est = sum(-(-c // 128) for c in Cb)          # estimation chunks (workgroups) per kv head
     # row workgroups per (b, h), as the library plans them: 176 rows each at the average
     # cluster size if the grid then fits 1024 resident workgroups, else 256
-    est_rows = k_max * -(-seg // K_s) + steady + n_tail
+    est_rows = k_max * -(-seg // K_s) + steady
+    n_tail_wg = -(-n_tail // 64)                  # appended-token workgroups per kv head
     P = -(-est_rows // 176)
     if B * H * P + G * n_est > 1024:
         P = -(-est_rows // 256)
@@ -480,7 +481,9 @@ def main():
     rows = G * int(ctx.sum())                     # index rows
     score_bytes = (G * Ctot * (128 * 2 + 4)       # bf16 centroid rows + sizes
                    + B * H * 128 * 2              # q
-                   + H * Ctot * 8)                # rank keys + sortable keys out
+                   + H * Ctot * 8                 # rank keys + sortable keys out
+                   + B * G * n_tail * 2 * 128 * 2  # appended tokens' K, V (their workgroups run in this grid)
+                   + (B * H * n_tail_wg * part if n_tail else 0))
     topk_bytes = (H * Ctot * 4 + G * Ctot * 8     # sortable keys; sizes + offsets
                   + sel_per_dec * (4 + 8 + 4 + 4)  # ids, spans, keys, member prefix out
                   + B * H * steady * 8)           # steady rows: cluster ids in, corrections out
@@ -488,13 +491,13 @@ def main():
                     + B * G * steady * (2 * 128 * 2 + 4)      # steady rows (a kv head's): K, V, inv_perm
                     + B * H * steady * 4                      # their corrections per q head
                     + sel_per_dec * 16                        # window metadata
-                    + B * G * n_tail * 2 * 128 * 2            # appended tokens' K, V
                     + B * H * 128 * 2 + B * H * P * part)     # q, row partials out
     if not blocks:
         attend_bytes += (G * Ctot * (128 * 4 + 4)             # estimation: value sums + sizes
                          + H * Ctot * 4                       # estimation: rank keys
                          + H * n_est * part)                  # estimation partials out
-    merge_bytes = B * H * P * part + (0 if blocks else H * n_est * part) + B * H * (128 * 4 + 4)
+    merge_bytes = (B * H * P * part + (0 if blocks else H * n_est * part) + B * H * n_tail_wg * part
+                   + B * H * (128 * 4 + 4))
     step_bytes = score_bytes + topk_bytes + attend_bytes + merge_bytes
     # per launch (one k-means round): every unit's tokens against its own clusters
     tok_clu = 0

@@ -85,8 +85,19 @@ struct ScoreLds {
 };
 
 template <int GS>
+__device__ void tail_role(const SeqArgs& sa, const DecodeArgs& da, const uint16_t* q, const DecodeWs& ws, int w);
+
+// TAIL: the grid also holds the appended-token workgroups (a separate instantiation, so
+// that their registers do not lower the scoring workgroups' occupancy elsewhere)
+template <int GS, bool TAIL>
 __global__ __launch_bounds__(SCORE_THREADS) void k_score(SeqArgs sa, DecodeArgs da, wave_index ix,
                                                          const uint16_t* __restrict__ q, DecodeWs ws) {
+  if constexpr (TAIL) {
+    if ((int)blockIdx.x >= da.nscore) {
+      tail_role<GS>(sa, da, q, ws, blockIdx.x - da.nscore);
+      return;
+    }
+  }
   __shared__ ScoreLds<GS> S;
   int w = blockIdx.x, b = 0;
   for (;; ++b) {
@@ -1031,8 +1042,98 @@ __device__ __forceinline__ void softmax_rows(RowState& st, const float* s, const
   st.m = mn;
 }
 
+// ------------------------------------------------------------------ appended tokens
+// Tokens decoded after the build, attended exactly. They need neither the selection nor
+// the rank keys, so their workgroups run in k_score's grid: workgroup (b, g, pt) takes
+// appended rows [pt DEC_TAIL_ROWS, +DEC_TAIL_ROWS) of kv head g and every q head of g,
+// each row read once for all of them; one partial softmax state per q head.
+template <int GS>
+__device__ void tail_role(const SeqArgs& sa, const DecodeArgs& da, const uint16_t* q, const DecodeWs& ws, int w) {
+  __shared__ float tred[4][GS][PART];
+  const int per = sa.G * da.PT;
+  const int b = w / per, g = (w / da.PT) % sa.G, pt = w % da.PT;
+  const int nT = min(max(da.tail_len[b], 0), da.tail_cap);
+  const int r0 = min(pt * DEC_TAIL_ROWS, nT), r1 = min(r0 + DEC_TAIL_ROWS, nT);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, l16 = lane & 15, grp = lane >> 4;
+  const int gi = wv * 4 + grp;
+  const int s0 = r0 + (r1 - r0) * gi / 16, s1 = r0 + (r1 - r0) * (gi + 1) / 16;
+  const float sc = da.tau * LOG2E;
+  float qf[GS][8];
+#pragma unroll
+  for (int hh = 0; hh < GS; ++hh) {
+    const uint4 v = *reinterpret_cast<const uint4*>(q + ((int64_t)b * da.H + g * GS + hh) * D + l16 * 8);
+    qf[hh][0] = bf16_lo(v.x) * sc; qf[hh][1] = bf16_hi(v.x) * sc; qf[hh][2] = bf16_lo(v.y) * sc;
+    qf[hh][3] = bf16_hi(v.y) * sc; qf[hh][4] = bf16_lo(v.z) * sc; qf[hh][5] = bf16_hi(v.z) * sc;
+    qf[hh][6] = bf16_lo(v.w) * sc; qf[hh][7] = bf16_hi(v.w) * sc;
+  }
+  RowState st[GS];
+#pragma unroll
+  for (int hh = 0; hh < GS; ++hh) {
+    st[hh].m = -INFINITY;
+    st[hh].l = 0.f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) st[hh].acc[d] = 0.f;
+  }
+  const uint16_t* Kt = da.kt + (int64_t)(b * sa.G + g) * da.tail_cap * D + l16 * 8;
+  const uint16_t* Vt = da.vt + (int64_t)(b * sa.G + g) * da.tail_cap * D + l16 * 8;
+  constexpr int U = 4;
+  for (int r = s0; r < s1; r += U) {
+    uint4 kv[U], vv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = min(r + u, s1 - 1);
+      kv[u] = *reinterpret_cast<const uint4*>(Kt + e * D);
+      vv[u] = *reinterpret_cast<const uint4*>(Vt + e * D);
+    }
+#pragma unroll
+    for (int hh = 0; hh < GS; ++hh) {
+      float sv[U], cs[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float x = dot8(qf[hh], kv[u]);
+        sv[u] = r + u < s1 ? x : -INFINITY;
+        cs[u] = -INFINITY;  // in no cluster: no centroid term to take back
+      }
+      softmax_rows<U>(st[hh], sv, cs, vv);
+    }
+  }
+  // per q head: merge the 4 groups of a wave, then the 4 waves
+#pragma unroll
+  for (int hh = 0; hh < GS; ++hh) {
+#pragma unroll
+    for (int o = 16; o < 64; o <<= 1) {
+      const float m2 = xor_shfl(st[hh].m, o), l2 = xor_shfl(st[hh].l, o);
+      float a2[8];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) a2[d] = xor_shfl(st[hh].acc[d], o);
+      merge_state(st[hh].m, st[hh].l, st[hh].acc, m2, l2, a2, 8);
+    }
+    if (grp == 0) {
+      if (l16 == 0) { tred[wv][hh][0] = st[hh].m; tred[wv][hh][1] = st[hh].l; }
+#pragma unroll
+      for (int d = 0; d < 8; ++d) tred[wv][hh][4 + l16 * 8 + d] = st[hh].acc[d];
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < GS * D; e += SCORE_THREADS) {
+    const int hh = e / D, d = e % D;
+    float Mx = -INFINITY;
+    for (int w2 = 0; w2 < 4; ++w2) Mx = fmaxf(Mx, tred[w2][hh][0]);
+    float Ls = 0.f, A = 0.f;
+    if (Mx != -INFINITY)
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const float f = exp2f(tred[w2][hh][0] - Mx);
+        Ls += tred[w2][hh][1] * f;
+        A += tred[w2][hh][4 + d] * f;
+      }
+    float* o = ws.part + (((int64_t)b * da.H + g * GS + hh) * da.NP + (da.NP - da.PT) + pt) * PART;
+    if (d == 0) { o[0] = Mx; o[1] = Ls; }
+    o[4 + d] = A;
+  }
+}
+
 // Rows of one (b, h): the members of the selected clusters in selection order,
-// then the steady rows, then the tokens appended after the build (if any). Workgroup `part` takes rows [part*T/P, (part+1)*T/P),
+// then the steady rows. Workgroup `part` takes rows [part*T/P, (part+1)*T/P),
 // each 16-lane group a contiguous 1/16 of that.
 template <int GS>
 __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs da, wave_index ix, DecodeWs ws,
@@ -1053,10 +1154,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
   const int64_t row0 = sb.row + (int64_t)g * N;
   const int64_t kbase = (int64_t)da.GS * sb.clu + (int64_t)h * sb.C;
   const int M = ws.counts[4 * bh + 0], k = ws.counts[4 * bh + 1], nS = ws.counts[4 * bh + 2];
-  // rows: the selected clusters' members [0, M), the steady rows [M, M + nS), then the
-  // tokens appended after the build [M + nS, T)
-  const int nT = da.kt != nullptr ? min(max(da.tail_len[b], 0), da.tail_cap) : 0;
-  const int T = M + nS + nT;
+  const int T = M + nS;
   const Steady sz = steady_of(da, N);
   const int i0 = (int)((int64_t)T * part / per_bh), i1 = (int)((int64_t)T * (part + 1) / per_bh);
   const int s0 = i0 + (int)((int64_t)(i1 - i0) * gi / 16), s1 = i0 + (int)((int64_t)(i1 - i0) * (gi + 1) / 16);
@@ -1195,8 +1293,8 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
     }
     softmax_rows<U>(st, sv, cs, vv);
   }
-  // steady rows: entries e = row - M for rows [max(s0, M), min(s1, M + nS))
-  const int r2 = min(s1, M + nS);
+  // steady rows: entries e = row - M for rows [max(s0, M), s1)
+  const int r2 = s1;
   for (int r = max(s0, M); r < r2; r += U) {
     int32_t p[U];
     float cvv[U];
@@ -1221,29 +1319,6 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
       cs[u] = (valid && da.est && cvv[u] == cvv[u]) ? cvv[u] * sc : -INFINITY;
     }
     softmax_rows<U>(st, sv, cs, vv);
-  }
-  // appended tokens: entries e = row - M - nS for rows [max(s0, M + nS), s1), exact, in no
-  // cluster (no centroid term to take back)
-  if (s1 > M + nS) {
-    const uint16_t* Kt = da.kt + (int64_t)(b * sa.G + g) * da.tail_cap * D + l16 * 8;
-    const uint16_t* Vt = da.vt + (int64_t)(b * sa.G + g) * da.tail_cap * D + l16 * 8;
-    for (int r = max(s0, M + nS); r < s1; r += U) {
-      uint4 kv[U], vv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t e = min(r + u, s1 - 1) - (M + nS);
-        kv[u] = *reinterpret_cast<const uint4*>(Kt + e * D);
-        vv[u] = *reinterpret_cast<const uint4*>(Vt + e * D);
-      }
-      float sv[U], cs[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float x = dot8(qf, kv[u]);
-        sv[u] = r + u < s1 ? x : -INFINITY;
-        cs[u] = -INFINITY;
-      }
-      softmax_rows<U>(st, sv, cs, vv);
-    }
   }
   // merge the 4 groups of the wave, then the 4 waves
 #pragma unroll
@@ -1289,11 +1364,16 @@ __global__ __launch_bounds__(256) void k_merge(SeqArgs sa, DecodeArgs da, Decode
   __shared__ float mx[4];
   const int bh = blockIdx.x;
   const int b = bh / da.H;
-  const int npart = da.P + (da.est ? (sa.C[b] + SC - 1) / SC : 0);
+  // partials: P row workgroups, this sequence's estimation chunks, then the PT appended-token
+  // workgroups (after the slots of the longest sequence's chunks)
+  const int nlead = da.P + (da.est ? (sa.C[b] + SC - 1) / SC : 0);
+  const int npart = nlead + da.PT;
+  const int skip = da.NP - da.PT - nlead;
+  auto slot = [&](int i) { return (int64_t)(i < nlead ? i : i + skip) * PART; };
   const float* pp = ws.part + (int64_t)bh * da.NP * PART;
   const int tid = threadIdx.x, dq = tid & 31, sub = tid >> 5;
   float M = -INFINITY;
-  for (int i = tid; i < npart; i += 256) M = fmaxf(M, pp[(int64_t)i * PART]);
+  for (int i = tid; i < npart; i += 256) M = fmaxf(M, pp[slot(i)]);
   M = wave_max(M);
   if ((tid & 63) == 0) mx[tid >> 6] = M;
   __syncthreads();
@@ -1302,7 +1382,7 @@ __global__ __launch_bounds__(256) void k_merge(SeqArgs sa, DecodeArgs da, Decode
   float Ls = 0.f;
 #pragma unroll 4
   for (int i = sub; i < npart; i += 8) {
-    const float* p = pp + (int64_t)i * PART;
+    const float* p = pp + slot(i);
     const float mi = p[0];
     const float4 a = *reinterpret_cast<const float4*>(p + 4 + 4 * dq);
     const float li = p[1];
@@ -1334,7 +1414,11 @@ static void launch_gs(const SeqArgs& sa, const DecodeArgs& da, const wave_index&
                       const uint16_t* q, float* out, int32_t* sel_ids, float* lse, hipStream_t st, int nscore,
                       int nest) {
   prof_begin("k_score", st);
-  hipLaunchKernelGGL(k_score<GS>, dim3(nscore), dim3(SCORE_THREADS), 0, st, sa, da, ix, q, ws);
+  if (da.PT > 0)
+    hipLaunchKernelGGL((k_score<GS, true>), dim3(nscore + sa.B * sa.G * da.PT), dim3(SCORE_THREADS), 0, st, sa, da,
+                       ix, q, ws);
+  else
+    hipLaunchKernelGGL((k_score<GS, false>), dim3(nscore), dim3(SCORE_THREADS), 0, st, sa, da, ix, q, ws);
   prof_end(st);
   prof_begin("k_topk", st);
   const dim3 tg(sa.B * da.H), tb(TK_THREADS);

@@ -16,7 +16,7 @@ struct DecodeArgs {
   int32_t k_max;          // id columns of the output
   int32_t P;              // gathered-row workgroups per (b, h)
   int32_t NV;             // keys per lane of the register top-k (1, 2, ..., 32), 0: keys read from memory
-  int32_t NP;             // partial slots per (b, h): P + max_b ceil(C_b / DEC_SCORE_CH)
+  int32_t NP;             // partial slots per (b, h): P + max_b ceil(C_b / DEC_SCORE_CH) + PT
   int32_t scap;           // steady entries per (b, h)
   float tau;              // 1/sqrt(128)
   int32_t sort_stride;    // per-(b, h) entries of the global sort buffer
@@ -27,6 +27,8 @@ struct DecodeArgs {
   const uint16_t* vt;     // and values
   const int32_t* tail_len;  // device [B]: appended tokens of sequence b (clamped to [0, tail_cap])
   int32_t tail_cap;
+  int32_t PT;             // appended-token workgroups per (b, g) in the k_score grid (0: none)
+  int32_t nscore;         // scoring workgroups of the k_score grid (the tail workgroups follow)
   int32_t kreq[MAXB];     // min(ceil(topk_frac * C_b), C_b), binary64 on the host
 };
 
@@ -39,7 +41,8 @@ struct DecodeWs {
   uint32_t* selw;    // [sum_b H*ceil(C_b/32)] selection bitmap when C_b > 65536
   float* corr;       // [B*H*scap] rank key of a steady row's cluster if it is not selected, else NaN
   int32_t* counts;   // [B*H*4] rows of the selected clusters, k, steady rows, 0
-  float* part;       // [B*H*NP*132] partial softmax states
+  float* part;       // [B*H*NP*132] partial softmax states: P row workgroups, then max_b ceil(C_b / 128)
+                     // estimation chunks, then PT appended-token workgroups
   uint32_t* ctop;    // [B*H*(NP-P)*8] per 128-cluster chunk of a (b, h): its 4 largest sortable keys, eligible count
   uint64_t* sortg;   // [B*H*pow2(C_max)] global sort buffer (only when k_max > 4096)
 };
@@ -58,6 +61,9 @@ constexpr int DEC_SORT_LDS = 4096;
 constexpr int DEC_ROWS_SMALL = 176;
 constexpr int DEC_ROWS_PER_WG = 256;
 constexpr int DEC_ATT_SLOTS = 1024;
+// Appended tokens per tail workgroup (in the k_score grid; 4 per 16-lane group, one batch of
+// loads: 4096 tokens take 64 workgroups per kv head).
+constexpr int DEC_TAIL_ROWS = 64;
 
 hipError_t launch_decode(const SeqArgs& sa, const DecodeArgs& da, const wave_index& ix, const DecodeWs& ws,
                          const uint16_t* q, float* out, int32_t* sel_ids, float* lse, hipStream_t st);

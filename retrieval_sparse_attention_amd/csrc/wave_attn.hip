@@ -167,7 +167,7 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
   // each if the k_attend grid (with one estimation workgroup per 128 clusters and kv
   // head) is then resident at once, else DEC_ROWS_PER_WG
   const int64_t avg = (ix->seg_len + ix->clusters_per_seg - 1) / ix->clusters_per_seg;
-  int64_t est = (int64_t)kmax * avg + nSmax + tail_cap;
+  int64_t est = (int64_t)kmax * avg + nSmax;
   int64_t nest = 0;
   for (int b = 0; b < sa.B; ++b) nest += (int64_t)G * ((sa.C[b] + wave::DEC_SCORE_CH - 1) / wave::DEC_SCORE_CH);
   int64_t Pw = (est + wave::DEC_ROWS_SMALL - 1) / wave::DEC_ROWS_SMALL;
@@ -176,7 +176,11 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
   if (Pw < 1) Pw = 1;
   if (Pw > 4096) Pw = 4096;
   da.P = (int32_t)Pw;
-  da.NP = da.P + nEmax;
+  da.PT = tail_cap > 0 ? (tail_cap + wave::DEC_TAIL_ROWS - 1) / wave::DEC_TAIL_ROWS : 0;
+  da.NP = da.P + nEmax + da.PT;
+  int64_t nscore = 0;
+  for (int b = 0; b < sa.B; ++b) nscore += (int64_t)G * ((sa.C[b] + wave::DEC_SCORE_CH - 1) / wave::DEC_SCORE_CH);
+  da.nscore = (int32_t)nscore;
   // keys per lane of the top-k (16 waves x 64 lanes): the fewest that hold every key, so
   // that every wave holds keys (its thresholds then bound the selection); 0: beyond registers
   da.NV = 0;
