@@ -75,6 +75,19 @@ def test_duplicate_keys_and_ties():
     _check_all("duplicates", K, V, 2, ctx, 1024, 64, 3, 9)
 
 
+@pytest.mark.parametrize("scale_log2", [60, 63])
+def test_huge_keys_take_the_exact_decision(scale_log2):
+    # keys scaled by 2^60 (x.c near the top of the fp32 range: the margin test sends every
+    # token to the exact binary64 decision) and 2^63 (|x|^2 and |c|^2 overflow fp32: the
+    # MFMA values are inf/NaN, and every centroid is a candidate of the exact decision)
+    ctx = [2048]
+    K, V, _ = synth.kv(26, 1, 1, np.array(ctx), 1024)
+    Kf = oracle.bf16_to_f32(K).astype(np.float64) * 2.0 ** scale_log2
+    Kh = oracle.f32_to_bf16(Kf.astype(np.float32))
+    assert np.isfinite(oracle.bf16_to_f32(Kh)).all()
+    _check_all("keys x 2^%d" % scale_log2, Kh, V, 1, ctx, 1024, 64, 2, 31)
+
+
 def test_singleton_clusters():
     ctx = [700, 300]
     K, V, _ = synth.kv(25, 2, 2, np.array(ctx), 256)
