@@ -207,7 +207,7 @@ __global__ __launch_bounds__(SCORE_THREADS) void k_score(SeqArgs sa, DecodeArgs 
         ws.key32[kb + jj] = elig ? float_sortable(group_key(jj)) : 0u;
     }
   }
-  // per q head (a wave each): the chunk's 4 largest sortable keys (a multiset) and its
+  // per q head (a wave each): the chunk's DEC_CHUNK_TOPS largest sortable keys (a multiset) and its
   // eligible count, from which the top-k takes a threshold when its keys do not fit
   // registers (da.NV == 0)
   const int chm = da.NP - da.P;
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(SCORE_THREADS) void k_score(SeqArgs sa, DecodeArgs 
     for (int o = 32; o > 0; o >>= 1) ne += __shfl_xor(ne, o, 64);
     uint32_t* ct = ws.ctop + ((int64_t)(b * da.H + g * GS + hh) * chm + chunk) * 8;
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
+    for (int r4 = 0; r4 < DEC_CHUNK_TOPS; ++r4) {
       uint32_t mx = max(u[0], u[1]);
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(SCORE_THREADS) void k_score(SeqArgs sa, DecodeArgs 
       }
       if (lane == 0) ct[r4] = mx;
     }
-    if (lane == 0) ct[4] = (uint32_t)ne;
+    if (lane == 0) ct[DEC_CHUNK_TOPS] = (uint32_t)ne;
   }
 }
 
@@ -602,7 +602,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
     const int nch = (C + SC - 1) / SC;
     const uint32_t* ct = ws.ctop + bhs * (da.NP - da.P) * 8;
     int e = 0;
-    for (int i = tid; i < nch; i += nt) e += (int)ct[(int64_t)i * 8 + 4];
+    for (int i = tid; i < nch; i += nt) e += (int)ct[(int64_t)i * 8 + DEC_CHUNK_TOPS];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) e += __shfl_xor(e, o, 64);
     Ew = e;
@@ -727,17 +727,17 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
     }
   }
 
-  // 3a. keys read from memory: a threshold t from the chunks' top-4 keys (the k-th largest
+  // 3a. keys read from memory: a threshold t from the chunks' top keys (the k-th largest
   // of them is at most the k-th largest key, so the keys >= t hold the selection), one
   // pass collecting those keys into LDS, and a sort of them
   bool done = false;
   if constexpr (!INREG) {
     const int nch = (C + SC - 1) / SC;
     const uint32_t* ct = ws.ctop + bhs * (da.NP - da.P) * 8;
-    if (k > 0 && k <= 4 * nch && nch <= TK_THREADS) {
-      uint32_t tv[4];
+    if (k > 0 && k <= DEC_CHUNK_TOPS * nch && nch <= TK_THREADS) {
+      uint32_t tv[DEC_CHUNK_TOPS];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) tv[r] = tid < nch ? ct[(int64_t)tid * 8 + r] : 0u;
+      for (int r = 0; r < DEC_CHUNK_TOPS; ++r) tv[r] = tid < nch ? ct[(int64_t)tid * 8 + r] : 0u;
       // t = the k-th largest of them (zeros included): a radix select, 8 bits a pass from
       // the top; a wave counts equal digits by matching the 8 digit bits with ballots and
       // the lowest lane of each match adds the count (one LDS atomic per distinct digit)
@@ -750,7 +750,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
           uint32_t* hist = L.rhist[pass & 1];
           if (tid < 256) L.rhist[(pass + 1) & 1][tid] = 0u;  // for the next pass (read two barriers ago)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
+          for (int r = 0; r < DEC_CHUNK_TOPS; ++r) {
             const uint32_t d = (tv[r] >> sh) & 255u;
             uint64_t m = __ballot((tv[r] & msk) == pre);
 #pragma unroll

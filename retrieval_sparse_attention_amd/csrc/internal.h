@@ -43,11 +43,17 @@ struct DecodeWs {
   int32_t* counts;   // [B*H*4] rows of the selected clusters, k, steady rows, 0
   float* part;       // [B*H*NP*132] partial softmax states: P row workgroups, then max_b ceil(C_b / 128)
                      // estimation chunks, then PT appended-token workgroups
-  uint32_t* ctop;    // [B*H*(NP-P)*8] per 128-cluster chunk of a (b, h): its 4 largest sortable keys, eligible count
+  uint32_t* ctop;    // [B*H*(NP-P)*8] per 128-cluster chunk of a (b, h): its DEC_CHUNK_TOPS largest sortable keys, eligible count
   uint64_t* sortg;   // [B*H*pow2(C_max)] global sort buffer (only when k_max > 4096)
 };
 
 constexpr int DEC_SCORE_CH = 128;
+// Largest sortable keys per 128-cluster chunk that k_score records for the top-k of keys
+// beyond registers (slots 0..6 of the chunk's 8-word record, the eligible count in slot 7):
+// the k-th largest of them bounds the k-th key from below. With 4 (1M layer: 1180 of 65,536)
+// up to 2,139 keys passed that bound and a few heads sorted 4,096 candidates (the slowest
+// head sets the launch time); with 7 the bound is nearly tight.
+constexpr int DEC_CHUNK_TOPS = 7;
 constexpr int DEC_TK_WAVES = 16;  // waves of a k_topk workgroup (one per (sequence, q head))
 constexpr int DEC_PART = 132;
 constexpr int DEC_SORT_LDS = 4096;
