@@ -426,6 +426,82 @@ __device__ inline void bitonic_desc_lds(uint64_t* a, int n) {
   if (waved) __syncthreads();
 }
 
+// The same sort for n = 1024 E keys and 16 waves, the keys in registers between the steps
+// that cross waves: lane l of wave w holds keys w 64 E + 64 e + l (e < E), so a step with
+// partner distance j < 64 is a lane shuffle, 64 <= j < 64 E a swap between a lane's own
+// registers, and only j >= 64 E goes through LDS with barriers (10 of the 66 steps of
+// 2048 keys; the LDS round trip of every wave-local step had made the sort the largest
+// phase of the top-k beyond registers).
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+template <int E>
+__device__ void bitonic_desc_reg(uint64_t* a, int n) {
+  constexpr int R = 64 * E;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint64_t x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = a[wv * R + 64 * e + lane];
+  bool inreg = true;
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= R) {
+        if (inreg) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) a[wv * R + 64 * e + lane] = x[e];
+          __syncthreads();
+          inreg = false;
+        }
+        for (int i = threadIdx.x; i < n; i += blockDim.x) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const uint64_t p = a[i], q = a[ixj];
+            const bool desc = (i & k) == 0;
+            if (desc ? (p < q) : (p > q)) { a[i] = q; a[ixj] = p; }
+          }
+        }
+        __syncthreads();
+        continue;
+      }
+      if (!inreg) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[e] = a[wv * R + 64 * e + lane];
+        inreg = true;
+      }
+      if (j >= 64) {
+        const int js = j >> 6;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if ((e & js) == 0) {
+            const int i = wv * R + 64 * e + lane;
+            const bool desc = (i & k) == 0;
+            const uint64_t p = x[e], q = x[e | js];
+            const uint64_t hi = p > q ? p : q, lo = p > q ? q : p;
+            x[e] = desc ? hi : lo;
+            x[e | js] = desc ? lo : hi;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = wv * R + 64 * e + lane;
+          const uint64_t q = shfl_xor64(x[e], j);
+          const bool keep_max = ((lane & j) == 0) == ((i & k) == 0);  // lower of the pair in a descending run
+          x[e] = keep_max ? (x[e] > q ? x[e] : q) : (x[e] > q ? q : x[e]);
+        }
+      }
+    }
+  }
+  if (inreg) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) a[wv * R + 64 * e + lane] = x[e];
+  }
+  __syncthreads();
+}
+
 // descending bitonic sort of n (power of two) unique u64 keys (LDS or global)
 __device__ inline void bitonic_desc(uint64_t* a, int n, bool global) {
   for (int k = 2; k <= n; k <<= 1) {
@@ -834,7 +910,14 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
           while (P2 < nc) P2 <<= 1;
           for (int i = nc + tid; i < P2; i += nt) cb[i] = 0ull;
           __syncthreads();
-          bitonic_desc_lds(cb, P2);
+          if (TK_WAVES == 16 && P2 == 1024)
+            bitonic_desc_reg<1>(cb, P2);
+          else if (TK_WAVES == 16 && P2 == 2048)
+            bitonic_desc_reg<2>(cb, P2);
+          else if (TK_WAVES == 16 && P2 == 4096)
+            bitonic_desc_reg<4>(cb, P2);
+          else
+            bitonic_desc_lds(cb, P2);
           // (key desc, id asc): the first k are the selection in rank order
           for (int r = tid; r < k; r += nt) {
             const int id = (int)(0xFFFFFFFFu - (uint32_t)(cb[r] & 0xFFFFFFFFu));
