@@ -829,6 +829,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
           for (int r = 0; r < DEC_CHUNK_TOPS; ++r) {
             const uint32_t d = (tv[r] >> sh) & 255u;
             uint64_t m = __ballot((tv[r] & msk) == pre);
+            if (m == 0ull) continue;  // no key of the wave still has the selected prefix
 #pragma unroll
             for (int b = 0; b < 8; ++b) {
               const uint64_t bb = __ballot((d >> b) & 1u);
