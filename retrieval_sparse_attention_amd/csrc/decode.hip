@@ -560,8 +560,12 @@ struct TopkLds {
   int32_t misc[8];
 };
 
-template <int NVR>
-__global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, wave_index ix, DecodeWs ws,
+// PF: prefetch every key's size and offset with the keys (as registers allow). That hides a
+// load round when the heads fit the CUs; with more heads than CUs its registers (72 at 8 keys
+// a lane) leave room for one workgroup per CU instead of two, so those launches take PF = false,
+// compiled for two workgroups per CU (64 registers).
+template <int NVR, bool PF = true>
+__global__ __launch_bounds__(TK_THREADS, PF ? 1 : 2 * TK_WAVES / 4) void k_topk(SeqArgs sa, DecodeArgs da, wave_index ix, DecodeWs ws,
                                                      int32_t* __restrict__ sel_ids) {
   constexpr bool INREG = NVR > 0;
   constexpr int CHK = INREG ? (NVR < 16 ? NVR : 16) : 8;  // keys per lane per chunk
@@ -599,7 +603,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(SeqArgs sa, DecodeArgs da, 
   // 0. loads in the order their values are needed (the load counter drains in issue
   // order): the keys, their sizes and offsets, then the steady tokens' clusters; LDS init
   // sizes and offsets of every key prefetched (as registers allow)
-  constexpr bool PRE = INREG && NVR <= (TK_WAVES <= 8 ? 16 : 8);
+  constexpr bool PRE = PF && INREG && NVR <= (TK_WAVES <= 8 ? 16 : 8);
   uint32_t ureg[INREG ? NVR : 1];
   int32_t nreg[PRE ? NVR : 1], oreg[PRE ? NVR : 1];
   if constexpr (INREG) {
@@ -1511,7 +1515,12 @@ static void launch_gs(const SeqArgs& sa, const DecodeArgs& da, const wave_index&
     case 1: hipLaunchKernelGGL(k_topk<1>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
     case 2: hipLaunchKernelGGL(k_topk<2>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
     case 4: hipLaunchKernelGGL(k_topk<4>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
-    case 8: hipLaunchKernelGGL(k_topk<8>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
+    case 8:
+      if (sa.B * da.H > 256)
+        hipLaunchKernelGGL((k_topk<8, false>), tg, tb, tl, st, sa, da, ix, ws, sel_ids);
+      else
+        hipLaunchKernelGGL((k_topk<8, true>), tg, tb, tl, st, sa, da, ix, ws, sel_ids);
+      break;
     case 16: hipLaunchKernelGGL(k_topk<16>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
     case 32: hipLaunchKernelGGL(k_topk<32>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
     default: hipLaunchKernelGGL(k_topk<0>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
@@ -1534,7 +1543,7 @@ hipError_t launch_decode(const SeqArgs& sa, const DecodeArgs& da, const wave_ind
     const void* fns[] = {reinterpret_cast<const void*>(&k_topk<0>),  reinterpret_cast<const void*>(&k_topk<1>),
                          reinterpret_cast<const void*>(&k_topk<2>),  reinterpret_cast<const void*>(&k_topk<4>),
                          reinterpret_cast<const void*>(&k_topk<8>),  reinterpret_cast<const void*>(&k_topk<16>),
-                         reinterpret_cast<const void*>(&k_topk<32>)};
+                         reinterpret_cast<const void*>(&k_topk<32>), reinterpret_cast<const void*>(&k_topk<8, false>)};
     for (const void* f : fns) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, tl);
     attrs = true;
   }
