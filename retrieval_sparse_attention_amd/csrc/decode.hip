@@ -502,6 +502,69 @@ __device__ void bitonic_desc_reg(uint64_t* a, int n) {
   __syncthreads();
 }
 
+// Descending sort of n = 1024 E keys in LDS by 16 waves: each wave sorts its 64 E keys in
+// registers (bitonic steps as lane shuffles and swaps inside a lane, no barrier), then every
+// key's place in the whole is its place in its own run plus, in each other run, the number of
+// keys above it (a binary search: the runs are sorted). Keys above 0 are distinct, so they
+// get distinct places; the zero padding gets places after them (possibly shared, never read).
+// Three barriers in all, against one per cross-wave step of a bitonic sort.
+template <int E>
+__device__ void sort_desc_runs(uint64_t* a, int n) {
+  constexpr int R = 64 * E;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint64_t x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = a[wv * R + 64 * e + lane];
+  for (int k = 2; k <= R; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= 64) {
+        const int js = j >> 6;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if ((e & js) == 0) {
+            const bool desc = ((64 * e + lane) & k) == 0;
+            const uint64_t p = x[e], q = x[e | js];
+            const uint64_t hi = p > q ? p : q, lo = p > q ? q : p;
+            x[e] = desc ? hi : lo;
+            x[e | js] = desc ? lo : hi;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint64_t q = shfl_xor64(x[e], j);
+          const bool keep_max = ((lane & j) == 0) == (((64 * e + lane) & k) == 0);
+          x[e] = keep_max ? (x[e] > q ? x[e] : q) : (x[e] > q ? q : x[e]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) a[wv * R + 64 * e + lane] = x[e];
+  __syncthreads();
+  // the 16 searches of a key advance together, one LDS read each per step (a search alone
+  // is a chain of 8 dependent reads); in its own run the count is its own place
+  int rank[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    int pos[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pos[r] = 0;
+#pragma unroll
+    for (int step = R / 2; step >= 1; step >>= 1)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pos[r] += a[r * R + pos[r] + step - 1] > x[e] ? step : 0;
+    int rk = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rk += pos[r] + ((pos[r] < R && a[r * R + min(pos[r], R - 1)] > x[e]) ? 1 : 0);
+    rank[e] = rk;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < E; ++e) a[rank[e]] = x[e];
+  __syncthreads();
+}
+
 // descending bitonic sort of n (power of two) unique u64 keys (LDS or global)
 __device__ inline void bitonic_desc(uint64_t* a, int n, bool global) {
   for (int k = 2; k <= n; k <<= 1) {
@@ -916,9 +979,9 @@ __global__ __launch_bounds__(TK_THREADS, PF ? 1 : 2 * TK_WAVES / 4) void k_topk(
           for (int i = nc + tid; i < P2; i += nt) cb[i] = 0ull;
           __syncthreads();
           if (TK_WAVES == 16 && P2 == 1024)
-            bitonic_desc_reg<1>(cb, P2);
+            sort_desc_runs<1>(cb, P2);
           else if (TK_WAVES == 16 && P2 == 2048)
-            bitonic_desc_reg<2>(cb, P2);
+            sort_desc_runs<2>(cb, P2);
           else if (TK_WAVES == 16 && P2 == 4096)
             bitonic_desc_reg<4>(cb, P2);
           else
