@@ -6,7 +6,9 @@
 // (steady zone), and every other cluster contributes through its centroid
 // (estimation zone). Four launches per call, all on the caller's stream:
 //   k_score  -- one pass over the centroid rows of a kv head: rank keys of the
-//               H/G q heads and eligibility
+//               H/G q heads (or, selection shared by the kv head, their sum) and
+//               eligibility; with tokens appended after the build, their exact
+//               attention too (tail workgroups, one partial per q head)
 //   k_topk   -- per (sequence, q head): exact top-k by (key desc, id asc), the
 //               selected ids and spans, steady-row corrections
 //   k_attend -- two roles in one grid: online-softmax attention over the selected
@@ -14,7 +16,8 @@
 //               cluster whose centroid term is counted takes that term back out);
 //               and the estimation term of every cluster (one pass over the value
 //               sums) as partial softmax states
-//   k_merge  -- log-sum-exp merge of the partials of every (sequence, q head)
+//   k_merge  -- log-sum-exp merge of the partials of every (sequence, q head): the
+//               row workgroups', the estimation chunks' and the tail workgroups'
 //
 // Estimation bookkeeping. The pages' estimation zone is E \ R with the value
 // sums and sizes of the clusters' non-steady members. k_attend adds the centroid
@@ -429,9 +432,8 @@ __device__ inline void bitonic_desc_lds(uint64_t* a, int n) {
 // The same sort for n = 1024 E keys and 16 waves, the keys in registers between the steps
 // that cross waves: lane l of wave w holds keys w 64 E + 64 e + l (e < E), so a step with
 // partner distance j < 64 is a lane shuffle, 64 <= j < 64 E a swap between a lane's own
-// registers, and only j >= 64 E goes through LDS with barriers (10 of the 66 steps of
-// 2048 keys; the LDS round trip of every wave-local step had made the sort the largest
-// phase of the top-k beyond registers).
+// registers, and only j >= 64 E goes through LDS with barriers (15 of the 78 steps of
+// 4096 keys, the size it serves; up to 2048 keys take sort_desc_runs below).
 __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
   const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
   const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
