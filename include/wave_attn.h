@@ -186,8 +186,8 @@ wave_status wave_attn_decode(const wave_index* index, const void* q, int32_t n_q
  *            Caller-owned, read only, 16-byte aligned.
  *  tail_cap: 1..WAVE_MAX_TAIL.
  *  tail_len: device int32 [B]; a value outside [0, tail_cap] is clamped to it.
- *  ws:       at least wave_attn_decode_tail_plan's size for this tail_cap (the
- *            row workgroups are planned for tail_cap appended tokens).
+ *  ws:       at least wave_attn_decode_tail_plan's size for this tail_cap (one
+ *            partial softmax state per q head and 64 appended tokens of capacity).
  * Other arguments and errors as wave_attn_decode; ARG also for a tail_cap out of
  * range or a NULL tail pointer, ALIGN for a misaligned one.
  */
