@@ -1506,16 +1506,23 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
 }
 
 // ------------------------------------------------------------------ k_merge
-// Log-sum-exp merge of the partials of one (b, h): the P row partials and one
-// centroid partial per estimation chunk. Thread (sub, dq) takes dims 4dq..4dq+3
-// over partials sub, sub + 8, ...; the 8 subsets meet in LDS. Row partials may
-// carry negative sums (they take centroid terms back out); the total is positive.
+// Log-sum-exp merge of the partials of one (b, h): the P row partials, one centroid
+// partial per estimation chunk and the tail workgroups' partials. SPLIT workgroups per
+// (b, h), each 128 / SPLIT dims: all take the maximum and the total weight over every
+// partial; thread (sub, dq) sums dims 4dq..4dq+3 of its workgroup's part over partials sub,
+// sub + nsub, ...; the subsets meet in LDS. Row partials may carry negative sums (they take
+// centroid terms back out); the total is positive. The host splits a head's merge 4 ways
+// when it has many partials (the 1M layer's ~590 per head: 19 -> 11 us) and not otherwise
+// (the batched layers' 512 heads with ~80 each merged 30% slower split).
+constexpr int MERGE_SPLIT_MIN_PARTIALS = 256;
+
+template <int SPLIT>
 __global__ __launch_bounds__(256) void k_merge(SeqArgs sa, DecodeArgs da, DecodeWs ws, float* __restrict__ out,
                                                float* __restrict__ lse) {
-  __shared__ float4 accs[8][32];
-  __shared__ float ls[8];
+  __shared__ float4 accs[256];
+  __shared__ float ls[32];
   __shared__ float mx[4];
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x / SPLIT, dpart = blockIdx.x % SPLIT;
   const int b = bh / da.H;
   // partials: P row workgroups, this sequence's estimation chunks, then the PT appended-token
   // workgroups (after the slots of the longest sequence's chunks)
@@ -1524,7 +1531,9 @@ __global__ __launch_bounds__(256) void k_merge(SeqArgs sa, DecodeArgs da, Decode
   const int skip = da.NP - da.PT - nlead;
   auto slot = [&](int i) { return (int64_t)(i < nlead ? i : i + skip) * PART; };
   const float* pp = ws.part + (int64_t)bh * da.NP * PART;
-  const int tid = threadIdx.x, dq = tid & 31, sub = tid >> 5;
+  constexpr int nd = 32 / SPLIT, nsub = 256 / nd;  // float4 columns of the part, subsets
+  const int tid = threadIdx.x, dq = tid % nd, sub = tid / nd;
+  const int d0 = (D / SPLIT) * dpart;
   float M = -INFINITY;
   for (int i = tid; i < npart; i += 256) M = fmaxf(M, pp[slot(i)]);
   M = wave_max(M);
@@ -1534,30 +1543,30 @@ __global__ __launch_bounds__(256) void k_merge(SeqArgs sa, DecodeArgs da, Decode
   float4 A = make_float4(0.f, 0.f, 0.f, 0.f);
   float Ls = 0.f;
 #pragma unroll 4
-  for (int i = sub; i < npart; i += 8) {
+  for (int i = sub; i < npart; i += nsub) {
     const float* p = pp + slot(i);
     const float mi = p[0];
-    const float4 a = *reinterpret_cast<const float4*>(p + 4 + 4 * dq);
+    const float4 a = *reinterpret_cast<const float4*>(p + 4 + d0 + 4 * dq);
     const float li = p[1];
     const float f = (mi == -INFINITY) ? 0.f : exp2f(mi - M);
     Ls += li * f;
     A.x += a.x * f; A.y += a.y * f; A.z += a.z * f; A.w += a.w * f;
   }
-  accs[sub][dq] = A;
+  accs[tid] = A;
   if (dq == 0) ls[sub] = Ls;
   __syncthreads();
-  if (tid < 32) {
-    float4 s = accs[0][tid];
+  if (tid < nd) {
+    float4 s = accs[tid];
     float Lt = ls[0];
-    for (int k = 1; k < 8; ++k) {
-      const float4 t = accs[k][tid];
+    for (int k = 1; k < nsub; ++k) {
+      const float4 t = accs[k * nd + tid];
       s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
       Lt += ls[k];
     }
     float4 r;
     r.x = s.x / Lt; r.y = s.y / Lt; r.z = s.z / Lt; r.w = s.w / Lt;
-    *reinterpret_cast<float4*>(out + (int64_t)bh * D + 4 * tid) = r;
-    if (lse != nullptr && tid == 0) lse[bh] = (M + log2f(Lt)) * 0.6931471805599453f;
+    *reinterpret_cast<float4*>(out + (int64_t)bh * D + d0 + 4 * tid) = r;
+    if (lse != nullptr && tid == 0 && dpart == 0) lse[bh] = (M + log2f(Lt)) * 0.6931471805599453f;
   }
 }
 
@@ -1596,7 +1605,10 @@ static void launch_gs(const SeqArgs& sa, const DecodeArgs& da, const wave_index&
                      ix, ws, q);
   prof_end(st);
   prof_begin("k_merge", st);
-  hipLaunchKernelGGL(k_merge, dim3(sa.B * da.H), dim3(256), 0, st, sa, da, ws, out, lse);
+  if (da.NP >= MERGE_SPLIT_MIN_PARTIALS)
+    hipLaunchKernelGGL(k_merge<4>, dim3(sa.B * da.H * 4), dim3(256), 0, st, sa, da, ws, out, lse);
+  else
+    hipLaunchKernelGGL(k_merge<1>, dim3(sa.B * da.H), dim3(256), 0, st, sa, da, ws, out, lse);
   prof_end(st);
 }
 
