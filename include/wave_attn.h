@@ -20,8 +20,12 @@
  *    consecutive blocks of N_b rows (kv head major): row of (b, g, t) is
  *    G * sum_{b'<b} N_b' + g * N_b + t;
  *  - the caller owns and allocates every buffer (device memory unless noted
- *    "host"); the library never allocates device memory and keeps no global
- *    state apart from a thread-local error message;
+ *    "host"); the library never allocates device memory;
+ *  - process-wide state: a thread-local error message; a once-per-device set-up
+ *    (kernel attributes, compute-unit count; std::call_once, so concurrent first
+ *    calls are safe); and the kernel timing hook below (mutex-guarded, off unless
+ *    enabled). Calls on different streams, each with its own workspace and
+ *    outputs, may run concurrently from several host threads over one index;
  *  - all argument checks run on the host before anything is enqueued; on an
  *    error status nothing is enqueued and no output is touched; device faults
  *    surface at the caller's next synchronisation of the stream;
@@ -135,7 +139,10 @@ wave_status wave_index_build(const wave_shape* shape, const void* K, const void*
                              size_t ws_bytes, int32_t* assign_trace, wave_stream_t stream);
 
 /*
- * wave_attn_decode_plan -- host only. For q heads n_q_heads (a multiple of G,
+ * wave_attn_decode_plan -- host only. Sizes of the query-dependent phase (Vortex
+ * technical summary, section 2.A: the indexer step runs per query against the
+ * pre-processed cache; RetroInfer page, section 2.A: the retrieval zone holds the
+ * clusters most similar to the query). For q heads n_q_heads (a multiple of G,
  * at most WAVE_MAX_GROUP per kv head), steady zone (n_sink, n_local) and
  * topk_frac in [0, 1]: k_max = max_b min(ceil(topk_frac*C_b), C_b) (the id
  * columns of wave_attn_decode) and the decode workspace size in bytes.
@@ -152,7 +159,8 @@ wave_status wave_attn_decode_plan(const wave_index* index, int32_t n_q_heads, in
  *   n'_j, Vsum'_j = cluster j's size and value sum without its steady tokens;
  *   E = {j : n'_j > 0};  k_b = min(ceil(topk_frac*C_b), |E|);
  *   R = the k_b clusters of E with the largest rank key (a fixed-order fp32
- *       inner product of q and the bf16 centroid; ties: lower id);
+ *       inner product of q and the bf16 centroid, each product rounded to fp32
+ *       before it is added; ties: lower id);
  *   retrieval zone: exact attention over the non-steady members of R;
  *   estimation zone: every j in E \ R adds exp(s_j)*n'_j to the denominator
  *       and exp(s_j)*Vsum'_j to the numerator, s_j = q . chat_j / sqrt(128);
@@ -251,13 +259,16 @@ wave_status wave_attn_decode_topk(const wave_index* index, const void* q, int32_
 const char* wave_last_error(void);
 
 /*
- * Kernel timing hook (not part of the method): while enabled, every kernel
- * launch of the calls above is bracketed by a pair of HIP events recorded on
- * the launch stream. wave_profiler_read synchronises on those events and
- * returns, per kernel name, the number of launches and their summed duration.
+ * Kernel timing hook (not part of the method): while enabled, every kernel of
+ * the calls above is launched with a start/stop HIP event pair that the dispatch
+ * itself records (hipExtLaunchKernel), so a pair times that kernel alone.
+ * wave_profiler_read synchronises on those events and returns, per kernel name,
+ * the number of launches and their summed duration.
  *  wave_profiler_enable(1) clears previous records and starts recording;
  *  wave_profiler_enable(0) stops. names: host buffer of n_max * 64 chars.
  * Returns the number of distinct kernels written (or a negative status).
+ * The records are process-wide (one list for every thread and device, guarded
+ * by a mutex); keep the hook off while capturing HIP graphs.
  */
 wave_status wave_profiler_enable(int32_t on);
 int32_t wave_profiler_read(char* names, int64_t* launches, double* total_ms, int32_t n_max);

@@ -443,7 +443,8 @@ void ref_block_assign(int32_t B, int32_t G, const int64_t* ctx, int32_t seg_len,
  * Rank key of a cluster for retrieval [bit-defined]. The retrieval zone ranks
  * clusters by similarity to the query; the reading is the inner product
  * q . chat_j, summed in a fixed fp32 order so that every implementation ranks
- * identically: p_i = fl32(q_i * c_i) (exact, both factors are bf16); 16 lane
+ * identically: p_i = fl32(q_i * c_i) (exact for bf16 factors unless the product
+ * is below 2^-126 in magnitude or overflows); 16 lane
  * sums u_l = (((+0 + p_8l) + p_8l+1) + ... + p_8l+7); a butterfly over the 16
  * lanes, for s = 8, 4, 2, 1 at once u_l = u_l + u_(l xor s); key = u_0 + 0.0f
  * (which turns -0 into +0).

@@ -106,6 +106,68 @@ def _shape(n_kv_heads, ctx):
     return sh, ctx_arr
 
 
+def _check_tensor(t, name, dtype, shape):
+    """Raise ValueError unless t is a contiguous `dtype` tensor of `shape`."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch tensor" % name)
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _check_devices(device, **tensors):
+    """Every tensor on the GPU `device` (the library reads and writes device memory only)."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError("%s must be on the GPU, got %s" % (name, t.device))
+        if t.device != device:
+            raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+
+
+def _check_reuse(index, n_kv_heads, ctx, seg_len, clusters_per_seg):
+    """An index passed for reuse must have been planned for exactly this shape."""
+    if (index.n_kv_heads != int(n_kv_heads) or index.ctx != [int(n) for n in ctx]
+            or index.seg_len != int(seg_len) or index.clusters_per_seg != int(clusters_per_seg)):
+        raise ValueError("index was allocated for n_kv_heads=%d ctx=%s seg_len=%d clusters_per_seg=%d, not for "
+                         "n_kv_heads=%d ctx=%s seg_len=%d clusters_per_seg=%d"
+                         % (index.n_kv_heads, index.ctx, index.seg_len, index.clusters_per_seg, int(n_kv_heads),
+                            [int(n) for n in ctx], int(seg_len), int(clusters_per_seg)))
+
+
+def _check_build_io(K, V, index, ws, z):
+    _check_tensor(K, "K", torch.bfloat16, (z["rows"], HEAD_DIM))
+    _check_tensor(V, "V", torch.bfloat16, (z["rows"], HEAD_DIM))
+    if ws is not None:
+        _check_tensor(ws, "ws", torch.uint8, (ws.numel(),))
+        if ws.numel() < z["build_ws_bytes"]:
+            raise ValueError("workspace has %d bytes, the build needs %d" % (ws.numel(), z["build_ws_bytes"]))
+    _check_devices(index.device if index is not None else K.device, K=K, V=V, ws=ws)
+
+
+def _check_decode_io(index, q, out, sel_ids, lse, ws, k_max, wsb, **more):
+    """q bf16 [B, H, 128] and the outputs of a decode call; then every tensor on the index's device."""
+    B, H = int(q.shape[0]), int(q.shape[1])
+    if B != len(index.ctx):
+        raise ValueError("q holds %d sequences, the index %d" % (B, len(index.ctx)))
+    _check_tensor(q, "q", torch.bfloat16, (B, H, HEAD_DIM))
+    if out is not None:
+        _check_tensor(out, "out", torch.float32, (B, H, HEAD_DIM))
+    if sel_ids is not None:
+        _check_tensor(sel_ids, "sel_ids", torch.int32, (B, H, max(k_max, 1)))
+    if lse is not None:
+        _check_tensor(lse, "lse", torch.float32, (B, H))
+    if ws is not None:
+        _check_tensor(ws, "ws", torch.uint8, (ws.numel(),))
+        if ws.numel() < wsb:
+            raise ValueError("workspace has %d bytes, the call needs %d" % (ws.numel(), wsb))
+    _check_devices(index.device, q=q, out=out, sel_ids=sel_ids, lse=lse, ws=ws, **more)
+
+
 def wave_index_plan(n_kv_heads, ctx, seg_len, clusters_per_seg):
     """Sizes of the index arrays and of the build workspace (dict)."""
     sh, _keep = _shape(n_kv_heads, ctx)
@@ -125,6 +187,7 @@ class WaveIndex:
         self.arrays = arrays
         for k, v in arrays.items():
             setattr(self, k, v)
+        self.device = arrays["k_sorted"].device
         sh, self._ctx_arr = _shape(n_kv_heads, self.ctx)
         self.c = _Index()
         self.c.shape = sh
@@ -161,10 +224,12 @@ def wave_index_build(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, iters, se
     Returns the WaveIndex (and the [iters, rows] int32 assignment trace if asked).  `index`
     and `ws` may be passed to reuse existing allocations.
     """
+    z = wave_index_plan(n_kv_heads, ctx, seg_len, clusters_per_seg)
+    if index is not None:
+        _check_reuse(index, n_kv_heads, ctx, seg_len, clusters_per_seg)
+    _check_build_io(K, V, index, ws, z)
     if index is None:
         index, z = WaveIndex.allocate(n_kv_heads, ctx, seg_len, clusters_per_seg, device=K.device)
-    else:
-        z = wave_index_plan(n_kv_heads, ctx, seg_len, clusters_per_seg)
     if ws is None:
         ws = torch.empty(max(int(z["build_ws_bytes"]), 16), dtype=torch.uint8, device=K.device)
     tr = torch.empty((iters, z["rows"]), dtype=torch.int32, device=K.device) if assign_trace else None
@@ -178,10 +243,12 @@ def wave_index_build(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, iters, se
 
 def wave_index_build_blocks(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, stream=None, index=None, ws=None):
     """Index of the block top-k baseline: contiguous blocks in place of the k-means clusters."""
+    z = wave_index_plan(n_kv_heads, ctx, seg_len, clusters_per_seg)
+    if index is not None:
+        _check_reuse(index, n_kv_heads, ctx, seg_len, clusters_per_seg)
+    _check_build_io(K, V, index, ws, z)
     if index is None:
         index, z = WaveIndex.allocate(n_kv_heads, ctx, seg_len, clusters_per_seg, device=K.device)
-    else:
-        z = wave_index_plan(n_kv_heads, ctx, seg_len, clusters_per_seg)
     if ws is None:
         ws = torch.empty(max(int(z["build_ws_bytes"]), 16), dtype=torch.uint8, device=K.device)
     sh = _Shape()
@@ -208,8 +275,11 @@ def wave_attn_decode(index, q, n_sink, n_local, topk_frac, ws=None, out=None, se
     estimate=False: top-k retrieval only (wave_attn_decode_topk); shared=True: one
     selection per kv head (wave_attn_decode_shared).
     """
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be a [B, H, 128] tensor")
     B, H = q.shape[0], q.shape[1]
     k_max, wsb = wave_attn_decode_plan(index, H, n_sink, n_local, topk_frac)
+    _check_decode_io(index, q, out, sel_ids, lse, ws, k_max, wsb)
     dev = q.device
     if ws is None:
         ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
@@ -246,13 +316,17 @@ def wave_attn_decode_tail(index, q, n_sink, n_local, topk_frac, k_tail, v_tail, 
                           sel_ids=None, lse=None, stream=None):
     """Wave attention plus the tokens appended after the build: k_tail, v_tail bf16 [B, G, cap, 128] and
     tail_len int32 [B] on the device. Returns as wave_attn_decode."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be a [B, H, 128] tensor")
     B, H = q.shape[0], q.shape[1]
+    if not isinstance(k_tail, torch.Tensor) or k_tail.dim() != 4:
+        raise ValueError("k_tail must be a [B, G, cap, 128] tensor")
     cap = int(k_tail.shape[2])
-    if tuple(v_tail.shape) != tuple(k_tail.shape) or tuple(k_tail.shape[:2]) != (B, index.n_kv_heads) or k_tail.shape[3] != 128:
-        raise ValueError("k_tail and v_tail must be [B, G, cap, 128]")
-    if tail_len.dtype != torch.int32 or tail_len.numel() != B:
-        raise ValueError("tail_len must be int32 [B]")
+    _check_tensor(k_tail, "k_tail", torch.bfloat16, (B, index.n_kv_heads, cap, HEAD_DIM))
+    _check_tensor(v_tail, "v_tail", torch.bfloat16, (B, index.n_kv_heads, cap, HEAD_DIM))
+    _check_tensor(tail_len, "tail_len", torch.int32, (B,))
     k_max, wsb = wave_attn_decode_tail_plan(index, H, n_sink, n_local, topk_frac, cap)
+    _check_decode_io(index, q, out, sel_ids, lse, ws, k_max, wsb, k_tail=k_tail, v_tail=v_tail, tail_len=tail_len)
     dev = q.device
     if ws is None:
         ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)

@@ -1171,20 +1171,23 @@ __global__ __launch_bounds__(1024) void k_block_assign(SeqArgs sa, int32_t* __re
 }
 
 // ------------------------------------------------------------------ host side
+hipError_t build_set_attrs() {
+  WAVE_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_init), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               160 * 1024));
+  WAVE_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_assign<false>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(AssignLds)));
+  WAVE_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_assign<true>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(AssignLds)));
+  WAVE_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sort), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               16 * WAVE_MAX_CLUSTERS_PER_SEG * 4));
+  WAVE_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sort_radix),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, 2 * RS_MAXL * 4));
+  return hipSuccess;
+}
+
 // Workgroups per unit of the LDS radix sort: 2 when the units alone would leave more than
 // half of the compute units idle (one 1024-thread workgroup per CU), else 1.
-static int sort_parts(int64_t units) {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      cus = n;
-    else
-      cus = 256;
-  }
-  return 2 * units <= cus ? 2 : 1;
-}
+static int sort_parts(int64_t units, int cus) { return 2 * units <= cus ? 2 : 1; }
 // Tokens per k_assign workgroup: enough workgroups per segment that the units fill
 // the 256 compute units once (one workgroup per CU: its LDS and registers take the CU),
 // in whole tiles.
@@ -1210,20 +1213,8 @@ static int64_t assign_grid(const SeqArgs& sa, int tpw) {
 hipError_t launch_build(const SeqArgs& sa, const void* Kv, const void* Vv, int32_t iters, uint64_t seed,
                         const wave_index& ix, const BuildWs& ws, int64_t units, int32_t* trace, int64_t rows,
                         hipStream_t st) {
-  static bool attrs = false;
-  if (!attrs) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_init), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              160 * 1024);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_assign<false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(AssignLds));
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_assign<true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(AssignLds));
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sort), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              16 * WAVE_MAX_CLUSTERS_PER_SEG * 4);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sort_radix),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 2 * RS_MAXL * 4);
-    attrs = true;
-  }
+  const DeviceInfo& di = device_info();
+  WAVE_TRY(di.status);
   const uint16_t* K = reinterpret_cast<const uint16_t*>(Kv);
   const uint16_t* V = reinterpret_cast<const uint16_t*>(Vv);
   int64_t nclu = 0;
@@ -1231,85 +1222,58 @@ hipError_t launch_build(const SeqArgs& sa, const void* Kv, const void* Vv, int32
   const size_t init_lds = ((2 * (size_t)sa.seg_len + 15) & ~(size_t)15) + 4 * (size_t)sa.K_s;
   const size_t sort_lds = 16 * (size_t)sa.K_s * 4;
   // two key buffers of E tiles; the counters (32 digits x E tiles x 16 waves) fit in one
-  const int sparts = sort_parts(units);
+  const int sparts = sort_parts(units, di.cus);
   const size_t radix_tiles = ((size_t)(sa.seg_len + sparts - 1) / sparts + RS_THREADS - 1) / RS_THREADS;
   const size_t radix_lds = 2 * radix_tiles * RS_THREADS * 4;
   const unsigned cgrid = (unsigned)((nclu + 3) / 4);
   uint16_t* chat = reinterpret_cast<uint16_t*>(ix.centroids_bf16);
-  prof_begin("k_init", st);
-  hipLaunchKernelGGL(k_init, dim3((unsigned)units), dim3(INIT_THREADS), init_lds, st, sa, seed, K, ix.centroids, chat,
-                     ws.norm);
-  prof_end(st);
+  WAVE_TRY(launch("k_init", k_init, dim3((unsigned)units), dim3(INIT_THREADS), init_lds, st, sa, seed, K,
+                  ix.centroids, chat, ws.norm));
   const int tpw = assign_tpw(sa, units);
   const int64_t agrid = assign_grid(sa, tpw);
   for (int it = 0; it < iters; ++it) {
-    prof_begin("k_assign", st);
-    if (sa.K_s > AS_GROUP)
-      hipLaunchKernelGGL(k_assign<true>, dim3((unsigned)agrid), dim3(AS_THREADS), sizeof(AssignLds), st, sa, tpw, K,
-                         chat, ws.norm, ix.assign, ws.xn2, it == 0 ? 1 : 0);
-    else
-      hipLaunchKernelGGL(k_assign<false>, dim3((unsigned)agrid), dim3(AS_THREADS), sizeof(AssignLds), st, sa, tpw, K,
-                         chat, ws.norm, ix.assign, ws.xn2, it == 0 ? 1 : 0);
-    prof_end(st);
-    if (trace != nullptr) {
-      hipError_t e = hipMemcpyAsync(trace + (int64_t)it * rows, ix.assign, sizeof(int32_t) * (size_t)rows,
-                                    hipMemcpyDeviceToDevice, st);
-      if (e != hipSuccess) return e;
-    }
-    prof_begin("k_sort", st);
+    WAVE_TRY(launch("k_assign", sa.K_s > AS_GROUP ? k_assign<true> : k_assign<false>, dim3((unsigned)agrid),
+                    dim3(AS_THREADS), sizeof(AssignLds), st, sa, tpw, K, chat, ws.norm, ix.assign, ws.xn2,
+                    it == 0 ? 1 : 0));
+    if (trace != nullptr)
+      WAVE_TRY(hipMemcpyAsync(trace + (int64_t)it * rows, ix.assign, sizeof(int32_t) * (size_t)rows,
+                              hipMemcpyDeviceToDevice, st));
     if (sa.seg_len <= RS_MAXL)
-      hipLaunchKernelGGL(k_sort_radix, dim3((unsigned)(units * sparts)), dim3(RS_THREADS), radix_lds, st, sa, sparts,
-                         ix.assign, ix.sizes, ix.offsets, ix.perm);
+      WAVE_TRY(launch("k_sort", k_sort_radix, dim3((unsigned)(units * sparts)), dim3(RS_THREADS), radix_lds, st, sa,
+                      sparts, ix.assign, ix.sizes, ix.offsets, ix.perm));
     else
-      hipLaunchKernelGGL(k_sort, dim3((unsigned)units), dim3(SORT_THREADS), sort_lds, st, sa, ix.assign, ws.rank,
-                         ix.sizes, ix.offsets, ix.perm);
-    prof_end(st);
-    prof_begin("k_update", st);
-    if (it + 1 < iters)
-      hipLaunchKernelGGL(k_update<false>, dim3(cgrid), dim3(256), 0, st, sa, nclu, K, V, ix, ws.norm);
-    else
-      hipLaunchKernelGGL(k_update<true>, dim3(cgrid), dim3(256), 0, st, sa, nclu, K, V, ix, ws.norm);
-    prof_end(st);
+      WAVE_TRY(launch("k_sort", k_sort, dim3((unsigned)units), dim3(SORT_THREADS), sort_lds, st, sa, ix.assign,
+                      ws.rank, ix.sizes, ix.offsets, ix.perm));
+    WAVE_TRY(launch("k_update", it + 1 < iters ? k_update<false> : k_update<true>, dim3(cgrid), dim3(256), 0, st, sa,
+                    nclu, K, V, ix, ws.norm));
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 hipError_t launch_build_blocks(const SeqArgs& sa, const void* Kv, const void* Vv, const wave_index& ix,
                                const BuildWs& ws, int64_t units, hipStream_t st) {
-  static bool attrs = false;
-  if (!attrs) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sort), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              16 * WAVE_MAX_CLUSTERS_PER_SEG * 4);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sort_radix),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 2 * RS_MAXL * 4);
-    attrs = true;
-  }
+  const DeviceInfo& di = device_info();
+  WAVE_TRY(di.status);
   const uint16_t* K = reinterpret_cast<const uint16_t*>(Kv);
   const uint16_t* V = reinterpret_cast<const uint16_t*>(Vv);
   int64_t nclu = 0;
   for (int b = 0; b < sa.B; ++b) nclu += (int64_t)sa.G * sa.C[b];
   const size_t sort_lds = 16 * (size_t)sa.K_s * 4;
-  const int sparts = sort_parts(units);
+  const int sparts = sort_parts(units, di.cus);
   const size_t radix_tiles = ((size_t)(sa.seg_len + sparts - 1) / sparts + RS_THREADS - 1) / RS_THREADS;
   const size_t radix_lds = 2 * radix_tiles * RS_THREADS * 4;
   const unsigned cgrid = (unsigned)((nclu + 3) / 4);
-  prof_begin("k_block_assign", st);
-  hipLaunchKernelGGL(k_block_assign, dim3((unsigned)units), dim3(1024), 0, st, sa, ix.assign);
-  prof_end(st);
+  WAVE_TRY(launch("k_block_assign", k_block_assign, dim3((unsigned)units), dim3(1024), 0, st, sa, ix.assign));
   // the layout pass of the k-means build over the block labels: counts, offsets, the
   // (identity) order, member means, bf16 centroids, value sums
-  prof_begin("k_sort", st);
   if (sa.seg_len <= RS_MAXL)
-    hipLaunchKernelGGL(k_sort_radix, dim3((unsigned)(units * sparts)), dim3(RS_THREADS), radix_lds, st, sa, sparts,
-                       ix.assign, ix.sizes, ix.offsets, ix.perm);
+    WAVE_TRY(launch("k_sort", k_sort_radix, dim3((unsigned)(units * sparts)), dim3(RS_THREADS), radix_lds, st, sa,
+                    sparts, ix.assign, ix.sizes, ix.offsets, ix.perm));
   else
-    hipLaunchKernelGGL(k_sort, dim3((unsigned)units), dim3(SORT_THREADS), sort_lds, st, sa, ix.assign, ws.rank,
-                       ix.sizes, ix.offsets, ix.perm);
-  prof_end(st);
-  prof_begin("k_update", st);
-  hipLaunchKernelGGL(k_update<true>, dim3(cgrid), dim3(256), 0, st, sa, nclu, K, V, ix, ws.norm);
-  prof_end(st);
-  return hipGetLastError();
+    WAVE_TRY(launch("k_sort", k_sort, dim3((unsigned)units), dim3(SORT_THREADS), sort_lds, st, sa, ix.assign,
+                    ws.rank, ix.sizes, ix.offsets, ix.perm));
+  WAVE_TRY(launch("k_update", k_update<true>, dim3(cgrid), dim3(256), 0, st, sa, nclu, K, V, ix, ws.norm));
+  return hipSuccess;
 }
 
 }  // namespace wave

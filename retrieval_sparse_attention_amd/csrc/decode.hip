@@ -72,9 +72,13 @@ __device__ __forceinline__ int64_t steady_pos(const Steady& s, int i) {
 
 // ------------------------------------------------------------------ k_score
 // Rank key r_{h,j}: 16 lanes each own 8 consecutive dims of the centroid row;
-// each lane sums its 8 exact bf16 products from +0 in dim order (an fma of
-// two bf16 values equals a rounded product then a rounded add), then an xor
-// butterfly over the 16 lanes with strides 8, 4, 2, 1, then +0.0f.
+// each lane sums its 8 products in dim order, every product rounded to fp32 on
+// its own before it is added (a bf16 x bf16 product is exact in fp32 unless it
+// falls below 2^-126 or overflows, so a fused multiply-add would differ there),
+// then an xor butterfly over the 16 lanes with strides 8, 4, 2, 1, then +0.0f.
+// The lane sum starts at the first product instead of +0 + it: the two differ
+// only in the sign of a zero, which every later addition either discards or
+// keeps as a zero, and the final +0.0f turns -0 into +0.
 //
 // One workgroup per (b, g, 128 clusters), 16-lane groups over the centroid rows.
 // A cluster is eligible (in E) when it has a member outside the steady zone; the
@@ -166,9 +170,13 @@ __global__ __launch_bounds__(SCORE_THREADS) void k_score(SeqArgs sa, DecodeArgs 
                         bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
 #pragma unroll
     for (int hh = 0; hh < GS; ++hh) {
-      float u = 0.f;
+      float u;
+      {
+#pragma clang fp contract(off)
+        u = qf[hh][0] * c[0];
 #pragma unroll
-      for (int m = 0; m < 8; ++m) u = fmaf(qf[hh][m], c[m], u);
+        for (int m = 1; m < 8; ++m) u = u + qf[hh][m] * c[m];
+      }
       u = row_sum16(u);
       if (l16 == hh) S.kw[hh][jj] = u + 0.0f;
     }
@@ -1571,75 +1579,65 @@ __global__ __launch_bounds__(256) void k_merge(SeqArgs sa, DecodeArgs da, Decode
 }
 
 // ------------------------------------------------------------------ host side
+hipError_t decode_set_attrs() {
+  const size_t tl = sizeof(TopkLds);
+  const void* fns[] = {reinterpret_cast<const void*>(&k_topk<0>),  reinterpret_cast<const void*>(&k_topk<1>),
+                       reinterpret_cast<const void*>(&k_topk<2>),  reinterpret_cast<const void*>(&k_topk<4>),
+                       reinterpret_cast<const void*>(&k_topk<8>),  reinterpret_cast<const void*>(&k_topk<16>),
+                       reinterpret_cast<const void*>(&k_topk<32>), reinterpret_cast<const void*>(&k_topk<8, false>)};
+  for (const void* f : fns) WAVE_TRY(hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, tl));
+  return hipSuccess;
+}
+
 template <int GS>
-static void launch_gs(const SeqArgs& sa, const DecodeArgs& da, const wave_index& ix, const DecodeWs& ws,
-                      const uint16_t* q, float* out, int32_t* sel_ids, float* lse, hipStream_t st, int nscore,
-                      int nest) {
-  prof_begin("k_score", st);
+static hipError_t launch_gs(const SeqArgs& sa, const DecodeArgs& da, const wave_index& ix, const DecodeWs& ws,
+                            const uint16_t* q, float* out, int32_t* sel_ids, float* lse, hipStream_t st, int nscore,
+                            int nest) {
   if (da.PT > 0)
-    hipLaunchKernelGGL((k_score<GS, true>), dim3(nscore + sa.B * sa.G * da.PT), dim3(SCORE_THREADS), 0, st, sa, da,
-                       ix, q, ws);
+    WAVE_TRY(launch("k_score", k_score<GS, true>, dim3(nscore + sa.B * sa.G * da.PT), dim3(SCORE_THREADS), 0, st, sa,
+                    da, ix, q, ws));
   else
-    hipLaunchKernelGGL((k_score<GS, false>), dim3(nscore), dim3(SCORE_THREADS), 0, st, sa, da, ix, q, ws);
-  prof_end(st);
-  prof_begin("k_topk", st);
+    WAVE_TRY(launch("k_score", k_score<GS, false>, dim3(nscore), dim3(SCORE_THREADS), 0, st, sa, da, ix, q, ws));
   const dim3 tg(sa.B * da.H), tb(TK_THREADS);
   const size_t tl = sizeof(TopkLds);
+  void (*tk)(SeqArgs, DecodeArgs, wave_index, DecodeWs, int32_t*);
   switch (da.NV) {
-    case 1: hipLaunchKernelGGL(k_topk<1>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
-    case 2: hipLaunchKernelGGL(k_topk<2>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
-    case 4: hipLaunchKernelGGL(k_topk<4>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
-    case 8:
-      if (sa.B * da.H > 256)
-        hipLaunchKernelGGL((k_topk<8, false>), tg, tb, tl, st, sa, da, ix, ws, sel_ids);
-      else
-        hipLaunchKernelGGL((k_topk<8, true>), tg, tb, tl, st, sa, da, ix, ws, sel_ids);
-      break;
-    case 16: hipLaunchKernelGGL(k_topk<16>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
-    case 32: hipLaunchKernelGGL(k_topk<32>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
-    default: hipLaunchKernelGGL(k_topk<0>, tg, tb, tl, st, sa, da, ix, ws, sel_ids); break;
+    case 1: tk = k_topk<1>; break;
+    case 2: tk = k_topk<2>; break;
+    case 4: tk = k_topk<4>; break;
+    case 8: tk = sa.B * da.H > 256 ? k_topk<8, false> : k_topk<8, true>; break;
+    case 16: tk = k_topk<16>; break;
+    case 32: tk = k_topk<32>; break;
+    default: tk = k_topk<0>; break;
   }
-  prof_end(st);
-  prof_begin("k_attend", st);
-  hipLaunchKernelGGL(k_attend<GS>, dim3(sa.B * da.H * da.P + (da.est ? nest : 0)), dim3(ATT_THREADS), 0, st, sa, da,
-                     ix, ws, q);
-  prof_end(st);
-  prof_begin("k_merge", st);
+  WAVE_TRY(launch("k_topk", tk, tg, tb, tl, st, sa, da, ix, ws, sel_ids));
+  WAVE_TRY(launch("k_attend", k_attend<GS>, dim3(sa.B * da.H * da.P + (da.est ? nest : 0)), dim3(ATT_THREADS), 0, st,
+                  sa, da, ix, ws, q));
   if (da.NP >= MERGE_SPLIT_MIN_PARTIALS)
-    hipLaunchKernelGGL(k_merge<4>, dim3(sa.B * da.H * 4), dim3(256), 0, st, sa, da, ws, out, lse);
+    WAVE_TRY(launch("k_merge", k_merge<4>, dim3(sa.B * da.H * 4), dim3(256), 0, st, sa, da, ws, out, lse));
   else
-    hipLaunchKernelGGL(k_merge<1>, dim3(sa.B * da.H), dim3(256), 0, st, sa, da, ws, out, lse);
-  prof_end(st);
+    WAVE_TRY(launch("k_merge", k_merge<1>, dim3(sa.B * da.H), dim3(256), 0, st, sa, da, ws, out, lse));
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const SeqArgs& sa, const DecodeArgs& da, const wave_index& ix, const DecodeWs& ws,
                          const uint16_t* q, float* out, int32_t* sel_ids, float* lse, hipStream_t st) {
-  static bool attrs = false;
-  if (!attrs) {
-    const size_t tl = sizeof(TopkLds);
-    const void* fns[] = {reinterpret_cast<const void*>(&k_topk<0>),  reinterpret_cast<const void*>(&k_topk<1>),
-                         reinterpret_cast<const void*>(&k_topk<2>),  reinterpret_cast<const void*>(&k_topk<4>),
-                         reinterpret_cast<const void*>(&k_topk<8>),  reinterpret_cast<const void*>(&k_topk<16>),
-                         reinterpret_cast<const void*>(&k_topk<32>), reinterpret_cast<const void*>(&k_topk<8, false>)};
-    for (const void* f : fns) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, tl);
-    attrs = true;
-  }
+  WAVE_TRY(device_info().status);
   int nscore = 0, nest = 0;
   for (int b = 0; b < sa.B; ++b) {
     nscore += sa.G * ((sa.C[b] + SC - 1) / SC);
     nest += sa.G * ((sa.C[b] + SC - 1) / SC);
   }
   switch (da.GS) {
-    case 1: launch_gs<1>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
-    case 2: launch_gs<2>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
-    case 3: launch_gs<3>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
-    case 4: launch_gs<4>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
-    case 5: launch_gs<5>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
-    case 6: launch_gs<6>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
-    case 7: launch_gs<7>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
-    default: launch_gs<8>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest); break;
+    case 1: return launch_gs<1>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest);
+    case 2: return launch_gs<2>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest);
+    case 3: return launch_gs<3>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest);
+    case 4: return launch_gs<4>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest);
+    case 5: return launch_gs<5>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest);
+    case 6: return launch_gs<6>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest);
+    case 7: return launch_gs<7>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest);
+    default: return launch_gs<8>(sa, da, ix, ws, q, out, sel_ids, lse, st, nscore, nest);
   }
-  return hipGetLastError();
 }
 
 }  // namespace wave

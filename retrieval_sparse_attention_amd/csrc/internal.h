@@ -1,9 +1,13 @@
 // internal.h -- declarations shared by the library's translation units (not installed).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+
+#include <tuple>
+#include <utility>
 
 #include "common.h"
 
@@ -87,8 +91,50 @@ hipError_t launch_build(const SeqArgs& sa, const void* K, const void* V, int32_t
 hipError_t launch_build_blocks(const SeqArgs& sa, const void* K, const void* V, const wave_index& ix,
                                const BuildWs& ws, int64_t units, hipStream_t st);
 
-// ------------------------------------------------------------------ kernel timing hook
-void prof_begin(const char* name, hipStream_t st);
-void prof_end(hipStream_t st);
+// ------------------------------------------------------------------ per-device set-up
+// Done once per device (std::call_once), on the first call that launches work there:
+// the dynamic LDS limits of the kernels that need more than the default, and the
+// device's compute-unit count. status is the first failing HIP call's code.
+struct DeviceInfo {
+  hipError_t status;
+  int cus;
+};
+const DeviceInfo& device_info();
+hipError_t build_set_attrs();   // build.hip
+hipError_t decode_set_attrs();  // decode.hip
+
+// ------------------------------------------------------------------ kernel launches
+// While the timing hook is on, prof_events hands out the start/stop event pair of one
+// launch (recorded by the dispatch itself through hipExtLaunchKernel, so the pair times
+// the kernel alone) and files it under `name`; otherwise it returns false.
+bool prof_events(const char* name, hipEvent_t* start, hipEvent_t* stop);
+
+template <typename Tup, size_t... I>
+void fill_ptrs(Tup& t, void** p, std::index_sequence<I...>) {
+  void* v[] = {static_cast<void*>(&std::get<I>(t))..., nullptr};
+  for (size_t i = 0; i < sizeof...(I); ++i) p[i] = v[i];
+}
+
+// Launch `kern` on `st` with arguments converted to the kernel's parameter types; returns
+// the launch status. `name` files the launch's duration while the timing hook is on.
+template <typename... KA, typename... A>
+hipError_t launch(const char* name, void (*kern)(KA...), dim3 grid, dim3 block, size_t lds, hipStream_t st,
+                  A&&... a) {
+  static_assert(sizeof...(KA) == sizeof...(A), "kernel argument count");
+  std::tuple<KA...> args(std::forward<A>(a)...);
+  void* ptrs[sizeof...(KA) + 1];
+  fill_ptrs(args, ptrs, std::index_sequence_for<KA...>{});
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (prof_events(name, &e0, &e1))
+    return hipExtLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs, lds, st, e0, e1, 0);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, ptrs, lds, st);
+}
+
+// return the status of a HIP call from the enclosing function unless it succeeded
+#define WAVE_TRY(...)                          \
+  do {                                         \
+    const hipError_t wave_e_ = (__VA_ARGS__);  \
+    if (wave_e_ != hipSuccess) return wave_e_; \
+  } while (0)
 
 }  // namespace wave

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -211,34 +212,56 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
   return WAVE_OK;
 }
 
-// ------------------------------------------------------------------ profiler
+// ------------------------------------------------------------------ per-device set-up
+constexpr int MAX_DEVICES = 64;
+std::once_flag g_dev_once[MAX_DEVICES];
+wave::DeviceInfo g_dev_info[MAX_DEVICES];
+
+// ------------------------------------------------------------------ timing hook
+// The library's only process-wide mutable state besides the per-device set-up: the
+// event pairs of the timed launches, guarded by a mutex, recorded only while enabled.
 struct ProfRec {
   std::string name;
   hipEvent_t a, b;
 };
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+std::atomic<bool> g_prof_on{false};
 std::vector<ProfRec> g_prof;
 
 }  // namespace
 
 namespace wave {
 
-void prof_begin(const char* name, hipStream_t st) {
-  if (!g_prof_on) return;
-  std::lock_guard<std::mutex> lk(g_prof_mu);
-  ProfRec r;
-  r.name = name;
-  (void)hipEventCreate(&r.a);
-  (void)hipEventCreate(&r.b);
-  (void)hipEventRecord(r.a, st);
-  g_prof.push_back(r);
+const DeviceInfo& device_info() {
+  static DeviceInfo bad{hipErrorInvalidDevice, 0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return bad;
+  std::call_once(g_dev_once[dev], [dev] {
+    DeviceInfo d{hipSuccess, 0};
+    d.status = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (d.status == hipSuccess && d.cus < 1) d.status = hipErrorInvalidDevice;
+    if (d.status == hipSuccess) d.status = build_set_attrs();
+    if (d.status == hipSuccess) d.status = decode_set_attrs();
+    g_dev_info[dev] = d;
+  });
+  return g_dev_info[dev];
 }
 
-void prof_end(hipStream_t st) {
-  if (!g_prof_on) return;
+bool prof_events(const char* name, hipEvent_t* start, hipEvent_t* stop) {
+  if (!g_prof_on.load(std::memory_order_acquire)) return false;
   std::lock_guard<std::mutex> lk(g_prof_mu);
-  if (!g_prof.empty()) (void)hipEventRecord(g_prof.back().b, st);
+  if (!g_prof_on.load(std::memory_order_relaxed)) return false;
+  ProfRec r;
+  r.name = name ? name : "";
+  if (hipEventCreate(&r.a) != hipSuccess) return false;
+  if (hipEventCreate(&r.b) != hipSuccess) {
+    (void)hipEventDestroy(r.a);
+    return false;
+  }
+  *start = r.a;
+  *stop = r.b;
+  g_prof.push_back(r);
+  return true;
 }
 
 }  // namespace wave
@@ -450,7 +473,7 @@ wave_status wave_profiler_enable(int32_t on) {
     }
     g_prof.clear();
   }
-  g_prof_on = on != 0;
+  g_prof_on.store(on != 0, std::memory_order_release);
   return ok();
 }
 

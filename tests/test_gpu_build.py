@@ -142,6 +142,17 @@ def _sampled_units(name, K, V, G, ctx, seg, K_s, iters, seed, sample):
                 units.append((b, g, s))
     rb = np.concatenate([[0], np.cumsum(G * np.array(ctx))])
     cb = np.concatenate([[0], np.cumsum(G * np.array(C))])
+    from concurrent.futures import ThreadPoolExecutor
+
+    def ref_unit(u):
+        b, g, s = units[u]
+        N = int(ctx[b])
+        r0 = rb[b] + g * N + s * seg
+        L = min(seg, N - s * seg)
+        return oracle.kmeans_segment(K[r0:r0 + L], oracle.segment_clusters(L, seg, K_s), iters, seed, unit=u)
+
+    with ThreadPoolExecutor(len(sample)) as ex:  # the oracle releases the GIL
+        refs = dict(zip(sample, ex.map(ref_unit, sample)))
     for u in sample:
         b, g, s = units[u]
         N = int(ctx[b])
@@ -149,7 +160,7 @@ def _sampled_units(name, K, V, G, ctx, seg, K_s, iters, seed, sample):
         L = min(seg, N - s * seg)
         kc = oracle.segment_clusters(L, seg, K_s)
         say("  unit %d (b=%d g=%d s=%d)" % (u, b, g, s))
-        a, c, _, _ = oracle.kmeans_segment(K[r0:r0 + L], kc, iters, seed, unit=u)
+        a, c, _, _ = refs[u]
         assert np.array_equal(got["assign"][r0:r0 + L], a + s * K_s)
         c0 = cb[b] + g * C[b] + s * K_s
         assert np.array_equal(got["centroids"][c0:c0 + kc], c)
@@ -165,3 +176,20 @@ def test_full_size_heavy_tailed_1m_keys():
     ctx = np.array([1048576], np.int64)
     K, _, _ = synth.kv(5, 1, 8, ctx, 8192, heavy=True, values=False)
     _sampled_units("1M x 8 student-t", K, K, 8, ctx, 8192, 512, 10, 1234, sample=[0, 511, 1023])
+
+
+def test_segments_of_16384_with_1024_clusters():
+    # the 1M layer's segment shape: the LDS radix sort at its 14-bit position limit and
+    # k_assign with more than 512 clusters per segment, 4096 tokens per workgroup; every
+    # array bit-exact (two kv heads, a full and a partial segment each)
+    ctx = [20000]
+    K, V, _ = synth.kv(27, 1, 2, np.array(ctx), 16384)
+    _check_all("seg=16384 K_s=1024", K, V, 2, ctx, 16384, 1024, 3, 41)
+
+
+def test_full_size_1m_layer_build():
+    # the 1M-token layer's build: 8 kv heads x 64 segments of 16384 tokens, 1024 clusters
+    # each, 10 rounds; layout invariants on every block, sampled units bit-exact
+    ctx = np.array([1048576], np.int64)
+    K, _, _ = synth.kv(3, 1, 8, ctx, 16384, values=False)
+    _sampled_units("1M layer", K, K, 8, ctx, 16384, 1024, 10, 1234, sample=[0, 262, 511])

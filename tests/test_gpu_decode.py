@@ -154,3 +154,61 @@ def test_full_size_prescribed_clustering(name, ctx, G, H, seg, K_s, frac, ns, nl
     ixd = upload_index(idx)
     for s in range(2):
         _compare(idx, K, V, q[s], ixd, ns, nl, frac, "%s step %d" % (name, s))
+
+
+def _tie_at_kth(idx, K, V, q, b, h, ns, nl, frac, width=3):
+    """Give the clusters ranked k-1-width .. k-1+width for q head h (in the oracle's order) the centroid of the
+    k-th ranked one, so that equal nonzero rank keys straddle the k-th place; returns the cluster ids."""
+    _, _, order, kc = oracle.decode(idx, K, V, q, ns, nl, 1.0)  # every eligible cluster in rank order
+    order = order[b, h, :kc[b, h]]
+    k = oracle.k_from_frac(frac, int(idx.C[b]))
+    assert width < k <= len(order) - width - 1
+    g = h * idx.G // q.shape[1]
+    base = int(idx.G * idx.C[:b].sum() + g * idx.C[b])
+    donor = int(order[k - 1])
+    tied = [int(j) for j in order[k - 1 - width:k + width]]
+    for j in tied:
+        idx.centroids_bf16[base + j] = idx.centroids_bf16[base + donor]
+    return tied
+
+
+# Cluster counts per (sequence, kv head) that select each register width of the top-k (keys
+# per lane of 16 waves x 64 lanes: 1 up to 1024 clusters, then 2, 4, 8, 16, 32 per doubling;
+# 0 = keys beyond registers: the chunk-top threshold path). 4 tokens per cluster; top 2%:
+# k = 21 .. 1311, the fast path (k <= 1024, up to 16 keys a lane), the general path at 32.
+@pytest.mark.parametrize("ctx", [4096, 8192, 16384, 32768, 65536, 131072, 262144])
+def test_topk_register_widths_with_ties_at_the_kth_place(ctx):
+    from gpu_util import upload_index
+    G, H, seg, K_s, frac, ns, nl = 2, 8, 1024, 256, 0.02, 4, 64
+    ctxa = np.array([ctx], np.int64)
+    K, V, comp = synth.kv(61, 1, G, ctxa, seg, comp=True)
+    idx = oracle.index_from_assign(K, V, G, ctxa, seg, K_s, 7, _label_assign(comp, ctxa, G, seg, K_s))
+    q, _ = synth.queries(62, 2, 1, H, G, ctxa, K)
+    # ties at the k-th place of q head 1 (kv head 0) and q head 6 (kv head 1), step 0
+    t0 = _tie_at_kth(idx, K, V, q[0], 0, 1, ns, nl, frac)
+    t1 = _tie_at_kth(idx, K, V, q[0], 0, 6, ns, nl, frac)
+    assert len(set(t0)) == len(t0) and len(set(t1)) == len(t1)
+    ixd = upload_index(idx)
+    for s in range(2):
+        _compare(idx, K, V, q[s], ixd, ns, nl, frac, "C=%d step %d" % (ctx // 4, s))
+
+
+def test_full_size_gpu_built_index_128k():
+    # the 128K layer end to end: the GPU builds the index (10 rounds), the GPU decodes against
+    # it, and the oracle decodes against the same index copied back to the host
+    import retrieval_sparse_attention_amd as rsa
+    from gpu_util import index_to_host, say, to_dev_bf16
+    ctx = np.array([131072], np.int64)
+    G, H, seg, K_s = 8, 32, 8192, 512
+    say("generating 128K")
+    K, V, _ = synth.kv(2, 1, G, ctx, seg)
+    q, _ = synth.queries(102, 3, 1, H, G, ctx, K)
+    say("GPU build 128K")
+    ixd = rsa.wave_index_build(to_dev_bf16(K), to_dev_bf16(V), G, ctx.tolist(), seg, K_s, 10, 1234)
+    torch.cuda.synchronize()
+    host = index_to_host(ixd)
+    idx = oracle.Index(G, ctx, seg, K_s)
+    for f in oracle.Index.FIELDS:
+        getattr(idx, f)[...] = host[f]
+    for s in range(3):
+        _compare(idx, K, V, q[s], ixd, 4, 64, 0.02, "GPU-built 128K step %d" % s)
