@@ -255,6 +255,23 @@ wave_status wave_attn_decode_topk(const wave_index* index, const void* q, int32_
                                   int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse,
                                   void* ws, size_t ws_bytes, wave_stream_t stream);
 
+/*
+ * wave_attn_decode_static -- wave_attn_decode without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). The call allocates nothing: its
+ * workspace is a static device array of WAVE_STATIC_SCRATCH_BYTES that every GPU the
+ * library runs on holds from the library's first call there until the process ends.
+ * Same kernels, results and errors as wave_attn_decode, plus WORKSPACE when
+ * wave_attn_decode_plan's workspace size exceeds WAVE_STATIC_SCRATCH_BYTES (the 128K
+ * layer of 32 q / 8 kv heads needs 7.4 MiB). Every call on one GPU shares that GPU's
+ * array, so calls that overlap on one GPU (different streams or host threads) race:
+ * serialise them, or use wave_attn_decode with one workspace per concurrent call.
+ */
+#define WAVE_STATIC_SCRATCH_BYTES (16 << 20)
+wave_status wave_attn_decode_static(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
+                                    int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse,
+                                    wave_stream_t stream);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* wave_last_error(void);
 

@@ -67,6 +67,7 @@ def lib():
                                             ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_size_t)]
         L.wave_attn_decode.argtypes = [ctypes.POINTER(_Index), P, i32, i32, i32, ctypes.c_double, P, P, P, P, sz, P]
         L.wave_attn_decode_topk.argtypes = L.wave_attn_decode.argtypes
+        L.wave_attn_decode_static.argtypes = [ctypes.POINTER(_Index), P, i32, i32, i32, ctypes.c_double, P, P, P, P]
         L.wave_attn_decode_shared.argtypes = L.wave_attn_decode.argtypes
         L.wave_attn_decode_tail_plan.argtypes = [ctypes.POINTER(_Index), i32, i32, i32, ctypes.c_double, i32,
                                                  ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_size_t)]
@@ -80,7 +81,8 @@ def lib():
         L.wave_profiler_read.restype = i32
         for f in ("wave_index_plan", "wave_index_build", "wave_attn_decode_plan", "wave_attn_decode",
                   "wave_profiler_enable", "wave_index_build_blocks", "wave_attn_decode_topk",
-                  "wave_attn_decode_shared", "wave_attn_decode_tail_plan", "wave_attn_decode_tail"):
+                  "wave_attn_decode_shared", "wave_attn_decode_tail_plan", "wave_attn_decode_tail",
+                  "wave_attn_decode_static"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -294,6 +296,30 @@ def wave_attn_decode(index, q, n_sink, n_local, topk_frac, ws=None, out=None, se
     fn = lib().wave_attn_decode_shared if shared else (lib().wave_attn_decode if estimate else lib().wave_attn_decode_topk)
     _check(fn(ctypes.byref(index.c), _ptr(q), H, int(n_sink), int(n_local), float(topk_frac), _ptr(out), _ptr(sel_ids),
               _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+    return out, sel_ids[:, :, :k_max], lse
+
+
+STATIC_SCRATCH_BYTES = 16 << 20  # WAVE_STATIC_SCRATCH_BYTES
+
+
+def wave_attn_decode_static(index, q, n_sink, n_local, topk_frac, out=None, sel_ids=None, lse=None, stream=None):
+    """wave_attn_decode on the library's static device scratch (no workspace; calls on one GPU must not overlap).
+
+    The outputs are allocated here unless given; pass preallocated ones where nothing may allocate."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be a [B, H, 128] tensor")
+    B, H = q.shape[0], q.shape[1]
+    k_max, wsb = wave_attn_decode_plan(index, H, n_sink, n_local, topk_frac)
+    _check_decode_io(index, q, out, sel_ids, lse, None, k_max, wsb)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, H, HEAD_DIM), dtype=torch.float32, device=dev)
+    if sel_ids is None:
+        sel_ids = torch.empty((B, H, max(k_max, 1)), dtype=torch.int32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _check(lib().wave_attn_decode_static(ctypes.byref(index.c), _ptr(q), H, int(n_sink), int(n_local),
+                                         float(topk_frac), _ptr(out), _ptr(sel_ids), _ptr(lse), _stream(stream)))
     return out, sel_ids[:, :, :k_max], lse
 
 

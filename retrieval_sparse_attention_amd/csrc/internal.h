@@ -93,11 +93,13 @@ hipError_t launch_build_blocks(const SeqArgs& sa, const void* K, const void* V, 
 
 // ------------------------------------------------------------------ per-device set-up
 // Done once per device (std::call_once), on the first call that launches work there:
-// the dynamic LDS limits of the kernels that need more than the default, and the
-// device's compute-unit count. status is the first failing HIP call's code.
+// the dynamic LDS limits of the kernels that need more than the default, the device's
+// compute-unit count and the address of its static decode scratch. status is the first
+// failing HIP call's code.
 struct DeviceInfo {
   hipError_t status;
   int cus;
+  void* scratch;  // device address of this device's copy of the static decode scratch
 };
 const DeviceInfo& device_info();
 hipError_t build_set_attrs();   // build.hip

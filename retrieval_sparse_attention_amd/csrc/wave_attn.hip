@@ -212,6 +212,14 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
   return WAVE_OK;
 }
 
+// ------------------------------------------------------------------ static decode scratch
+// The workspace of wave_attn_decode_static: every device holds its own copy of this
+// array (from the code object's load until the process ends). Host code never passes
+// the array's name to a kernel (on the host it only stands for the symbol): the set-up
+// below takes each device's address with hipGetSymbolAddress, and only that address
+// reaches the kernels.
+__device__ __align__(256) uint8_t scratch[WAVE_STATIC_SCRATCH_BYTES];
+
 // ------------------------------------------------------------------ per-device set-up
 constexpr int MAX_DEVICES = 64;
 std::once_flag g_dev_once[MAX_DEVICES];
@@ -233,12 +241,14 @@ std::vector<ProfRec> g_prof;
 namespace wave {
 
 const DeviceInfo& device_info() {
-  static DeviceInfo bad{hipErrorInvalidDevice, 0};
+  static DeviceInfo bad{hipErrorInvalidDevice, 0, nullptr};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return bad;
   std::call_once(g_dev_once[dev], [dev] {
-    DeviceInfo d{hipSuccess, 0};
+    DeviceInfo d{hipSuccess, 0, nullptr};
     d.status = hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (d.status == hipSuccess) d.status = hipGetSymbolAddress(&d.scratch, HIP_SYMBOL(scratch));
+    if (d.status == hipSuccess && d.scratch == nullptr) d.status = hipErrorInvalidSymbol;
     if (d.status == hipSuccess && d.cus < 1) d.status = hipErrorInvalidDevice;
     if (d.status == hipSuccess) d.status = build_set_attrs();
     if (d.status == hipSuccess) d.status = decode_set_attrs();
@@ -423,6 +433,23 @@ wave_status wave_attn_decode(const wave_index* index, const void* q, int32_t n_q
                              int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse, void* ws,
                              size_t ws_bytes, wave_stream_t stream) {
   return decode_call(index, q, n_q_heads, n_sink, n_local, topk_frac, out, sel_ids, lse, ws, ws_bytes, stream, 1, 0);
+}
+
+wave_status wave_attn_decode_static(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
+                                    int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse,
+                                    wave_stream_t stream) {
+  DecodePlan P;
+  wave_status st = decode_plan(index, n_q_heads, n_sink, n_local, topk_frac, &P);
+  if (st != WAVE_OK) return st;
+  if (P.total > (size_t)WAVE_STATIC_SCRATCH_BYTES)
+    return fail(WAVE_ERR_WORKSPACE, "this call needs %zu bytes of workspace, more than the %d of the static scratch",
+                P.total, (int)WAVE_STATIC_SCRATCH_BYTES);
+  st = hip_device_ok();
+  if (st != WAVE_OK) return st;
+  const wave::DeviceInfo& di = wave::device_info();
+  if (di.status != hipSuccess) return fail(WAVE_ERR_HIP, "device set-up failed: %s", hipGetErrorString(di.status));
+  return decode_call(index, q, n_q_heads, n_sink, n_local, topk_frac, out, sel_ids, lse, di.scratch,
+                     (size_t)WAVE_STATIC_SCRATCH_BYTES, stream, 1, 0);
 }
 
 wave_status wave_attn_decode_tail_plan(const wave_index* index, int32_t n_q_heads, int32_t n_sink, int32_t n_local,
