@@ -82,7 +82,12 @@ def parse():
                    help="workload of the line (default: the 128K layer, the headline one)")
     p.add_argument("--layers", type=int, default=None, help="layer indexes in HBM (default: the workload's)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true",
+                   help="the headline line without the 1m, batched and stress workloads' figures")
     p.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the oracle timing sample")
+    p.add_argument("--cpu-single-thread", action="store_true",
+                   help="(run by the CPU baseline in a child process with OMP_NUM_THREADS=1) time one k-means "
+                        "unit, one index layout and two decode queries of the 128K layer and print them")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a device copy of 1 GiB (scale of the HBM byte counters)")
     p.add_argument("--eager", action="store_true",
@@ -93,6 +98,9 @@ def parse():
                                                             "CAL_WRITE_DIR"),
                    help="print HBM bytes per launch of KERNEL from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv "
                         "runs of the benchmark and of --calibrate-copy, and exit")
+    p.add_argument("--summarize-mfma", nargs=2, metavar=("KERNEL", "DIR"),
+                   help="print the MFMA utilisation of KERNEL from a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES "
+                        "GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 csv run, and exit")
     p.add_argument("--command", default="", help="command line recorded in a summary")
     p.add_argument("--accuracy", action="store_true",
                    help="only measure the error of the wave attention against dense attention over a grid of "
@@ -192,6 +200,41 @@ def summarize_traffic(kernel, fdir, wdir, cfdir, cwdir, command):
         "source_sha: %s" % sha]))
 
 
+def summarize_mfma(kernel, d, command):
+    """MFMA utilisation of a kernel's dispatches: busy cycles of the matrix cores summed over the SIMDs
+    against the GPU's active cycles times the SIMD count, and the bf16 MFMA work the counters saw."""
+    per = {}
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if _short(r["Kernel_Name"]).split("<")[0] != kernel:
+            continue
+        key = r["Dispatch_Id"]
+        e = per.setdefault(key, {})
+        name = r["Counter_Name"]
+        v = float(r["Counter_Value"])
+        e[name] = max(e.get(name, 0.0), v) if name == "GRBM_GUI_ACTIVE" else e.get(name, 0.0) + v
+    if not per:
+        raise SystemExit("no dispatch of %s in %s" % (kernel, d))
+    simds = 256 * 4
+    rows = []
+    for key, e in sorted(per.items(), key=lambda kv: int(kv[0])):
+        busy, gui = e.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), e.get("GRBM_GUI_ACTIVE", 0.0)
+        mops = e.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
+        rows.append((busy, gui, mops * 512.0, busy / (gui * simds) if gui else float("nan")))
+    busy = sum(r[0] for r in rows) / len(rows)
+    gui = sum(r[1] for r in rows) / len(rows)
+    flops = sum(r[2] for r in rows) / len(rows)
+    print("\n".join([
+        "# MFMA utilisation of %s (rocprofv3 --pmc, one dispatch at a time)" % kernel,
+        "command: %s" % command,
+        "dispatches: %d" % len(rows),
+        "SQ_VALU_MFMA_BUSY_CYCLES per dispatch (sum over %d SIMDs): %.0f" % (simds, busy),
+        "GRBM_GUI_ACTIVE per dispatch (GPU cycles): %.0f" % gui,
+        "mfma_busy_fraction: %.4f" % (busy / (gui * simds)),
+        "bf16 MFMA flops per dispatch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512): %.4g" % flops,
+        "bf16 MFMA flops per GPU cycle: %.0f (peak 256 CUs x 4096 = 1048576)" % (flops / gui),
+        "per-dispatch busy fractions: %s" % " ".join("%.3f" % r[3] for r in rows[:16])]))
+
+
 SOURCES = ["retrieval_sparse_attention_amd/csrc/decode.hip", "retrieval_sparse_attention_amd/csrc/build.hip",
            "retrieval_sparse_attention_amd/csrc/common.h", "retrieval_sparse_attention_amd/csrc/internal.h",
            "retrieval_sparse_attention_amd/csrc/wave_attn.hip"]
@@ -282,6 +325,12 @@ def main():
     if args.summarize_traffic:
         summarize_traffic(*args.summarize_traffic, command=args.command)
         return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma, command=args.command)
+        return
+    if args.cpu_single_thread:
+        cpu_single_thread_sample()
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU: this build has no multi-GPU path (the kv-head sharding it "
               "would use is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
@@ -314,6 +363,55 @@ def main():
     if args.layers is not None:
         W["layers"] = args.layers
     headline = args.workload == "128k"
+    result, (K, V, ctx, q) = measure(W, args.steps, args.warmup, args.eager, headline, dev)
+    if headline and not args.no_extra:
+        # the method's other evaluated shapes, each from its own inputs and indexes, on fewer steps
+        # (decode per query, achieved bandwidth of the decode, index build, k_assign's MFMA rate)
+        extra = {}
+        for name, st in (("1m", 4), ("batched", 4), ("stress", 3)):
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            r, _ = measure(dict(WORKLOADS[name]), st, 1, args.eager, False, dev)
+            extra[name] = workload_summary(r)
+        result["workloads"] = extra
+        torch.cuda.empty_cache()
+    if headline and not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(W, K, V, ctx, q, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+def workload_summary(r):
+    """The figures of another workload's line that the headline line carries."""
+    ka = r["kernel_roofline"].get("k_assign", {})
+    out = {"metric": r["metric"], "value": r["value"], "unit": r["unit"], "steps": r["steps"],
+           "ms_per_step": r["ms_per_step"], "config": r["config"],
+           "decode_only_us_per_query": r["decode_only_us_per_query"],
+           "decode_only_effective_GBs": r["decode_only_effective_GBs"],
+           "decode_only_frac_of_hbm_peak": (round(r["decode_only_effective_GBs"] / HBM_PEAK_GBS, 4)
+                                            if r["decode_only_effective_GBs"] else None),
+           "decode_bytes_per_query": r["decode_bytes_per_query"],
+           "build_tokens_per_s": r["build_tokens_per_s"],
+           "k_assign_TFLOPs": ka.get("achieved_TFLOPs"), "k_assign_frac_of_bf16_peak": ka.get("frac"),
+           "kernels": r["kernels"],
+           "kernel_roofline": {k: {kk: v[kk] for kk in ("frac", "achieved_GBs", "achieved_TFLOPs") if kk in v}
+                               for k, v in r["kernel_roofline"].items()}}
+    return out
+
+
+def measure(W, steps, warmup, eager, headline, dev):
+    """One workload: inputs, L layer indexes, captured step graphs, the timed steps, the
+    decode-only steps, and an eager pass with dispatch-recorded events per kernel. Returns the
+    JSON fields of its line and the host inputs (for the oracle's timing)."""
+    import numpy as np
+    import torch
+
+    import retrieval_sparse_attention_amd as rsa
+    import synth
+
+    class _A:  # the step counts of this measurement
+        pass
+    args = _A()
+    args.steps, args.warmup, args.eager = steps, warmup, eager
     B, H, G = W["batch"], W["q_heads"], W["kv_heads"]
     seg, K_s, iters = W["seg_len"], W["clusters_per_seg"], W["kmeans_iters"]
     ns, nl, frac, QPS = W["n_sink"], W["n_local"], W["topk_frac"], W["decode_queries_per_step"]
@@ -586,9 +684,9 @@ def main():
         "kernel_roofline": extra,
         "source_sha": sha,
     }
-    if headline and not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(W, K, V, ctx, q, args.cpu_seconds)
-    print(json.dumps(result))
+    return result, (K, V, ctx, q)
+
+
 
 
 def cpu_baseline(W, K, V, ctx, q, budget_s):
@@ -636,11 +734,70 @@ def cpu_baseline(W, K, V, ctx, q, budget_s):
         n_dec += 1
     t_dec = (time.time() - t2) / n_dec
     step_s = units_total * t_unit + t_layout + W["decode_queries_per_step"] * t_dec
-    return {"value": round(W["decode_queries_per_step"] / step_s, 4), "unit": "decode steps/s",
-            "cores": threads, "kind": "oracle",
-            "sample": "%d of %d k-means units (%.2f s each), one index layout (%.2f s), %d of 64 decode queries "
-                      "(%.3f s each); step time %.1f s extrapolated" % (n_units, units_total, t_unit, t_layout, n_dec,
-                                                                      t_dec, step_s)}
+    out = {"value": round(W["decode_queries_per_step"] / step_s, 4), "unit": "decode steps/s",
+           "cores": threads, "kind": "oracle",
+           "sample": "%d of %d k-means units (%.2f s each), one index layout (%.2f s), %d of 64 decode queries "
+                     "(%.3f s each); step time %.1f s extrapolated" % (n_units, units_total, t_unit, t_layout, n_dec,
+                                                                     t_dec, step_s)}
+    out.update(cpu_info())
+    # the same sample on one thread, in a child process (OpenMP reads its thread count at start)
+    import subprocess
+    try:
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-single-thread"], env=env,
+                           capture_output=True, text=True, timeout=120)
+        one = json.loads(r.stdout.strip().splitlines()[-1])
+        step1 = units_total * one["t_unit"] + one["t_layout"] + W["decode_queries_per_step"] * one["t_dec"]
+        out["single_thread"] = {"value": round(W["decode_queries_per_step"] / step1, 5), "unit": "decode steps/s",
+                                "cores": 1, "sample": "1 k-means unit (%.2f s), one index layout (%.2f s), 2 decode "
+                                "queries (%.3f s each); step time %.1f s extrapolated"
+                                % (one["t_unit"], one["t_layout"], one["t_dec"], step1)}
+    except Exception as e:  # the figure is optional; the multi-thread baseline stands on its own
+        out["single_thread"] = {"error": repr(e)[:200]}
+    return out
+
+
+def cpu_info():
+    """CPU model, logical CPUs and the CPUs this process may run on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "cpus_usable": len(os.sched_getaffinity(0))}
+
+
+def cpu_single_thread_sample():
+    """One k-means unit, one layout and two decode queries of the 128K layer's oracle on this process's
+    threads (run with OMP_NUM_THREADS=1); prints their times as JSON."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    W = WORKLOAD
+    G, seg, K_s, N = W["kv_heads"], W["seg_len"], W["clusters_per_seg"], W["ctx"]
+    ctx = np.array([N], np.int64)
+    K, V, _ = synth.kv(W["seed_data"], 1, G, ctx, seg)
+    q, _ = synth.queries(W["seed_query"], 2, 1, W["q_heads"], G, ctx, K)
+    t0 = time.time()
+    oracle.kmeans_segment(K[:seg], K_s, W["kmeans_iters"], W["seed_build"], unit=0)
+    t_unit = time.time() - t0
+    lab = (np.arange(K.shape[0]) % seg) % K_s + (np.arange(K.shape[0]) % N) // seg * K_s
+    t0 = time.time()
+    idx = oracle.index_from_assign(K, V, G, ctx, seg, K_s, W["seed_build"], lab.astype(np.int32))
+    t_layout = time.time() - t0
+    t0 = time.time()
+    for s in range(2):
+        oracle.decode(idx, K, V, q[s], W["n_sink"], W["n_local"], W["topk_frac"])
+    t_dec = (time.time() - t0) / 2
+    print(json.dumps({"t_unit": t_unit, "t_layout": t_layout, "t_dec": t_dec}))
+
+
+
 
 
 if __name__ == "__main__":
