@@ -708,7 +708,8 @@ def cpu_baseline(W, K, V, ctx, q, budget_s):
     t0 = time.time()
     n_units = 0
     while n_units < units_total and (n_units == 0 or time.time() - t0 < 0.5 * budget_s):
-        oracle.kmeans_segment(K[n_units * seg:(n_units + 1) * seg], K_s, iters, W["seed_build"], unit=n_units)
+        key = oracle.seed_key(0, n_units // (N // seg), n_units % (N // seg))
+        oracle.kmeans_segment(K[n_units * seg:(n_units + 1) * seg], K_s, iters, W["seed_build"], key=key)
         n_units += 1
     t_unit = (time.time() - t0) / n_units
     # decode sample on an oracle index over the generator's labels (k-means cost already sampled)
@@ -784,7 +785,7 @@ def cpu_single_thread_sample():
     K, V, _ = synth.kv(W["seed_data"], 1, G, ctx, seg)
     q, _ = synth.queries(W["seed_query"], 2, 1, W["q_heads"], G, ctx, K)
     t0 = time.time()
-    oracle.kmeans_segment(K[:seg], K_s, W["kmeans_iters"], W["seed_build"], unit=0)
+    oracle.kmeans_segment(K[:seg], K_s, W["kmeans_iters"], W["seed_build"], key=oracle.seed_key(0, 0, 0))
     t_unit = time.time() - t0
     lab = (np.arange(K.shape[0]) % seg) % K_s + (np.arange(K.shape[0]) % N) // seg * K_s
     t0 = time.time()

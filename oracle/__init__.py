@@ -40,7 +40,9 @@ def _load():
         lib.ref_f32_to_bf16.restype = ctypes.c_uint16
         lib.ref_f32_to_bf16_array.argtypes = [P, i64, P]
         lib.ref_splitmix64_stream.argtypes = [u64, i64, P]
-        lib.ref_init_indices.argtypes = [i32, i32, u64, i64, P]
+        lib.ref_seed_key.argtypes = [i32, i32, i64]
+        lib.ref_seed_key.restype = u64
+        lib.ref_init_indices.argtypes = [i32, i32, u64, u64, P]
         lib.ref_segment_clusters.argtypes = [i64, i32, i32]
         lib.ref_segment_clusters.restype = i64
         lib.ref_num_clusters.argtypes = [i64, i32, i32]
@@ -51,7 +53,7 @@ def _load():
         lib.ref_sq_dist.restype = f64
         lib.ref_assign_point.argtypes = [P, P, i32]
         lib.ref_assign_point.restype = i32
-        lib.ref_kmeans_segment.argtypes = [P, i32, i32, i32, u64, i64, i32, P, P, P, P]
+        lib.ref_kmeans_segment.argtypes = [P, i32, i32, i32, u64, u64, i32, P, P, P, P]
         lib.ref_build.argtypes = [i32, i32, P, P, P, i32, i32, i32, u64] + [P] * 11
         lib.ref_build.restype = ctypes.c_int
         lib.ref_index_from_assign.argtypes = [i32, i32, P, P, P, i32, i32, u64, P] + [P] * 10
@@ -100,9 +102,14 @@ def splitmix64_stream(state, n):
     return out
 
 
-def init_indices(L, K, seed, unit):
+def seed_key(b, g, s):
+    """Stream key of the k-means problem of (sequence b, kv head g, segment s)."""
+    return _load().ref_seed_key(b, g, s)
+
+
+def init_indices(L, K, seed, key):
     out = np.empty(K, dtype=np.int32)
-    _load().ref_init_indices(L, K, seed, unit, _p(out))
+    _load().ref_init_indices(L, K, seed, key, _p(out))
     return out
 
 
@@ -129,15 +136,16 @@ def assign_point(x, chat):
     return _load().ref_assign_point(_p(_c(x, np.uint16)), _p(chat), chat.shape[0])
 
 
-def kmeans_segment(X, K, iters, seed, unit=0, exact=False):
-    """Lloyd's k-means of one segment. Returns (assign, centroids fp32, trace [iters][L], objective [iters])."""
+def kmeans_segment(X, K, iters, seed, key=0, exact=False):
+    """Lloyd's k-means of one segment seeded by stream key `key` (seed_key(b, g, s) inside a build).
+    Returns (assign, centroids fp32, trace [iters][L], objective [iters])."""
     X = _c(X, np.uint16)
     L = X.shape[0]
     a = np.empty(L, dtype=np.int32)
     c = np.empty((K, D), dtype=np.float32)
     tr = np.empty((iters, L), dtype=np.int32)
     obj = np.empty(iters, dtype=np.float64)
-    _load().ref_kmeans_segment(_p(X), L, K, iters, seed, unit, 1 if exact else 0, _p(a), _p(c), _p(tr), _p(obj))
+    _load().ref_kmeans_segment(_p(X), L, K, iters, seed, key, 1 if exact else 0, _p(a), _p(c), _p(tr), _p(obj))
     return a, c, tr, obj
 
 

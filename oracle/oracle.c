@@ -72,17 +72,32 @@ void ref_splitmix64_stream(uint64_t state, int64_t n, uint64_t* out) {
 }
 
 /*
- * Seeded initial centroids of one segment [bit-defined]. The pages fix no
- * initialisation; the reading is a fixed-seed choice of K distinct tokens of
- * the segment: unit u (units enumerated by sequence, then kv head, then
- * segment) seeds SplitMix64 with seed + GAMMA*(u+1); a partial Fisher-Yates
- * shuffle of [0, L) then picks positions: for i < K, j = i + next() mod (L-i),
- * swap. idx receives the first K entries.
+ * Stream key of the k-means problem of (sequence b, kv head g, segment s)
+ * [bit-defined]. The pages fix no initialisation. The reading keys each
+ * segment's random stream by its coordinates, not by its rank in an
+ * enumeration, so that a segment's seeds do not depend on how many segments
+ * the sequences hold: clustering the segments of a longer context leaves the
+ * earlier segments as they were, which is what an index that grows segment by
+ * segment needs (RetroInfer page, section 2.A: segments are clustered
+ * independently). key = b*2^56 + g*2^40 + s*2^16 (mod 2^64); with at most
+ * 2^16 draws per segment the streams of distinct (b, g, s) with b < 2^8,
+ * g < 2^16 and s < 2^24 never share a state.
  */
-void ref_init_indices(int32_t L, int32_t K, uint64_t seed, int64_t unit, int32_t* idx) {
+uint64_t ref_seed_key(int32_t b, int32_t g, int64_t s) {
+  return ((uint64_t)(uint32_t)b << 56) + ((uint64_t)(uint32_t)g << 40) + ((uint64_t)s << 16);
+}
+
+/*
+ * Seeded initial centroids of one segment [bit-defined]: a fixed-seed choice of
+ * K distinct tokens of the segment. The segment with stream key `key` seeds
+ * SplitMix64 with seed + GAMMA*(key+1); a partial Fisher-Yates shuffle of
+ * [0, L) then picks positions: for i < K, j = i + next() mod (L-i), swap. idx
+ * receives the first K entries.
+ */
+void ref_init_indices(int32_t L, int32_t K, uint64_t seed, uint64_t key, int32_t* idx) {
   int32_t* a = (int32_t*)malloc(sizeof(int32_t) * (size_t)L);
   for (int32_t i = 0; i < L; ++i) a[i] = i;
-  uint64_t st = seed + GAMMA * (uint64_t)(unit + 1);
+  uint64_t st = seed + GAMMA * (key + 1);
   for (int32_t i = 0; i < K; ++i) {
     uint64_t r = ref_splitmix64_next(&st);
     int32_t j = i + (int32_t)(r % (uint64_t)(L - i));
@@ -193,10 +208,10 @@ static void update_centroids_exact(const uint16_t* X, int32_t L, int32_t K, cons
  * objective after round it: sum over tokens of the squared distance to the
  * assigned centroid (chat in spec mode, c in exact mode).
  */
-void ref_kmeans_segment(const uint16_t* X, int32_t L, int32_t K, int32_t iters, uint64_t seed, int64_t unit,
+void ref_kmeans_segment(const uint16_t* X, int32_t L, int32_t K, int32_t iters, uint64_t seed, uint64_t key,
                         int32_t exact_mode, int32_t* assign, float* cent, int32_t* trace, double* objective) {
   int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)K);
-  ref_init_indices(L, K, seed, unit, idx);
+  ref_init_indices(L, K, seed, key, idx);
   /* the bf16 inputs widened to binary64 once (exact), so the distance loops
    * below do the same operations as ref_sq_dist without re-widening */
   double* xd = (double*)malloc(sizeof(double) * (size_t)L * D);
@@ -358,7 +373,7 @@ static int build_impl(int32_t B, int32_t G, const int64_t* ctx, const uint16_t* 
     float* cent = centroids + clu0 * D;
     if (given_assign) {
       int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)Kc);
-      ref_init_indices(L, Kc, seed, uu, idx);
+      ref_init_indices(L, Kc, seed, ref_seed_key(b, g, s), idx);
       for (int32_t j = 0; j < Kc; ++j)
         for (int i = 0; i < D; ++i) cent[(int64_t)j * D + i] = ref_bf16_to_f32(X[(int64_t)idx[j] * D + i]);
       free(idx);
@@ -375,7 +390,7 @@ static int build_impl(int32_t B, int32_t G, const int64_t* ctx, const uint16_t* 
       update_centroids_f32(X, L, Kc, la, cent);
     } else {
       int32_t* tr = trace ? (int32_t*)malloc(sizeof(int32_t) * (size_t)L * iters) : NULL;
-      ref_kmeans_segment(X, L, Kc, iters, seed, uu, 0, la, cent, tr, NULL);
+      ref_kmeans_segment(X, L, Kc, iters, seed, ref_seed_key(b, g, s), 0, la, cent, tr, NULL);
       if (tr) {
         for (int32_t it = 0; it < iters; ++it)
           for (int32_t t = 0; t < L; ++t) trace[(int64_t)it * rows + row0 + t] = tr[(int64_t)it * L + t] + (int32_t)(s * K_s);

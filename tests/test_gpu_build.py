@@ -149,7 +149,7 @@ def _sampled_units(name, K, V, G, ctx, seg, K_s, iters, seed, sample):
         N = int(ctx[b])
         r0 = rb[b] + g * N + s * seg
         L = min(seg, N - s * seg)
-        return oracle.kmeans_segment(K[r0:r0 + L], oracle.segment_clusters(L, seg, K_s), iters, seed, unit=u)
+        return oracle.kmeans_segment(K[r0:r0 + L], oracle.segment_clusters(L, seg, K_s), iters, seed, key=oracle.seed_key(b, g, s))
 
     with ThreadPoolExecutor(len(sample)) as ex:  # the oracle releases the GIL
         refs = dict(zip(sample, ex.map(ref_unit, sample)))

@@ -71,17 +71,46 @@ def test_splitmix64_published_outputs():
         16408922859458223821]
 
 
+def test_seed_key_closed_form():
+    # stream key of (b, g, s): b*2^56 + g*2^40 + s*2^16 modulo 2^64
+    assert oracle.seed_key(0, 0, 0) == 0
+    assert oracle.seed_key(0, 0, 1) == 1 << 16
+    assert oracle.seed_key(0, 1, 0) == 1 << 40
+    assert oracle.seed_key(1, 0, 0) == 1 << 56
+    assert oracle.seed_key(3, 7, 11) == (3 << 56) + (7 << 40) + (11 << 16)
+    assert oracle.seed_key(255, (1 << 16) - 1, (1 << 24) - 1) == (1 << 64) - (1 << 16)
+
+
+def _fisher_yates(L, K, state):
+    # the partial shuffle written out from its definition over the pinned SplitMix64 stream
+    a = list(range(L))
+    for i, r in enumerate(oracle.splitmix64_stream(state, K).tolist()):
+        j = i + r % (L - i)
+        a[i], a[j] = a[j], a[i]
+    return a[:K]
+
+
+def test_init_indices_are_the_seeded_partial_shuffle():
+    # segment with stream key k: SplitMix64 from state seed + gamma*(k+1), one draw per swap
+    gamma = 0x9E3779B97F4A7C15
+    for L, K, seed, key in [(37, 3, 5, 0), (100, 100, 1234, oracle.seed_key(1, 2, 3)), (8192, 64, 99, 1 << 16),
+                            (5, 5, (1 << 64) - 1, oracle.seed_key(255, 3, 0))]:
+        st = (seed + gamma * (key + 1)) % (1 << 64)
+        assert oracle.init_indices(L, K, seed, key).tolist() == _fisher_yates(L, K, st), (L, K, key)
+
+
 def test_init_indices_distinct_in_range():
     for L, K in [(8192, 512), (100, 100), (37, 3), (1, 1)]:
-        for u in range(5):
-            idx = oracle.init_indices(L, K, 1234, u)
+        for s in range(5):
+            idx = oracle.init_indices(L, K, 1234, oracle.seed_key(0, 0, s))
             assert len(set(idx.tolist())) == K
             assert idx.min() >= 0 and idx.max() < L
     # K = L: the shuffle is a full permutation
     assert sorted(oracle.init_indices(64, 64, 7, 3).tolist()) == list(range(64))
-    # deterministic, and different units differ
-    assert np.array_equal(oracle.init_indices(8192, 512, 1, 0), oracle.init_indices(8192, 512, 1, 0))
-    assert not np.array_equal(oracle.init_indices(8192, 512, 1, 0), oracle.init_indices(8192, 512, 1, 1))
+    # deterministic, and different keys differ
+    k0, k1 = oracle.seed_key(0, 0, 0), oracle.seed_key(0, 1, 0)
+    assert np.array_equal(oracle.init_indices(8192, 512, 1, k0), oracle.init_indices(8192, 512, 1, k0))
+    assert not np.array_equal(oracle.init_indices(8192, 512, 1, k0), oracle.init_indices(8192, 512, 1, k1))
 
 
 def test_init_shuffle_is_uniform():
@@ -89,8 +118,8 @@ def test_init_shuffle_is_uniform():
     # "j = next() mod L" mistake does not (chi-square over the 24 orders of 4 items).
     counts = {}
     n = 48000
-    for u in range(n):
-        p = tuple(oracle.init_indices(4, 4, 99, u).tolist())
+    for s in range(n):
+        p = tuple(oracle.init_indices(4, 4, 99, oracle.seed_key(0, 0, s)).tolist())
         counts[p] = counts.get(p, 0) + 1
     assert len(counts) == 24
     exp = n / 24
@@ -172,11 +201,11 @@ def test_kmeans_exact_mode_matches_sklearn_lloyd():
 
 def test_kmeans_exact_mode_objective_monotone():
     K, _, _ = synth.kv(11, 1, 1, np.array([2048]), 2048)
-    for unit in range(3):
-        _, _, _, obj = oracle.kmeans_segment(K, 128, 10, 5, unit=unit, exact=True)
+    for s in range(3):
+        _, _, _, obj = oracle.kmeans_segment(K, 128, 10, 5, key=oracle.seed_key(0, 0, s), exact=True)
         assert np.all(obj[1:] <= obj[:-1] * (1 + 1e-12)), obj
     # spec mode (bf16 centroids in the assignment) stays monotone to 1e-3
-    _, _, _, obj = oracle.kmeans_segment(K, 128, 10, 5, unit=0, exact=False)
+    _, _, _, obj = oracle.kmeans_segment(K, 128, 10, 5, key=0, exact=False)
     assert np.all(obj[1:] <= obj[:-1] * (1 + 1e-3)), obj
 
 
@@ -186,7 +215,7 @@ def test_kmeans_update_is_ordered_fp32_mean():
     # empty clusters keep the initial token.
     Xb = _tiny_data(5, 300)
     K = 40
-    a, c, tr, _ = oracle.kmeans_segment(Xb, K, 1, 77, unit=2)
+    a, c, tr, _ = oracle.kmeans_segment(Xb, K, 1, 77, key=2)
     X = oracle.bf16_to_f32(Xb)
     init = oracle.init_indices(300, K, 77, 2)
     for j in range(K):
@@ -274,14 +303,57 @@ def test_layout_invariants():
 
 
 def test_build_equals_per_segment_kmeans():
-    K, V, ctx, idx = _small_build(ctx=(2500,), G=1, iters=4)
-    # units are enumerated (b, g, segment); unit u seeds segment u here (B=1, G=1)
-    for s in range(3):
-        t0, t1 = s * 1024, min((s + 1) * 1024, 2500)
-        kc = oracle.segment_clusters(t1 - t0, 1024, 64)
-        a, c, _, _ = oracle.kmeans_segment(K[t0:t1], kc, 4, 1234, unit=s)
-        assert np.array_equal(idx.assign[t0:t1], a + s * 64)
-        assert np.array_equal(idx.centroids[s * 64:s * 64 + kc], c)
+    # every (b, g, s) problem of a build is the segment's own k-means seeded by seed_key(b, g, s)
+    K, V, ctx, idx = _small_build(ctx=(2500, 1100), G=2, iters=4)
+    row = clu = 0
+    for b, N in enumerate(ctx):
+        C = oracle.num_clusters(int(N), 1024, 64)
+        for g in range(2):
+            for s in range(-(-int(N) // 1024)):
+                t0, t1 = s * 1024, min((s + 1) * 1024, int(N))
+                kc = oracle.segment_clusters(t1 - t0, 1024, 64)
+                a, c, _, _ = oracle.kmeans_segment(K[row + t0:row + t1], kc, 4, 1234, key=oracle.seed_key(b, g, s))
+                assert np.array_equal(idx.assign[row + t0:row + t1], a + s * 64), (b, g, s)
+                assert np.array_equal(idx.centroids[clu + s * 64:clu + s * 64 + kc], c), (b, g, s)
+            row += int(N)
+            clu += C
+
+
+def _block(idx, ctx, b, g):
+    """(rows, clusters, offsets) slices of block (b, g) of an oracle index."""
+    row = clu = off = 0
+    for bb in range(b):
+        C = oracle.num_clusters(int(ctx[bb]), idx.seg_len, idx.K_s)
+        row, clu, off = row + idx.G * int(ctx[bb]), clu + idx.G * C, off + idx.G * (C + 1)
+    N, C = int(ctx[b]), oracle.num_clusters(int(ctx[b]), idx.seg_len, idx.K_s)
+    return (slice(row + g * N, row + (g + 1) * N), slice(clu + g * C, clu + (g + 1) * C),
+            slice(off + g * (C + 1), off + (g + 1) * (C + 1)))
+
+
+def test_build_of_a_longer_context_keeps_the_full_segments():
+    # Segments are clustered independently and seeded by their own coordinates, so the index
+    # of a longer context (same leading tokens) repeats every segment that was already full:
+    # labels, centroids and value sums of its clusters, its sorted rows and offsets. Only
+    # the segments from the first one that was partial on are new.
+    seg, K_s, G = 512, 32, 3
+    long = np.array([2300, 1600], np.int64)
+    Kf, Vf, _ = synth.kv(21, 2, G, long, seg)
+    full = oracle.build(Kf, Vf, G, long, seg, K_s, 3, 77)
+    for short in ([1024, 1537], [2047, 512], [1, 1600]):
+        short = np.array(short, np.int64)
+        rows = np.concatenate([np.arange(sum(G * long[:b]) + g * long[b], sum(G * long[:b]) + g * long[b] + short[b])
+                               for b in range(2) for g in range(G)])
+        part = oracle.build(Kf[rows], Vf[rows], G, short, seg, K_s, 3, 77)
+        for b in range(2):
+            keep = int(short[b]) // seg  # segments full in the shorter context
+            nk, ck = keep * seg, keep * K_s
+            for g in range(G):
+                (rs, cs, os_), (rl, cl, ol) = _block(part, short, b, g), _block(full, long, b, g)
+                for name in ("assign", "perm", "inv_perm", "k_sorted", "v_sorted"):
+                    assert np.array_equal(getattr(part, name)[rs][:nk], getattr(full, name)[rl][:nk]), (name, b, g)
+                for name in ("sizes", "centroids", "centroids_bf16", "vsum"):
+                    assert np.array_equal(getattr(part, name)[cs][:ck], getattr(full, name)[cl][:ck]), (name, b, g)
+                assert np.array_equal(part.offsets[os_][:ck + 1], full.offsets[ol][:ck + 1]), (b, g)
 
 
 # ---------------------------------------------------------------------- rank key
