@@ -118,8 +118,9 @@ wave_status wave_index_plan(const wave_shape* shape, int32_t seg_len, int32_t cl
 /*
  * wave_index_build -- the query-independent phase (RetroInfer page, section
  * 2.A: segmented clustering at prefill). Per (sequence, kv head, segment):
- * seeded init (SplitMix64 seeded at seed + 0x9E3779B97F4A7C15*(u+1) for unit u
- * in (b, g, s) order, partial Fisher-Yates choice of K(s) tokens), then exactly
+ * seeded init (SplitMix64 seeded at seed + 0x9E3779B97F4A7C15*(k+1) with the
+ * segment's key k = b*2^56 + g*2^40 + s*2^16 mod 2^64, partial Fisher-Yates
+ * choice of K(s) tokens), then exactly
  * `iters` Lloyd rounds: assignment to the nearest bf16-rounded centroid by
  * squared Euclidean distance (exact ties: lowest id), update to the ordered
  * fp32 mean of the members (empty clusters keep their centroid). Then the

@@ -108,8 +108,17 @@ __device__ __forceinline__ uint64_t sm64_mix(uint64_t z) {
 }
 
 // ------------------------------------------------------------------ k_init
-// One workgroup per unit. The i-th SplitMix64 draw of unit u is
-// mix(seed + GAMMA*(u+1) + GAMMA*(i+1)); the draws do not depend on the
+// Stream key of the unit (b, g, s): b*2^56 + g*2^40 + s*2^16 (mod 2^64). Keyed by the
+// segment's coordinates, a segment draws the same initial tokens whatever the number
+// of segments around it, so an index grown by appending segments equals one built
+// over the longer context (segments are clustered independently, RetroInfer page,
+// section 2.A).
+__device__ __forceinline__ uint64_t seed_key(int b, int g, int s) {
+  return ((uint64_t)(uint32_t)b << 56) + ((uint64_t)(uint32_t)g << 40) + ((uint64_t)(uint32_t)s << 16);
+}
+
+// One workgroup per unit. The i-th SplitMix64 draw of the unit with key k is
+// mix(seed + GAMMA*(k+1) + GAMMA*(i+1)); the draws do not depend on the
 // shuffle, so they are taken in parallel and one lane then performs the K(s)
 // swaps of the partial Fisher-Yates shuffle of [0, L) held in LDS (16-bit
 // entries). Centroid i becomes the fp32 copy of key row idx[i]; its bf16
@@ -123,7 +132,7 @@ __global__ __launch_bounds__(INIT_THREADS) void k_init(SeqArgs sa, uint64_t seed
   const Unit U = unit_of(sa, blockIdx.x);
   uint16_t* idx = reinterpret_cast<uint16_t*>(smem);
   int32_t* jsel = reinterpret_cast<int32_t*>(smem + ((2 * (size_t)U.L + 15) & ~(size_t)15));
-  const uint64_t st0 = seed + GAMMA * (uint64_t)(U.u + 1);
+  const uint64_t st0 = seed + GAMMA * (seed_key(U.b, U.g, U.s) + 1);
   for (int i = threadIdx.x; i < U.L; i += blockDim.x) idx[i] = (uint16_t)i;
   for (int i = threadIdx.x; i < U.Kc; i += blockDim.x) {
     const uint64_t r = sm64_mix(st0 + GAMMA * (uint64_t)(i + 1));
@@ -203,16 +212,19 @@ __global__ __launch_bounds__(INIT_THREADS) void k_init(SeqArgs sa, uint64_t seed
 // every token not sent there has the exact argmin.
 
 // scheduling of one pipeline step (see tile() in k_assign): nds LDS reads, then 16 x
-// (1 MFMA, 6 vector-ALU operations); nothing moves across the step's end
-#define AS_STEP(nds)                                                              \
+// (1 MFMA, 6 vector-ALU operations), the first nvm of them followed by one global load;
+// nothing moves across the step's end
+#define AS_STEP_V(nds, nvm)                                                       \
   do {                                                                            \
     if ((nds) > 0) __builtin_amdgcn_sched_group_barrier(0x100, (nds), 0);         \
     _Pragma("unroll") for (int i_ = 0; i_ < 16; ++i_) {                           \
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                          \
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);                          \
+      if (i_ < (nvm)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);         \
     }                                                                             \
     __builtin_amdgcn_sched_barrier(0);                                            \
   } while (0)
+#define AS_STEP(nds) AS_STEP_V(nds, 0)
 
 constexpr int AS_WAVES = 4;
 constexpr int AS_THREADS = AS_WAVES * 64;
@@ -224,8 +236,11 @@ constexpr int AS_MAXTPW_M = 4096;            // the same with more than AS_GROUP
 
 // Token tiles are double buffered and loaded straight into LDS (global_load_lds,
 // 16 bytes per lane); one barrier per tile. The work of a tile's start (the
-// previous tile's decisions, this tile's key norms, the next tile's loads) is
-// straight-line code, so it overlaps the first MFMAs of the tile.
+// previous tile's decisions, this tile's key norms) is straight-line code, so it
+// overlaps the first MFMAs of the tile. The next tile's 8 loads per wave go out two
+// at a time between the MFMAs of the first four steps: issued together at the tile's
+// start, the 32 loads of the workgroup queued behind each other in the address unit
+// and held the issuing waves back (about 5% of the launch).
 struct AssignLds {
   u32x4 tile[2][AS_TT * 16];         // token rows, 16-byte chunk c of row t stored at slot t*16 + (c ^ (t & 15))
   float red[2][AS_WAVES][AS_TT][3];  // per tile buffer and wave: best, second best, winner's position (bits)
@@ -333,16 +348,17 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
   // rows of tile T into buffer bi: wave wv fills slots [(8 wv + m) * 64, +64), m < 8; lane i of
   // a load writes slot base + i, i.e. token t = slot / 16, chunk (slot % 16) ^ (t % 16).
   // Rows past the range end repeat its last row: their results equal that row's.
+  auto issue_m = [&](int T, int bi, int m) {
+    const int s0 = (wv * 8 + m) * 64;
+    const int slot = s0 + lane;
+    const int t = slot >> 4, c = (slot & 15) ^ (t & 15);
+    const int tt = min(T * AS_TT + t, nrow - 1);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(Kr + tt * D + c * 8),
+                                     (__attribute__((address_space(3))) void*)(&S.tile[bi][s0]), 16, 0, 0);
+  };
   auto issue = [&](int T, int bi) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int s0 = (wv * 8 + m) * 64;
-      const int slot = s0 + lane;
-      const int t = slot >> 4, c = (slot & 15) ^ (t & 15);
-      const int tt = min(T * AS_TT + t, nrow - 1);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(Kr + tt * D + c * 8),
-                                       (__attribute__((address_space(3))) void*)(&S.tile[bi][s0]), 16, 0, 0);
-    }
+    for (int m = 0; m < 8; ++m) issue_m(T, bi, m);
   };
   issue(0, 0);
   const int ngroups = (U.Kc + AS_GROUP - 1) / AS_GROUP;
@@ -523,27 +539,36 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
   // next to the MFMAs of step j. Each step is its own scheduling region: first the LDS
   // reads of a later block's B fragments, then one MFMA followed by up to 6 vector-ALU
   // operations, 16 times (the matrix core takes 32 cycles per MFMA, in which this wave
-  // issues the selection work).
-  auto tile = [&](int bi, int grp) {
+  // issues the selection work). Steps 1-4 also issue the loads of tile Tn into the other
+  // buffer, which every wave finished reading before this tile's barrier.
+  auto tile = [&](int bi, int grp, int Tn) {
     const u32x4* tl = S.tile[bi];
     bf16x8_t B0[8], B1[8];
     floatx16 accA[2], accB[2];
     float b1 = -INFINITY, b2 = -INFINITY;
+    issue_m(Tn, bi ^ 1, 0);
+    issue_m(Tn, bi ^ 1, 1);
     load_b(tl, 0, B0);
     load_b(tl, 1, B1);
     mma_half(B0, 0, accA);
-    AS_STEP(16);
+    AS_STEP_V(16, 2);
+    issue_m(Tn, bi ^ 1, 2);
+    issue_m(Tn, bi ^ 1, 3);
     mma_half(B0, 1, accB);
     sel_half(accA, 0, b1, b2);
-    AS_STEP(0);
+    AS_STEP_V(0, 2);
+    issue_m(Tn, bi ^ 1, 4);
+    issue_m(Tn, bi ^ 1, 5);
     mma_half(B1, 0, accA);
     sel_half(accB, 1, b1, b2);
     finish(0, bi, grp, b1, b2);
-    AS_STEP(0);
+    AS_STEP_V(0, 2);
+    issue_m(Tn, bi ^ 1, 6);
+    issue_m(Tn, bi ^ 1, 7);
     load_b(tl, 2, B0);
     mma_half(B1, 1, accB);
     sel_half(accA, 0, b1, b2);
-    AS_STEP(8);
+    AS_STEP_V(8, 2);
     mma_half(B0, 0, accA);
     sel_half(accB, 1, b1, b2);
     finish(1, bi, grp, b1, b2);
@@ -576,9 +601,6 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of tile T have landed
       __syncthreads();  // tile T is in LDS; red[(T - 1) & 1] is complete
       const int bi = T & 1;
-      // into the buffer of tile T - 1, which every wave has finished; after the last tile a
-      // harmless reload of it
-      issue(min(T + 1, ntiles - 1), bi ^ 1);
       const float xnext = fresh ? 0.f : xn2[xrow(min(T + 1, ntiles - 1))];
       reduce(T - 1, xn, grp, last);
       if (fresh) {
@@ -588,7 +610,9 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
         xn = xc;
       }
       xc = xnext;
-      tile(bi, grp);
+      // the next tile's loads go into the buffer of tile T - 1, which every wave has
+      // finished; after the last tile a harmless reload of it
+      tile(bi, grp, min(T + 1, ntiles - 1));
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the trailing reload has landed: the buffers are free
     __syncthreads();
