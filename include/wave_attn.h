@@ -71,15 +71,21 @@ typedef struct wave_shape {
   const int64_t* ctx;   /* host [B]: N_b, 1 <= N_b < 2^31 */
 } wave_shape;
 
-/* Sizes of the index arrays (element counts) and of the build workspace (bytes). */
+/*
+ * Sizes of the index arrays (element counts) and of the build workspace (bytes).
+ * Per (b, g) block the index arrays hold R_b rows and CS_b clusters: R_b = N_b and
+ * CS_b = C_b in the dense layout; R_b = cap_segs * L_s and CS_b = cap_segs * K_s
+ * with a capacity (wave_index_plan_cap).
+ */
 typedef struct wave_index_sizes {
-  int64_t rows;          /* sum_b G * N_b: rows of k_sorted, v_sorted; length of perm, inv_perm, assign */
-  int64_t clusters;      /* sum_b G * C_b: rows of centroids, centroids_bf16, vsum; length of sizes */
-  int64_t offsets_len;   /* sum_b G * (C_b + 1): length of offsets */
+  int64_t rows;          /* sum_b G * R_b: rows of k_sorted, v_sorted; length of perm, inv_perm, assign */
+  int64_t clusters;      /* sum_b G * CS_b: rows of centroids, centroids_bf16, vsum; length of sizes */
+  int64_t offsets_len;   /* sum_b G * (CS_b + 1): length of offsets */
   int64_t units;         /* sum_b G * ceil(N_b / seg_len): independent k-means problems */
   int32_t max_clusters;  /* max_b C_b */
-  int32_t reserved;
+  int32_t cap_segs;      /* the capacity planned for (0: dense layout) */
   size_t build_ws_bytes; /* workspace wave_index_build needs */
+  int64_t kv_rows;       /* sum_b G * N_b: rows of the K and V that wave_index_build reads */
 } wave_index_sizes;
 
 /*
@@ -87,11 +93,18 @@ typedef struct wave_index_sizes {
  * wave_index_build (or uploaded by the caller in exactly this layout).
  * Cluster ids are local to one (sequence b, kv head g) block, in [0, C_b),
  * segment major: segment s owns ids [s*K_s, s*K_s + K(s)).
+ * Block (b, g) starts at row G*sum_{b'<b} R_b' + g*R_b, cluster
+ * G*sum_{b'<b} CS_b' + g*CS_b and offsets entry G*sum_{b'<b} (CS_b'+1) + g*(CS_b+1)
+ * (R_b, CS_b as in wave_index_sizes); a block's first N_b rows and C_b clusters
+ * (C_b + 1 offsets entries) are filled, the rest of a capacity block is room to grow.
  */
 typedef struct wave_index {
   wave_shape shape;         /* ctx points at caller host memory that must outlive the index */
   int32_t seg_len;          /* L_s */
   int32_t clusters_per_seg; /* K_s */
+  int32_t cap_segs;         /* 0: dense layout; else segments of room per block. Set by the caller
+                               before wave_index_build (the arrays' sizes come from the plan) */
+  int32_t reserved;         /* 0 */
   void* k_sorted;           /* bf16 [rows][128]: K rows grouped by cluster, ascending position inside a cluster */
   void* v_sorted;           /* bf16 [rows][128]: V rows in the same order */
   int32_t* perm;            /* [rows]: original position (within its block) of sorted slot p */
@@ -116,6 +129,17 @@ wave_status wave_index_plan(const wave_shape* shape, int32_t seg_len, int32_t cl
                             wave_index_sizes* out);
 
 /*
+ * wave_index_plan_cap -- host only. As wave_index_plan, for an index whose blocks
+ * have room for cap_segs segments each (cap_segs * L_s rows and cap_segs * K_s
+ * clusters per (b, g) block), which wave_index_append can then grow in place up
+ * to cap_segs * L_s tokens per sequence. cap_segs 0 is the dense layout.
+ * Errors: as wave_index_plan; ARG if cap_segs < 0; SHAPE if some N_b >
+ * cap_segs * L_s; UNSUPPORTED if cap_segs * L_s >= 2^31.
+ */
+wave_status wave_index_plan_cap(const wave_shape* shape, int32_t seg_len, int32_t clusters_per_seg, int32_t cap_segs,
+                                wave_index_sizes* out);
+
+/*
  * wave_index_build -- the query-independent phase (RetroInfer page, section
  * 2.A: segmented clustering at prefill). Per (sequence, kv head, segment):
  * seeded init (SplitMix64 seeded at seed + 0x9E3779B97F4A7C15*(k+1) with the
@@ -125,19 +149,52 @@ wave_status wave_index_plan(const wave_shape* shape, int32_t seg_len, int32_t cl
  * squared Euclidean distance (exact ties: lowest id), update to the ordered
  * fp32 mean of the members (empty clusters keep their centroid). Then the
  * layout of wave_index.
- *  K, V:   device bf16, rows [sizes.rows][128] in the ragged layout; read only.
- *  out:    caller-filled device pointers of every wave_index array (sizes
- *          from wave_index_plan); the call writes shape, seg_len and
- *          clusters_per_seg and fills the arrays.
+ *  K, V:   device bf16, rows [sizes.kv_rows][128] in the dense ragged layout; read only.
+ *  out:    caller-filled device pointers of every wave_index array and
+ *          cap_segs (sizes from wave_index_plan_cap with that cap_segs); the
+ *          call writes shape, seg_len and clusters_per_seg and fills the arrays.
  *  ws:     device workspace of at least build_ws_bytes (16-byte aligned).
- *  assign_trace: nullable device int32 [iters][rows]: the assignment after
- *          every round.
- * Errors: ARG (null pointer), SHAPE / UNSUPPORTED (as in wave_index_plan,
+ *  assign_trace: nullable device int32 [iters][sizes.rows]: the assignment
+ *          array after every round.
+ * Errors: ARG (null pointer), SHAPE / UNSUPPORTED (as in wave_index_plan_cap,
  * iters < 1), WORKSPACE, ALIGN, HIP.
  */
 wave_status wave_index_build(const wave_shape* shape, const void* K, const void* V, int32_t seg_len,
                              int32_t clusters_per_seg, int32_t iters, uint64_t seed, wave_index* out, void* ws,
                              size_t ws_bytes, int32_t* assign_trace, wave_stream_t stream);
+
+/*
+ * wave_index_append_plan -- host only. Workspace bytes of wave_index_append
+ * growing `index` to new_ctx. Errors as wave_index_append's argument checks.
+ */
+wave_status wave_index_append_plan(const wave_index* index, const int64_t* new_ctx, size_t* ws_bytes);
+
+/*
+ * wave_index_append -- grow a capacity index in place by the tokens decoded
+ * since its build (RetroInfer page, section 2.A: segments are clustered
+ * independently, so the index of a longer context differs from that of the
+ * shorter one only from the segment that held the old end on; IceCache page:
+ * tokens generated during decoding join the indexed cache as they accumulate).
+ * For every sequence b with new_ctx[b] > ctx[b] (ctx: index->shape.ctx), the
+ * segments s >= floor(ctx[b] / L_s) of every kv head are clustered again over
+ * the longer context, with the seeded init and the `iters` Lloyd rounds of
+ * wave_index_build, and written in place: the old tokens of segment
+ * floor(ctx[b] / L_s) are read from the index itself, the new ones from K_new
+ * and V_new. Earlier segments are not touched. Given the build's iters and seed,
+ * every array equals that of wave_index_build over the longer context.
+ *  index:   a capacity index (cap_segs > 0) filled by wave_index_build or an
+ *           earlier append; on success index->shape.ctx = new_ctx.
+ *  new_ctx: host [B], ctx[b] <= new_ctx[b] <= cap_segs * L_s; must outlive the index.
+ *  K_new, V_new: device bf16 [sum_b G * A_b][128], A_b = new_ctx[b] - ctx[b],
+ *           ragged over the appended tokens: row of (b, g, i) is
+ *           G * sum_{b'<b} A_b' + g * A_b + i (NULL allowed when no A_b > 0).
+ *  ws:      device workspace of at least wave_index_append_plan bytes.
+ * Calls on one index must not overlap one another or a decode over it.
+ * Errors: ARG (null pointer, iters < 1, cap_segs = 0), SHAPE (new_ctx[b] < ctx[b]
+ * or beyond the capacity), WORKSPACE, ALIGN, HIP.
+ */
+wave_status wave_index_append(wave_index* index, const int64_t* new_ctx, const void* K_new, const void* V_new,
+                              int32_t iters, uint64_t seed, void* ws, size_t ws_bytes, wave_stream_t stream);
 
 /*
  * wave_attn_decode_plan -- host only. Sizes of the query-dependent phase (Vortex

@@ -36,13 +36,13 @@ class _Shape(ctypes.Structure):
 
 class _Sizes(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_int64), ("clusters", ctypes.c_int64), ("offsets_len", ctypes.c_int64),
-                ("units", ctypes.c_int64), ("max_clusters", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("build_ws_bytes", ctypes.c_size_t)]
+                ("units", ctypes.c_int64), ("max_clusters", ctypes.c_int32), ("cap_segs", ctypes.c_int32),
+                ("build_ws_bytes", ctypes.c_size_t), ("kv_rows", ctypes.c_int64)]
 
 
 class _Index(ctypes.Structure):
     _fields_ = [("shape", _Shape), ("seg_len", ctypes.c_int32), ("clusters_per_seg", ctypes.c_int32),
-                ("k_sorted", ctypes.c_void_p), ("v_sorted", ctypes.c_void_p), ("perm", ctypes.c_void_p),
+                ("cap_segs", ctypes.c_int32), ("reserved", ctypes.c_int32), ("k_sorted", ctypes.c_void_p), ("v_sorted", ctypes.c_void_p), ("perm", ctypes.c_void_p),
                 ("inv_perm", ctypes.c_void_p), ("assign", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
                 ("sizes", ctypes.c_void_p), ("centroids", ctypes.c_void_p), ("centroids_bf16", ctypes.c_void_p),
                 ("vsum", ctypes.c_void_p)]
@@ -61,6 +61,11 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         P, i32, u64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
         L.wave_index_plan.argtypes = [ctypes.POINTER(_Shape), i32, i32, ctypes.POINTER(_Sizes)]
+        L.wave_index_plan_cap.argtypes = [ctypes.POINTER(_Shape), i32, i32, i32, ctypes.POINTER(_Sizes)]
+        L.wave_index_append_plan.argtypes = [ctypes.POINTER(_Index), ctypes.POINTER(ctypes.c_int64),
+                                             ctypes.POINTER(ctypes.c_size_t)]
+        L.wave_index_append.argtypes = [ctypes.POINTER(_Index), ctypes.POINTER(ctypes.c_int64), P, P, i32, u64, P,
+                                        sz, P]
         L.wave_index_build.argtypes = [ctypes.POINTER(_Shape), P, P, i32, i32, i32, u64, ctypes.POINTER(_Index), P,
                                        sz, P, P]
         L.wave_attn_decode_plan.argtypes = [ctypes.POINTER(_Index), i32, i32, i32, ctypes.c_double,
@@ -82,7 +87,7 @@ def lib():
         for f in ("wave_index_plan", "wave_index_build", "wave_attn_decode_plan", "wave_attn_decode",
                   "wave_profiler_enable", "wave_index_build_blocks", "wave_attn_decode_topk",
                   "wave_attn_decode_shared", "wave_attn_decode_tail_plan", "wave_attn_decode_tail",
-                  "wave_attn_decode_static"):
+                  "wave_attn_decode_static", "wave_index_plan_cap", "wave_index_append_plan", "wave_index_append"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -131,8 +136,17 @@ def _check_devices(device, **tensors):
             raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
 
 
-def _check_reuse(index, n_kv_heads, ctx, seg_len, clusters_per_seg):
+def _check_reuse(index, n_kv_heads, ctx, seg_len, clusters_per_seg, cap_segs=0):
     """An index passed for reuse must have been planned for exactly this shape."""
+    if index.cap_segs != int(cap_segs):
+        raise ValueError("index was allocated with cap_segs=%d, not %d" % (index.cap_segs, int(cap_segs)))
+    if index.cap_segs > 0:
+        # a capacity index takes any contexts of its batch size that fit (the plan checks them)
+        if (index.n_kv_heads != int(n_kv_heads) or len(index.ctx) != len(ctx) or index.seg_len != int(seg_len)
+                or index.clusters_per_seg != int(clusters_per_seg)):
+            raise ValueError("index was allocated for n_kv_heads=%d batch=%d seg_len=%d clusters_per_seg=%d"
+                             % (index.n_kv_heads, len(index.ctx), index.seg_len, index.clusters_per_seg))
+        return
     if (index.n_kv_heads != int(n_kv_heads) or index.ctx != [int(n) for n in ctx]
             or index.seg_len != int(seg_len) or index.clusters_per_seg != int(clusters_per_seg)):
         raise ValueError("index was allocated for n_kv_heads=%d ctx=%s seg_len=%d clusters_per_seg=%d, not for "
@@ -142,8 +156,8 @@ def _check_reuse(index, n_kv_heads, ctx, seg_len, clusters_per_seg):
 
 
 def _check_build_io(K, V, index, ws, z):
-    _check_tensor(K, "K", torch.bfloat16, (z["rows"], HEAD_DIM))
-    _check_tensor(V, "V", torch.bfloat16, (z["rows"], HEAD_DIM))
+    _check_tensor(K, "K", torch.bfloat16, (z["kv_rows"], HEAD_DIM))
+    _check_tensor(V, "V", torch.bfloat16, (z["kv_rows"], HEAD_DIM))
     if ws is not None:
         _check_tensor(ws, "ws", torch.uint8, (ws.numel(),))
         if ws.numel() < z["build_ws_bytes"]:
@@ -170,22 +184,25 @@ def _check_decode_io(index, q, out, sel_ids, lse, ws, k_max, wsb, **more):
     _check_devices(index.device, q=q, out=out, sel_ids=sel_ids, lse=lse, ws=ws, **more)
 
 
-def wave_index_plan(n_kv_heads, ctx, seg_len, clusters_per_seg):
-    """Sizes of the index arrays and of the build workspace (dict)."""
+def wave_index_plan(n_kv_heads, ctx, seg_len, clusters_per_seg, cap_segs=0):
+    """Sizes of the index arrays and of the build workspace (dict); cap_segs > 0: every
+    (sequence, kv head) block has room for that many segments (wave_index_append)."""
     sh, _keep = _shape(n_kv_heads, ctx)
     z = _Sizes()
-    _check(lib().wave_index_plan(ctypes.byref(sh), int(seg_len), int(clusters_per_seg), ctypes.byref(z)))
+    _check(lib().wave_index_plan_cap(ctypes.byref(sh), int(seg_len), int(clusters_per_seg), int(cap_segs),
+                                     ctypes.byref(z)))
     return {f: getattr(z, f) for f, _ in _Sizes._fields_}
 
 
 class WaveIndex:
     """Device arrays of one index (torch tensors) and the C struct pointing at them."""
 
-    def __init__(self, n_kv_heads, ctx, seg_len, clusters_per_seg, arrays):
+    def __init__(self, n_kv_heads, ctx, seg_len, clusters_per_seg, arrays, cap_segs=0):
         self.n_kv_heads = int(n_kv_heads)
         self.ctx = [int(n) for n in ctx]
         self.seg_len = int(seg_len)
         self.clusters_per_seg = int(clusters_per_seg)
+        self.cap_segs = int(cap_segs)
         self.arrays = arrays
         for k, v in arrays.items():
             setattr(self, k, v)
@@ -195,13 +212,20 @@ class WaveIndex:
         self.c.shape = sh
         self.c.seg_len = self.seg_len
         self.c.clusters_per_seg = self.clusters_per_seg
+        self.c.cap_segs = self.cap_segs
         for k in ("k_sorted", "v_sorted", "perm", "inv_perm", "assign", "offsets", "sizes", "centroids",
                   "centroids_bf16", "vsum"):
             setattr(self.c, k, arrays[k].data_ptr())
 
+    def set_ctx(self, ctx):
+        """Point the index at new contexts (host array kept alive here)."""
+        self.ctx = [int(n) for n in ctx]
+        self._ctx_arr = (ctypes.c_int64 * len(self.ctx))(*self.ctx)
+        self.c.shape.ctx = ctypes.cast(self._ctx_arr, ctypes.POINTER(ctypes.c_int64))
+
     @staticmethod
-    def allocate(n_kv_heads, ctx, seg_len, clusters_per_seg, device="cuda"):
-        z = wave_index_plan(n_kv_heads, ctx, seg_len, clusters_per_seg)
+    def allocate(n_kv_heads, ctx, seg_len, clusters_per_seg, device="cuda", cap_segs=0):
+        z = wave_index_plan(n_kv_heads, ctx, seg_len, clusters_per_seg, cap_segs)
         R, Cn, O = z["rows"], z["clusters"], z["offsets_len"]
         e = dict(device=device)
         arrays = {
@@ -216,24 +240,35 @@ class WaveIndex:
             "centroids_bf16": torch.empty((Cn, HEAD_DIM), dtype=torch.bfloat16, **e),
             "vsum": torch.empty((Cn, HEAD_DIM), dtype=torch.float32, **e),
         }
-        return WaveIndex(n_kv_heads, ctx, seg_len, clusters_per_seg, arrays), z
+        return WaveIndex(n_kv_heads, ctx, seg_len, clusters_per_seg, arrays, cap_segs), z
+
+
+def _build_prep(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, cap_segs, index, ws):
+    """Checks, and the index and workspace of a build (allocated unless passed)."""
+    if index is not None:
+        cap_segs = index.cap_segs
+    z = wave_index_plan(n_kv_heads, ctx, seg_len, clusters_per_seg, cap_segs)
+    if index is not None:
+        _check_reuse(index, n_kv_heads, ctx, seg_len, clusters_per_seg, cap_segs)
+    _check_build_io(K, V, index, ws, z)
+    if index is None:
+        index, z = WaveIndex.allocate(n_kv_heads, ctx, seg_len, clusters_per_seg, device=K.device, cap_segs=cap_segs)
+    else:
+        index.set_ctx(ctx)
+    if ws is None:
+        ws = torch.empty(max(int(z["build_ws_bytes"]), 16), dtype=torch.uint8, device=K.device)
+    return index, ws, z
 
 
 def wave_index_build(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, iters, seed, assign_trace=False,
-                     stream=None, index=None, ws=None):
+                     stream=None, index=None, ws=None, cap_segs=0):
     """Build the index of K, V (bf16 [sum_b G*N_b, 128] device tensors) on the current stream.
 
     Returns the WaveIndex (and the [iters, rows] int32 assignment trace if asked).  `index`
-    and `ws` may be passed to reuse existing allocations.
+    and `ws` may be passed to reuse existing allocations; cap_segs > 0 lays the index out
+    with room for that many segments per (sequence, kv head) block, for wave_index_append.
     """
-    z = wave_index_plan(n_kv_heads, ctx, seg_len, clusters_per_seg)
-    if index is not None:
-        _check_reuse(index, n_kv_heads, ctx, seg_len, clusters_per_seg)
-    _check_build_io(K, V, index, ws, z)
-    if index is None:
-        index, z = WaveIndex.allocate(n_kv_heads, ctx, seg_len, clusters_per_seg, device=K.device)
-    if ws is None:
-        ws = torch.empty(max(int(z["build_ws_bytes"]), 16), dtype=torch.uint8, device=K.device)
+    index, ws, z = _build_prep(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, cap_segs, index, ws)
     tr = torch.empty((iters, z["rows"]), dtype=torch.int32, device=K.device) if assign_trace else None
     sh = _Shape()
     ctypes.pointer(sh)[0] = index.c.shape  # a copy whose ctx points at the index's own array
@@ -243,20 +278,55 @@ def wave_index_build(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, iters, se
     return (index, tr) if assign_trace else index
 
 
-def wave_index_build_blocks(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, stream=None, index=None, ws=None):
+def wave_index_build_blocks(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, stream=None, index=None, ws=None,
+                            cap_segs=0):
     """Index of the block top-k baseline: contiguous blocks in place of the k-means clusters."""
-    z = wave_index_plan(n_kv_heads, ctx, seg_len, clusters_per_seg)
-    if index is not None:
-        _check_reuse(index, n_kv_heads, ctx, seg_len, clusters_per_seg)
-    _check_build_io(K, V, index, ws, z)
-    if index is None:
-        index, z = WaveIndex.allocate(n_kv_heads, ctx, seg_len, clusters_per_seg, device=K.device)
-    if ws is None:
-        ws = torch.empty(max(int(z["build_ws_bytes"]), 16), dtype=torch.uint8, device=K.device)
+    index, ws, z = _build_prep(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, cap_segs, index, ws)
     sh = _Shape()
     ctypes.pointer(sh)[0] = index.c.shape
     _check(lib().wave_index_build_blocks(ctypes.byref(sh), _ptr(K), _ptr(V), int(seg_len), int(clusters_per_seg),
                                          ctypes.byref(index.c), _ptr(ws), ws.numel(), _stream(stream)))
+    return index
+
+
+def wave_index_append_plan(index, new_ctx):
+    """Workspace bytes of wave_index_append(index, ..., new_ctx)."""
+    arr = (ctypes.c_int64 * len(new_ctx))(*[int(n) for n in new_ctx])
+    n = ctypes.c_size_t()
+    _check(lib().wave_index_append_plan(ctypes.byref(index.c), arr, ctypes.byref(n)))
+    return n.value
+
+
+def wave_index_append(index, K_new, V_new, new_ctx, iters, seed, ws=None, stream=None):
+    """Grow a capacity index in place to new_ctx: K_new, V_new are bf16 device tensors of the
+    appended tokens, [sum_b G*(new_ctx[b] - ctx[b]), 128] ragged over the appended counts.
+    Only the segments from the one that held the old end on are clustered again; with the
+    build's iters and seed the index equals a build over the longer context."""
+    if index.cap_segs < 1:
+        raise ValueError("the index has no capacity (built with cap_segs=0)")
+    if len(new_ctx) != len(index.ctx):
+        raise ValueError("new_ctx has %d sequences, the index %d" % (len(new_ctx), len(index.ctx)))
+    new_ctx = [int(n) for n in new_ctx]
+    A = [n - o for n, o in zip(new_ctx, index.ctx)]
+    if min(A) < 0:
+        raise ValueError("new_ctx %s is shorter than the index's ctx %s" % (new_ctx, index.ctx))
+    rows = index.n_kv_heads * sum(A)
+    _check_tensor(K_new, "K_new", torch.bfloat16, (rows, HEAD_DIM))
+    _check_tensor(V_new, "V_new", torch.bfloat16, (rows, HEAD_DIM))
+    wsb = wave_index_append_plan(index, new_ctx)
+    if ws is not None:
+        _check_tensor(ws, "ws", torch.uint8, (ws.numel(),))
+        if ws.numel() < wsb:
+            raise ValueError("workspace has %d bytes, the append needs %d" % (ws.numel(), wsb))
+    _check_devices(index.device, K_new=K_new, V_new=V_new, ws=ws)
+    if ws is None:
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=index.device)
+    arr = (ctypes.c_int64 * len(new_ctx))(*new_ctx)
+    _check(lib().wave_index_append(ctypes.byref(index.c), arr, _ptr(K_new) if rows else None,
+                                   _ptr(V_new) if rows else None, int(iters), ctypes.c_uint64(seed), _ptr(ws),
+                                   ws.numel(), _stream(stream)))
+    index.ctx = new_ctx
+    index._ctx_arr = arr  # the C struct now points at it
     return index
 
 

@@ -31,73 +31,91 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 constexpr uint64_t GAMMA = 0x9E3779B97F4A7C15ULL;
 
 // ------------------------------------------------------------------ unit lookup
+// The batch of one build call. first[b] is the first segment of sequence b that the
+// call clusters (0 for a whole build; ceil(N_b / seg_len): none): an append re-clusters
+// only the segments from the first one it changes on. The call's input rows (K, V and
+// the per-row workspaces) are ragged over M_b = N_b - first[b] * seg_len tokens per
+// block: row of (b, g, t) = G * sum_{b'<b} M_b' + g * M_b + t - first[b] * seg_len,
+// which is the layout of the index's own rows for a whole dense build.
+struct BuildSeq : SeqArgs {
+  int32_t first[MAXB];
+};
+
+__device__ inline int64_t nseg_of(const BuildSeq& sa, int b) { return (sa.N[b] + sa.seg_len - 1) / sa.seg_len; }
+
 struct Unit {
   int b, g, s;
-  int64_t row0;   // first row of the segment
-  int64_t brow;   // first row of the (b, g) block
-  int64_t gclu;   // global index of the segment's first cluster
+  int64_t row0;   // index row of the segment's first token
+  int64_t brow;   // index row of the (b, g) block's token 0
+  int64_t irow0;  // input row of the segment's first token
+  int64_t gclu;   // index of the segment's first cluster
   int32_t L, Kc;  // segment length and clusters
   int32_t cbase;  // block-level id of the first cluster (s * K_s)
   int32_t tok0;   // segment start within the block (s * L_s)
   int64_t boff;   // first offsets entry of the block
   int32_t N, C;
-  int64_t u;      // unit index
 };
 
-__device__ inline Unit unit_of(const SeqArgs& sa, int64_t u) {
+// unit u of the call: units in (b, g, s) order, segments s >= first[b]
+__device__ inline Unit unit_of(const BuildSeq& sa, int64_t u) {
   Unit r;
-  r.u = u;
   int b = 0;
-  int64_t row = 0, clu = 0, off = 0;
+  int64_t irow = 0;
   for (;; ++b) {
-    const int64_t nseg = (sa.N[b] + sa.seg_len - 1) / sa.seg_len;
-    if (u < sa.G * nseg) break;
-    u -= sa.G * nseg;
-    row += (int64_t)sa.G * sa.N[b];
-    clu += (int64_t)sa.G * sa.C[b];
-    off += (int64_t)sa.G * (sa.C[b] + 1);
+    const int64_t nu = nseg_of(sa, b) - sa.first[b];
+    if (u < sa.G * nu) break;
+    u -= sa.G * nu;
+    if (nu > 0) irow += (int64_t)sa.G * (sa.N[b] - (int64_t)sa.first[b] * sa.seg_len);
   }
-  const int64_t nseg = (sa.N[b] + sa.seg_len - 1) / sa.seg_len;
+  const SeqBase sb = seq_base(sa, b);
+  const int64_t f = sa.first[b], nu = nseg_of(sa, b) - f, M = sb.N - f * sa.seg_len;
   r.b = b;
-  r.g = (int)(u / nseg);
-  r.s = (int)(u % nseg);
-  r.N = sa.N[b];
-  r.C = sa.C[b];
-  r.brow = row + (int64_t)r.g * r.N;
+  r.g = (int)(u / nu);
+  r.s = (int)(f + u % nu);
+  r.N = sb.N;
+  r.C = sb.C;
+  r.brow = sb.row + (int64_t)r.g * sb.NS;
   r.tok0 = r.s * sa.seg_len;
   r.row0 = r.brow + r.tok0;
+  r.irow0 = irow + (int64_t)r.g * M + (r.tok0 - f * sa.seg_len);
   r.L = (int32_t)min((int64_t)sa.seg_len, (int64_t)r.N - r.tok0);
   r.Kc = seg_clusters(r.L, sa.seg_len, sa.K_s);
   r.cbase = r.s * sa.K_s;
-  r.gclu = clu + (int64_t)r.g * r.C + r.cbase;
-  r.boff = off + (int64_t)r.g * (r.C + 1);
+  r.gclu = sb.clu + (int64_t)r.g * sb.CS + r.cbase;
+  r.boff = sb.off + (int64_t)r.g * (sb.CS + 1);
   return r;
 }
 
-// global cluster index -> (block row base, block cluster base, offsets base, local id)
+// cluster F of the call (the clusters of its units in (b, g, id) order) -> its block
 struct CluRef {
   int64_t brow, bclu, boff;
+  int64_t ib;  // input row of block position t is ib + t (t >= first[b] * seg_len)
+  int64_t gF;  // index of the cluster
   int32_t j, N, C;
 };
 
-__device__ inline CluRef clu_of(const SeqArgs& sa, int64_t F) {
+__device__ inline CluRef clu_of(const BuildSeq& sa, int64_t F) {
   int b = 0;
-  int64_t row = 0, clu = 0, off = 0;
+  int64_t irow = 0;
   for (;; ++b) {
-    if (F < clu + (int64_t)sa.G * sa.C[b]) break;
-    row += (int64_t)sa.G * sa.N[b];
-    clu += (int64_t)sa.G * sa.C[b];
-    off += (int64_t)sa.G * (sa.C[b] + 1);
+    const int64_t nu = nseg_of(sa, b) - sa.first[b];
+    const int64_t nc = nu > 0 ? sa.C[b] - (int64_t)sa.first[b] * sa.K_s : 0;
+    if (F < sa.G * nc) break;
+    F -= sa.G * nc;
+    if (nu > 0) irow += (int64_t)sa.G * (sa.N[b] - (int64_t)sa.first[b] * sa.seg_len);
   }
+  const SeqBase sb = seq_base(sa, b);
+  const int64_t f = sa.first[b], nc = sb.C - f * sa.K_s, M = sb.N - f * sa.seg_len;
+  const int g = (int)(F / nc);
   CluRef r;
-  const int64_t rel = F - clu;
-  const int g = (int)(rel / sa.C[b]);
-  r.j = (int32_t)(rel % sa.C[b]);
-  r.N = sa.N[b];
-  r.C = sa.C[b];
-  r.brow = row + (int64_t)g * r.N;
-  r.bclu = clu + (int64_t)g * r.C;
-  r.boff = off + (int64_t)g * (r.C + 1);
+  r.j = (int32_t)(f * sa.K_s + F % nc);
+  r.N = sb.N;
+  r.C = sb.C;
+  r.brow = sb.row + (int64_t)g * sb.NS;
+  r.bclu = sb.clu + (int64_t)g * sb.CS;
+  r.boff = sb.off + (int64_t)g * (sb.CS + 1);
+  r.ib = irow + (int64_t)g * M - f * sa.seg_len;
+  r.gF = r.bclu + r.j;
   return r;
 }
 
@@ -125,7 +143,7 @@ __device__ __forceinline__ uint64_t seed_key(int b, int g, int s) {
 // rounding is the key itself and its squared norm is summed here too.
 constexpr int INIT_THREADS = 1024;
 
-__global__ __launch_bounds__(INIT_THREADS) void k_init(SeqArgs sa, uint64_t seed, const uint16_t* __restrict__ K,
+__global__ __launch_bounds__(INIT_THREADS) void k_init(BuildSeq sa, uint64_t seed, const uint16_t* __restrict__ K,
                                                        float* __restrict__ cent, uint16_t* __restrict__ chat,
                                                        float* __restrict__ norm) {
   extern __shared__ uint8_t smem[];
@@ -156,7 +174,7 @@ __global__ __launch_bounds__(INIT_THREADS) void k_init(SeqArgs sa, uint64_t seed
 #pragma unroll
     for (int u = 0; u < UI; ++u) {
       const int i = min(i0 + u * (INIT_THREADS / 16), U.Kc - 1);
-      v[u] = *reinterpret_cast<const u32x4*>(K + (U.row0 + idx[i]) * D + l16 * 8);
+      v[u] = *reinterpret_cast<const u32x4*>(K + (U.irow0 + idx[i]) * D + l16 * 8);
     }
 #pragma unroll
     for (int u = 0; u < UI; ++u) {
@@ -257,28 +275,27 @@ struct AssignLds {
 };
 
 // Workgroups per unit: ceil(L / tpw) with tpw tokens per workgroup (a multiple of
-// AS_TT chosen by the host); units in (b, g, s) order.
-__device__ inline void assign_wg_map(const SeqArgs& sa, int tpw, int w, Unit& U, int& tok_begin) {
+// AS_TT chosen by the host); units in (b, g, s) order, segments s >= first[b].
+__device__ inline void assign_wg_map(const BuildSeq& sa, int tpw, int w, Unit& U, int& tok_begin) {
   int64_t u = 0;
-  int b = 0;
-  for (;; ++b) {
+  for (int b = 0;; ++b) {
     const int64_t N = sa.N[b];
-    const int64_t nseg = (N + sa.seg_len - 1) / sa.seg_len;
+    const int64_t nseg = (N + sa.seg_len - 1) / sa.seg_len, nu = nseg - sa.first[b];
     const int64_t last = N - (nseg - 1) * sa.seg_len;
     const int wf = (sa.seg_len + tpw - 1) / tpw, wl = (int)((last + tpw - 1) / tpw);
-    const int64_t per_g = (nseg - 1) * wf + wl;
+    const int64_t per_g = nu > 0 ? (nu - 1) * wf + wl : 0;
     if (w < sa.G * per_g) {
       const int g = (int)(w / per_g);
       const int64_t r = w % per_g;
       int64_t s = r / wf;
       int64_t k = r % wf;
-      if (s >= nseg - 1) { s = nseg - 1; k = r - (nseg - 1) * wf; }
-      U = unit_of(sa, u + (int64_t)g * nseg + s);
+      if (s >= nu - 1) { s = nu - 1; k = r - (nu - 1) * wf; }
+      U = unit_of(sa, u + (int64_t)g * nu + s);
       tok_begin = (int)(k * tpw);
       return;
     }
     w -= (int)(sa.G * per_g);
-    u += sa.G * nseg;
+    u += sa.G * nu;
   }
 }
 
@@ -331,7 +348,7 @@ __device__ __forceinline__ void top2_tree32(const float (&v)[32], float& b1, flo
 }
 
 template <bool MULTI>
-__global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, const uint16_t* __restrict__ K,
+__global__ __launch_bounds__(AS_THREADS, 1) void k_assign(BuildSeq sa, int tpw, const uint16_t* __restrict__ K,
                                                           const uint16_t* __restrict__ chat,
                                                           const float* __restrict__ norm,
                                                           int32_t* __restrict__ assign, float* __restrict__ xn2,
@@ -344,7 +361,7 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
   const int nrow = min(tpw, U.L - tb0);  // rows of the workgroup's range
   const int ntiles = (nrow + AS_TT - 1) / AS_TT;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, h = lane >> 5, col = lane & 31;
-  const uint16_t* Kr = K + (U.row0 + tb0) * D;  // first row of the range
+  const uint16_t* Kr = K + (U.irow0 + tb0) * D;  // first input row of the range
   // rows of tile T into buffer bi: wave wv fills slots [(8 wv + m) * 64, +64), m < 8; lane i of
   // a load writes slot base + i, i.e. token t = slot / 16, chunk (slot % 16) ^ (t % 16).
   // Rows past the range end repeat its last row: their results equal that row's.
@@ -592,7 +609,7 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
   // pass computes them from the tiles in LDS and stores them; later passes load them with
   // the tile loads, a tile ahead (the serial LDS reads of the computation cost a tenth of
   // the launch).
-  auto xrow = [&](int T) { return U.row0 + tb0 + min(T * AS_TT + wv * 32 + col, nrow - 1); };
+  auto xrow = [&](int T) { return U.irow0 + tb0 + min(T * AS_TT + wv * 32 + col, nrow - 1); };
   auto pass = [&](int grp, bool last) {
     const bool fresh = first && grp == 0;
     float xn = 0.f;                                 // |x|^2 of this wave's tokens of the previous tile
@@ -788,7 +805,7 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(SeqArgs sa, int tpw, c
 // per-wave bases. Writes sizes, offsets (block level) and perm.
 constexpr int SORT_THREADS = 1024;
 
-__global__ __launch_bounds__(SORT_THREADS) void k_sort(SeqArgs sa, const int32_t* __restrict__ assign,
+__global__ __launch_bounds__(SORT_THREADS) void k_sort(BuildSeq sa, const int32_t* __restrict__ assign,
                                                        int32_t* __restrict__ rank, int32_t* __restrict__ sizes,
                                                        int32_t* __restrict__ offsets, int32_t* __restrict__ perm) {
   extern __shared__ uint8_t smem[];
@@ -822,7 +839,7 @@ __global__ __launch_bounds__(SORT_THREADS) void k_sort(SeqArgs sa, const int32_t
       active &= ~same;
     }
     const int base = __shfl(old, myleader, 64);
-    if (valid) rank[U.row0 + t] = base + myrank;
+    if (valid) rank[U.irow0 + t] = base + myrank;
   }
   __syncthreads();
   // per-cluster totals, per-wave bases, exclusive offsets over clusters
@@ -873,7 +890,7 @@ __global__ __launch_bounds__(SORT_THREADS) void k_sort(SeqArgs sa, const int32_t
   for (int t = tid; t < U.L; t += SORT_THREADS) {
     const int c = min(max(assign[U.row0 + t] - U.cbase, 0), Kc - 1);
     const int w = t / span;
-    const int p = U.tok0 + hist[w * Kc + c] + rank[U.row0 + t];
+    const int p = U.tok0 + hist[w * Kc + c] + rank[U.irow0 + t];
     perm[U.brow + p] = U.tok0 + t;
   }
 }
@@ -934,7 +951,7 @@ __device__ inline uint64_t block_scan_u64(uint64_t v, uint64_t* tmp, uint64_t* t
   return r;
 }
 
-__global__ __launch_bounds__(RS_THREADS) void k_sort_radix(SeqArgs sa, int parts, const int32_t* __restrict__ assign,
+__global__ __launch_bounds__(RS_THREADS) void k_sort_radix(BuildSeq sa, int parts, const int32_t* __restrict__ assign,
                                                            int32_t* __restrict__ sizes,
                                                            int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ perm) {
@@ -1118,21 +1135,23 @@ __global__ __launch_bounds__(RS_THREADS) void k_sort_radix(SeqArgs sa, int parts
 // squared norm. The last round (FINAL) also copies every member's K and V row
 // to its sorted slot, writes inv_perm and the ordered fp32 value sums.
 template <bool FINAL>
-__global__ __launch_bounds__(256) void k_update(SeqArgs sa, int64_t nclu, const uint16_t* __restrict__ K,
+__global__ __launch_bounds__(256) void k_update(BuildSeq sa, int64_t nclu, const uint16_t* __restrict__ K,
                                                 const uint16_t* __restrict__ V, wave_index ix,
                                                 float* __restrict__ norm) {
-  const int64_t F = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t Fc = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (F >= nclu) return;
+  if (Fc >= nclu) return;
+  const CluRef cr = clu_of(sa, Fc);
+  const int64_t F = cr.gF;
   const int n = ix.sizes[F];
   if (n == 0) {
     if (FINAL) *reinterpret_cast<float2*>(ix.vsum + F * D + 2 * lane) = make_float2(0.f, 0.f);
     return;
   }
-  const CluRef cr = clu_of(sa, F);
   const int off = ix.offsets[cr.boff + cr.j];
-  const uint16_t* Kb = K + cr.brow * D + 2 * lane;
-  const uint16_t* Vb = V + cr.brow * D + 2 * lane;
+  // input rows of the block's positions (index arithmetic: the base row alone may lie
+  // before the first input row)
+  const int64_t eb = cr.ib * D + 2 * lane;
   uint16_t* Ks = reinterpret_cast<uint16_t*>(ix.k_sorted) + cr.brow * D + 2 * lane;
   uint16_t* Vs = reinterpret_cast<uint16_t*>(ix.v_sorted) + cr.brow * D + 2 * lane;
   const int32_t* pb = ix.perm + cr.brow + off;
@@ -1146,8 +1165,8 @@ __global__ __launch_bounds__(256) void k_update(SeqArgs sa, int64_t nclu, const 
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       tt[u] = __shfl(ptv, min(u, m - 1), 64);
-      kr[u] = *reinterpret_cast<const uint32_t*>(Kb + (int64_t)tt[u] * D);
-      if (FINAL) vr[u] = *reinterpret_cast<const uint32_t*>(Vb + (int64_t)tt[u] * D);
+      kr[u] = *reinterpret_cast<const uint32_t*>(K + (eb + (int64_t)tt[u] * D));
+      if (FINAL) vr[u] = *reinterpret_cast<const uint32_t*>(V + (eb + (int64_t)tt[u] * D));
     }
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
@@ -1188,10 +1207,57 @@ __global__ __launch_bounds__(256) void k_update(SeqArgs sa, int64_t nclu, const 
 // per-block summaries built once, blocks scored and the top-k attended per query):
 // token i of a unit of L tokens and Kc clusters goes to block floor(i Kc / L), the
 // contiguous balanced blocks in the clusters' id space. One workgroup per unit.
-__global__ __launch_bounds__(1024) void k_block_assign(SeqArgs sa, int32_t* __restrict__ assign) {
+__global__ __launch_bounds__(1024) void k_block_assign(BuildSeq sa, int32_t* __restrict__ assign) {
   const Unit U = unit_of(sa, blockIdx.x);
   for (int i = threadIdx.x; i < U.L; i += blockDim.x)
     assign[U.row0 + i] = U.cbase + (int32_t)((int64_t)i * U.Kc / U.L);
+}
+
+// ------------------------------------------------------------------ k_stage
+// Input rows of an append (RetroInfer page, section 2.A: segments are clustered
+// independently, so a longer context changes only its last segments). For every
+// sequence with new tokens, the tokens of each block from the start of the segment
+// that held the old end (first[b] * seg_len) to the new end, in the call's input
+// layout. Tokens already in the index come from its sorted copy (slot inv_perm[t]);
+// the new ones from the caller's rows, ragged over the appended counts
+// A_b = N_b - n_old[b]: row of (b, g, i) is G * sum_{b'<b} A_b' + g * A_b + i.
+// Grid (B * G, ceil(max_b M_b / 64)); 16 lanes per row, 64 rows per workgroup.
+struct StageArgs {
+  int32_t B, G, seg_len, cap;
+  int32_t n_new[MAXB];
+  int32_t n_old[MAXB];
+};
+
+constexpr int STAGE_ROWS = 64;
+
+__global__ __launch_bounds__(1024) void k_stage(StageArgs a, const uint16_t* __restrict__ Kn,
+                                                const uint16_t* __restrict__ Vn, wave_index ix,
+                                                uint16_t* __restrict__ Ko, uint16_t* __restrict__ Vo) {
+  const int b = (int)blockIdx.x / a.G, g = (int)blockIdx.x % a.G;
+  const int64_t A = (int64_t)a.n_new[b] - a.n_old[b];
+  if (A <= 0) return;
+  const int64_t t0 = (int64_t)(a.n_old[b] / a.seg_len) * a.seg_len;  // first re-clustered token
+  const int64_t M = a.n_new[b] - t0;
+  const int r = (int)blockIdx.y * STAGE_ROWS + (int)(threadIdx.x >> 4);
+  if (r >= M) return;
+  int64_t irow = 0, arow = 0;
+  for (int i = 0; i < b; ++i) {
+    const int64_t Ai = (int64_t)a.n_new[i] - a.n_old[i];
+    if (Ai > 0) {
+      irow += (int64_t)a.G * (a.n_new[i] - (int64_t)(a.n_old[i] / a.seg_len) * a.seg_len);
+      arow += (int64_t)a.G * Ai;
+    }
+  }
+  const int l16 = threadIdx.x & 15;
+  const int64_t t = t0 + r;
+  const int64_t brow = ((int64_t)b * a.G + g) * a.cap * a.seg_len;
+  const bool old = t < a.n_old[b];
+  const int64_t src = old ? brow + ix.inv_perm[brow + t] : arow + (int64_t)g * A + (t - a.n_old[b]);
+  const uint16_t* SK = old ? reinterpret_cast<const uint16_t*>(ix.k_sorted) : Kn;
+  const uint16_t* SV = old ? reinterpret_cast<const uint16_t*>(ix.v_sorted) : Vn;
+  const int64_t dst = irow + (int64_t)g * M + r;
+  *reinterpret_cast<u32x4*>(Ko + dst * D + l16 * 8) = *reinterpret_cast<const u32x4*>(SK + src * D + l16 * 8);
+  *reinterpret_cast<u32x4*>(Vo + dst * D + l16 * 8) = *reinterpret_cast<const u32x4*>(SV + src * D + l16 * 8);
 }
 
 // ------------------------------------------------------------------ host side
@@ -1222,81 +1288,138 @@ static int assign_tpw(const SeqArgs& sa, int64_t units) {
   return (int)std::min<int64_t>(sa.K_s > AS_GROUP ? AS_MAXTPW_M : AS_MAXTPW, std::max<int64_t>(AS_TT, t));
 }
 
-static int64_t assign_grid(const SeqArgs& sa, int tpw) {
+static int64_t host_nseg(const BuildSeq& bs, int b) { return (bs.N[b] + bs.seg_len - 1) / bs.seg_len; }
+
+static int64_t assign_grid(const BuildSeq& bs, int tpw) {
   int64_t n = 0;
-  for (int b = 0; b < sa.B; ++b) {
-    const int64_t N = sa.N[b];
-    const int64_t nseg = (N + sa.seg_len - 1) / sa.seg_len;
-    const int64_t last = N - (nseg - 1) * sa.seg_len;
-    const int64_t wf = (sa.seg_len + tpw - 1) / tpw, wl = (last + tpw - 1) / tpw;
-    n += (int64_t)sa.G * ((nseg - 1) * wf + wl);
+  for (int b = 0; b < bs.B; ++b) {
+    const int64_t N = bs.N[b], nseg = host_nseg(bs, b), nu = nseg - bs.first[b];
+    if (nu <= 0) continue;
+    const int64_t last = N - (nseg - 1) * bs.seg_len;
+    const int64_t wf = (bs.seg_len + tpw - 1) / tpw, wl = (last + tpw - 1) / tpw;
+    n += (int64_t)bs.G * ((nu - 1) * wf + wl);
   }
   return n;
 }
 
-hipError_t launch_build(const SeqArgs& sa, const void* Kv, const void* Vv, int32_t iters, uint64_t seed,
-                        const wave_index& ix, const BuildWs& ws, int64_t units, int32_t* trace, int64_t rows,
-                        hipStream_t st) {
+// units and clusters of a call
+static void call_counts(const BuildSeq& bs, int64_t* units, int64_t* nclu) {
+  *units = *nclu = 0;
+  for (int b = 0; b < bs.B; ++b) {
+    const int64_t nu = host_nseg(bs, b) - bs.first[b];
+    if (nu <= 0) continue;
+    *units += (int64_t)bs.G * nu;
+    *nclu += (int64_t)bs.G * (bs.C[b] - (int64_t)bs.first[b] * bs.K_s);
+  }
+}
+
+static BuildSeq whole(const SeqArgs& sa) {
+  BuildSeq bs;
+  static_cast<SeqArgs&>(bs) = sa;
+  for (int b = 0; b < MAXB; ++b) bs.first[b] = 0;
+  return bs;
+}
+
+// seeded init and `iters` Lloyd rounds of the call's units (input rows K, V), then the layout
+static hipError_t run_build(const BuildSeq& bs, const uint16_t* K, const uint16_t* V, int32_t iters, uint64_t seed,
+                            const wave_index& ix, const BuildWs& ws, int32_t* trace, int64_t rows, hipStream_t st) {
   const DeviceInfo& di = device_info();
   WAVE_TRY(di.status);
-  const uint16_t* K = reinterpret_cast<const uint16_t*>(Kv);
-  const uint16_t* V = reinterpret_cast<const uint16_t*>(Vv);
-  int64_t nclu = 0;
-  for (int b = 0; b < sa.B; ++b) nclu += (int64_t)sa.G * sa.C[b];
-  const size_t init_lds = ((2 * (size_t)sa.seg_len + 15) & ~(size_t)15) + 4 * (size_t)sa.K_s;
-  const size_t sort_lds = 16 * (size_t)sa.K_s * 4;
+  int64_t units, nclu;
+  call_counts(bs, &units, &nclu);
+  if (units == 0) return hipSuccess;
+  const size_t init_lds = ((2 * (size_t)bs.seg_len + 15) & ~(size_t)15) + 4 * (size_t)bs.K_s;
+  const size_t sort_lds = 16 * (size_t)bs.K_s * 4;
   // two key buffers of E tiles; the counters (32 digits x E tiles x 16 waves) fit in one
   const int sparts = sort_parts(units, di.cus);
-  const size_t radix_tiles = ((size_t)(sa.seg_len + sparts - 1) / sparts + RS_THREADS - 1) / RS_THREADS;
+  const size_t radix_tiles = ((size_t)(bs.seg_len + sparts - 1) / sparts + RS_THREADS - 1) / RS_THREADS;
   const size_t radix_lds = 2 * radix_tiles * RS_THREADS * 4;
   const unsigned cgrid = (unsigned)((nclu + 3) / 4);
   uint16_t* chat = reinterpret_cast<uint16_t*>(ix.centroids_bf16);
-  WAVE_TRY(launch("k_init", k_init, dim3((unsigned)units), dim3(INIT_THREADS), init_lds, st, sa, seed, K,
+  WAVE_TRY(launch("k_init", k_init, dim3((unsigned)units), dim3(INIT_THREADS), init_lds, st, bs, seed, K,
                   ix.centroids, chat, ws.norm));
-  const int tpw = assign_tpw(sa, units);
-  const int64_t agrid = assign_grid(sa, tpw);
+  const int tpw = assign_tpw(bs, units);
+  const int64_t agrid = assign_grid(bs, tpw);
   for (int it = 0; it < iters; ++it) {
-    WAVE_TRY(launch("k_assign", sa.K_s > AS_GROUP ? k_assign<true> : k_assign<false>, dim3((unsigned)agrid),
-                    dim3(AS_THREADS), sizeof(AssignLds), st, sa, tpw, K, chat, ws.norm, ix.assign, ws.xn2,
+    WAVE_TRY(launch("k_assign", bs.K_s > AS_GROUP ? k_assign<true> : k_assign<false>, dim3((unsigned)agrid),
+                    dim3(AS_THREADS), sizeof(AssignLds), st, bs, tpw, K, chat, ws.norm, ix.assign, ws.xn2,
                     it == 0 ? 1 : 0));
     if (trace != nullptr)
       WAVE_TRY(hipMemcpyAsync(trace + (int64_t)it * rows, ix.assign, sizeof(int32_t) * (size_t)rows,
                               hipMemcpyDeviceToDevice, st));
-    if (sa.seg_len <= RS_MAXL)
-      WAVE_TRY(launch("k_sort", k_sort_radix, dim3((unsigned)(units * sparts)), dim3(RS_THREADS), radix_lds, st, sa,
+    if (bs.seg_len <= RS_MAXL)
+      WAVE_TRY(launch("k_sort", k_sort_radix, dim3((unsigned)(units * sparts)), dim3(RS_THREADS), radix_lds, st, bs,
                       sparts, ix.assign, ix.sizes, ix.offsets, ix.perm));
     else
-      WAVE_TRY(launch("k_sort", k_sort, dim3((unsigned)units), dim3(SORT_THREADS), sort_lds, st, sa, ix.assign,
+      WAVE_TRY(launch("k_sort", k_sort, dim3((unsigned)units), dim3(SORT_THREADS), sort_lds, st, bs, ix.assign,
                       ws.rank, ix.sizes, ix.offsets, ix.perm));
-    WAVE_TRY(launch("k_update", it + 1 < iters ? k_update<false> : k_update<true>, dim3(cgrid), dim3(256), 0, st, sa,
+    WAVE_TRY(launch("k_update", it + 1 < iters ? k_update<false> : k_update<true>, dim3(cgrid), dim3(256), 0, st, bs,
                     nclu, K, V, ix, ws.norm));
   }
   return hipSuccess;
 }
 
+hipError_t launch_build(const SeqArgs& sa, const void* Kv, const void* Vv, int32_t iters, uint64_t seed,
+                        const wave_index& ix, const BuildWs& ws, int32_t* trace, int64_t rows, hipStream_t st) {
+  return run_build(whole(sa), reinterpret_cast<const uint16_t*>(Kv), reinterpret_cast<const uint16_t*>(Vv), iters,
+                   seed, ix, ws, trace, rows, st);
+}
+
+hipError_t launch_append(const SeqArgs& sa, const int32_t* n_old, const void* Kn, const void* Vn, int32_t iters,
+                         uint64_t seed, const wave_index& ix, const BuildWs& ws, void* stage_k, void* stage_v,
+                         hipStream_t st) {
+  BuildSeq bs = whole(sa);
+  StageArgs a;
+  a.B = sa.B;
+  a.G = sa.G;
+  a.seg_len = sa.seg_len;
+  a.cap = sa.cap;
+  int64_t Mmax = 0;
+  for (int b = 0; b < MAXB; ++b) {
+    a.n_new[b] = b < sa.B ? sa.N[b] : 0;
+    a.n_old[b] = b < sa.B ? n_old[b] : 0;
+  }
+  for (int b = 0; b < sa.B; ++b) {
+    if (sa.N[b] > n_old[b]) {
+      bs.first[b] = n_old[b] / sa.seg_len;
+      Mmax = std::max<int64_t>(Mmax, sa.N[b] - (int64_t)bs.first[b] * sa.seg_len);
+    } else {
+      bs.first[b] = (int32_t)host_nseg(bs, b);  // unchanged: no units
+    }
+  }
+  if (Mmax == 0) return hipSuccess;
+  uint16_t* Ko = reinterpret_cast<uint16_t*>(stage_k);
+  uint16_t* Vo = reinterpret_cast<uint16_t*>(stage_v);
+  WAVE_TRY(launch("k_stage", k_stage, dim3((unsigned)(sa.B * sa.G), (unsigned)((Mmax + STAGE_ROWS - 1) / STAGE_ROWS)),
+                  dim3(STAGE_ROWS * 16), 0, st, a, reinterpret_cast<const uint16_t*>(Kn),
+                  reinterpret_cast<const uint16_t*>(Vn), ix, Ko, Vo));
+  return run_build(bs, Ko, Vo, iters, seed, ix, ws, nullptr, 0, st);
+}
+
 hipError_t launch_build_blocks(const SeqArgs& sa, const void* Kv, const void* Vv, const wave_index& ix,
-                               const BuildWs& ws, int64_t units, hipStream_t st) {
+                               const BuildWs& ws, hipStream_t st) {
   const DeviceInfo& di = device_info();
   WAVE_TRY(di.status);
+  const BuildSeq bs = whole(sa);
   const uint16_t* K = reinterpret_cast<const uint16_t*>(Kv);
   const uint16_t* V = reinterpret_cast<const uint16_t*>(Vv);
-  int64_t nclu = 0;
-  for (int b = 0; b < sa.B; ++b) nclu += (int64_t)sa.G * sa.C[b];
+  int64_t units, nclu;
+  call_counts(bs, &units, &nclu);
   const size_t sort_lds = 16 * (size_t)sa.K_s * 4;
   const int sparts = sort_parts(units, di.cus);
   const size_t radix_tiles = ((size_t)(sa.seg_len + sparts - 1) / sparts + RS_THREADS - 1) / RS_THREADS;
   const size_t radix_lds = 2 * radix_tiles * RS_THREADS * 4;
   const unsigned cgrid = (unsigned)((nclu + 3) / 4);
-  WAVE_TRY(launch("k_block_assign", k_block_assign, dim3((unsigned)units), dim3(1024), 0, st, sa, ix.assign));
+  WAVE_TRY(launch("k_block_assign", k_block_assign, dim3((unsigned)units), dim3(1024), 0, st, bs, ix.assign));
   // the layout pass of the k-means build over the block labels: counts, offsets, the
   // (identity) order, member means, bf16 centroids, value sums
   if (sa.seg_len <= RS_MAXL)
-    WAVE_TRY(launch("k_sort", k_sort_radix, dim3((unsigned)(units * sparts)), dim3(RS_THREADS), radix_lds, st, sa,
+    WAVE_TRY(launch("k_sort", k_sort_radix, dim3((unsigned)(units * sparts)), dim3(RS_THREADS), radix_lds, st, bs,
                     sparts, ix.assign, ix.sizes, ix.offsets, ix.perm));
   else
-    WAVE_TRY(launch("k_sort", k_sort, dim3((unsigned)units), dim3(SORT_THREADS), sort_lds, st, sa, ix.assign,
+    WAVE_TRY(launch("k_sort", k_sort, dim3((unsigned)units), dim3(SORT_THREADS), sort_lds, st, bs, ix.assign,
                     ws.rank, ix.sizes, ix.offsets, ix.perm));
-  WAVE_TRY(launch("k_update", k_update<true>, dim3(cgrid), dim3(256), 0, st, sa, nclu, K, V, ix, ws.norm));
+  WAVE_TRY(launch("k_update", k_update<true>, dim3(cgrid), dim3(256), 0, st, bs, nclu, K, V, ix, ws.norm));
   return hipSuccess;
 }
 

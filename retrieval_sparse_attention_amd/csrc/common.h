@@ -12,30 +12,41 @@ constexpr int D = WAVE_HEAD_DIM;  // 128
 constexpr int MAXB = WAVE_MAX_BATCH;
 
 // Per-call description of the ragged batch, passed to kernels by value.
-// N[b]: tokens of sequence b; C[b]: its clusters per kv head.
+// N[b]: tokens of sequence b; C[b]: its clusters per kv head. cap: 0 for the dense
+// ragged layout of the index arrays (block (b, g) holds N_b rows and C_b clusters),
+// else the capacity of every block in segments (cap * seg_len rows, cap * K_s
+// clusters, of which the first N_b and C_b are filled).
 struct SeqArgs {
   int32_t B, G, seg_len, K_s;
+  int32_t cap, pad_;
   int32_t N[MAXB];
   int32_t C[MAXB];
 };
 
-// Bases of sequence b in the ragged arrays (all per-sequence blocks are G-fold).
+// Bases of sequence b (all per-sequence blocks are G-fold).
 struct SeqBase {
-  int64_t row;   // first row: G * sum_{b'<b} N_b'
-  int64_t clu;   // first cluster: G * sum C_b'
-  int64_t off;   // first offsets entry: G * sum (C_b' + 1)
+  int64_t row;   // index: first row, G * sum_{b'<b} NS_b'
+  int64_t clu;   // index: first cluster, G * sum CS_b'
+  int64_t off;   // index: first offsets entry, G * sum (CS_b' + 1)
+  int64_t wclu;  // G * sum_{b'<b} C_b': first cluster in the dense per-call workspaces
   int32_t N, C;
+  int32_t NS, CS;  // rows and clusters of one block (kv head) of sequence b in the index arrays
 };
 
 __host__ __device__ inline SeqBase seq_base(const SeqArgs& s, int b) {
-  SeqBase r{0, 0, 0, 0, 0};
+  SeqBase r{0, 0, 0, 0, 0, 0, 0, 0};
   for (int i = 0; i < b; ++i) {
-    r.row += (int64_t)s.G * s.N[i];
-    r.clu += (int64_t)s.G * s.C[i];
-    r.off += (int64_t)s.G * (s.C[i] + 1);
+    const int64_t R = s.cap ? (int64_t)s.cap * s.seg_len : s.N[i];
+    const int64_t Cs = s.cap ? (int64_t)s.cap * s.K_s : s.C[i];
+    r.row += (int64_t)s.G * R;
+    r.clu += (int64_t)s.G * Cs;
+    r.off += (int64_t)s.G * (Cs + 1);
+    r.wclu += (int64_t)s.G * s.C[i];
   }
   r.N = s.N[b];
   r.C = s.C[b];
+  r.NS = s.cap ? s.cap * s.seg_len : s.N[b];
+  r.CS = s.cap ? s.cap * s.K_s : s.C[b];
   return r;
 }
 

@@ -117,7 +117,7 @@ __global__ __launch_bounds__(SCORE_THREADS) void k_score(SeqArgs sa, DecodeArgs 
   const int nch = (C + SC - 1) / SC;
   const int g = w / nch, chunk = w % nch;
   const int j0 = chunk * SC, nc = min(SC, C - j0);
-  const int64_t clu0 = sb.clu + (int64_t)g * C, row0 = sb.row + (int64_t)g * N;
+  const int64_t clu0 = sb.clu + (int64_t)g * sb.CS, row0 = sb.row + (int64_t)g * sb.NS;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, l16 = lane & 15, grp = lane >> 4;
   const int gi = wv * 4 + grp;
 
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(SCORE_THREADS) void k_score(SeqArgs sa, DecodeArgs 
     for (int hh = 1; hh < GS; ++hh) s = s + S.kw[hh][jj];
     return s + 0.0f;
   };
-  const int64_t kb = (int64_t)GS * sb.clu + (int64_t)g * GS * C + j0;
+  const int64_t kb = (int64_t)GS * sb.wclu + (int64_t)g * GS * C + j0;
   for (int e = tid; e < GS * SC; e += SCORE_THREADS) {
     const int hh = e / SC, jj = e % SC;
     if (jj < nc) {
@@ -283,7 +283,7 @@ __device__ void est_role(const SeqArgs& sa, const DecodeArgs& da, const wave_ind
   const int nch = (C + SC - 1) / SC;
   const int g = w / nch, chunk = w % nch;
   const int j0 = chunk * SC, nc = min(SC, C - j0);
-  const int64_t clu0 = sb.clu + (int64_t)g * C;
+  const int64_t clu0 = sb.clu + (int64_t)g * sb.CS;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int sub = tid >> 5, dq = tid & 31;
   const float sc = da.tau * LOG2E;
@@ -291,7 +291,7 @@ __device__ void est_role(const SeqArgs& sa, const DecodeArgs& da, const wave_ind
   const int jj = tid;
   const int jc = min(jj, nc - 1);
   const int n0 = ix.sizes[clu0 + j0 + jc];
-  const float* kb = ws.keys + (int64_t)GS * sb.clu + (int64_t)g * GS * C + j0;
+  const float* kb = ws.keys + (int64_t)GS * sb.wclu + (int64_t)g * GS * C + j0;
   float kr[GS];
 #pragma unroll
   for (int hh = 0; hh < GS; ++hh) kr[hh] = kb[(int64_t)hh * C + jc];
@@ -649,16 +649,16 @@ __global__ __launch_bounds__(TK_THREADS, PF ? 1 : 2 * TK_WAVES / 4) void k_topk(
   const int b = bh / da.H, h = bh % da.H, g = h / da.GS;
   const SeqBase sb = seq_base(sa, b);
   const int N = sb.N, C = sb.C;
-  const int64_t row0 = sb.row + (int64_t)g * N;
-  const int64_t clu0 = sb.clu + (int64_t)g * C;
-  const int64_t off0 = sb.off + (int64_t)g * (C + 1);
-  const int64_t kbase = (int64_t)da.GS * sb.clu + (int64_t)h * C;
+  const int64_t row0 = sb.row + (int64_t)g * sb.NS;
+  const int64_t clu0 = sb.clu + (int64_t)g * sb.CS;
+  const int64_t off0 = sb.off + (int64_t)g * (sb.CS + 1);
+  const int64_t kbase = (int64_t)da.GS * sb.wclu + (int64_t)h * C;
   // sortable keys of the selection: the head's own, or its kv head's group keys (first q head's slot)
   const int hs = da.shared ? g * da.GS : h;
   const int64_t bhs = (int64_t)b * da.H + hs;
   const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wv = tid >> 6;
   const uint64_t ltmask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const uint32_t* key32 = ws.key32 + (int64_t)da.GS * sb.clu + (int64_t)hs * C;
+  const uint32_t* key32 = ws.key32 + (int64_t)da.GS * sb.wclu + (int64_t)hs * C;
   const float* keys = ws.keys + kbase;
   int2* span = ws.span + kbase;
   float* skey = ws.skey + kbase;
@@ -1312,8 +1312,8 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
   const int b = bh / da.H, h = bh % da.H, g = h / da.GS;
   const SeqBase sb = seq_base(sa, b);
   const int N = sb.N;
-  const int64_t row0 = sb.row + (int64_t)g * N;
-  const int64_t kbase = (int64_t)da.GS * sb.clu + (int64_t)h * sb.C;
+  const int64_t row0 = sb.row + (int64_t)g * sb.NS;
+  const int64_t kbase = (int64_t)da.GS * sb.wclu + (int64_t)h * sb.C;
   const int M = ws.counts[4 * bh + 0], k = ws.counts[4 * bh + 1], nS = ws.counts[4 * bh + 2];
   const int T = M + nS;
   const Steady sz = steady_of(da, N);

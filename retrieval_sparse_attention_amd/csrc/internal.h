@@ -80,16 +80,20 @@ hipError_t launch_decode(const SeqArgs& sa, const DecodeArgs& da, const wave_ind
 
 // ------------------------------------------------------------------ build
 struct BuildWs {
-  float* norm;        // [clusters] |chat_j|^2 (fp32) of the current round
-  int32_t* rank;      // [rows] scratch of the counting sort
-  float* xn2;         // [rows] |x|^2 of every key (written by the first k_assign round)
+  float* norm;        // [index clusters] |chat_j|^2 (fp32) of the current round
+  int32_t* rank;      // [input rows] scratch of the counting sort
+  float* xn2;         // [input rows] |x|^2 of every key (written by the first k_assign round)
 };
 
 hipError_t launch_build(const SeqArgs& sa, const void* K, const void* V, int32_t iters, uint64_t seed,
-                        const wave_index& ix, const BuildWs& ws, int64_t units, int32_t* trace, int64_t rows,
-                        hipStream_t st);
+                        const wave_index& ix, const BuildWs& ws, int32_t* trace, int64_t rows, hipStream_t st);
 hipError_t launch_build_blocks(const SeqArgs& sa, const void* K, const void* V, const wave_index& ix,
-                               const BuildWs& ws, int64_t units, hipStream_t st);
+                               const BuildWs& ws, hipStream_t st);
+// sa: the longer context (sa.cap > 0); n_old: host [B], the context the index holds.
+// stage_k, stage_v: workspace of [append input rows][128] bf16 each.
+hipError_t launch_append(const SeqArgs& sa, const int32_t* n_old, const void* Kn, const void* Vn, int32_t iters,
+                         uint64_t seed, const wave_index& ix, const BuildWs& ws, void* stage_k, void* stage_v,
+                         hipStream_t st);
 
 // ------------------------------------------------------------------ per-device set-up
 // Done once per device (std::call_once), on the first call that launches work there:

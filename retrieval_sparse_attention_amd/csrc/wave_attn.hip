@@ -59,13 +59,27 @@ wave_status check_seg(int32_t seg_len, int32_t K_s) {
   return WAVE_OK;
 }
 
-wave::SeqArgs make_seq(const wave_shape* s, int32_t seg_len, int32_t K_s) {
+// capacity of cap segments per block (0: dense) for the contexts of s
+wave_status check_cap(const wave_shape* s, int32_t seg_len, int32_t cap) {
+  if (cap < 0) return fail(WAVE_ERR_ARG, "cap_segs %d < 0", cap);
+  if (cap == 0) return WAVE_OK;
+  if ((int64_t)cap * seg_len >= ((int64_t)1 << 31))
+    return fail(WAVE_ERR_UNSUPPORTED, "cap_segs * seg_len = %lld >= 2^31", (long long)cap * seg_len);
+  for (int b = 0; b < s->batch; ++b)
+    if (s->ctx[b] > (int64_t)cap * seg_len)
+      return fail(WAVE_ERR_SHAPE, "ctx[%d] = %lld exceeds the capacity of %lld tokens", b, (long long)s->ctx[b],
+                  (long long)cap * seg_len);
+  return WAVE_OK;
+}
+
+wave::SeqArgs make_seq(const wave_shape* s, int32_t seg_len, int32_t K_s, int32_t cap = 0) {
   wave::SeqArgs sa;
   memset(&sa, 0, sizeof(sa));
   sa.B = s->batch;
   sa.G = s->n_kv_heads;
   sa.seg_len = seg_len;
   sa.K_s = K_s;
+  sa.cap = cap;
   for (int b = 0; b < s->batch; ++b) {
     sa.N[b] = (int32_t)s->ctx[b];
     sa.C[b] = (int32_t)wave::num_clusters(s->ctx[b], seg_len, K_s);
@@ -75,25 +89,36 @@ wave::SeqArgs make_seq(const wave_shape* s, int32_t seg_len, int32_t K_s) {
 
 void index_sizes(const wave::SeqArgs& sa, wave_index_sizes* o) {
   memset(o, 0, sizeof(*o));
+  o->cap_segs = sa.cap;
   for (int b = 0; b < sa.B; ++b) {
-    o->rows += (int64_t)sa.G * sa.N[b];
-    o->clusters += (int64_t)sa.G * sa.C[b];
-    o->offsets_len += (int64_t)sa.G * (sa.C[b] + 1);
+    const int64_t R = sa.cap ? (int64_t)sa.cap * sa.seg_len : sa.N[b];
+    const int64_t Cs = sa.cap ? (int64_t)sa.cap * sa.K_s : sa.C[b];
+    o->rows += (int64_t)sa.G * R;
+    o->clusters += (int64_t)sa.G * Cs;
+    o->offsets_len += (int64_t)sa.G * (Cs + 1);
+    o->kv_rows += (int64_t)sa.G * sa.N[b];
     o->units += (int64_t)sa.G * ((sa.N[b] + sa.seg_len - 1) / sa.seg_len);
     if (sa.C[b] > o->max_clusters) o->max_clusters = sa.C[b];
   }
 }
 
+// Build and append workspaces: the norms per index cluster; per input row the sort's
+// ranks and the keys' squared norms; an append also stages its input rows (K and V).
 struct BuildLayout {
-  size_t norm, rank, xn2, total;
+  size_t norm, rank, xn2, stage_k, stage_v, total;
 };
 
-BuildLayout build_layout(const wave_index_sizes& z) {
+BuildLayout build_layout(int64_t clusters, int64_t in_rows, bool stage) {
   BuildLayout L;
   size_t o = 0;
-  L.norm = o;  o += align256(sizeof(float) * (size_t)z.clusters);
-  L.rank = o;  o += align256(sizeof(int32_t) * (size_t)z.rows);
-  L.xn2 = o;   o += align256(sizeof(float) * (size_t)z.rows);
+  L.norm = o;  o += align256(sizeof(float) * (size_t)clusters);
+  L.rank = o;  o += align256(sizeof(int32_t) * (size_t)in_rows);
+  L.xn2 = o;   o += align256(sizeof(float) * (size_t)in_rows);
+  L.stage_k = L.stage_v = o;
+  if (stage) {
+    L.stage_k = o;  o += align256(2 * (size_t)WAVE_HEAD_DIM * (size_t)in_rows);
+    L.stage_v = o;  o += align256(2 * (size_t)WAVE_HEAD_DIM * (size_t)in_rows);
+  }
   L.total = o;
   return L;
 }
@@ -123,7 +148,9 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
   if (H / G > WAVE_MAX_GROUP) return fail(WAVE_ERR_UNSUPPORTED, "%d q heads per kv head > %d", H / G, WAVE_MAX_GROUP);
   if (n_sink < 0 || n_local < 0) return fail(WAVE_ERR_ARG, "n_sink %d / n_local %d negative", n_sink, n_local);
   if (!(frac >= 0.0 && frac <= 1.0)) return fail(WAVE_ERR_ARG, "topk_frac %g outside [0, 1]", frac);
-  const wave::SeqArgs sa = make_seq(&ix->shape, ix->seg_len, ix->clusters_per_seg);
+  st = check_cap(&ix->shape, ix->seg_len, ix->cap_segs);
+  if (st != WAVE_OK) return st;
+  const wave::SeqArgs sa = make_seq(&ix->shape, ix->seg_len, ix->clusters_per_seg, ix->cap_segs);
   wave::DecodeArgs& da = P->da;
   memset(&da, 0, sizeof(da));
   da.H = H;
@@ -280,68 +307,38 @@ extern "C" {
 
 const char* wave_last_error(void) { return g_err; }
 
-wave_status wave_index_plan(const wave_shape* shape, int32_t seg_len, int32_t clusters_per_seg,
-                            wave_index_sizes* out) {
+wave_status wave_index_plan_cap(const wave_shape* shape, int32_t seg_len, int32_t clusters_per_seg, int32_t cap_segs,
+                                wave_index_sizes* out) {
   wave_status st = check_shape(shape);
   if (st != WAVE_OK) return st;
   st = check_seg(seg_len, clusters_per_seg);
+  if (st != WAVE_OK) return st;
+  st = check_cap(shape, seg_len, cap_segs);
   if (st != WAVE_OK) return st;
   if (out == nullptr) return fail(WAVE_ERR_ARG, "out is NULL");
-  const wave::SeqArgs sa = make_seq(shape, seg_len, clusters_per_seg);
+  const wave::SeqArgs sa = make_seq(shape, seg_len, clusters_per_seg, cap_segs);
   index_sizes(sa, out);
-  out->build_ws_bytes = build_layout(*out).total;
+  out->build_ws_bytes = build_layout(out->clusters, out->kv_rows, false).total;
   return ok();
 }
 
-wave_status wave_index_build(const wave_shape* shape, const void* K, const void* V, int32_t seg_len,
-                             int32_t clusters_per_seg, int32_t iters, uint64_t seed, wave_index* out, void* ws,
-                             size_t ws_bytes, int32_t* assign_trace, wave_stream_t stream) {
-  wave_status st = check_shape(shape);
-  if (st != WAVE_OK) return st;
-  st = check_seg(seg_len, clusters_per_seg);
-  if (st != WAVE_OK) return st;
-  if (iters < 1) return fail(WAVE_ERR_SHAPE, "iters %d < 1", iters);
-  if (K == nullptr || V == nullptr || out == nullptr || ws == nullptr)
-    return fail(WAVE_ERR_ARG, "K, V, out and ws must be non-NULL");
-  const void* ptrs[] = {out->k_sorted, out->v_sorted, out->perm, out->inv_perm, out->assign, out->offsets,
-                        out->sizes, out->centroids, out->centroids_bf16, out->vsum};
-  for (const void* p : ptrs)
-    if (p == nullptr) return fail(WAVE_ERR_ARG, "an index array pointer is NULL");
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return fail(WAVE_ERR_ALIGN, "index arrays must be 16-byte aligned");
-  if (!aligned16(K) || !aligned16(V) || !aligned16(ws) || (assign_trace && !aligned16(assign_trace)))
-    return fail(WAVE_ERR_ALIGN, "K, V, ws and assign_trace must be 16-byte aligned");
-  wave_index_sizes z;
-  const wave::SeqArgs sa = make_seq(shape, seg_len, clusters_per_seg);
-  index_sizes(sa, &z);
-  const BuildLayout L = build_layout(z);
-  if (ws_bytes < L.total)
-    return fail(WAVE_ERR_WORKSPACE, "build workspace %zu bytes < %zu", ws_bytes, L.total);
-  st = hip_device_ok();
-  if (st != WAVE_OK) return st;
-  out->shape = *shape;
-  out->seg_len = seg_len;
-  out->clusters_per_seg = clusters_per_seg;
-  uint8_t* w = reinterpret_cast<uint8_t*>(ws);
-  wave::BuildWs bw;
-  bw.norm = reinterpret_cast<float*>(w + L.norm);
-  bw.rank = reinterpret_cast<int32_t*>(w + L.rank);
-  bw.xn2 = reinterpret_cast<float*>(w + L.xn2);
-  hipError_t e = wave::launch_build(sa, K, V, iters, seed, *out, bw, z.units, assign_trace, z.rows,
-                                    reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(WAVE_ERR_HIP, "build launch failed: %s", hipGetErrorString(e));
-  return ok();
+wave_status wave_index_plan(const wave_shape* shape, int32_t seg_len, int32_t clusters_per_seg,
+                            wave_index_sizes* out) {
+  return wave_index_plan_cap(shape, seg_len, clusters_per_seg, 0, out);
 }
 
-wave_status wave_index_build_blocks(const wave_shape* shape, const void* K, const void* V, int32_t seg_len,
-                                    int32_t clusters_per_seg, wave_index* out, void* ws, size_t ws_bytes,
-                                    wave_stream_t stream) {
+// checks shared by the builds; on success *sa, *z and *L describe the call
+static wave_status build_checks(const wave_shape* shape, const void* K, const void* V, int32_t seg_len,
+                                int32_t clusters_per_seg, const wave_index* out, const void* ws, size_t ws_bytes,
+                                wave::SeqArgs* sa, wave_index_sizes* z, BuildLayout* L) {
   wave_status st = check_shape(shape);
   if (st != WAVE_OK) return st;
   st = check_seg(seg_len, clusters_per_seg);
   if (st != WAVE_OK) return st;
   if (K == nullptr || V == nullptr || out == nullptr || ws == nullptr)
     return fail(WAVE_ERR_ARG, "K, V, out and ws must be non-NULL");
+  st = check_cap(shape, seg_len, out->cap_segs);
+  if (st != WAVE_OK) return st;
   const void* ptrs[] = {out->k_sorted, out->v_sorted, out->perm, out->inv_perm, out->assign, out->offsets,
                         out->sizes, out->centroids, out->centroids_bf16, out->vsum};
   for (const void* p : ptrs)
@@ -350,24 +347,138 @@ wave_status wave_index_build_blocks(const wave_shape* shape, const void* K, cons
     if (!aligned16(p)) return fail(WAVE_ERR_ALIGN, "index arrays must be 16-byte aligned");
   if (!aligned16(K) || !aligned16(V) || !aligned16(ws))
     return fail(WAVE_ERR_ALIGN, "K, V and ws must be 16-byte aligned");
-  wave_index_sizes z;
-  const wave::SeqArgs sa = make_seq(shape, seg_len, clusters_per_seg);
-  index_sizes(sa, &z);
-  const BuildLayout L = build_layout(z);
-  if (ws_bytes < L.total)
-    return fail(WAVE_ERR_WORKSPACE, "build workspace %zu bytes < %zu", ws_bytes, L.total);
-  st = hip_device_ok();
-  if (st != WAVE_OK) return st;
-  out->shape = *shape;
-  out->seg_len = seg_len;
-  out->clusters_per_seg = clusters_per_seg;
+  *sa = make_seq(shape, seg_len, clusters_per_seg, out->cap_segs);
+  index_sizes(*sa, z);
+  *L = build_layout(z->clusters, z->kv_rows, false);
+  if (ws_bytes < L->total)
+    return fail(WAVE_ERR_WORKSPACE, "build workspace %zu bytes < %zu", ws_bytes, L->total);
+  return hip_device_ok();
+}
+
+static wave::BuildWs carve_build(void* ws, const BuildLayout& L) {
   uint8_t* w = reinterpret_cast<uint8_t*>(ws);
   wave::BuildWs bw;
   bw.norm = reinterpret_cast<float*>(w + L.norm);
   bw.rank = reinterpret_cast<int32_t*>(w + L.rank);
   bw.xn2 = reinterpret_cast<float*>(w + L.xn2);
-  hipError_t e = wave::launch_build_blocks(sa, K, V, *out, bw, z.units, reinterpret_cast<hipStream_t>(stream));
+  return bw;
+}
+
+wave_status wave_index_build(const wave_shape* shape, const void* K, const void* V, int32_t seg_len,
+                             int32_t clusters_per_seg, int32_t iters, uint64_t seed, wave_index* out, void* ws,
+                             size_t ws_bytes, int32_t* assign_trace, wave_stream_t stream) {
+  if (iters < 1) return fail(WAVE_ERR_SHAPE, "iters %d < 1", iters);
+  if (assign_trace && !aligned16(assign_trace)) return fail(WAVE_ERR_ALIGN, "assign_trace must be 16-byte aligned");
+  wave::SeqArgs sa;
+  wave_index_sizes z;
+  BuildLayout L;
+  wave_status st = build_checks(shape, K, V, seg_len, clusters_per_seg, out, ws, ws_bytes, &sa, &z, &L);
+  if (st != WAVE_OK) return st;
+  out->shape = *shape;
+  out->seg_len = seg_len;
+  out->clusters_per_seg = clusters_per_seg;
+  hipError_t e = wave::launch_build(sa, K, V, iters, seed, *out, carve_build(ws, L), assign_trace, z.rows,
+                                    reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(WAVE_ERR_HIP, "build launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+wave_status wave_index_build_blocks(const wave_shape* shape, const void* K, const void* V, int32_t seg_len,
+                                    int32_t clusters_per_seg, wave_index* out, void* ws, size_t ws_bytes,
+                                    wave_stream_t stream) {
+  wave::SeqArgs sa;
+  wave_index_sizes z;
+  BuildLayout L;
+  wave_status st = build_checks(shape, K, V, seg_len, clusters_per_seg, out, ws, ws_bytes, &sa, &z, &L);
+  if (st != WAVE_OK) return st;
+  out->shape = *shape;
+  out->seg_len = seg_len;
+  out->clusters_per_seg = clusters_per_seg;
+  hipError_t e = wave::launch_build_blocks(sa, K, V, *out, carve_build(ws, L), reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(WAVE_ERR_HIP, "block build launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// An append of `index` to new_ctx: the checks, the longer context's SeqArgs, the old
+// lengths and the workspace layout (input rows: the tokens from the first changed
+// segment to the new end, per appended block).
+static wave_status append_checks(const wave_index* ix, const int64_t* new_ctx, wave::SeqArgs* sa, int32_t* n_old,
+                                 int64_t* appended, BuildLayout* L) {
+  if (ix == nullptr || new_ctx == nullptr) return fail(WAVE_ERR_ARG, "index and new_ctx must be non-NULL");
+  wave_status st = check_shape(&ix->shape);
+  if (st != WAVE_OK) return st;
+  st = check_seg(ix->seg_len, ix->clusters_per_seg);
+  if (st != WAVE_OK) return st;
+  if (ix->cap_segs < 1) return fail(WAVE_ERR_ARG, "the index has no capacity (cap_segs = %d)", ix->cap_segs);
+  st = check_cap(&ix->shape, ix->seg_len, ix->cap_segs);
+  if (st != WAVE_OK) return st;
+  wave_shape ns = ix->shape;
+  ns.ctx = new_ctx;
+  st = check_shape(&ns);
+  if (st != WAVE_OK) return st;
+  const int64_t room = (int64_t)ix->cap_segs * ix->seg_len;
+  int64_t in_rows = 0;
+  *appended = 0;
+  for (int b = 0; b < ns.batch; ++b) {
+    const int64_t o = ix->shape.ctx[b], n = new_ctx[b];
+    if (n < o) return fail(WAVE_ERR_SHAPE, "new_ctx[%d] = %lld < ctx[%d] = %lld", b, (long long)n, b, (long long)o);
+    if (n > room)
+      return fail(WAVE_ERR_SHAPE, "new_ctx[%d] = %lld exceeds the capacity of %lld tokens", b, (long long)n,
+                  (long long)room);
+    n_old[b] = (int32_t)o;
+    if (n > o) {
+      in_rows += (int64_t)ns.n_kv_heads * (n - (o / ix->seg_len) * ix->seg_len);
+      *appended += (int64_t)ns.n_kv_heads * (n - o);
+    }
+  }
+  *sa = make_seq(&ns, ix->seg_len, ix->clusters_per_seg, ix->cap_segs);
+  wave_index_sizes z;
+  index_sizes(*sa, &z);
+  *L = build_layout(z.clusters, in_rows, true);
+  return WAVE_OK;
+}
+
+wave_status wave_index_append_plan(const wave_index* index, const int64_t* new_ctx, size_t* ws_bytes) {
+  if (ws_bytes == nullptr) return fail(WAVE_ERR_ARG, "ws_bytes is NULL");
+  wave::SeqArgs sa;
+  int32_t n_old[WAVE_MAX_BATCH];
+  int64_t appended;
+  BuildLayout L;
+  wave_status st = append_checks(index, new_ctx, &sa, n_old, &appended, &L);
+  if (st != WAVE_OK) return st;
+  *ws_bytes = L.total;
+  return ok();
+}
+
+wave_status wave_index_append(wave_index* index, const int64_t* new_ctx, const void* K_new, const void* V_new,
+                              int32_t iters, uint64_t seed, void* ws, size_t ws_bytes, wave_stream_t stream) {
+  if (iters < 1) return fail(WAVE_ERR_ARG, "iters %d < 1", iters);
+  wave::SeqArgs sa;
+  int32_t n_old[WAVE_MAX_BATCH];
+  int64_t appended;
+  BuildLayout L;
+  wave_status st = append_checks(index, new_ctx, &sa, n_old, &appended, &L);
+  if (st != WAVE_OK) return st;
+  const void* ptrs[] = {index->k_sorted, index->v_sorted, index->perm, index->inv_perm, index->assign,
+                        index->offsets, index->sizes, index->centroids, index->centroids_bf16, index->vsum};
+  for (const void* p : ptrs)
+    if (p == nullptr) return fail(WAVE_ERR_ARG, "an index array pointer is NULL");
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return fail(WAVE_ERR_ALIGN, "index arrays must be 16-byte aligned");
+  if (appended > 0) {
+    if (K_new == nullptr || V_new == nullptr || ws == nullptr)
+      return fail(WAVE_ERR_ARG, "K_new, V_new and ws must be non-NULL when tokens are appended");
+    if (!aligned16(K_new) || !aligned16(V_new) || !aligned16(ws))
+      return fail(WAVE_ERR_ALIGN, "K_new, V_new and ws must be 16-byte aligned");
+    if (ws_bytes < L.total) return fail(WAVE_ERR_WORKSPACE, "append workspace %zu bytes < %zu", ws_bytes, L.total);
+    st = hip_device_ok();
+    if (st != WAVE_OK) return st;
+    uint8_t* w = reinterpret_cast<uint8_t*>(ws);
+    hipError_t e = wave::launch_append(sa, n_old, K_new, V_new, iters, seed, *index, carve_build(ws, L),
+                                       w + L.stage_k, w + L.stage_v, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(WAVE_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
+  }
+  index->shape.ctx = new_ctx;
   return ok();
 }
 
@@ -409,7 +520,7 @@ static wave_status decode_call(const wave_index* index, const void* q, int32_t n
   if (ws_bytes < P.total) return fail(WAVE_ERR_WORKSPACE, "decode workspace %zu bytes < %zu", ws_bytes, P.total);
   st = hip_device_ok();
   if (st != WAVE_OK) return st;
-  const wave::SeqArgs sa = make_seq(&index->shape, index->seg_len, index->clusters_per_seg);
+  const wave::SeqArgs sa = make_seq(&index->shape, index->seg_len, index->clusters_per_seg, index->cap_segs);
   uint8_t* w = reinterpret_cast<uint8_t*>(ws);
   wave::DecodeWs dw;
   dw.keys = reinterpret_cast<float*>(w + P.keys);

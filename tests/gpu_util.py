@@ -43,3 +43,26 @@ def index_to_host(ix):
 
 def say(msg):
     print(msg, flush=True)
+
+
+def dense_from_capacity(h, G, ctx, seg_len, K_s, cap):
+    """Host arrays of a capacity index (every (b, g) block with room for `cap` segments) in
+    the dense ragged layout of the oracle: each block's filled rows, clusters and offsets."""
+    from oracle import Index, num_clusters
+    R, Cs = cap * seg_len, cap * K_s
+    rows, clus, offs = [], [], []
+    for b, N in enumerate(ctx):
+        N = int(N)
+        C = num_clusters(N, seg_len, K_s)
+        for g in range(G):
+            blk = b * G + g
+            rows.append((blk * R, blk * R + N))
+            clus.append((blk * Cs, blk * Cs + C))
+            offs.append((blk * (Cs + 1), blk * (Cs + 1) + C + 1))
+    out = {}
+    for f in Index.FIELDS:
+        a = h[f]
+        sel = rows if f in ("k_sorted", "v_sorted", "perm", "inv_perm", "assign") else (
+            offs if f == "offsets" else clus)
+        out[f] = np.concatenate([a[i:j] for i, j in sel])
+    return out

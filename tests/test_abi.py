@@ -216,3 +216,105 @@ def test_calls_fail_cleanly_without_device():
     bad = list(dargs)
     bad[2] = 7  # not a multiple of the 2 kv heads
     assert L.wave_attn_decode_shared(*bad) == SHAPE
+
+
+def _plan_cap(G, ctx, L, K, cap):
+    sh, keep = _shape(G, ctx)
+    z = rsa._Sizes()
+    return rsa.lib().wave_index_plan_cap(ctypes.byref(sh), L, K, cap, ctypes.byref(z)), z
+
+
+def test_capacity_plan_sizes():
+    # every (b, g) block holds cap segments of room; the build reads the dense K and V
+    for G, ctx, L, K, cap in [(8, [131072], 8192, 512, 17), (3, [70000, 16389, 1], 8192, 512, 9), (2, [5], 4, 3, 2)]:
+        st, z = _plan_cap(G, ctx, L, K, cap)
+        assert st == OK
+        B = len(ctx)
+        assert z.rows == B * G * cap * L
+        assert z.clusters == B * G * cap * K
+        assert z.offsets_len == B * G * (cap * K + 1)
+        assert z.kv_rows == G * sum(ctx)
+        assert z.cap_segs == cap
+        assert z.units == G * sum(-(-n // L) for n in ctx)
+        assert z.build_ws_bytes >= 4 * z.clusters + 8 * z.kv_rows
+        st0, z0 = _plan_cap(G, ctx, L, K, 0)  # cap 0: the dense plan
+        st1, z1 = _plan(G, ctx, L, K)
+        assert st0 == st1 == OK and (z0.rows, z0.clusters, z0.kv_rows) == (z1.rows, z1.clusters, z1.rows)
+
+
+@pytest.mark.parametrize("cap,status", [(-1, ARG), (1, SHAPE), (1 << 20, UNSUP)])
+def test_capacity_plan_rejects(cap, status):
+    st, _ = _plan_cap(2, [3000], 2048, 64, cap)
+    assert st == status
+
+
+def _append_plan(ix, new_ctx):
+    arr = (ctypes.c_int64 * len(new_ctx))(*new_ctx)
+    n = ctypes.c_size_t()
+    return rsa.lib().wave_index_append_plan(ctypes.byref(ix), arr, ctypes.byref(n)), n.value
+
+
+def test_append_plan_sizes_and_rejects():
+    ix, keep = _fake_index(2, [2500, 1024], 1024, 64)
+    assert _append_plan(ix, [2600, 1024])[0] == ARG  # a dense index cannot grow
+    ix.cap_segs = 4
+    st, w = _append_plan(ix, [3000, 2100])
+    assert st == OK
+    # input rows: b0 from token 2048 (segment 2 held the old end), b1 from 1024, both kv heads
+    rows = 2 * (3000 - 2048) + 2 * (2100 - 1024)
+    assert w >= 4 * 2 * 2 * 4 * 64 + 8 * rows + 2 * 2 * 128 * rows
+    assert _append_plan(ix, [2400, 1024])[0] == SHAPE   # shorter
+    assert _append_plan(ix, [4097, 1024])[0] == SHAPE   # beyond 4 segments of 1024
+    st, w0 = _append_plan(ix, [2500, 1024])              # nothing appended
+    assert st == OK
+
+
+def test_append_fails_cleanly_without_device():
+    if os.path.exists("/dev/kfd"):
+        pytest.skip("a GPU is present")
+    L = rsa.lib()
+    ix, keep = _fake_index(2, [2500], 1024, 64)
+    ix.cap_segs = 4
+    new = (ctypes.c_int64 * 1)(3000)
+    st, w = _append_plan(ix, [3000])
+    args = [ctypes.byref(ix), new, ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), 2, ctypes.c_uint64(1),
+            ctypes.c_void_p(0x3000), w, None]
+    assert L.wave_index_append(*args) == HIP
+    assert ix.shape.ctx[0] == 2500  # unchanged on an error
+    bad = list(args)
+    bad[2] = None
+    assert L.wave_index_append(*bad) == ARG
+    bad = list(args)
+    bad[3] = ctypes.c_void_p(0x2008)
+    assert L.wave_index_append(*bad) == ALIGN
+    bad = list(args)
+    bad[7] = w - 1
+    assert L.wave_index_append(*bad) == WS
+    bad = list(args)
+    bad[4] = 0
+    assert L.wave_index_append(*bad) == ARG
+    # nothing appended: no device work, the index takes the new (equal) contexts
+    same = (ctypes.c_int64 * 1)(2500)
+    assert L.wave_index_append(ctypes.byref(ix), same, None, None, 2, ctypes.c_uint64(1), None, 0, None) == OK
+    assert ctypes.addressof(ix.shape.ctx.contents) == ctypes.addressof(same)
+
+
+def test_struct_layout_matches_the_header(tmp_path):
+    # the binding's ctypes mirrors have the C structs' sizes and field offsets
+    src = tmp_path / "layout.c"
+    fields = {"wave_shape": rsa._Shape, "wave_index_sizes": rsa._Sizes, "wave_index": rsa._Index}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "wave_attn.h"', "int main(void) {"]
+    for cname, py in fields.items():
+        lines.append('printf("%s %%zu\\n", sizeof(%s));' % (cname, cname))
+        for f, _ in py._fields_:
+            lines.append('printf("%s.%s %%zu\\n", offsetof(%s, %s));' % (cname, f, cname, f))
+    lines.append("return 0; }")
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.check_call(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = dict(l.split() for l in subprocess.check_output([str(exe)]).decode().split("\n") if l)
+    for cname, py in fields.items():
+        assert int(got[cname]) == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert int(got["%s.%s" % (cname, f)]) == getattr(py, f).offset, (cname, f)

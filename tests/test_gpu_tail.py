@@ -84,24 +84,29 @@ def test_tail_128k():
 
 def test_decode_loop_with_growing_context():
     # A decode loop on the GPU: tokens join the tail after the index; when the tail holds
-    # a full segment the index is rebuilt over the longer context (segments are clustered
-    # independently) and the tail starts again. Every step checked against the oracle.
+    # a full segment, that segment is appended to the index in place (wave_index_append:
+    # segments are clustered independently) and the tail starts again. Every step is
+    # checked against the oracle's decode over its build of the indexed prefix.
     import retrieval_sparse_attention_amd as rsa
     from gpu_util import say, to_dev_bf16
     G, H, seg, K_s, iters, seed = 2, 8, 1024, 64, 3, 99
-    N0, cap, total = 2048, 1024, 2048 + 1024 + 300
+    N0, cap, total = 2048, 1024, 2048 + 2 * 1024 + 300
     Kf, Vf, _ = synth.kv(81, 1, G, np.array([total], np.int64), seg)
     q, _ = synth.queries(82, 1, 1, H, G, np.array([total], np.int64), Kf)
+
+    def rows_of(lo, hi):
+        return np.concatenate([np.arange(g * total + lo, g * total + hi) for g in range(G)])
+
+    ixd = rsa.wave_index_build(to_dev_bf16(Kf[rows_of(0, N0)]), to_dev_bf16(Vf[rows_of(0, N0)]), G, [N0], seg, K_s,
+                               iters, seed, cap_segs=total // seg + 1)
     n_idx = N0
-    for n_now in (N0, N0 + 1, N0 + 517, N0 + cap, N0 + cap + 1, N0 + cap + 300):
-        if n_now - n_idx >= cap:  # a full segment waits: fold it into the index
+    for n_now in (N0, N0 + 1, N0 + 517, N0 + cap, N0 + cap + 1, N0 + 2 * cap, N0 + 2 * cap + 300):
+        if n_now - n_idx >= cap:  # a full segment waits: append it to the index
+            r = rows_of(n_idx, n_idx + cap)
+            rsa.wave_index_append(ixd, to_dev_bf16(Kf[r]), to_dev_bf16(Vf[r]), [n_idx + cap], iters, seed)
             n_idx += cap
         say("growing context: %d tokens, %d indexed" % (n_now, n_idx))
-        rows = np.concatenate([np.arange(g * total, g * total + n_now) for g in range(G)])
-        Kn, Vn = Kf[rows], Vf[rows]
+        Kn, Vn = Kf[rows_of(0, n_now)], Vf[rows_of(0, n_now)]
         Ki, Vi, ctx, Kt, Vt = _split_tail(Kn, Vn, np.array([n_now], np.int64), (n_now - n_idx,), G, cap)
-        Kd = torch.from_numpy(Ki.view(np.int16)).cuda().view(torch.bfloat16)
-        Vd = torch.from_numpy(Vi.view(np.int16)).cuda().view(torch.bfloat16)
-        ixd = rsa.wave_index_build(Kd, Vd, G, [n_idx], seg, K_s, iters, seed)
         idx = oracle.build(Ki, Vi, G, ctx, seg, K_s, iters, seed)
         _compare(idx, Ki, Vi, q[0], ixd, 4, 64, 0.05, Kt, Vt, (n_now - n_idx,), "growing %d" % n_now)
