@@ -375,9 +375,74 @@ def main():
             extra[name] = workload_summary(r)
         result["workloads"] = extra
         torch.cuda.empty_cache()
+        result["append"] = measure_append(W, dev)
+        torch.cuda.empty_cache()
     if headline and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(W, K, V, ctx, q, args.cpu_seconds)
     print(json.dumps(result))
+
+
+def measure_append(W, dev, reps=10):
+    """In-place growth of the 128K layer's index (wave_index_append) against a rebuild over
+    the longer context: one appended segment of seg_len tokens per kv head, and one token
+    appended into a half-full last segment (which re-clusters that whole segment)."""
+    import numpy as np
+    import torch
+
+    import retrieval_sparse_attention_amd as rsa
+    import synth
+    G, seg, K_s, iters, seed = W["kv_heads"], W["seg_len"], W["clusters_per_seg"], W["kmeans_iters"], W["seed_build"]
+    N0 = W["ctx"]
+    N1 = N0 + seg
+    cap = N1 // seg + 1
+    K, V, _ = synth.kv(W["seed_data"], 1, G, np.array([N1 + seg], np.int64), seg)
+    Nf = N1 + seg
+
+    def rows(lo, hi):
+        return np.concatenate([np.arange(g * Nf + lo, g * Nf + hi) for g in range(G)])
+
+    def dev_rows(lo, hi):
+        r = rows(lo, hi)
+        return (torch.from_numpy(K[r].view(np.int16)).to(dev).view(torch.bfloat16),
+                torch.from_numpy(V[r].view(np.int16)).to(dev).view(torch.bfloat16))
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn, before=None):
+        ts = []
+        for _ in range(reps):
+            if before:
+                before()
+            torch.cuda.synchronize()
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]))
+        return float(np.median(ts))
+
+    K0, V0 = dev_rows(0, N0)
+    ix = rsa.wave_index_build(K0, V0, G, [N0], seg, K_s, iters, seed, cap_segs=cap)
+    kn, vn = dev_rows(N0, N1)
+    ws = torch.empty(rsa.wave_index_append_plan(ix, [N1]), dtype=torch.uint8, device=dev)
+    t_seg = timed(lambda: rsa.wave_index_append(ix, kn, vn, [N1], iters, seed, ws=ws), before=lambda: ix.set_ctx([N0]))
+    K1, V1 = dev_rows(0, N1)
+    ix1 = rsa.wave_index_build(K1, V1, G, [N1], seg, K_s, iters, seed)
+    bws = torch.empty(rsa.wave_index_plan(G, [N1], seg, K_s)["build_ws_bytes"], dtype=torch.uint8, device=dev)
+    t_re = timed(lambda: rsa.wave_index_build(K1, V1, G, [N1], seg, K_s, iters, seed, index=ix1, ws=bws))
+    # one token into a half-full last segment
+    Nh = N0 + seg // 2
+    Kh, Vh = dev_rows(0, Nh)
+    ixh = rsa.wave_index_build(Kh, Vh, G, [Nh], seg, K_s, iters, seed, cap_segs=cap)
+    k1, v1 = dev_rows(Nh, Nh + 1)
+    ws1 = torch.empty(rsa.wave_index_append_plan(ixh, [Nh + 1]), dtype=torch.uint8, device=dev)
+    t_tok = timed(lambda: rsa.wave_index_append(ixh, k1, v1, [Nh + 1], iters, seed, ws=ws1),
+                  before=lambda: ixh.set_ctx([Nh]))
+    torch.cuda.synchronize()
+    return {"workload": "llama3-8b-attention-layer-128k-append", "kv_heads": G, "seg_len": seg,
+            "ms_append_one_segment": round(t_seg, 3), "append_tokens_per_s": round(G * seg / (t_seg / 1000.0)),
+            "ms_rebuild_%d" % N1: round(t_re, 3), "rebuild_over_append": round(t_re / t_seg, 2),
+            "ms_append_one_token_into_half_segment": round(t_tok, 3), "reps": reps, "timing": "median of reps"}
 
 
 def workload_summary(r):
