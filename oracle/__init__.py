@@ -234,9 +234,21 @@ def decode_k_max(C_list, topk_frac):
     return max([k_from_frac(topk_frac, int(C)) for C in C_list] + [0])
 
 
-def decode(index, K, V, q, n_sink, n_local, topk_frac, k_max=None, shared=False):
+def value_sums_bf16(index):
+    """The bf16 value sums of an index: round-to-nearest-even of the ordered fp32 sums (the
+    estimation zone's per-cluster value sums, RetroInfer page section 2.A, stored at half the
+    bytes, as the Vortex page's byte-lean variants do)."""
+    return f32_to_bf16(index.vsum)
+
+
+def _vsum(index, vsum_bf16):
+    return bf16_to_f32(value_sums_bf16(index)).astype(np.float32) if vsum_bf16 else index.vsum
+
+
+def decode(index, K, V, q, n_sink, n_local, topk_frac, k_max=None, shared=False, vsum_bf16=False):
     """Wave-index decode for q [B][H][128] against `index`. Returns (out [B,H,128] f64, lse [B,H], ids, k [B,H]).
-    shared: one retrieval set per kv head, chosen by the group key (ref_decode_shared)."""
+    shared: one retrieval set per kv head, chosen by the group key (ref_decode_shared).
+    vsum_bf16: the estimation zone reads the bf16 value sums (value_sums_bf16) widened exactly."""
     q = _c(q, np.uint16)
     B, H = q.shape[0], q.shape[1]
     if k_max is None:
@@ -247,14 +259,14 @@ def decode(index, K, V, q, n_sink, n_local, topk_frac, k_max=None, shared=False)
     kc = np.empty((B, H), np.int32)
     fn = _load().ref_decode_shared if shared else _load().ref_decode
     rc = fn(B, H, index.G, _p(index.ctx), index.seg_len, index.K_s, _p(_c(K, np.uint16)),
-            _p(_c(V, np.uint16)), _p(index.assign), _p(index.centroids_bf16), _p(index.vsum), _p(q),
-            n_sink, n_local, topk_frac, k_max, _p(out), _p(lse), _p(ids), _p(kc))
+            _p(_c(V, np.uint16)), _p(index.assign), _p(index.centroids_bf16), _p(_c(_vsum(index, vsum_bf16), np.float32)),
+            _p(q), n_sink, n_local, topk_frac, k_max, _p(out), _p(lse), _p(ids), _p(kc))
     if rc != 0:
         raise ValueError("ref_decode rejected its arguments (rc=%d)" % rc)
     return out, lse, ids[:, :, :k_max], kc
 
 
-def decode_tail(index, K, V, q, n_sink, n_local, topk_frac, Kt, Vt, tail_len, k_max=None):
+def decode_tail(index, K, V, q, n_sink, n_local, topk_frac, Kt, Vt, tail_len, k_max=None, vsum_bf16=False):
     """Wave-index decode plus the tokens appended after the build (exact): Kt, Vt [B][G][cap][128] bf16 bits,
     tail_len [B] <= cap. Returns as decode()."""
     q = _c(q, np.uint16)
@@ -270,7 +282,8 @@ def decode_tail(index, K, V, q, n_sink, n_local, topk_frac, Kt, Vt, tail_len, k_
     ids = np.empty((B, H, max(k_max, 1)), np.int32)
     kc = np.empty((B, H), np.int32)
     rc = _load().ref_decode_tail(B, H, index.G, _p(index.ctx), index.seg_len, index.K_s, _p(_c(K, np.uint16)),
-                                 _p(_c(V, np.uint16)), _p(index.assign), _p(index.centroids_bf16), _p(index.vsum),
+                                 _p(_c(V, np.uint16)), _p(index.assign), _p(index.centroids_bf16),
+                                 _p(_c(_vsum(index, vsum_bf16), np.float32)),
                                  _p(q), n_sink, n_local, topk_frac, _p(Kt), _p(Vt), cap, _p(tl), k_max, _p(out),
                                  _p(lse), _p(ids), _p(kc))
     if rc != 0:

@@ -812,3 +812,62 @@ def test_decode_tail_rejects_lengths_beyond_capacity():
     Kf, Vf, cf, Ki, Vi, ctx, Kt, Vt, idx, q = _tail_setup()
     with pytest.raises(ValueError):
         oracle.decode_tail(idx, Ki, Vi, q, 4, 64, 0.05, Kt, Vt, [65, 0])
+
+
+# ------------------------------------------------------------ bf16 value sums
+def test_value_sums_bf16_is_rne_of_the_fp32_sums():
+    # the reading: bf16 sums are the round-to-nearest-even of the ordered fp32 sums (torch's
+    # float32 -> bfloat16 conversion is an independent implementation of that rounding)
+    K, V, ctx, idx, q = _setup_decode()
+    ref = torch.from_numpy(idx.vsum).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.value_sums_bf16(idx), ref)
+
+
+def test_decode_bf16_sums_estimation_only_closed_form():
+    # topk_frac = 0 and no steady tokens: o = sum_j e^{s_j} bf16(Vsum_j) / sum_j e^{s_j} n_j
+    K, V, ctx, idx, q = _setup_decode()
+    o, lse, _, _ = oracle.decode(idx, K, V, q, 0, 0, 0.0, vsum_bf16=True)
+    vb = torch.from_numpy(idx.vsum).to(torch.bfloat16).to(torch.float64).numpy()
+    clu = 0
+    for b, N in enumerate(ctx):
+        C = int(idx.C[b])
+        for h in range(q.shape[1]):
+            g = h * idx.G // q.shape[1]
+            cs = slice(clu + g * C, clu + (g + 1) * C)
+            n = idx.sizes[cs].astype(np.float64)
+            chat = oracle.bf16_to_f32(idx.centroids_bf16[cs]).astype(np.float64)
+            s = chat @ oracle.bf16_to_f32(q[b, h]).astype(np.float64) / math.sqrt(D)
+            s = np.where(n > 0, s, -np.inf)
+            w = np.exp(s - s.max())
+            want = (w[:, None] * vb[cs]).sum(0) / (w * n).sum()
+            np.testing.assert_allclose(o[b, h], want, rtol=1e-10, atol=1e-10)
+        clu += idx.G * C
+
+
+@pytest.mark.parametrize("frac,ns,nl", [(0.05, 4, 64), (0.0, 0, 0), (0.3, 16, 16)])
+def test_decode_bf16_sums_bound(frac, ns, nl):
+    # Only the estimation zone's value sums change, each by at most 2^-8 of itself (bf16 has
+    # 8 significant bits): |o_bf16 - o_fp32| <= 2^-8 sum_E w_j |Vsum_j| / Z <= 2^-8 max_t |v_t|
+    # per dim; the selection and the lse do not change (they do not read the values).
+    K, V, ctx, idx, q = _setup_decode()
+    o1, l1, i1, _ = oracle.decode(idx, K, V, q, ns, nl, frac)
+    o2, l2, i2, _ = oracle.decode(idx, K, V, q, ns, nl, frac, vsum_bf16=True)
+    assert np.array_equal(i1, i2) and np.array_equal(l1, l2)
+    vmax = np.abs(oracle.bf16_to_f32(V).astype(np.float64)).max(0)
+    assert np.all(np.abs(o2 - o1) <= 2.0 ** -8 * vmax[None, None, :] + 1e-12)
+    if frac < 1.0 and not (ns == 0 and nl == 0 and frac == 0.0):
+        assert np.abs(o2 - o1).max() > 0  # the rounding is visible
+
+
+def test_decode_bf16_sums_exact_when_sums_are_representable():
+    # values in {-1, 0, 1} and clusters of at most 256 members: every value sum is an integer
+    # of magnitude <= 256, exact in bf16, so both decodes agree bit for bit
+    K, V, ctx, idx, q = _setup_decode()
+    rng = np.random.default_rng(5)
+    Vi = oracle.f32_to_bf16(rng.integers(-1, 2, V.shape).astype(np.float32))
+    idx2 = oracle.build(K, Vi, idx.G, ctx, idx.seg_len, idx.K_s, 3, 1234)
+    assert idx2.sizes.max() <= 256
+    for frac, ns, nl in [(0.05, 4, 64), (0.0, 0, 0)]:
+        o1, l1, i1, _ = oracle.decode(idx2, K, Vi, q, ns, nl, frac)
+        o2, l2, i2, _ = oracle.decode(idx2, K, Vi, q, ns, nl, frac, vsum_bf16=True)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2) and np.array_equal(i1, i2)
