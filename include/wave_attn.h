@@ -114,7 +114,11 @@ typedef struct wave_index {
   int32_t* sizes;           /* [clusters]: members per cluster */
   float* centroids;         /* [clusters][128]: fp32 centroids (member means) */
   void* centroids_bf16;     /* bf16 [clusters][128]: round-to-nearest-even of centroids */
-  float* vsum;              /* [clusters][128]: ordered fp32 sum of the members' V rows */
+  float* vsum;              /* nullable [clusters][128]: ordered fp32 sum of the members' V rows */
+  void* vsum_bf16;          /* nullable bf16 [clusters][128]: round-to-nearest-even of the ordered fp32
+                               sums (half the bytes). A build or append writes each of vsum and
+                               vsum_bf16 that is non-NULL (at least one must be); the estimation zone
+                               reads vsum_bf16 when it is non-NULL, else vsum */
 } wave_index;
 
 /*

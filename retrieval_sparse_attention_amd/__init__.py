@@ -45,7 +45,7 @@ class _Index(ctypes.Structure):
                 ("cap_segs", ctypes.c_int32), ("reserved", ctypes.c_int32), ("k_sorted", ctypes.c_void_p), ("v_sorted", ctypes.c_void_p), ("perm", ctypes.c_void_p),
                 ("inv_perm", ctypes.c_void_p), ("assign", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
                 ("sizes", ctypes.c_void_p), ("centroids", ctypes.c_void_p), ("centroids_bf16", ctypes.c_void_p),
-                ("vsum", ctypes.c_void_p)]
+                ("vsum", ctypes.c_void_p), ("vsum_bf16", ctypes.c_void_p)]
 
 
 _lib = None
@@ -214,8 +214,11 @@ class WaveIndex:
         self.c.clusters_per_seg = self.clusters_per_seg
         self.c.cap_segs = self.cap_segs
         for k in ("k_sorted", "v_sorted", "perm", "inv_perm", "assign", "offsets", "sizes", "centroids",
-                  "centroids_bf16", "vsum"):
-            setattr(self.c, k, arrays[k].data_ptr())
+                  "centroids_bf16", "vsum", "vsum_bf16"):
+            if k in arrays:
+                setattr(self.c, k, arrays[k].data_ptr())
+        self.value_sums = "both" if ("vsum" in arrays and "vsum_bf16" in arrays) else (
+            "bf16" if "vsum_bf16" in arrays else "f32")
 
     def set_ctx(self, ctx):
         """Point the index at new contexts (host array kept alive here)."""
@@ -224,7 +227,11 @@ class WaveIndex:
         self.c.shape.ctx = ctypes.cast(self._ctx_arr, ctypes.POINTER(ctypes.c_int64))
 
     @staticmethod
-    def allocate(n_kv_heads, ctx, seg_len, clusters_per_seg, device="cuda", cap_segs=0):
+    def allocate(n_kv_heads, ctx, seg_len, clusters_per_seg, device="cuda", cap_segs=0, value_sums="f32"):
+        """Device arrays of an index. value_sums: "f32" (ordered fp32 sums), "bf16" (their
+        round-to-nearest-even bf16, which the estimation zone then reads) or "both"."""
+        if value_sums not in ("f32", "bf16", "both"):
+            raise ValueError("value_sums must be 'f32', 'bf16' or 'both', got %r" % (value_sums,))
         z = wave_index_plan(n_kv_heads, ctx, seg_len, clusters_per_seg, cap_segs)
         R, Cn, O = z["rows"], z["clusters"], z["offsets_len"]
         e = dict(device=device)
@@ -238,12 +245,15 @@ class WaveIndex:
             "sizes": torch.empty(Cn, dtype=torch.int32, **e),
             "centroids": torch.empty((Cn, HEAD_DIM), dtype=torch.float32, **e),
             "centroids_bf16": torch.empty((Cn, HEAD_DIM), dtype=torch.bfloat16, **e),
-            "vsum": torch.empty((Cn, HEAD_DIM), dtype=torch.float32, **e),
         }
+        if value_sums in ("f32", "both"):
+            arrays["vsum"] = torch.empty((Cn, HEAD_DIM), dtype=torch.float32, **e)
+        if value_sums in ("bf16", "both"):
+            arrays["vsum_bf16"] = torch.empty((Cn, HEAD_DIM), dtype=torch.bfloat16, **e)
         return WaveIndex(n_kv_heads, ctx, seg_len, clusters_per_seg, arrays, cap_segs), z
 
 
-def _build_prep(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, cap_segs, index, ws):
+def _build_prep(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, cap_segs, index, ws, value_sums="f32"):
     """Checks, and the index and workspace of a build (allocated unless passed)."""
     if index is not None:
         cap_segs = index.cap_segs
@@ -252,7 +262,8 @@ def _build_prep(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, cap_segs, inde
         _check_reuse(index, n_kv_heads, ctx, seg_len, clusters_per_seg, cap_segs)
     _check_build_io(K, V, index, ws, z)
     if index is None:
-        index, z = WaveIndex.allocate(n_kv_heads, ctx, seg_len, clusters_per_seg, device=K.device, cap_segs=cap_segs)
+        index, z = WaveIndex.allocate(n_kv_heads, ctx, seg_len, clusters_per_seg, device=K.device, cap_segs=cap_segs,
+                                      value_sums=value_sums)
     else:
         index.set_ctx(ctx)
     if ws is None:
@@ -261,14 +272,15 @@ def _build_prep(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, cap_segs, inde
 
 
 def wave_index_build(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, iters, seed, assign_trace=False,
-                     stream=None, index=None, ws=None, cap_segs=0):
+                     stream=None, index=None, ws=None, cap_segs=0, value_sums="f32"):
     """Build the index of K, V (bf16 [sum_b G*N_b, 128] device tensors) on the current stream.
 
     Returns the WaveIndex (and the [iters, rows] int32 assignment trace if asked).  `index`
     and `ws` may be passed to reuse existing allocations; cap_segs > 0 lays the index out
-    with room for that many segments per (sequence, kv head) block, for wave_index_append.
+    with room for that many segments per (sequence, kv head) block, for wave_index_append;
+    value_sums picks the value sums a new index stores (WaveIndex.allocate).
     """
-    index, ws, z = _build_prep(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, cap_segs, index, ws)
+    index, ws, z = _build_prep(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, cap_segs, index, ws, value_sums)
     tr = torch.empty((iters, z["rows"]), dtype=torch.int32, device=K.device) if assign_trace else None
     sh = _Shape()
     ctypes.pointer(sh)[0] = index.c.shape  # a copy whose ctx points at the index's own array
@@ -279,9 +291,9 @@ def wave_index_build(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, iters, se
 
 
 def wave_index_build_blocks(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, stream=None, index=None, ws=None,
-                            cap_segs=0):
+                            cap_segs=0, value_sums="f32"):
     """Index of the block top-k baseline: contiguous blocks in place of the k-means clusters."""
-    index, ws, z = _build_prep(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, cap_segs, index, ws)
+    index, ws, z = _build_prep(K, V, n_kv_heads, ctx, seg_len, clusters_per_seg, cap_segs, index, ws, value_sums)
     sh = _Shape()
     ctypes.pointer(sh)[0] = index.c.shape
     _check(lib().wave_index_build_blocks(ctypes.byref(sh), _ptr(K), _ptr(V), int(seg_len), int(clusters_per_seg),

@@ -1133,7 +1133,8 @@ __global__ __launch_bounds__(RS_THREADS) void k_sort_radix(BuildSeq sa, int part
 // per cluster, 2 dims per lane, members fetched 16 at a time (their positions
 // with one load, then 16 row loads in flight). Writes the bf16 centroid and its
 // squared norm. The last round (FINAL) also copies every member's K and V row
-// to its sorted slot, writes inv_perm and the ordered fp32 value sums.
+// to its sorted slot, writes inv_perm and the ordered fp32 value sums (and/or
+// their round-to-nearest-even bf16 copy).
 template <bool FINAL>
 __global__ __launch_bounds__(256) void k_update(BuildSeq sa, int64_t nclu, const uint16_t* __restrict__ K,
                                                 const uint16_t* __restrict__ V, wave_index ix,
@@ -1145,7 +1146,9 @@ __global__ __launch_bounds__(256) void k_update(BuildSeq sa, int64_t nclu, const
   const int64_t F = cr.gF;
   const int n = ix.sizes[F];
   if (n == 0) {
-    if (FINAL) *reinterpret_cast<float2*>(ix.vsum + F * D + 2 * lane) = make_float2(0.f, 0.f);
+    if (FINAL && ix.vsum) *reinterpret_cast<float2*>(ix.vsum + F * D + 2 * lane) = make_float2(0.f, 0.f);
+    if (FINAL && ix.vsum_bf16)
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(ix.vsum_bf16) + F * D + 2 * lane) = 0u;
     return;
   }
   const int off = ix.offsets[cr.boff + cr.j];
@@ -1199,7 +1202,10 @@ __global__ __launch_bounds__(256) void k_update(BuildSeq sa, int64_t nclu, const
   const float a = bf16_to_f(h0), b = bf16_to_f(h1);
   const float q2 = wave_sum(fmaf(a, a, b * b));
   if (lane == 0) norm[F] = q2;
-  if (FINAL) *reinterpret_cast<float2*>(ix.vsum + F * D + 2 * lane) = make_float2(w0, w1);
+  if (FINAL && ix.vsum) *reinterpret_cast<float2*>(ix.vsum + F * D + 2 * lane) = make_float2(w0, w1);
+  if (FINAL && ix.vsum_bf16)
+    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(ix.vsum_bf16) + F * D + 2 * lane) =
+        (uint32_t)f_to_bf16(w0) | ((uint32_t)f_to_bf16(w1) << 16);
 }
 
 // ------------------------------------------------------------------ k_block_assign

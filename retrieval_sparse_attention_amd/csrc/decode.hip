@@ -20,12 +20,12 @@
 //               row workgroups', the estimation chunks' and the tail workgroups'
 //
 // Estimation bookkeeping. The pages' estimation zone is E \ R with the value
-// sums and sizes of the clusters' non-steady members. k_attend adds the centroid
-// term e^{s_j} (n_j, Vsum_j) of EVERY cluster; each member row t of a selected
-// cluster and each steady row t of a cluster that is not selected then adds
-// -e^{s_j} (1, v_t) in k_attend. Summed, this leaves exactly the centroid terms
-// of E \ R over their non-steady members (clusters outside E have only steady
-// members and cancel), up to fp32 rounding of the stored sums.
+// sums and sizes of the clusters' non-steady members. k_score marks the clusters
+// outside E (no non-steady member) with a NaN rank key, k_topk leaves each q head's
+// selection bitmap in the workspace, and k_attend adds the centroid term
+// e^{s_j} (n_j, Vsum_j) of every cluster of E \ R; each steady row t of such a
+// cluster adds -e^{s_j} (1, v_t). Summed, this is exactly the centroid term of
+// E \ R over the non-steady members, whatever the precision of the stored sums.
 #include <math.h>
 
 #include "common.h"
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(SCORE_THREADS) void k_score(SeqArgs sa, DecodeArgs 
       const float key = S.kw[hh][jj];
       const int n = S.nsz[jj];
       const bool elig = !sz.all && n > 0 && S.scnt[jj] < n;
-      ws.keys[kb + (int64_t)hh * C + jj] = key;
+      ws.keys[kb + (int64_t)hh * C + jj] = elig ? key : __uint_as_float(0x7FC00000u);  // NaN: outside E
       if (!da.shared)
         ws.key32[kb + (int64_t)hh * C + jj] = elig ? float_sortable(key) : 0u;
       else if (hh == 0)
@@ -296,7 +296,19 @@ __device__ void est_role(const SeqArgs& sa, const DecodeArgs& da, const wave_ind
 #pragma unroll
   for (int hh = 0; hh < GS; ++hh) kr[hh] = kb[(int64_t)hh * C + jc];
   float4 vreg[SC / 8];
-  {
+  if (ix.vsum_bf16 != nullptr) {
+    // bf16 value sums (half the bytes), widened exactly
+    const char* vsrc = reinterpret_cast<const char*>(reinterpret_cast<const uint16_t*>(ix.vsum_bf16) + (clu0 + j0) * D);
+    uint2 wreg[SC / 8];
+#pragma unroll
+    for (int u = 0; u < SC / 8; ++u) {
+      const uint32_t off = (uint32_t)(min(sub + 8 * u, nc - 1) * (D * 2) + dq * 8);
+      wreg[u] = *reinterpret_cast<const uint2*>(vsrc + off);
+    }
+#pragma unroll
+    for (int u = 0; u < SC / 8; ++u)
+      vreg[u] = make_float4(bf16_lo(wreg[u].x), bf16_hi(wreg[u].x), bf16_lo(wreg[u].y), bf16_hi(wreg[u].y));
+  } else {
     // a uniform base and 32-bit lane offsets: one address register per load
     const char* vsrc = reinterpret_cast<const char*>(ix.vsum + (clu0 + j0) * D);
 #pragma unroll
@@ -305,11 +317,20 @@ __device__ void est_role(const SeqArgs& sa, const DecodeArgs& da, const wave_ind
       vreg[u] = *reinterpret_cast<const float4*>(vsrc + off);
     }
   }
-  const bool live = jj < nc && n0 > 0;
+  // the q heads' selections (k_topk's bitmaps): a selected cluster is attended row by row
+  int64_t wb = 0;
+  for (int i = 0; i < b; ++i) wb += (int64_t)da.H * ((sa.C[i] + 31) >> 5);
+  const int nwords = (C + 31) >> 5, jw = j0 + jc;
+  uint32_t selb[GS];
+#pragma unroll
+  for (int hh = 0; hh < GS; ++hh)
+    selb[hh] = (ws.selw[wb + (int64_t)(g * GS + hh) * nwords + (jw >> 5)] >> (jw & 31)) & 1u;
   float sv[GS];
   if (tid < SC) {
 #pragma unroll
     for (int hh = 0; hh < GS; ++hh) {
+      // E \ R: eligible (a rank key, not NaN), not selected by this q head
+      const bool live = jj < nc && n0 > 0 && kr[hh] == kr[hh] && selb[hh] == 0u;
       sv[hh] = live ? kr[hh] * sc : -INFINITY;
       const float mx = wave_max(sv[hh]);
       if (lane == 0) S.hred[hh][wv][0] = mx;
@@ -322,7 +343,7 @@ __device__ void est_role(const SeqArgs& sa, const DecodeArgs& da, const wave_ind
       const float M = fmaxf(S.hred[hh][0][0], S.hred[hh][1][0]);
       const float wgt = sv[hh] == -INFINITY ? 0.f : exp2f(sv[hh] - M);
       S.kw[hh][tid] = wgt;
-      const float ls = wave_sum(wgt * (float)(live ? n0 : 0));
+      const float ls = wave_sum(wgt * (float)(jj < nc ? n0 : 0));
       if (lane == 0) S.hred[hh][wv][1] = ls;
     }
   }
@@ -661,7 +682,6 @@ __global__ __launch_bounds__(TK_THREADS, PF ? 1 : 2 * TK_WAVES / 4) void k_topk(
   const uint32_t* key32 = ws.key32 + (int64_t)da.GS * sb.wclu + (int64_t)hs * C;
   const float* keys = ws.keys + kbase;
   int2* span = ws.span + kbase;
-  float* skey = ws.skey + kbase;
   int32_t* out = sel_ids + (int64_t)bh * da.k_max;
   const int32_t* sizes = ix.sizes + clu0;
   const int32_t* offs = ix.offsets + off0;
@@ -868,7 +888,6 @@ __global__ __launch_bounds__(TK_THREADS, PF ? 1 : 2 * TK_WAVES / 4) void k_topk(
           const int n = (int)r.z, pre = L.u.c.pre[ci];
           out[rank] = id;
           span[rank] = make_int2((int)r.w, n);
-          skey[rank] = da.shared ? keys[id] : sortable_float(r.y);  // the head's own rank key
           selpre[rank] = pre;
           atomicOr(&L.selw[id >> 5], 1u << (id & 31));
           if (rank == k - 1) {
@@ -1001,7 +1020,6 @@ __global__ __launch_bounds__(TK_THREADS, PF ? 1 : 2 * TK_WAVES / 4) void k_topk(
             const int id = (int)(0xFFFFFFFFu - (uint32_t)(cb[r] & 0xFFFFFFFFu));
             out[r] = id;
             span[r] = make_int2(offs[id], sizes[id]);
-            skey[r] = keys[id];
             atomicOr(&selw[id >> 5], 1u << (id & 31));
           }
           done = true;
@@ -1072,7 +1090,6 @@ __global__ __launch_bounds__(TK_THREADS, PF ? 1 : 2 * TK_WAVES / 4) void k_topk(
           const int j = id_of(c0 + v);
           const int p = pos + __popcll(sm & ltmask);
           span[p] = make_int2(offs[j], sizes[j]);
-          skey[p] = keys[j];
           sb_[p] = ((uint64_t)x << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)j);
           atomicOr(&selw[j >> 5], 1u << (j & 31));
         }
@@ -1148,7 +1165,13 @@ __global__ __launch_bounds__(TK_THREADS, PF ? 1 : 2 * TK_WAVES / 4) void k_topk(
       kj = keys[j];
     }
     const bool sel = (selw[j >> 5] >> (j & 31)) & 1u;
-    corr[i] = sel ? __uint_as_float(0x7FC00000u) : kj;
+    corr[i] = sel ? __uint_as_float(0x7FC00000u) : kj;  // NaN also outside E (its key)
+  }
+  // the selection bitmap for the estimation role of k_attend (in the workspace already
+  // when it did not fit LDS)
+  if (lds_sel) {
+    uint32_t* gw = ws.selw + wbase + (int64_t)h * nwords;
+    for (int i = tid; i < nwords; i += nt) gw[i] = L.selw[i];
   }
 }
 
@@ -1329,7 +1352,6 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
   const uint16_t* Vs = reinterpret_cast<const uint16_t*>(ix.v_sorted) + row0 * D + l16 * 8;
   const int32_t* selpre = ws.selpre + kbase + bh;
   const int2* span = ws.span + kbase;
-  const float* skey = ws.skey + kbase;
   const float* corr = ws.corr + (int64_t)bh * da.scap;
   // The selection's metadata (member prefix, span, rank key of up to kreq clusters)
   // and the steady rows' sorted slots and corrections, loaded into LDS in the same
@@ -1337,7 +1359,6 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
   // latency instead of one dependent global round trip each.
   __shared__ int32_t m_pre[ATT_KCAP + 1];
   __shared__ int2 m_span[ATT_KCAP];
-  __shared__ float m_key[ATT_KCAP];
   __shared__ int32_t m_sp[ATT_SCAP];
   __shared__ float m_corr[ATT_SCAP];
   const int kq = da.kreq[b];  // k <= kq <= C: entries up to kq are this head's
@@ -1346,17 +1367,13 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
     const int tid = threadIdx.x;
     int32_t rp[ATT_KCAP / ATT_THREADS + 1];
     int2 rs[ATT_KCAP / ATT_THREADS];
-    float rk[ATT_KCAP / ATT_THREADS];
     int32_t rq[ATT_SCAP / ATT_THREADS];
     float rc[ATT_SCAP / ATT_THREADS];
 #pragma unroll
     for (int u = 0; u <= ATT_KCAP / ATT_THREADS; ++u) {
       const int c = tid + u * ATT_THREADS;
       if (c <= kq) rp[u] = selpre[c];
-      if (u < ATT_KCAP / ATT_THREADS && c < kq) {
-        rs[u] = span[c];
-        rk[u] = skey[c];
-      }
+      if (u < ATT_KCAP / ATT_THREADS && c < kq) rs[u] = span[c];
     }
 #pragma unroll
     for (int u = 0; u < ATT_SCAP / ATT_THREADS; ++u) {
@@ -1370,10 +1387,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
     for (int u = 0; u <= ATT_KCAP / ATT_THREADS; ++u) {
       const int c = tid + u * ATT_THREADS;
       if (c <= kq) m_pre[c] = rp[u];
-      if (u < ATT_KCAP / ATT_THREADS && c < kq) {
-        m_span[c] = rs[u];
-        m_key[c] = rk[u];
-      }
+      if (u < ATT_KCAP / ATT_THREADS && c < kq) m_span[c] = rs[u];
     }
 #pragma unroll
     for (int u = 0; u < ATT_SCAP / ATT_THREADS; ++u) {
@@ -1392,16 +1406,14 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
 #pragma unroll
   for (int d = 0; d < 8; ++d) st.acc[d] = 0.f;
   // window of 16 selected clusters [ci0, ci0 + 16) held one per lane of the group:
-  // wpre = first row of the cluster, wsx = its first sorted slot, wkey = its centroid score
+  // wpre = first row of the cluster, wsx = its first sorted slot
   const int gbase = grp * 16;
   int ci0 = 0, wpre = 0x7FFFFFFF, wsx = 0, wend = 0;
-  float wkey = -INFINITY;
   auto load_window = [&](int c0) {
     ci0 = c0;
     const int c = c0 + l16;
     wpre = c <= k ? pre_of(c) : 0x7FFFFFFF;
     wsx = c < k ? (lds_meta ? m_span[c].x : span[c].x) : 0;
-    wkey = c < k ? (lds_meta ? m_key[c] : skey[c]) * sc : -INFINITY;
     wend = __shfl(c0 + 16 <= k ? pre_of(min(c0 + 16, k)) : 0x7FFFFFFF, gbase, 64);
   };
   if (s0 < min(s1, M)) {
@@ -1431,14 +1443,12 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
     }
     uint4 kv[U], vv[U];
     int32_t t[U];
-    float ck[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int row = min(r + u, r1 - 1);
       const uint32_t m = (uint32_t)(__ballot(wpre <= row) >> gbase) & 0xFFFFu;
       const int l = gbase + __popc(m) - 1;
       const int32_t p = __shfl(wsx, l, 64) + row - __shfl(wpre, l, 64);
-      ck[u] = __shfl(wkey, l, 64);
       t[u] = ix.perm[row0 + p];
       kv[u] = *reinterpret_cast<const uint4*>(Ks + (int64_t)p * D);
       vv[u] = *reinterpret_cast<const uint4*>(Vs + (int64_t)p * D);
@@ -1450,7 +1460,7 @@ __global__ __launch_bounds__(ATT_THREADS) void k_attend(SeqArgs sa, DecodeArgs d
       const bool valid = r + u < r1;
       const bool steady = t[u] < sz.a_end || t[u] >= sz.c_beg;  // counted exactly with the steady rows
       sv[u] = (valid && !steady) ? x : -INFINITY;
-      cs[u] = (valid && da.est) ? ck[u] : -INFINITY;  // no centroid term to take back without estimation
+      cs[u] = -INFINITY;  // a selected cluster has no centroid term to take back
     }
     softmax_rows<U>(st, sv, cs, vv);
   }

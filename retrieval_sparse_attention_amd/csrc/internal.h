@@ -40,9 +40,8 @@ struct DecodeWs {
   float* keys;       // [sum_b H*C_b] rank keys
   uint32_t* key32;   // [sum_b H*C_b] sortable keys, 0 = not eligible
   int2* span;        // [sum_b H*C_b] (first sorted slot, size) of the i-th selected cluster
-  float* skey;       // [sum_b H*C_b] rank key of the i-th selected cluster
   int32_t* selpre;   // [sum_b H*(C_b+1)] rows of the selection before its i-th cluster
-  uint32_t* selw;    // [sum_b H*ceil(C_b/32)] selection bitmap when C_b > 65536
+  uint32_t* selw;    // [sum_b H*ceil(C_b/32)] each q head's selection bitmap (k_topk; read by the estimation role)
   float* corr;       // [B*H*scap] rank key of a steady row's cluster if it is not selected, else NaN
   int32_t* counts;   // [B*H*4] rows of the selected clusters, k, steady rows, 0
   float* part;       // [B*H*NP*132] partial softmax states: P row workgroups, then max_b ceil(C_b / 128)

@@ -34,6 +34,15 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// the value sums: each given array 16-byte aligned; at least one when `need`
+wave_status check_vsums(const wave_index* ix, bool need) {
+  if (need && ix->vsum == nullptr && ix->vsum_bf16 == nullptr)
+    return fail(WAVE_ERR_ARG, "vsum and vsum_bf16 are both NULL");
+  if ((ix->vsum && !aligned16(ix->vsum)) || (ix->vsum_bf16 && !aligned16(ix->vsum_bf16)))
+    return fail(WAVE_ERR_ALIGN, "index arrays must be 16-byte aligned");
+  return WAVE_OK;
+}
+
 // ------------------------------------------------------------------ shape checks
 wave_status check_shape(const wave_shape* s) {
   if (s == nullptr) return fail(WAVE_ERR_ARG, "shape is NULL");
@@ -133,7 +142,7 @@ wave_status hip_device_ok() {
 // ------------------------------------------------------------------ decode sizes
 struct DecodePlan {
   wave::DecodeArgs da;
-  size_t keys, key32, span, skey, selpre, selw, corr, counts, part, ctop, sortg, total;
+  size_t keys, key32, span, selpre, selw, corr, counts, part, ctop, sortg, total;
 };
 
 wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t n_local, double frac,
@@ -227,7 +236,6 @@ wave_status decode_plan(const wave_index* ix, int32_t H, int32_t n_sink, int32_t
   P->keys = o;   o += align256(4 * (size_t)(H * sumC));
   P->key32 = o;  o += align256(4 * (size_t)(H * sumC));
   P->span = o;   o += align256(8 * (size_t)(H * sumC));
-  P->skey = o;   o += align256(4 * (size_t)(H * sumC));
   P->selpre = o; o += align256(4 * (size_t)(H * sumC + BH));
   P->selw = o;   o += align256(4 * (size_t)(H * sumW));
   P->corr = o;   o += align256(4 * (size_t)(BH * da.scap));
@@ -340,11 +348,13 @@ static wave_status build_checks(const wave_shape* shape, const void* K, const vo
   st = check_cap(shape, seg_len, out->cap_segs);
   if (st != WAVE_OK) return st;
   const void* ptrs[] = {out->k_sorted, out->v_sorted, out->perm, out->inv_perm, out->assign, out->offsets,
-                        out->sizes, out->centroids, out->centroids_bf16, out->vsum};
+                        out->sizes, out->centroids, out->centroids_bf16};
   for (const void* p : ptrs)
     if (p == nullptr) return fail(WAVE_ERR_ARG, "an index array pointer is NULL");
   for (const void* p : ptrs)
     if (!aligned16(p)) return fail(WAVE_ERR_ALIGN, "index arrays must be 16-byte aligned");
+  st = check_vsums(out, true);
+  if (st != WAVE_OK) return st;
   if (!aligned16(K) || !aligned16(V) || !aligned16(ws))
     return fail(WAVE_ERR_ALIGN, "K, V and ws must be 16-byte aligned");
   *sa = make_seq(shape, seg_len, clusters_per_seg, out->cap_segs);
@@ -460,11 +470,13 @@ wave_status wave_index_append(wave_index* index, const int64_t* new_ctx, const v
   wave_status st = append_checks(index, new_ctx, &sa, n_old, &appended, &L);
   if (st != WAVE_OK) return st;
   const void* ptrs[] = {index->k_sorted, index->v_sorted, index->perm, index->inv_perm, index->assign,
-                        index->offsets, index->sizes, index->centroids, index->centroids_bf16, index->vsum};
+                        index->offsets, index->sizes, index->centroids, index->centroids_bf16};
   for (const void* p : ptrs)
     if (p == nullptr) return fail(WAVE_ERR_ARG, "an index array pointer is NULL");
   for (const void* p : ptrs)
     if (!aligned16(p)) return fail(WAVE_ERR_ALIGN, "index arrays must be 16-byte aligned");
+  st = check_vsums(index, true);
+  if (st != WAVE_OK) return st;
   if (appended > 0) {
     if (K_new == nullptr || V_new == nullptr || ws == nullptr)
       return fail(WAVE_ERR_ARG, "K_new, V_new and ws must be non-NULL when tokens are appended");
@@ -509,11 +521,13 @@ static wave_status decode_call(const wave_index* index, const void* q, int32_t n
   if (q == nullptr || out == nullptr || ws == nullptr) return fail(WAVE_ERR_ARG, "q, out and ws must be non-NULL");
   if (P.da.k_max > 0 && sel_ids == nullptr) return fail(WAVE_ERR_ARG, "sel_ids is NULL but k_max = %d", P.da.k_max);
   const void* ptrs[] = {index->k_sorted, index->v_sorted, index->perm, index->inv_perm, index->assign,
-                        index->offsets, index->sizes, index->centroids_bf16, index->vsum};
+                        index->offsets, index->sizes, index->centroids_bf16};
   for (const void* p : ptrs)
     if (p == nullptr) return fail(WAVE_ERR_ARG, "an index array pointer is NULL");
   for (const void* p : ptrs)
     if (!aligned16(p)) return fail(WAVE_ERR_ALIGN, "index arrays must be 16-byte aligned");
+  st = check_vsums(index, est != 0);
+  if (st != WAVE_OK) return st;
   if (!aligned16(q) || !aligned16(out) || !aligned16(ws) || (sel_ids && !aligned16(sel_ids)) ||
       (lse && !aligned16(lse)))
     return fail(WAVE_ERR_ALIGN, "q, out, sel_ids, lse and ws must be 16-byte aligned");
@@ -526,7 +540,6 @@ static wave_status decode_call(const wave_index* index, const void* q, int32_t n
   dw.keys = reinterpret_cast<float*>(w + P.keys);
   dw.key32 = reinterpret_cast<uint32_t*>(w + P.key32);
   dw.span = reinterpret_cast<int2*>(w + P.span);
-  dw.skey = reinterpret_cast<float*>(w + P.skey);
   dw.selpre = reinterpret_cast<int32_t*>(w + P.selpre);
   dw.selw = reinterpret_cast<uint32_t*>(w + P.selw);
   dw.corr = reinterpret_cast<float*>(w + P.corr);

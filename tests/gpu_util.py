@@ -16,8 +16,9 @@ def to_host_u16(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def upload_index(idx):
-    """An oracle.Index as a device WaveIndex (same arrays, same layout)."""
+def upload_index(idx, value_sums="f32"):
+    """An oracle.Index as a device WaveIndex (same arrays, same layout). value_sums "bf16" or
+    "both" also uploads the oracle's bf16 value sums (the estimation zone then reads those)."""
     arrays = {
         "k_sorted": to_dev_bf16(idx.k_sorted),
         "v_sorted": to_dev_bf16(idx.v_sorted),
@@ -28,8 +29,12 @@ def upload_index(idx):
         "sizes": torch.from_numpy(idx.sizes).to(DEV),
         "centroids": torch.from_numpy(idx.centroids).to(DEV),
         "centroids_bf16": to_dev_bf16(idx.centroids_bf16),
-        "vsum": torch.from_numpy(idx.vsum).to(DEV),
     }
+    if value_sums in ("f32", "both"):
+        arrays["vsum"] = torch.from_numpy(idx.vsum).to(DEV)
+    if value_sums in ("bf16", "both"):
+        import oracle
+        arrays["vsum_bf16"] = to_dev_bf16(oracle.value_sums_bf16(idx))
     return rsa.WaveIndex(idx.G, idx.ctx.tolist(), idx.seg_len, idx.K_s, arrays)
 
 
