@@ -58,6 +58,12 @@ def _load():
         lib.ref_build.restype = ctypes.c_int
         lib.ref_index_from_assign.argtypes = [i32, i32, P, P, P, i32, i32, u64, P] + [P] * 10
         lib.ref_index_from_assign.restype = ctypes.c_int
+        lib.ref_sortable.argtypes = [ctypes.c_float]
+        lib.ref_sortable.restype = ctypes.c_uint32
+        lib.ref_select_stochastic.argtypes = [P, P, i32, i32, i32, u64, P]
+        lib.ref_decode_stochastic.argtypes = [i32, i32, i32, P, i32, i32, P, P, P, P, P, P, i32, i32, f64, i32, u64,
+                                              i32, P, P, P, P]
+        lib.ref_decode_stochastic.restype = ctypes.c_int
         lib.ref_rank_key.argtypes = [P, P]
         lib.ref_rank_key.restype = ctypes.c_float
         lib.ref_select.argtypes = [P, P, i32, i32, P]
@@ -228,6 +234,43 @@ def select(keys, ids, k):
     out = np.empty(k, np.int32)
     _load().ref_select(_p(keys), _p(ids), len(keys), k, _p(out))
     return out
+
+
+def sortable(f):
+    """Order-preserving 32-bit key of a float (-0 ranks with +0; 0 is never produced)."""
+    return _load().ref_sortable(float(np.float32(f)))
+
+
+def select_stochastic(keys, ids, k, passes, phase_state):
+    """Stochastic radix top-k of eligible (keys, ids) (ids ascending): ids in ascending order."""
+    keys, ids = _c(keys, np.float32), _c(ids, np.int32)
+    out = np.empty(max(k, 1), np.int32)
+    _load().ref_select_stochastic(_p(keys), _p(ids), len(keys), k, passes, ctypes.c_uint64(phase_state), _p(out))
+    return out[:k]
+
+
+def stochastic_phase_state(seed, b, h):
+    """State whose first SplitMix64 output gives the sampling phase of (b, h)."""
+    return (int(seed) + 0x9E3779B97F4A7C15 * (((int(b) << 32) | int(h)) + 1)) % (1 << 64)
+
+
+def decode_stochastic(index, K, V, q, n_sink, n_local, topk_frac, passes, seed, k_max=None):
+    """Wave-index decode with the stochastic radix top-k (ids ascending). Returns as decode()."""
+    q = _c(q, np.uint16)
+    B, H = q.shape[0], q.shape[1]
+    if k_max is None:
+        k_max = decode_k_max(index.C, topk_frac)
+    out = np.empty((B, H, D), np.float64)
+    lse = np.empty((B, H), np.float64)
+    ids = np.empty((B, H, max(k_max, 1)), np.int32)
+    kc = np.empty((B, H), np.int32)
+    rc = _load().ref_decode_stochastic(B, H, index.G, _p(index.ctx), index.seg_len, index.K_s, _p(_c(K, np.uint16)),
+                                       _p(_c(V, np.uint16)), _p(index.assign), _p(index.centroids_bf16),
+                                       _p(index.vsum), _p(q), n_sink, n_local, topk_frac, passes,
+                                       ctypes.c_uint64(seed), k_max, _p(out), _p(lse), _p(ids), _p(kc))
+    if rc != 0:
+        raise ValueError("ref_decode_stochastic rejected its arguments (rc=%d)" % rc)
+    return out, lse, ids[:, :, :k_max], kc
 
 
 def decode_k_max(C_list, topk_frac):

@@ -508,6 +508,76 @@ void ref_select(const float* keys, const int32_t* cand, int32_t n, int32_t k, in
 }
 
 /*
+ * Sortable key of a float: an order-preserving map to 32-bit unsigned integers
+ * [bit-defined]. For f >= 0 (and for -0, which ranks equal to +0) it is
+ * 2^31 + |bits|, for f < 0 it is 2^31 - 1 - |bits|, |bits| being the 31 bits of
+ * magnitude. Finite floats land in [2^23, 2^32 - 2^23], so 0 is free.
+ */
+uint32_t ref_sortable(float f) {
+  uint32_t b;
+  memcpy(&b, &f, 4);
+  const uint32_t mag = b & 0x7FFFFFFFu;
+  if (mag == 0u || !(b >> 31)) return 0x80000000u + mag;
+  return 0x7FFFFFFFu - mag;
+}
+
+/*
+ * Stochastic radix top-k (Vortex page, section 2.C: the top-k terminates early and
+ * samples the rest from the threshold bin) [bit-defined reading]. cand[0..n) are
+ * the eligible ids in ascending order with their rank keys, k <= n.
+ *  - Radix descent over the sortable keys, 8 bits a pass from the top: pass r
+ *    counts, among the keys whose first 8r bits equal the prefix P so far, the
+ *    keys per value of their next 8 bits; the threshold bin is the value t at
+ *    which the count of keys above reaches k (all keys in higher bins are taken,
+ *    `above` of them), P becomes P.t. The descent stops after `passes` passes, or
+ *    earlier when the threshold bin is needed whole (above + its count = k).
+ *  - The m = k - above remaining ids come from the n members of the threshold bin
+ *    (prefix P) by systematic sampling with a random phase: with members b_0 <
+ *    b_1 < ... in ascending id order and phase c in [0, n), b_r is taken when
+ *    floor((r m + c) / n) < floor(((r + 1) m + c) / n): exactly m members, evenly
+ *    spread over the bin. c = splitmix64 output of the stream starting at state
+ *    phase_state, mod n.
+ * out[0..k) receives the selection in ascending id order.
+ */
+void ref_select_stochastic(const float* keys, const int32_t* cand, int32_t n, int32_t k, int32_t passes,
+                           uint64_t phase_state, int32_t* out) {
+  uint32_t* u = (uint32_t*)malloc(sizeof(uint32_t) * (size_t)(n > 0 ? n : 1));
+  for (int32_t i = 0; i < n; ++i) u[i] = ref_sortable(keys[i]);
+  uint32_t P = 0;
+  int32_t above = 0, done = 0;
+  while (done < passes && done < 4) {
+    int64_t hist[256];
+    for (int v = 0; v < 256; ++v) hist[v] = 0;
+    const int shift = 24 - 8 * done;
+    for (int32_t i = 0; i < n; ++i)
+      if (done == 0 || (u[i] >> (shift + 8)) == P) hist[(u[i] >> shift) & 255u] += 1;
+    int t = 255;
+    while (t > 0 && above + hist[t] < k) above += (int32_t)hist[t--];
+    P = (P << 8) | (uint32_t)t;
+    ++done;
+    if (above + hist[t] == k) break;
+  }
+  const int fs = 32 - 8 * done;  /* bits below the prefix */
+  int64_t nb = 0;
+  for (int32_t i = 0; i < n; ++i)
+    if ((uint32_t)((uint64_t)u[i] >> fs) == P) ++nb;
+  const int64_t m = k - above;
+  const uint64_t c = nb > 0 ? ref_splitmix64_next(&phase_state) % (uint64_t)nb : 0;
+  int32_t o = 0;
+  int64_t r = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const uint32_t pre = (uint32_t)((uint64_t)u[i] >> fs);
+    if (pre > P) {
+      out[o++] = cand[i];
+    } else if (pre == P) {
+      if (((uint64_t)r * m + c) / nb < ((uint64_t)(r + 1) * m + c) / nb) out[o++] = cand[i];
+      ++r;
+    }
+  }
+  free(u);
+}
+
+/*
  * One decode query per (sequence b, q head h) against the index (section 2.A,
  * the three zones), in binary64 apart from the rank key:
  *   S   = steady zone: positions t < n_sink or t >= N - n_local (sink tokens at
@@ -528,13 +598,16 @@ void ref_select(const float* keys, const int32_t* cand, int32_t n, int32_t k, in
  * (rank order, -1 padded). Returns k_b per (b, h) in kcount (nullable).
  * shared: R is chosen once per kv head by the group key of each cluster (see
  * ref_decode_shared); the zones of every q head then follow from that R.
+ * sto_passes > 0: R is the stochastic radix top-k (ref_select_stochastic, the
+ * phase of (b, h) from the stream of key b*2^32 + h under sto_seed), ids in
+ * ascending order.
  */
 static int decode_impl(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int32_t seg_len, int32_t K_s,
                        const uint16_t* K, const uint16_t* V, const int32_t* assign, const uint16_t* chat,
                        const float* vsum, const uint16_t* q, int32_t n_sink, int32_t n_local, double topk_frac,
                        int32_t k_max, double* out, double* lse, int32_t* ids, int32_t* kcount, int estimate,
                        int shared, const uint16_t* Kt, const uint16_t* Vt, int32_t tail_cap,
-                       const int32_t* tail_len) {
+                       const int32_t* tail_len, int32_t sto_passes, uint64_t sto_seed) {
   if (B < 1 || G < 1 || H < 1 || H % G != 0 || n_sink < 0 || n_local < 0 || !(topk_frac >= 0.0 && topk_frac <= 1.0))
     return -1;
   seq_base* sb = make_bases(B, G, ctx, seg_len, K_s);
@@ -586,7 +659,11 @@ static int decode_impl(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int3
     int64_t kreq = ref_k_from_frac(topk_frac, C);
     int32_t k = (int32_t)(kreq < nE ? kreq : nE);
     int32_t* sel = (int32_t*)malloc(sizeof(int32_t) * (size_t)(k > 0 ? k : 1));
-    ref_select(keys, cand, nE, k, sel);
+    if (sto_passes > 0)
+      ref_select_stochastic(keys, cand, nE, k, sto_passes,
+                            sto_seed + GAMMA * ((((uint64_t)(uint32_t)b << 32) | (uint32_t)h) + 1), sel);
+    else
+      ref_select(keys, cand, nE, k, sel);
     if (kcount) kcount[bh] = k;
     if (ids) {
       if (k > k_max) {
@@ -672,7 +749,23 @@ int ref_decode(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int32_t seg_
                int32_t n_sink, int32_t n_local, double topk_frac, int32_t k_max, double* out, double* lse,
                int32_t* ids, int32_t* kcount) {
   return decode_impl(B, H, G, ctx, seg_len, K_s, K, V, assign, chat, vsum, q, n_sink, n_local, topk_frac, k_max, out,
-                     lse, ids, kcount, 1, 0, NULL, NULL, 0, NULL);
+                     lse, ids, kcount, 1, 0, NULL, NULL, 0, NULL, 0, 0);
+}
+
+/*
+ * Wave attention with the stochastic radix top-k in place of the exact top-k
+ * (Vortex page, section 2.C; an inexact variant): R = ref_select_stochastic with
+ * `passes` 8-bit passes, phase stream of (b, h) under `seed`; ids in ascending
+ * order. Everything else as ref_decode.
+ */
+int ref_decode_stochastic(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int32_t seg_len, int32_t K_s,
+                          const uint16_t* K, const uint16_t* V, const int32_t* assign, const uint16_t* chat,
+                          const float* vsum, const uint16_t* q, int32_t n_sink, int32_t n_local, double topk_frac,
+                          int32_t passes, uint64_t seed, int32_t k_max, double* out, double* lse, int32_t* ids,
+                          int32_t* kcount) {
+  if (passes < 1 || passes > 4) return -1;
+  return decode_impl(B, H, G, ctx, seg_len, K_s, K, V, assign, chat, vsum, q, n_sink, n_local, topk_frac, k_max, out,
+                     lse, ids, kcount, 1, 0, NULL, NULL, 0, NULL, passes, seed);
 }
 
 /*
@@ -693,7 +786,7 @@ int ref_decode_tail(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int32_t
   for (int32_t b = 0; b < B; ++b)
     if (tail_len[b] < 0 || tail_len[b] > tail_cap) return -1;
   return decode_impl(B, H, G, ctx, seg_len, K_s, K, V, assign, chat, vsum, q, n_sink, n_local, topk_frac, k_max, out,
-                     lse, ids, kcount, 1, 0, Kt, Vt, tail_cap, tail_len);
+                     lse, ids, kcount, 1, 0, Kt, Vt, tail_cap, tail_len, 0, 0);
 }
 
 /*
@@ -714,7 +807,7 @@ int ref_decode_shared(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int32
                       const float* vsum, const uint16_t* q, int32_t n_sink, int32_t n_local, double topk_frac,
                       int32_t k_max, double* out, double* lse, int32_t* ids, int32_t* kcount) {
   return decode_impl(B, H, G, ctx, seg_len, K_s, K, V, assign, chat, vsum, q, n_sink, n_local, topk_frac, k_max, out,
-                     lse, ids, kcount, 1, 1, NULL, NULL, 0, NULL);
+                     lse, ids, kcount, 1, 1, NULL, NULL, 0, NULL, 0, 0);
 }
 
 /*
@@ -732,7 +825,7 @@ int ref_decode_topk(int32_t B, int32_t H, int32_t G, const int64_t* ctx, int32_t
   /* the value sums are not read without the estimation zone; a zero array stands in */
   float* vz = (float*)calloc((size_t)(clusters > 0 ? clusters : 1) * D, sizeof(float));
   int rc = decode_impl(B, H, G, ctx, seg_len, K_s, K, V, assign, chat, vz, q, n_sink, n_local, topk_frac, k_max, out,
-                       lse, ids, kcount, 0, 0, NULL, NULL, 0, NULL);
+                       lse, ids, kcount, 0, 0, NULL, NULL, 0, NULL, 0, 0);
   free(vz);
   return rc;
 }

@@ -871,3 +871,97 @@ def test_decode_bf16_sums_exact_when_sums_are_representable():
         o1, l1, i1, _ = oracle.decode(idx2, K, Vi, q, ns, nl, frac)
         o2, l2, i2, _ = oracle.decode(idx2, K, Vi, q, ns, nl, frac, vsum_bf16=True)
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2) and np.array_equal(i1, i2)
+
+
+# ------------------------------------------------------- stochastic radix top-k
+def test_sortable_key_order_and_zero():
+    # an order-preserving map of floats to 32-bit keys: +0 and -0 equal, 0 never produced
+    assert oracle.sortable(0.0) == oracle.sortable(-0.0) == 0x80000000
+    assert oracle.sortable(1.0) == 0xBF800000 and oracle.sortable(-1.0) == 0x407FFFFF
+    fmax = float(np.finfo(np.float32).max)
+    assert oracle.sortable(-fmax) == 0x00800000 and oracle.sortable(fmax) == 0xFF7FFFFF
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal(3000) * np.exp(rng.uniform(-80, 80, 3000))).astype(np.float32)
+    x = np.concatenate([x, np.float32([1e-45, -1e-45, 0.0, 3.0, -3.0])])
+    u = np.array([oracle.sortable(v) for v in x], np.uint64)
+    i, j = rng.integers(0, len(x), (2, 20000))
+    assert np.all((x[i] < x[j]) == (u[i] < u[j]))
+    assert np.all((x[i] == x[j]) == (u[i] == u[j]))
+
+
+def _exact_top(keys, k):
+    return set(np.lexsort((np.arange(len(keys)), -keys.astype(np.float64)))[:k].tolist())
+
+
+@pytest.mark.parametrize("passes", [1, 2, 3, 4])
+def test_select_stochastic_invariants(passes):
+    # exactly k distinct eligible ids in ascending order; every key whose first 8*passes bits
+    # exceed those of the k-th largest key is taken, none below them is
+    rng = np.random.default_rng(passes)
+    for n, k in [(1000, 50), (300, 1), (64, 64), (5000, 1180), (10, 0)]:
+        keys = (rng.standard_normal(n) * rng.choice([0.01, 1.0, 100.0])).astype(np.float32)
+        ids = np.arange(n, dtype=np.int32) * 3
+        s = oracle.select_stochastic(keys, ids, k, passes, 77 + n)
+        assert len(s) == k and len(set(s.tolist())) == k and np.all(np.diff(s) > 0)
+        if k == 0:
+            continue
+        u = np.array([oracle.sortable(v) for v in keys], np.uint64)
+        sh = 32 - 8 * passes
+        pk = np.sort(u)[::-1][k - 1] >> sh
+        pre = u >> sh
+        chosen = np.isin(ids, s)
+        assert np.all(chosen[pre > pk]) and not np.any(chosen[pre < pk])
+
+
+def test_select_stochastic_full_resolution_is_the_exact_top_k():
+    # four passes resolve every bit: with distinct keys the set is the exact top-k
+    rng = np.random.default_rng(9)
+    keys = rng.standard_normal(4000).astype(np.float32)
+    keys = np.unique(keys)
+    rng.shuffle(keys)
+    ids = np.arange(len(keys), dtype=np.int32)
+    for k in (1, 37, 500, len(keys)):
+        assert set(oracle.select_stochastic(keys, ids, k, 4, 5).tolist()) == _exact_top(keys, k)
+
+
+def test_select_stochastic_whole_threshold_bin_is_exact():
+    # the k-th and (k+1)-th keys differ in their first byte: the first pass takes its
+    # threshold bin whole, and the result is the exact top-k whatever the phase
+    keys = np.float32([3.0, 2.5, -1.0, -1.5, 0.25, 0.3])  # 2.5 (0xC0..) vs 0.3 (0xBE..)
+    ids = np.arange(6, dtype=np.int32)
+    for ph in range(20):
+        assert oracle.select_stochastic(keys, ids, 2, 1, ph).tolist() == [0, 1]
+
+
+def test_select_stochastic_sampling_is_uniform_over_the_bin():
+    # systematic sampling with a random phase: each member of the threshold bin is taken
+    # with probability m / n (here 3 of 10 members of one bin, nothing above it)
+    keys = np.float32(1.0) + np.arange(10, dtype=np.float32) * np.float32(2 ** -20)  # one first-2-byte bin
+    ids = np.arange(10, dtype=np.int32)
+    cnt = np.zeros(10)
+    T = 6000
+    for t in range(T):
+        s = oracle.select_stochastic(keys, ids, 3, 2, oracle.stochastic_phase_state(t, 0, 0))
+        assert len(s) == 3
+        cnt[s] += 1
+    np.testing.assert_allclose(cnt / T, 0.3, atol=0.03)
+
+
+def test_decode_stochastic_special_cases():
+    K, V, ctx, idx, q = _setup_decode()
+    # every eligible cluster selected: dense attention, ids ascending
+    o, lse, ids, kc = oracle.decode_stochastic(idx, K, V, q, 4, 64, 1.0, 1, 3)
+    of, lf = oracle.full_attention(K, V, q, idx.G, ctx)
+    np.testing.assert_allclose(o, of, rtol=1e-12, atol=1e-12)
+    for b in range(len(ctx)):
+        for h in range(q.shape[1]):
+            v = ids[b, h, :kc[b, h]]
+            assert np.all(np.diff(v) > 0)
+    # four passes on distinct rank keys: the exact selection's set, hence the exact output
+    o1, l1, i1, k1 = oracle.decode(idx, K, V, q, 4, 64, 0.05)
+    o2, l2, i2, k2 = oracle.decode_stochastic(idx, K, V, q, 4, 64, 0.05, 4, 11)
+    assert np.array_equal(k1, k2)
+    for b in range(len(ctx)):
+        for h in range(q.shape[1]):
+            assert np.array_equal(np.sort(i1[b, h, :k1[b, h]]), i2[b, h, :k2[b, h]])
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
