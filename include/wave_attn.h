@@ -269,6 +269,26 @@ wave_status wave_attn_decode_tail(const wave_index* index, const void* q, int32_
                                   float* lse, void* ws, size_t ws_bytes, wave_stream_t stream);
 
 /*
+ * wave_attn_decode_stochastic -- wave_attn_decode with the stochastic radix
+ * top-k in place of the exact selection (Vortex page, section 2.C: the top-k
+ * terminates early and samples the rest from a threshold bin); an inexact
+ * variant, reported by its recall of the exact ids. Per (b, h): a radix descent
+ * over the order-preserving 32-bit map of the rank keys, 8 bits a pass, for
+ * `passes` passes (1..4; fewer when the threshold bin is needed whole); every
+ * bin above the threshold bin is selected whole, and the m ids still missing
+ * are the members r (ascending id order, n of them) of the threshold bin with
+ * floor((r m + c) / n) < floor(((r + 1) m + c) / n), c = the first SplitMix64
+ * output of the stream starting at seed + 0x9E3779B97F4A7C15*((b*2^32 + h) + 1),
+ * mod n. Exactly k ids, in ascending order (not rank order), -1 padded.
+ * Arguments, workspace (wave_attn_decode_plan) and errors as wave_attn_decode;
+ * ARG if passes is outside [1, 4].
+ */
+wave_status wave_attn_decode_stochastic(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
+                                        int32_t n_local, double topk_frac, int32_t passes, uint64_t seed, float* out,
+                                        int32_t* sel_ids, float* lse, void* ws, size_t ws_bytes,
+                                        wave_stream_t stream);
+
+/*
  * wave_attn_decode_shared -- wave attention with one retrieval set per kv head.
  * The RetroInfer page (section 2.A) retrieves the clusters most similar to the
  * query; under grouped-query attention the q heads of a kv head read the same

@@ -74,6 +74,8 @@ def lib():
         L.wave_attn_decode_topk.argtypes = L.wave_attn_decode.argtypes
         L.wave_attn_decode_static.argtypes = [ctypes.POINTER(_Index), P, i32, i32, i32, ctypes.c_double, P, P, P, P]
         L.wave_attn_decode_shared.argtypes = L.wave_attn_decode.argtypes
+        L.wave_attn_decode_stochastic.argtypes = [ctypes.POINTER(_Index), P, i32, i32, i32, ctypes.c_double, i32, u64,
+                                                  P, P, P, P, sz, P]
         L.wave_attn_decode_tail_plan.argtypes = [ctypes.POINTER(_Index), i32, i32, i32, ctypes.c_double, i32,
                                                  ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_size_t)]
         L.wave_attn_decode_tail.argtypes = [ctypes.POINTER(_Index), P, i32, i32, i32, ctypes.c_double, P, P, i32, P,
@@ -87,7 +89,8 @@ def lib():
         for f in ("wave_index_plan", "wave_index_build", "wave_attn_decode_plan", "wave_attn_decode",
                   "wave_profiler_enable", "wave_index_build_blocks", "wave_attn_decode_topk",
                   "wave_attn_decode_shared", "wave_attn_decode_tail_plan", "wave_attn_decode_tail",
-                  "wave_attn_decode_static", "wave_index_plan_cap", "wave_index_append_plan", "wave_index_append"):
+                  "wave_attn_decode_static", "wave_index_plan_cap", "wave_index_append_plan", "wave_index_append",
+                  "wave_attn_decode_stochastic"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -447,6 +450,30 @@ def wave_attn_decode_tail(index, q, n_sink, n_local, topk_frac, k_tail, v_tail, 
     _check(lib().wave_attn_decode_tail(ctypes.byref(index.c), _ptr(q), H, int(n_sink), int(n_local), float(topk_frac),
                                        _ptr(k_tail), _ptr(v_tail), cap, _ptr(tail_len), _ptr(out), _ptr(sel_ids),
                                        _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+    return out, sel_ids[:, :, :k_max], lse
+
+
+def wave_attn_decode_stochastic(index, q, n_sink, n_local, topk_frac, passes, seed, ws=None, out=None, sel_ids=None,
+                                lse=None, stream=None):
+    """Wave attention with the stochastic radix top-k (an inexact variant of the selection; ids in
+    ascending order). passes: 8-bit radix passes before the threshold bin is sampled (1..4)."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be a [B, H, 128] tensor")
+    B, H = int(q.shape[0]), int(q.shape[1])
+    k_max, wsb = wave_attn_decode_plan(index, H, n_sink, n_local, topk_frac)
+    _check_decode_io(index, q, out, sel_ids, lse, ws, k_max, wsb)
+    dev = index.device
+    if ws is None:
+        ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty((B, H, HEAD_DIM), dtype=torch.float32, device=dev)
+    if sel_ids is None:
+        sel_ids = torch.empty((B, H, max(k_max, 1)), dtype=torch.int32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _check(lib().wave_attn_decode_stochastic(ctypes.byref(index.c), _ptr(q), H, int(n_sink), int(n_local),
+                                             float(topk_frac), int(passes), ctypes.c_uint64(seed), _ptr(out),
+                                             _ptr(sel_ids), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
     return out, sel_ids[:, :, :k_max], lse
 
 

@@ -28,8 +28,6 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr uint64_t GAMMA = 0x9E3779B97F4A7C15ULL;
-
 // ------------------------------------------------------------------ unit lookup
 // The batch of one build call. first[b] is the first segment of sequence b that the
 // call clusters (0 for a whole build; ceil(N_b / seg_len): none): an append re-clusters
@@ -119,11 +117,6 @@ __device__ inline CluRef clu_of(const BuildSeq& sa, int64_t F) {
   return r;
 }
 
-__device__ __forceinline__ uint64_t sm64_mix(uint64_t z) {
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
-  return z ^ (z >> 31);
-}
 
 // ------------------------------------------------------------------ k_init
 // Stream key of the unit (b, g, s): b*2^56 + g*2^40 + s*2^16 (mod 2^64). Keyed by the

@@ -62,6 +62,19 @@ __host__ __device__ inline int64_t num_clusters(int64_t N, int32_t seg_len, int3
   return (nseg - 1) * (int64_t)K_s + seg_clusters(N - (nseg - 1) * seg_len, seg_len, K_s);
 }
 
+// ---------------------------------------------------------------- SplitMix64
+// Steele, Lea and Flood, "Fast splittable pseudorandom number generators" (OOPSLA
+// 2014): the state advances by GAMMA and each output is the state through this mixer
+// (variant 13), so the i-th output of the stream starting at state s is
+// sm64_mix(s + GAMMA * (i + 1)).
+constexpr uint64_t GAMMA = 0x9E3779B97F4A7C15ULL;
+
+__device__ __forceinline__ uint64_t sm64_mix(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+
 // ---------------------------------------------------------------- XCD-aware workgroup order
 // Workgroups are dispatched round robin over the 8 XCDs (workgroup w runs on XCD
 // w mod 8), each with its own L2. The linear index of w in a grid of n puts

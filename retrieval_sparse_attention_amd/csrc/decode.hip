@@ -1175,6 +1175,193 @@ __global__ __launch_bounds__(TK_THREADS, PF ? 1 : 2 * TK_WAVES / 4) void k_topk(
   }
 }
 
+// ------------------------------------------------------------------ k_topk_sto
+// The stochastic radix top-k (Vortex page, section 2.C: the top-k terminates early and
+// samples the rest of the selection from a threshold bin), an inexact variant of k_topk
+// with the same outputs (ids, spans, member prefix, counts, selection bitmap, steady
+// corrections); ids in ascending order. One workgroup per (sequence, q head); thread i
+// owns the clusters [i per, (i + 1) per), so scans over the threads run in id order.
+// Radix descent over the sortable keys, 8 bits a pass: an LDS histogram of the next
+// digit of the keys that share the prefix so far, and one wave scanning its 256 bins
+// from the top for the threshold bin; after da.sto_passes passes (fewer when the
+// threshold bin is needed whole) the bins above it are taken whole, and its members
+// by systematic sampling with a random phase: member r (in id order) of the n is
+// taken when floor((r m + c) / n) < floor(((r + 1) m + c) / n), m the ids still
+// missing, c = the first SplitMix64 output of the stream of (b, h) under the seed,
+// mod n. NK: keys a thread holds in registers (0: re-read from memory each pass).
+template <int NK>
+__global__ __launch_bounds__(TK_THREADS) void k_topk_sto(SeqArgs sa, DecodeArgs da, wave_index ix, DecodeWs ws,
+                                                         int32_t* __restrict__ sel_ids) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint64_t tmp[17];
+  __shared__ int32_t res[4];
+  const int bh = blockIdx.x;
+  const int b = bh / da.H, h = bh % da.H, g = h / da.GS;
+  const SeqBase sb = seq_base(sa, b);
+  const int N = sb.N, C = sb.C;
+  const int64_t row0 = sb.row + (int64_t)g * sb.NS;
+  const int64_t clu0 = sb.clu + (int64_t)g * sb.CS;
+  const int64_t off0 = sb.off + (int64_t)g * (sb.CS + 1);
+  const int64_t kbase = (int64_t)da.GS * sb.wclu + (int64_t)h * C;
+  const uint32_t* key32 = ws.key32 + kbase;
+  const float* keys = ws.keys + kbase;
+  int2* span = ws.span + kbase;
+  int32_t* selpre = ws.selpre + kbase + bh;
+  int32_t* out = sel_ids + (int64_t)bh * da.k_max;
+  const int32_t* sizes = ix.sizes + clu0;
+  const int32_t* offs = ix.offsets + off0;
+  const int nwords = (C + 31) >> 5;
+  int64_t wbase = 0;
+  for (int i = 0; i < b; ++i) wbase += (int64_t)da.H * ((sa.C[i] + 31) >> 5);
+  uint32_t* selw = ws.selw + wbase + (int64_t)h * nwords;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int per = (C + TK_THREADS - 1) / TK_THREADS;
+  const int j0 = min(tid * per, C), j1 = min(j0 + per, C), nmine = j1 - j0;
+  uint32_t ur[NK > 0 ? NK : 1];
+  if constexpr (NK > 0) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) ur[i] = i < nmine ? key32[j0 + i] : 0u;
+  }
+  // visit f(i, u) for every key the thread owns, in id order
+  auto each = [&](auto&& f) {
+    if constexpr (NK > 0) {
+#pragma unroll
+      for (int i = 0; i < NK; ++i)
+        if (i < nmine) f(i, ur[i]);
+    } else {
+      for (int i = 0; i < nmine; ++i) f(i, key32[j0 + i]);
+    }
+  };
+  for (int i = tid; i < nwords; i += TK_THREADS) selw[i] = 0u;
+  int ne = 0;
+  each([&](int, uint32_t u) { ne += u != 0u; });
+  uint64_t tot;
+  (void)block_scan_excl((uint64_t)ne, tmp, &tot);
+  const int k = min(da.kreq[b], (int)tot);
+  // 1. radix descent
+  uint32_t P = 0u;
+  int above = 0, done = 0;
+  while (k > 0 && done < da.sto_passes && done < 4) {
+    if (tid < 256) hist[tid] = 0u;
+    __syncthreads();
+    const int shift = 24 - 8 * done;
+    each([&](int, uint32_t u) {
+      if (u != 0u && (done == 0 || (u >> (shift + 8)) == P)) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+    });
+    __syncthreads();
+    if (wv == 0) {
+      // lane l holds bins 255 - 4l .. 252 - 4l; counts from the top as an inclusive scan
+      uint32_t c4[4];
+      int sum = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        c4[e] = hist[255 - 4 * lane - e];
+        sum += (int)c4[e];
+      }
+      int incl = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      const int excl = incl - sum;
+      if (above + excl < k && k <= above + incl) {  // one lane: the k-th key's bin is here
+        int cum = above + excl, t = 255 - 4 * lane, whole = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (cum + (int)c4[e] >= k) {
+            t = 255 - 4 * lane - e;
+            whole = cum + (int)c4[e] == k;
+            break;
+          }
+          cum += (int)c4[e];
+        }
+        res[0] = t;
+        res[1] = cum;
+        res[2] = whole;
+      }
+    }
+    __syncthreads();
+    P = (P << 8) | (uint32_t)res[0];
+    above = res[1];
+    ++done;
+    if (res[2]) break;
+  }
+  // 2. the threshold bin's members in id order, and the sampling phase
+  const int fs = 32 - 8 * max(done, 1);
+  int nbo = 0;
+  each([&](int, uint32_t u) { nbo += u != 0u && (u >> fs) == P; });
+  uint64_t nbt;
+  const uint64_t rb = block_scan_excl((uint64_t)nbo, tmp, &nbt);
+  const uint64_t nb = nbt, mm = (uint64_t)(k - above);
+  const uint64_t c =
+      nb > 0 ? sm64_mix(da.sto_seed + GAMMA * ((((uint64_t)(uint32_t)b << 32) | (uint32_t)h) + 1) + GAMMA) % nb : 0;
+  // 3. the selection: per thread its count and rows, then positions and member prefixes
+  // from one scan of (count << 40) + rows over the threads (ids in order)
+  uint64_t r = rb;
+  auto take = [&](uint32_t u) {
+    bool s = false;
+    if (k > 0 && u != 0u) {
+      const uint32_t p = u >> fs;
+      if (p > P) {
+        s = true;
+      } else if (p == P) {
+        s = (r * mm + c) / nb < ((r + 1) * mm + c) / nb;
+        ++r;
+      }
+    }
+    return s;
+  };
+  uint64_t flags = 0ull, mine = 0ull;  // flags bit i: key j0 + i selected (NK > 0: per <= 64)
+  each([&](int i, uint32_t u) {
+    if (take(u)) {
+      if constexpr (NK > 0) flags |= 1ull << i;
+      mine += (1ull << 40) + (uint64_t)sizes[j0 + i];
+    }
+  });
+  uint64_t all;
+  const uint64_t base = block_scan_excl(mine, tmp, &all);
+  int pos = (int)(base >> 40);
+  int32_t pre = (int32_t)(base & ((1ull << 40) - 1));
+  r = rb;  // keys re-read from memory: the same decisions again
+  each([&](int i, uint32_t u) {
+    bool s;
+    if constexpr (NK > 0) s = (flags >> i) & 1ull;
+    else s = take(u);
+    if (!s) return;
+    const int j = j0 + i;
+    const int n = sizes[j];
+    out[pos] = j;
+    span[pos] = make_int2(offs[j], n);
+    selpre[pos] = pre;
+    atomicOr(&selw[j >> 5], 1u << (j & 31));
+    ++pos;
+    pre += n;
+  });
+  const int32_t rows = (int32_t)(all & ((1ull << 40) - 1));
+  if (tid == 0) {
+    selpre[k] = rows;
+    ws.counts[4 * bh + 0] = rows;
+    ws.counts[4 * bh + 1] = k;
+  }
+  for (int i = k + tid; i < da.k_max; i += TK_THREADS) out[i] = -1;
+  // 4. steady rows: the rank key of their cluster if it is not selected (NaN outside E)
+  const Steady sz = steady_of(da, N);
+  if (tid == 0) {
+    ws.counts[4 * bh + 2] = sz.nS;
+    ws.counts[4 * bh + 3] = 0;
+  }
+  __threadfence_block();
+  __syncthreads();
+  float* corr = ws.corr + (int64_t)bh * da.scap;
+  for (int i = tid; i < sz.nS; i += TK_THREADS) {
+    const int32_t j = ix.assign[row0 + steady_pos(sz, i)];
+    // the bitmap word as the other threads' atomics left it (read at device scope)
+    const uint32_t w = __hip_atomic_load(&selw[j >> 5], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    corr[i] = ((w >> (j & 31)) & 1u) ? __uint_as_float(0x7FC00000u) : keys[j];
+  }
+}
+
 // ------------------------------------------------------------------ k_attend
 __device__ inline void merge_state(float& m, float& l, float* acc, float m2, float l2, const float* acc2, int n) {
   const float M = fmaxf(m, m2);
@@ -1620,7 +1807,15 @@ static hipError_t launch_gs(const SeqArgs& sa, const DecodeArgs& da, const wave_
     case 32: tk = k_topk<32>; break;
     default: tk = k_topk<0>; break;
   }
-  WAVE_TRY(launch("k_topk", tk, tg, tb, tl, st, sa, da, ix, ws, sel_ids));
+  if (da.sto_passes > 0) {
+    int cmax = 0;
+    for (int b = 0; b < sa.B; ++b) cmax = sa.C[b] > cmax ? sa.C[b] : cmax;
+    const int per = (cmax + TK_THREADS - 1) / TK_THREADS;
+    WAVE_TRY(launch("k_topk_sto", per <= 8 ? k_topk_sto<8> : per <= 64 ? k_topk_sto<64> : k_topk_sto<0>, tg, tb, 0,
+                    st, sa, da, ix, ws, sel_ids));
+  } else {
+    WAVE_TRY(launch("k_topk", tk, tg, tb, tl, st, sa, da, ix, ws, sel_ids));
+  }
   WAVE_TRY(launch("k_attend", k_attend<GS>, dim3(sa.B * da.H * da.P + (da.est ? nest : 0)), dim3(ATT_THREADS), 0, st,
                   sa, da, ix, ws, q));
   if (da.NP >= MERGE_SPLIT_MIN_PARTIALS)

@@ -33,6 +33,8 @@ struct DecodeArgs {
   int32_t tail_cap;
   int32_t PT;             // appended-token workgroups per (b, g) in the k_score grid (0: none)
   int32_t nscore;         // scoring workgroups of the k_score grid (the tail workgroups follow)
+  int32_t sto_passes;     // > 0: the stochastic radix top-k (k_topk_sto) with that many 8-bit passes
+  uint64_t sto_seed;      // its sampling seed
   int32_t kreq[MAXB];     // min(ceil(topk_frac * C_b), C_b), binary64 on the host
 };
 

@@ -508,12 +508,14 @@ static wave_status decode_call(const wave_index* index, const void* q, int32_t n
                                int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse, void* ws,
                                size_t ws_bytes, wave_stream_t stream, int est, int shared,
                                const void* k_tail = nullptr, const void* v_tail = nullptr, int32_t tail_cap = 0,
-                               const int32_t* tail_len = nullptr) {
+                               const int32_t* tail_len = nullptr, int32_t sto_passes = 0, uint64_t sto_seed = 0) {
   DecodePlan P;
   wave_status st = decode_plan(index, n_q_heads, n_sink, n_local, topk_frac, &P, tail_cap);
   if (st != WAVE_OK) return st;
   P.da.est = est;
   P.da.shared = shared;
+  P.da.sto_passes = sto_passes;
+  P.da.sto_seed = sto_seed;
   P.da.kt = reinterpret_cast<const uint16_t*>(k_tail);
   P.da.vt = reinterpret_cast<const uint16_t*>(v_tail);
   P.da.tail_len = tail_len;
@@ -607,6 +609,15 @@ wave_status wave_attn_decode_shared(const wave_index* index, const void* q, int3
                                     int32_t n_local, double topk_frac, float* out, int32_t* sel_ids, float* lse,
                                     void* ws, size_t ws_bytes, wave_stream_t stream) {
   return decode_call(index, q, n_q_heads, n_sink, n_local, topk_frac, out, sel_ids, lse, ws, ws_bytes, stream, 1, 1);
+}
+
+wave_status wave_attn_decode_stochastic(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
+                                        int32_t n_local, double topk_frac, int32_t passes, uint64_t seed, float* out,
+                                        int32_t* sel_ids, float* lse, void* ws, size_t ws_bytes,
+                                        wave_stream_t stream) {
+  if (passes < 1 || passes > 4) return fail(WAVE_ERR_ARG, "passes %d outside [1, 4]", passes);
+  return decode_call(index, q, n_q_heads, n_sink, n_local, topk_frac, out, sel_ids, lse, ws, ws_bytes, stream, 1, 0,
+                     nullptr, nullptr, 0, nullptr, passes, seed);
 }
 
 wave_status wave_attn_decode_topk(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
