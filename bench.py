@@ -59,6 +59,11 @@ WORKLOADS = {
     "tail": dict(WORKLOAD, workload="llama3-8b-attention-layer-128k-plus-4096-decoded", tail=4096),
     # the 128K layer with one retrieval set per kv head (wave_attn_decode_shared)
     "shared": dict(WORKLOAD, workload="llama3-8b-attention-layer-128k-shared-selection", shared=True),
+    # the 1M layer with bf16 value sums (the estimation zone reads half the bytes)
+    "1m-bf16-sums": dict(workload="llama3-8b-attention-layer-1m-bf16-value-sums", batch=1, q_heads=32, kv_heads=8,
+                         head_dim=128, ctx=1048576, seg_len=16384, clusters_per_seg=1024, kmeans_iters=10, n_sink=4,
+                         n_local=512, topk_frac=0.018, decode_queries_per_step=32, layers=2, seed_data=3,
+                         seed_build=1234, seed_query=103, value_sums="bf16"),
     "stress": dict(workload="index-build-1m-keys-student-t", batch=1, q_heads=8, kv_heads=8, head_dim=128,
                    ctx=1048576, seg_len=8192, clusters_per_seg=512, kmeans_iters=10, heavy_tailed=True,
                    n_sink=4, n_local=64, topk_frac=0.02, decode_queries_per_step=0, layers=1, seed_data=5,
@@ -368,7 +373,7 @@ def main():
         # the method's other evaluated shapes, each from its own inputs and indexes, on fewer steps
         # (decode per query, achieved bandwidth of the decode, index build, k_assign's MFMA rate)
         extra = {}
-        for name, st in (("1m", 4), ("batched", 4), ("stress", 3)):
+        for name, st in (("1m", 4), ("1m-bf16-sums", 4), ("batched", 4), ("stress", 3)):
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
             r, _ = measure(dict(WORKLOADS[name]), st, 1, args.eager, False, dev)
@@ -376,6 +381,8 @@ def main():
         result["workloads"] = extra
         torch.cuda.empty_cache()
         result["append"] = measure_append(W, dev)
+        torch.cuda.empty_cache()
+        result["stochastic_topk"] = {n: measure_stochastic(dict(WORKLOADS[n]), dev) for n in ("128k", "1m")}
         torch.cuda.empty_cache()
     if headline and not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(W, K, V, ctx, q, args.cpu_seconds)
@@ -445,6 +452,84 @@ def measure_append(W, dev, reps=10):
             "ms_append_one_token_into_half_segment": round(t_tok, 3), "reps": reps, "timing": "median of reps"}
 
 
+def measure_stochastic(W, dev, nq=16, seed=2024):
+    """The stochastic radix top-k variant (wave_attn_decode_stochastic) against the exact selection
+    on one layer of workload W: recall of the exact ids, relative L2 error of both against dense
+    float32 softmax attention, the top-k kernel's average time (dispatch-recorded events) and
+    the decode call's time (event-timed eager calls), over nq queries."""
+    import numpy as np
+    import torch
+
+    import retrieval_sparse_attention_amd as rsa
+    import synth
+    G, H, N, seg, K_s = W["kv_heads"], W["q_heads"], W["ctx"], W["seg_len"], W["clusters_per_seg"]
+    ns, nl, frac = W["n_sink"], W["n_local"], W["topk_frac"]
+    ctx = np.array([N], np.int64)
+    K, V, _ = synth.kv(W["seed_data"], 1, G, ctx, seg)
+    q, _ = synth.queries(W["seed_query"], nq, 1, H, G, ctx, K)
+    Kd = torch.from_numpy(K.view(np.int16)).to(dev).view(torch.bfloat16)
+    Vd = torch.from_numpy(V.view(np.int16)).to(dev).view(torch.bfloat16)
+    qd = torch.from_numpy(q.view(np.int16)).to(dev).view(torch.bfloat16)
+    del K, V
+    ix = rsa.wave_index_build(Kd, Vd, G, [N], seg, K_s, W["kmeans_iters"], W["seed_build"])
+    tau = 1.0 / math.sqrt(128.0)
+    ref = torch.empty((nq, H, 128), dtype=torch.float32, device=dev)
+    for g in range(G):
+        Kg, Vg = Kd[g * N:(g + 1) * N].float(), Vd[g * N:(g + 1) * N].float()
+        qg = qd[:, 0, g * (H // G):(g + 1) * (H // G)].float().reshape(-1, 128)
+        s = torch.matmul(qg, Kg.t().contiguous()) * tau
+        ref[:, g * (H // G):(g + 1) * (H // G)] = torch.matmul(torch.softmax(s, dim=1), Vg).view(nq, H // G, 128)
+        del Kg, Vg, s
+    k_max, wsb = rsa.wave_attn_decode_plan(ix, H, ns, nl, frac)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def run(passes):
+        call = (lambda t: rsa.wave_attn_decode(ix, qd[t], ns, nl, frac, ws=ws)) if passes == 0 else (
+            lambda t: rsa.wave_attn_decode_stochastic(ix, qd[t], ns, nl, frac, passes, seed + t, ws=ws))
+        outs = [call(t) for t in range(nq)]  # warm
+        torch.cuda.synchronize()
+        ev[0].record()
+        for t in range(nq):
+            call(t)
+        ev[1].record()
+        torch.cuda.synchronize()
+        us = 1000.0 * ev[0].elapsed_time(ev[1]) / nq
+        rsa.wave_profiler_enable(True)
+        for t in range(nq):
+            call(t)
+        torch.cuda.synchronize()
+        rsa.wave_profiler_enable(False)
+        prof = rsa.wave_profiler_read()
+        name = "k_topk" if passes == 0 else "k_topk_sto"
+        tk = 1000.0 * prof[name][1] / prof[name][0]
+        ids = [o[1].cpu().numpy() for o in outs]
+        err = torch.cat([((o[0][0] - ref[t]).norm(dim=1) / ref[t].norm(dim=1)) for t, o in enumerate(outs)])
+        return ids, err.cpu().numpy(), us, tk
+
+    ex_ids, ex_err, ex_us, ex_tk = run(0)
+    out = {"workload": W["workload"], "queries": nq, "k_max": k_max,
+           "exact": {"rel_err_mean": round(float(ex_err.mean()), 5), "decode_us_per_query": round(ex_us, 2),
+                     "topk_us": round(ex_tk, 2)}}
+    for passes in (1, 2, 3):
+        ids, err, us, tk = run(passes)
+        hit = tot = 0
+        for a, e in zip(ids, ex_ids):
+            for h in range(H):
+                sa_, se = a[0, h], e[0, h]
+                sa_, se = set(sa_[sa_ >= 0].tolist()), set(se[se >= 0].tolist())
+                hit += len(sa_ & se)
+                tot += len(se)
+        out["passes_%d" % passes] = {"recall": round(hit / max(tot, 1), 4), "rel_err_mean": round(float(err.mean()), 5),
+                                     "rel_err_max": round(float(err.max()), 5), "decode_us_per_query": round(us, 2),
+                                     "topk_us": round(tk, 2)}
+        print("stochastic top-k %s passes %d: recall %.4f, rel err %.5f (exact %.5f), top-k %.1f us (exact %.1f)"
+              % (W["workload"], passes, hit / max(tot, 1), err.mean(), ex_err.mean(), tk, ex_tk), file=sys.stderr,
+              flush=True)
+    del ix, Kd, Vd, ref
+    return out
+
+
 def workload_summary(r):
     """The figures of another workload's line that the headline line carries."""
     ka = r["kernel_roofline"].get("k_assign", {})
@@ -500,7 +585,8 @@ def measure(W, steps, warmup, eager, headline, dev):
     Ks = [Kd0] + [Kd0.clone() for _ in range(L - 1)]
     Vs = [Vd0] + [Vd0.clone() for _ in range(L - 1)]
     z = rsa.wave_index_plan(G, ctx.tolist(), seg, K_s)
-    idxs = [rsa.WaveIndex.allocate(G, ctx.tolist(), seg, K_s, device=dev)[0] for _ in range(L)]
+    vsums = W.get("value_sums", "f32")
+    idxs = [rsa.WaveIndex.allocate(G, ctx.tolist(), seg, K_s, device=dev, value_sums=vsums)[0] for _ in range(L)]
     bws = torch.empty(int(z["build_ws_bytes"]), dtype=torch.uint8, device=dev)
     print("building %d layer indexes" % L, file=sys.stderr, flush=True)
     def build_layer(l):
@@ -647,17 +733,20 @@ def measure(W, steps, warmup, eager, headline, dev):
                    + H * Ctot * 8                 # rank keys + sortable keys out
                    + B * G * n_tail * 2 * 128 * 2  # appended tokens' K, V (their workgroups run in this grid)
                    + (B * H * n_tail_wg * part if n_tail else 0))
+    sel_words = H * sum(-(-c // 32) for c in Cb)  # selection bitmap words (all q heads)
     topk_bytes = (H * Ctot * 4 + G * Ctot * 8     # sortable keys; sizes + offsets
-                  + sel_per_dec * (4 + 8 + 4 + 4)  # ids, spans, keys, member prefix out
+                  + sel_per_dec * (4 + 8 + 4)     # ids, spans, member prefix out
+                  + sel_words * 4                 # the selection bitmaps out (for the estimation role)
                   + B * H * steady * 8)           # steady rows: cluster ids in, corrections out
     attend_bytes = (rows_per_dec * (2 * 128 * 2 + 4)         # K, V and perm of the retrieved rows
                     + B * G * steady * (2 * 128 * 2 + 4)      # steady rows (a kv head's): K, V, inv_perm
                     + B * H * steady * 4                      # their corrections per q head
-                    + sel_per_dec * 16                        # window metadata
+                    + sel_per_dec * 12                        # window metadata
                     + B * H * 128 * 2 + B * H * P * part)     # q, row partials out
     if not blocks:
-        attend_bytes += (G * Ctot * (128 * 4 + 4)             # estimation: value sums + sizes
-                         + H * Ctot * 4                       # estimation: rank keys
+        vs_read = 128 * 2 if vsums in ("bf16", "both") else 128 * 4
+        attend_bytes += (G * Ctot * (vs_read + 4)             # estimation: value sums + sizes
+                         + H * Ctot * 4 + sel_words * 4       # estimation: rank keys, selection bitmaps
                          + H * n_est * part)                  # estimation partials out
     merge_bytes = (B * H * P * part + (0 if blocks else H * n_est * part) + B * H * n_tail_wg * part
                    + B * H * (128 * 4 + 4))
@@ -672,7 +761,8 @@ def measure(W, steps, warmup, eager, headline, dev):
             tok_clu += ls * (K_s if ls >= seg else -(-ls * K_s // seg))
     assign_flops = 2.0 * 128 * G * tok_clu
     assign_bytes = rows * (128 * 2 + 4) + G * Ctot * (128 * 2 + 4)
-    final_update = rows * (4 * 128 * 2 + 3 * 4) + G * Ctot * (2 * 128 * 4 + 128 * 2 + 4)
+    vs_write = {"f32": 128 * 4, "bf16": 128 * 2, "both": 128 * 6}[vsums]
+    final_update = rows * (4 * 128 * 2 + 3 * 4) + G * Ctot * (128 * 4 + vs_write + 128 * 2 + 4)
     update_bytes = (final_update if blocks else
                     ((iters - 1) * (rows * (128 * 2 + 4) + G * Ctot * (128 * 4 + 128 * 2 + 4)) + final_update) / iters)
     sort_bytes = rows * 12 + G * Ctot * 8
