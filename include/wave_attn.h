@@ -281,7 +281,8 @@ wave_status wave_attn_decode_tail(const wave_index* index, const void* q, int32_
  * output of the stream starting at seed + 0x9E3779B97F4A7C15*((b*2^32 + h) + 1),
  * mod n. Exactly k ids, in ascending order (not rank order), -1 padded.
  * Arguments, workspace (wave_attn_decode_plan) and errors as wave_attn_decode;
- * ARG if passes is outside [1, 4].
+ * ARG if passes is outside [1, 4]; UNSUPPORTED with 2^26 or more clusters per
+ * (sequence, kv head).
  */
 wave_status wave_attn_decode_stochastic(const wave_index* index, const void* q, int32_t n_q_heads, int32_t n_sink,
                                         int32_t n_local, double topk_frac, int32_t passes, uint64_t seed, float* out,

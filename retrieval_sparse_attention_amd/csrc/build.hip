@@ -36,10 +36,26 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // block: row of (b, g, t) = G * sum_{b'<b} M_b' + g * M_b + t - first[b] * seg_len,
 // which is the layout of the index's own rows for a whole dense build.
 struct BuildSeq : SeqArgs {
+  int32_t ident;  // 1: a whole dense build, where cluster F of the call is index cluster F
   int32_t first[MAXB];
 };
 
-__device__ inline int64_t nseg_of(const BuildSeq& sa, int b) { return (sa.N[b] + sa.seg_len - 1) / sa.seg_len; }
+// N_b < 2^31 and seg_len <= 2^16: the division fits 32 bits
+__device__ inline int64_t nseg_of(const BuildSeq& sa, int b) {
+  return (int64_t)(((uint32_t)sa.N[b] + (uint32_t)sa.seg_len - 1u) / (uint32_t)sa.seg_len);
+}
+
+// x / d and x % d for non-negative x, d > 0, in 32 bits when both fit
+__device__ inline void divmod64(int64_t x, int64_t d, int64_t& q, int64_t& r) {
+  if (((uint64_t)x | (uint64_t)d) < (1ull << 32)) {
+    const uint32_t qq = (uint32_t)x / (uint32_t)d;
+    q = qq;
+    r = (int64_t)((uint32_t)x - qq * (uint32_t)d);
+  } else {
+    q = x / d;
+    r = x % d;
+  }
+}
 
 struct Unit {
   int b, g, s;
@@ -67,9 +83,11 @@ __device__ inline Unit unit_of(const BuildSeq& sa, int64_t u) {
   }
   const SeqBase sb = seq_base(sa, b);
   const int64_t f = sa.first[b], nu = nseg_of(sa, b) - f, M = sb.N - f * sa.seg_len;
+  int64_t gq, sr;
+  divmod64(u, nu, gq, sr);
   r.b = b;
-  r.g = (int)(u / nu);
-  r.s = (int)(f + u % nu);
+  r.g = (int)gq;
+  r.s = (int)(f + sr);
   r.N = sb.N;
   r.C = sb.C;
   r.brow = sb.row + (int64_t)r.g * sb.NS;
@@ -104,9 +122,11 @@ __device__ inline CluRef clu_of(const BuildSeq& sa, int64_t F) {
   }
   const SeqBase sb = seq_base(sa, b);
   const int64_t f = sa.first[b], nc = sb.C - f * sa.K_s, M = sb.N - f * sa.seg_len;
-  const int g = (int)(F / nc);
+  int64_t gq, jr;
+  divmod64(F, nc, gq, jr);
+  const int g = (int)gq;
   CluRef r;
-  r.j = (int32_t)(f * sa.K_s + F % nc);
+  r.j = (int32_t)(f * sa.K_s + jr);
   r.N = sb.N;
   r.C = sb.C;
   r.brow = sb.row + (int64_t)g * sb.NS;
@@ -1135,9 +1155,12 @@ __global__ __launch_bounds__(256) void k_update(BuildSeq sa, int64_t nclu, const
   const int64_t Fc = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (Fc >= nclu) return;
+  // a whole dense build: the size load goes out before the block lookup, which then
+  // overlaps its latency
+  int n = sa.ident ? ix.sizes[Fc] : 0;
   const CluRef cr = clu_of(sa, Fc);
   const int64_t F = cr.gF;
-  const int n = ix.sizes[F];
+  if (!sa.ident) n = ix.sizes[F];
   if (n == 0) {
     if (FINAL && ix.vsum) *reinterpret_cast<float2*>(ix.vsum + F * D + 2 * lane) = make_float2(0.f, 0.f);
     if (FINAL && ix.vsum_bf16)
@@ -1315,6 +1338,7 @@ static void call_counts(const BuildSeq& bs, int64_t* units, int64_t* nclu) {
 static BuildSeq whole(const SeqArgs& sa) {
   BuildSeq bs;
   static_cast<SeqArgs&>(bs) = sa;
+  bs.ident = sa.cap == 0 ? 1 : 0;
   for (int b = 0; b < MAXB; ++b) bs.first[b] = 0;
   return bs;
 }
@@ -1368,6 +1392,7 @@ hipError_t launch_append(const SeqArgs& sa, const int32_t* n_old, const void* Kn
                          uint64_t seed, const wave_index& ix, const BuildWs& ws, void* stage_k, void* stage_v,
                          hipStream_t st) {
   BuildSeq bs = whole(sa);
+  bs.ident = 0;  // the call's clusters start at each sequence's first changed segment
   StageArgs a;
   a.B = sa.B;
   a.G = sa.G;

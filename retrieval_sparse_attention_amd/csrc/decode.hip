@@ -1179,22 +1179,28 @@ __global__ __launch_bounds__(TK_THREADS, PF ? 1 : 2 * TK_WAVES / 4) void k_topk(
 // The stochastic radix top-k (Vortex page, section 2.C: the top-k terminates early and
 // samples the rest of the selection from a threshold bin), an inexact variant of k_topk
 // with the same outputs (ids, spans, member prefix, counts, selection bitmap, steady
-// corrections); ids in ascending order. One workgroup per (sequence, q head); thread i
-// owns the clusters [i per, (i + 1) per), so scans over the threads run in id order.
-// Radix descent over the sortable keys, 8 bits a pass: an LDS histogram of the next
-// digit of the keys that share the prefix so far, and one wave scanning its 256 bins
-// from the top for the threshold bin; after da.sto_passes passes (fewer when the
-// threshold bin is needed whole) the bins above it are taken whole, and its members
-// by systematic sampling with a random phase: member r (in id order) of the n is
-// taken when floor((r m + c) / n) < floor(((r + 1) m + c) / n), m the ids still
-// missing, c = the first SplitMix64 output of the stream of (b, h) under the seed,
-// mod n. NK: keys a thread holds in registers (0: re-read from memory each pass).
+// corrections); ids in ascending order. One workgroup per (sequence, q head); wave w owns
+// the clusters [w 64 per, (w + 1) 64 per) and its lane l key slot i is cluster
+// w 64 per + 64 i + l, so loads are coalesced and id order is (wave, slot, lane): ranks in
+// id order come from ballots within a wave and one scan over the 16 waves.
+// Radix descent over the sortable keys, 8 bits a pass: a per-wave LDS histogram of the
+// next digit of the keys that share the prefix so far (in the first pass, where nearly all
+// keys share the top byte, a wave's equal digits are counted with one atomic), summed,
+// and one wave scanning its 256 bins from the top for the threshold bin. After
+// da.sto_passes passes (fewer when the threshold bin is needed whole) the bins above it
+// are taken whole and its members by systematic sampling with a random phase: member r
+// (in id order) of the n is taken when floor((r m + c) / n) < floor(((r + 1) m + c) / n),
+// i.e. (r m + c) mod n >= n - m, m the ids still missing, c = the first SplitMix64 output
+// of the stream of (b, h) under the seed, mod n (32-bit arithmetic: C < 2^26). The ids
+// go to the output in ascending order, then one pass over them, split over the threads,
+// writes spans, member prefixes and the bitmap. NK: key slots a lane holds in registers
+// (0: re-read from memory).
 template <int NK>
 __global__ __launch_bounds__(TK_THREADS) void k_topk_sto(SeqArgs sa, DecodeArgs da, wave_index ix, DecodeWs ws,
                                                          int32_t* __restrict__ sel_ids) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint64_t tmp[17];
+  __shared__ uint32_t hist[TK_WAVES][256];  // per wave, then the sum in hist[0]
   __shared__ int32_t res[4];
+  __shared__ int64_t wsum[3][TK_WAVES];     // per wave: eligible keys / bin members / selected (then scan space)
   const int bh = blockIdx.x;
   const int b = bh / da.H, h = bh % da.H, g = h / da.GS;
   const SeqBase sb = seq_base(sa, b);
@@ -1215,39 +1221,82 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_sto(SeqArgs sa, DecodeArgs 
   for (int i = 0; i < b; ++i) wbase += (int64_t)da.H * ((sa.C[i] + 31) >> 5);
   uint32_t* selw = ws.selw + wbase + (int64_t)h * nwords;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int per = (C + TK_THREADS - 1) / TK_THREADS;
-  const int j0 = min(tid * per, C), j1 = min(j0 + per, C), nmine = j1 - j0;
+  const uint64_t ltmask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int per = (C + TK_THREADS - 1) / TK_THREADS;  // key slots per lane
+  const int id0 = wv * 64 * per;
   uint32_t ur[NK > 0 ? NK : 1];
   if constexpr (NK > 0) {
 #pragma unroll
-    for (int i = 0; i < NK; ++i) ur[i] = i < nmine ? key32[j0 + i] : 0u;
+    for (int i = 0; i < NK; ++i) {
+      const int j = id0 + 64 * i + lane;
+      ur[i] = i < per && j < C ? key32[j] : 0u;
+    }
   }
-  // visit f(i, u) for every key the thread owns, in id order
+  // f(i, j, u) for every key slot of the lane, slots in order (uniform trip count; u = 0
+  // past the clusters)
   auto each = [&](auto&& f) {
     if constexpr (NK > 0) {
 #pragma unroll
       for (int i = 0; i < NK; ++i)
-        if (i < nmine) f(i, ur[i]);
+        if (i < per) f(i, id0 + 64 * i + lane, ur[i]);
     } else {
-      for (int i = 0; i < nmine; ++i) f(i, key32[j0 + i]);
+      for (int i = 0; i < per; ++i) {
+        const int j = id0 + 64 * i + lane;
+        f(i, j, j < C ? key32[j] : 0u);
+      }
     }
+  };
+  // sum of a per-wave value over the waves before this one, and over all (one sync)
+  auto wave_scan = [&](int slot, int64_t v, int64_t* total) {
+    if (lane == 0) wsum[slot][wv] = v;
+    __syncthreads();
+    int64_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < TK_WAVES; ++w) {
+      const int64_t x = wsum[slot][w];
+      before += w < wv ? x : 0;
+      all += x;
+    }
+    *total = all;
+    return before;
   };
   for (int i = tid; i < nwords; i += TK_THREADS) selw[i] = 0u;
   int ne = 0;
-  each([&](int, uint32_t u) { ne += u != 0u; });
-  uint64_t tot;
-  (void)block_scan_excl((uint64_t)ne, tmp, &tot);
-  const int k = min(da.kreq[b], (int)tot);
+  each([&](int, int, uint32_t u) { ne += __popcll(__ballot(u != 0u)); });
+  int64_t nE;
+  (void)wave_scan(0, ne, &nE);
+  const int k = (int)min((int64_t)da.kreq[b], nE);
   // 1. radix descent
   uint32_t P = 0u;
   int above = 0, done = 0;
   while (k > 0 && done < da.sto_passes && done < 4) {
-    if (tid < 256) hist[tid] = 0u;
+    for (int i = tid; i < TK_WAVES * 256; i += TK_THREADS) (&hist[0][0])[i] = 0u;
     __syncthreads();
     const int shift = 24 - 8 * done;
-    each([&](int, uint32_t u) {
-      if (u != 0u && (done == 0 || (u >> (shift + 8)) == P)) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+    const bool merge = done == 0;
+    each([&](int, int, uint32_t u) {
+      const bool valid = u != 0u && (done == 0 || (u >> (shift + 8)) == P);
+      const uint32_t d = (u >> shift) & 255u;
+      if (!merge) {
+        if (valid) atomicAdd(&hist[wv][d], 1u);
+        return;
+      }
+      uint64_t active = __ballot(valid);
+      while (active != 0ull) {
+        const int leader = __ffsll((unsigned long long)active) - 1;
+        const uint32_t dv = (uint32_t)__shfl((int)d, leader, 64);
+        const uint64_t same = __ballot(valid && d == dv);
+        if (lane == leader) atomicAdd(&hist[wv][dv], (uint32_t)__popcll(same));
+        active &= ~same;
+      }
     });
+    __syncthreads();
+    if (tid < 256) {
+      uint32_t t = 0u;
+#pragma unroll
+      for (int w = 0; w < TK_WAVES; ++w) t += hist[w][tid];
+      hist[0][tid] = t;
+    }
     __syncthreads();
     if (wv == 0) {
       // lane l holds bins 255 - 4l .. 252 - 4l; counts from the top as an inclusive scan
@@ -1255,7 +1304,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_sto(SeqArgs sa, DecodeArgs 
       int sum = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        c4[e] = hist[255 - 4 * lane - e];
+        c4[e] = hist[0][255 - 4 * lane - e];
         sum += (int)c4[e];
       }
       int incl = sum;
@@ -1287,61 +1336,63 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk_sto(SeqArgs sa, DecodeArgs 
     ++done;
     if (res[2]) break;
   }
-  // 2. the threshold bin's members in id order, and the sampling phase
+  // 2. the threshold bin's members: per wave in slot order, then over the waves
   const int fs = 32 - 8 * max(done, 1);
-  int nbo = 0;
-  each([&](int, uint32_t u) { nbo += u != 0u && (u >> fs) == P; });
-  uint64_t nbt;
-  const uint64_t rb = block_scan_excl((uint64_t)nbo, tmp, &nbt);
-  const uint64_t nb = nbt, mm = (uint64_t)(k - above);
+  int nbw = 0;
+  each([&](int, int, uint32_t u) { nbw += __popcll(__ballot(u != 0u && (u >> fs) == P)); });
+  int64_t nbt;
+  const int64_t rb = wave_scan(1, nbw, &nbt);
+  // sampling: member r is taken when (r m + c) mod n >= n - m, with n = nb, m = k - above.
+  // The wave tracks rem = (r0 m + c) mod n for its next member rank r0; a lane's member
+  // rank is r0 + t (t < 64), so (rem + t m) mod n decides in 32 bits (n < 2^26).
+  const uint32_t nb = (uint32_t)nbt, mm = (uint32_t)(k - above);
   const uint64_t c =
       nb > 0 ? sm64_mix(da.sto_seed + GAMMA * ((((uint64_t)(uint32_t)b << 32) | (uint32_t)h) + 1) + GAMMA) % nb : 0;
-  // 3. the selection: per thread its count and rows, then positions and member prefixes
-  // from one scan of (count << 40) + rows over the threads (ids in order)
-  uint64_t r = rb;
-  auto take = [&](uint32_t u) {
-    bool s = false;
-    if (k > 0 && u != 0u) {
-      const uint32_t p = u >> fs;
-      if (p > P) {
-        s = true;
-      } else if (p == P) {
-        s = (r * mm + c) / nb < ((r + 1) * mm + c) / nb;
-        ++r;
-      }
-    }
+  const uint32_t rem0 = nb > 0 ? (uint32_t)(((uint64_t)rb * mm + c) % nb) : 0u;
+  uint32_t rem = rem0;
+  auto take = [&](uint32_t u) {  // called for every slot in order by the whole wave
+    const bool member = u != 0u && (u >> fs) == P;
+    const uint64_t mb = __ballot(member);
+    const uint32_t t = (uint32_t)__popcll(mb & ltmask);
+    const bool s = k > 0 && u != 0u && ((u >> fs) > P || (member && (rem + t * mm) % nb >= nb - mm));
+    if (mb != 0ull) rem = (rem + (uint32_t)__popcll(mb) * mm) % nb;
     return s;
   };
-  uint64_t flags = 0ull, mine = 0ull;  // flags bit i: key j0 + i selected (NK > 0: per <= 64)
-  each([&](int i, uint32_t u) {
-    if (take(u)) {
-      if constexpr (NK > 0) flags |= 1ull << i;
-      mine += (1ull << 40) + (uint64_t)sizes[j0 + i];
-    }
+  // 3. the selection: its count per wave, the waves' bases, then the ids in ascending order
+  // into the output; spans, member prefixes and the bitmap from one parallel pass over them
+  int cnt_w = 0;
+  each([&](int, int, uint32_t u) { cnt_w += __popcll(__ballot(take(u))); });
+  int64_t kk;
+  int64_t pos = wave_scan(2, cnt_w, &kk);
+  rem = rem0;
+  each([&](int, int j, uint32_t u) {
+    const bool s = take(u);
+    const uint64_t sm = __ballot(s);
+    if (s) out[pos + __popcll(sm & ltmask)] = j;
+    pos += __popcll(sm);
   });
-  uint64_t all;
-  const uint64_t base = block_scan_excl(mine, tmp, &all);
-  int pos = (int)(base >> 40);
-  int32_t pre = (int32_t)(base & ((1ull << 40) - 1));
-  r = rb;  // keys re-read from memory: the same decisions again
-  each([&](int i, uint32_t u) {
-    bool s;
-    if constexpr (NK > 0) s = (flags >> i) & 1ull;
-    else s = take(u);
-    if (!s) return;
-    const int j = j0 + i;
+  __threadfence_block();
+  __syncthreads();
+  // entries [e0, e1) of the k per thread, in order
+  const int q = (k + TK_THREADS - 1) / TK_THREADS;
+  const int e0 = min(tid * q, k), e1 = min(e0 + q, k);
+  int64_t mine = 0;
+  for (int e = e0; e < e1; ++e)
+    mine += sizes[__hip_atomic_load(&out[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)];
+  uint64_t rows_all;
+  int64_t pre = (int64_t)block_scan_excl((uint64_t)mine, reinterpret_cast<uint64_t*>(&wsum[0][0]), &rows_all);
+  for (int e = e0; e < e1; ++e) {
+    const int j = __hip_atomic_load(&out[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int n = sizes[j];
-    out[pos] = j;
-    span[pos] = make_int2(offs[j], n);
-    selpre[pos] = pre;
-    atomicOr(&selw[j >> 5], 1u << (j & 31));
-    ++pos;
+    span[e] = make_int2(offs[j], n);
+    selpre[e] = (int32_t)pre;
     pre += n;
-  });
-  const int32_t rows = (int32_t)(all & ((1ull << 40) - 1));
+    atomicOr(&selw[j >> 5], 1u << (j & 31));
+  }
+  const int64_t tot_rows = (int64_t)rows_all;
   if (tid == 0) {
-    selpre[k] = rows;
-    ws.counts[4 * bh + 0] = rows;
+    selpre[k] = (int32_t)tot_rows;
+    ws.counts[4 * bh + 0] = (int32_t)tot_rows;
     ws.counts[4 * bh + 1] = k;
   }
   for (int i = k + tid; i < da.k_max; i += TK_THREADS) out[i] = -1;

@@ -616,6 +616,10 @@ wave_status wave_attn_decode_stochastic(const wave_index* index, const void* q, 
                                         int32_t* sel_ids, float* lse, void* ws, size_t ws_bytes,
                                         wave_stream_t stream) {
   if (passes < 1 || passes > 4) return fail(WAVE_ERR_ARG, "passes %d outside [1, 4]", passes);
+  if (index != nullptr && check_shape(&index->shape) == WAVE_OK && check_seg(index->seg_len, index->clusters_per_seg) == WAVE_OK)
+    for (int b = 0; b < index->shape.batch; ++b)
+      if (wave::num_clusters(index->shape.ctx[b], index->seg_len, index->clusters_per_seg) >= ((int64_t)1 << 26))
+        return fail(WAVE_ERR_UNSUPPORTED, "sequence %d has 2^26 or more clusters per kv head", b);
   return decode_call(index, q, n_q_heads, n_sink, n_local, topk_frac, out, sel_ids, lse, ws, ws_bytes, stream, 1, 0,
                      nullptr, nullptr, 0, nullptr, passes, seed);
 }
