@@ -121,9 +121,11 @@ def source_sha(files):
     return h.hexdigest()[:16]
 
 
-def counter_traffic(kernel, sha):
-    """HBM bytes per launch from a committed rocprofv3 counter summary, if it matches the source."""
-    path = os.path.join(ROOT, "profiles", "traffic_%s_128k.txt" % kernel)
+def counter_traffic(kernel, sha, tag="128k"):
+    """HBM bytes per launch from a committed rocprofv3 counter summary of workload `tag`, if it matches the
+    source."""
+    kernel = {"k_sort": "k_sort_radix"}.get(kernel, kernel)  # the launch name of the LDS radix sort
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.txt" % (kernel, tag))
     if not os.path.exists(path):
         return None
     vals = {}
@@ -206,38 +208,39 @@ def summarize_traffic(kernel, fdir, wdir, cfdir, cwdir, command):
 
 
 def summarize_mfma(kernel, d, command):
-    """MFMA utilisation of a kernel's dispatches: busy cycles of the matrix cores summed over the SIMDs
-    against the GPU's active cycles times the SIMD count, and the bf16 MFMA work the counters saw."""
+    """MFMA utilisation of a kernel's dispatches. On this GPU rocprofv3 reports one row per dispatch and
+    counter, summed over the chip: GRBM_GUI_ACTIVE over its 8 XCDs (so per-XCD cycles are a
+    dispatch's clock cycles, which against the dispatch's duration give the clock it ran at) and
+    SQ_VALU_MFMA_BUSY_CYCLES over its 1024 SIMDs. Busy fraction = busy cycles per SIMD over
+    per-XCD cycles; bf16 flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512."""
     per = {}
     for r in _csv_rows(d, "counter_collection.csv"):
         if _short(r["Kernel_Name"]).split("<")[0] != kernel:
             continue
-        key = r["Dispatch_Id"]
-        e = per.setdefault(key, {})
-        name = r["Counter_Name"]
-        v = float(r["Counter_Value"])
-        e[name] = max(e.get(name, 0.0), v) if name == "GRBM_GUI_ACTIVE" else e.get(name, 0.0) + v
+        e = per.setdefault(r["Dispatch_Id"], {})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        e["ns"] = float(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     if not per:
         raise SystemExit("no dispatch of %s in %s" % (kernel, d))
-    simds = 256 * 4
-    rows = []
-    for key, e in sorted(per.items(), key=lambda kv: int(kv[0])):
-        busy, gui = e.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0), e.get("GRBM_GUI_ACTIVE", 0.0)
-        mops = e.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0)
-        rows.append((busy, gui, mops * 512.0, busy / (gui * simds) if gui else float("nan")))
-    busy = sum(r[0] for r in rows) / len(rows)
-    gui = sum(r[1] for r in rows) / len(rows)
-    flops = sum(r[2] for r in rows) / len(rows)
+    xcds, simds = 8, 256 * 4
+    n = len(per)
+    mean = lambda key: sum(e.get(key, 0.0) for e in per.values()) / n
+    busy, gui, ns = mean("SQ_VALU_MFMA_BUSY_CYCLES"), mean("GRBM_GUI_ACTIVE") / xcds, mean("ns")
+    flops = mean("SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512.0
+    frac = busy / simds / gui
+    fpc = flops / gui
     print("\n".join([
         "# MFMA utilisation of %s (rocprofv3 --pmc, one dispatch at a time)" % kernel,
         "command: %s" % command,
-        "dispatches: %d" % len(rows),
-        "SQ_VALU_MFMA_BUSY_CYCLES per dispatch (sum over %d SIMDs): %.0f" % (simds, busy),
-        "GRBM_GUI_ACTIVE per dispatch (GPU cycles): %.0f" % gui,
-        "mfma_busy_fraction: %.4f" % (busy / (gui * simds)),
+        "dispatches: %d, mean duration %.1f us (profiled)" % (n, ns / 1000.0),
+        "GRBM_GUI_ACTIVE per dispatch: %.0f summed over %d XCDs = %.0f cycles per XCD (clock %.3f GHz)"
+        % (gui * xcds, xcds, gui, gui / ns),
+        "SQ_VALU_MFMA_BUSY_CYCLES per dispatch: %.0f summed over %d SIMDs = %.0f per SIMD" % (busy, simds, busy / simds),
+        "mfma_busy_fraction (per SIMD, of the dispatch's cycles): %.4f" % frac,
         "bf16 MFMA flops per dispatch (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512): %.4g" % flops,
-        "bf16 MFMA flops per GPU cycle: %.0f (peak 256 CUs x 4096 = 1048576)" % (flops / gui),
-        "per-dispatch busy fractions: %s" % " ".join("%.3f" % r[3] for r in rows[:16])]))
+        "bf16 MFMA flops per cycle: %.0f of 1048576 (256 CUs x 4096) = %.4f" % (fpc, fpc / 1048576.0),
+        "achieved over the profiled duration: %.1f TFLOP/s = %.4f of the 2.5 PFLOP/s peak (at 2.4 GHz)"
+        % (flops / ns / 1e3, flops / ns / 1e3 / BF16_PEAK_TFLOPS)]))
 
 
 SOURCES = ["retrieval_sparse_attention_amd/csrc/decode.hip", "retrieval_sparse_attention_amd/csrc/build.hip",
@@ -566,6 +569,7 @@ def measure(W, steps, warmup, eager, headline, dev):
     seg, K_s, iters = W["seg_len"], W["clusters_per_seg"], W["kmeans_iters"]
     ns, nl, frac, QPS = W["n_sink"], W["n_local"], W["topk_frac"], W["decode_queries_per_step"]
     L = W["layers"]
+    tag = next((k for k, v in WORKLOADS.items() if v["workload"] == W["workload"]), "")  # profiles/ file tag
     blocks = W.get("blocks", False)
     shared = W.get("shared", False)
     if isinstance(W["ctx"], list):  # ragged: N_b ~ U{lo..hi} from the data seed
@@ -773,32 +777,32 @@ def measure(W, steps, warmup, eager, headline, dev):
     kern = {}
     for name, (cnt, ms) in prof.items():
         kern[name] = {"launches": cnt, "avg_us": 1000.0 * ms / cnt, "total_ms": ms}
-    # the committed counter summaries are of the 128K workload
-    sha = source_sha(SOURCES) if headline else "not-the-128k-workload"
+    # committed counter summaries exist for the 128K and 1M workloads (profiles/traffic_<kernel>_<tag>.txt)
+    sha = source_sha(SOURCES)
     dom = max((k for k in kern if k in hbm_bytes or k == "k_assign"), key=lambda k: kern[k]["total_ms"])
     if dom == "k_assign":
         ach = assign_flops / (kern[dom]["avg_us"] * 1e-6) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": counter_traffic(dom, sha),
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": counter_traffic(dom, sha, tag),
                 "algorithmic_per_launch": assign_flops}
     else:
         per = hbm_bytes.get(dom)
         ach = per / (kern[dom]["avg_us"] * 1e-6) / 1e9 if per else None
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1) if ach else None, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4) if ach else None,
-                "traffic": counter_traffic(dom, sha), "algorithmic_per_launch": per}
+                "traffic": counter_traffic(dom, sha, tag), "algorithmic_per_launch": per}
     # every kernel's own roofline figure, for the record
     extra = {}
     for name, per in hbm_bytes.items():
         if name in kern:
             a = per / (kern[name]["avg_us"] * 1e-6) / 1e9
             extra[name] = {"bound": "hbm", "achieved_GBs": round(a, 1), "frac": round(a / HBM_PEAK_GBS, 4),
-                           "bytes_per_launch": int(per), "traffic": counter_traffic(name, sha)}
+                           "bytes_per_launch": int(per), "traffic": counter_traffic(name, sha, tag)}
     if "k_assign" in kern:
         a = assign_flops / (kern["k_assign"]["avg_us"] * 1e-6) / 1e12
         extra["k_assign"] = {"bound": "mfma", "achieved_TFLOPs": round(a, 1), "frac": round(a / BF16_PEAK_TFLOPS, 4),
                              "flops_per_launch": assign_flops, "hbm_bytes_per_launch": int(assign_bytes),
-                             "traffic": counter_traffic("k_assign", sha)}
+                             "traffic": counter_traffic("k_assign", sha, tag)}
 
     decodes = args.steps * QPS
     build_ms = sum(kern[k]["total_ms"] for k in kern if k not in ("k_score", "k_topk", "k_attend", "k_merge"))
