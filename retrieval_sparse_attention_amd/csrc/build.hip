@@ -57,6 +57,31 @@ __device__ inline void divmod64(int64_t x, int64_t d, int64_t& q, int64_t& r) {
   }
 }
 
+// Clusters of at least BIG_MEMBERS members, listed by the sort so that k_update starts their
+// waves first: a wave adds its cluster's members in order, so a large cluster that started
+// late would set the launch's end (a whole dense build only).
+constexpr int BIG_MEMBERS = 64;
+constexpr int BIG_CAP = 1024;
+struct BigList {
+  int32_t* cnt;    // [2]: clusters listed in the rounds of each parity
+  int32_t* ids;    // [2][BIG_CAP]
+  uint8_t* flag;   // [index clusters]: 1 if the cluster is in its round's list
+  int32_t parity;  // this round's
+};
+
+// the sort's note of cluster F (index id) of n members
+__device__ inline void big_note(const BuildSeq& sa, const BigList& bl, int64_t F, int32_t n) {
+  uint8_t in = 0;
+  if (sa.ident && n >= BIG_MEMBERS) {
+    const int i = atomicAdd(&bl.cnt[bl.parity], 1);
+    if (i < BIG_CAP) {
+      bl.ids[bl.parity * BIG_CAP + i] = (int32_t)F;
+      in = 1;
+    }
+  }
+  bl.flag[F] = in;
+}
+
 struct Unit {
   int b, g, s;
   int64_t row0;   // index row of the segment's first token
@@ -158,7 +183,8 @@ constexpr int INIT_THREADS = 1024;
 
 __global__ __launch_bounds__(INIT_THREADS) void k_init(BuildSeq sa, uint64_t seed, const uint16_t* __restrict__ K,
                                                        float* __restrict__ cent, uint16_t* __restrict__ chat,
-                                                       float* __restrict__ norm) {
+                                                       float* __restrict__ norm, BigList bl) {
+  if (blockIdx.x == 0 && threadIdx.x < 2) bl.cnt[threadIdx.x] = 0;  // the first round's lists
   extern __shared__ uint8_t smem[];
   const Unit U = unit_of(sa, blockIdx.x);
   uint16_t* idx = reinterpret_cast<uint16_t*>(smem);
@@ -820,7 +846,7 @@ constexpr int SORT_THREADS = 1024;
 
 __global__ __launch_bounds__(SORT_THREADS) void k_sort(BuildSeq sa, const int32_t* __restrict__ assign,
                                                        int32_t* __restrict__ rank, int32_t* __restrict__ sizes,
-                                                       int32_t* __restrict__ offsets, int32_t* __restrict__ perm) {
+                                                       int32_t* __restrict__ offsets, int32_t* __restrict__ perm, BigList bl) {
   extern __shared__ uint8_t smem[];
   const Unit U = unit_of(sa, blockIdx.x);
   const int Kc = U.Kc;
@@ -867,6 +893,7 @@ __global__ __launch_bounds__(SORT_THREADS) void k_sort(BuildSeq sa, const int32_
       run += x;
     }
     sizes[U.gclu + c] = run;
+    big_note(sa, bl, U.gclu + c, run);
     mysum += run;
   }
   // exclusive scan of mysum over threads
@@ -967,7 +994,7 @@ __device__ inline uint64_t block_scan_u64(uint64_t v, uint64_t* tmp, uint64_t* t
 __global__ __launch_bounds__(RS_THREADS) void k_sort_radix(BuildSeq sa, int parts, const int32_t* __restrict__ assign,
                                                            int32_t* __restrict__ sizes,
                                                            int32_t* __restrict__ offsets,
-                                                           int32_t* __restrict__ perm) {
+                                                           int32_t* __restrict__ perm, BigList bl) {
   extern __shared__ uint8_t smem[];
   const Unit U = unit_of(sa, blockIdx.x / parts);
   const int part = (int)(blockIdx.x % parts);
@@ -1108,6 +1135,7 @@ __global__ __launch_bounds__(RS_THREADS) void k_sort_radix(BuildSeq sa, int part
       if (part == 0 && c0 + r < Kc) {
         offsets[U.boff + U.cbase + c0 + r] = U.tok0 + off;
         sizes[U.gclu + c0 + r] = (int32_t)(v[r] >> 32);
+        big_note(sa, bl, U.gclu + c0 + r, (int32_t)(v[r] >> 32));
       }
       run += v[r];
     }
@@ -1136,7 +1164,10 @@ __global__ __launch_bounds__(RS_THREADS) void k_sort_radix(BuildSeq sa, int part
     first[c] = lo;
   }
   __syncthreads();
-  for (int c = tid; c < Kc; c += RS_THREADS) sizes[U.gclu + c] = first[c + 1] - first[c];
+  for (int c = tid; c < Kc; c += RS_THREADS) {
+    sizes[U.gclu + c] = first[c + 1] - first[c];
+    big_note(sa, bl, U.gclu + c, first[c + 1] - first[c]);
+  }
   if (tid == 0 && U.tok0 + U.L == U.N) offsets[U.boff + U.C] = U.N;
 }
 
@@ -1151,10 +1182,25 @@ __global__ __launch_bounds__(RS_THREADS) void k_sort_radix(BuildSeq sa, int part
 template <bool FINAL>
 __global__ __launch_bounds__(256) void k_update(BuildSeq sa, int64_t nclu, const uint16_t* __restrict__ K,
                                                 const uint16_t* __restrict__ V, wave_index ix,
-                                                float* __restrict__ norm) {
-  const int64_t Fc = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+                                                float* __restrict__ norm, BigList bl) {
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (Fc >= nclu) return;
+  if (blockIdx.x == 0 && threadIdx.x == 0) bl.cnt[bl.parity ^ 1] = 0;  // the next round's list
+  // a whole dense build: waves [0, BIG_CAP) take the sort's list of large clusters, the
+  // rest every cluster in order except those
+  int64_t Fc;
+  if (sa.ident) {
+    if (w < BIG_CAP) {
+      if (w >= min(bl.cnt[bl.parity], BIG_CAP)) return;
+      Fc = bl.ids[bl.parity * BIG_CAP + w];
+    } else {
+      Fc = w - BIG_CAP;
+      if (Fc >= nclu || bl.flag[Fc]) return;
+    }
+  } else {
+    Fc = w;
+    if (Fc >= nclu) return;
+  }
   // a whole dense build: the size load goes out before the block lookup, which then
   // overlaps its latency
   int n = sa.ident ? ix.sizes[Fc] : 0;
@@ -1175,9 +1221,20 @@ __global__ __launch_bounds__(256) void k_update(BuildSeq sa, int64_t nclu, const
   uint16_t* Vs = reinterpret_cast<uint16_t*>(ix.v_sorted) + cr.brow * D + 2 * lane;
   const int32_t* pb = ix.perm + cr.brow + off;
   float s0 = 0.f, s1 = 0.f, w0 = 0.f, w1 = 0.f;
+  // A wave's time is the chain of its chunks' loads, so the launch ends with the largest
+  // cluster's wave (615 members at 128K: 39 chunks). Before the last round each chunk's
+  // member positions are loaded one chunk ahead, so a chunk waits for its rows only, not
+  // for positions then rows (the last round, with V rows too, would lose occupancy).
+  int ptv_next = !FINAL && lane < min(n, 16) ? pb[lane] : 0;
   for (int k0 = 0; k0 < n; k0 += 16) {
     const int m = min(16, n - k0);
-    const int ptv = lane < m ? pb[k0 + lane] : 0;
+    int ptv;
+    if constexpr (FINAL) {
+      ptv = lane < m ? pb[k0 + lane] : 0;
+    } else {
+      ptv = ptv_next;
+      ptv_next = k0 + 16 + lane < n && lane < 16 ? pb[k0 + 16 + lane] : 0;
+    }
     // unconditional loads (clamped to the last member) keep all 16 in flight
     uint32_t kr[16], vr[16];
     int tt[16];
@@ -1229,7 +1286,8 @@ __global__ __launch_bounds__(256) void k_update(BuildSeq sa, int64_t nclu, const
 // per-block summaries built once, blocks scored and the top-k attended per query):
 // token i of a unit of L tokens and Kc clusters goes to block floor(i Kc / L), the
 // contiguous balanced blocks in the clusters' id space. One workgroup per unit.
-__global__ __launch_bounds__(1024) void k_block_assign(BuildSeq sa, int32_t* __restrict__ assign) {
+__global__ __launch_bounds__(1024) void k_block_assign(BuildSeq sa, int32_t* __restrict__ assign, BigList bl) {
+  if (blockIdx.x == 0 && threadIdx.x < 2) bl.cnt[threadIdx.x] = 0;  // the layout pass's list
   const Unit U = unit_of(sa, blockIdx.x);
   for (int i = threadIdx.x; i < U.L; i += blockDim.x)
     assign[U.row0 + i] = U.cbase + (int32_t)((int64_t)i * U.Kc / U.L);
@@ -1359,11 +1417,14 @@ static hipError_t run_build(const BuildSeq& bs, const uint16_t* K, const uint16_
   const size_t radix_lds = 2 * radix_tiles * RS_THREADS * 4;
   const unsigned cgrid = (unsigned)((nclu + 3) / 4);
   uint16_t* chat = reinterpret_cast<uint16_t*>(ix.centroids_bf16);
+  BigList bl{ws.big, ws.big + 2, reinterpret_cast<uint8_t*>(ws.big + 2 + 2 * BIG_CAP), 0};
   WAVE_TRY(launch("k_init", k_init, dim3((unsigned)units), dim3(INIT_THREADS), init_lds, st, bs, seed, K,
-                  ix.centroids, chat, ws.norm));
+                  ix.centroids, chat, ws.norm, bl));
   const int tpw = assign_tpw(bs, units);
   const int64_t agrid = assign_grid(bs, tpw);
+  const unsigned ugrid = cgrid + (bs.ident ? BIG_CAP / 4 : 0);
   for (int it = 0; it < iters; ++it) {
+    bl.parity = it & 1;
     WAVE_TRY(launch("k_assign", bs.K_s > AS_GROUP ? k_assign<true> : k_assign<false>, dim3((unsigned)agrid),
                     dim3(AS_THREADS), sizeof(AssignLds), st, bs, tpw, K, chat, ws.norm, ix.assign, ws.xn2,
                     it == 0 ? 1 : 0));
@@ -1372,12 +1433,12 @@ static hipError_t run_build(const BuildSeq& bs, const uint16_t* K, const uint16_
                               hipMemcpyDeviceToDevice, st));
     if (bs.seg_len <= RS_MAXL)
       WAVE_TRY(launch("k_sort", k_sort_radix, dim3((unsigned)(units * sparts)), dim3(RS_THREADS), radix_lds, st, bs,
-                      sparts, ix.assign, ix.sizes, ix.offsets, ix.perm));
+                      sparts, ix.assign, ix.sizes, ix.offsets, ix.perm, bl));
     else
       WAVE_TRY(launch("k_sort", k_sort, dim3((unsigned)units), dim3(SORT_THREADS), sort_lds, st, bs, ix.assign,
-                      ws.rank, ix.sizes, ix.offsets, ix.perm));
-    WAVE_TRY(launch("k_update", it + 1 < iters ? k_update<false> : k_update<true>, dim3(cgrid), dim3(256), 0, st, bs,
-                    nclu, K, V, ix, ws.norm));
+                      ws.rank, ix.sizes, ix.offsets, ix.perm, bl));
+    WAVE_TRY(launch("k_update", it + 1 < iters ? k_update<false> : k_update<true>, dim3(ugrid), dim3(256), 0, st, bs,
+                    nclu, K, V, ix, ws.norm, bl));
   }
   return hipSuccess;
 }
@@ -1434,16 +1495,18 @@ hipError_t launch_build_blocks(const SeqArgs& sa, const void* Kv, const void* Vv
   const size_t radix_tiles = ((size_t)(sa.seg_len + sparts - 1) / sparts + RS_THREADS - 1) / RS_THREADS;
   const size_t radix_lds = 2 * radix_tiles * RS_THREADS * 4;
   const unsigned cgrid = (unsigned)((nclu + 3) / 4);
-  WAVE_TRY(launch("k_block_assign", k_block_assign, dim3((unsigned)units), dim3(1024), 0, st, bs, ix.assign));
+  const BigList bl{ws.big, ws.big + 2, reinterpret_cast<uint8_t*>(ws.big + 2 + 2 * BIG_CAP), 0};
+  WAVE_TRY(launch("k_block_assign", k_block_assign, dim3((unsigned)units), dim3(1024), 0, st, bs, ix.assign, bl));
   // the layout pass of the k-means build over the block labels: counts, offsets, the
   // (identity) order, member means, bf16 centroids, value sums
   if (sa.seg_len <= RS_MAXL)
     WAVE_TRY(launch("k_sort", k_sort_radix, dim3((unsigned)(units * sparts)), dim3(RS_THREADS), radix_lds, st, bs,
-                    sparts, ix.assign, ix.sizes, ix.offsets, ix.perm));
+                    sparts, ix.assign, ix.sizes, ix.offsets, ix.perm, bl));
   else
     WAVE_TRY(launch("k_sort", k_sort, dim3((unsigned)units), dim3(SORT_THREADS), sort_lds, st, bs, ix.assign,
-                    ws.rank, ix.sizes, ix.offsets, ix.perm));
-  WAVE_TRY(launch("k_update", k_update<true>, dim3(cgrid), dim3(256), 0, st, bs, nclu, K, V, ix, ws.norm));
+                    ws.rank, ix.sizes, ix.offsets, ix.perm, bl));
+  WAVE_TRY(launch("k_update", k_update<true>, dim3(cgrid + (bs.ident ? BIG_CAP / 4 : 0)), dim3(256), 0, st, bs, nclu,
+                  K, V, ix, ws.norm, bl));
   return hipSuccess;
 }
 

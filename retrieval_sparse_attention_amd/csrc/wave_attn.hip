@@ -114,7 +114,7 @@ void index_sizes(const wave::SeqArgs& sa, wave_index_sizes* o) {
 // Build and append workspaces: the norms per index cluster; per input row the sort's
 // ranks and the keys' squared norms; an append also stages its input rows (K and V).
 struct BuildLayout {
-  size_t norm, rank, xn2, stage_k, stage_v, total;
+  size_t norm, rank, xn2, big, stage_k, stage_v, total;
 };
 
 BuildLayout build_layout(int64_t clusters, int64_t in_rows, bool stage) {
@@ -123,6 +123,7 @@ BuildLayout build_layout(int64_t clusters, int64_t in_rows, bool stage) {
   L.norm = o;  o += align256(sizeof(float) * (size_t)clusters);
   L.rank = o;  o += align256(sizeof(int32_t) * (size_t)in_rows);
   L.xn2 = o;   o += align256(sizeof(float) * (size_t)in_rows);
+  L.big = o;   o += align256(sizeof(int32_t) * (size_t)wave::BUILD_BIG_WORDS + (size_t)clusters);
   L.stage_k = L.stage_v = o;
   if (stage) {
     L.stage_k = o;  o += align256(2 * (size_t)WAVE_HEAD_DIM * (size_t)in_rows);
@@ -371,6 +372,7 @@ static wave::BuildWs carve_build(void* ws, const BuildLayout& L) {
   bw.norm = reinterpret_cast<float*>(w + L.norm);
   bw.rank = reinterpret_cast<int32_t*>(w + L.rank);
   bw.xn2 = reinterpret_cast<float*>(w + L.xn2);
+  bw.big = reinterpret_cast<int32_t*>(w + L.big);
   return bw;
 }
 
