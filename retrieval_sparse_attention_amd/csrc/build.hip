@@ -61,7 +61,7 @@ __device__ inline void divmod64(int64_t x, int64_t d, int64_t& q, int64_t& r) {
 // waves first: a wave adds its cluster's members in order, so a large cluster that started
 // late would set the launch's end (a whole dense build only).
 constexpr int BIG_MEMBERS = 64;
-constexpr int BIG_CAP = 1024;
+constexpr int BIG_CAP = BUILD_BIG_CAP;  // listed per round at most (the first waves of k_update)
 struct BigList {
   int32_t* cnt;    // [2]: clusters listed in the rounds of each parity
   int32_t* ids;    // [2][BIG_CAP]
@@ -69,17 +69,41 @@ struct BigList {
   int32_t parity;  // this round's
 };
 
-// the sort's note of cluster F (index id) of n members
-__device__ inline void big_note(const BuildSeq& sa, const BigList& bl, int64_t F, int32_t n) {
-  uint8_t in = 0;
+// A sorting workgroup stages its large clusters in LDS and takes their slots of the list
+// with one atomic (one per cluster on a single counter serialised: 21 -> 30 us a sort).
+constexpr int BIG_WG = 256;  // large clusters staged per sorting workgroup at most
+struct BigStage {
+  int32_t n;
+  int32_t id[BIG_WG];
+};
+
+// the sort's note of cluster F (index id) of n members: a large one is staged, any other
+// one's flag cleared (a staged one's is written by big_flush)
+__device__ inline void big_note(const BuildSeq& sa, const BigList& bl, BigStage& bs, int64_t F, int32_t n) {
   if (sa.ident && n >= BIG_MEMBERS) {
-    const int i = atomicAdd(&bl.cnt[bl.parity], 1);
-    if (i < BIG_CAP) {
-      bl.ids[bl.parity * BIG_CAP + i] = (int32_t)F;
-      in = 1;
+    const int i = atomicAdd(&bs.n, 1);
+    if (i < BIG_WG) {
+      bs.id[i] = (int32_t)F;
+      return;
     }
   }
-  bl.flag[F] = in;
+  bl.flag[F] = 0;
+}
+
+// one wave, after a barrier that follows every big_note of its workgroup: slots of the
+// round's list for the staged clusters, their ids and flags
+__device__ inline void big_flush(const BigList& bl, const BigStage& bs) {
+  const int lane = threadIdx.x & 63;
+  const int m = min(bs.n, BIG_WG);
+  int base = 0;
+  if (lane == 0 && m > 0) base = atomicAdd(&bl.cnt[bl.parity], m);
+  base = __shfl(base, 0, 64);
+  for (int i = lane; i < m; i += 64) {
+    const int p = base + i, F = bs.id[i];
+    const bool in = p < BIG_CAP;
+    if (in) bl.ids[bl.parity * BIG_CAP + p] = F;
+    bl.flag[F] = in ? 1 : 0;
+  }
 }
 
 struct Unit {
@@ -852,8 +876,10 @@ __global__ __launch_bounds__(SORT_THREADS) void k_sort(BuildSeq sa, const int32_
   const int Kc = U.Kc;
   int32_t* hist = reinterpret_cast<int32_t*>(smem);  // [16][Kc]
   __shared__ uint64_t scan[17];
+  __shared__ BigStage bs;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   for (int e = tid; e < 16 * Kc; e += SORT_THREADS) hist[e] = 0;
+  if (tid == 0) bs.n = 0;
   __syncthreads();
   const int span = (U.L + 15) / 16;
   const int w0 = min(wv * span, U.L), w1 = min(w0 + span, U.L);
@@ -893,7 +919,7 @@ __global__ __launch_bounds__(SORT_THREADS) void k_sort(BuildSeq sa, const int32_
       run += x;
     }
     sizes[U.gclu + c] = run;
-    big_note(sa, bl, U.gclu + c, run);
+    big_note(sa, bl, bs, U.gclu + c, run);
     mysum += run;
   }
   // exclusive scan of mysum over threads
@@ -917,6 +943,7 @@ __global__ __launch_bounds__(SORT_THREADS) void k_sort(BuildSeq sa, const int32_
       if (lane < 16) scan[lane] = tt - v0;
     }
     __syncthreads();
+    if (wv == 1) big_flush(bl, bs);
     int64_t run = (int64_t)(scan[wv] + x - (uint64_t)mysum);
     for (int c = c0; c < c1; ++c) {
       const int sz = sizes[U.gclu + c];
@@ -1006,7 +1033,9 @@ __global__ __launch_bounds__(RS_THREADS) void k_sort_radix(BuildSeq sa, int part
   __shared__ uint64_t scan[17];
   __shared__ int32_t first[WAVE_MAX_CLUSTERS_PER_SEG + 1];  // first sorted slot of cluster c (c <= Kc)
   __shared__ int32_t hist1[WAVE_MAX_CLUSTERS_PER_SEG];      // parts = 2: members of c in half 1
+  __shared__ BigStage bs;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid == 0) bs.n = 0;
   const uint64_t ltmask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int nbits = 0;
   while ((1 << nbits) < Kc) ++nbits;
@@ -1135,11 +1164,12 @@ __global__ __launch_bounds__(RS_THREADS) void k_sort_radix(BuildSeq sa, int part
       if (part == 0 && c0 + r < Kc) {
         offsets[U.boff + U.cbase + c0 + r] = U.tok0 + off;
         sizes[U.gclu + c0 + r] = (int32_t)(v[r] >> 32);
-        big_note(sa, bl, U.gclu + c0 + r, (int32_t)(v[r] >> 32));
+        big_note(sa, bl, bs, U.gclu + c0 + r, (int32_t)(v[r] >> 32));
       }
       run += v[r];
     }
     __syncthreads();  // first[] and hist1[] are read
+    if (part == 0 && wv == 0) big_flush(bl, bs);
 #pragma unroll
     for (int r = 0; r < 2; ++r)
       if (c0 + r < Kc) first[c0 + r] = delta[r];
@@ -1166,9 +1196,11 @@ __global__ __launch_bounds__(RS_THREADS) void k_sort_radix(BuildSeq sa, int part
   __syncthreads();
   for (int c = tid; c < Kc; c += RS_THREADS) {
     sizes[U.gclu + c] = first[c + 1] - first[c];
-    big_note(sa, bl, U.gclu + c, first[c + 1] - first[c]);
+    big_note(sa, bl, bs, U.gclu + c, first[c + 1] - first[c]);
   }
   if (tid == 0 && U.tok0 + U.L == U.N) offsets[U.boff + U.C] = U.N;
+  __syncthreads();
+  if (wv == 0) big_flush(bl, bs);
 }
 
 // ------------------------------------------------------------------ k_update

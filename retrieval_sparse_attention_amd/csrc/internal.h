@@ -84,10 +84,11 @@ struct BuildWs {
   float* norm;        // [index clusters] |chat_j|^2 (fp32) of the current round
   int32_t* rank;      // [input rows] scratch of the counting sort
   float* xn2;         // [input rows] |x|^2 of every key (written by the first k_assign round)
-  int32_t* big;       // the sort's lists of large clusters: 2 counters, 2 x 1024 ids, then a byte per
-                      // index cluster (BUILD_BIG_WORDS + clusters bytes)
+  int32_t* big;       // the sort's lists of large clusters: 2 counters, 2 x BUILD_BIG_CAP ids, then a
+                      // byte per index cluster (BUILD_BIG_WORDS + clusters bytes)
 };
-constexpr int64_t BUILD_BIG_WORDS = 2 + 2 * 1024;
+constexpr int BUILD_BIG_CAP = 4096;
+constexpr int64_t BUILD_BIG_WORDS = 2 + 2 * (int64_t)BUILD_BIG_CAP;
 
 hipError_t launch_build(const SeqArgs& sa, const void* K, const void* V, int32_t iters, uint64_t seed,
                         const wave_index& ix, const BuildWs& ws, int32_t* trace, int64_t rows, hipStream_t st);
