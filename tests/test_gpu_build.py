@@ -133,6 +133,15 @@ def _sampled_units(name, K, V, G, ctx, seg, K_s, iters, seed, sample):
             assert np.array_equal(got["sizes"][clu:clu + C[b]], np.bincount(a, minlength=C[b]))
             row += N
             clu += C[b]
+    # the whole layout of the final assignment, every cluster: the oracle's layout and update
+    # of the GPU's assignments (the last update pass took every cluster exactly once, in
+    # whatever order it started them); an empty cluster keeps its centroid, not compared
+    lay = oracle.index_from_assign(K, V, G, ctx, seg, K_s, seed, got["assign"])
+    for f in ("perm", "inv_perm", "offsets", "sizes", "k_sorted", "v_sorted"):
+        assert np.array_equal(got[f], getattr(lay, f)), "%s differs from the oracle's layout" % f
+    nz = lay.sizes > 0
+    for f in ("centroids", "centroids_bf16", "vsum"):
+        assert np.array_equal(got[f][nz], getattr(lay, f)[nz]), "%s of a non-empty cluster differs" % f
     # sampled units bit-exact
     nseg = [-(-int(n) // seg) for n in ctx]
     units = []
