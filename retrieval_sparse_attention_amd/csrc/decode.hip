@@ -758,6 +758,9 @@ __global__ __launch_bounds__(TK_THREADS, PF ? 1 : 2 * TK_WAVES / 4) void k_topk(
   int Ew = 0;
   uint32_t tw = 0u;
   uint32_t lmax = 0u;
+  // keys read from memory: chunk t's summary record (its largest keys, then its eligible
+  // count) in thread t's registers, both words loaded at once for the threshold below
+  uint4 crec[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
   if constexpr (INREG) {
 #pragma unroll
     for (int v = 0; v < NVR; ++v) {
@@ -774,8 +777,12 @@ __global__ __launch_bounds__(TK_THREADS, PF ? 1 : 2 * TK_WAVES / 4) void k_topk(
     // eligible keys from k_score's chunk summaries (thread t adds chunks t, t + TK_THREADS, ...)
     const int nch = (C + SC - 1) / SC;
     const uint32_t* ct = ws.ctop + bhs * (da.NP - da.P) * 8;
-    int e = 0;
-    for (int i = tid; i < nch; i += nt) e += (int)ct[(int64_t)i * 8 + DEC_CHUNK_TOPS];
+    if (tid < nch) {
+      crec[0] = reinterpret_cast<const uint4*>(ct)[2 * tid];
+      crec[1] = reinterpret_cast<const uint4*>(ct)[2 * tid + 1];
+    }
+    int e = (int)crec[1].w;
+    for (int i = tid + nt; i < nch; i += nt) e += (int)ct[(int64_t)i * 8 + DEC_CHUNK_TOPS];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) e += __shfl_xor(e, o, 64);
     Ew = e;
@@ -909,7 +916,7 @@ __global__ __launch_bounds__(TK_THREADS, PF ? 1 : 2 * TK_WAVES / 4) void k_topk(
     if (k > 0 && k <= DEC_CHUNK_TOPS * nch && nch <= TK_THREADS) {
       uint32_t tv[DEC_CHUNK_TOPS];
 #pragma unroll
-      for (int r = 0; r < DEC_CHUNK_TOPS; ++r) tv[r] = tid < nch ? ct[(int64_t)tid * 8 + r] : 0u;
+      for (int r = 0; r < DEC_CHUNK_TOPS; ++r) tv[r] = r < 4 ? crec[0][r] : crec[1][r - 4];
       // t = the k-th largest of them (zeros included): a radix select, 8 bits a pass from
       // the top; a wave counts equal digits by matching the 8 digit bits with ballots and
       // the lowest lane of each match adds the count (one LDS atomic per distinct digit)
@@ -1015,12 +1022,40 @@ __global__ __launch_bounds__(TK_THREADS, PF ? 1 : 2 * TK_WAVES / 4) void k_topk(
             bitonic_desc_reg<4>(cb, P2);
           else
             bitonic_desc_lds(cb, P2);
-          // (key desc, id asc): the first k are the selection in rank order
-          for (int r = tid; r < k; r += nt) {
-            const int id = (int)(0xFFFFFFFFu - (uint32_t)(cb[r] & 0xFFFFFFFFu));
-            out[r] = id;
-            span[r] = make_int2(offs[id], sizes[id]);
-            atomicOr(&selw[id >> 5], 1u << (id & 31));
+          // (key desc, id asc): the first k are the selection in rank order. Thread t takes
+          // ranks [t R, (t + 1) R) (R <= 4) and keeps their sizes for the member-count prefix
+          const int R = (k + nt - 1) / nt;
+          const int q0 = min(tid * R, k), q1 = min(q0 + R, k);
+          int nn[TK_SORT / TK_THREADS];
+          int64_t msum = 0;
+#pragma unroll
+          for (int u = 0; u < TK_SORT / TK_THREADS; ++u) {
+            const int r = q0 + u;
+            nn[u] = 0;
+            if (r < q1) {
+              const int id = (int)(0xFFFFFFFFu - (uint32_t)(cb[r] & 0xFFFFFFFFu));
+              const int n = sizes[id];
+              out[r] = id;
+              span[r] = make_int2(offs[id], n);
+              atomicOr(&selw[id >> 5], 1u << (id & 31));
+              nn[u] = n;
+              msum += n;
+            }
+          }
+          uint64_t tot;
+          int64_t run = (int64_t)block_scan_excl((uint64_t)msum, L.scan, &tot);
+          int32_t* selpre = ws.selpre + kbase + bh;
+#pragma unroll
+          for (int u = 0; u < TK_SORT / TK_THREADS; ++u) {
+            const int r = q0 + u;
+            if (r < q1) {
+              selpre[r] = (int32_t)run;
+              run += nn[u];
+            }
+          }
+          if (tid == 0) {
+            selpre[k] = (int32_t)tot;
+            ws.counts[4 * bh + 0] = (int32_t)tot;
           }
           done = true;
         }
@@ -1120,7 +1155,7 @@ __global__ __launch_bounds__(TK_THREADS, PF ? 1 : 2 * TK_WAVES / 4) void k_topk(
   }
 
   // 4. member-count prefix of the general path's selection, counts
-  if (!fast) {
+  if (!fast && !done) {
     int32_t* selpre = ws.selpre + kbase + bh;
     __threadfence_block();
     __syncthreads();
