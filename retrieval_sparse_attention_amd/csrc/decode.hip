@@ -648,9 +648,9 @@ struct TopkLds {
   uint32_t bis[34];             // block counts of the bisection, then of keys above T
   uint32_t rhist[2][256];       // digit counts of the radix select over the chunks' top keys
   uint32_t rsel[2];             // its digit and the count above it
-  int32_t wE[16];
-  uint32_t wt[16];
-  int32_t tcnt[16];             // keys >= wt[i] over the workgroup
+  alignas(16) int32_t wE[16];   // read as vectors: four reads, not a chain of sixteen
+  alignas(16) uint32_t wt[16];
+  alignas(16) int32_t tcnt[16]; // keys >= wt[i] over the workgroup
   int32_t misc[8];
 };
 
@@ -796,13 +796,24 @@ __global__ __launch_bounds__(TK_THREADS, PF ? 1 : 2 * TK_WAVES / 4) void k_topk(
     L.wt[wv] = tw;
   }
   lds_barrier();
+  // every wave's eligible count and threshold, into registers by vector reads
+  static_assert(TK_WAVES % 4 == 0 && TK_WAVES <= 16, "per-wave values read four at a time");
+  uint32_t wtr[TK_WAVES];
   int nE = 0;
   uint32_t X = 0xFFFFFFFFu;
 #pragma unroll
-  for (int i = 0; i < TK_WAVES; ++i) {
-    nE += L.wE[i];
-    X = min(X, L.wt[i]);
+  for (int q4 = 0; q4 < TK_WAVES / 4; ++q4) {
+    const int4 e4 = reinterpret_cast<const int4*>(L.wE)[q4];
+    const uint4 t4 = reinterpret_cast<const uint4*>(L.wt)[q4];
+    nE += e4.x + e4.y + e4.z + e4.w;
+    // uniform values: scalar registers
+    wtr[4 * q4 + 0] = __builtin_amdgcn_readfirstlane(t4.x);
+    wtr[4 * q4 + 1] = __builtin_amdgcn_readfirstlane(t4.y);
+    wtr[4 * q4 + 2] = __builtin_amdgcn_readfirstlane(t4.z);
+    wtr[4 * q4 + 3] = __builtin_amdgcn_readfirstlane(t4.w);
   }
+#pragma unroll
+  for (int i = 0; i < TK_WAVES; ++i) X = min(X, wtr[i]);
   const int k = min(kreq, nE);
   if constexpr (INREG) {
     if (k > 0 && k == kreq && X > 0u) {
@@ -810,16 +821,19 @@ __global__ __launch_bounds__(TK_THREADS, PF ? 1 : 2 * TK_WAVES / 4) void k_topk(
       int mine = 0;
 #pragma unroll
       for (int i = 0; i < TK_WAVES; ++i) {
-        const int cnt = __popcll(__ballot(lmax >= L.wt[i]));
+        const int cnt = __popcll(__ballot(lmax >= wtr[i]));
         mine = (lane == i) ? cnt : mine;
       }
       if (lane < TK_WAVES) atomicAdd(&L.tcnt[lane], mine);
       lds_barrier();
+      // the counts by vector reads (a loop of scalar reads became a chain of round trips)
 #pragma unroll
-      for (int i = 0; i < TK_WAVES; ++i) {
-        const int tc = L.tcnt[i];  // both read unconditionally: no serial LDS round trips
-        const uint32_t ti = L.wt[i];
-        X = tc >= k ? max(X, ti) : X;
+      for (int q4 = 0; q4 < TK_WAVES / 4; ++q4) {
+        const int4 c4 = reinterpret_cast<const int4*>(L.tcnt)[q4];
+        X = c4.x >= k ? max(X, wtr[4 * q4 + 0]) : X;
+        X = c4.y >= k ? max(X, wtr[4 * q4 + 1]) : X;
+        X = c4.z >= k ? max(X, wtr[4 * q4 + 2]) : X;
+        X = c4.w >= k ? max(X, wtr[4 * q4 + 3]) : X;
       }
     }
   }
@@ -875,12 +889,19 @@ __global__ __launch_bounds__(TK_THREADS, PF ? 1 : 2 * TK_WAVES / 4) void k_topk(
         const uint64_t c = ((uint64_t)ri.y << 32) | ri.x;
         const int j0 = nc * part / P, j1 = nc * (part + 1) / P;  // nc <= 1024: no overflow
         int rank = 0, pre = 0;
-#pragma unroll 8
-        for (int j = j0; j < j1; ++j) {
+        auto count = [&](int j) {
           const uint4 rj = L.u.c.rec[j];
           const bool gt = (((uint64_t)rj.y << 32) | rj.x) > c;
           rank += gt;
           pre += (int)(rj.z & (0u - (uint32_t)gt));
+        };
+        // 16 records a batch of LDS reads (8 in the 64-register variant)
+        if constexpr (PF) {
+#pragma unroll 16
+          for (int j = j0; j < j1; ++j) count(j);
+        } else {
+#pragma unroll 8
+          for (int j = j0; j < j1; ++j) count(j);
         }
         atomicAdd(&L.u.c.rank[i], rank);
         atomicAdd(&L.u.c.pre[i], pre);
