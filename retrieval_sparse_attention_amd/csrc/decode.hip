@@ -295,6 +295,15 @@ __device__ void est_role(const SeqArgs& sa, const DecodeArgs& da, const wave_ind
   float kr[GS];
 #pragma unroll
   for (int hh = 0; hh < GS; ++hh) kr[hh] = kb[(int64_t)hh * C + jc];
+  // the q heads' selections (k_topk's bitmaps): a selected cluster is attended row by row;
+  // loaded before the value sums, so that the weights need not wait for those
+  int64_t wb = 0;
+  for (int i = 0; i < b; ++i) wb += (int64_t)da.H * ((sa.C[i] + 31) >> 5);
+  const int nwords = (C + 31) >> 5, jw = j0 + jc;
+  uint32_t selb[GS];
+#pragma unroll
+  for (int hh = 0; hh < GS; ++hh)
+    selb[hh] = (ws.selw[wb + (int64_t)(g * GS + hh) * nwords + (jw >> 5)] >> (jw & 31)) & 1u;
   float4 vreg[SC / 8];
   if (ix.vsum_bf16 != nullptr) {
     // bf16 value sums (half the bytes), widened exactly
@@ -317,14 +326,6 @@ __device__ void est_role(const SeqArgs& sa, const DecodeArgs& da, const wave_ind
       vreg[u] = *reinterpret_cast<const float4*>(vsrc + off);
     }
   }
-  // the q heads' selections (k_topk's bitmaps): a selected cluster is attended row by row
-  int64_t wb = 0;
-  for (int i = 0; i < b; ++i) wb += (int64_t)da.H * ((sa.C[i] + 31) >> 5);
-  const int nwords = (C + 31) >> 5, jw = j0 + jc;
-  uint32_t selb[GS];
-#pragma unroll
-  for (int hh = 0; hh < GS; ++hh)
-    selb[hh] = (ws.selw[wb + (int64_t)(g * GS + hh) * nwords + (jw >> 5)] >> (jw & 31)) & 1u;
   float sv[GS];
   if (tid < SC) {
 #pragma unroll
