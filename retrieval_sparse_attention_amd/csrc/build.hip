@@ -10,10 +10,12 @@
 //   iters x { k_assign       nearest centroid on bf16 MFMA (32x32x16), fp32, and the
 //                            binary64 decision where fp32 cannot separate the two best
 //             k_sort         stable counting sort of each unit by cluster (LSD radix in LDS
-//                            for segments of at most 16384 tokens)
+//                            for segments of at most 16384 tokens); lists the round's
+//                            large clusters
 //             k_update       ordered fp32 member sums, correctly rounded means, bf16
-//                            centroids and norms; the last round also writes the
-//                            sorted K/V, inv_perm and the ordered fp32 value sums }
+//                            centroids and norms, the listed clusters' waves first; the
+//                            last round also writes the sorted K/V, inv_perm and the
+//                            ordered fp32 value sums }
 #include <math.h>
 
 #include <algorithm>
