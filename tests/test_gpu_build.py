@@ -65,6 +65,16 @@ def test_long_segments_general_sort():
     _check_all("seg=20000", K, V, 1, ctx, 20000, 64, 2, 13)
 
 
+def test_large_cluster_list_overflow():
+    # 16 segments of 65536 tokens with 512 clusters each (128 members on average): more than
+    # the 256 large clusters a sorting workgroup stages (up to ~350 of 64 or more members in a
+    # segment) and more than the 4096 entries of the update's list (over 5000 in all), so some
+    # large clusters run in the plain order; every array of both rounds bit-exact
+    ctx = [262144]
+    K, V, _ = synth.kv(28, 1, 4, np.array(ctx), 65536)
+    _check_all("large-cluster list overflow", K, V, 4, ctx, 65536, 512, 2, 29)
+
+
 def test_duplicate_keys_and_ties():
     # many identical keys: exact distance ties go to the lowest id (binary64 decision path)
     ctx = [2048]
