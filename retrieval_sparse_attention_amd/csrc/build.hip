@@ -201,10 +201,10 @@ __device__ __forceinline__ uint64_t seed_key(int b, int g, int s) {
 
 // One workgroup per unit. The i-th SplitMix64 draw of the unit with key k is
 // mix(seed + GAMMA*(k+1) + GAMMA*(i+1)); the draws do not depend on the
-// shuffle, so they are taken in parallel and one lane then performs the K(s)
-// swaps of the partial Fisher-Yates shuffle of [0, L) held in LDS (16-bit
-// entries). Centroid i becomes the fp32 copy of key row idx[i]; its bf16
-// rounding is the key itself and its squared norm is summed here too.
+// shuffle, so they are taken in parallel, and so is the outcome of the K(s)
+// swaps of the partial Fisher-Yates shuffle of [0, L) (below). Centroid i
+// becomes the fp32 copy of key row idx[i]; its bf16 rounding is the key itself
+// and its squared norm is summed here too.
 constexpr int INIT_THREADS = 1024;
 
 __global__ __launch_bounds__(INIT_THREADS) void k_init(BuildSeq sa, uint64_t seed, const uint16_t* __restrict__ K,
@@ -213,22 +213,67 @@ __global__ __launch_bounds__(INIT_THREADS) void k_init(BuildSeq sa, uint64_t see
   if (blockIdx.x == 0 && threadIdx.x < 2) bl.cnt[threadIdx.x] = 0;  // the first round's lists
   extern __shared__ uint8_t smem[];
   const Unit U = unit_of(sa, blockIdx.x);
-  uint16_t* idx = reinterpret_cast<uint16_t*>(smem);
-  int32_t* jsel = reinterpret_cast<int32_t*>(smem + ((2 * (size_t)U.L + 15) & ~(size_t)15));
+  // LDS (all of it dynamic: the attribute allows the whole 160 KB): the pair count, the
+  // draws, the (position, step) pairs a chain can meet, two bitmaps over the positions
+  // (drawn at least once, more than once), the chosen rows (16-bit)
+  const int Kc = U.Kc, nbw = (U.L + 31) >> 5;
+  int32_t& ntab = *reinterpret_cast<int32_t*>(smem);
+  int32_t* jsel = reinterpret_cast<int32_t*>(smem + 16);
+  int2* tab = reinterpret_cast<int2*>(jsel + ((Kc + 3) & ~3));
+  uint32_t* seen1 = reinterpret_cast<uint32_t*>(tab + Kc);
+  uint32_t* seen2 = seen1 + nbw;
+  uint16_t* idx = reinterpret_cast<uint16_t*>(seen2 + nbw);
   const uint64_t st0 = seed + GAMMA * (seed_key(U.b, U.g, U.s) + 1);
-  for (int i = threadIdx.x; i < U.L; i += blockDim.x) idx[i] = (uint16_t)i;
-  for (int i = threadIdx.x; i < U.Kc; i += blockDim.x) {
+  for (int i = threadIdx.x; i < nbw; i += blockDim.x) {
+    seen1[i] = 0u;
+    seen2[i] = 0u;
+  }
+  if (threadIdx.x == 0) ntab = 0;
+  for (int i = threadIdx.x; i < Kc; i += blockDim.x) {
     const uint64_t r = sm64_mix(st0 + GAMMA * (uint64_t)(i + 1));
     jsel[i] = i + (int32_t)(r % (uint64_t)(U.L - i));
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int i = 0; i < U.Kc; ++i) {
-      const int j = jsel[i];
-      const uint16_t a = idx[i];
-      idx[i] = idx[j];
-      idx[j] = a;
+  // The swaps, all positions at once. Step i swaps positions i and jsel[i] >= i, so position
+  // t < Kc is final after step t and holds what position jsel[t] held just before it: jsel[t]
+  // itself unless an earlier step s drew it too (jsel[s] == jsel[t]); then, for the last such
+  // s, what position s held just before step s, found the same way (a position below Kc that
+  // an earlier step drew). Such chains need a position drawn twice: the positions drawn more
+  // than once are marked, the draws on them and on positions below Kc (the only draws a chain
+  // can meet) listed, and a thread follows its positions' chains through that short list.
+  for (int i = threadIdx.x; i < Kc; i += blockDim.x) {
+    const int j = jsel[i];
+    const uint32_t bit = 1u << (j & 31);
+    if (atomicOr(&seen1[j >> 5], bit) & bit) atomicOr(&seen2[j >> 5], bit);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < Kc; i += blockDim.x) {
+    const int j = jsel[i];
+    if (j < Kc || ((seen2[j >> 5] >> (j & 31)) & 1u)) {
+      tab[atomicAdd(&ntab, 1)] = make_int2(j, i);
     }
+  }
+  __syncthreads();
+  const int nt = ntab;
+  for (int t = threadIdx.x; t < Kc; t += blockDim.x) {
+    int p = jsel[t], cur = t;
+    if ((seen2[p >> 5] >> (p & 31)) & 1u) {
+      for (;;) {
+        int s = -1;  // the last step before cur that drew p
+        for (int e0 = 0; e0 < nt; e0 += 8) {
+          int2 pr[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) pr[u] = tab[min(e0 + u, nt - 1)];  // repeats are harmless
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (pr[u].x == p && pr[u].y < cur && pr[u].y > s) s = pr[u].y;
+        }
+        if (s < 0) break;
+        p = s;
+        cur = s;
+      }
+    }
+    idx[t] = (uint16_t)p;
   }
   __syncthreads();
   // (centroid i, 16-byte chunk c): 16 lanes per centroid, 8 rows in flight per thread
@@ -1443,7 +1488,9 @@ static hipError_t run_build(const BuildSeq& bs, const uint16_t* K, const uint16_
   int64_t units, nclu;
   call_counts(bs, &units, &nclu);
   if (units == 0) return hipSuccess;
-  const size_t init_lds = ((2 * (size_t)bs.seg_len + 15) & ~(size_t)15) + 4 * (size_t)bs.K_s;
+  // k_init: count, draws and pairs (12 B per cluster), two position bitmaps, 16-bit rows
+  const size_t init_lds = 16 + 4 * (((size_t)bs.K_s + 3) & ~(size_t)3) + 10 * (size_t)bs.K_s +
+                          8 * (((size_t)bs.seg_len + 31) / 32);
   const size_t sort_lds = 16 * (size_t)bs.K_s * 4;
   // two key buffers of E tiles; the counters (32 digits x E tiles x 16 waves) fit in one
   const int sparts = sort_parts(units, di.cus);
