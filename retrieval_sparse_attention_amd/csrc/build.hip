@@ -9,6 +9,8 @@
 //   k_init                   seeded choice of K(s) tokens per unit (bf16 centroids, norms)
 //   iters x { k_assign       nearest centroid on bf16 MFMA (32x32x16), fp32, and the
 //                            binary64 decision where fp32 cannot separate the two best
+//                            (k_assign_lds: centroids resident in LDS, up to 512 per
+//                            segment; k_assign<true>: groups of 512 from registers)
 //             k_sort         stable counting sort of each unit by cluster (LSD radix in LDS
 //                            for segments of at most 16384 tokens); lists the round's
 //                            large clusters
@@ -907,6 +909,382 @@ __global__ __launch_bounds__(AS_THREADS, 1) void k_assign(BuildSeq sa, int tpw, 
   }
 }
 
+// ------------------------------------------------------------------ k_assign_lds
+// Units of at most 512 clusters. The unit's bf16 centroids stay in LDS for the whole
+// launch (128 KB at 512 clusters, chunk-major: 16-byte chunk c of row j at slot 512 c + j, so
+// an A fragment read covers two runs of 32 consecutive slots, and a block's reads differ by
+// constant offsets) and every wave owns its tokens
+// outright: 64 at a time (two 32-token blocks, their B fragments loaded from memory into
+// registers), run against each 32-row block of centroids in turn (A fragments and the
+// accumulator start -|c_j|^2/2 read from LDS, each A fragment serving both token
+// blocks), the best and second best folded in on the way. No token meets another wave's
+// results, so the main loop has no barrier; eight waves, two per SIMD, cover each other's
+// load latency and vector-ALU work. Block r of centroids runs on the matrix core while the
+// vector ALU selects over block r - 1 (two accumulator sets), and block r + 1's A fragments
+// are read from LDS as block r's MFMAs free their registers.
+//
+// Selection: a value's position i (0..15) among the lane's 16 results of a block goes into
+// its low 4 mantissa bits (moving it by less than 2^-19 |f|), the block's best and second
+// best come from a tournament of triples against the running pair, and the block of the
+// running best is kept beside it. The margin test and the exact binary64 decision of the
+// tokens it cannot separate are the same as in k_assign (the packing error here is smaller).
+constexpr int AL_WAVES = 8;
+constexpr int AL_THREADS = 64 * AL_WAVES;
+constexpr int AL_TPG = 64;  // tokens per wave group
+constexpr int AL_MAXC = AS_GROUP;
+
+struct AssignLdsL {
+  float nh[AL_MAXC];                 // -|c_j|^2 / 2; padding rows -FLT_MAX
+  u32x4 cent[16 * AL_MAXC];          // the unit's bf16 centroids, chunk c of row j at 512 c + j
+                                     // (rows up to a multiple of 64 zero)
+  uint32_t nearw[AS_MAXTPW / 32];    // near-tie flags of the range's tokens
+  u32x4 rows[32 * 16];               // exact decision: the batch's rows (slot t*16 + (c ^ (t & 15)))
+  float red[AL_WAVES][32];           // exact decision: per wave the best fp32 value of each token
+  unsigned long long fd[32];         // exact decision: per token the least D_j (bits), then its id
+  int32_t fj[32];
+  int32_t flist[32];                 // exact decision: the batch's tokens
+  int32_t wcnt[AS_MAXTPW / 32];      // near-tie flags before each flag word
+  float rmx[AL_WAVES];               // per wave: max |c_j|^2
+  int32_t total;
+  int32_t gnext;                     // the next unclaimed token group
+};
+
+// value with its position p (0..15) in the low 4 mantissa bits
+__device__ __forceinline__ float pack4(float v, int p) {
+  return __uint_as_float((__float_as_uint(v) & ~15u) | (unsigned)p);
+}
+
+// Best and second best of a block's 16 values of one token block folded into the running
+// pair (b1 of block bk, b2), in four stages so that each can sit between two MFMAs: a
+// triple's maximum goes up a level, its median is kept, and the second best overall is the
+// largest median (with the running b2 as one more). 38 operations.
+struct Top2 {
+  float v[16], up[6], md[8];
+  __device__ __forceinline__ void stage(int k, const floatx16& a, float& b1, float& b2, int& bk, int r) {
+    if (k == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = pack4(a[i], i);
+    } else if (k == 1) {
+#pragma unroll
+      for (int i = 8; i < 16; ++i) v[i] = pack4(a[i], i);
+    } else if (k == 2) {
+#pragma unroll
+      for (int t = 0; t < 5; ++t) {
+        up[t] = max3f(v[3 * t], v[3 * t + 1], v[3 * t + 2]);
+        md[t] = __builtin_amdgcn_fmed3f(v[3 * t], v[3 * t + 1], v[3 * t + 2]);
+      }
+      up[5] = v[15];
+    } else {
+      const float z0 = max3f(up[0], up[1], up[2]), z1 = max3f(up[3], up[4], up[5]);
+      md[5] = __builtin_amdgcn_fmed3f(up[0], up[1], up[2]);
+      md[6] = __builtin_amdgcn_fmed3f(up[3], up[4], up[5]);
+      const float nb1 = max3f(z0, z1, b1);
+      md[7] = __builtin_amdgcn_fmed3f(z0, z1, b1);
+      float s = max3f(md[0], md[1], md[2]);
+      s = max3f(s, md[3], md[4]);
+      s = max3f(s, md[5], md[6]);
+      b2 = max3f(s, md[7], b2);
+      bk = nb1 > b1 ? r : bk;
+      b1 = nb1;
+    }
+  }
+};
+
+__global__ __attribute__((amdgpu_flat_work_group_size(AL_THREADS, AL_THREADS), amdgpu_waves_per_eu(2, 2))) void
+k_assign_lds(BuildSeq sa, int tpw, const uint16_t* __restrict__ K, const uint16_t* __restrict__ chat,
+             const float* __restrict__ norm, int32_t* __restrict__ assign) {
+  extern __shared__ uint8_t smem[];
+  AssignLdsL& S = *reinterpret_cast<AssignLdsL*>(smem);
+  Unit U;
+  int tb0;
+  assign_wg_map(sa, tpw, xcd_linear(blockIdx.x, gridDim.x), U, tb0);
+  const int nrow = min(tpw, U.L - tb0);  // rows of the workgroup's range
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, h = lane >> 5, col = lane & 31;
+  const int Kc = U.Kc, nA2 = ((Kc + 63) >> 6) * 2;  // 32-row blocks, an even count
+  const uint16_t* Kr = K + (U.irow0 + tb0) * D;    // first input row of the range
+  // B fragments of the group at t: token block tb, lane (col, h) holds chunks 2 st + h of token
+  // t + 32 tb + col, loaded k-step by k-step in the order the MFMAs take them; rows past the
+  // range end repeat its last row (their results are not used). The first group's are loaded
+  // before the centroids.
+  auto load_b = [&](bf16x8_t (&Bv)[2][8], int t) {
+    const uint16_t* x0 = Kr + (int64_t)min(t + col, nrow - 1) * D + h * 8;
+    const uint16_t* x1 = Kr + (int64_t)min(t + 32 + col, nrow - 1) * D + h * 8;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      Bv[0][st] = *reinterpret_cast<const bf16x8_t*>(x0 + st * 16);
+      Bv[1][st] = *reinterpret_cast<const bf16x8_t*>(x1 + st * 16);
+    }
+  };
+  const int t_first = wv * AL_TPG;
+  bf16x8_t B[2][8];
+  load_b(B, t_first);
+
+  // 1. the centroids into LDS (rows past Kc zero), -|c|^2/2 (padding rows: a finite floor
+  // every real value beats), max |c|^2, the near-tie flags cleared
+  {
+    constexpr int CL = AL_MAXC * 16 / AL_THREADS;
+    u32x4 cv[CL];
+#pragma unroll
+    for (int i = 0; i < CL; ++i) {
+      const int s = tid + i * AL_THREADS, j = s >> 4, c = s & 15;
+      cv[i] = *reinterpret_cast<const u32x4*>(chat + (U.gclu + min(j, Kc - 1)) * D + c * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < CL; ++i) {
+      const int s = tid + i * AL_THREADS, j = s >> 4, c = s & 15;
+      if (j < nA2 * 32) S.cent[c * AL_MAXC + j] = j < Kc ? cv[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+    float m = 0.f;
+    for (int j = tid; j < nA2 * 32; j += AL_THREADS) {
+      const float v = j < Kc ? norm[U.gclu + j] : 0.f;
+      S.nh[j] = j < Kc ? -0.5f * v : -__FLT_MAX__;
+      m = fmaxf(m, v);
+    }
+    m = wave_max(m);
+    if (lane == 0) S.rmx[wv] = m;
+    for (int i = tid; i < AS_MAXTPW / 32; i += AL_THREADS) S.nearw[i] = 0u;
+    if (tid == 0) S.gnext = AL_WAVES;  // groups 0..7 are the waves' first
+  }
+  __syncthreads();
+  float R2 = S.rmx[0];
+#pragma unroll
+  for (int w2 = 1; w2 < AL_WAVES; ++w2) R2 = fmaxf(R2, S.rmx[w2]);
+  const float R = __builtin_amdgcn_sqrtf(R2);
+
+  // A fragments of block r, k-step st: lane (col, h) reads chunk 2 st + h of row 32 r + col
+  const u32x4* cl = S.cent + h * AL_MAXC + col;
+  auto read_a = [&](int r, int st) { return __builtin_bit_cast(bf16x8_t, cl[32 * r + 2 * st * AL_MAXC]); };
+  // accumulator start of block r: rows 32 r + 8 a + 4 h + k at element 4 a + k
+  auto read_n = [&](int r) {
+    const float4* nb = reinterpret_cast<const float4*>(S.nh) + 8 * r + h;
+    floatx16 n;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const float4 t = nb[2 * a];
+      n[4 * a + 0] = t.x;
+      n[4 * a + 1] = t.y;
+      n[4 * a + 2] = t.z;
+      n[4 * a + 3] = t.w;
+    }
+    return n;
+  };
+
+  // 2. The wave's token groups, 64 tokens each: group wv first, then the next unclaimed one of
+  // the workgroup's range, claimed when the current one starts (its B fragments are loaded as
+  // soon as the current group's last MFMAs have read theirs). The two waves of a SIMD do not
+  // progress alike (the arbiter favours the older one), so claimed groups keep both busy to the
+  // end, where a fixed share left the younger wave running its last groups alone.
+  bf16x8_t A[8];
+  floatx16 nv;
+  for (int t0 = t_first; t0 < nrow;) {
+    int qn = 0;
+    if (lane == 0) qn = atomicAdd(&S.gnext, 1);
+    const int tn = __builtin_amdgcn_readfirstlane(qn) * AL_TPG;
+    // |x|^2 of the group's tokens (lane (col, h): half h of token col, then both halves)
+    float x2[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      float s2 = 0.f;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const u32x4 w = __builtin_bit_cast(u32x4, B[tb][st]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t we = w[e];  // bit-cast a named scalar (see xnorm in k_assign)
+          const bf16x2_t x = __builtin_bit_cast(bf16x2_t, we);
+          s2 = __builtin_amdgcn_fdot2_f32_bf16(x, x, s2, false);
+        }
+      }
+      x2[tb] = s2 + swap32(s2);
+    }
+    nv = read_n(0);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) A[st] = read_a(0, st);
+    floatx16 accX[2], accY[2];
+    float b1[2] = {-INFINITY, -INFINITY}, b2[2] = {-INFINITY, -INFINITY};
+    int bk[2] = {0, 0};
+    // One block step, in program order, k-step by k-step: the two MFMAs of block r (one per
+    // token block: independent accumulators, so neither waits for the other), the LDS read of
+    // block rn's A fragment that those MFMAs just freed (and after the first pair its start
+    // values), and an eighth of the selection over the previous block (block rp, in pacc);
+    // a scheduling fence after each k-step keeps that order.
+    Top2 T;
+    auto step = [&](floatx16 (&acc)[2], int rn, floatx16 (&pacc)[2], int rp, bool sel_prev, bool mfma) {
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        if (mfma) {
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+            acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A[st], B[tb][st], st == 0 ? nv : acc[tb], 0, 0, 0);
+          if (st == 0) nv = read_n(rn);
+          A[st] = read_a(rn, st);
+        }
+        if (sel_prev) T.stage(st & 3, pacc[st >> 2], b1[st >> 2], b2[st >> 2], bk[st >> 2], rp);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    step(accX, 1, accY, 0, false, true);  // block 0
+    int r = 0;
+    for (; r + 2 < nA2; r += 2) {
+      step(accY, r + 2, accX, r, true, true);      // block r + 1; selection of block r
+      step(accX, r + 3, accY, r + 1, true, true);  // block r + 2; selection of block r + 1
+    }
+    step(accY, r + 1, accX, r, true, true);  // block r + 1 (the reads of it again: harmless)
+    load_b(B, tn);  // the next group's fragments (past the range end: its last row)
+    step(accY, 0, accY, r + 1, true, false);
+    // merge the two half-waves, the margin test, the ids
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const float ob1 = swap32(b1[tb]), ob2 = swap32(b2[tb]);
+      const int obk = swap32(bk[tb]);
+      const bool take = ob1 > b1[tb];
+      const float nb2 = fmaxf(fminf(b1[tb], ob1), fmaxf(b2[tb], ob2));
+      const float nb1 = fmaxf(b1[tb], ob1);
+      const int p = (int)(__float_as_uint(nb1) & 15u), hw = take ? h ^ 1 : h, blk = take ? obk : bk[tb];
+      const int best_id = 32 * blk + 8 * (p >> 2) + 4 * hw + (p & 3);
+      const float margin = 0x1p-14f * (__builtin_amdgcn_sqrtf(x2[tb]) * R + R2) + 0x1p-100f;
+      const bool near = !(nb1 - nb2 > margin) || !(nb1 > -0x1p127f) || !(margin < 0x1p100f);
+      const int t = t0 + 32 * tb + col;
+      if (h == 0 && t < nrow) {
+        assign[U.row0 + tb0 + t] = U.cbase + best_id;
+        if (near) atomicOr(&S.nearw[t >> 5], 1u << (t & 31));
+      }
+    }
+    t0 = tn;
+  }
+
+  // 3. near-tie tokens: flag words counted, a workgroup scan
+  __syncthreads();
+  const int nwd = (nrow + 31) >> 5;
+  for (int i = tid; i < nwd; i += AL_THREADS) S.wcnt[i] = __builtin_popcount(S.nearw[i]);  // its prefix below
+  __syncthreads();
+  if (wv == 0) {
+    int run = 0;
+    for (int i0 = 0; i0 < nwd; i0 += 64) {
+      const int i = i0 + lane;
+      const int c = i < nwd ? S.wcnt[i] : 0;
+      int incl = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      if (i < nwd) S.wcnt[i] = run + incl - c;
+      run += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) S.total = run;
+  }
+  __syncthreads();
+  const int total = S.total;
+  if (total == 0) return;
+  // Exact decision, 32 tokens at a time: their rows go through the MFMAs again (wave wv takes
+  // blocks 2 wv and 2 wv + 1); every centroid within 2^-14 (|x| R + R^2) + 2^-40 (|x| + R)^2
+  // + 2^-100 of the best fp32 value gets D_j = sum_i (x_i - c_j,i)^2 in binary64, dims in
+  // order, each operation rounded; argmin with the lowest id on ties (as in k_assign).
+  for (int f0 = 0; f0 < total; f0 += 32) {
+    const int nb = min(32, total - f0);
+    for (int i = tid; i < nwd; i += AL_THREADS) {
+      uint32_t f = S.nearw[i];
+      int k = S.wcnt[i];
+      while (f != 0u) {
+        const int b = __builtin_ctz(f);
+        f &= f - 1u;
+        if (k >= f0 && k < f0 + 32) S.flist[k - f0] = 32 * i + b;
+        ++k;
+      }
+    }
+    if (tid < 32) {
+      S.fd[tid] = ~0ull;
+      S.fj[tid] = 0x7FFFFFFF;
+    }
+    __syncthreads();
+    {
+      const int slot = tid, t = slot >> 4, c = (slot & 15) ^ (t & 15);
+      S.rows[slot] = *reinterpret_cast<const u32x4*>(Kr + (int64_t)S.flist[min(t, nb - 1)] * D + c * 8);
+    }
+    __syncthreads();
+    bf16x8_t Bx[8];
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+      Bx[st] = __builtin_bit_cast(bf16x8_t, S.rows[col * 16 + ((2 * st + h) ^ (col & 15))]);
+    float s2 = 0.f;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const u32x4 w = __builtin_bit_cast(u32x4, Bx[st]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t we = w[e];
+        const float a = bf16_lo(we), b = bf16_hi(we);
+        s2 = fmaf(a, a, s2);
+        s2 = fmaf(b, b, s2);
+      }
+    }
+    s2 += swap32(s2);
+    const float X = sqrtf(s2);
+    const float win = 0x1p-14f * (X * R + R2) + 0x1p-40f * (X + R) * (X + R) + 0x1p-100f;
+    floatx16 av[2];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r = min(2 * wv + q, nA2 - 1);
+      av[q] = read_n(r);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) av[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_a(r, st), Bx[st], av[q], 0, 0, 0);
+      if (2 * wv + q < nA2) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, av[q][i]);
+      }
+    }
+    mx = fmaxf(mx, swap32(mx));
+    if (h == 0) S.red[wv][col] = mx;
+    __syncthreads();
+    float M = S.red[0][col];
+#pragma unroll
+    for (int w2 = 1; w2 < AL_WAVES; ++w2) M = fmaxf(M, S.red[w2][col]);
+    const float thr = M - win;
+    const u32x4* xr = S.rows + col * 16;
+    double best = INFINITY;
+    int bj = 0x7FFFFFFF;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (2 * wv + q >= nA2) continue;
+      uint32_t cm = 0u;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) cm |= (uint32_t)!(av[q][i] < thr) << i;  // NaN: a candidate
+      while (cm != 0u) {
+        const int i = __builtin_ctz(cm);
+        cm &= cm - 1u;
+        const int j = 32 * (2 * wv + q) + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (j >= Kc) continue;
+        const u32x4* cj = S.cent + j;
+        double acc = 0.0;
+        for (int c = 0; c < 16; ++c) {
+          const u32x4 xv = xr[c ^ (col & 15)], cw = cj[c * AL_MAXC];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t xe = xv[e], ce = cw[e];
+            const double d0 = __dsub_rn((double)bf16_lo(xe), (double)bf16_lo(ce));
+            acc = __dadd_rn(acc, __dmul_rn(d0, d0));
+            const double d1 = __dsub_rn((double)bf16_hi(xe), (double)bf16_hi(ce));
+            acc = __dadd_rn(acc, __dmul_rn(d1, d1));
+          }
+        }
+        if (acc < best || (acc == best && j < bj)) {
+          best = acc;
+          bj = j;
+        }
+      }
+    }
+    const unsigned long long bd = (unsigned long long)__double_as_longlong(best);
+    if (bj != 0x7FFFFFFF) atomicMin(&S.fd[col], bd);
+    __syncthreads();
+    if (bj != 0x7FFFFFFF && bd == S.fd[col]) atomicMin(&S.fj[col], bj);
+    __syncthreads();
+    if (tid < nb) assign[U.row0 + tb0 + S.flist[tid]] = U.cbase + S.fj[tid];
+    __syncthreads();
+  }
+}
+
 // ------------------------------------------------------------------ k_sort
 // Stable counting sort of one unit by cluster: sorted slot of token t is
 // offset(c) + #{t' < t in the unit : a(t') = c}. The 16 waves take consecutive
@@ -1423,10 +1801,10 @@ __global__ __launch_bounds__(1024) void k_stage(StageArgs a, const uint16_t* __r
 hipError_t build_set_attrs() {
   WAVE_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_init), hipFuncAttributeMaxDynamicSharedMemorySize,
                                160 * 1024));
-  WAVE_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_assign<false>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(AssignLds)));
   WAVE_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_assign<true>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(AssignLds)));
+  WAVE_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_assign_lds),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, sizeof(AssignLdsL)));
   WAVE_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sort), hipFuncAttributeMaxDynamicSharedMemorySize,
                                16 * WAVE_MAX_CLUSTERS_PER_SEG * 4));
   WAVE_TRY(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sort_radix),
@@ -1506,9 +1884,12 @@ static hipError_t run_build(const BuildSeq& bs, const uint16_t* K, const uint16_
   const unsigned ugrid = cgrid + (bs.ident ? BIG_CAP / 4 : 0);
   for (int it = 0; it < iters; ++it) {
     bl.parity = it & 1;
-    WAVE_TRY(launch("k_assign", bs.K_s > AS_GROUP ? k_assign<true> : k_assign<false>, dim3((unsigned)agrid),
-                    dim3(AS_THREADS), sizeof(AssignLds), st, bs, tpw, K, chat, ws.norm, ix.assign, ws.xn2,
-                    it == 0 ? 1 : 0));
+    if (bs.K_s <= AL_MAXC)
+      WAVE_TRY(launch("k_assign", k_assign_lds, dim3((unsigned)agrid), dim3(AL_THREADS), sizeof(AssignLdsL), st, bs,
+                      tpw, K, chat, ws.norm, ix.assign));
+    else
+      WAVE_TRY(launch("k_assign", k_assign<true>, dim3((unsigned)agrid), dim3(AS_THREADS), sizeof(AssignLds), st, bs,
+                      tpw, K, chat, ws.norm, ix.assign, ws.xn2, it == 0 ? 1 : 0));
     if (trace != nullptr)
       WAVE_TRY(hipMemcpyAsync(trace + (int64_t)it * rows, ix.assign, sizeof(int32_t) * (size_t)rows,
                               hipMemcpyDeviceToDevice, st));
