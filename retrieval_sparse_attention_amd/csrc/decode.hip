@@ -94,6 +94,16 @@ struct ScoreLds {
 template <int GS>
 __device__ void tail_role(const SeqArgs& sa, const DecodeArgs& da, const uint16_t* q, const DecodeWs& ws, int w);
 
+// maximum over the wave: rows of 16 by DPP, then lanes i ^ 16 and i ^ 32 (one LDS exchange)
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror 8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror 4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xF, 0xF, false));  // row_ror 2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xF, 0xF, false));  // row_ror 1
+  v = max(v, (uint32_t)__shfl_xor((int)v, 16, 64));
+  return max(v, swap32(v));
+}
+
 // TAIL: the grid also holds the appended-token workgroups (a separate instantiation, so
 // that their registers do not lower the scoring workgroups' occupancy elsewhere)
 template <int GS, bool TAIL>
@@ -239,9 +249,7 @@ __global__ __launch_bounds__(SCORE_THREADS) void k_score(SeqArgs sa, DecodeArgs 
     uint32_t* ct = ws.ctop + ((int64_t)(b * da.H + g * GS + hh) * chm + chunk) * 8;
 #pragma unroll
     for (int r4 = 0; r4 < DEC_CHUNK_TOPS; ++r4) {
-      uint32_t mx = max(u[0], u[1]);
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+      const uint32_t mx = wave_umax(max(u[0], u[1]));
       const uint64_t b0 = __ballot(u[0] == mx), b1 = __ballot(u[1] == mx);
       // take out one instance: the lowest lane's
       if (b0 != 0ull) {
