@@ -170,6 +170,15 @@ def summarize_trace(d, command):
     print("\n".join(out))
 
 
+# kernels launched under one name: the assign runs k_assign_lds up to 512 clusters a segment,
+# k_assign<true> above
+_KERNELS_OF = {"k_assign": ("k_assign", "k_assign_lds")}
+
+
+def _is_kernel(name, kernel):
+    return _short(name).split("<")[0] in _KERNELS_OF.get(kernel, (kernel,))
+
+
 def _counter_per_dispatch(d, counter, kernel=None):
     """Per-dispatch values of one counter; the kernel's dispatches, or the largest one."""
     vals = {}
@@ -180,7 +189,7 @@ def _counter_per_dispatch(d, counter, kernel=None):
         vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
     if kernel is None:
         return [max(vals.values())]
-    return [v for (_, n), v in vals.items() if _short(n).split("<")[0] == kernel]
+    return [v for (_, n), v in vals.items() if _is_kernel(n, kernel)]
 
 
 def summarize_traffic(kernel, fdir, wdir, cfdir, cwdir, command):
@@ -215,7 +224,7 @@ def summarize_mfma(kernel, d, command):
     per-XCD cycles; bf16 flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512."""
     per = {}
     for r in _csv_rows(d, "counter_collection.csv"):
-        if _short(r["Kernel_Name"]).split("<")[0] != kernel:
+        if not _is_kernel(r["Kernel_Name"], kernel):
             continue
         e = per.setdefault(r["Dispatch_Id"], {})
         e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
