@@ -949,6 +949,8 @@ struct AssignLdsL {
   int32_t gnext;                     // the next unclaimed token group
 };
 
+static_assert(sizeof(AssignLdsL) <= 160 * 1024, "k_assign_lds LDS");
+
 // value with its position p (0..15) in the low 4 mantissa bits
 __device__ __forceinline__ float pack4(float v, int p) {
   return __uint_as_float((__float_as_uint(v) & ~15u) | (unsigned)p);
