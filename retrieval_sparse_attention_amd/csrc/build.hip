@@ -1121,7 +1121,13 @@ k_assign_lds(BuildSeq sa, int tpw, const uint16_t* __restrict__ K, const uint16_
           if (st == 0) nv = read_n(rn);
           A[st] = read_a(rn, st);
         }
-        if (sel_prev) T.stage(st & 3, pacc[st >> 2], b1[st >> 2], b2[st >> 2], bk[st >> 2], rp);
+        if (sel_prev) {
+          // the selection at a raised wave priority, so that the arbiter takes it before the
+          // other wave of the SIMD (≈ 2% faster than leaving the older wave first throughout)
+          __builtin_amdgcn_s_setprio(1);
+          T.stage(st & 3, pacc[st >> 2], b1[st >> 2], b2[st >> 2], bk[st >> 2], rp);
+          __builtin_amdgcn_s_setprio(0);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     };
